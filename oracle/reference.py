@@ -1,0 +1,341 @@
+"""Plain CPU definitions of the block-draft readout hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke entry point and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+Every step is written as its definition, with float64 accumulation (numpy) and
+explicit Python loops for the argmax chain and the verification scan.  Nothing
+is blocked, fused or reordered except where noted (the LM head is evaluated in
+slices of vocabulary rows purely to bound host memory; every logit is still one
+float64 dot product rounded once to float32).
+
+Stored tensors arrive as numpy arrays in their storage dtype: ``'f32'`` ->
+float32, ``'bf16'`` -> uint16 bfloat16 bit patterns.  ``widen`` turns either into
+exact float64 values.
+
+Sources (web pages; cited by title and section):
+  * "docs(vllm): Qwen3.8-27B DFlash drafter recipe" (intel/llm-scaler PR #620),
+    DSpark port notes -- the Markov head (markov_w1 embedding, markov_w2
+    projection, compute_markov_bias), the proposer's capture of the accepted
+    bonus token, the semi-autoregressive biased greedy sample, and the adaptive
+    block truncation by confidence; "Summary / Quality" -- greedy speculative
+    decoding is lossless.
+  * "Qwen3.8-27B-DSpark -- vLLM-ready" model card (Doopeworld), "Target
+    quantisation" and "Limitations" -- taps at layers 4/16/28/40/52, fc input
+    5 x 5120; "Measured results" -- per-position acceptance at k=7.
+  * "Qwen4Exp DFlash drafter" (wtdcode/vllm-backport PR #128), "What was
+    missing" item 1 -- features at target_layer_ids are concatenated, fc.weight
+    is [2560, 12800]; "Benchmarks / Acceptance detail" -- definitions of mean
+    acceptance length and drafted-token rate.
+
+Readings where the pages leave a step open are listed in the design notes and
+restated at each function.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+# Rows of the LM head evaluated at once (host-memory bound only).
+LM_HEAD_SLICE = 16384
+
+
+# ----------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of a stored tensor.
+
+    bfloat16 is the upper 16 bits of an IEEE binary32, so its value is the
+    float32 whose bit pattern is ``bits << 16``; float32 -> float64 is exact.
+    """
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def round_to_f32(x: np.ndarray) -> np.ndarray:
+    """float64 -> float32, IEEE round to nearest even (numpy's cast)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+
+    Keep the upper 16 bits; the dropped lower 16 bits decide: above half an ulp
+    round up, below round down, exactly half round to the even upper value.  A
+    carry out of the mantissa correctly bumps the exponent.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding is defined here for finite values only")
+    u = x.view(np.uint32).astype(np.uint64)
+    hi = u >> np.uint64(16)
+    lo = u & np.uint64(0xFFFF)
+    half = np.uint64(0x8000)
+    up = (lo > half) | ((lo == half) & ((hi & np.uint64(1)) == np.uint64(1)))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+def _finite(a: np.ndarray, what: str) -> None:
+    if not np.all(np.isfinite(a)):
+        raise ValueError(f"{what} must be finite")
+
+
+# ----------------------------------------------------------------------------
+# S1: fuse the tapped hidden states and apply the drafter fc
+# ----------------------------------------------------------------------------
+
+def fuse_fc(taps: Sequence[np.ndarray], fc_w: np.ndarray, dtype: str) -> np.ndarray:
+    """F = concat_t(X_t) @ fc_w^T, float32 result of a float64 sum.
+
+    The drafter reads the target's hidden states at its target layers and
+    concatenates them feature-wise (vllm-backport PR #128, "What was missing"
+    item 1); tap t fills columns [t*H, (t+1)*H) in the listed layer order.
+    fc_w is [out=H, in=T*H] -- [2560, 12800] for five 2560-wide features in
+    the same item, 5 x 5120 inputs on the Qwen3.8-27B-DSpark model card
+    ("Limitations").  Reading: the fc is a plain linear map (no bias, norm or
+    activation is described).
+    """
+    T = len(taps)
+    if T < 1:
+        raise ValueError("at least one tap is required")
+    rows, H = np.shape(taps[0])
+    for t in taps:
+        if np.shape(t) != (rows, H):
+            raise ValueError("all taps must be [rows, H]")
+    if np.shape(fc_w) != (H, T * H):
+        raise ValueError(f"fc weight must be [H, T*H] = [{H}, {T * H}], got {np.shape(fc_w)}")
+    X = np.concatenate([widen(t, dtype) for t in taps], axis=1)
+    W = widen(fc_w, dtype)
+    _finite(X, "taps")
+    return round_to_f32(X @ W.T)
+
+
+# ----------------------------------------------------------------------------
+# S2: LM-head logits for the k block positions
+# ----------------------------------------------------------------------------
+
+def lm_head(hidden: np.ndarray, lm_w: np.ndarray, dtype: str) -> np.ndarray:
+    """Z[..., v] = sum_h hidden[..., h] * lm_w[v, h]; float32 result of a float64 sum.
+
+    Full-vocabulary logits that the DSpark greedy sample biases and argmaxes
+    (llm-scaler PR #620, DSpark port notes, dflash.py).  lm_w is [V, H].
+    """
+    hid = widen(hidden, dtype)
+    _finite(hid, "hidden")
+    lead = hid.shape[:-1]
+    H = hid.shape[-1]
+    V, H2 = np.shape(lm_w)
+    if H2 != H:
+        raise ValueError("lm head must be [V, H]")
+    h2 = hid.reshape(-1, H)
+    Z = np.empty((h2.shape[0], V), dtype=np.float32)
+    for v0 in range(0, V, LM_HEAD_SLICE):
+        v1 = min(V, v0 + LM_HEAD_SLICE)
+        Z[:, v0:v1] = round_to_f32(h2 @ widen(lm_w[v0:v1], dtype).T)
+    return Z.reshape(*lead, V)
+
+
+# ----------------------------------------------------------------------------
+# S3: DSpark low-rank Markov bias, semi-autoregressive greedy argmax
+# ----------------------------------------------------------------------------
+
+def markov_bias(w1_64: np.ndarray, w2_64: np.ndarray, prev: int) -> np.ndarray:
+    """bias[v] = sum_j w2[v, j] * w1[prev, j], rounded once to float32.
+
+    The Markov head embeds the previous token with markov_w1 ([V, r]) and
+    projects the r-vector to the full vocabulary with markov_w2 ([V, r])
+    (llm-scaler PR #620, DSpark port notes, qwen3_dflash.py: VanillaMarkov /
+    compute_markov_bias).  Reading: no scale, bias term or activation.
+    Arguments are already-widened float64 weights.
+    """
+    e = w1_64[int(prev)]
+    return round_to_f32(w2_64 @ e)
+
+
+def first_argmax(s: np.ndarray) -> int:
+    """Lowest index among the maximal entries: min{v : s[v] = max s}.
+
+    Finite inputs only; -0.0 and +0.0 compare equal and so tie.
+    """
+    s = np.asarray(s)
+    _finite(s, "argmax input")
+    return int(np.flatnonzero(s == s.max())[0])
+
+
+def top2_gap(s: np.ndarray) -> float:
+    """Largest minus second-largest entry, duplicates counted (an exact tie gives 0)."""
+    s = np.asarray(s, dtype=np.float64).ravel()
+    n = s.size
+    if n < 2:
+        return float("inf")
+    part = np.partition(s, [n - 2, n - 1])
+    return float(part[n - 1] - part[n - 2])
+
+
+def semi_ar_argmax(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndarray],
+                   prev0: np.ndarray, dtype: str):
+    """Draft tokens d [B, k] and top-2 gaps [B, k] of the biased greedy chain.
+
+    For each sequence the context starts at the accepted bonus token of the
+    previous step (the proposer captures it as the Markov previous token,
+    llm-scaler PR #620, DSpark port notes, dflash.py).  Position i adds the
+    bigram bias of the context, takes the full-vocabulary argmax of the biased
+    float32 logits, and that biased prediction becomes the context of position
+    i+1 (same notes: the bias is applied semi-autoregressively across the
+    block).  Reading: the bias is added to the raw logits (adding it to
+    log-softmax gives the same argmax).  ``w1 is None`` or rank 0 means no bias.
+    """
+    Z = np.asarray(Z, dtype=np.float32)
+    B, k, V = Z.shape
+    prev0 = np.asarray(prev0).reshape(B)
+    use_bias = w1 is not None and w2 is not None and np.shape(w1)[-1] > 0
+    if use_bias:
+        W1 = widen(w1, dtype)
+        W2 = widen(w2, dtype)
+        if W1.shape != W2.shape or W1.shape[0] != V:
+            raise ValueError("markov weights must both be [V, r]")
+    d = np.zeros((B, k), dtype=np.int64)
+    gap = np.zeros((B, k), dtype=np.float64)
+    for b in range(B):
+        p = int(prev0[b])
+        if not 0 <= p < V:
+            raise ValueError("previous token out of range")
+        for i in range(k):
+            if use_bias:
+                s = Z[b, i] + markov_bias(W1, W2, p)  # float32 + float32, IEEE RNE
+            else:
+                s = Z[b, i].copy()
+            d[b, i] = first_argmax(s)
+            gap[b, i] = top2_gap(s)
+            p = int(d[b, i])
+    return d, gap
+
+
+# ----------------------------------------------------------------------------
+# S4: greedy exact-match verification
+# ----------------------------------------------------------------------------
+
+def truncate_by_confidence(conf: Optional[np.ndarray], threshold: Optional[float],
+                           batch: int, k: int) -> np.ndarray:
+    """Block length L_b after adaptive truncation.
+
+    The DSpark proposer can shorten the draft block where the per-position
+    acceptance confidence is low (llm-scaler PR #620, DSpark port notes,
+    _truncate_by_confidence).  Reading: L_b is the first position whose
+    confidence is strictly below the threshold (that position and all later
+    ones are dropped), else k; no scores or a NaN threshold means L_b = k.
+    L_b = 0 is allowed.
+    """
+    L = np.full(batch, k, dtype=np.int64)
+    if conf is None or threshold is None or np.isnan(threshold):
+        return L
+    c = np.asarray(conf, dtype=np.float32).reshape(batch, k)
+    th = np.float32(threshold)
+    for b in range(batch):
+        for i in range(k):
+            if c[b, i] < th:
+                L[b] = i
+                break
+    return L
+
+
+def target_argmax(Y: np.ndarray, dtype: str, L: Optional[np.ndarray] = None) -> np.ndarray:
+    """t[b, j] = lowest-index argmax of the target logits at block position j.
+
+    Greedy verification compares each draft token with the target's own greedy
+    choice (model card, "Tuning notes": greedy exact-match).  Positions beyond
+    the (possibly truncated) block, j > L_b, are not verified and get -1.
+    """
+    Yw = widen(Y, dtype)
+    B, k1, V = Yw.shape
+    t = np.full((B, k1), -1, dtype=np.int64)
+    for b in range(B):
+        last = k1 - 1 if L is None else int(L[b])
+        for j in range(last + 1):
+            t[b, j] = first_argmax(Yw[b, j])
+    return t
+
+
+def verify_greedy(d: np.ndarray, t: np.ndarray, L: np.ndarray):
+    """Accepted prefix a_b, bonus token, per-position accepted/proposed counts.
+
+    a_b is the longest prefix of the (truncated) draft on which every draft
+    token equals the target argmax; the target's token at position a_b is
+    always emitted as the bonus, so the emitted tokens equal the target's own
+    greedy tokens (llm-scaler PR #620, "Summary / Quality": greedy speculative
+    decoding is lossless).  Counts follow the spec-decode per-position
+    accounting (vllm-backport PR #128, "Acceptance detail"): position i counts
+    as accepted when a_b > i and as proposed when L_b > i.
+    """
+    d = np.asarray(d, dtype=np.int64)
+    t = np.asarray(t, dtype=np.int64)
+    B, k = d.shape
+    a = np.zeros(B, dtype=np.int64)
+    bonus = np.zeros(B, dtype=np.int64)
+    acc = np.zeros(k, dtype=np.int64)
+    prop = np.zeros(k, dtype=np.int64)
+    for b in range(B):
+        Lb = int(L[b])
+        n = 0
+        while n < Lb and d[b, n] == t[b, n]:
+            n += 1
+        a[b] = n
+        bonus[b] = t[b, n]
+        for i in range(k):
+            if n > i:
+                acc[i] += 1
+            if Lb > i:
+                prop[i] += 1
+    return a, bonus, acc, prop
+
+
+def mean_acceptance_length(acc: np.ndarray, steps: int, batch: int) -> float:
+    """Tokens emitted per sequence per verification step: 1 (bonus) + accepted.
+
+    vllm-backport PR #128 ("Acceptance detail") defines mean acceptance length
+    as accepted tokens per verification step; the bonus token is counted, which
+    is what makes the model card's k=7 curve ("Measured results", sum 1.78)
+    land at 2.78 inside its 2.45-2.79 range ("Target quantisation").
+    """
+    return 1.0 + float(np.sum(acc)) / float(steps * batch)
+
+
+def drafted_token_rate(acc: np.ndarray, prop: np.ndarray) -> float:
+    """Accepted over drafted tokens (vllm-backport PR #128, "Acceptance detail")."""
+    return float(np.sum(acc)) / float(np.sum(prop))
+
+
+# ----------------------------------------------------------------------------
+# one block-step
+# ----------------------------------------------------------------------------
+
+def block_step(dtype: str, taps, fc_w, draft_hidden, lm_w, w1, w2, prev0,
+               target_logits=None, confidence=None, threshold=None,
+               draft_tokens=None):
+    """S1..S4 for one batch.  Returns a dict of every intermediate.
+
+    ``target_logits`` may be None (draft only).  ``draft_tokens`` overrides the
+    drafted tokens fed to verification (verification-only use).
+    """
+    out = {}
+    out["fc_out"] = fuse_fc(taps, fc_w, dtype)
+    Z = lm_head(draft_hidden, lm_w, dtype)
+    out["logits"] = Z
+    d, gap = semi_ar_argmax(Z, w1, w2, prev0, dtype)
+    out["draft_tokens"], out["gap"] = d, gap
+    if target_logits is not None:
+        B, k = d.shape
+        dv = d if draft_tokens is None else np.asarray(draft_tokens, dtype=np.int64)
+        L = truncate_by_confidence(confidence, threshold, B, k)
+        t = target_argmax(target_logits, dtype, L)
+        a, bonus, acc, prop = verify_greedy(dv, t, L)
+        out.update(block_len=L, target_argmax=t, accepted=a, bonus=bonus,
+                   accept_counts=acc, proposed_counts=prop)
+    return out
