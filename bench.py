@@ -1,0 +1,317 @@
+"""Benchmark of the block-draft readout hot path on one MI355X.
+
+One step = one block-step over one batch: dflash_fuse_fc (S1) ->
+dspark_lm_head + dspark_markov_argmax (S2 + S3; dspark_draft_block is exactly
+these two calls) -> spec_verify_greedy (S4).  Inputs cycle through a pool of
+pre-generated seeded steps that are resident in HBM before timing starts.
+
+Prints ONE JSON line: block-steps/s, the roofline of the dominant kernel (the
+LM-head GEMM, timed with HIP events on its launch stream), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources that define the LM-head GEMM kernel."""
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "bdr_device.h", "bdr_internal.h"):
+        with open(os.path.join(ROOT, "block_draft_readout_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter summary,
+    or None when the summary is missing or the kernel has changed since."""
+    path = os.path.join(PROFILES, f"lm_head_gemm_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+class Step:
+    """Pre-bound C-ABI calls of one pool slot (pointers resolved once)."""
+
+    def __init__(self, L, w, dt, g, slot, bufs, stream):
+        self.L, self.w, self.dt, self.g, self.s, self.b = L, w, dt, g, slot, bufs
+        self.stream = stream
+        self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
+
+    def fc(self):
+        w, b = self.w, self.b
+        return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+                                     self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
+                                     b["ws_fc"], b["ws_fc_n"], self.stream)
+
+    def lm_head(self):
+        w = self.w
+        return self.L.dspark_lm_head(self.s["draft_hidden"].data_ptr(), w.batch * w.k, w.hidden,
+                                     w.vocab, self.dt, self.g["lm_w"].data_ptr(),
+                                     self.b["logits"].data_ptr(), self.stream)
+
+    def markov(self):
+        w, b = self.w, self.b
+        return self.L.dspark_markov_argmax(b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt,
+                                           self.g["w1"].data_ptr(), self.g["w2"].data_ptr(),
+                                           w.rank, self.s["prev0"].data_ptr(), b["d"].data_ptr(),
+                                           b["ws_m"], b["ws_m_n"], self.stream)
+
+    def draft_block(self):
+        w, b = self.w, self.b
+        return self.L.dspark_draft_block(self.s["draft_hidden"].data_ptr(), w.batch, w.k,
+                                         w.hidden, w.vocab, self.dt, self.g["lm_w"].data_ptr(),
+                                         self.g["w1"].data_ptr(), self.g["w2"].data_ptr(), w.rank,
+                                         self.s["prev0"].data_ptr(), b["d"].data_ptr(),
+                                         b["logits"].data_ptr(), b["ws_m"], b["ws_m_n"],
+                                         self.stream)
+
+    def verify(self):
+        w, b = self.w, self.b
+        conf = self.s.get("conf")
+        th = float("nan") if w.threshold is None else w.threshold
+        return self.L.spec_verify_greedy(
+            self.s["Y"].data_ptr(), self.dt, w.batch, w.k, w.vocab, b["d"].data_ptr(),
+            None if conf is None else conf.data_ptr(), th, b["bl"].data_ptr(),
+            b["acc_len"].data_ptr(), b["bonus"].data_ptr(), b["targ"].data_ptr(),
+            b["acc"].data_ptr(), b["prop"].data_ptr(), b["ws_v"], b["ws_v_n"], self.stream)
+
+
+def check(rc, what):
+    if rc != 0:
+        import block_draft_readout_amd as bdr
+        raise RuntimeError(f"{what} failed ({rc}): {bdr.lib().bdr_last_error().decode()}")
+
+
+def cpu_baseline(w, W, slot_host):
+    """The oracle, as it stands, on one full block-step of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    t0 = time.perf_counter()
+    oracle.block_step(w.dtype, slot_host["taps"], W["fc_w"], slot_host["draft_hidden"],
+                      W["lm_w"], W["w1"], W["w2"], slot_host["prev0"],
+                      target_logits=slot_host["Y"], confidence=slot_host["conf"],
+                      threshold=w.threshold)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / dt, "unit": "block-steps/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"1 full block-step of {w.name} (S1-S4, all {w.batch} rows), "
+                      f"{dt:.1f} s on the host; numpy float64, BLAS threads={blas}, "
+                      f"affinity cores={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen27b_b1")
+    ap.add_argument("--pool", type=int, default=8)
+    ap.add_argument("--graph", action="store_true", help="replay HIP graphs of whole steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import block_draft_readout_amd as bdr
+    import workloads
+    from workloads import synth
+
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = bdr.lib()
+    dt = bdr.BDR_BF16 if w.dtype == "bf16" else bdr.BDR_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.time()
+    W = synth.make_weights(w)
+    g = {k: up(v) for k, v in W.items()}
+    log(f"{w.describe()}: weights ready in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = C.c_void_p(stream.cuda_stream)
+
+    def ws(n):
+        if n == 0:
+            return None, 0, None
+        t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        p = (t.data_ptr() + 255) & ~255
+        return C.c_void_p(p), n, t
+
+    B, k, V, H = w.batch, w.k, w.vocab, w.hidden
+    keep = []
+    bufs = {"F": torch.empty((w.rows, H), dtype=tdt, device=dev),
+            "logits": torch.empty((B, k, V), dtype=torch.float32, device=dev),
+            "d": torch.empty((B, k), dtype=torch.int32, device=dev),
+            "bl": torch.empty(B, dtype=torch.int32, device=dev),
+            "acc_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "bonus": torch.empty(B, dtype=torch.int32, device=dev),
+            "targ": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
+            "acc": torch.zeros(k, dtype=torch.int64, device=dev),
+            "prop": torch.zeros(k, dtype=torch.int64, device=dev)}
+    for key, n in (("ws_fc", L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
+                   ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
+                   ("ws_v", L.spec_verify_workspace_bytes(B, k, V))):
+        p, n2, t = ws(n)
+        bufs[key], bufs[key + "_n"] = p, n2
+        keep.append(t)
+
+    # pool of steps resident in HBM; targets planted on this path's own draft
+    t0 = time.time()
+    slots, host0 = [], None
+    for p in range(args.pool):
+        s = synth.make_step(w, p)
+        slot = {"taps": [up(t) for t in s["taps"]], "draft_hidden": up(s["draft_hidden"]),
+                "prev0": up(s["prev0"])}
+        conf = synth.make_confidence(w, p)
+        slot["conf"] = None if conf is None else up(conf)
+        st = Step(L, w, dt, g, slot, bufs, sptr)
+        check(st.draft_block(), "dspark_draft_block")
+        torch.cuda.synchronize()
+        d_host = bufs["d"].cpu().numpy()
+        Y = synth.plant_targets(w, p, s["noise"], d_host)["target_logits"]
+        slot["Y"] = up(Y)
+        slots.append(st)
+        if p == 0:
+            host0 = {"taps": s["taps"], "draft_hidden": s["draft_hidden"], "prev0": s["prev0"],
+                     "Y": Y, "conf": conf}
+    log(f"pool of {args.pool} steps ready in {time.time() - t0:.1f}s")
+
+    def run_step(st):
+        check(st.fc(), "dflash_fuse_fc")
+        check(st.lm_head(), "dspark_lm_head")
+        check(st.markov(), "dspark_markov_argmax")
+        check(st.verify(), "spec_verify_greedy")
+
+    graphs = None
+    if args.graph:
+        graphs = []
+        for st in slots:  # warm once eagerly (device checks, caches), then capture
+            run_step(st)
+        torch.cuda.synchronize()
+        for st in slots:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                cs = C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+                st.stream = cs
+                run_step(st)
+            st.stream = sptr
+            graphs.append(gr)
+
+    def step_i(i):
+        if graphs is not None:
+            graphs[i % len(graphs)].replay()
+        else:
+            run_step(slots[i % len(slots)])
+
+    for i in range(args.warmup):
+        step_i(i)
+    torch.cuda.synchronize()
+
+    # phase 1: whole steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step_i(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # phase 2: the same steps eagerly, with HIP events around each LM-head launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        st = slots[i % len(slots)]
+        check(st.fc(), "dflash_fuse_fc")
+        evs[i][0].record(stream)
+        check(st.lm_head(), "dspark_lm_head")
+        evs[i][1].record(stream)
+        check(st.markov(), "dspark_markov_argmax")
+        check(st.verify(), "spec_verify_greedy")
+    torch.cuda.synchronize()
+    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    lm_bytes = V * H * (2 if w.dtype == "bf16" else 4) + B * k * H * (2 if w.dtype == "bf16" else 4) \
+        + B * k * V * 4
+    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(w.name)
+    log(f"step {ms_step * 1e3:.1f} us; LM head {lm_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one block-step ...")
+        cpu = cpu_baseline(w, W, host0)
+        log(f"cpu oracle: {1.0 / cpu['value']:.1f} s per block-step")
+
+    out = {
+        "metric": "draft+verify block-steps/sec per GPU; HBM GB/s and % roofline",
+        "value": 1000.0 / ms_step,
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "batch": B, "k": k, "hidden": H, "vocab": V,
+                   "rank": w.rank, "n_taps": w.n_taps,
+                   "launch": "hip-graph" if graphs is not None else "eager",
+                   "pool_steps": args.pool},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "ws_gemm_kernel (LM head)", "avg_launch_us": lm_ms * 1e3,
+                     "algorithmic_bytes_per_launch": lm_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+"""Python binding of libbdr: the block-draft readout hot path on MI355X (gfx950).
+
+Each function marshals torch device tensors into the C ABI of ``include/bdr.h``
+(``data_ptr()`` and the current HIP stream) and raises ``BdrError`` on a non-zero
+return.  Every step of the path runs in the HIP kernels of libbdr; there is no
+other implementation behind these names.  Output tensors and workspaces that are
+not supplied are allocated with torch on the input's device.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _abi
+from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
+
+__all__ = [
+    "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
+    "spec_verify_greedy", "workspace_bytes", "lib", "BdrError",
+]
+
+
+def lib():
+    """The loaded libbdr (raises ImportError when it has not been built)."""
+    return _abi.load()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BDR_BF16
+    if t.dtype == torch.float32:
+        return BDR_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _ws_ptr(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    p = ws.data_ptr()
+    al = (p + 255) & ~255
+    return C.c_void_p(al), ws.numel() * ws.element_size() - (al - p)
+
+
+def workspace_bytes(kind: str, **kw) -> int:
+    """Workspace size the library needs for ``kind`` in {fc, markov, draft, verify}."""
+    L = lib()
+    if kind == "fc":
+        return L.dflash_fuse_fc_workspace_bytes(kw["rows"], kw["hidden"], kw["n_taps"], kw["dtype"])
+    if kind == "markov":
+        return L.dspark_markov_workspace_bytes(kw["batch"], kw["k"])
+    if kind == "draft":
+        return L.dspark_draft_workspace_bytes(kw["batch"], kw["k"], kw["vocab"],
+                                              int(kw.get("logits_in_workspace", True)))
+    if kind == "verify":
+        return L.spec_verify_workspace_bytes(kw["batch"], kw["k"], kw["vocab"])
+    raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------- S1
+def dflash_fuse_fc(taps: Sequence[torch.Tensor], fc_w: torch.Tensor,
+                   out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[rows, H] = concat(taps) @ fc_w^T  (taps: T tensors [rows, H]; fc_w [H, T*H])."""
+    L = lib()
+    T = len(taps)
+    rows, H = taps[0].shape
+    for i, t in enumerate(taps):
+        _dev(t, f"taps[{i}]")
+        if t.shape != (rows, H) or t.dtype != fc_w.dtype:
+            raise ValueError("taps must all be [rows, H] with fc_w's dtype")
+    _dev(fc_w, "fc_w")
+    if tuple(fc_w.shape) != (H, T * H):
+        raise ValueError(f"fc_w must be [{H}, {T * H}]")
+    dt = _dt(fc_w)
+    if out is None:
+        out = torch.empty((rows, H), dtype=fc_w.dtype, device=fc_w.device)
+    _dev(out, "out")
+    need = L.dflash_fuse_fc_workspace_bytes(rows, H, T, dt)
+    ws = _workspace(need, fc_w.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    _abi.check("dflash_fuse_fc", L.dflash_fuse_fc(arr, T, rows, H, dt, _ptr(fc_w), _ptr(out), wp,
+                                                  wn, _stream(fc_w.device)))
+    return out
+
+
+# ----------------------------------------------------------------------------- S2
+def dspark_lm_head(hidden: torch.Tensor, lm_head_w: torch.Tensor,
+                   logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 logits [..., V] = hidden[..., H] @ lm_head_w[V, H]^T."""
+    L = lib()
+    _dev(hidden, "hidden")
+    _dev(lm_head_w, "lm_head_w")
+    V, H = lm_head_w.shape
+    if hidden.shape[-1] != H or hidden.dtype != lm_head_w.dtype:
+        raise ValueError("hidden must be [..., H] with lm_head_w's dtype")
+    rows = hidden.numel() // H
+    if logits is None:
+        logits = torch.empty((*hidden.shape[:-1], V), dtype=torch.float32, device=hidden.device)
+    _dev(logits, "logits")
+    _abi.check("dspark_lm_head", L.dspark_lm_head(_ptr(hidden), rows, H, V, _dt(lm_head_w),
+                                                  _ptr(lm_head_w), _ptr(logits),
+                                                  _stream(hidden.device)))
+    return logits
+
+
+# ----------------------------------------------------------------------------- S3
+def _markov_args(w1, w2, dt_ref):
+    if w1 is None and w2 is None:
+        return None, None, 0
+    _dev(w1, "markov_w1")
+    _dev(w2, "markov_w2")
+    if w1.shape != w2.shape or w1.dtype != w2.dtype:
+        raise ValueError("markov_w1 and markov_w2 must both be [V, r] of one dtype")
+    return w1, w2, int(w1.shape[1])
+
+
+def dspark_markov_argmax(logits: torch.Tensor, markov_w1: Optional[torch.Tensor],
+                         markov_w2: Optional[torch.Tensor], prev_token: torch.Tensor,
+                         draft_tokens: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Draft tokens [B, k] (int32) from fp32 logits [B, k, V] and the Markov head."""
+    L = lib()
+    _dev(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 3:
+        raise ValueError("logits must be fp32 [B, k, V]")
+    B, k, V = logits.shape
+    w1, w2, r = _markov_args(markov_w1, markov_w2, logits)
+    wdt = _dt(w1) if w1 is not None else BDR_F32
+    _dev(prev_token, "prev_token")
+    if prev_token.dtype != torch.int32 or prev_token.numel() != B:
+        raise ValueError("prev_token must be int32 [B]")
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, k), dtype=torch.int32, device=logits.device)
+    _dev(draft_tokens, "draft_tokens")
+    ws = _workspace(L.dspark_markov_workspace_bytes(B, k), logits.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    _abi.check("dspark_markov_argmax",
+               L.dspark_markov_argmax(_ptr(logits), B, k, V, wdt, _ptr(w1), _ptr(w2), r,
+                                      _ptr(prev_token), _ptr(draft_tokens), wp, wn,
+                                      _stream(logits.device)))
+    return draft_tokens
+
+
+# ----------------------------------------------------------------------------- S2+S3
+def dspark_draft_block(draft_hidden: torch.Tensor, lm_head_w: torch.Tensor,
+                       markov_w1: Optional[torch.Tensor], markov_w2: Optional[torch.Tensor],
+                       prev_token: torch.Tensor, draft_tokens: Optional[torch.Tensor] = None,
+                       logits_out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Draft one block: LM head over draft_hidden [B, k, H], then the Markov argmax chain."""
+    L = lib()
+    _dev(draft_hidden, "draft_hidden")
+    _dev(lm_head_w, "lm_head_w")
+    B, k, H = draft_hidden.shape
+    V = lm_head_w.shape[0]
+    if lm_head_w.shape[1] != H or draft_hidden.dtype != lm_head_w.dtype:
+        raise ValueError("lm_head_w must be [V, H] with draft_hidden's dtype")
+    w1, w2, r = _markov_args(markov_w1, markov_w2, lm_head_w)
+    if w1 is not None and w1.dtype != lm_head_w.dtype:
+        raise ValueError("Markov weights must share the LM head's dtype")
+    _dev(prev_token, "prev_token")
+    if prev_token.dtype != torch.int32 or prev_token.numel() != B:
+        raise ValueError("prev_token must be int32 [B]")
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, k), dtype=torch.int32, device=draft_hidden.device)
+    _dev(draft_tokens, "draft_tokens")
+    if logits_out is not None:
+        _dev(logits_out, "logits_out")
+    need = L.dspark_draft_workspace_bytes(B, k, V, int(logits_out is None))
+    ws = _workspace(need, draft_hidden.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    _abi.check("dspark_draft_block",
+               L.dspark_draft_block(_ptr(draft_hidden), B, k, H, V, _dt(lm_head_w),
+                                    _ptr(lm_head_w), _ptr(w1), _ptr(w2), r, _ptr(prev_token),
+                                    _ptr(draft_tokens), _ptr(logits_out), wp, wn,
+                                    _stream(draft_hidden.device)))
+    return draft_tokens
+
+
+# ----------------------------------------------------------------------------- S4
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                       confidence: Optional[torch.Tensor] = None,
+                       threshold: float = math.nan,
+                       accept_counts: Optional[torch.Tensor] = None,
+                       proposed_counts: Optional[torch.Tensor] = None,
+                       target_argmax: bool = True,
+                       out: Optional[Dict[str, torch.Tensor]] = None,
+                       workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Greedy verification of draft_tokens [B, k] against target_logits [B, k+1, V].
+
+    Returns block_len, accepted, bonus ([B] int32) and, if requested,
+    target_argmax ([B, k+1] int32, -1 past the block).  accept_counts /
+    proposed_counts ([k] int64) are accumulated in place when given.
+    """
+    L = lib()
+    _dev(target_logits, "target_logits")
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _dev(draft_tokens, "draft_tokens")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, k):
+        raise ValueError("draft_tokens must be int32 [B, k]")
+    if confidence is not None:
+        _dev(confidence, "confidence")
+        if confidence.dtype != torch.float32 or tuple(confidence.shape) != (B, k):
+            raise ValueError("confidence must be fp32 [B, k]")
+    for name, t in (("accept_counts", accept_counts), ("proposed_counts", proposed_counts)):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.int64 or t.numel() != k:
+                raise ValueError(f"{name} must be int64 [k]")
+    dev = target_logits.device
+    res = dict(out) if out is not None else {}
+    for name in ("block_len", "accepted", "bonus"):
+        if name not in res:
+            res[name] = torch.empty(B, dtype=torch.int32, device=dev)
+    if target_argmax and "target_argmax" not in res:
+        res["target_argmax"] = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    ws = _workspace(L.spec_verify_workspace_bytes(B, k, V), dev, workspace)
+    wp, wn = _ws_ptr(ws)
+    _abi.check("spec_verify_greedy",
+               L.spec_verify_greedy(_ptr(target_logits), _dt(target_logits), B, k, V,
+                                    _ptr(draft_tokens), _ptr(confidence), float(threshold),
+                                    _ptr(res["block_len"]), _ptr(res["accepted"]),
+                                    _ptr(res["bonus"]), _ptr(res.get("target_argmax")),
+                                    _ptr(accept_counts), _ptr(proposed_counts), wp, wn,
+                                    _stream(dev)))
+    return res

@@ -1,0 +1,293 @@
+// C ABI of libbdr: argument validation, workspace sizing and dispatch to the
+// gfx950 kernel launchers.  Every host-checkable argument is validated before
+// anything is enqueued; the device architecture is checked once per device.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "bdr_internal.h"
+
+using namespace bdr;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(BDR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool valid_dtype(int dt) { return dt == BDR_F32 || dt == BDR_BF16; }
+
+constexpr int64_t kMaxVocab = 0x7FFFFFFELL;
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor; keeps index math in range
+
+// 0 unknown, 1 gfx950, 2 other
+int g_dev_state[256];
+std::mutex g_dev_mu;
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 256) return fail(BDR_EUNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (g_dev_state[dev] == 2)
+      return fail(BDR_EUNSUPPORTED, "device %d is %s; libbdr is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (g_dev_state[dev] != 1)
+    return fail(BDR_EUNSUPPORTED, "device %d is not gfx950; libbdr is built for gfx950 only", dev);
+  return BDR_OK;
+}
+
+int need_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(BDR_EINVAL, "%s must not be NULL", name);
+  if (!aligned(p, align)) return fail(BDR_EINVAL, "%s must be %zu-byte aligned", name, align);
+  return BDR_OK;
+}
+
+int need_ws(const void* ws, size_t have, size_t need) {
+  if (need == 0) return BDR_OK;
+  if (!ws) return fail(BDR_EWORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(ws, 256)) return fail(BDR_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(BDR_EWORKSPACE, "workspace of %zu bytes required, got %zu", need, have);
+  return BDR_OK;
+}
+
+#define BDR_TRY(x)               \
+  do {                           \
+    const int rc_ = (x);         \
+    if (rc_ != BDR_OK) return rc_; \
+  } while (0)
+
+int fc_shape(int64_t rows, int64_t hidden, int n_taps, int dt) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  if (n_taps < 1) return fail(BDR_EINVAL, "n_taps must be >= 1, got %d", n_taps);
+  if (n_taps > BDR_MAX_TAPS) return fail(BDR_EUNSUPPORTED, "n_taps %d > %d", n_taps, BDR_MAX_TAPS);
+  if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
+  if (hidden <= 0) return fail(BDR_EINVAL, "hidden must be > 0");
+  const int ks = dt == BDR_BF16 ? 32 : 16;
+  if (hidden % ks)
+    return fail(BDR_EUNSUPPORTED, "hidden %lld must be a multiple of %d for this dtype",
+                static_cast<long long>(hidden), ks);
+  if (hidden * n_taps > kMaxElems / std::max<int64_t>(hidden, 1) ||
+      rows > kMaxElems / (hidden * n_taps))
+    return fail(BDR_EUNSUPPORTED, "fc problem too large");
+  return BDR_OK;
+}
+
+int lm_shape(int64_t rows, int64_t hidden, int64_t vocab, int dt) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
+  if (hidden <= 0) return fail(BDR_EINVAL, "hidden must be > 0");
+  if (vocab <= 0) return fail(BDR_EINVAL, "vocab must be > 0");
+  if (vocab > kMaxVocab) return fail(BDR_EUNSUPPORTED, "vocab must be < 2^31 - 1");
+  const int e = dt == BDR_BF16 ? 8 : 4;
+  if (hidden % e)
+    return fail(BDR_EUNSUPPORTED, "hidden %lld must be a multiple of %d for this dtype",
+                static_cast<long long>(hidden), e);
+  if (vocab > kMaxElems / hidden || rows > kMaxElems / std::max(hidden, vocab))
+    return fail(BDR_EUNSUPPORTED, "LM-head problem too large");
+  return BDR_OK;
+}
+
+int block_shape(int64_t batch, int k, int64_t vocab) {
+  if (batch < 0) return fail(BDR_EINVAL, "batch must be >= 0");
+  if (k < 1) return fail(BDR_EINVAL, "k must be >= 1, got %d", k);
+  if (k > BDR_MAX_K) return fail(BDR_EUNSUPPORTED, "k %d > %d", k, BDR_MAX_K);
+  if (vocab <= 0) return fail(BDR_EINVAL, "vocab must be > 0");
+  if (vocab > kMaxVocab) return fail(BDR_EUNSUPPORTED, "vocab must be < 2^31 - 1");
+  if (batch > 0x7FFFFFFFLL / (k + 1)) return fail(BDR_EUNSUPPORTED, "batch too large");
+  if (batch * (k + 1) > kMaxElems / vocab) return fail(BDR_EUNSUPPORTED, "block too large");
+  return BDR_OK;
+}
+
+int markov_shape(int dt, const void* w1, const void* w2, int rank) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  if (rank < 0) return fail(BDR_EINVAL, "rank must be >= 0");
+  if (rank > BDR_MAX_RANK) return fail(BDR_EUNSUPPORTED, "rank %d > %d", rank, BDR_MAX_RANK);
+  if ((w1 == nullptr) != (w2 == nullptr))
+    return fail(BDR_EINVAL, "markov_w1 and markov_w2 must both be given or both be NULL");
+  if (w1 && rank > 0) {
+    const int e = dt == BDR_BF16 ? 8 : 4;
+    if (rank % e) return fail(BDR_EUNSUPPORTED, "rank %d must be a multiple of %d for this dtype", rank, e);
+    BDR_TRY(need_ptr(w1, "markov_w1"));
+    BDR_TRY(need_ptr(w2, "markov_w2"));
+  }
+  return BDR_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int bdr_abi_version(void) { return 1; }
+
+const char* bdr_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------- S1
+size_t dflash_fuse_fc_workspace_bytes(int64_t rows, int64_t hidden, int n_taps, bdr_dtype dt) {
+  if (fc_shape(rows, hidden, n_taps, dt) != BDR_OK || rows == 0) return 0;
+  return plan_gemm(rows, hidden, hidden * n_taps, dt, true).workspace;
+}
+
+int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                   bdr_dtype dt, const void* fc_w, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  BDR_TRY(fc_shape(rows, hidden, n_taps, dt));
+  if (rows == 0) return BDR_OK;
+  if (!taps) return fail(BDR_EINVAL, "taps must not be NULL");
+  for (int t = 0; t < n_taps; ++t) {
+    if (!taps[t]) return fail(BDR_EINVAL, "taps[%d] must not be NULL", t);
+    if (!aligned(taps[t], 16)) return fail(BDR_EINVAL, "taps[%d] must be 16-byte aligned", t);
+  }
+  BDR_TRY(need_ptr(fc_w, "fc_w"));
+  BDR_TRY(need_ptr(out, "out"));
+  const GemmPlan p = plan_gemm(rows, hidden, hidden * n_taps, dt, true);
+  BDR_TRY(need_ws(workspace, workspace_bytes, p.workspace));
+  BDR_TRY(check_device());
+  hipError_t e = launch_gemm(p, dt, taps, n_taps, hidden, rows, hidden, fc_w, out,
+                             dt == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S2
+int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size, int64_t vocab,
+                   bdr_dtype dt, const void* lm_head_w, float* logits, void* stream) {
+  BDR_TRY(lm_shape(rows, hidden_size, vocab, dt));
+  if (rows == 0) return BDR_OK;
+  BDR_TRY(need_ptr(hidden, "hidden"));
+  BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));
+  BDR_TRY(need_ptr(logits, "logits"));
+  BDR_TRY(check_device());
+  const GemmPlan p = plan_gemm(rows, vocab, hidden_size, dt, false);
+  const void* a[1] = {hidden};
+  hipError_t e = launch_gemm(p, dt, a, 1, hidden_size, rows, vocab, lm_head_w, logits, OUT_F32,
+                             nullptr, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_lm_head launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S3
+size_t dspark_markov_workspace_bytes(int64_t batch, int k) {
+  if (batch < 0 || k < 1 || k > BDR_MAX_K) return 0;
+  return markov_workspace(batch, k);
+}
+
+int dspark_markov_argmax(const float* logits, int64_t batch, int k, int64_t vocab,
+                         bdr_dtype wdt, const void* markov_w1, const void* markov_w2, int rank,
+                         const int32_t* prev_token, int32_t* draft_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  BDR_TRY(block_shape(batch, k, vocab));
+  BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank));
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(logits, "logits"));
+  BDR_TRY(need_ptr(prev_token, "prev_token", 4));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  BDR_TRY(need_ws(workspace, workspace_bytes, markov_workspace(batch, k)));
+  BDR_TRY(check_device());
+  hipError_t e = launch_markov(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
+                               prev_token, draft_tokens, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_markov_argmax launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S2+S3
+size_t dspark_draft_workspace_bytes(int64_t batch, int k, int64_t vocab, int logits_in_workspace) {
+  if (batch < 0 || k < 1 || k > BDR_MAX_K || vocab <= 0 || vocab > kMaxVocab) return 0;
+  size_t n = markov_workspace(batch, k);
+  if (logits_in_workspace) n += align256(static_cast<size_t>(batch) * k * vocab * 4);
+  return n;
+}
+
+int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t hidden,
+                       int64_t vocab, bdr_dtype dt, const void* lm_head_w, const void* markov_w1,
+                       const void* markov_w2, int rank, const int32_t* prev_token,
+                       int32_t* draft_tokens, float* logits_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  BDR_TRY(block_shape(batch, k, vocab));
+  BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
+  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank));
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(draft_hidden, "draft_hidden"));
+  BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));
+  BDR_TRY(need_ptr(prev_token, "prev_token", 4));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  if (logits_out) BDR_TRY(need_ptr(logits_out, "logits_out"));
+  const size_t need = dspark_draft_workspace_bytes(batch, k, vocab, logits_out == nullptr);
+  BDR_TRY(need_ws(workspace, workspace_bytes, need));
+  BDR_TRY(check_device());
+  char* ws = static_cast<char*>(workspace);
+  float* logits = logits_out;
+  if (!logits) {
+    logits = reinterpret_cast<float*>(ws);
+    ws += align256(static_cast<size_t>(batch) * k * vocab * 4);
+  }
+  const GemmPlan p = plan_gemm(batch * k, vocab, hidden, dt, false);
+  const void* a[1] = {draft_hidden};
+  hipError_t e = launch_gemm(p, dt, a, 1, hidden, batch * k, vocab, lm_head_w, logits, OUT_F32,
+                             nullptr, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_draft_block LM-head launch");
+  e = launch_markov(logits, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
+                    draft_tokens, ws, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_draft_block Markov launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S4
+size_t spec_verify_workspace_bytes(int64_t batch, int k, int64_t vocab) {
+  if (batch < 0 || k < 1 || k > BDR_MAX_K || vocab <= 0 || vocab > kMaxVocab) return 0;
+  return verify_workspace(batch, k, vocab);
+}
+
+int spec_verify_greedy(const void* target_logits, bdr_dtype dt, int64_t batch, int k,
+                       int64_t vocab, const int32_t* draft_tokens, const float* confidence,
+                       float threshold, int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                       int32_t* target_argmax, int64_t* accept_counts, int64_t* proposed_counts,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  BDR_TRY(block_shape(batch, k, vocab));
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(target_logits, "target_logits"));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  if (confidence) BDR_TRY(need_ptr(confidence, "confidence", 4));
+  BDR_TRY(need_ptr(block_len, "block_len", 4));
+  BDR_TRY(need_ptr(accepted, "accepted", 4));
+  BDR_TRY(need_ptr(bonus, "bonus", 4));
+  if (target_argmax) BDR_TRY(need_ptr(target_argmax, "target_argmax", 4));
+  if (accept_counts) BDR_TRY(need_ptr(accept_counts, "accept_counts", 8));
+  if (proposed_counts) BDR_TRY(need_ptr(proposed_counts, "proposed_counts", 8));
+  BDR_TRY(need_ws(workspace, workspace_bytes, verify_workspace(batch, k, vocab)));
+  BDR_TRY(check_device());
+  hipError_t e = launch_verify(target_logits, dt, batch, k, vocab, draft_tokens, confidence,
+                               threshold, block_len, accepted, bonus, target_argmax,
+                               accept_counts, proposed_counts, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_greedy launch");
+  return BDR_OK;
+}
+
+}  // extern "C"

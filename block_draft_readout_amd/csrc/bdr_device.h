@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels of libbdr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bdr {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Storage element traits.  Every lane moves 16 bytes per load; KSTEP is the
+// reduction depth one 16-byte load per lane covers across the four 16-lane
+// groups of a wave (the K extent of the MFMA work issued for it).
+template <typename S> struct Elem;
+template <> struct Elem<uint16_t> {  // bfloat16 bit patterns
+  static constexpr int PER16 = 8;
+  static constexpr int KSTEP = 32;
+};
+template <> struct Elem<float> {
+  static constexpr int PER16 = 4;
+  static constexpr int KSTEP = 16;
+};
+
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// D(16x16, fp32) += A(16 x KSTEP) * B(KSTEP x 16) for one 16-byte operand chunk
+// per lane.  Lane l supplies row/column (l & 15) and reduction group (l >> 4) of
+// both operands with the same element order, so the reduction index is paired
+// identically on both sides whatever the hardware's slot order within a group.
+__device__ __forceinline__ f32x4_t mma16(u32x4_t a, u32x4_t b, f32x4_t c, uint16_t) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(u32x4_t a, u32x4_t b, f32x4_t c, float) {
+  // four K=4 fp32 MFMAs; element e of lane group g is reduction index 4g + e
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bfloat16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename S> __device__ __forceinline__ float to_f32(S x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+
+// ---------------------------------------------------------------------------
+// Argmax keys.  A (value, index) pair packs into a uint64 whose unsigned order
+// is: larger value first, then lower index.  -0.0 is folded into +0.0 so the
+// two tie.  Key 0 is below every real key and serves as "empty".
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long pack_key(float v, uint32_t idx) {
+  return (static_cast<unsigned long long>(ordered_bits(v)) << 32) |
+         static_cast<unsigned long long>(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ int32_t key_index(unsigned long long key) {
+  return static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+// max over the 16 lanes of a row group (lanes with equal l >> 4)
+__device__ __forceinline__ unsigned long long rowgroup_max16(unsigned long long k) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) k = umax64(k, __shfl_xor(k, off, 64));
+  return k;
+}
+
+// max over a whole 64-lane wave
+__device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) k = umax64(k, __shfl_xor(k, off, 64));
+  return k;
+}
+
+}  // namespace bdr

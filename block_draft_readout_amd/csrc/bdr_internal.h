@@ -1,0 +1,57 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/bdr.h"
+
+namespace bdr {
+
+// ----------------------------------------------------------------------------
+// Weight-streaming GEMM: C[M, N] = A[M, K] * W[N, K]^T with fp32 accumulation.
+// A is given as n_seg row-major segments [M, seg] laid side by side along K
+// (the fc's tap concatenation; one segment for the LM head).
+// ----------------------------------------------------------------------------
+struct GemmPlan {
+  int mt = 1;             // 16-row tiles per workgroup (1..9)
+  int m_groups = 1;       // workgroups along M
+  int jn = 4;             // 16-column tiles per wave
+  int wk = 4;             // waves of a workgroup splitting K (WN = 4 / wk along N)
+  int64_t n_wg = 1;       // workgroups along N
+  int ksplit = 1;         // workgroups along K (partials reduced by a second kernel)
+  int64_t steps_per_split = 0;
+  size_t workspace = 0;   // bytes of split-K partials
+};
+
+enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
+
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split);
+
+hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
+                       int64_t seg, int64_t M, int64_t N, const void* w, void* out,
+                       OutKind out_kind, void* workspace, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Markov bias + semi-autoregressive argmax over k positions.
+// ----------------------------------------------------------------------------
+size_t markov_workspace(int64_t B, int k);
+hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
+                         const void* w1, const void* w2, int rank, const int32_t* prev,
+                         int32_t* draft, void* workspace, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Greedy verification.
+// ----------------------------------------------------------------------------
+int verify_chunks(int64_t B, int k, int64_t V);
+size_t verify_workspace(int64_t B, int k, int64_t V);
+hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
+                         const int32_t* draft, const float* conf, float threshold,
+                         int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                         int32_t* target_argmax, int64_t* acc, int64_t* prop,
+                         void* workspace, hipStream_t stream);
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace bdr

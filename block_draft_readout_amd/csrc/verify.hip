@@ -1,0 +1,208 @@
+// Greedy exact-match verification of a draft block (gfx950).
+//
+// Two launches:
+//   1. verify_argmax_kernel -- grid (row b*(k+1)+j, vocab chunk).  A workgroup
+//      whose position lies beyond the row's (confidence-truncated) block exits
+//      at once, so only the ragged truncated blocks are read.  The others
+//      stream their chunk of target logits with 16-byte loads, keep a running
+//      (value, index) maximum per lane, and write one packed uint64 key per
+//      (row, chunk): no atomics, no pre-zeroed memory.
+//   2. verify_scan_kernel -- one workgroup: per row, fold the chunk keys into
+//      the target argmax of each verified position, take the longest draft
+//      prefix that matches, emit the bonus token, and add the per-position
+//      accepted / proposed counts (LDS histogram, then one int64 += per
+//      position).
+// Greedy verification emits exactly the target's own greedy tokens (llm-scaler
+// PR #620, "Summary / Quality"); the block length follows the proposer's
+// truncation by confidence (same page, DSpark port notes, dflash.py); the
+// counters are the spec-decode per-position acceptance accounting
+// (vllm-backport PR #128, "Acceptance detail").
+
+#include <algorithm>
+#include <cmath>
+
+#include "bdr_device.h"
+#include "bdr_internal.h"
+
+namespace bdr {
+
+struct VerifyArgs {
+  const void* Y;                 // [B, k+1, V]
+  int64_t B, V;
+  int k;
+  const int32_t* draft;          // [B, k]
+  const float* conf;             // [B, k] or null
+  float th;
+  int use_conf;
+  int chunks;
+  int64_t chunk_len;             // multiple of 8 elements
+  unsigned long long* part;      // [B*(k+1), chunks]
+  int32_t* block_len;
+  int32_t* accepted;
+  int32_t* bonus;
+  int32_t* targ;                 // [B, k+1] or null
+  int64_t* acc;                  // [k] or null
+  int64_t* prop;                 // [k] or null
+};
+
+// L_b: first position whose confidence is strictly below the threshold, else k.
+__device__ __forceinline__ int block_length(const VerifyArgs& g, int64_t b) {
+  if (!g.use_conf) return g.k;
+  for (int i = 0; i < g.k; ++i)
+    if (g.conf[b * g.k + i] < g.th) return i;
+  return g.k;
+}
+
+template <typename S, bool VEC>
+__global__ __launch_bounds__(256) void verify_argmax_kernel(const VerifyArgs g) {
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / (g.k + 1);
+  const int j = static_cast<int>(row - b * (g.k + 1));
+  if (j > block_length(g, b)) return;  // same decision for the whole workgroup
+
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.chunk_len;
+  const int64_t c1 = std::min<int64_t>(g.V, c0 + g.chunk_len);
+  const S* y = static_cast<const S*>(g.Y) + row * g.V;
+  float bv = -INFINITY;
+  uint32_t bi = 0xFFFFFFFFu;
+  if constexpr (VEC) {
+    constexpr int E = Elem<S>::PER16;
+    for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * E; v < c1; v += 256 * E) {
+      const u32x4_t q = load16_stream(y + v);
+      const S* e = reinterpret_cast<const S*>(&q);
+#pragma unroll
+      for (int t = 0; t < E; ++t) {
+        const float f = to_f32<S>(e[t]);
+        if (f > bv) {
+          bv = f;
+          bi = static_cast<uint32_t>(v + t);
+        }
+      }
+    }
+  } else {
+    for (int64_t v = c0 + threadIdx.x; v < c1; v += 256) {
+      const float f = to_f32<S>(y[v]);
+      if (f > bv) {
+        bv = f;
+        bi = static_cast<uint32_t>(v);
+      }
+    }
+  }
+  unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+  key = wave_max64(key);
+  __shared__ unsigned long long sk[4];
+  if ((threadIdx.x & 63) == 0) sk[threadIdx.x >> 6] = key;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    g.part[row * g.chunks + blockIdx.y] = umax64(umax64(sk[0], sk[1]), umax64(sk[2], sk[3]));
+}
+
+__global__ __launch_bounds__(256) void verify_scan_kernel(const VerifyArgs g) {
+  __shared__ int cacc[BDR_MAX_K];
+  __shared__ int cprop[BDR_MAX_K];
+  if (threadIdx.x < BDR_MAX_K) {
+    cacc[threadIdx.x] = 0;
+    cprop[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  for (int64_t b = threadIdx.x; b < g.B; b += 256) {
+    const int L = block_length(g, b);
+    int a = 0;
+    int32_t bonus = -1;
+    bool done = false;
+    for (int j = 0; j <= g.k; ++j) {
+      int32_t t = -1;
+      if (j <= L) {
+        const unsigned long long* pp = g.part + (b * (g.k + 1) + j) * g.chunks;
+        unsigned long long key = 0ull;
+        for (int c = 0; c < g.chunks; ++c) key = umax64(key, pp[c]);
+        t = key_index(key);
+        if (!done) {
+          if (j < L && g.draft[b * g.k + j] == t) {
+            ++a;
+          } else {
+            bonus = t;
+            done = true;
+          }
+        }
+      }
+      if (g.targ) g.targ[b * (g.k + 1) + j] = t;
+    }
+    g.block_len[b] = L;
+    g.accepted[b] = a;
+    g.bonus[b] = bonus;
+    for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
+    for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < g.k) {
+    if (g.acc) g.acc[threadIdx.x] += cacc[threadIdx.x];
+    if (g.prop) g.prop[threadIdx.x] += cprop[threadIdx.x];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+static void chunk_plan(int64_t B, int k, int64_t V, int* chunks, int64_t* len) {
+  const int64_t rows = std::max<int64_t>(1, B * (k + 1));
+  int64_t c = std::max<int64_t>(1, (2048 + rows - 1) / rows);
+  c = std::min<int64_t>(c, std::max<int64_t>(1, (V + 2047) / 2048));
+  c = std::min<int64_t>(c, 256);
+  int64_t l = (V + c - 1) / c;
+  l = (l + 7) / 8 * 8;
+  *len = l;
+  *chunks = static_cast<int>((V + l - 1) / l);
+}
+
+int verify_chunks(int64_t B, int k, int64_t V) {
+  int c;
+  int64_t l;
+  chunk_plan(B, k, V, &c, &l);
+  return c;
+}
+
+size_t verify_workspace(int64_t B, int k, int64_t V) {
+  return align256(static_cast<size_t>(B) * (k + 1) * verify_chunks(B, k, V) * 8);
+}
+
+hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
+                         const int32_t* draft, const float* conf, float threshold,
+                         int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                         int32_t* target_argmax, int64_t* acc, int64_t* prop,
+                         void* workspace, hipStream_t stream) {
+  VerifyArgs g{};
+  g.Y = Y;
+  g.B = B;
+  g.V = V;
+  g.k = k;
+  g.draft = draft;
+  g.conf = conf;
+  g.th = threshold;
+  g.use_conf = (conf != nullptr && !std::isnan(threshold)) ? 1 : 0;
+  chunk_plan(B, k, V, &g.chunks, &g.chunk_len);
+  g.part = static_cast<unsigned long long*>(workspace);
+  g.block_len = block_len;
+  g.accepted = accepted;
+  g.bonus = bonus;
+  g.targ = target_argmax;
+  g.acc = acc;
+  g.prop = prop;
+  const dim3 grid(static_cast<unsigned>(B * (k + 1)), static_cast<unsigned>(g.chunks));
+  if (dt == BDR_BF16) {
+    if (V % 8 == 0)
+      hipLaunchKernelGGL((verify_argmax_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((verify_argmax_kernel<uint16_t, false>), grid, dim3(256), 0, stream, g);
+  } else {
+    if (V % 4 == 0)
+      hipLaunchKernelGGL((verify_argmax_kernel<float, true>), grid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((verify_argmax_kernel<float, false>), grid, dim3(256), 0, stream, g);
+  }
+  hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace bdr

@@ -1,0 +1,200 @@
+/*
+ * bdr.h -- C ABI of the block-draft readout hot path (DFlash feature fusion,
+ * LM head, DSpark Markov-biased semi-autoregressive argmax, greedy
+ * verification) for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [recipe] "docs(vllm): Qwen3.8-27B DFlash drafter recipe" (intel/llm-scaler
+ *            PR #620), DSpark port notes and "Summary / Quality".
+ *   [card]   "Qwen3.8-27B-DSpark -- vLLM-ready" (Doopeworld model card).
+ *   [pr128]  "Qwen4Exp DFlash drafter support" (wtdcode/vllm-backport PR #128).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous memory owned
+ *     by the caller, 16-byte aligned; workspaces are 256-byte aligned.  The
+ *     library never allocates or frees device memory and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream); all work is
+ *     enqueued on it in order, so calls on one stream see each other's results.
+ *   - A call with no work (rows == 0 or batch == 0) returns BDR_OK after
+ *     checking its scalar arguments; its pointers may then be NULL.
+ *   - Every argument that can be checked on the host is checked BEFORE anything
+ *     is enqueued.  On a non-zero return nothing was launched and accumulating
+ *     outputs are untouched.  bdr_last_error() then describes the failure
+ *     (thread-local text).
+ *   - Values that live on the device (token ids, logits) are not checked: a
+ *     draft token outside [0, V) never matches, and a previous token outside
+ *     [0, V) contributes no Markov bias.  Floating inputs must be finite.
+ *   - Token ids are int32, counters int64.  dtype selects the storage of
+ *     weights and activations (BDR_BF16 or BDR_F32); accumulation is fp32.
+ *   - Entry points are reentrant; calls that share a workspace must be ordered
+ *     on one stream.
+ */
+#ifndef BDR_H
+#define BDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bdr_dtype { BDR_F32 = 0, BDR_BF16 = 1 } bdr_dtype;
+
+#define BDR_OK            0
+#define BDR_EINVAL       -1  /* null required pointer, bad size, misalignment     */
+#define BDR_EUNSUPPORTED -2  /* size beyond a documented limit, non-gfx950 device */
+#define BDR_EWORKSPACE   -3  /* workspace missing or smaller than required        */
+#define BDR_EHIP         -4  /* a HIP runtime call or kernel launch failed        */
+
+#define BDR_MAX_TAPS   8
+#define BDR_MAX_K      16
+#define BDR_MAX_RANK   128
+
+/* Version of this interface (incremented on any signature change). */
+int bdr_abi_version(void);
+
+/* Text describing the last non-zero return on the calling thread. */
+const char* bdr_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * S1  dflash_fuse_fc -- fuse the tapped target hidden states and apply the fc.
+ *
+ * out[m, o] = sum_t sum_h taps[t][m, h] * fc_w[o, t*H + h]
+ *
+ * The drafter reads the target's hidden states at its target layers and
+ * concatenates them feature-wise before one linear projection back to H
+ * ([pr128] "What was missing" item 1: five 2560-wide features, fc.weight
+ * [2560, 12800]; [card] "Target quantisation" / "Limitations": taps at layers
+ * 4/16/28/40/52, fc input 5 x 5120).  Tap t fills columns [t*H, (t+1)*H) in
+ * the order given.  No bias, norm or activation.
+ *
+ *   taps      HOST array of n_taps device pointers, each [rows, H] (dtype)
+ *   n_taps    1..BDR_MAX_TAPS
+ *   rows      >= 0 (0: no work); hidden H > 0 with H % 32 == 0 (bf16) or
+ *             H % 16 == 0 (f32)
+ *   fc_w      [H, n_taps*H] (out x in), dtype
+ *   out       [rows, H], dtype (bf16 output is rounded to nearest even from
+ *             the fp32 sum)
+ *   workspace split-K partial sums; size from dflash_fuse_fc_workspace_bytes
+ *             (may be NULL when that returns 0)
+ * ------------------------------------------------------------------------- */
+size_t dflash_fuse_fc_workspace_bytes(int64_t rows, int64_t hidden, int n_taps,
+                                      bdr_dtype dt);
+int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows,
+                   int64_t hidden, bdr_dtype dt, const void* fc_w, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * S2  dspark_lm_head -- full-vocabulary logits of the drafted positions.
+ *
+ * logits[m, v] = sum_h hidden[m, h] * lm_head_w[v, h]     (fp32 out)
+ *
+ * These are the logits the DSpark greedy sample biases and argmaxes ([recipe]
+ * DSpark port notes, dflash.py).  rows = B*k for a draft block.
+ *
+ *   hidden    [rows, H], dtype; rows >= 0; H > 0, H % 8 == 0 (bf16) or
+ *             H % 4 == 0 (f32)
+ *   lm_head_w [V, H], dtype; 0 < V < 2^31 - 1
+ *   logits    [rows, V] fp32
+ * ------------------------------------------------------------------------- */
+int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size,
+                   int64_t vocab, bdr_dtype dt, const void* lm_head_w,
+                   float* logits, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * S3  dspark_markov_argmax -- Markov bigram bias + semi-autoregressive argmax.
+ *
+ * For each row b: p = prev_token[b]; for i = 0..k-1:
+ *     bias[v]  = sum_j markov_w2[v, j] * markov_w1[p, j]        (fp32)
+ *     s[v]     = logits[b, i, v] + bias[v]                      (fp32)
+ *     d[b, i]  = min{ v : s[v] = max s }                        (lowest index)
+ *     p        = d[b, i]
+ *
+ * The Markov head embeds the previous token with markov_w1 and projects it to
+ * the vocabulary with markov_w2 ([recipe] DSpark port notes, qwen3_dflash.py:
+ * VanillaMarkov / compute_markov_bias); the proposer conditions position 0 on
+ * the accepted bonus token and each later position on the previous position's
+ * biased prediction ([recipe] DSpark port notes, dflash.py).
+ *
+ *   logits      [B, k, V] fp32 (finite)
+ *   batch B >= 0, 1 <= k <= BDR_MAX_K, 0 < V < 2^31 - 1
+ *   wdt         dtype of the Markov weights
+ *   markov_w1   [V, r] embedding, markov_w2 [V, r] projection; both NULL or
+ *               rank == 0 means no bias (plain argmax per position).
+ *               0 <= r <= BDR_MAX_RANK, r % 8 == 0 (bf16) or r % 4 == 0 (f32)
+ *   prev_token  [B] int32, the accepted bonus token of the previous step
+ *   draft_tokens[B, k] int32 out
+ *   workspace   >= dspark_markov_workspace_bytes(B, k)
+ * ------------------------------------------------------------------------- */
+size_t dspark_markov_workspace_bytes(int64_t batch, int k);
+int dspark_markov_argmax(const float* logits, int64_t batch, int k,
+                         int64_t vocab, bdr_dtype wdt, const void* markov_w1,
+                         const void* markov_w2, int rank,
+                         const int32_t* prev_token, int32_t* draft_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * S2+S3  dspark_draft_block -- draft one block: LM head, then the Markov
+ * semi-autoregressive argmax (exactly dspark_lm_head followed by
+ * dspark_markov_argmax on the same stream).
+ *
+ *   draft_hidden [B, k, H] dtype -- the drafter's hidden states of the block
+ *   lm_head_w    [V, H] dtype; markov_w1/markov_w2/rank as in S3 (dtype dt)
+ *   prev_token   [B] int32; draft_tokens [B, k] int32 out
+ *   logits_out   [B, k, V] fp32, optional: NULL keeps the logits in the
+ *                workspace
+ *   workspace    >= dspark_draft_workspace_bytes(B, k, V, logits_out == NULL)
+ * ------------------------------------------------------------------------- */
+size_t dspark_draft_workspace_bytes(int64_t batch, int k, int64_t vocab,
+                                    int logits_in_workspace);
+int dspark_draft_block(const void* draft_hidden, int64_t batch, int k,
+                       int64_t hidden, int64_t vocab, bdr_dtype dt,
+                       const void* lm_head_w, const void* markov_w1,
+                       const void* markov_w2, int rank,
+                       const int32_t* prev_token, int32_t* draft_tokens,
+                       float* logits_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * S4  spec_verify_greedy -- greedy exact-match verification of a draft block.
+ *
+ *   L_b   = min{ i < k : confidence[b, i] < threshold }, else k
+ *           (truncation only when confidence != NULL and threshold is not NaN;
+ *            L_b = 0 is allowed)
+ *   t[b,j]= min{ v : Y[b, j, v] = max_v Y[b, j, v] }  for j <= L_b
+ *   a_b   = longest prefix with d[b, j] == t[b, j] for all j < a_b <= L_b
+ *   bonus = t[b, a_b]   (always emitted)
+ *   accept_counts[i]   += #{ b : a_b > i },  proposed_counts[i] += #{ b : L_b > i }
+ *
+ * Greedy verification accepts the longest draft prefix that agrees with the
+ * target's own greedy tokens and emits the target's token after it, so the
+ * output equals target-only greedy decoding ([recipe] "Summary / Quality";
+ * [card] "Tuning notes").  The adaptive block length follows the proposer's
+ * truncation by confidence ([recipe] DSpark port notes, dflash.py).  The
+ * per-position counts are the spec-decode acceptance accounting ([pr128]
+ * "Acceptance detail").  Positions j > L_b are not read.
+ *
+ *   target_logits  [B, k+1, V] dtype (finite)
+ *   batch B >= 0, 1 <= k <= BDR_MAX_K, 0 < V < 2^31 - 1
+ *   draft_tokens   [B, k] int32
+ *   confidence     [B, k] fp32 or NULL
+ *   block_len, accepted, bonus   [B] int32 out
+ *   target_argmax  [B, k+1] int32 out, optional (-1 for j > L_b)
+ *   accept_counts, proposed_counts  [k] int64, ACCUMULATED (+=), optional
+ *   workspace      >= spec_verify_workspace_bytes(B, k, V)
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_workspace_bytes(int64_t batch, int k, int64_t vocab);
+int spec_verify_greedy(const void* target_logits, bdr_dtype dt, int64_t batch,
+                       int k, int64_t vocab, const int32_t* draft_tokens,
+                       const float* confidence, float threshold,
+                       int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                       int32_t* target_argmax, int64_t* accept_counts,
+                       int64_t* proposed_counts, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BDR_H */

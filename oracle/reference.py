@@ -253,13 +253,12 @@ def target_argmax(Y: np.ndarray, dtype: str, L: Optional[np.ndarray] = None) -> 
     choice (model card, "Tuning notes": greedy exact-match).  Positions beyond
     the (possibly truncated) block, j > L_b, are not verified and get -1.
     """
-    Yw = widen(Y, dtype)
-    B, k1, V = Yw.shape
+    B, k1, V = np.shape(Y)
     t = np.full((B, k1), -1, dtype=np.int64)
     for b in range(B):
         last = k1 - 1 if L is None else int(L[b])
         for j in range(last + 1):
-            t[b, j] = first_argmax(Yw[b, j])
+            t[b, j] = first_argmax(widen(Y[b, j], dtype))
     return t
 
 

@@ -1,0 +1,167 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports every
+symbol include/bdr.h declares, sizes workspaces, and rejects invalid arguments
+with the documented codes before touching the device (no compute calls here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bdr.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_draft_readout_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from block_draft_readout_amd import build
+        build.build()
+    return _abi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_header_declares_the_three_path_calls():
+    names = _declared()
+    for n in ("dflash_fuse_fc", "dspark_draft_block", "spec_verify_greedy"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_declares_every_header_symbol():
+    from block_draft_readout_amd import _abi
+    assert sorted(_abi.SIGNATURES) == _declared()
+
+
+def test_version(L):
+    assert L.bdr_abi_version() == 1
+
+
+def test_workspace_sizes(L):
+    from block_draft_readout_amd import _abi
+    assert L.dspark_markov_workspace_bytes(16, 8) == 1024
+    assert L.dspark_markov_workspace_bytes(1, 7) == 256
+    V = 151936
+    with_logits = L.dspark_draft_workspace_bytes(16, 8, V, 1)
+    assert with_logits == 1024 + 16 * 8 * V * 4
+    assert L.dspark_draft_workspace_bytes(16, 8, V, 0) == 1024
+    v = L.spec_verify_workspace_bytes(16, 8, V)
+    assert v > 0 and v % 256 == 0
+    # fc: split-K partials only when K is split
+    assert L.dflash_fuse_fc_workspace_bytes(8, 5120, 5, _abi.BDR_BF16) > 0
+    assert L.dflash_fuse_fc_workspace_bytes(0, 5120, 5, _abi.BDR_BF16) == 0
+    # invalid shapes size to 0
+    assert L.dflash_fuse_fc_workspace_bytes(8, 5120, 9, _abi.BDR_BF16) == 0
+    assert L.spec_verify_workspace_bytes(1, 17, V) == 0
+
+
+def _rc(L, fn, *args):
+    return getattr(L, fn)(*args)
+
+
+def test_fc_argument_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)  # never dereferenced: every call below fails validation first
+    taps = (C.c_void_p * 5)(*([4096] * 5))
+    assert L.dflash_fuse_fc(None, 5, 8, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 0, 8, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 9, 8, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EUNSUPPORTED
+    assert L.dflash_fuse_fc(taps, 5, -1, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 5, 8, 0, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, 7, P, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 5, 8, 5121, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EUNSUPPORTED
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, A.BDR_BF16, None, P, None, 0, None) == A.BDR_EINVAL
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, A.BDR_BF16, C.c_void_p(4098), P, None, 0, None) == A.BDR_EINVAL
+    bad = (C.c_void_p * 5)(4096, 4096, None, 4096, 4096)
+    assert L.dflash_fuse_fc(bad, 5, 8, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EINVAL
+    assert b"taps[2]" in L.bdr_last_error()
+    # split-K workspace required
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_EWORKSPACE
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, A.BDR_BF16, P, P, C.c_void_p(4096), 16, None) == A.BDR_EWORKSPACE
+    assert L.dflash_fuse_fc(taps, 5, 8, 5120, A.BDR_BF16, P, P, C.c_void_p(4096 + 16), 1 << 30, None) == A.BDR_EWORKSPACE
+    # rows == 0 is a no-op that succeeds without touching the device
+    assert L.dflash_fuse_fc(taps, 5, 0, 5120, A.BDR_BF16, P, P, None, 0, None) == A.BDR_OK
+
+
+def test_lm_head_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    assert L.dspark_lm_head(P, 7, 5120, 0, A.BDR_BF16, P, P, None) == A.BDR_EINVAL
+    assert L.dspark_lm_head(P, 7, 5120, 1 << 31, A.BDR_BF16, P, P, None) == A.BDR_EUNSUPPORTED
+    assert L.dspark_lm_head(P, 7, 5124, 1000, A.BDR_BF16, P, P, None) == A.BDR_EUNSUPPORTED
+    assert L.dspark_lm_head(None, 7, 5120, 1000, A.BDR_BF16, P, P, None) == A.BDR_EINVAL
+    assert L.dspark_lm_head(P, 0, 5120, 1000, A.BDR_BF16, P, P, None) == A.BDR_OK
+
+
+def test_markov_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    ws = C.c_void_p(4096)
+    args = lambda B=16, k=8, V=1000, dt=A.BDR_BF16, w1=P, w2=P, r=64, prev=P, d=P, wp=ws, wn=4096: \
+        L.dspark_markov_argmax(P, B, k, V, dt, w1, w2, r, prev, d, wp, wn, None)
+    assert args(k=0) == A.BDR_EINVAL
+    assert args(k=17) == A.BDR_EUNSUPPORTED
+    assert args(r=129) == A.BDR_EUNSUPPORTED
+    assert args(r=60) == A.BDR_EUNSUPPORTED          # not a multiple of 8 for bf16
+    assert args(r=-1) == A.BDR_EINVAL
+    assert args(w2=None) == A.BDR_EINVAL             # only one Markov matrix
+    assert args(prev=None) == A.BDR_EINVAL
+    assert args(B=-1) == A.BDR_EINVAL
+    assert args(wp=None) == A.BDR_EWORKSPACE
+    assert args(wn=8) == A.BDR_EWORKSPACE
+    assert args(B=0) == A.BDR_OK
+
+
+def test_draft_block_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    f = lambda **kw: L.dspark_draft_block(kw.get("h", P), kw.get("B", 16), kw.get("k", 8), 5120,
+                                          kw.get("V", 151936), A.BDR_BF16, kw.get("lm", P), P, P,
+                                          64, P, P, kw.get("lo", None), kw.get("ws", P),
+                                          kw.get("wn", 1024), None)
+    assert f(h=None) == A.BDR_EINVAL
+    assert f(lm=None) == A.BDR_EINVAL
+    assert f(k=20) == A.BDR_EUNSUPPORTED
+    assert f() == A.BDR_EWORKSPACE                   # logits need workspace when logits_out is NULL
+    assert f(B=0) == A.BDR_OK
+
+
+def test_verify_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    f = lambda **kw: L.spec_verify_greedy(kw.get("y", P), kw.get("dt", A.BDR_BF16), kw.get("B", 16),
+                                          kw.get("k", 8), kw.get("V", 151936), kw.get("d", P),
+                                          kw.get("c", None), 0.3, kw.get("bl", P), P, P, None,
+                                          kw.get("acc", None), None, kw.get("ws", None),
+                                          kw.get("wn", 0), None)
+    assert f(y=None) == A.BDR_EINVAL
+    assert f(dt=5) == A.BDR_EINVAL
+    assert f(d=None) == A.BDR_EINVAL
+    assert f(bl=None) == A.BDR_EINVAL
+    assert f(acc=C.c_void_p(4100)) == A.BDR_EINVAL   # int64 counters must be 8-byte aligned
+    assert f(k=0) == A.BDR_EINVAL
+    assert f(V=0) == A.BDR_EINVAL
+    assert f() == A.BDR_EWORKSPACE
+    assert f(B=0) == A.BDR_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from block_draft_readout_amd import _abi
+    saved = _abi._lib
+    try:
+        _abi._lib = None
+        with pytest.raises(ImportError):
+            _abi.load(str(tmp_path / "missing.so"))
+    finally:
+        _abi._lib = saved

@@ -1,0 +1,287 @@
+"""GPU parity of each stage on small and mid-size seeded inputs that span several
+tiles with ragged tails, plus the degenerate cases of the method.
+
+Every call goes through the C ABI (libbdr) via the binding; expected values come
+only from the CPU oracle.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import synth
+from gpu_util import REL_TOL, compare_drafts, dev, host_bits, log, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_readout_amd as bdr
+    bdr.lib()
+
+
+def bdr():
+    import block_draft_readout_amd as m
+    return m
+
+
+# mid-size shapes: 3 m-tiles with a ragged row tail, ragged vocabulary, K tails
+MID = {
+    "mid_bf16": dataclasses.replace(workloads.get("b16"), cid=20, name="mid_bf16", batch=3,
+                                    hidden=96, n_taps=3, k=5, vocab=4099, rank=16),
+    "mid_f32": dataclasses.replace(workloads.get("tiny"), cid=21, name="mid_f32", batch=5,
+                                   hidden=48, n_taps=4, fake_layers=0, tap_layers=(0, 1, 2, 3),
+                                   k=6, vocab=2053, rank=12,
+                                   plant_p=(0.76, 0.45, 0.31, 0.14, 0.10, 0.02)),
+    "mid_bf16_b20": dataclasses.replace(workloads.get("b16"), cid=22, name="mid_bf16_b20",
+                                        batch=20, hidden=64, n_taps=2, k=3, vocab=1031, rank=8),
+}
+
+
+def _data(w, step=0):
+    W = synth.make_weights(w)
+    s = synth.make_step(w, step)
+    return W, s
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_fc_parity_mid(name):
+    w = MID[name]
+    W, s = _data(w)
+    log(f"fc parity {w.describe()} rows={w.rows}")
+    ref = oracle.fuse_fc(s["taps"], W["fc_w"], w.dtype)
+    out = bdr().dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]))
+    got = oracle.widen(host_bits(out), w.dtype)
+    err = max_rel_err(got, ref)
+    log(f"  max rel err {err:.3e}")
+    assert err <= REL_TOL[w.dtype]
+    if w.dtype == "bf16":   # rounding of the fp32 sum to bf16 dominates: <= 2^-8 relative
+        assert err <= 4e-3
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_lm_head_parity_mid(name):
+    w = MID[name]
+    W, s = _data(w)
+    log(f"lm head parity {w.describe()}")
+    ref = oracle.lm_head(s["draft_hidden"], W["lm_w"], w.dtype)
+    got = bdr().dspark_lm_head(dev(s["draft_hidden"]), dev(W["lm_w"])).cpu().numpy()
+    err = max_rel_err(got, ref)
+    log(f"  max rel err {err:.3e}")
+    assert err <= min(REL_TOL[w.dtype], 1e-3)
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_markov_parity_identical_logits(name):
+    w = MID[name]
+    W, s = _data(w)
+    Z = oracle.lm_head(s["draft_hidden"], W["lm_w"], w.dtype)
+    d_ref, gap = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], s["prev0"], w.dtype)
+    d = bdr().dspark_markov_argmax(dev(Z), dev(W["w1"]), dev(W["w2"]), dev(s["prev0"]))
+    n_cmp, n_ex = compare_drafts(d.cpu().numpy(), d_ref, gap)
+    log(f"markov {name}: compared {n_cmp}, excluded {n_ex}")
+    assert n_cmp > 0
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_draft_block_parity(name):
+    w = MID[name]
+    W, s = _data(w)
+    Z = oracle.lm_head(s["draft_hidden"], W["lm_w"], w.dtype)
+    d_ref, gap = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], s["prev0"], w.dtype)
+    logits = torch.full((w.batch, w.k, w.vocab), float("nan"), device="cuda")
+    d = bdr().dspark_draft_block(dev(s["draft_hidden"]), dev(W["lm_w"]), dev(W["w1"]),
+                                 dev(W["w2"]), dev(s["prev0"]), logits_out=logits)
+    assert max_rel_err(logits.cpu().numpy(), Z) <= 1e-3
+    compare_drafts(d.cpu().numpy(), d_ref, gap)
+    # logits kept in the workspace gives the same tokens
+    d2 = bdr().dspark_draft_block(dev(s["draft_hidden"]), dev(W["lm_w"]), dev(W["w1"]),
+                                  dev(W["w2"]), dev(s["prev0"]))
+    assert torch.equal(d, d2)
+
+
+def _verify_both(w, d, Y, conf, acc0=None):
+    L = oracle.truncate_by_confidence(conf, w.threshold, w.batch, w.k)
+    t = oracle.target_argmax(Y, w.dtype, L)
+    a, bonus, acc, prop = oracle.verify_greedy(d, t, L)
+    accd = torch.zeros(w.k, dtype=torch.int64, device="cuda") if acc0 is None else acc0
+    propd = torch.zeros(w.k, dtype=torch.int64, device="cuda")
+    th = math.nan if w.threshold is None else w.threshold
+    r = bdr().spec_verify_greedy(dev(Y), dev(d.astype(np.int32)),
+                                 None if conf is None else dev(conf), th, accd, propd)
+    assert np.array_equal(r["block_len"].cpu().numpy(), L)
+    assert np.array_equal(r["target_argmax"].cpu().numpy(), t)
+    assert np.array_equal(r["accepted"].cpu().numpy(), a)
+    assert np.array_equal(r["bonus"].cpu().numpy(), bonus)
+    return accd, propd, acc, prop
+
+
+@pytest.mark.parametrize("name", list(MID))
+@pytest.mark.parametrize("threshold", [None, 0.3])
+def test_verify_parity_identical_inputs(name, threshold):
+    w = dataclasses.replace(MID[name], threshold=threshold)
+    for step in range(3):
+        d = synth.random_drafts(w, step)
+        s = synth.make_step(w, step)
+        Y = synth.plant_targets(w, step, s["noise"], d)["target_logits"]
+        conf = synth.make_confidence(w, step)
+        accd, propd, acc, prop = _verify_both(w, d, Y, conf)
+        assert np.array_equal(accd.cpu().numpy(), acc)
+        assert np.array_equal(propd.cpu().numpy(), prop)
+
+
+def test_verify_counts_accumulate():
+    w = MID["mid_bf16"]
+    d = synth.random_drafts(w, 0)
+    Y = synth.plant_targets(w, 0, synth.make_step(w, 0)["noise"], d)["target_logits"]
+    acc0 = torch.full((w.k,), 1000, dtype=torch.int64, device="cuda")
+    accd, _, acc, _ = _verify_both(w, d, Y, None, acc0=acc0)
+    assert np.array_equal(accd.cpu().numpy(), acc + 1000)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_single_row_context():
+    """rows = 1: a one-token context through the fc (the short-prompt edge case
+    in the replication report of llm-scaler PR #620)."""
+    g = np.random.default_rng(1)
+    H, T = 128, 5
+    taps = [synth.to_bf16_bits(g.standard_normal((1, H)).astype(np.float32)) for _ in range(T)]
+    Wf = synth.to_bf16_bits((g.standard_normal((H, T * H)) / np.sqrt(T * H)).astype(np.float32))
+    ref = oracle.fuse_fc(taps, Wf, "bf16")
+    out = bdr().dflash_fuse_fc([dev(t) for t in taps], dev(Wf))
+    assert max_rel_err(oracle.widen(host_bits(out), "bf16"), ref) <= 4e-3
+
+
+def test_k1_and_vocab_one():
+    g = np.random.default_rng(2)
+    for V in (1, 17, 64):
+        Z = g.standard_normal((2, 1, V)).astype(np.float32)
+        w1 = synth.to_bf16_bits(g.standard_normal((V, 8)).astype(np.float32))
+        w2 = synth.to_bf16_bits(g.standard_normal((V, 8)).astype(np.float32))
+        prev = g.integers(0, V, 2).astype(np.int32)
+        d_ref, gap = oracle.semi_ar_argmax(Z, w1, w2, prev, "bf16")
+        d = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+        compare_drafts(d, d_ref, gap)
+        if V == 1:
+            assert d.tolist() == [[0], [0]]
+
+
+def test_empty_batch_is_a_noop():
+    V, k = 100, 3
+    Y = torch.zeros((0, k + 1, V), dtype=torch.bfloat16, device="cuda")
+    d = torch.zeros((0, k), dtype=torch.int32, device="cuda")
+    acc = torch.full((k,), 7, dtype=torch.int64, device="cuda")
+    r = bdr().spec_verify_greedy(Y, d, accept_counts=acc)
+    torch.cuda.synchronize()
+    assert acc.tolist() == [7, 7, 7] and r["accepted"].numel() == 0
+    Z = torch.zeros((0, k, V), dtype=torch.float32, device="cuda")
+    out = bdr().dspark_markov_argmax(Z, None, None, torch.zeros(0, dtype=torch.int32, device="cuda"))
+    assert out.shape == (0, k)
+
+
+def test_exact_ties_across_tiles_and_tail():
+    """Equal maxima placed in different workgroups / chunks and at V-1: the
+    lowest index wins; -0.0 ties +0.0."""
+    V, k = 151936, 4
+    Z = np.full((3, k, V), -3.0, np.float32)
+    Z[0, 0, [150000, 77, 151935]] = 5.0
+    Z[0, 1, [151935, 151934]] = 5.0
+    Z[0, 2, [40000, 120000]] = 5.0
+    Z[0, 3, 3] = -0.0                     # -0.0 at the lower index ...
+    Z[0, 3, 9] = 0.0                      # ... ties +0.0: index 3 wins
+    Z[0, 3, :3] = -4.0
+    Z[1] = Z[0, ::-1]
+    Z[2, :, :] = 1.0                      # every entry ties: index 0
+    d_ref, _ = oracle.semi_ar_argmax(Z, None, None, np.zeros(3, np.int32), "f32")
+    d = bdr().dspark_markov_argmax(dev(Z), None, None, dev(np.zeros(3, np.int32))).cpu().numpy()
+    assert np.array_equal(d, d_ref)
+    # same rows as bf16 target logits through verification
+    Yb = synth.to_bf16_bits(np.concatenate([Z, Z[:, :1]], axis=1))
+    t_ref = oracle.target_argmax(Yb, "bf16")
+    r = bdr().spec_verify_greedy(dev(Yb), dev(d_ref.astype(np.int32)))
+    assert np.array_equal(r["target_argmax"].cpu().numpy(), t_ref)
+
+
+def test_zero_markov_equals_plain_argmax():
+    g = np.random.default_rng(4)
+    B, k, V, r = 4, 6, 3001, 32
+    Z = g.standard_normal((B, k, V)).astype(np.float32)
+    zeros = np.zeros((V, r), np.uint16)
+    w = synth.to_bf16_bits(g.standard_normal((V, r)).astype(np.float32))
+    prev = g.integers(0, V, B).astype(np.int32)
+    want = np.argmax(Z, axis=-1)
+    for w1, w2 in ((zeros, w), (w, zeros)):
+        d = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+        assert np.array_equal(d, want)
+    d = bdr().dspark_markov_argmax(dev(Z), None, None, dev(prev)).cpu().numpy()
+    assert np.array_equal(d, want)
+
+
+def test_planted_successor_map_on_gpu():
+    V, r, k, B = 4096, 8, 16, 5
+    sigma = np.array([13, 4000, 2, 777, 61, 3000, 1, 4095])
+    w1 = np.zeros((V, r), np.float32)
+    w1[np.arange(V), np.arange(V) % r] = 1.0
+    w2 = np.zeros((V, r), np.float32)
+    w2[sigma, np.arange(r)] = 100.0
+    prev = np.array([5, 50, 96, 13, 4095], np.int32)
+    Z = np.zeros((B, k, V), np.float32)
+    d = bdr().dspark_markov_argmax(dev(Z), dev(synth.to_bf16_bits(w1)), dev(synth.to_bf16_bits(w2)),
+                                   dev(prev)).cpu().numpy()
+    for b in range(B):
+        p = prev[b]
+        for i in range(k):
+            p = sigma[p % r]
+            assert d[b, i] == p
+
+
+def test_block_truncated_to_zero_and_max_sizes():
+    """L = 0 rows (first confidence below threshold), k = 16, rank = 128, 8 taps."""
+    w = dataclasses.replace(MID["mid_bf16"], cid=23, k=16, rank=128, n_taps=8, hidden=64,
+                            batch=6, threshold=0.5,
+                            plant_hi=tuple(0.9 * 0.85 ** i for i in range(16)),
+                            plant_lo=tuple(0.6 * 0.5 ** i for i in range(16)))
+    d = synth.random_drafts(w, 0)
+    Y = synth.plant_targets(w, 0, synth.make_step(w, 0)["noise"], d)["target_logits"]
+    conf = synth.make_confidence(w, 0)
+    conf[0, 0] = 0.1                                  # row 0: L = 0
+    conf[1, :] = 0.9                                  # row 1: full block
+    accd, propd, acc, prop = _verify_both(w, d, Y, conf)
+    assert np.array_equal(accd.cpu().numpy(), acc) and np.array_equal(propd.cpu().numpy(), prop)
+    W, s = _data(w)
+    ref = oracle.fuse_fc(s["taps"], W["fc_w"], w.dtype)
+    out = bdr().dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]))
+    assert max_rel_err(oracle.widen(host_bits(out), w.dtype), ref) <= 4e-3
+    Z = oracle.lm_head(s["draft_hidden"], W["lm_w"], w.dtype)
+    d_ref, gap = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], s["prev0"], w.dtype)
+    dg = bdr().dspark_markov_argmax(dev(Z), dev(W["w1"]), dev(W["w2"]), dev(s["prev0"]))
+    compare_drafts(dg.cpu().numpy(), d_ref, gap)
+
+
+def test_sentinel_outputs_all_written_and_deterministic():
+    w = MID["mid_bf16"]
+    W, s = _data(w)
+    outs = []
+    for _ in range(2):
+        out = torch.full((w.rows, w.hidden), 12345.0, dtype=torch.bfloat16, device="cuda")
+        bdr().dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]), out=out)
+        logits = torch.full((w.batch, w.k, w.vocab), float("nan"), device="cuda")
+        dd = torch.full((w.batch, w.k), -7, dtype=torch.int32, device="cuda")
+        bdr().dspark_draft_block(dev(s["draft_hidden"]), dev(W["lm_w"]), dev(W["w1"]),
+                                 dev(W["w2"]), dev(s["prev0"]), draft_tokens=dd, logits_out=logits)
+        torch.cuda.synchronize()
+        assert not torch.isnan(logits).any()
+        assert not (out == 12345.0).any()
+        assert (dd >= 0).all() and (dd < w.vocab).all()
+        outs.append((out.clone(), logits.clone(), dd.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)          # bitwise identical run to run

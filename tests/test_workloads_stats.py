@@ -126,3 +126,13 @@ def test_acceptance_statistics_mixture_with_truncation():
     assert np.all(np.abs(acc - N * q) <= 4 * sd + 1), (acc, N * q)
     sdp = np.sqrt(N * keep * (1 - keep))
     assert np.all(np.abs(prop - N * keep) <= 4 * sdp + 1)
+
+
+def test_plant_fast_path_is_identical():
+    w = _small(workloads.get("adaptive_b16"), hidden=64, vocab=3000)
+    s = synth.make_step(w, 5)
+    d = synth.random_drafts(w, 5)
+    slow = synth.plant_targets(w, 5, s["noise"], d)
+    fast = synth.plant_targets(w, 5, s["noise"], d, noise_stored=synth.store(s["noise"], w.dtype))
+    assert np.array_equal(slow["target_logits"], fast["target_logits"])
+    assert np.array_equal(slow["planted_token"], fast["planted_token"])

@@ -130,6 +130,9 @@ def make_step(w: Workload, step: int, noise: bool = True,
 def plant_probabilities(w: Workload, step: int) -> np.ndarray:
     """[B, k] per-position match probability used when planting this step."""
     B, k = w.batch, w.k
+    for name in (("plant_p",) if w.plant == "fixed" else ("plant_hi", "plant_lo")):
+        if len(getattr(w, name)) < k:
+            raise ValueError(f"{w.name}: {name} needs {k} probabilities")
     if w.plant == "fixed":
         return np.tile(np.asarray(w.plant_p, dtype=np.float64)[None, :k], (B, 1))
     if w.plant == "mixture":
@@ -141,13 +144,18 @@ def plant_probabilities(w: Workload, step: int) -> np.ndarray:
 
 
 def plant_targets(w: Workload, step: int, noise: np.ndarray,
-                  draft_tokens: np.ndarray) -> Dict[str, np.ndarray]:
+                  draft_tokens: np.ndarray,
+                  noise_stored: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Target logits [B, k+1, V] in storage dtype.
 
     For position j < k, +boost goes on the draft token with the position's match
     probability, else on a token drawn uniformly from the other V-1; position k
     (no draft) gets +boost on a uniformly drawn token.  ``draft_tokens`` [B, k] is
     supplied by the caller.
+
+    ``noise_stored`` (optional) is ``store(noise, w.dtype)`` computed once by the
+    caller; only the planted entries are then recomputed.  Rounding to the
+    storage dtype is elementwise, so the result is identical.
     """
     B, k, V = w.batch, w.k, w.vocab
     d = np.asarray(draft_tokens, dtype=np.int64).reshape(B, k)
@@ -158,14 +166,20 @@ def plant_targets(w: Workload, step: int, noise: np.ndarray,
     last = g.integers(0, V, size=B, dtype=np.int64)
     hit = u < p
     tok = np.where(hit, d, other + (other >= d))
-    y = np.array(noise, dtype=np.float32, copy=True).reshape(B, k + 1, V)
+    all_tok = np.concatenate([tok, last[:, None]], axis=1)          # [B, k+1]
     boost = np.float32(w.plant_boost)
-    bi = np.arange(B)
-    for j in range(k):
-        y[bi, j, tok[:, j]] += boost
-    y[bi, k, last] += boost
-    return {"target_logits": store(y, w.dtype), "planted_hit": hit,
-            "planted_token": np.concatenate([tok, last[:, None]], axis=1)}
+    noise = np.asarray(noise, dtype=np.float32).reshape(B, k + 1, V)
+    bi = np.repeat(np.arange(B), k + 1)
+    ji = np.tile(np.arange(k + 1), B)
+    vi = all_tok.reshape(-1)
+    if noise_stored is None:
+        y = noise.copy()
+        y[bi, ji, vi] += boost
+        out = store(y, w.dtype)
+    else:
+        out = np.array(noise_stored, copy=True).reshape(B, k + 1, V)
+        out[bi, ji, vi] = store(noise[bi, ji, vi] + boost, w.dtype)
+    return {"target_logits": out, "planted_hit": hit, "planted_token": all_tok}
 
 
 def make_confidence(w: Workload, step: int) -> Optional[np.ndarray]:
