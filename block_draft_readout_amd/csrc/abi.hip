@@ -36,6 +36,8 @@ bool valid_dtype(int dt) { return dt == BDR_F32 || dt == BDR_BF16; }
 
 constexpr int64_t kMaxVocab = 0x7FFFFFFELL;
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor; keeps index math in range
+constexpr int64_t kMaxBytes = 0x7FFFFFFFLL;      // per buffer resource
+constexpr int64_t kMaxMarkovVocab = int64_t(1) << 21;
 
 // 0 unknown, 1 gfx950, 2 other
 int g_dev_state[256];
@@ -91,9 +93,10 @@ int fc_shape(int64_t rows, int64_t hidden, int n_taps, int dt) {
   if (hidden % ks)
     return fail(BDR_EUNSUPPORTED, "hidden %lld must be a multiple of %d for this dtype",
                 static_cast<long long>(hidden), ks);
-  if (hidden * n_taps > kMaxElems / std::max<int64_t>(hidden, 1) ||
-      rows > kMaxElems / (hidden * n_taps))
-    return fail(BDR_EUNSUPPORTED, "fc problem too large");
+  // each tap [rows, H] and each 64-row slab of fc_w must stay below 2^31 bytes
+  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+  if (rows > kMaxBytes / (hidden * es) || hidden * n_taps > kMaxBytes / (64 * es))
+    return fail(BDR_EUNSUPPORTED, "fc problem too large (per-operand byte limit 2^31)");
   return BDR_OK;
 }
 
@@ -107,8 +110,10 @@ int lm_shape(int64_t rows, int64_t hidden, int64_t vocab, int dt) {
   if (hidden % e)
     return fail(BDR_EUNSUPPORTED, "hidden %lld must be a multiple of %d for this dtype",
                 static_cast<long long>(hidden), e);
-  if (vocab > kMaxElems / hidden || rows > kMaxElems / std::max(hidden, vocab))
-    return fail(BDR_EUNSUPPORTED, "LM-head problem too large");
+  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+  if (rows > kMaxBytes / (hidden * es) || hidden > kMaxBytes / (64 * es) ||
+      vocab > kMaxElems / hidden || rows > kMaxElems / vocab)
+    return fail(BDR_EUNSUPPORTED, "LM-head problem too large (per-operand byte limit 2^31)");
   return BDR_OK;
 }
 
@@ -123,8 +128,10 @@ int block_shape(int64_t batch, int k, int64_t vocab) {
   return BDR_OK;
 }
 
-int markov_shape(int dt, const void* w1, const void* w2, int rank) {
+int markov_shape(int dt, const void* w1, const void* w2, int rank, int64_t vocab, int k) {
   if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  // logits of 16 rows of one position, and each Markov matrix, under 2^31 bytes
+  if (vocab > kMaxMarkovVocab) return fail(BDR_EUNSUPPORTED, "vocab must be <= 2^21 here");
   if (rank < 0) return fail(BDR_EINVAL, "rank must be >= 0");
   if (rank > BDR_MAX_RANK) return fail(BDR_EUNSUPPORTED, "rank %d > %d", rank, BDR_MAX_RANK);
   if ((w1 == nullptr) != (w2 == nullptr))
@@ -151,7 +158,7 @@ const char* bdr_last_error(void) { return g_err; }
 // ---------------------------------------------------------------------------- S1
 size_t dflash_fuse_fc_workspace_bytes(int64_t rows, int64_t hidden, int n_taps, bdr_dtype dt) {
   if (fc_shape(rows, hidden, n_taps, dt) != BDR_OK || rows == 0) return 0;
-  return plan_gemm(rows, hidden, hidden * n_taps, dt, true).workspace;
+  return plan_gemm(rows, hidden, hidden * n_taps, dt, true, n_taps).workspace;
 }
 
 int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
@@ -166,7 +173,7 @@ int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows, int64_t hi
   }
   BDR_TRY(need_ptr(fc_w, "fc_w"));
   BDR_TRY(need_ptr(out, "out"));
-  const GemmPlan p = plan_gemm(rows, hidden, hidden * n_taps, dt, true);
+  const GemmPlan p = plan_gemm(rows, hidden, hidden * n_taps, dt, true, n_taps);
   BDR_TRY(need_ws(workspace, workspace_bytes, p.workspace));
   BDR_TRY(check_device());
   hipError_t e = launch_gemm(p, dt, taps, n_taps, hidden, rows, hidden, fc_w, out,
@@ -203,7 +210,7 @@ int dspark_markov_argmax(const float* logits, int64_t batch, int k, int64_t voca
                          const int32_t* prev_token, int32_t* draft_tokens, void* workspace,
                          size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
-  BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank));
+  BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank, vocab, k));
   if (batch == 0) return BDR_OK;
   BDR_TRY(need_ptr(logits, "logits"));
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
@@ -231,7 +238,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
                        size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
-  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank));
+  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank, vocab, k));
   if (batch == 0) return BDR_OK;
   BDR_TRY(need_ptr(draft_hidden, "draft_hidden"));
   BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));

@@ -23,6 +23,28 @@ template <> struct Elem<float> {
   static constexpr int KSTEP = 16;
 };
 
+// ----------------------------------------------------------------------------
+// Raw buffer loads.  A buffer resource carries a base address and a byte size;
+// a 16-byte load whose offset lies at or beyond the size returns zeros without
+// touching memory, which pads ragged tiles with no branches.
+// ----------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw-buffer data format word
+constexpr uint32_t kOOB = 0x80000000u;   // an offset beyond every resource used here
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

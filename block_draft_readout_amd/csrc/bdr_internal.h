@@ -17,17 +17,26 @@ namespace bdr {
 struct GemmPlan {
   int mt = 1;             // 16-row tiles per workgroup (1..9)
   int m_groups = 1;       // workgroups along M
-  int jn = 4;             // 16-column tiles per wave
-  int wk = 4;             // waves of a workgroup splitting K (WN = 4 / wk along N)
+  int jn = 4;             // 16-column tiles per workgroup (one wave)
   int64_t n_wg = 1;       // workgroups along N
   int ksplit = 1;         // workgroups along K (partials reduced by a second kernel)
   int64_t steps_per_split = 0;
   size_t workspace = 0;   // bytes of split-K partials
+  // streaming variant (M <= 16): balanced row ranges x K-block ranges
+  bool stream = false;
+  int64_t n_waves = 0;
+  int64_t kblocks = 0;
+  int64_t kb_per_split = 0;
 };
+
+// Compute units of a gfx950 part (MI350X / MI355X); fixed so that workspace
+// queries and launches always plan identically.
+constexpr int kNumCU = 256;
 
 enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split);
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split,
+                   int n_seg = 1);
 
 hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,

@@ -5,19 +5,22 @@
 // hidden states; W = [V, H]).  Both are dense contractions with few rows
 // (M = 4..144) against a large weight read exactly once, so the kernel is
 // organised around streaming W from HBM:
-//   * each wave owns JN 16-column tiles of W and all MT*16 rows of A;
-//   * every lane moves 16 contiguous bytes of one W row per load (4 lanes
-//     cover 64 contiguous bytes of a row), with PF steps of loads in flight;
-//   * the WK waves of a workgroup interleave K steps so that neighbouring
-//     waves read neighbouring bytes of the same W rows, and their partial sums
-//     are combined in LDS in a fixed order;
-//   * when N alone gives too few workgroups (the fc: N = H) K is also split
-//     across workgroups, each writing fp32 partials that a second kernel sums
-//     in a fixed order -- the result is deterministic.
+//   * a workgroup is one wave; it owns JN 16-column tiles of W (16*JN rows of
+//     the weight) and all MT*16 rows of A over its K range, so waves never
+//     wait on each other and all of them can be resident at once;
+//   * every lane moves 16 contiguous bytes of one W row per load, and PF
+//     steps of loads stay in flight ahead of the MFMAs that consume them;
+//   * loads are raw buffer loads: a lane whose row or K index falls outside
+//     the operand reads zeros from the hardware range check, so ragged M, N
+//     and K need no branches;
+//   * when N alone gives too few waves (the fc: N = H), K is split across
+//     workgroups too; each writes fp32 partials that a second kernel sums in a
+//     fixed order, so the result is deterministic.
 // Inputs are bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32),
 // accumulation is fp32.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "bdr_device.h"
 #include "bdr_internal.h"
@@ -35,40 +38,45 @@ struct GemmArgs {
   int64_t steps_per_split;      // K steps handled by one workgroup along K
 };
 
-template <typename S, int MT, int JN, int WK, int PF>
-__global__ __launch_bounds__(256) void ws_gemm_kernel(const GemmArgs g) {
+// Segment base pointer chosen with scalar selects (t is uniform), so the
+// pointer array is never indexed dynamically.
+__device__ __forceinline__ const void* seg_base(const GemmArgs& g, int t) {
+  const void* p = g.a[0];
+#pragma unroll
+  for (int c = 1; c < BDR_MAX_TAPS; ++c)
+    if (t == c) p = g.a[c];
+  return p;
+}
+
+template <typename S, int MT, int JN, int PF>
+__global__ __launch_bounds__(64) void ws_gemm_kernel(const GemmArgs g) {
   constexpr int E = Elem<S>::PER16;
   constexpr int KS = Elem<S>::KSTEP;
-  constexpr int WN = 4 / WK;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wn = wave % WN;
-  const int wk = wave / WN;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  const int lane = threadIdx.x;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (WN * 16 * JN) + wn * (16 * JN);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * JN);
   const int64_t m0 = static_cast<int64_t>(blockIdx.z) * (MT * 16);
   const int64_t total_steps = (g.K + KS - 1) / KS;
   const int64_t s_lo = static_cast<int64_t>(blockIdx.y) * g.steps_per_split;
   const int64_t s_hi = min(total_steps, s_lo + g.steps_per_split);
 
-  const S* wrow[JN];
-  bool nok[JN];
+  // W rows [n0, n0 + 16*JN) as one resource; rows past N read zeros
+  const int64_t nrows = min<int64_t>(16 * JN, g.N - n0);
+  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + n0 * g.K,
+                              static_cast<uint32_t>(nrows * g.K * ES));
+  uint32_t offw[JN];
 #pragma unroll
-  for (int j = 0; j < JN; ++j) {
-    const int64_t n = n0 + 16 * j + r16;
-    nok[j] = n < g.N;
-    wrow[j] = static_cast<const S*>(g.w) + (nok[j] ? n : 0) * g.K + grp * E;
-  }
-  int64_t arow[MT];
-  bool mok[MT];
+  for (int j = 0; j < JN; ++j)
+    offw[j] = static_cast<uint32_t>(((16 * j + r16) * g.K + grp * E) * ES);
+  // A rows past M lie beyond the segment resource and read zeros
+  const uint32_t abytes = static_cast<uint32_t>(g.M * g.seg * ES);
+  uint32_t offa[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = m0 + 16 * mt + r16;
-    mok[mt] = m < g.M;
-    arow[mt] = (mok[mt] ? m : 0) * g.seg + grp * E;
-  }
+  for (int mt = 0; mt < MT; ++mt)
+    offa[mt] = static_cast<uint32_t>(((m0 + 16 * mt + r16) * g.seg + grp * E) * ES);
 
   f32x4_t acc[MT][JN];
 #pragma unroll
@@ -76,77 +84,44 @@ __global__ __launch_bounds__(256) void ws_gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < JN; ++j) acc[mt][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  u32x4_t bb[PF][JN];
-  u32x4_t aa[PF][MT];
+  // next step to issue, with its A segment and offset inside the segment
+  int64_t si = s_lo;
+  int ti = static_cast<int>((s_lo * KS) / g.seg);
+  int64_t hi = s_lo * KS - static_cast<int64_t>(ti) * g.seg;
 
-  // Next step to load, with its A segment and offset inside the segment.
-  int64_t sl = s_lo + wk;
-  int tl = 0;
-  int64_t hl = 0;
-  if (sl < s_hi) {
-    const int64_t kb = sl * KS;
-    tl = static_cast<int>(kb / g.seg);
-    hl = kb - static_cast<int64_t>(tl) * g.seg;
-  }
-
-  auto load_step = [&](u32x4_t(&b)[JN], u32x4_t(&a)[MT]) {
-    const int64_t kb = sl * KS;
-    const bool kok = kb + grp * E < g.K;
+  auto issue = [&](u32x4_t(&b)[JN], u32x4_t(&a)[MT]) {
+    const int64_t kb = si * KS;
+    const bool kok = si < s_hi && kb + grp * E < g.K;
+    const uint32_t kw = kok ? static_cast<uint32_t>(kb * ES) : kOOB;
 #pragma unroll
-    for (int j = 0; j < JN; ++j) b[j] = (nok[j] && kok) ? load16(wrow[j] + kb) : zero;
-    const S* abase = static_cast<const S*>(g.a[tl]) + hl;
+    for (int j = 0; j < JN; ++j) b[j] = bload16(rw, offw[j] + kw);
+    const rsrc_t ra = make_rsrc(seg_base(g, ti), abytes);
+    const uint32_t ka = kok ? static_cast<uint32_t>(hi * ES) : kOOB;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = (mok[mt] && kok) ? load16(abase + arow[mt]) : zero;
-    hl += WK * KS;
-    while (hl >= g.seg) {
-      hl -= g.seg;
-      ++tl;
+    for (int mt = 0; mt < MT; ++mt) a[mt] = bload16(ra, offa[mt] + ka);
+    ++si;
+    hi += KS;
+    if (hi >= g.seg) {
+      hi -= g.seg;
+      ++ti;
     }
   };
 
+  u32x4_t bb[PF][JN];
+  u32x4_t aa[PF][MT];
 #pragma unroll
-  for (int d = 0; d < PF; ++d) {
-    if (sl < s_hi) load_step(bb[d], aa[d]);
-    sl += WK;
-  }
+  for (int d = 0; d < PF; ++d) issue(bb[d], aa[d]);
 
-  for (int64_t sc = s_lo + wk; sc < s_hi; sc += PF * WK) {
+  for (int64_t sc = s_lo; sc < s_hi; sc += PF) {
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
-      if (sc + d * WK < s_hi) {
+      if (sc + d < s_hi) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int j = 0; j < JN; ++j) acc[mt][j] = mma16(aa[d][mt], bb[d][j], acc[mt][j], S());
-        if (sl < s_hi) load_step(bb[d], aa[d]);
-        sl += WK;
+        issue(bb[d], aa[d]);
       }
-    }
-  }
-
-  if constexpr (WK > 1) {
-    __shared__ float red[(WK - 1) * WN * MT * JN * 4 * 64];
-    auto ridx = [&](int w, int mt, int j, int i) {
-      return ((((w * WN + wn) * MT + mt) * JN + j) * 4 + i) * 64 + lane;
-    };
-    if (wk > 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[ridx(wk - 1, mt, j, i)] = acc[mt][j][i];
-    }
-    __syncthreads();
-    if (wk != 0) return;
-    for (int w = 0; w < WK - 1; ++w) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] += red[ridx(w, mt, j, i)];
     }
   }
 
@@ -173,6 +148,167 @@ __global__ __launch_bounds__(256) void ws_gemm_kernel(const GemmArgs g) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// Streaming variant for M <= 16 (one 16-row tile of A).
+//
+// Each one-wave workgroup owns a balanced contiguous range of W rows and a
+// range of K blocks of KBB bytes per row.  The loop runs K blocks outside and
+// 16-row tiles of its range inside ("visits"); every visit copies 16 rows x
+// KBB contiguous bytes of W straight into LDS with buffer-to-LDS loads (one
+// row per instruction, 1 KB contiguous, non-temporal), double-buffered, and
+// the MFMAs read it back in operand layout from padded rows (no bank
+// conflicts).  The accumulators of every tile of the range live in registers,
+// and the A slice of a K block is loaded once into registers and reused by all
+// tiles of the range, so A costs ~M/(16*tiles) of the W traffic.  The loads to
+// LDS are not tracked by the compiler's wait insertion, so the waits on them
+// are explicit: the only memory operations issued after a visit's loads are
+// the next visit's 16, hence "vmcnt <= 16" before reading a visit.
+// ----------------------------------------------------------------------------
+constexpr int kKBB = 1024;            // bytes of each W row per visit
+constexpr int kPadRow = kKBB + 16;    // LDS row stride (breaks bank aliasing)
+constexpr int kStreamTiles = 16;      // max 16-row tiles per workgroup
+
+#define BDR_WAIT_VM(n)                                                                   \
+  do {                                                                                   \
+    __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)); \
+    __builtin_amdgcn_sched_barrier(0);                                                   \
+  } while (0)
+
+struct StreamArgs {
+  GemmArgs g;
+  int64_t n_waves;      // workgroups along N (balanced row ranges)
+  int64_t kblocks;      // K blocks of kKBB bytes per row (last may be partial)
+  int64_t kb_per_split; // K blocks per workgroup along K
+};
+
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, every index a compile-time constant
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// NT: 16-row tiles per workgroup (compile time; the last ones may be empty)
+template <typename S, int NT>
+__global__ __launch_bounds__(64) void ws_gemm_stream_kernel(const StreamArgs sa) {
+  constexpr int STEPS = kKBB / 64;      // 16-byte-per-lane MFMA operand steps per visit
+  constexpr int ES = static_cast<int>(sizeof(S));
+  const GemmArgs& g = sa.g;
+  __shared__ __attribute__((aligned(16))) char lds[2][16 * kPadRow];
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int64_t n_lo = static_cast<int64_t>(blockIdx.x) * g.N / sa.n_waves;
+  const int64_t n_hi = static_cast<int64_t>(blockIdx.x + 1) * g.N / sa.n_waves;
+  const int ntiles = static_cast<int>((n_hi - n_lo + 15) / 16);
+  const uint32_t kb_lo = static_cast<uint32_t>(blockIdx.y * sa.kb_per_split);
+  const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
+  if (ntiles <= 0 || kb_lo >= kb_hi) return;
+  const uint32_t kbytes = static_cast<uint32_t>(g.K * ES);
+  const uint32_t segbytes = static_cast<uint32_t>(g.seg * ES);
+
+  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + n_lo * g.K,
+                              static_cast<uint32_t>(n_hi - n_lo) * kbytes);
+  const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16;
+  const uint32_t a_lane = static_cast<uint32_t>(r16) * segbytes + static_cast<uint32_t>(grp) * 16;
+  const uint32_t lds_rd = static_cast<uint32_t>(r16 * kPadRow + grp * 16);
+
+  f32x4_t acc[NT];
+  static_for<NT>([&](auto t) { acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f}; });
+  u32x4_t a0[STEPS], a1[STEPS];
+
+  // 16 rows of tile t, K block kb -> LDS buffer b (rows past the range and
+  // bytes past a row read zeros)
+  auto dma = [&](uint32_t kb, int t, int b) {
+    const uint32_t k0 = kb * kKBB;
+    const uint32_t lo = k0 + lane16 < kbytes ? lane16 : kOOB;
+    const uint32_t base = static_cast<uint32_t>(16 * t) * kbytes + k0;
+    char* dst = &lds[b][0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(dst + r * kPadRow), 16,
+          lo + base + static_cast<uint32_t>(r) * kbytes, 0, 0, 2);
+  };
+  // A slice of K block kb in operand layout (rows >= M read zeros); blocks
+  // never straddle A segments
+  auto load_a = [&](uint32_t kb, u32x4_t(&a)[STEPS]) {
+    const uint32_t k0 = kb * kKBB;
+    const uint32_t ts = k0 / segbytes;
+    const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
+    const uint32_t off = a_lane + (k0 - ts * segbytes);
+    static_for<STEPS>([&](auto st) { a[st] = bload16(ra, off + st * 64); });
+  };
+  auto compute = [&](auto t, int b, const u32x4_t(&a)[STEPS], int nsteps) {
+    const char* src = &lds[b][0] + lds_rd;
+    if (nsteps == STEPS) {
+      static_for<STEPS>([&](auto st) {
+        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(src + st * 64);
+        acc[t] = mma16(a[st], bv, acc[t], S());
+      });
+    } else {
+      static_for<STEPS>([&](auto st) {
+        if (st < nsteps) {
+          const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(src + st * 64);
+          acc[t] = mma16(a[st], bv, acc[t], S());
+        }
+      });
+    }
+  };
+
+  int buf = 0;
+  // one K block: visit every tile; prefetch the next visit (and the next
+  // block's A slice) before waiting on the current one
+  auto block = [&](uint32_t kb, const u32x4_t(&acur)[STEPS], u32x4_t(&anext)[STEPS]) {
+    const int nsteps = static_cast<int>(min<uint32_t>(STEPS, (kbytes - kb * kKBB) / 64));
+    static_for<NT>([&](auto t) {
+      if (t < ntiles) {
+        if (t + 1 < ntiles) {
+          dma(kb, t + 1, buf ^ 1);
+          BDR_WAIT_VM(16);
+        } else if (kb + 1 < kb_hi) {
+          load_a(kb + 1, anext);
+          dma(kb + 1, 0, buf ^ 1);
+          BDR_WAIT_VM(16);
+        } else {
+          BDR_WAIT_VM(0);
+        }
+        compute(t, buf, acur, nsteps);
+        buf ^= 1;
+      }
+    });
+  };
+
+  load_a(kb_lo, a0);
+  dma(kb_lo, 0, 0);
+  for (uint32_t kb = kb_lo; kb < kb_hi; kb += 2) {
+    block(kb, a0, a1);
+    if (kb + 1 < kb_hi) block(kb + 1, a1, a0);
+  }
+
+  static_for<NT>([&](auto t) {
+    const int64_t n = n_lo + 16 * t + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = 4 * grp + i;
+      if (t < ntiles && m < g.M && n < n_hi) {
+        const float v = acc[t][i];
+        if (g.partial)
+          static_cast<float*>(g.out)[(static_cast<int64_t>(blockIdx.y) * g.M + m) * g.N + n] = v;
+        else if (g.out_kind == OUT_BF16)
+          static_cast<uint16_t*>(g.out)[m * g.N + n] = f32_to_bf16(v);
+        else
+          static_cast<float*>(g.out)[m * g.N + n] = v;
+      }
+    }
+  });
+}
+
 // out[i] = sum_p part[p][i] in order p = 0, 1, ...
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int ksplit, int64_t mn, void* out,
@@ -192,20 +328,51 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // host side
 // ----------------------------------------------------------------------------
 
-static void pick_tiles(int mt, int* jn, int* wk) {
-  if (mt <= 2) {
-    *jn = 4;
-    *wk = 4;
-  } else {
-    *jn = 2;
-    *wk = 4;
+// Column tiles per wave and prefetch depth by the number of 16-row tiles of A.
+static int pick_jn(int mt) { return mt <= 2 ? 4 : 2; }
+
+// Streaming plan: balanced row ranges (at most kStreamTiles tiles each) and a
+// K split chosen to minimise per-wave cost = W bytes + a quarter of the A bytes
+// it re-reads from L2 (+ the partial-sum round trip and a second launch).
+static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
+                        GemmPlan* p) {
+  const int64_t kbytes = K * esize;
+  const int64_t segbytes = kbytes / n_seg;
+  if (M > 16 || kbytes % 64 != 0 || (n_seg > 1 && segbytes % kKBB != 0)) return false;
+  const int64_t waves = 4 * static_cast<int64_t>(kNumCU);
+  const int64_t kblocks = (kbytes + kKBB - 1) / kKBB;
+  double best = 1e300;
+  for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
+    int64_t nw = std::max<int64_t>(1, waves / ks);
+    nw = std::max<int64_t>(nw, (N + 16 * kStreamTiles - 1) / (16 * kStreamTiles));
+    nw = std::min<int64_t>(nw, N);
+    const int64_t kbps = (kblocks + ks - 1) / ks;
+    const int64_t ks_eff = (kblocks + kbps - 1) / kbps;
+    const int64_t rows = (N + nw - 1) / nw;
+    const int64_t rounds = (nw * ks_eff + waves - 1) / waves;
+    double cost = static_cast<double>(rounds) * kbps * kKBB * (rows + 0.25 * M);
+    if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / waves;
+    if (cost < best) {
+      best = cost;
+      p->n_waves = nw;
+      p->kb_per_split = kbps;
+      p->ksplit = static_cast<int>(ks_eff);
+    }
   }
+  p->stream = true;
+  p->kblocks = kblocks;
+  p->mt = 1;
+  p->m_groups = 1;
+  p->n_wg = p->n_waves;
+  p->workspace = p->ksplit > 1 ? align256(static_cast<size_t>(p->ksplit) * M * N * 4) : 0;
+  return true;
 }
 
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split, int n_seg) {
   GemmPlan p;
   const int ks = dt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
   const int esize = dt == BDR_BF16 ? 2 : 4;
+  if (plan_stream(M, N, K, esize, allow_split, n_seg, &p)) return p;
   const int64_t mtiles = std::max<int64_t>(1, (M + 15) / 16);
   if (mtiles <= 9) {
     p.mt = static_cast<int>(mtiles);
@@ -214,16 +381,17 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
     p.mt = 8;
     p.m_groups = static_cast<int>((mtiles + 7) / 8);
   }
-  pick_tiles(p.mt, &p.jn, &p.wk);
-  const int64_t cols = (4 / p.wk) * 16 * p.jn;
+  p.jn = pick_jn(p.mt);
+  const int64_t cols = 16 * p.jn;
   p.n_wg = (N + cols - 1) / cols;
   const int64_t steps = (K + ks - 1) / ks;
   int64_t split = 1;
   if (allow_split) {
-    const int64_t target_wgs = 2048;
+    // about ten resident waves per compute unit
+    const int64_t target_wgs = 2560;
     const int64_t base = p.n_wg * p.m_groups;
     split = (target_wgs + base - 1) / base;
-    split = std::min<int64_t>(split, std::max<int64_t>(1, steps / (p.wk * 4)));
+    split = std::min<int64_t>(split, std::max<int64_t>(1, steps / 16));
     // keep partial-sum traffic (write + read, fp32) under ~8% of the weight bytes
     const int64_t cap = std::max<int64_t>(
         1, static_cast<int64_t>(0.08 * static_cast<double>(K) * esize / (8.0 * std::max<int64_t>(M, 1))));
@@ -239,11 +407,13 @@ template <typename S, int MT>
 static void launch_mt(const GemmPlan& p, const GemmArgs& g, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.n_wg), static_cast<unsigned>(p.ksplit),
                   static_cast<unsigned>(p.m_groups));
-  // tile shapes per MT as chosen by pick_tiles()
+  // tile shapes per MT as chosen by pick_jn()
   if constexpr (MT <= 2)
-    hipLaunchKernelGGL((ws_gemm_kernel<S, MT, 4, 4, 2>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((ws_gemm_kernel<S, MT, 4, 4>), grid, dim3(64), 0, st, g);
+  else if constexpr (MT <= 4)
+    hipLaunchKernelGGL((ws_gemm_kernel<S, MT, 2, 4>), grid, dim3(64), 0, st, g);
   else
-    hipLaunchKernelGGL((ws_gemm_kernel<S, MT, 2, 4, 2>), grid, dim3(256), 0, st, g);
+    hipLaunchKernelGGL((ws_gemm_kernel<S, MT, 2, 2>), grid, dim3(64), 0, st, g);
 }
 
 template <typename S>
@@ -261,6 +431,20 @@ static void launch_typed(const GemmPlan& p, const GemmArgs& g, hipStream_t st) {
   }
 }
 
+template <typename S>
+static void launch_stream(const GemmPlan& p, const GemmArgs& g, hipStream_t st) {
+  const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
+  const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
+  const int64_t tiles = ((g.N + p.n_waves - 1) / p.n_waves + 15) / 16;
+  if (tiles <= 1) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 1>), grid, dim3(64), 0, st, sa);
+  else if (tiles <= 2) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 2>), grid, dim3(64), 0, st, sa);
+  else if (tiles <= 4) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 4>), grid, dim3(64), 0, st, sa);
+  else if (tiles <= 8) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 8>), grid, dim3(64), 0, st, sa);
+  else if (tiles <= 10) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 10>), grid, dim3(64), 0, st, sa);
+  else if (tiles <= 12) hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 12>), grid, dim3(64), 0, st, sa);
+  else hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 16>), grid, dim3(64), 0, st, sa);
+}
+
 hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,
                        OutKind out_kind, void* workspace, hipStream_t stream) {
@@ -276,10 +460,16 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   const bool split = p.ksplit > 1;
   g.partial = split ? 1 : 0;
   g.out = split ? workspace : out;
-  if (dt == BDR_BF16)
+  if (p.stream) {
+    if (dt == BDR_BF16)
+      launch_stream<uint16_t>(p, g, stream);
+    else
+      launch_stream<float>(p, g, stream);
+  } else if (dt == BDR_BF16) {
     launch_typed<uint16_t>(p, g, stream);
-  else
+  } else {
     launch_typed<float>(p, g, stream);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t mn = M * N;

@@ -43,15 +43,19 @@ __global__ __launch_bounds__(256) void markov_init_kernel(unsigned long long* ke
     keys[i] = 0ull;
 }
 
-template <typename S, int RKS>
+// TPW vocabulary tiles of 16 per wave; all their loads are issued before any
+// is consumed, so one pass costs about one memory round trip per wave.
+template <typename S, int RKS, int TPW>
 __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, int pos) {
   constexpr int E = Elem<S>::PER16;
   constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int64_t nb = min<int64_t>(16, g.B - b0);
 
   // Context token of A-operand row r16.
   const int64_t brow = b0 + r16;
@@ -61,17 +65,30 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
   if (pos > 0 && blockIdx.x == 0 && threadIdx.x < 16 && brow < g.B)
     g.draft[brow * g.k + (pos - 1)] = p;
 
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const uint32_t wbytes = static_cast<uint32_t>(g.V * g.r * ES);
   u32x4_t ef[RKS > 0 ? RKS : 1];
   if constexpr (RKS > 0) {
+    const rsrc_t r1 = make_rsrc(g.w1, wbytes);
     const bool pok = p >= 0 && static_cast<int64_t>(p) < g.V;  // out-of-range context: no bias
 #pragma unroll
     for (int c = 0; c < RKS; ++c) {
       const int j = c * KS + grp * E;
-      ef[c] = (pok && j < g.r)
-                  ? load16(static_cast<const S*>(g.w1) + static_cast<int64_t>(p) * g.r + j)
-                  : zero;
+      ef[c] = bload16(r1, (pok && j < g.r)
+                              ? static_cast<uint32_t>((static_cast<int64_t>(p) * g.r + j) * ES)
+                              : kOOB);
     }
+  }
+  const rsrc_t r2 = make_rsrc(g.w2, wbytes);
+  // logits of this position for rows b0..b0+nb-1 (row stride k*V floats)
+  const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V,
+                              static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4));
+  uint32_t zrow[4];
+  bool bok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rb = 4 * grp + i;
+    bok[i] = rb < nb;
+    zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
   }
 
   float bv[4];
@@ -81,36 +98,39 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
     bv[i] = -INFINITY;
     bi[i] = 0xFFFFFFFFu;
   }
-  // rows of the D tile held by this lane: b = b0 + 4*grp + i
-  const float* zrow[4];
-  bool bok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t b = b0 + 4 * grp + i;
-    bok[i] = b < g.B;
-    zrow[i] = g.logits + ((bok[i] ? b : 0) * g.k + pos) * g.V;
-  }
 
-  for (int64_t vt = static_cast<int64_t>(blockIdx.x) * 4 + wave; vt < g.vtiles;
-       vt += static_cast<int64_t>(gridDim.x) * 4) {
-    const int64_t v = vt * 16 + r16;
-    const bool vok = v < g.V;
-    f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (RKS > 0) {
-      u32x4_t wf[RKS];
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 4 + wave; base < g.vtiles;
+       base += nw * TPW) {
+    u32x4_t wf[TPW][RKS > 0 ? RKS : 1];
+    float zv[TPW][4];
 #pragma unroll
-      for (int c = 0; c < RKS; ++c) {
-        const int j = c * KS + grp * E;
-        wf[c] = (vok && j < g.r) ? load16(static_cast<const S*>(g.w2) + v * g.r + j) : zero;
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t v = (base + u * nw) * 16 + r16;
+      const bool vok = v < g.V;
+      if constexpr (RKS > 0) {
+#pragma unroll
+        for (int c = 0; c < RKS; ++c) {
+          const int j = c * KS + grp * E;
+          wf[u][c] = bload16(r2, (vok && j < g.r) ? static_cast<uint32_t>((v * g.r + j) * ES) : kOOB);
+        }
       }
 #pragma unroll
-      for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], wf[c], bias, S());
+      for (int i = 0; i < 4; ++i)
+        zv[u][i] = bload_f32(rz, (vok && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (vok && bok[i]) {
-        const float s = zrow[i][v] + bias[i];
-        if (s > bv[i]) {
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t v = (base + u * nw) * 16 + r16;
+      f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (RKS > 0) {
+#pragma unroll
+        for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], wf[u][c], bias, S());
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = zv[u][i] + bias[i];
+        if (v < g.V && bok[i] && s > bv[i]) {
           bv[i] = s;
           bi[i] = static_cast<uint32_t>(v);
         }
@@ -150,23 +170,26 @@ size_t markov_workspace(int64_t B, int k) {
 }
 
 template <typename S, int RKS>
-static void launch_passes(const MarkovArgs& g, dim3 grid, hipStream_t st) {
+static void launch_passes(const MarkovArgs& g, hipStream_t st) {
+  constexpr int TPW = RKS <= 2 ? 8 : (RKS <= 4 ? 4 : 2);
+  const int64_t wgs = std::min<int64_t>((g.vtiles + 4 * TPW - 1) / (4 * TPW), 1024);
+  const dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>((g.B + 15) / 16));
   for (int pos = 0; pos < g.k; ++pos)
-    hipLaunchKernelGGL((markov_pass_kernel<S, RKS>), grid, dim3(256), 0, st, g, pos);
+    hipLaunchKernelGGL((markov_pass_kernel<S, RKS, TPW>), grid, dim3(256), 0, st, g, pos);
 }
 
 template <typename S>
-static void launch_typed(const MarkovArgs& g, int rks, dim3 grid, hipStream_t st) {
+static void launch_typed(const MarkovArgs& g, int rks, hipStream_t st) {
   switch (rks) {
-    case 0: launch_passes<S, 0>(g, grid, st); break;
-    case 1: launch_passes<S, 1>(g, grid, st); break;
-    case 2: launch_passes<S, 2>(g, grid, st); break;
-    case 3: launch_passes<S, 3>(g, grid, st); break;
-    case 4: launch_passes<S, 4>(g, grid, st); break;
-    case 5: launch_passes<S, 5>(g, grid, st); break;
-    case 6: launch_passes<S, 6>(g, grid, st); break;
-    case 7: launch_passes<S, 7>(g, grid, st); break;
-    default: launch_passes<S, 8>(g, grid, st); break;
+    case 0: launch_passes<S, 0>(g, st); break;
+    case 1: launch_passes<S, 1>(g, st); break;
+    case 2: launch_passes<S, 2>(g, st); break;
+    case 3: launch_passes<S, 3>(g, st); break;
+    case 4: launch_passes<S, 4>(g, st); break;
+    case 5: launch_passes<S, 5>(g, st); break;
+    case 6: launch_passes<S, 6>(g, st); break;
+    case 7: launch_passes<S, 7>(g, st); break;
+    default: launch_passes<S, 8>(g, st); break;
   }
 }
 
@@ -192,12 +215,10 @@ hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_d
   hipLaunchKernelGGL(markov_init_kernel,
                      dim3(static_cast<unsigned>(std::min<int64_t>((nkeys + 255) / 256, 1024))),
                      dim3(256), 0, stream, g.keys, nkeys);
-  const int64_t wgs = std::min<int64_t>((g.vtiles + 3) / 4, 512);
-  const dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>((B + 15) / 16));
   if (wdt == BDR_BF16)
-    launch_typed<uint16_t>(g, rks, grid, stream);
+    launch_typed<uint16_t>(g, rks, stream);
   else
-    launch_typed<float>(g, rks, grid, stream);
+    launch_typed<float>(g, rks, stream);
   hipLaunchKernelGGL(markov_finalize_kernel,
                      dim3(static_cast<unsigned>(std::min<int64_t>((B + 255) / 256, 1024))),
                      dim3(256), 0, stream, g.keys, B, k, draft);

@@ -97,47 +97,59 @@ __global__ __launch_bounds__(256) void verify_argmax_kernel(const VerifyArgs g) 
     g.part[row * g.chunks + blockIdx.y] = umax64(umax64(sk[0], sk[1]), umax64(sk[2], sk[3]));
 }
 
-__global__ __launch_bounds__(256) void verify_scan_kernel(const VerifyArgs g) {
+// 1024 threads; sequences in groups of 64: each wave folds the chunk keys of one
+// verified (sequence, position) row at a time, then one thread per sequence
+// scans its block.
+__global__ __launch_bounds__(1024) void verify_scan_kernel(const VerifyArgs g) {
+  constexpr int GROUP = 64;
+  __shared__ int32_t ts[GROUP * (BDR_MAX_K + 1)];
+  __shared__ int Ls[GROUP];
   __shared__ int cacc[BDR_MAX_K];
   __shared__ int cprop[BDR_MAX_K];
-  if (threadIdx.x < BDR_MAX_K) {
-    cacc[threadIdx.x] = 0;
-    cprop[threadIdx.x] = 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int k1 = g.k + 1;
+  if (tid < BDR_MAX_K) {
+    cacc[tid] = 0;
+    cprop[tid] = 0;
   }
-  __syncthreads();
-  for (int64_t b = threadIdx.x; b < g.B; b += 256) {
-    const int L = block_length(g, b);
-    int a = 0;
-    int32_t bonus = -1;
-    bool done = false;
-    for (int j = 0; j <= g.k; ++j) {
+  for (int64_t b0 = 0; b0 < g.B; b0 += GROUP) {
+    const int nb = static_cast<int>(min<int64_t>(GROUP, g.B - b0));
+    if (tid < nb) Ls[tid] = block_length(g, b0 + tid);
+    __syncthreads();
+    for (int r = wave; r < nb * k1; r += nwaves) {
+      const int lb = r / k1;
+      const int j = r - lb * k1;
       int32_t t = -1;
-      if (j <= L) {
-        const unsigned long long* pp = g.part + (b * (g.k + 1) + j) * g.chunks;
+      if (j <= Ls[lb]) {
+        const unsigned long long* pp = g.part + ((b0 + lb) * k1 + j) * g.chunks;
         unsigned long long key = 0ull;
-        for (int c = 0; c < g.chunks; ++c) key = umax64(key, pp[c]);
-        t = key_index(key);
-        if (!done) {
-          if (j < L && g.draft[b * g.k + j] == t) {
-            ++a;
-          } else {
-            bonus = t;
-            done = true;
-          }
-        }
+        for (int c = lane; c < g.chunks; c += 64) key = umax64(key, pp[c]);
+        t = key_index(wave_max64(key));
       }
-      if (g.targ) g.targ[b * (g.k + 1) + j] = t;
+      if (lane == 0) ts[r] = t;
     }
-    g.block_len[b] = L;
-    g.accepted[b] = a;
-    g.bonus[b] = bonus;
-    for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
-    for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
+    __syncthreads();
+    if (tid < nb) {
+      const int64_t b = b0 + tid;
+      const int L = Ls[tid];
+      int a = 0;
+      while (a < L && g.draft[b * g.k + a] == ts[tid * k1 + a]) ++a;
+      g.block_len[b] = L;
+      g.accepted[b] = a;
+      g.bonus[b] = ts[tid * k1 + a];
+      if (g.targ)
+        for (int j = 0; j <= g.k; ++j) g.targ[b * k1 + j] = ts[tid * k1 + j];
+      for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
+      for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < g.k) {
-    if (g.acc) g.acc[threadIdx.x] += cacc[threadIdx.x];
-    if (g.prop) g.prop[threadIdx.x] += cprop[threadIdx.x];
+  if (tid < g.k) {
+    if (g.acc) g.acc[tid] += cacc[tid];
+    if (g.prop) g.prop[tid] += cprop[tid];
   }
 }
 
@@ -201,7 +213,7 @@ hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t 
     else
       hipLaunchKernelGGL((verify_argmax_kernel<float, false>), grid, dim3(256), 0, stream, g);
   }
-  hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(256), 0, stream, g);
+  hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(1024), 0, stream, g);
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@
  *   - Values that live on the device (token ids, logits) are not checked: a
  *     draft token outside [0, V) never matches, and a previous token outside
  *     [0, V) contributes no Markov bias.  Floating inputs must be finite.
+ *   - Operands are read with 32-bit-offset buffer loads: each tap / hidden
+ *     tensor, each 64-row slab of a weight and each Markov matrix must be
+ *     under 2^31 bytes (BDR_EUNSUPPORTED otherwise).
  *   - Token ids are int32, counters int64.  dtype selects the storage of
  *     weights and activations (BDR_BF16 or BDR_F32); accumulation is fp32.
  *   - Entry points are reentrant; calls that share a workspace must be ordered
@@ -118,7 +121,7 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size,
  * biased prediction ([recipe] DSpark port notes, dflash.py).
  *
  *   logits      [B, k, V] fp32 (finite)
- *   batch B >= 0, 1 <= k <= BDR_MAX_K, 0 < V < 2^31 - 1
+ *   batch B >= 0, 1 <= k <= BDR_MAX_K, 0 < V <= 2^21
  *   wdt         dtype of the Markov weights
  *   markov_w1   [V, r] embedding, markov_w2 [V, r] projection; both NULL or
  *               rank == 0 means no bias (plain argmax per position).
