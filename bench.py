@@ -182,7 +182,7 @@ def main():
     def ws(n):
         if n == 0:
             return None, 0, None
-        t = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        t = torch.zeros(n + 256, dtype=torch.uint8, device=dev)
         p = (t.data_ptr() + 255) & ~255
         return C.c_void_p(p), n, t
 

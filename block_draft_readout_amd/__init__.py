@@ -4,7 +4,8 @@ Each function marshals torch device tensors into the C ABI of ``include/bdr.h``
 (``data_ptr()`` and the current HIP stream) and raises ``BdrError`` on a non-zero
 return.  Every step of the path runs in the HIP kernels of libbdr; there is no
 other implementation behind these names.  Output tensors and workspaces that are
-not supplied are allocated with torch on the input's device.
+not supplied are allocated with torch on the input's device; a workspace passed
+in must have been zero-filled once (``torch.zeros``) and may be reused.
 """
 from __future__ import annotations
 
@@ -58,7 +59,8 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torc
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError(f"workspace too small: need {nbytes} bytes")
         return ws
-    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    # zero-filled: the library's counters start at zero and are left at zero
+    return torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
 
 
 def _ws_ptr(ws: Optional[torch.Tensor]):

@@ -39,11 +39,13 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor; keeps index math
 constexpr int64_t kMaxBytes = 0x7FFFFFFFLL;      // per buffer resource
 constexpr int64_t kMaxMarkovVocab = int64_t(1) << 21;
 
-// 0 unknown, 1 gfx950, 2 other
+// 0 unknown, 1 gfx950, 2 other; compute units per device
 int g_dev_state[256];
+int g_dev_cus[256];
 std::mutex g_dev_mu;
 
-int check_device() {
+// Checks that the current device is gfx950; *cus receives its compute-unit count.
+int check_device(int* cus = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -54,12 +56,14 @@ int check_device() {
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev] = prop.multiProcessorCount;
     if (g_dev_state[dev] == 2)
       return fail(BDR_EUNSUPPORTED, "device %d is %s; libbdr is built for gfx950 only", dev,
                   prop.gcnArchName);
   }
   if (g_dev_state[dev] != 1)
     return fail(BDR_EUNSUPPORTED, "device %d is not gfx950; libbdr is built for gfx950 only", dev);
+  if (cus) *cus = g_dev_cus[dev];
   return BDR_OK;
 }
 
@@ -216,9 +220,10 @@ int dspark_markov_argmax(const float* logits, int64_t batch, int k, int64_t voca
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
   BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
   BDR_TRY(need_ws(workspace, workspace_bytes, markov_workspace(batch, k)));
-  BDR_TRY(check_device());
+  int cus = 0;
+  BDR_TRY(check_device(&cus));
   hipError_t e = launch_markov(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
-                               prev_token, draft_tokens, workspace, as_stream(stream));
+                               prev_token, draft_tokens, workspace, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_markov_argmax launch");
   return BDR_OK;
 }
@@ -247,7 +252,8 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
   if (logits_out) BDR_TRY(need_ptr(logits_out, "logits_out"));
   const size_t need = dspark_draft_workspace_bytes(batch, k, vocab, logits_out == nullptr);
   BDR_TRY(need_ws(workspace, workspace_bytes, need));
-  BDR_TRY(check_device());
+  int cus = 0;
+  BDR_TRY(check_device(&cus));
   char* ws = static_cast<char*>(workspace);
   float* logits = logits_out;
   if (!logits) {
@@ -260,7 +266,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
                              nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block LM-head launch");
   e = launch_markov(logits, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
-                    draft_tokens, ws, as_stream(stream));
+                    draft_tokens, ws, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block Markov launch");
   return BDR_OK;
 }

@@ -45,6 +45,59 @@ __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained), and keep the
+// scheduler from moving anything across.  Needed after buffer-to-LDS loads,
+// which the compiler's own wait insertion does not track.
+#define BDR_WAIT_VM(n)                                                                        \
+  do {                                                                                        \
+    __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)); \
+    __builtin_amdgcn_sched_barrier(0);                                                        \
+  } while (0)
+
+// Cross-workgroup hand-off without cache maintenance: data published for other
+// workgroups is stored and loaded with agent-scope atomic accesses (coherent
+// across the chip's L2 slices), and a wave orders its publications before an
+// arrival counter by waiting for its own outstanding memory operations.
+// (A full __threadfence() writes back and invalidates the whole L2 slice.)
+__device__ __forceinline__ void publish_u64(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long fetch_u64(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned fetch_u32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#define BDR_WAIT_ALL_MEM()                    \
+  do {                                        \
+    __builtin_amdgcn_s_waitcnt(0);            \
+    __builtin_amdgcn_sched_barrier(0);        \
+  } while (0)
+
+// Two-level arrival counting.  Same-address device-scope atomics serialise,
+// so G workgroups arrive on group counters (workgroup w in group w % 16, each
+// counter on its own 128-byte line) and only each group's last arriver
+// touches the top counter.  Called by one thread per workgroup.
+constexpr int kArriveGroups = 16;
+constexpr int kLineWords = 32;   // 128-byte stride between counters (uint32 units)
+
+__device__ __forceinline__ unsigned arrive_groups(unsigned G) {
+  return G < kArriveGroups ? G : kArriveGroups;
+}
+
+// true for the last workgroup of w's group to arrive
+__device__ __forceinline__ bool arrive_group(unsigned* grp_cnt, unsigned w, unsigned G) {
+  const unsigned gi = w % kArriveGroups;
+  const unsigned gsz = G < kArriveGroups ? 1u : G / kArriveGroups + (gi < G % kArriveGroups ? 1u : 0u);
+  return atomicAdd(&grp_cnt[gi * kLineWords], 1u) + 1 == gsz;
+}
+
+// true for the last group to arrive
+__device__ __forceinline__ bool arrive_top(unsigned* top_cnt, unsigned G) {
+  return atomicAdd(top_cnt, 1u) + 1 == arrive_groups(G);
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

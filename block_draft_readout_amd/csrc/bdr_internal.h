@@ -48,7 +48,7 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
 size_t markov_workspace(int64_t B, int k);
 hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                          const void* w1, const void* w2, int rank, const int32_t* prev,
-                         int32_t* draft, void* workspace, hipStream_t stream);
+                         int32_t* draft, void* workspace, int n_cu, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // Greedy verification.

@@ -168,12 +168,6 @@ constexpr int kKBB = 1024;            // bytes of each W row per visit
 constexpr int kPadRow = kKBB + 16;    // LDS row stride (breaks bank aliasing)
 constexpr int kStreamTiles = 16;      // max 16-row tiles per workgroup
 
-#define BDR_WAIT_VM(n)                                                                   \
-  do {                                                                                   \
-    __builtin_amdgcn_s_waitcnt(((n)&0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)); \
-    __builtin_amdgcn_sched_barrier(0);                                                   \
-  } while (0)
-
 struct StreamArgs {
   GemmArgs g;
   int64_t n_waves;      // workgroups along N (balanced row ranges)
@@ -307,20 +301,37 @@ __global__ __launch_bounds__(64) void ws_gemm_stream_kernel(const StreamArgs sa)
       }
     }
   });
+
 }
 
-// out[i] = sum_p part[p][i] in order p = 0, 1, ...
+// out[i] = sum_p part[p][i] in order p = 0, 1, ...; four outputs per thread,
+// all splits' loads issued before the (ordered) sums.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int ksplit, int64_t mn, void* out,
                                                             int out_kind) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < mn;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    float s = 0.f;
-    for (int p = 0; p < ksplit; ++p) s += part[p * mn + i];
+  constexpr int PMAX = 16;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i0 >= mn) return;
+  const int n = static_cast<int>(min<int64_t>(4, mn - i0));
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < ksplit; p0 += PMAX) {
+    float v[PMAX][4];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[p][e] = (p0 + p < ksplit && e < n) ? part[(p0 + p) * mn + i0 + e] : 0.f;
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p0 + p < ksplit) sum[e] += v[p][e];
+  }
+  for (int e = 0; e < n; ++e) {
     if (out_kind == OUT_BF16)
-      static_cast<uint16_t*>(out)[i] = f32_to_bf16(s);
+      static_cast<uint16_t*>(out)[i0 + e] = f32_to_bf16(sum[e]);
     else
-      static_cast<float*>(out)[i] = s;
+      static_cast<float*>(out)[i0 + e] = sum[e];
   }
 }
 
@@ -473,7 +484,7 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   const int64_t mn = M * N;
-  const int64_t blocks = std::min<int64_t>((mn + 255) / 256, 4096);
+  const int64_t blocks = (mn + 1023) / 1024;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const float*>(workspace), p.ksplit, mn, out,
                      static_cast<int>(out_kind));

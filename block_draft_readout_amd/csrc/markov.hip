@@ -3,20 +3,35 @@
 // For each row b the context token p starts at the accepted bonus token of the
 // previous step and, position after position, becomes the biased argmax just
 // taken (llm-scaler PR #620, DSpark port notes: dflash.py and qwen3_dflash.py).
-// One kernel launch handles one position for every row:
+//
+// Arithmetic of one position, for 16 rows at a time:
 //   * the low-rank bias of 16 rows for 16 vocabulary entries is one MFMA tile:
-//     A = markov_w1 rows of the 16 contexts ([16, r]), B = markov_w2 rows of the
-//     16 entries ([r, 16]); r = 32/64 is one or two 16-byte loads per lane;
+//     A = markov_w1 rows of the 16 contexts ([16, r]), B = markov_w2 rows of
+//     the 16 entries ([r, 16]); r = 32/64 is one or two 16-byte operand chunks;
 //   * the fp32 logits of the position are added and each lane keeps a running
 //     (value, index) maximum over the entries it visits in increasing order;
-//   * the running maxima are packed into order-preserving uint64 keys (value,
-//     then lower index), reduced across lanes and waves, and folded into one
-//     key per row with a device-scope atomic max -- max is order-independent,
-//     so the result is deterministic;
-//   * the next launch reads the previous position's key as its context and
-//     writes the previous position's token out.
-// Positions are separate launches because position i+1 needs the whole-vocab
-// argmax of position i; the stream order provides that grid-wide dependency.
+//   * maxima are packed into order-preserving uint64 keys (value, then lower
+//     index) and folded across lanes, waves and workgroups with max, which is
+//     order-independent: the result is deterministic.
+//
+// Two schedules:
+//   chain  -- one persistent launch for all k positions.  One workgroup per
+//             compute unit keeps its slice of markov_w2 in LDS for the whole
+//             chain; positions are separated by a grid barrier with two-level
+//             arrival counters (the last arriver writes that position's tokens,
+//             and the final one returns the workspace to zero).  All
+//             workgroups must be resident at once: the grid is at most the
+//             number of compute units and each workgroup fits in one.  The spin
+//             on the barrier is bounded; a time-out sets the error word of the
+//             workspace instead of hanging.
+//   passes -- one launch per position (used when the markov_w2 slice does not
+//             fit in LDS); stream order provides the grid-wide dependency.
+// Workgroup w folds its keys into group slot w % 16 (atomic max; 16-way at
+// most), and readers take the max over the 16 group slots.
+//
+// Workspace (zero-filled before first use; every call leaves it zeroed):
+//   keys[k][16][B] uint64 | group counters [k][16] | top counters [k]
+//   (one 128-byte line each) | error uint32
 
 #include <algorithm>
 
@@ -32,43 +47,38 @@ struct MarkovArgs {
   const void* w1;                // [V, r] embedding of the context token
   const void* w2;                // [V, r] projection to the vocabulary
   const int32_t* prev;           // [B] context of position 0
-  unsigned long long* keys;      // [k, B] per-position argmax keys (zeroed first)
+  unsigned long long* keys;      // [k, 16, B] per-position argmax keys per arrival group
+  unsigned* gcnt;                // [k][16] group arrival counters (128-byte stride)
+  unsigned* tcnt;                // [k] top arrival counters (128-byte stride)
+  unsigned* err;                 // error word
   int32_t* draft;                // [B, k]
   int64_t vtiles;                // ceil(V / 16)
 };
 
-__global__ __launch_bounds__(256) void markov_init_kernel(unsigned long long* keys, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    keys[i] = 0ull;
+constexpr unsigned kSpinLimit = 1u << 22;   // ~0.2 s of polling before giving up
+
+// final key of row b at position pos: max over the 16 group slots
+__device__ __forceinline__ unsigned long long final_key(const MarkovArgs& g, int pos, int64_t b) {
+  const unsigned long long* p = g.keys + static_cast<int64_t>(pos) * kArriveGroups * g.B + b;
+  unsigned long long k = 0ull;
+#pragma unroll
+  for (int i = 0; i < kArriveGroups; ++i) k = umax64(k, fetch_u64(p + i * g.B));
+  return k;
 }
 
-// TPW vocabulary tiles of 16 per wave; all their loads are issued before any
-// is consumed, so one pass costs about one memory round trip per wave.
-template <typename S, int RKS, int TPW>
-__global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, int pos) {
+// E fragments: markov_w1 rows of the contexts of rows b0 + (lane & 15)
+template <typename S, int RKS>
+__device__ __forceinline__ void context_frags(const MarkovArgs& g, int64_t b0, int pos, int r16,
+                                              int grp, u32x4_t (&ef)[RKS > 0 ? RKS : 1]) {
   constexpr int E = Elem<S>::PER16;
   constexpr int KS = Elem<S>::KSTEP;
   constexpr int ES = static_cast<int>(sizeof(S));
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int grp = lane >> 4;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
-  const int64_t nb = min<int64_t>(16, g.B - b0);
-
-  // Context token of A-operand row r16.
   const int64_t brow = b0 + r16;
   int32_t p = -1;
   if (brow < g.B)
-    p = pos == 0 ? g.prev[brow] : key_index(g.keys[static_cast<int64_t>(pos - 1) * g.B + brow]);
-  if (pos > 0 && blockIdx.x == 0 && threadIdx.x < 16 && brow < g.B)
-    g.draft[brow * g.k + (pos - 1)] = p;
-
-  const uint32_t wbytes = static_cast<uint32_t>(g.V * g.r * ES);
-  u32x4_t ef[RKS > 0 ? RKS : 1];
+    p = pos == 0 ? g.prev[brow] : key_index(final_key(g, pos - 1, brow));
   if constexpr (RKS > 0) {
-    const rsrc_t r1 = make_rsrc(g.w1, wbytes);
+    const rsrc_t r1 = make_rsrc(g.w1, static_cast<uint32_t>(g.V * g.r * ES));
     const bool pok = p >= 0 && static_cast<int64_t>(p) < g.V;  // out-of-range context: no bias
 #pragma unroll
     for (int c = 0; c < RKS; ++c) {
@@ -78,23 +88,191 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
                               : kOOB);
     }
   }
-  const rsrc_t r2 = make_rsrc(g.w2, wbytes);
-  // logits of this position for rows b0..b0+nb-1 (row stride k*V floats)
+}
+
+// Fold the per-lane maxima of 16 rows into the position's keys.
+__device__ __forceinline__ void publish_rows(const MarkovArgs& g, int64_t b0, int pos, int wave,
+                                             int r16, int grp, const float (&bv)[4],
+                                             const uint32_t (&bi)[4],
+                                             unsigned long long (&sk)[4][16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned long long key = bi[i] != 0xFFFFFFFFu ? pack_key(bv[i], bi[i]) : 0ull;
+    key = rowgroup_max16(key);
+    if (r16 == 0) sk[wave][4 * grp + i] = key;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const unsigned long long key = umax64(umax64(sk[0][threadIdx.x], sk[1][threadIdx.x]),
+                                          umax64(sk[2][threadIdx.x], sk[3][threadIdx.x]));
+    const int64_t b = b0 + threadIdx.x;
+    const int64_t slot = (static_cast<int64_t>(pos) * kArriveGroups + blockIdx.x % kArriveGroups) * g.B;
+    if (b < g.B && key != 0ull) atomicMax(&g.keys[slot + b], key);
+  }
+  BDR_WAIT_ALL_MEM();  // the key updates are performed before this workgroup arrives
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------------------
+// chain: persistent, all positions in one launch
+// ----------------------------------------------------------------------------
+template <typename S, int RKS>
+__global__ __launch_bounds__(256) void markov_chain_kernel(const MarkovArgs g) {
+  extern __shared__ u32x4_t w2s[];   // [tile][chunk][lane] operand chunks of markov_w2
+  constexpr int E = Elem<S>::PER16;
+  constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  constexpr int NC = RKS > 0 ? RKS : 1;
+  constexpr int TPW = 4;                      // tiles per wave per round (loads issued together)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const unsigned G = gridDim.x;
+  const int64_t t_lo = static_cast<int64_t>(blockIdx.x) * g.vtiles / G;
+  const int64_t t_hi = static_cast<int64_t>(blockIdx.x + 1) * g.vtiles / G;
+  const int ntl = static_cast<int>(t_hi - t_lo);
+
+  __shared__ unsigned long long sk[4][16];
+  __shared__ int last_flag;
+
+  // stage this workgroup's markov_w2 rows in operand layout (lane l's 16 bytes
+  // of chunk q land at w2s[q*64 + l])
+  if constexpr (RKS > 0) {
+    const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
+    for (int q = wave; q < ntl * RKS; q += 4) {
+      const int tile = q / RKS;
+      const int c = q - tile * RKS;
+      const int64_t v = (t_lo + tile) * 16 + r16;
+      const int j = c * KS + grp * E;
+      const uint32_t off = (v < g.V && j < g.r) ? static_cast<uint32_t>((v * g.r + j) * ES) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r2, (__attribute__((address_space(3))) void*)(&w2s[q * 64]), 16, off, 0, 0, 0);
+    }
+    BDR_WAIT_VM(0);
+  }
+  __syncthreads();
+
+  for (int pos = 0; pos < g.k; ++pos) {
+    for (int64_t b0 = 0; b0 < g.B; b0 += 16) {
+      u32x4_t ef[NC];
+      context_frags<S, RKS>(g, b0, pos, r16, grp, ef);
+      const int64_t nb = min<int64_t>(16, g.B - b0);
+      const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V,
+                                  static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4));
+      uint32_t zrow[4];
+      bool bok[4];
+      float bv[4];
+      uint32_t bi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = 4 * grp + i;
+        bok[i] = rb < nb;
+        zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
+        bv[i] = -INFINITY;
+        bi[i] = 0xFFFFFFFFu;
+      }
+      for (int base = wave; base < ntl; base += 4 * TPW) {
+        float zv[TPW][4];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int tile = base + 4 * u;
+          const int64_t v = (t_lo + tile) * 16 + r16;
+          const bool vok = tile < ntl && v < g.V;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            zv[u][i] = bload_f32(rz, (vok && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          const int tile = base + 4 * u;
+          if (tile < ntl) {
+            const int64_t v = (t_lo + tile) * 16 + r16;
+            f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (RKS > 0) {
+#pragma unroll
+              for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], w2s[(tile * RKS + c) * 64 + lane], bias, S());
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float s = zv[u][i] + bias[i];
+              if (v < g.V && bok[i] && s > bv[i]) {
+                bv[i] = s;
+                bi[i] = static_cast<uint32_t>(v);
+              }
+            }
+          }
+        }
+      }
+      publish_rows(g, b0, pos, wave, r16, grp, bv, bi, sk);
+    }
+
+    // grid barrier for this position; its last arriver writes the tokens
+    if (threadIdx.x == 0) {
+      last_flag = 0;
+      if (arrive_group(g.gcnt + pos * kArriveGroups * kLineWords, blockIdx.x, G))
+        last_flag = arrive_top(g.tcnt + pos * kLineWords, G) ? 1 : 0;
+      if (!last_flag && pos + 1 < g.k) {
+        const unsigned ng = arrive_groups(G);
+        unsigned it = 0;
+        while (fetch_u32(g.tcnt + pos * kLineWords) < ng) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++it > kSpinLimit) {
+            atomicOr(g.err, 1u);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (last_flag) {
+      for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x)
+        g.draft[b * g.k + pos] = key_index(final_key(g, pos, b));
+      if (pos + 1 == g.k) {  // everyone has passed every barrier: return the workspace to zero
+        __syncthreads();
+        const int64_t nkeys = static_cast<int64_t>(g.k) * kArriveGroups * g.B;
+        for (int64_t i = threadIdx.x; i < nkeys; i += blockDim.x) g.keys[i] = 0ull;
+        for (int i = threadIdx.x; i < g.k * kArriveGroups; i += blockDim.x) g.gcnt[i * kLineWords] = 0u;
+        for (int i = threadIdx.x; i < g.k; i += blockDim.x) g.tcnt[i * kLineWords] = 0u;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// passes: one launch per position
+// ----------------------------------------------------------------------------
+template <typename S, int RKS, int TPW>
+__global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, int pos) {
+  constexpr int E = Elem<S>::PER16;
+  constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  constexpr int NC = RKS > 0 ? RKS : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int64_t nb = min<int64_t>(16, g.B - b0);
+  __shared__ unsigned long long sk[4][16];
+
+  if (pos > 0 && blockIdx.x == 0 && threadIdx.x < 16 && b0 + r16 < g.B)
+    g.draft[(b0 + r16) * g.k + (pos - 1)] = key_index(final_key(g, pos - 1, b0 + r16));
+  u32x4_t ef[NC];
+  context_frags<S, RKS>(g, b0, pos, r16, grp, ef);
+
+  const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
   const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V,
                               static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4));
   uint32_t zrow[4];
   bool bok[4];
+  float bv[4];
+  uint32_t bi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rb = 4 * grp + i;
     bok[i] = rb < nb;
     zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
-  }
-
-  float bv[4];
-  uint32_t bi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
     bv[i] = -INFINITY;
     bi[i] = 0xFFFFFFFFu;
   }
@@ -102,7 +280,7 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
   const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * 4 + wave; base < g.vtiles;
        base += nw * TPW) {
-    u32x4_t wf[TPW][RKS > 0 ? RKS : 1];
+    u32x4_t wf[TPW][NC];
     float zv[TPW][4];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -137,36 +315,38 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
       }
     }
   }
-
-  __shared__ unsigned long long sk[4][16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    unsigned long long key = bi[i] != 0xFFFFFFFFu ? pack_key(bv[i], bi[i]) : 0ull;
-    key = rowgroup_max16(key);
-    if (r16 == 0) sk[wave][4 * grp + i] = key;
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    unsigned long long key = umax64(umax64(sk[0][threadIdx.x], sk[1][threadIdx.x]),
-                                    umax64(sk[2][threadIdx.x], sk[3][threadIdx.x]));
-    const int64_t b = b0 + threadIdx.x;
-    if (b < g.B && key != 0ull) atomicMax(&g.keys[static_cast<int64_t>(pos) * g.B + b], key);
-  }
+  publish_rows(g, b0, pos, wave, r16, grp, bv, bi, sk);
 }
 
-__global__ void markov_finalize_kernel(const unsigned long long* keys, int64_t B, int k,
-                                       int32_t* draft) {
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; b < B;
-       b += static_cast<int64_t>(gridDim.x) * 256)
-    draft[b * k + (k - 1)] = key_index(keys[static_cast<int64_t>(k - 1) * B + b]);
+// last position's tokens; then the keys go back to zero
+__global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs g) {
+  for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x)
+    g.draft[b * g.k + (g.k - 1)] = key_index(final_key(g, g.k - 1, b));
+  __syncthreads();
+  const int64_t nkeys = static_cast<int64_t>(g.k) * kArriveGroups * g.B;
+  for (int64_t i = threadIdx.x; i < nkeys; i += blockDim.x) g.keys[i] = 0ull;
 }
 
 // ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
 
+// keys | group counters | top counters | error word
+static size_t keys_bytes(int64_t B, int k) {
+  return align256(static_cast<size_t>(B) * k * kArriveGroups * 8);
+}
+static size_t gcnt_bytes(int k) { return align256(static_cast<size_t>(k) * kArriveGroups * 128); }
+static size_t tcnt_bytes(int k) { return align256(static_cast<size_t>(k) * 128); }
+
 size_t markov_workspace(int64_t B, int k) {
-  return align256(static_cast<size_t>(B) * static_cast<size_t>(k) * 8);
+  return keys_bytes(B, k) + gcnt_bytes(k) + tcnt_bytes(k) + 256;
+}
+
+constexpr size_t kChainLdsMax = 150 * 1024;
+
+template <typename S, int RKS>
+static void launch_chain(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((markov_chain_kernel<S, RKS>), dim3(G), dim3(256), lds, st, g);
 }
 
 template <typename S, int RKS>
@@ -176,10 +356,35 @@ static void launch_passes(const MarkovArgs& g, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>((g.B + 15) / 16));
   for (int pos = 0; pos < g.k; ++pos)
     hipLaunchKernelGGL((markov_pass_kernel<S, RKS, TPW>), grid, dim3(256), 0, st, g, pos);
+  hipLaunchKernelGGL(markov_finalize_kernel, dim3(1), dim3(256), 0, st, g);
 }
 
 template <typename S>
-static void launch_typed(const MarkovArgs& g, int rks, hipStream_t st) {
+static hipError_t launch_typed(const MarkovArgs& g, int rks, int n_cu, hipStream_t st) {
+  const unsigned G = static_cast<unsigned>(std::min<int64_t>(n_cu, g.vtiles));
+  const int64_t tiles = (g.vtiles + G - 1) / G;
+  const size_t lds = static_cast<size_t>(tiles) * std::max(rks, 1) * 64 * 16;
+  const bool chain = lds <= kChainLdsMax;
+  if (chain) {
+    static bool attr_set[9] = {};
+    hipError_t e = hipSuccess;
+    auto set = [&](const void* fn) {
+      if (!attr_set[rks]) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(kChainLdsMax));
+        attr_set[rks] = e == hipSuccess;
+      }
+    };
+    switch (rks) {
+      case 0: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 0>)); if (e) return e; launch_chain<S, 0>(g, G, lds, st); break;
+      case 1: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 1>)); if (e) return e; launch_chain<S, 1>(g, G, lds, st); break;
+      case 2: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 2>)); if (e) return e; launch_chain<S, 2>(g, G, lds, st); break;
+      case 3: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 3>)); if (e) return e; launch_chain<S, 3>(g, G, lds, st); break;
+      case 4: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 4>)); if (e) return e; launch_chain<S, 4>(g, G, lds, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
+  }
   switch (rks) {
     case 0: launch_passes<S, 0>(g, st); break;
     case 1: launch_passes<S, 1>(g, st); break;
@@ -191,11 +396,12 @@ static void launch_typed(const MarkovArgs& g, int rks, hipStream_t st) {
     case 7: launch_passes<S, 7>(g, st); break;
     default: launch_passes<S, 8>(g, st); break;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                          const void* w1, const void* w2, int rank, const int32_t* prev,
-                         int32_t* draft, void* workspace, hipStream_t stream) {
+                         int32_t* draft, void* workspace, int n_cu, hipStream_t stream) {
   MarkovArgs g{};
   g.logits = logits;
   g.B = B;
@@ -205,23 +411,18 @@ hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_d
   g.w1 = w1;
   g.w2 = w2;
   g.prev = prev;
-  g.keys = static_cast<unsigned long long*>(workspace);
+  char* ws = static_cast<char*>(workspace);
+  g.keys = reinterpret_cast<unsigned long long*>(ws);
+  g.gcnt = reinterpret_cast<unsigned*>(ws + keys_bytes(B, k));
+  g.tcnt = reinterpret_cast<unsigned*>(ws + keys_bytes(B, k) + gcnt_bytes(k));
+  g.err = reinterpret_cast<unsigned*>(ws + keys_bytes(B, k) + gcnt_bytes(k) + tcnt_bytes(k));
   g.draft = draft;
   g.vtiles = (V + 15) / 16;
   const int ks = wdt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
   const int rks = (g.r + ks - 1) / ks;
-
-  const int64_t nkeys = B * k;
-  hipLaunchKernelGGL(markov_init_kernel,
-                     dim3(static_cast<unsigned>(std::min<int64_t>((nkeys + 255) / 256, 1024))),
-                     dim3(256), 0, stream, g.keys, nkeys);
-  if (wdt == BDR_BF16)
-    launch_typed<uint16_t>(g, rks, stream);
-  else
-    launch_typed<float>(g, rks, stream);
-  hipLaunchKernelGGL(markov_finalize_kernel,
-                     dim3(static_cast<unsigned>(std::min<int64_t>((B + 255) / 256, 1024))),
-                     dim3(256), 0, stream, g.keys, B, k, draft);
+  hipError_t e = wdt == BDR_BF16 ? launch_typed<uint16_t>(g, rks, n_cu, stream)
+                                 : launch_typed<float>(g, rks, n_cu, stream);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

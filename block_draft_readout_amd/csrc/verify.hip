@@ -1,22 +1,24 @@
-// Greedy exact-match verification of a draft block (gfx950).
+// Greedy exact-match verification of a draft block (gfx950), one launch.
 //
-// Two launches:
-//   1. verify_argmax_kernel -- grid (row b*(k+1)+j, vocab chunk).  A workgroup
-//      whose position lies beyond the row's (confidence-truncated) block exits
-//      at once, so only the ragged truncated blocks are read.  The others
-//      stream their chunk of target logits with 16-byte loads, keep a running
-//      (value, index) maximum per lane, and write one packed uint64 key per
-//      (row, chunk): no atomics, no pre-zeroed memory.
-//   2. verify_scan_kernel -- one workgroup: per row, fold the chunk keys into
-//      the target argmax of each verified position, take the longest draft
-//      prefix that matches, emit the bonus token, and add the per-position
-//      accepted / proposed counts (LDS histogram, then one int64 += per
-//      position).
+// Grid (row b*(k+1)+j, vocab chunk).  A workgroup whose position lies beyond
+// the row's (confidence-truncated) block reads nothing, so only the ragged
+// truncated blocks are streamed.  The others stream their chunk of target
+// logits with 16-byte loads, keep a running (value, index) maximum per lane
+// and write one packed uint64 key per (row, chunk).  Every workgroup then
+// arrives on a counter; the last to arrive folds the chunk keys into the
+// target argmax of each verified position (one wave per row), takes the
+// longest draft prefix that matches, emits the bonus token, adds the
+// per-position accepted / proposed counts, and returns the counter to zero.
+//
 // Greedy verification emits exactly the target's own greedy tokens (llm-scaler
 // PR #620, "Summary / Quality"); the block length follows the proposer's
 // truncation by confidence (same page, DSpark port notes, dflash.py); the
 // counters are the spec-decode per-position acceptance accounting
 // (vllm-backport PR #128, "Acceptance detail").
+//
+// Workspace (zero-filled before first use; every call leaves it zeroed):
+//   keys[B*(k+1)][chunks] uint64 | 16 group counters | top counter (one
+//   128-byte line each; two-level arrival, see arrive_group)
 
 #include <algorithm>
 #include <cmath>
@@ -37,6 +39,8 @@ struct VerifyArgs {
   int chunks;
   int64_t chunk_len;             // multiple of 8 elements
   unsigned long long* part;      // [B*(k+1), chunks]
+  unsigned* gcnt;                // [16] group arrival counters (128-byte stride)
+  unsigned* tcnt;                // top arrival counter
   int32_t* block_len;
   int32_t* accepted;
   int32_t* bonus;
@@ -53,54 +57,10 @@ __device__ __forceinline__ int block_length(const VerifyArgs& g, int64_t b) {
   return g.k;
 }
 
-template <typename S, bool VEC>
-__global__ __launch_bounds__(256) void verify_argmax_kernel(const VerifyArgs g) {
-  const int64_t row = blockIdx.x;
-  const int64_t b = row / (g.k + 1);
-  const int j = static_cast<int>(row - b * (g.k + 1));
-  if (j > block_length(g, b)) return;  // same decision for the whole workgroup
-
-  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.chunk_len;
-  const int64_t c1 = std::min<int64_t>(g.V, c0 + g.chunk_len);
-  const S* y = static_cast<const S*>(g.Y) + row * g.V;
-  float bv = -INFINITY;
-  uint32_t bi = 0xFFFFFFFFu;
-  if constexpr (VEC) {
-    constexpr int E = Elem<S>::PER16;
-    for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * E; v < c1; v += 256 * E) {
-      const u32x4_t q = load16_stream(y + v);
-      const S* e = reinterpret_cast<const S*>(&q);
-#pragma unroll
-      for (int t = 0; t < E; ++t) {
-        const float f = to_f32<S>(e[t]);
-        if (f > bv) {
-          bv = f;
-          bi = static_cast<uint32_t>(v + t);
-        }
-      }
-    }
-  } else {
-    for (int64_t v = c0 + threadIdx.x; v < c1; v += 256) {
-      const float f = to_f32<S>(y[v]);
-      if (f > bv) {
-        bv = f;
-        bi = static_cast<uint32_t>(v);
-      }
-    }
-  }
-  unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
-  key = wave_max64(key);
-  __shared__ unsigned long long sk[4];
-  if ((threadIdx.x & 63) == 0) sk[threadIdx.x >> 6] = key;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    g.part[row * g.chunks + blockIdx.y] = umax64(umax64(sk[0], sk[1]), umax64(sk[2], sk[3]));
-}
-
-// 1024 threads; sequences in groups of 64: each wave folds the chunk keys of one
-// verified (sequence, position) row at a time, then one thread per sequence
-// scans its block.
-__global__ __launch_bounds__(1024) void verify_scan_kernel(const VerifyArgs g) {
+// Fold the chunk keys into target argmaxes and scan every row's block.
+// Called by one whole workgroup (sequences in groups of 64, one wave per
+// verified (sequence, position) row).
+__device__ void verify_scan(const VerifyArgs& g) {
   constexpr int GROUP = 64;
   __shared__ int32_t ts[GROUP * (BDR_MAX_K + 1)];
   __shared__ int Ls[GROUP];
@@ -126,22 +86,22 @@ __global__ __launch_bounds__(1024) void verify_scan_kernel(const VerifyArgs g) {
       if (j <= Ls[lb]) {
         const unsigned long long* pp = g.part + ((b0 + lb) * k1 + j) * g.chunks;
         unsigned long long key = 0ull;
-        for (int c = lane; c < g.chunks; c += 64) key = umax64(key, pp[c]);
+        for (int c = lane; c < g.chunks; c += 64) key = umax64(key, fetch_u64(&pp[c]));
         t = key_index(wave_max64(key));
       }
       if (lane == 0) ts[r] = t;
     }
     __syncthreads();
-    if (tid < nb) {
-      const int64_t b = b0 + tid;
-      const int L = Ls[tid];
+    for (int lb = tid; lb < nb; lb += blockDim.x) {
+      const int64_t b = b0 + lb;
+      const int L = Ls[lb];
       int a = 0;
-      while (a < L && g.draft[b * g.k + a] == ts[tid * k1 + a]) ++a;
+      while (a < L && g.draft[b * g.k + a] == ts[lb * k1 + a]) ++a;
       g.block_len[b] = L;
       g.accepted[b] = a;
-      g.bonus[b] = ts[tid * k1 + a];
+      g.bonus[b] = ts[lb * k1 + a];
       if (g.targ)
-        for (int j = 0; j <= g.k; ++j) g.targ[b * k1 + j] = ts[tid * k1 + j];
+        for (int j = 0; j <= g.k; ++j) g.targ[b * k1 + j] = ts[lb * k1 + j];
       for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
       for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
     }
@@ -151,6 +111,64 @@ __global__ __launch_bounds__(1024) void verify_scan_kernel(const VerifyArgs g) {
     if (g.acc) g.acc[tid] += cacc[tid];
     if (g.prop) g.prop[tid] += cprop[tid];
   }
+}
+
+template <typename S, bool VEC>
+__global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs g) {
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / (g.k + 1);
+  const int j = static_cast<int>(row - b * (g.k + 1));
+  __shared__ unsigned long long sk[4];
+  __shared__ int last;
+  if (j <= block_length(g, b)) {  // same decision for the whole workgroup
+    const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.chunk_len;
+    const int64_t c1 = std::min<int64_t>(g.V, c0 + g.chunk_len);
+    const S* y = static_cast<const S*>(g.Y) + row * g.V;
+    float bv = -INFINITY;
+    uint32_t bi = 0xFFFFFFFFu;
+    if constexpr (VEC) {
+      constexpr int E = Elem<S>::PER16;
+      for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * E; v < c1; v += 256 * E) {
+        const u32x4_t q = load16_stream(y + v);
+        const S* e = reinterpret_cast<const S*>(&q);
+#pragma unroll
+        for (int t = 0; t < E; ++t) {
+          const float f = to_f32<S>(e[t]);
+          if (f > bv) {
+            bv = f;
+            bi = static_cast<uint32_t>(v + t);
+          }
+        }
+      }
+    } else {
+      for (int64_t v = c0 + threadIdx.x; v < c1; v += 256) {
+        const float f = to_f32<S>(y[v]);
+        if (f > bv) {
+          bv = f;
+          bi = static_cast<uint32_t>(v);
+        }
+      }
+    }
+    unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+    key = wave_max64(key);
+    if ((threadIdx.x & 63) == 0) sk[threadIdx.x >> 6] = key;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      publish_u64(&g.part[row * g.chunks + blockIdx.y],
+                  umax64(umax64(sk[0], sk[1]), umax64(sk[2], sk[3])));
+  }
+  // arrive (two-level); the last workgroup to arrive runs the scan
+  if (threadIdx.x == 0) {
+    BDR_WAIT_ALL_MEM();
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned w = blockIdx.y * gridDim.x + blockIdx.x;
+    last = arrive_group(g.gcnt, w, total) && arrive_top(g.tcnt, total);
+  }
+  __syncthreads();
+  if (!last) return;
+  verify_scan(g);
+  if (threadIdx.x < kArriveGroups) g.gcnt[threadIdx.x * kLineWords] = 0u;
+  if (threadIdx.x == 0) *g.tcnt = 0u;
 }
 
 // ----------------------------------------------------------------------------
@@ -175,8 +193,10 @@ int verify_chunks(int64_t B, int k, int64_t V) {
   return c;
 }
 
+// keys | group counters (16 x 128 B) | top counter
 size_t verify_workspace(int64_t B, int k, int64_t V) {
-  return align256(static_cast<size_t>(B) * (k + 1) * verify_chunks(B, k, V) * 8);
+  return align256(static_cast<size_t>(B) * (k + 1) * verify_chunks(B, k, V) * 8) +
+         kArriveGroups * 128 + 256;
 }
 
 hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
@@ -195,6 +215,9 @@ hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t 
   g.use_conf = (conf != nullptr && !std::isnan(threshold)) ? 1 : 0;
   chunk_plan(B, k, V, &g.chunks, &g.chunk_len);
   g.part = static_cast<unsigned long long*>(workspace);
+  char* cnt = static_cast<char*>(workspace) + align256(static_cast<size_t>(B) * (k + 1) * g.chunks * 8);
+  g.gcnt = reinterpret_cast<unsigned*>(cnt);
+  g.tcnt = reinterpret_cast<unsigned*>(cnt + kArriveGroups * 128);
   g.block_len = block_len;
   g.accepted = accepted;
   g.bonus = bonus;
@@ -204,16 +227,15 @@ hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t 
   const dim3 grid(static_cast<unsigned>(B * (k + 1)), static_cast<unsigned>(g.chunks));
   if (dt == BDR_BF16) {
     if (V % 8 == 0)
-      hipLaunchKernelGGL((verify_argmax_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((verify_kernel<uint16_t, true>), grid, dim3(256), 0, stream, g);
     else
-      hipLaunchKernelGGL((verify_argmax_kernel<uint16_t, false>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((verify_kernel<uint16_t, false>), grid, dim3(256), 0, stream, g);
   } else {
     if (V % 4 == 0)
-      hipLaunchKernelGGL((verify_argmax_kernel<float, true>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((verify_kernel<float, true>), grid, dim3(256), 0, stream, g);
     else
-      hipLaunchKernelGGL((verify_argmax_kernel<float, false>), grid, dim3(256), 0, stream, g);
+      hipLaunchKernelGGL((verify_kernel<float, false>), grid, dim3(256), 0, stream, g);
   }
-  hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(1024), 0, stream, g);
   return hipGetLastError();
 }
 

@@ -13,6 +13,11 @@
  *   - Tensor arguments are DEVICE pointers to row-major, contiguous memory owned
  *     by the caller, 16-byte aligned; workspaces are 256-byte aligned.  The
  *     library never allocates or frees device memory and never synchronises.
+ *   - Workspaces hold cross-workgroup counters and argmax keys: a workspace
+ *     must be zero-filled once before its first use, and every call that
+ *     completes leaves it zero-filled again (except the Markov error word
+ *     below), so it can be reused by later calls and by graph replays.  One
+ *     workspace must not be used by two calls that can run concurrently.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream); all work is
  *     enqueued on it in order, so calls on one stream see each other's results.
  *   - A call with no work (rows == 0 or batch == 0) returns BDR_OK after
@@ -128,7 +133,13 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size,
  *               0 <= r <= BDR_MAX_RANK, r % 8 == 0 (bf16) or r % 4 == 0 (f32)
  *   prev_token  [B] int32, the accepted bonus token of the previous step
  *   draft_tokens[B, k] int32 out
- *   workspace   >= dspark_markov_workspace_bytes(B, k)
+ *   workspace   >= dspark_markov_workspace_bytes(B, k).  When markov_w2's
+ *               per-compute-unit slice fits in LDS, all k positions run in one
+ *               persistent launch whose workgroups meet at a grid barrier; if
+ *               the workgroups cannot all be resident the bounded wait gives up
+ *               and sets the uint32 error word that starts the last 256 bytes
+ *               of dspark_markov_workspace_bytes(B, k) (the tokens are then
+ *               invalid).
  * ------------------------------------------------------------------------- */
 size_t dspark_markov_workspace_bytes(int64_t batch, int k);
 int dspark_markov_argmax(const float* logits, int64_t batch, int k,

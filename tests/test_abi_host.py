@@ -50,12 +50,16 @@ def test_version(L):
 
 def test_workspace_sizes(L):
     from block_draft_readout_amd import _abi
-    assert L.dspark_markov_workspace_bytes(16, 8) == 1024
-    assert L.dspark_markov_workspace_bytes(1, 7) == 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    # keys [k][16 groups][B] uint64 | group counters [k][16] | top counters [k]
+    # (one 128-byte line per counter) | a 256-byte error block
+    markov = lambda B, k: a256(8 * 16 * B * k) + a256(128 * 16 * k) + a256(128 * k) + 256
+    assert L.dspark_markov_workspace_bytes(16, 8) == markov(16, 8)
+    assert L.dspark_markov_workspace_bytes(1, 7) == markov(1, 7)
     V = 151936
     with_logits = L.dspark_draft_workspace_bytes(16, 8, V, 1)
-    assert with_logits == 1024 + 16 * 8 * V * 4
-    assert L.dspark_draft_workspace_bytes(16, 8, V, 0) == 1024
+    assert with_logits == markov(16, 8) + a256(16 * 8 * V * 4)
+    assert L.dspark_draft_workspace_bytes(16, 8, V, 0) == markov(16, 8)
     v = L.spec_verify_workspace_bytes(16, 8, V)
     assert v > 0 and v % 256 == 0
     # fc: split-K partials only when K is split

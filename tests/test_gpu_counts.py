@@ -34,7 +34,7 @@ def test_adaptive_counts_over_1000_steps():
     prop_g = torch.zeros(w.k, dtype=torch.int64, device="cuda")
     acc_o = np.zeros(w.k, np.int64)
     prop_o = np.zeros(w.k, np.int64)
-    ws = torch.empty(bdr.workspace_bytes("verify", batch=w.batch, k=w.k, vocab=w.vocab) + 256,
+    ws = torch.zeros(bdr.workspace_bytes("verify", batch=w.batch, k=w.k, vocab=w.vocab) + 256,
                      dtype=torch.uint8, device="cuda")
     t0 = time.time()
     for step in range(steps):

@@ -285,3 +285,98 @@ def test_sentinel_outputs_all_written_and_deterministic():
         outs.append((out.clone(), logits.clone(), dd.clone()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)          # bitwise identical run to run
+
+
+def test_workspace_reuse_and_restored_to_zero():
+    """One zero-filled workspace per entry point reused across calls with
+    different inputs gives the results of fresh workspaces, and is left zeroed."""
+    w = MID["mid_bf16"]
+    W, _ = _data(w)
+    m = bdr()
+    ws_fc = torch.zeros(m.workspace_bytes("fc", rows=w.rows, hidden=w.hidden, n_taps=w.n_taps,
+                                          dtype=m.BDR_BF16) + 256, dtype=torch.uint8, device="cuda")
+    ws_dr = torch.zeros(m.workspace_bytes("draft", batch=w.batch, k=w.k, vocab=w.vocab) + 256,
+                        dtype=torch.uint8, device="cuda")
+    ws_v = torch.zeros(m.workspace_bytes("verify", batch=w.batch, k=w.k, vocab=w.vocab) + 256,
+                       dtype=torch.uint8, device="cuda")
+    for step in range(3):
+        s = synth.make_step(w, step)
+        F1 = m.dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]), workspace=ws_fc)
+        F2 = m.dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]))
+        d1 = m.dspark_draft_block(dev(s["draft_hidden"]), dev(W["lm_w"]), dev(W["w1"]),
+                                  dev(W["w2"]), dev(s["prev0"]), workspace=ws_dr)
+        d2 = m.dspark_draft_block(dev(s["draft_hidden"]), dev(W["lm_w"]), dev(W["w1"]),
+                                  dev(W["w2"]), dev(s["prev0"]))
+        Y = synth.plant_targets(w, step, s["noise"], d2.cpu().numpy())["target_logits"]
+        r1 = m.spec_verify_greedy(dev(Y), d1, workspace=ws_v)
+        r2 = m.spec_verify_greedy(dev(Y), d2)
+        torch.cuda.synchronize()
+        assert torch.equal(F1, F2) and torch.equal(d1, d2)
+        for key in r2:
+            assert torch.equal(r1[key], r2[key]), key
+    # keys, barrier counter and error word are back at zero; the draft workspace
+    # holds the logits first, the verify workspace ends with its counter block
+    for t in (ws_fc, ws_dr, ws_v):
+        assert t.data_ptr() % 256 == 0
+    logits_bytes = (w.batch * w.k * w.vocab * 4 + 255) // 256 * 256
+    need_dr = m.workspace_bytes("draft", batch=w.batch, k=w.k, vocab=w.vocab)
+    assert int(ws_dr[logits_bytes:need_dr].count_nonzero()) == 0
+    need_v = m.workspace_bytes("verify", batch=w.batch, k=w.k, vocab=w.vocab)
+    assert int(ws_v[need_v - 256 - 16 * 128:need_v].count_nonzero()) == 0
+
+
+def test_graph_replay_matches_eager():
+    """A HIP graph of the whole step replayed several times, with eager work in
+    between, reproduces the eager results every time."""
+    w = MID["mid_bf16"]
+    W, s = _data(w)
+    m = bdr()
+    gW = {k: dev(v) for k, v in W.items()}
+    taps = [dev(t) for t in s["taps"]]
+    hid, prev = dev(s["draft_hidden"]), dev(s["prev0"])
+    Yd = dev(synth.plant_targets(w, 0, s["noise"], synth.random_drafts(w, 0))["target_logits"])
+    F = torch.empty((w.rows, w.hidden), dtype=torch.bfloat16, device="cuda")
+    d = torch.empty((w.batch, w.k), dtype=torch.int32, device="cuda")
+    out = {"block_len": torch.empty(w.batch, dtype=torch.int32, device="cuda"),
+           "accepted": torch.empty(w.batch, dtype=torch.int32, device="cuda"),
+           "bonus": torch.empty(w.batch, dtype=torch.int32, device="cuda"),
+           "target_argmax": torch.empty((w.batch, w.k + 1), dtype=torch.int32, device="cuda")}
+    acc = torch.zeros(w.k, dtype=torch.int64, device="cuda")
+    ws = {k: torch.zeros(m.workspace_bytes(k, **a) + 256, dtype=torch.uint8, device="cuda")
+          for k, a in (("fc", dict(rows=w.rows, hidden=w.hidden, n_taps=w.n_taps, dtype=m.BDR_BF16)),
+                       ("draft", dict(batch=w.batch, k=w.k, vocab=w.vocab)),
+                       ("verify", dict(batch=w.batch, k=w.k, vocab=w.vocab)))}
+
+    def step():
+        m.dflash_fuse_fc(taps, gW["fc_w"], out=F, workspace=ws["fc"])
+        m.dspark_draft_block(hid, gW["lm_w"], gW["w1"], gW["w2"], prev, draft_tokens=d,
+                             workspace=ws["draft"])
+        m.spec_verify_greedy(Yd, d, accept_counts=acc, out=out, workspace=ws["verify"])
+
+    step()
+    torch.cuda.synchronize()
+    eager = [F.clone(), d.clone()] + [out[k].clone() for k in sorted(out)]
+    acc_eager = acc.clone()
+    g = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_cap):
+        step()                                   # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(s_cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in [F, d] + list(out.values()):
+            t.fill_(-3) if t.dtype == torch.int32 else t.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [F, d] + [out[k] for k in sorted(out)]
+        for a, b in zip(got, eager):
+            assert torch.equal(a, b), f"replay {rep}"
+        # eager work between replays
+        step()
+        torch.cuda.synchronize()
+    # counts: eager once + warm-up + 4 replays + 4 eager = 10 accumulations
+    assert torch.equal(acc, acc_eager * 10)
