@@ -116,14 +116,13 @@ __device__ __forceinline__ void publish_rows(const MarkovArgs& g, int64_t b0, in
 // ----------------------------------------------------------------------------
 // chain: persistent, all positions in one launch
 // ----------------------------------------------------------------------------
-template <typename S, int RKS>
+template <typename S, int RKS, int MAXT>
 __global__ __launch_bounds__(256) void markov_chain_kernel(const MarkovArgs g) {
   extern __shared__ u32x4_t w2s[];   // [tile][chunk][lane] operand chunks of markov_w2
   constexpr int E = Elem<S>::PER16;
   constexpr int KS = Elem<S>::KSTEP;
   constexpr int ES = static_cast<int>(sizeof(S));
   constexpr int NC = RKS > 0 ? RKS : 1;
-  constexpr int TPW = 4;                      // tiles per wave per round (loads issued together)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(256) void markov_chain_kernel(const MarkovArgs g) {
   const unsigned G = gridDim.x;
   const int64_t t_lo = static_cast<int64_t>(blockIdx.x) * g.vtiles / G;
   const int64_t t_hi = static_cast<int64_t>(blockIdx.x + 1) * g.vtiles / G;
-  const int ntl = static_cast<int>(t_hi - t_lo);
+  const int ntl = static_cast<int>(t_hi - t_lo);   // wave w owns tiles w, w+4, ... (< 4*MAXT)
 
   __shared__ unsigned long long sk[4][16];
   __shared__ int last_flag;
@@ -153,60 +152,62 @@ __global__ __launch_bounds__(256) void markov_chain_kernel(const MarkovArgs g) {
   }
   __syncthreads();
 
+  // logits of position pos, rows b0.., for this wave's tiles
+  float zv[MAXT][4];
+  auto load_z = [&](int pos, int64_t b0) {
+    const int64_t nb = min<int64_t>(16, g.B - b0);
+    const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V,
+                                static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4));
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int tile = wave + 4 * u;
+      const int64_t v = (t_lo + tile) * 16 + r16;
+      const bool vok = tile < ntl && v < g.V;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = 4 * grp + i;
+        zv[u][i] = bload_f32(rz, (vok && rb < nb)
+                                     ? static_cast<uint32_t>((rb * g.k * g.V + v) * 4)
+                                     : kOOB);
+      }
+    }
+  };
+
   for (int pos = 0; pos < g.k; ++pos) {
     for (int64_t b0 = 0; b0 < g.B; b0 += 16) {
+      load_z(pos, b0);  // independent of the context: in flight while the context is fetched
       u32x4_t ef[NC];
       context_frags<S, RKS>(g, b0, pos, r16, grp, ef);
       const int64_t nb = min<int64_t>(16, g.B - b0);
-      const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V,
-                                  static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4));
-      uint32_t zrow[4];
-      bool bok[4];
       float bv[4];
       uint32_t bi[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rb = 4 * grp + i;
-        bok[i] = rb < nb;
-        zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
         bv[i] = -INFINITY;
         bi[i] = 0xFFFFFFFFu;
       }
-      for (int base = wave; base < ntl; base += 4 * TPW) {
-        float zv[TPW][4];
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tile = base + 4 * u;
+      for (int u = 0; u < MAXT; ++u) {
+        const int tile = wave + 4 * u;
+        if (tile < ntl) {
           const int64_t v = (t_lo + tile) * 16 + r16;
-          const bool vok = tile < ntl && v < g.V;
+          f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (RKS > 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            zv[u][i] = bload_f32(rz, (vok && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
-        }
+            for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], w2s[(tile * RKS + c) * 64 + lane], bias, S());
+          }
 #pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tile = base + 4 * u;
-          if (tile < ntl) {
-            const int64_t v = (t_lo + tile) * 16 + r16;
-            f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (RKS > 0) {
-#pragma unroll
-              for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], w2s[(tile * RKS + c) * 64 + lane], bias, S());
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float s = zv[u][i] + bias[i];
-              if (v < g.V && bok[i] && s > bv[i]) {
-                bv[i] = s;
-                bi[i] = static_cast<uint32_t>(v);
-              }
+          for (int i = 0; i < 4; ++i) {
+            const float s = zv[u][i] + bias[i];
+            if (v < g.V && 4 * grp + i < nb && s > bv[i]) {
+              bv[i] = s;
+              bi[i] = static_cast<uint32_t>(v);
             }
           }
         }
       }
       publish_rows(g, b0, pos, wave, r16, grp, bv, bi, sk);
     }
-
     // grid barrier for this position; its last arriver writes the tokens
     if (threadIdx.x == 0) {
       last_flag = 0;
@@ -344,9 +345,30 @@ size_t markov_workspace(int64_t B, int k) {
 
 constexpr size_t kChainLdsMax = 150 * 1024;
 
+template <typename S, int RKS, int MAXT>
+static hipError_t launch_chain_t(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kChainLdsMax));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT>), dim3(G), dim3(256), lds, st, g);
+  return hipSuccess;
+}
+
+// MAXT: 16-entry vocabulary tiles per wave (the workgroup's tiles / 4, rounded up)
 template <typename S, int RKS>
-static void launch_chain(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((markov_chain_kernel<S, RKS>), dim3(G), dim3(256), lds, st, g);
+static hipError_t launch_chain(const MarkovArgs& g, unsigned G, size_t lds, int64_t tiles_per_wg,
+                               hipStream_t st) {
+  const int64_t per_wave = (tiles_per_wg + 3) / 4;
+  if (per_wave <= 2) return launch_chain_t<S, RKS, 2>(g, G, lds, st);
+  if (per_wave <= 4) return launch_chain_t<S, RKS, 4>(g, G, lds, st);
+  if (per_wave <= 8) return launch_chain_t<S, RKS, 8>(g, G, lds, st);
+  if (per_wave <= 12) return launch_chain_t<S, RKS, 12>(g, G, lds, st);
+  return launch_chain_t<S, RKS, 16>(g, G, lds, st);
 }
 
 template <typename S, int RKS>
@@ -361,29 +383,18 @@ static void launch_passes(const MarkovArgs& g, hipStream_t st) {
 
 template <typename S>
 static hipError_t launch_typed(const MarkovArgs& g, int rks, int n_cu, hipStream_t st) {
-  const unsigned G = static_cast<unsigned>(std::min<int64_t>(n_cu, g.vtiles));
+  const unsigned G = static_cast<unsigned>(std::min<int64_t>(std::max(n_cu, 1), g.vtiles));
   const int64_t tiles = (g.vtiles + G - 1) / G;
-  const size_t lds = static_cast<size_t>(tiles) * std::max(rks, 1) * 64 * 16;
-  const bool chain = lds <= kChainLdsMax;
-  if (chain) {
-    static bool attr_set[9] = {};
-    hipError_t e = hipSuccess;
-    auto set = [&](const void* fn) {
-      if (!attr_set[rks]) {
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(kChainLdsMax));
-        attr_set[rks] = e == hipSuccess;
-      }
-    };
+  const size_t lds = static_cast<size_t>(tiles) * rks * 64 * 16;
+  if (lds <= kChainLdsMax && tiles <= 64) {
     switch (rks) {
-      case 0: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 0>)); if (e) return e; launch_chain<S, 0>(g, G, lds, st); break;
-      case 1: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 1>)); if (e) return e; launch_chain<S, 1>(g, G, lds, st); break;
-      case 2: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 2>)); if (e) return e; launch_chain<S, 2>(g, G, lds, st); break;
-      case 3: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 3>)); if (e) return e; launch_chain<S, 3>(g, G, lds, st); break;
-      case 4: set(reinterpret_cast<const void*>(&markov_chain_kernel<S, 4>)); if (e) return e; launch_chain<S, 4>(g, G, lds, st); break;
-      default: return hipErrorInvalidValue;
+      case 0: return launch_chain<S, 0>(g, G, lds, tiles, st);
+      case 1: return launch_chain<S, 1>(g, G, lds, tiles, st);
+      case 2: return launch_chain<S, 2>(g, G, lds, tiles, st);
+      case 3: return launch_chain<S, 3>(g, G, lds, tiles, st);
+      case 4: return launch_chain<S, 4>(g, G, lds, tiles, st);
+      default: break;  // larger fp32 ranks: per-position launches
     }
-    return hipSuccess;
   }
   switch (rks) {
     case 0: launch_passes<S, 0>(g, st); break;

@@ -58,18 +58,18 @@ __device__ __forceinline__ int block_length(const VerifyArgs& g, int64_t b) {
 }
 
 // Fold the chunk keys into target argmaxes and scan every row's block.
-// Called by one whole workgroup (sequences in groups of 64, one wave per
-// verified (sequence, position) row).
+// Called by one whole workgroup, sequences in groups of 64: every thread
+// fetches up to FETCH (row, chunk) keys at once and folds them with an LDS
+// atomic max, then one thread per sequence scans its block.
 __device__ void verify_scan(const VerifyArgs& g) {
   constexpr int GROUP = 64;
-  __shared__ int32_t ts[GROUP * (BDR_MAX_K + 1)];
+  constexpr int FETCH = 8;
+  __shared__ unsigned long long tk[GROUP * (BDR_MAX_K + 1)];
   __shared__ int Ls[GROUP];
   __shared__ int cacc[BDR_MAX_K];
   __shared__ int cprop[BDR_MAX_K];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
+  const int nthr = blockDim.x;
   const int k1 = g.k + 1;
   if (tid < BDR_MAX_K) {
     cacc[tid] = 0;
@@ -78,30 +78,37 @@ __device__ void verify_scan(const VerifyArgs& g) {
   for (int64_t b0 = 0; b0 < g.B; b0 += GROUP) {
     const int nb = static_cast<int>(min<int64_t>(GROUP, g.B - b0));
     if (tid < nb) Ls[tid] = block_length(g, b0 + tid);
+    for (int r = tid; r < nb * k1; r += nthr) tk[r] = 0ull;
     __syncthreads();
-    for (int r = wave; r < nb * k1; r += nwaves) {
-      const int lb = r / k1;
-      const int j = r - lb * k1;
-      int32_t t = -1;
-      if (j <= Ls[lb]) {
-        const unsigned long long* pp = g.part + ((b0 + lb) * k1 + j) * g.chunks;
-        unsigned long long key = 0ull;
-        for (int c = lane; c < g.chunks; c += 64) key = umax64(key, fetch_u64(&pp[c]));
-        t = key_index(wave_max64(key));
+    const int total = nb * k1 * g.chunks;   // (row, chunk) pairs of this group
+    const unsigned long long* base = g.part + b0 * k1 * g.chunks;
+    for (int i0 = tid; i0 < total; i0 += nthr * FETCH) {
+      unsigned long long kv[FETCH];
+#pragma unroll
+      for (int u = 0; u < FETCH; ++u) {
+        const int i = i0 + u * nthr;
+        const int r = i / g.chunks;
+        kv[u] = 0ull;
+        if (i < total && (r % k1) <= Ls[r / k1]) kv[u] = fetch_u64(base + i);
       }
-      if (lane == 0) ts[r] = t;
+#pragma unroll
+      for (int u = 0; u < FETCH; ++u) {
+        const int i = i0 + u * nthr;
+        if (i < total && kv[u] != 0ull) atomicMax(&tk[i / g.chunks], kv[u]);
+      }
     }
     __syncthreads();
-    for (int lb = tid; lb < nb; lb += blockDim.x) {
+    for (int lb = tid; lb < nb; lb += nthr) {
       const int64_t b = b0 + lb;
       const int L = Ls[lb];
+      auto tok = [&](int j) { return j <= L ? key_index(tk[lb * k1 + j]) : -1; };
       int a = 0;
-      while (a < L && g.draft[b * g.k + a] == ts[lb * k1 + a]) ++a;
+      while (a < L && g.draft[b * g.k + a] == tok(a)) ++a;
       g.block_len[b] = L;
       g.accepted[b] = a;
-      g.bonus[b] = ts[lb * k1 + a];
+      g.bonus[b] = tok(a);
       if (g.targ)
-        for (int j = 0; j <= g.k; ++j) g.targ[b * k1 + j] = ts[lb * k1 + j];
+        for (int j = 0; j <= g.k; ++j) g.targ[b * k1 + j] = tok(j);
       for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
       for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
     }
