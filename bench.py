@@ -34,10 +34,14 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "gemm_wg3.hip",
+                "bdr_device.h", "bdr_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the sources that define the LM-head GEMM kernel."""
+    """Hash of the sources that define the LM-head GEMM kernels."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "bdr_device.h", "bdr_internal.h"):
+    for f in GEMM_SOURCES:
         with open(os.path.join(ROOT, "block_draft_readout_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -63,13 +67,14 @@ class Step:
     def __init__(self, L, w, dt, g, slot, bufs, stream):
         self.L, self.w, self.dt, self.g, self.s, self.b = L, w, dt, g, slot, bufs
         self.stream = stream
+        self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
 
     def fc(self):
         w, b = self.w, self.b
         return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
                                      self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
-                                     b["ws_fc"], b["ws_fc_n"], self.stream)
+                                     b["ws_fc"], b["ws_fc_n"], self.fc_stream)
 
     def lm_head(self):
         w = self.w
@@ -144,6 +149,10 @@ def main():
     ap.add_argument("--workload", default="qwen27b_b1")
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--graph", action="store_true", help="replay HIP graphs of whole steps")
+    ap.add_argument("--overlap", choices=("none", "lm", "chain"), default="none",
+                    help="run the fc on a second stream, concurrently with the LM head "
+                         "(lm) or with the Markov chain and verification (chain); the fc "
+                         "output feeds the next step's drafter, not S2-S4 of this step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
@@ -225,11 +234,33 @@ def main():
                      "Y": Y, "conf": conf}
     log(f"pool of {args.pool} steps ready in {time.time() - t0:.1f}s")
 
+    stream2 = torch.cuda.Stream(dev)          # default priority
+    s2ptr = C.c_void_p(stream2.cuda_stream)
+    ev_fork = torch.cuda.Event()
+    ev_join = torch.cuda.Event()
+
     def run_step(st):
+        if args.overlap == "none":
+            check(st.fc(), "dflash_fuse_fc")
+            check(st.lm_head(), "dspark_lm_head")
+            check(st.markov(), "dspark_markov_argmax")
+            check(st.verify(), "spec_verify_greedy")
+            return
+        main = torch.cuda.current_stream(dev)
+        fc_ptr = st.fc_stream
+        st.fc_stream = s2ptr
+        if args.overlap == "chain":
+            check(st.lm_head(), "dspark_lm_head")
+        ev_fork.record(main)
+        stream2.wait_event(ev_fork)
         check(st.fc(), "dflash_fuse_fc")
-        check(st.lm_head(), "dspark_lm_head")
+        ev_join.record(stream2)
+        if args.overlap == "lm":
+            check(st.lm_head(), "dspark_lm_head")
         check(st.markov(), "dspark_markov_argmax")
         check(st.verify(), "spec_verify_greedy")
+        main.wait_event(ev_join)
+        st.fc_stream = fc_ptr
 
     graphs = None
     if args.graph:
@@ -241,9 +272,9 @@ def main():
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
                 cs = C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-                st.stream = cs
+                st.stream = st.fc_stream = cs
                 run_step(st)
-            st.stream = sptr
+            st.stream = st.fc_stream = sptr
             graphs.append(gr)
 
     def step_i(i):
@@ -282,6 +313,23 @@ def main():
     torch.cuda.synchronize()
     lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    # phase 3: per-stage times (one stage at a time, events on the launch stream)
+    stage_fns = (("fc", "fc"), ("lm_head", "lm_head"), ("markov", "markov"), ("verify", "verify"))
+    sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in stage_fns] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        st = slots[i % len(slots)]
+        for j, (_, fn) in enumerate(stage_fns):
+            sev[i][j][0].record(stream)
+            check(getattr(st, fn)(), fn)
+            sev[i][j][1].record(stream)
+    torch.cuda.synchronize()
+    stages_us = {name: round(float(np.mean([sev[i][j][0].elapsed_time(sev[i][j][1])
+                                            for i in range(args.steps)])) * 1e3, 1)
+                 for j, (name, _) in enumerate(stage_fns)}
+    log(f"stages (us): {stages_us}")
+
     lm_bytes = V * H * (2 if w.dtype == "bf16" else 4) + B * k * H * (2 if w.dtype == "bf16" else 4) \
         + B * k * V * 4
     achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
@@ -319,12 +367,15 @@ def main():
         "config": {"workload": w.describe(), "batch": B, "k": k, "hidden": H, "vocab": V,
                    "rank": w.rank, "n_taps": w.n_taps,
                    "launch": "hip-graph" if graphs is not None else "eager",
+                   "fc_overlap": args.overlap,
                    "pool_steps": args.pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "ws_gemm_kernel (LM head)", "avg_launch_us": lm_ms * 1e3,
+                     "kernel": "LM-head weight-streaming GEMM (dspark_lm_head)",
+                     "avg_launch_us": lm_ms * 1e3,
                      "algorithmic_bytes_per_launch": lm_bytes},
+        "stages_us": stages_us,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -17,10 +17,12 @@ template <typename S> struct Elem;
 template <> struct Elem<uint16_t> {  // bfloat16 bit patterns
   static constexpr int PER16 = 8;
   static constexpr int KSTEP = 32;
+  static constexpr int MFMA_PER16 = 1;   // MFMA instructions per 16-byte operand chunk
 };
 template <> struct Elem<float> {
   static constexpr int PER16 = 4;
   static constexpr int KSTEP = 16;
+  static constexpr int MFMA_PER16 = 4;
 };
 
 // ----------------------------------------------------------------------------

@@ -22,31 +22,10 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "bdr_device.h"
-#include "bdr_internal.h"
+#include "gemm_kernels.h"
 
 namespace bdr {
 
-struct GemmArgs {
-  const void* a[BDR_MAX_TAPS];  // A segments, each [M, seg]
-  int64_t seg;
-  int64_t M, N, K;              // K = n_seg * seg
-  const void* w;                // [N, K]
-  void* out;                    // final [M, N] or fp32 partials [ksplit, M, N]
-  int out_kind;                 // OutKind of a final output
-  int partial;                  // 1: write fp32 partials indexed by blockIdx.y
-  int64_t steps_per_split;      // K steps handled by one workgroup along K
-};
-
-// Segment base pointer chosen with scalar selects (t is uniform), so the
-// pointer array is never indexed dynamically.
-__device__ __forceinline__ const void* seg_base(const GemmArgs& g, int t) {
-  const void* p = g.a[0];
-#pragma unroll
-  for (int c = 1; c < BDR_MAX_TAPS; ++c)
-    if (t == c) p = g.a[c];
-  return p;
-}
 
 template <typename S, int MT, int JN, int PF>
 __global__ __launch_bounds__(64) void ws_gemm_kernel(const GemmArgs g) {
@@ -168,22 +147,7 @@ constexpr int kKBB = 1024;            // bytes of each W row per visit
 constexpr int kPadRow = kKBB + 16;    // LDS row stride (breaks bank aliasing)
 constexpr int kStreamTiles = 16;      // max 16-row tiles per workgroup
 
-struct StreamArgs {
-  GemmArgs g;
-  int64_t n_waves;      // workgroups along N (balanced row ranges)
-  int64_t kblocks;      // K blocks of kKBB bytes per row (last may be partial)
-  int64_t kb_per_split; // K blocks per workgroup along K
-};
 
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-// f(integral_constant<int, i>) for i = 0 .. N-1, every index a compile-time constant
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // NT: 16-row tiles per workgroup (compile time; the last ones may be empty)
 template <typename S, int NT>
@@ -202,6 +166,7 @@ __global__ __launch_bounds__(64) void ws_gemm_stream_kernel(const StreamArgs sa)
   const uint32_t kb_lo = static_cast<uint32_t>(blockIdx.y * sa.kb_per_split);
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
   if (ntiles <= 0 || kb_lo >= kb_hi) return;
+  const OutRef out(g, blockIdx.y);
   const uint32_t kbytes = static_cast<uint32_t>(g.K * ES);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * ES);
 
@@ -290,19 +255,12 @@ __global__ __launch_bounds__(64) void ws_gemm_stream_kernel(const StreamArgs sa)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = 4 * grp + i;
-      if (t < ntiles && m < g.M && n < n_hi) {
-        const float v = acc[t][i];
-        if (g.partial)
-          static_cast<float*>(g.out)[(static_cast<int64_t>(blockIdx.y) * g.M + m) * g.N + n] = v;
-        else if (g.out_kind == OUT_BF16)
-          static_cast<uint16_t*>(g.out)[m * g.N + n] = f32_to_bf16(v);
-        else
-          static_cast<float*>(g.out)[m * g.N + n] = v;
-      }
+      if (t < ntiles && m < out.M && n < n_hi) out.put(m, n, acc[t][i]);
     }
   });
 
 }
+
 
 // out[i] = sum_p part[p][i] in order p = 0, 1, ...; four outputs per thread,
 // all splits' loads issued before the (ordered) sums.
@@ -379,11 +337,85 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
   return true;
 }
 
+// Workgroup streaming plan (16 < M <= 160): one workgroup per compute unit
+// and K split (a single round), each walking its row range in passes of at
+// most wg_nt_max tiles (accumulator budget), rounded up to an instantiated
+// tile count.  The K split minimises the per-compute-unit cost W bytes + a
+// quarter of the A bytes re-read per pass (+ the partial-sum round trip).
+static int wg_nt_max(int mtw, bool bf16) {
+  if (!bf16) return 8;
+  return mtw == 1 ? 40 : mtw == 2 ? 20 : 12;
+}
+static int wg_nt_round(int tiles, int mtw, bool bf16) {
+  static const int kSet1[] = {8, 16, 24, 32, 40};
+  static const int kSet2[] = {8, 16, 20};
+  static const int kSet3[] = {8, 12};
+  if (!bf16) return tiles <= 8 ? 8 : 0;
+  if (mtw == 1) {
+    for (int v : kSet1) if (tiles <= v) return v;
+  } else if (mtw == 2) {
+    for (int v : kSet2) if (tiles <= v) return v;
+  } else {
+    for (int v : kSet3) if (tiles <= v) return v;
+  }
+  return 0;
+}
+
+static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allow_split,
+                           int n_seg, GemmPlan* p) {
+  const int64_t kbytes = K * esize;
+  const int64_t segbytes = kbytes / n_seg;
+  const int64_t mtiles = (M + 15) / 16;
+  if (M <= 16 || mtiles > kWgMaxTiles || kbytes % 64 != 0) return false;
+  const int mtw = static_cast<int>((mtiles + kWgWaves - 1) / kWgWaves);
+  const int kbb = kWgKBB;
+  if (n_seg > 1 && segbytes % kbb != 0) return false;
+  const bool bf16 = esize == 2;
+  const int ntmax = wg_nt_max(mtw, bf16);
+  const int64_t kblocks = (kbytes + kbb - 1) / kbb;
+  double best = 1e300;
+  int64_t best_tiles = 0;
+  for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
+    const int64_t kbps = (kblocks + ks - 1) / ks;
+    const int64_t ks_eff = (kblocks + kbps - 1) / kbps;
+    if (ks_eff > kNumCU) continue;
+    int64_t nw = std::max<int64_t>(1, kNumCU / ks_eff);
+    nw = std::min<int64_t>(nw, (N + 15) / 16);
+    const int64_t rows = (N + nw - 1) / nw;
+    const int64_t tiles = (rows + 15) / 16;
+    const int64_t npass = (tiles + ntmax - 1) / ntmax;
+    double cost = static_cast<double>(kbps) * kbb * (rows + 0.25 * M * npass);
+    if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / kNumCU;
+    if (cost < best) {
+      best = cost;
+      best_tiles = (tiles + npass - 1) / npass;
+      p->n_waves = nw;
+      p->kb_per_split = kbps;
+      p->ksplit = static_cast<int>(ks_eff);
+    }
+  }
+  p->stream = true;
+  p->wg = true;
+  p->kbb = kbb;
+  p->mtw = mtw;
+  p->kblocks = kblocks;
+  p->nt = wg_nt_round(static_cast<int>(best_tiles), mtw, bf16);
+  p->mt = static_cast<int>(mtiles);
+  p->m_groups = 1;
+  p->n_wg = p->n_waves;
+  p->workspace = p->ksplit > 1 ? align256(static_cast<size_t>(p->ksplit) * M * N * 4) : 0;
+  return p->nt > 0;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split, int n_seg) {
   GemmPlan p;
   const int ks = dt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
   const int esize = dt == BDR_BF16 ? 2 : 4;
   if (plan_stream(M, N, K, esize, allow_split, n_seg, &p)) return p;
+  {
+    GemmPlan q;
+    if (plan_stream_wg(M, N, K, esize, allow_split, n_seg, &q)) return q;
+  }
   const int64_t mtiles = std::max<int64_t>(1, (M + 15) / 16);
   if (mtiles <= 9) {
     p.mt = static_cast<int>(mtiles);
@@ -471,7 +503,14 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   const bool split = p.ksplit > 1;
   g.partial = split ? 1 : 0;
   g.out = split ? workspace : out;
-  if (p.stream) {
+  if (p.wg) {
+    const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
+    const bool bf16 = dt == BDR_BF16;
+    const hipError_t le = p.mtw == 1   ? launch_wg_mtw1(p, sa, bf16, stream)
+                          : p.mtw == 2 ? launch_wg_mtw2(p, sa, bf16, stream)
+                                       : launch_wg_mtw3(p, sa, bf16, stream);
+    if (le != hipSuccess) return le;
+  } else if (p.stream) {
     if (dt == BDR_BF16)
       launch_stream<uint16_t>(p, g, stream);
     else

@@ -1,0 +1,98 @@
+"""GPU parity of the weight-streaming GEMM (drafter fc and LM head) across the
+shapes that select each kernel variant: one to three A row tiles per wave of
+the four-wave streaming kernel, tap segments, ragged M / N / K, split K, the
+fp32 path, and the fallbacks just outside those shapes.  Compared with the
+oracle's float64 products."""
+import dataclasses
+
+import pytest
+
+import oracle
+import workloads
+from workloads import synth
+from gpu_util import REL_TOL, dev, host_bits, log, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(name, cid, base, **kw):
+    return dataclasses.replace(workloads.get(base), cid=cid, name=name, fake_layers=0,
+                               tap_layers=tuple(range(kw["n_taps"])), **kw)
+
+
+# fc rows = batch * (k + 1), LM-head rows = batch * k
+SHAPES = {
+    # fc M=144 (3 tiles / wave), LM M=128 (2 tiles / wave); 512-byte tap segments
+    "m144_seg512": _w("m144_seg512", 40, "b16", batch=16, k=8, hidden=256, n_taps=3,
+                      vocab=3001, rank=16),
+    # fc M=120 on 1 KB segments; LM M=100 with a ragged last tile and a ragged K block
+    "m100_ragged": _w("m100_ragged", 41, "b16", batch=20, k=5, hidden=512, n_taps=5,
+                      vocab=5003, rank=8),
+    # LM K = 640 bytes: one full and one partial K block
+    "m100_k640": _w("m100_k640", 42, "b16", batch=20, k=5, hidden=320, n_taps=2,
+                    vocab=4099, rank=8),
+    # fc M=36 / LM M=30: one tile per wave, two waves idle on the MFMAs
+    "m36_flashnext_like": _w("m36_flashnext_like", 43, "flashnext_b4", batch=6, k=5,
+                             hidden=512, n_taps=5, vocab=7001, rank=8),
+    # LM M=160: the largest workgroup shape; fc M=176 falls back
+    "m160": _w("m160", 44, "b16", batch=16, k=10, hidden=128, n_taps=2, vocab=2048, rank=8),
+    # ranges longer than the load ring, crossing K-block boundaries:
+    # LM M=112 over 40000 rows x 4 K blocks; LM M=30 over 60000 rows x 2 K blocks
+    "m112_v40k": _w("m112_v40k", 47, "b16", batch=16, k=7, hidden=1024, n_taps=2,
+                    vocab=40000, rank=8),
+    "m30_v60k": _w("m30_v60k", 48, "flashnext_b4", batch=6, k=5, hidden=512, n_taps=2,
+                   vocab=60000, rank=8),
+    # ranges walked in two passes: LM M=112 over 100003 rows (25 tiles per range),
+    # and fp32 LM M=40 over 40000 rows (10 tiles per range, 8 per pass)
+    "m112_v100k": _w("m112_v100k", 49, "b16", batch=16, k=7, hidden=256, n_taps=2,
+                     vocab=100003, rank=8),
+    "f32_m40_v40k": _w("f32_m40_v40k", 50, "tiny", batch=8, k=5, hidden=64, n_taps=2,
+                       vocab=40000, rank=8),
+    # fp32: fc M=42, LM M=35 on 512-byte segments
+    "f32_m42": _w("f32_m42", 45, "tiny", batch=7, k=5, hidden=128, n_taps=2, vocab=2999,
+                  rank=8),
+    # fp32: LM M=140 (3 tiles / wave) with a partial K block; fc falls back (256-byte segments)
+    "f32_m140": _w("f32_m140", 46, "tiny", batch=20, k=7, hidden=64, n_taps=2, vocab=1500,
+                   rank=8),
+}
+
+
+def _data(w):
+    return synth.make_weights(w), synth.make_step(w, 0, noise=False)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_fc_parity(name):
+    import block_draft_readout_amd as bdr
+    w = SHAPES[name]
+    W, s = _data(w)
+    log(f"fc {w.describe()} rows={w.rows}")
+    ref = oracle.fuse_fc(s["taps"], W["fc_w"], w.dtype)
+    out = bdr.dflash_fuse_fc([dev(t) for t in s["taps"]], dev(W["fc_w"]))
+    err = max_rel_err(oracle.widen(host_bits(out), w.dtype), ref)
+    log(f"  max rel err {err:.3e}")
+    assert err <= (4e-3 if w.dtype == "bf16" else REL_TOL["f32"])
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_lm_head_parity(name):
+    import block_draft_readout_amd as bdr
+    w = SHAPES[name]
+    W, s = _data(w)
+    log(f"lm head {w.describe()} rows={w.batch * w.k}")
+    ref = oracle.lm_head(s["draft_hidden"], W["lm_w"], w.dtype)
+    got = bdr.dspark_lm_head(dev(s["draft_hidden"]), dev(W["lm_w"])).cpu().numpy()
+    err = max_rel_err(got, ref)
+    log(f"  max rel err {err:.3e}")
+    assert err <= min(REL_TOL[w.dtype], 1e-3)
+
+
+def test_lm_head_repeat_is_bitwise_identical():
+    """Fixed reduction order: two launches give the same bits."""
+    import block_draft_readout_amd as bdr
+    w = SHAPES["m144_seg512"]
+    W, s = _data(w)
+    h, lw = dev(s["draft_hidden"]), dev(W["lm_w"])
+    a = bdr.dspark_lm_head(h, lw).cpu().numpy()
+    b = bdr.dspark_lm_head(h, lw).cpu().numpy()
+    assert (a.view("u4") == b.view("u4")).all()
