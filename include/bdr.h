@@ -134,12 +134,13 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size,
  *   prev_token  [B] int32, the accepted bonus token of the previous step
  *   draft_tokens[B, k] int32 out
  *   workspace   >= dspark_markov_workspace_bytes(B, k).  When markov_w2's
- *               per-compute-unit slice fits in LDS, all k positions run in one
- *               persistent launch whose workgroups meet at a grid barrier; if
- *               the workgroups cannot all be resident the bounded wait gives up
- *               and sets the uint32 error word that starts the last 256 bytes
- *               of dspark_markov_workspace_bytes(B, k) (the tokens are then
- *               invalid).
+ *               per-compute-unit slice fits in LDS and B <= 256, all k
+ *               positions run in one persistent launch whose workgroups hand
+ *               each position's maxima to one another through the workspace;
+ *               if the workgroups cannot all be resident the bounded waits give
+ *               up and set the uint32 error word that starts the last 256
+ *               bytes of dspark_markov_workspace_bytes(B, k) (the tokens are
+ *               then invalid).
  * ------------------------------------------------------------------------- */
 size_t dspark_markov_workspace_bytes(int64_t batch, int k);
 int dspark_markov_argmax(const float* logits, int64_t batch, int k,

@@ -51,9 +51,9 @@ def test_version(L):
 def test_workspace_sizes(L):
     from block_draft_readout_amd import _abi
     a256 = lambda x: (x + 255) // 256 * 256
-    # keys [k][16 groups][B] uint64 | group counters [k][16] | top counters [k]
-    # (one 128-byte line per counter) | a 256-byte error block
-    markov = lambda B, k: a256(8 * 16 * B * k) + a256(128 * 16 * k) + a256(128 * k) + 256
+    # per-position keys [k][16 groups][B] | per-workgroup slots [k][256][B] |
+    # tokens [k][B] (all uint64) | a completion-counter block | an error block
+    markov = lambda B, k: a256(8 * 16 * B * k) + a256(8 * 256 * B * k) + a256(8 * B * k) + 256 + 256
     assert L.dspark_markov_workspace_bytes(16, 8) == markov(16, 8)
     assert L.dspark_markov_workspace_bytes(1, 7) == markov(1, 7)
     V = 151936
