@@ -39,11 +39,15 @@ GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "g
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources that define the LM-head GEMM kernels."""
+    """Hash of the code (comments and whitespace removed) of the sources that
+    define the LM-head GEMM kernels."""
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "block_draft_readout_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_draft_readout_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -149,7 +153,7 @@ def main():
     ap.add_argument("--workload", default="qwen27b_b1")
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--graph", action="store_true", help="replay HIP graphs of whole steps")
-    ap.add_argument("--overlap", choices=("none", "lm", "chain"), default="none",
+    ap.add_argument("--overlap", choices=("none", "lm", "chain"), default="chain",
                     help="run the fc on a second stream, concurrently with the LM head "
                          "(lm) or with the Markov chain and verification (chain); the fc "
                          "output feeds the next step's drafter, not S2-S4 of this step")

@@ -3,21 +3,23 @@
 // Serves the drafter fc (A = the tapped hidden states, concatenated along K
 // segment by segment; W = fc.weight [H, T*H]) and the LM head (A = the block's
 // hidden states; W = [V, H]).  Both are dense contractions with few rows
-// (M = 4..144) against a large weight read exactly once, so the kernel is
+// (M = 4..144) against a large weight read exactly once, so every variant is
 // organised around streaming W from HBM:
-//   * a workgroup is one wave; it owns JN 16-column tiles of W (16*JN rows of
-//     the weight) and all MT*16 rows of A over its K range, so waves never
-//     wait on each other and all of them can be resident at once;
-//   * every lane moves 16 contiguous bytes of one W row per load, and PF
-//     steps of loads stay in flight ahead of the MFMAs that consume them;
-//   * loads are raw buffer loads: a lane whose row or K index falls outside
-//     the operand reads zeros from the hardware range check, so ragged M, N
-//     and K need no branches;
-//   * when N alone gives too few waves (the fc: N = H), K is split across
-//     workgroups too; each writes fp32 partials that a second kernel sums in a
-//     fixed order, so the result is deterministic.
-// Inputs are bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32),
-// accumulation is fp32.
+//   * ws_gemm_stream_kernel (M <= 16): one-wave workgroups, each streaming a
+//     balanced range of W rows through LDS with buffer-to-LDS loads while
+//     holding A in registers (this file);
+//   * ws_gemm_stream_wg_kernel (16 < M <= 160): four-wave workgroups sharing
+//     each W visit, A staged once per workgroup (gemm_kernels.h, instantiated
+//     in gemm_wg1/2/3.hip);
+//   * ws_gemm_kernel: a register-only fallback for the shapes the streaming
+//     kernels do not take (tap segments not a multiple of 512 bytes, M > 160);
+//   * when N alone gives too few workgroups (the fc: N = H), K is split too;
+//     partials are summed in a fixed order by splitk_reduce_kernel, so the
+//     result is deterministic.
+// Loads are raw buffer loads: a lane whose row or K index falls outside an
+// operand reads zeros from the hardware range check, so ragged M, N and K need
+// no branches.  Inputs are bf16 (v_mfma_f32_16x16x32_bf16) or fp32
+// (v_mfma_f32_16x16x4_f32); accumulation is fp32.
 
 #include <algorithm>
 #include <type_traits>
