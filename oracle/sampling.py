@@ -1,0 +1,242 @@
+"""Probabilistic drafting and rejection-sampling verification (plain CPU definitions).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke entry point and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+Sources (web pages; cited by title and section):
+  * "Qwen3.8-27B-DSpark -- vLLM-ready" model card (Doopeworld), "Usage" and
+    "Tuning notes": the recommended serving mode draws draft tokens with
+    draft_sample_method = "probabilistic" (measured faster than greedy).
+  * "Qwen4Exp DFlash drafter support" (wtdcode/vllm-backport PR #128), "Not
+    covered": speculative decoding there is verified by rejection sampling.
+The pages give no further detail, so the plain reading is taken: the standard
+speculative-sampling rule (Leviathan, Kalman and Matias, "Fast Inference from
+Transformers via Speculative Decoding", ICML 2023; Chen et al., "Accelerating
+Large Language Model Decoding with Speculative Sampling", 2023) applied to the
+DSpark draft distribution q = softmax((logits + Markov bias) / T), with the
+sampled token as the next position's Markov context, and the target
+distribution p = softmax(target logits / T).
+
+Random numbers come from Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+"Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011), a counter-based
+generator both sides implement from its published definition; a uniform is
+((x >> 9) + 0.5) * 2^-23 = (2m + 1) * 2^-24: 23 random bits, strictly inside
+(0, 1) and exactly representable in float32.  Sampling from a
+distribution with log-weights w uses the Gumbel-max rule: argmax_v w_v + G_v
+with G_v = -log(-log(u_v)).  Decisions are taken here in float64.
+
+Counter layout (word 0..3): (index // 4, row, position, stream); the key is the
+64-bit seed (low word, high word); index is the vocabulary entry (word
+index % 4 of the output) or 0 for the single acceptance uniform.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .reference import widen, markov_bias, truncate_by_confidence, _finite
+
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
+_MASK = 0xFFFFFFFF
+
+STREAM_DRAFT = 0       # Gumbel noise of the draft samples
+STREAM_ACCEPT = 1      # one uniform per (row, position) for the acceptance test
+STREAM_RESAMPLE = 2    # Gumbel noise of the residual / bonus sample
+
+
+def philox4x32(ctr: np.ndarray, key, rounds: int = 10) -> np.ndarray:
+    """Philox4x32 with ``rounds`` rounds on counters ``ctr`` [..., 4] (uint32).
+
+    One round maps (c0, c1, c2, c3) with key (k0, k1) to
+    (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)), where hi
+    and lo are the upper and lower 32 bits of the 64-bit product; the key is
+    bumped by the Weyl constants (W0, W1) before every round but the first.
+    """
+    c = np.asarray(ctr, dtype=np.uint32).astype(np.uint64)
+    c0, c1, c2, c3 = c[..., 0], c[..., 1], c[..., 2], c[..., 3]
+    k0 = np.uint64(int(key[0]) & _MASK)
+    k1 = np.uint64(int(key[1]) & _MASK)
+    m = np.uint64(_MASK)
+    for r in range(rounds):
+        if r > 0:
+            k0 = np.uint64((int(k0) + PHILOX_W0) & _MASK)
+            k1 = np.uint64((int(k1) + PHILOX_W1) & _MASK)
+        p0 = np.uint64(PHILOX_M0) * c0
+        p1 = np.uint64(PHILOX_M1) * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & m
+        hi1, lo1 = p1 >> np.uint64(32), p1 & m
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def seed_key(seed: int):
+    return (int(seed) & _MASK, (int(seed) >> 32) & _MASK)
+
+
+def to_uniform(x: np.ndarray) -> np.ndarray:
+    """((x >> 9) + 0.5) * 2^-23: 23 random bits, an odd multiple of 2^-24 (exact
+    in float32), never 0 or 1."""
+    return ((np.asarray(x, dtype=np.uint32) >> np.uint32(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+
+
+def uniforms(seed: int, stream: int, row: int, pos: int, n: int) -> np.ndarray:
+    """u[v], v < n: word v % 4 of Philox((v // 4, row, pos, stream), seed)."""
+    quads = (n + 3) // 4
+    ctr = np.zeros((quads, 4), dtype=np.uint32)
+    ctr[:, 0] = np.arange(quads, dtype=np.uint32)
+    ctr[:, 1] = np.uint32(row)
+    ctr[:, 2] = np.uint32(pos)
+    ctr[:, 3] = np.uint32(stream)
+    x = philox4x32(ctr, seed_key(seed)).reshape(-1)[:n]
+    return to_uniform(x)
+
+
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """Standard Gumbel variates -log(-log(u)) of uniforms in (0, 1)."""
+    return -np.log(-np.log(np.asarray(u, dtype=np.float64)))
+
+
+def gumbel_max(logw: np.ndarray, u: np.ndarray):
+    """Index drawn with probability proportional to exp(logw) (entries with
+    logw = -inf never drawn), and the gap between the two largest perturbed
+    keys (an exact tie gives 0).  Lowest index on exact ties."""
+    keys = np.asarray(logw, dtype=np.float64) + gumbel(u)
+    keys = np.where(np.isneginf(logw), -np.inf, keys)
+    finite = keys[np.isfinite(keys)]
+    if finite.size == 0:
+        raise ValueError("no entry with positive weight")
+    idx = int(np.flatnonzero(keys == finite.max())[0])
+    if finite.size < 2:
+        return idx, float("inf")
+    part = np.partition(finite, [finite.size - 2, finite.size - 1])
+    return idx, float(part[-1] - part[-2])
+
+
+def log_softmax(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    m = x.max()
+    return x - (m + np.log(np.sum(np.exp(x - m))))
+
+
+# ----------------------------------------------------------------------------
+# S3 (probabilistic): semi-autoregressive sampling from the biased distribution
+# ----------------------------------------------------------------------------
+
+def semi_ar_sample(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndarray],
+                   prev0: np.ndarray, dtype: str, temperature: float, seed: int):
+    """Draft tokens d [B, k], Gumbel-key gaps [B, k] and the biased logits x [B, k, V].
+
+    As the greedy chain (llm-scaler PR #620, DSpark port notes: position 0 is
+    conditioned on the accepted bonus token, each later position on the
+    previous position's draft token), except that the draft token at position
+    i is drawn from q_i = softmax(x_i / T), x_i = float32(Z_i + bias(context)),
+    by the Gumbel-max rule with noise from stream STREAM_DRAFT (row b, position
+    i).  The drawn token is the next context (model card, "Tuning notes":
+    probabilistic draft sampling).
+    """
+    if not temperature > 0:
+        raise ValueError("temperature must be positive")
+    Z = np.asarray(Z, dtype=np.float32)
+    B, k, V = Z.shape
+    prev0 = np.asarray(prev0).reshape(B)
+    use_bias = w1 is not None and w2 is not None and np.shape(w1)[-1] > 0
+    if use_bias:
+        W1, W2 = widen(w1, dtype), widen(w2, dtype)
+    d = np.zeros((B, k), dtype=np.int64)
+    gap = np.zeros((B, k), dtype=np.float64)
+    x = np.zeros((B, k, V), dtype=np.float32)
+    for b in range(B):
+        p = int(prev0[b])
+        if not 0 <= p < V:
+            raise ValueError("previous token out of range")
+        for i in range(k):
+            s = Z[b, i] + markov_bias(W1, W2, p) if use_bias else Z[b, i].copy()
+            _finite(s, "biased logits")
+            x[b, i] = s
+            u = uniforms(seed, STREAM_DRAFT, b, i, V)
+            d[b, i], gap[b, i] = gumbel_max(s.astype(np.float64) / temperature, u)
+            p = int(d[b, i])
+    return d, gap, x
+
+
+# ----------------------------------------------------------------------------
+# S4 (probabilistic): rejection-sampling verification
+# ----------------------------------------------------------------------------
+
+def verify_sample(d: np.ndarray, x: np.ndarray, Y: np.ndarray, dtype: str, L: np.ndarray,
+                  temperature: float, seed: int):
+    """Speculative-sampling verification of a drafted block, row by row.
+
+    p_i = softmax(y_i / T) (target), q_i = softmax(x_i / T) (the distribution
+    d_i was drawn from).  For i < L_b: with r = the uniform of stream
+    STREAM_ACCEPT (row b, position i), d_i is accepted iff r * q_i(d_i) <
+    p_i(d_i), i.e. with probability min(1, p_i(d_i) / q_i(d_i)).  At the first
+    rejection the emitted token is drawn from max(0, p_i - q_i) (normalised; if
+    it is zero everywhere, from p_i) and verification stops; if all L_b draft
+    tokens are accepted, the bonus token is drawn from p_{L_b}.  Both draws use
+    the Gumbel-max rule with noise of stream STREAM_RESAMPLE at that position.
+    The emitted tokens are then distributed exactly as tokens drawn from the
+    target (the losslessness of speculative sampling).  Counts as in greedy
+    verification: accepted when a_b > i, proposed when L_b > i.
+
+    Also returns, per row, the acceptance margins |r q - p| / max(p, q) of the
+    tested positions (inf where untested) and the gap of the final draw, so
+    that callers can exclude decisions that rounding could flip.
+    """
+    d = np.asarray(d, dtype=np.int64)
+    B, k = d.shape
+    V = np.shape(Y)[-1]
+    a = np.zeros(B, dtype=np.int64)
+    bonus = np.zeros(B, dtype=np.int64)
+    acc = np.zeros(k, dtype=np.int64)
+    prop = np.zeros(k, dtype=np.int64)
+    margin = np.full((B, k), np.inf)
+    draw_gap = np.zeros(B)
+    resampled = np.zeros(B, dtype=bool)
+    for b in range(B):
+        Lb = int(L[b])
+        n = 0
+        while n < Lb:
+            lp = log_softmax(widen(Y[b, n], dtype) / temperature)
+            lq = log_softmax(np.asarray(x[b, n], dtype=np.float64) / temperature)
+            pd, qd = np.exp(lp[d[b, n]]), np.exp(lq[d[b, n]])
+            r = uniforms(seed, STREAM_ACCEPT, b, n, 1)[0]
+            margin[b, n] = abs(r * qd - pd) / max(pd, qd)
+            if r * qd < pd:
+                n += 1
+                continue
+            w = np.maximum(np.exp(lp) - np.exp(lq), 0.0)
+            if w.max() > 0:
+                with np.errstate(divide="ignore"):
+                    logw = np.log(w)          # log 0 = -inf: never drawn
+            else:
+                logw = lp
+            u = uniforms(seed, STREAM_RESAMPLE, b, n, V)
+            bonus[b], draw_gap[b] = gumbel_max(logw, u)
+            resampled[b] = True
+            break
+        a[b] = n
+        if not resampled[b]:
+            lp = widen(Y[b, Lb], dtype) / temperature
+            u = uniforms(seed, STREAM_RESAMPLE, b, Lb, V)
+            bonus[b], draw_gap[b] = gumbel_max(lp, u)
+        for i in range(k):
+            acc[i] += n > i
+            prop[i] += Lb > i
+    return dict(accepted=a, bonus=bonus, accept_counts=acc, proposed_counts=prop,
+                margin=margin, draw_gap=draw_gap, resampled=resampled)
+
+
+def block_step_sample(dtype: str, Z, w1, w2, prev0, target_logits, temperature: float,
+                      seed: int, confidence=None, threshold=None):
+    """S3 + S4 of one probabilistic block-step on given draft logits Z."""
+    d, gap, x = semi_ar_sample(Z, w1, w2, prev0, dtype, temperature, seed)
+    B, k = d.shape
+    L = truncate_by_confidence(confidence, threshold, B, k)
+    out = verify_sample(d, x, target_logits, dtype, L, temperature, seed)
+    out.update(draft_tokens=d, gap=gap, draft_logits=x, block_len=L)
+    return out
