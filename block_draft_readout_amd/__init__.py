@@ -20,7 +20,8 @@ from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
 
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
-    "spec_verify_greedy", "workspace_bytes", "lib", "BdrError",
+    "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
+    "workspace_bytes", "lib", "BdrError",
 ]
 
 
@@ -83,6 +84,10 @@ def workspace_bytes(kind: str, **kw) -> int:
                                               int(kw.get("logits_in_workspace", True)))
     if kind == "verify":
         return L.spec_verify_workspace_bytes(kw["batch"], kw["k"], kw["vocab"])
+    if kind == "markov_sample":
+        return L.dspark_markov_sample_workspace_bytes(kw["batch"], kw["k"], kw["vocab"])
+    if kind == "verify_sample":
+        return L.spec_verify_sample_workspace_bytes(kw["batch"], kw["k"], kw["vocab"])
     raise ValueError(kind)
 
 
@@ -255,4 +260,108 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
                                     _ptr(res["bonus"]), _ptr(res.get("target_argmax")),
                                     _ptr(accept_counts), _ptr(proposed_counts), wp, wn,
                                     _stream(dev)))
+    return res
+
+
+# ----------------------------------------------------------------------------- sampling
+def dspark_gumbel_noise(batch: int, k: int, vocab: int, seed: int, stream_id: int = 0,
+                        out: Optional[torch.Tensor] = None, device="cuda") -> torch.Tensor:
+    """Gumbel noise [B, k, V] fp32 of a stream of the sampling path's generator."""
+    L = lib()
+    if out is None:
+        out = torch.empty((batch, k, vocab), dtype=torch.float32, device=device)
+    _dev(out, "out")
+    if out.dtype != torch.float32 or tuple(out.shape) != (batch, k, vocab):
+        raise ValueError("out must be fp32 [B, k, V]")
+    _abi.check("dspark_gumbel_noise",
+               L.dspark_gumbel_noise(batch, k, vocab, int(seed), int(stream_id), _ptr(out),
+                                     _stream(out.device)))
+    return out
+
+
+def dspark_markov_sample(logits: torch.Tensor, markov_w1: Optional[torch.Tensor],
+                         markov_w2: Optional[torch.Tensor], prev_token: torch.Tensor,
+                         temperature: float, seed: int,
+                         draft_tokens: Optional[torch.Tensor] = None,
+                         draft_logits: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Probabilistic drafting: (draft_tokens [B, k] int32, draft_logits [B, k, V] fp32).
+
+    Each position's token is drawn from softmax((logits + Markov bias) / T) and
+    becomes the next position's Markov context; draft_logits holds the biased
+    logits the tokens were drawn from (the q of rejection sampling).
+    """
+    L = lib()
+    _dev(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 3:
+        raise ValueError("logits must be fp32 [B, k, V]")
+    B, k, V = logits.shape
+    w1, w2, r = _markov_args(markov_w1, markov_w2, logits)
+    wdt = _dt(w1) if w1 is not None else BDR_F32
+    _dev(prev_token, "prev_token")
+    if prev_token.dtype != torch.int32 or prev_token.numel() != B:
+        raise ValueError("prev_token must be int32 [B]")
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, k), dtype=torch.int32, device=logits.device)
+    if draft_logits is None:
+        draft_logits = torch.empty((B, k, V), dtype=torch.float32, device=logits.device)
+    _dev(draft_tokens, "draft_tokens")
+    _dev(draft_logits, "draft_logits")
+    ws = _workspace(L.dspark_markov_sample_workspace_bytes(B, k, V), logits.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    _abi.check("dspark_markov_sample",
+               L.dspark_markov_sample(_ptr(logits), B, k, V, wdt, _ptr(w1), _ptr(w2), r,
+                                      _ptr(prev_token), float(temperature), int(seed),
+                                      _ptr(draft_tokens), _ptr(draft_logits), wp, wn,
+                                      _stream(logits.device)))
+    return draft_tokens, draft_logits
+
+
+def spec_verify_sample(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                       draft_logits: torch.Tensor, temperature: float, seed: int,
+                       confidence: Optional[torch.Tensor] = None,
+                       threshold: float = math.nan,
+                       accept_counts: Optional[torch.Tensor] = None,
+                       proposed_counts: Optional[torch.Tensor] = None,
+                       out: Optional[Dict[str, torch.Tensor]] = None,
+                       workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Rejection-sampling verification of draft_tokens [B, k] drawn from
+    draft_logits [B, k, V] against target_logits [B, k+1, V].
+
+    Returns block_len, accepted, bonus ([B] int32); accept_counts /
+    proposed_counts ([k] int64) are accumulated in place when given.
+    """
+    L = lib()
+    _dev(target_logits, "target_logits")
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _dev(draft_tokens, "draft_tokens")
+    if draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != (B, k):
+        raise ValueError("draft_tokens must be int32 [B, k]")
+    _dev(draft_logits, "draft_logits")
+    if draft_logits.dtype != torch.float32 or tuple(draft_logits.shape) != (B, k, V):
+        raise ValueError("draft_logits must be fp32 [B, k, V]")
+    if confidence is not None:
+        _dev(confidence, "confidence")
+        if confidence.dtype != torch.float32 or tuple(confidence.shape) != (B, k):
+            raise ValueError("confidence must be fp32 [B, k]")
+    for name, t in (("accept_counts", accept_counts), ("proposed_counts", proposed_counts)):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.int64 or t.numel() != k:
+                raise ValueError(f"{name} must be int64 [k]")
+    dev = target_logits.device
+    res = dict(out) if out is not None else {}
+    for name in ("block_len", "accepted", "bonus"):
+        if name not in res:
+            res[name] = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(L.spec_verify_sample_workspace_bytes(B, k, V), dev, workspace)
+    wp, wn = _ws_ptr(ws)
+    _abi.check("spec_verify_sample",
+               L.spec_verify_sample(_ptr(target_logits), _dt(target_logits), B, k, V,
+                                    _ptr(draft_tokens), _ptr(draft_logits), _ptr(confidence),
+                                    float(threshold), float(temperature), int(seed),
+                                    _ptr(res["block_len"]), _ptr(res["accepted"]),
+                                    _ptr(res["bonus"]), _ptr(accept_counts),
+                                    _ptr(proposed_counts), wp, wn, _stream(dev)))
     return res

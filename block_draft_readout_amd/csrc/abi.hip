@@ -155,7 +155,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int bdr_abi_version(void) { return 1; }
+int bdr_abi_version(void) { return 2; }
 
 const char* bdr_last_error(void) { return g_err; }
 
@@ -300,6 +300,89 @@ int spec_verify_greedy(const void* target_logits, bdr_dtype dt, int64_t batch, i
                                threshold, block_len, accepted, bonus, target_argmax,
                                accept_counts, proposed_counts, workspace, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "spec_verify_greedy launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- sampling
+int dspark_gumbel_noise(int64_t batch, int k, int64_t vocab, uint64_t seed, int stream_id,
+                        float* noise, void* stream) {
+  BDR_TRY(block_shape(batch, k, vocab));
+  if (vocab > kMaxMarkovVocab) return fail(BDR_EUNSUPPORTED, "vocab must be <= 2^21 here");
+  if (stream_id < 0) return fail(BDR_EINVAL, "stream_id must be >= 0");
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(noise, "noise", 4));
+  BDR_TRY(check_device());
+  hipError_t e = launch_gumbel_noise(noise, batch, k, vocab, seed,
+                                     static_cast<uint32_t>(stream_id), as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_gumbel_noise launch");
+  return BDR_OK;
+}
+
+static int need_temperature(float t) {
+  if (!(t > 0.f) || !std::isfinite(t)) return fail(BDR_EINVAL, "temperature must be finite and > 0");
+  if (!std::isfinite(1.0f / t)) return fail(BDR_EUNSUPPORTED, "temperature too small");
+  return BDR_OK;
+}
+
+size_t dspark_markov_sample_workspace_bytes(int64_t batch, int k, int64_t vocab) {
+  if (batch < 0 || k < 1 || k > BDR_MAX_K || vocab <= 0 || vocab > kMaxMarkovVocab) return 0;
+  return markov_sample_workspace(batch, k, vocab);
+}
+
+int dspark_markov_sample(const float* logits, int64_t batch, int k, int64_t vocab,
+                         bdr_dtype wdt, const void* markov_w1, const void* markov_w2, int rank,
+                         const int32_t* prev_token, float temperature, uint64_t seed,
+                         int32_t* draft_tokens, float* draft_logits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  BDR_TRY(block_shape(batch, k, vocab));
+  BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank, vocab, k));
+  BDR_TRY(need_temperature(temperature));
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(logits, "logits"));
+  BDR_TRY(need_ptr(prev_token, "prev_token", 4));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  BDR_TRY(need_ptr(draft_logits, "draft_logits"));
+  BDR_TRY(need_ws(workspace, workspace_bytes, markov_sample_workspace(batch, k, vocab)));
+  int cus = 0;
+  BDR_TRY(check_device(&cus));
+  hipError_t e = launch_markov_sample(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
+                                      prev_token, 1.0f / temperature, seed, draft_tokens,
+                                      draft_logits, workspace, cus, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_markov_sample launch");
+  return BDR_OK;
+}
+
+size_t spec_verify_sample_workspace_bytes(int64_t batch, int k, int64_t vocab) {
+  if (batch < 0 || k < 1 || k > BDR_MAX_K || vocab <= 0 || vocab > kMaxVocab) return 0;
+  return sample_verify_workspace(batch, k, vocab);
+}
+
+int spec_verify_sample(const void* target_logits, bdr_dtype dt, int64_t batch, int k,
+                       int64_t vocab, const int32_t* draft_tokens, const float* draft_logits,
+                       const float* confidence, float threshold, float temperature, uint64_t seed,
+                       int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                       int64_t* accept_counts, int64_t* proposed_counts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  BDR_TRY(block_shape(batch, k, vocab));
+  BDR_TRY(need_temperature(temperature));
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(target_logits, "target_logits"));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  BDR_TRY(need_ptr(draft_logits, "draft_logits"));
+  if (confidence) BDR_TRY(need_ptr(confidence, "confidence", 4));
+  BDR_TRY(need_ptr(block_len, "block_len", 4));
+  BDR_TRY(need_ptr(accepted, "accepted", 4));
+  BDR_TRY(need_ptr(bonus, "bonus", 4));
+  if (accept_counts) BDR_TRY(need_ptr(accept_counts, "accept_counts", 8));
+  if (proposed_counts) BDR_TRY(need_ptr(proposed_counts, "proposed_counts", 8));
+  BDR_TRY(need_ws(workspace, workspace_bytes, sample_verify_workspace(batch, k, vocab)));
+  BDR_TRY(check_device());
+  hipError_t e = launch_verify_sample(target_logits, dt, batch, k, vocab, draft_tokens,
+                                      draft_logits, confidence, threshold, 1.0f / temperature,
+                                      seed, block_len, accepted, bonus, accept_counts,
+                                      proposed_counts, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_verify_sample launch");
   return BDR_OK;
 }
 

@@ -47,6 +47,15 @@ __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Buffer stores: a store whose offset lies at or beyond the size is dropped.
+__device__ __forceinline__ void bstore16(f32x4_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void bstore_f32(float v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // Wait until at most n vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained), and keep the
 // scheduler from moving anything across.  Needed after buffer-to-LDS loads,
@@ -176,6 +185,50 @@ __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) k = umax64(k, __shfl_xor(k, off, 64));
   return k;
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011).  A round multiplies
+// words 0 and 2 by the two round constants, swaps the word pairs and mixes the
+// high halves of the products with the other words and the key; the key grows
+// by the two Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+// Streams of the sampling path (counter word 3).
+constexpr uint32_t kStreamDraft = 0;      // Gumbel noise of the draft draws
+constexpr uint32_t kStreamAccept = 1;     // acceptance uniform of (row, position)
+constexpr uint32_t kStreamResample = 2;   // Gumbel noise of the residual / bonus draw
+
+__device__ __forceinline__ u32x4_t philox4x32_10(u32x4_t c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(kPhiloxM0, c.x);
+    const uint32_t lo0 = kPhiloxM0 * c.x;
+    const uint32_t hi1 = __umulhi(kPhiloxM1, c.z);
+    const uint32_t lo1 = kPhiloxM1 * c.z;
+    c = u32x4_t{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return c;
+}
+
+// (2m + 1) * 2^-24 with m the top 23 bits: strictly inside (0, 1), exact in fp32.
+__device__ __forceinline__ float bits_to_uniform(uint32_t x) {
+  return static_cast<float>(x >> 9) * 0x1p-23f + 0x1p-24f;
+}
+
+// Standard Gumbel variate -log(-log(u)).  -log(u) is taken as -log1p(u - 1)
+// above 1/2 (u - 1 is exact there), where it is small and log(u) would lose
+// its relative accuracy.
+__device__ __forceinline__ float gumbel_of(float u) {
+  const float t = u >= 0.5f ? -log1pf(u - 1.0f) : -logf(u);
+  return -logf(t);
 }
 
 }  // namespace bdr

@@ -66,6 +66,24 @@ hipError_t launch_verify(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t 
                          int32_t* target_argmax, int64_t* acc, int64_t* prop,
                          void* workspace, hipStream_t stream);
 
+// ----------------------------------------------------------------------------
+// Probabilistic drafting and rejection-sampling verification.
+// ----------------------------------------------------------------------------
+// noise[(b * k + i) * V + v] = Gumbel noise of stream stream_id at (b, i, v)
+hipError_t launch_gumbel_noise(float* noise, int64_t B, int k, int64_t V, uint64_t seed,
+                               uint32_t stream_id, hipStream_t stream);
+size_t markov_sample_workspace(int64_t B, int k, int64_t V);
+hipError_t launch_markov_sample(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
+                                const void* w1, const void* w2, int rank, const int32_t* prev,
+                                float inv_t, uint64_t seed, int32_t* draft, float* xout,
+                                void* workspace, int n_cu, hipStream_t stream);
+size_t sample_verify_workspace(int64_t B, int k, int64_t V);
+hipError_t launch_verify_sample(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
+                                const int32_t* draft, const float* X, const float* conf,
+                                float threshold, float inv_t, uint64_t seed, int32_t* block_len,
+                                int32_t* accepted, int32_t* bonus, int64_t* acc, int64_t* prop,
+                                void* workspace, hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace bdr

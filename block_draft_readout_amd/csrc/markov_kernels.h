@@ -1,0 +1,609 @@
+#pragma once
+
+// DSpark Markov bigram bias + semi-autoregressive full-vocabulary argmax (gfx950).
+//
+// For each row b the context token p starts at the accepted bonus token of the
+// previous step and, position after position, becomes the biased argmax just
+// taken (llm-scaler PR #620, DSpark port notes: dflash.py and qwen3_dflash.py).
+//
+// Arithmetic of one position, for 16 rows at a time:
+//   * the low-rank bias of 16 rows for 16 vocabulary entries is one MFMA tile:
+//     A = markov_w1 rows of the 16 contexts ([16, r]), B = markov_w2 rows of
+//     the 16 entries ([r, 16]); r = 32/64 is one or two 16-byte operand chunks;
+//   * the fp32 logits of the position are added and each lane keeps a running
+//     (value, index) maximum over the entries it visits in increasing order;
+//   * maxima are packed into order-preserving uint64 keys (value, then lower
+//     index) and folded across lanes, waves and workgroups with max, which is
+//     order-independent: the result is deterministic.
+//
+// Two schedules:
+//   chain  -- one persistent launch for all k positions.  One workgroup per
+//             compute unit keeps its slice of markov_w2 in LDS for the whole
+//             chain.  At each position every workgroup stores its local
+//             maxima, tagged with the position, into its own slots (a plain
+//             store, no read-modify-write), and the contexts of the next
+//             position are formed from the slots:
+//               B <= 2: every workgroup polls all slots until every tag is
+//                       current and reduces them itself;
+//               B > 2:  workgroup b % G reduces row b, stores the row's tagged
+//                       token, and every workgroup polls the B tokens.
+//             All workgroups must be resident at once: the grid is at most the
+//             number of compute units and each workgroup fits in one.  Polls
+//             are bounded; a time-out sets the error word of the workspace
+//             instead of hanging.  The last workgroup to finish (a completion
+//             counter) returns the slots to zero.
+//   passes -- one launch per position (used when the markov_w2 slice does not
+//             fit in LDS); stream order provides the grid-wide dependency, and
+//             workgroup w folds its keys into group slot w % 16 (atomic max;
+//             readers take the max over the 16 group slots).
+//
+// Workspace (zero-filled before first use; every call leaves it zeroed):
+//   keys[k][16][B] uint64 (passes) | slots[k][B][256] uint64 (chain, per
+//   workgroup) | tokens[k][B] uint64 (chain, B > 2) | completion counter
+//   (128 bytes) | error uint32 (the last 256 bytes)
+
+#include <algorithm>
+
+#include "bdr_device.h"
+#include "bdr_internal.h"
+
+namespace bdr {
+
+struct MarkovArgs {
+  const float* logits;           // [B, k, V]
+  int64_t B, V;
+  int k, r;
+  const void* w1;                // [V, r] embedding of the context token
+  const void* w2;                // [V, r] projection to the vocabulary
+  const int32_t* prev;           // [B] context of position 0
+  unsigned long long* keys;      // passes: [k, 16, B] per-position argmax keys per group
+  unsigned long long* slots;     // chain: [k, B, kChainSlots] tagged local maxima
+  unsigned long long* tokens;    // chain: [k, B] tagged tokens (B > 2)
+  unsigned* done;                // chain: completion counter
+  unsigned* err;                 // error word
+  int32_t* draft;                // [B, k]
+  int64_t vtiles;                // ceil(V / 16)
+  // sampling (probabilistic drafting): the token of a position is the argmax
+  // of x * inv_t + noise, x = logits + bias, and x is stored
+  const float* noise;            // [B, k, V] Gumbel noise of the draws
+  float* xout;                   // [B, k, V] biased logits x (the draft distribution)
+  float inv_t;                   // 1 / temperature
+};
+
+constexpr int kChainSlots = kNumCU;   // workgroups of the chain (at most)
+constexpr int kChainMaxB = 256;       // rows the chain keeps contexts of in LDS
+constexpr int kSinglePhaseB = 2;      // up to this many rows every workgroup reduces all slots
+
+constexpr unsigned kSpinLimit = 1u << 22;   // ~0.2 s of polling before giving up
+
+// final key of row b at position pos: max over the 16 group slots
+__device__ __forceinline__ unsigned long long final_key(const MarkovArgs& g, int pos, int64_t b) {
+  const unsigned long long* p = g.keys + static_cast<int64_t>(pos) * kArriveGroups * g.B + b;
+  unsigned long long k = 0ull;
+#pragma unroll
+  for (int i = 0; i < kArriveGroups; ++i) k = umax64(k, fetch_u64(p + i * g.B));
+  return k;
+}
+
+// Tagged keys of the chain hand-off: ordered value bits (32) | 0x1FFFFF - index
+// (21) | tag (11), tag = position + 1.  Max order is the packed-key order
+// (value, then lower index) among keys of one tag; a slot is current for a
+// position iff its tag matches, and "no candidate" is the bare tag, below every
+// real key.  Requires V <= 2^21.
+constexpr int kTagBits = 11;
+constexpr unsigned long long kTagMask = (1ull << kTagBits) - 1;
+__device__ __forceinline__ unsigned long long tag_key(unsigned long long key, unsigned tag) {
+  if (key == 0ull) return tag;
+  const unsigned long long low = 0x1FFFFFull - key_index(key);
+  return (key & 0xFFFFFFFF00000000ull) | (low << kTagBits) | tag;
+}
+__device__ __forceinline__ int32_t tagged_index(unsigned long long t) {
+  return static_cast<int32_t>(0x1FFFFFu - static_cast<uint32_t>((t >> kTagBits) & 0x1FFFFFull));
+}
+
+// E fragments: markov_w1 row of context token p (the lane's row; p < 0 or
+// p >= V: no bias)
+template <typename S, int RKS>
+__device__ __forceinline__ void context_frags(const MarkovArgs& g, int32_t p, int grp,
+                                              u32x4_t (&ef)[RKS > 0 ? RKS : 1]) {
+  constexpr int E = Elem<S>::PER16;
+  constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  if constexpr (RKS > 0) {
+    const rsrc_t r1 = make_rsrc(g.w1, static_cast<uint32_t>(g.V * g.r * ES));
+    const bool pok = p >= 0 && static_cast<int64_t>(p) < g.V;
+#pragma unroll
+    for (int c = 0; c < RKS; ++c) {
+      const int j = c * KS + grp * E;
+      ef[c] = bload16(r1, (pok && j < g.r)
+                              ? static_cast<uint32_t>((static_cast<int64_t>(p) * g.r + j) * ES)
+                              : kOOB);
+    }
+  }
+}
+
+// context token of row b at position pos for the passes schedule
+__device__ __forceinline__ int32_t pass_context(const MarkovArgs& g, int pos, int64_t b) {
+  if (b >= g.B) return -1;
+  return pos == 0 ? g.prev[b] : key_index(final_key(g, pos - 1, b));
+}
+
+// Fold the per-lane maxima of 16 rows into the position's keys.
+__device__ __forceinline__ void publish_rows(const MarkovArgs& g, int64_t b0, int pos, int wave,
+                                             int r16, int grp, const float (&bv)[4],
+                                             const uint32_t (&bi)[4],
+                                             unsigned long long (&sk)[4][16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned long long key = bi[i] != 0xFFFFFFFFu ? pack_key(bv[i], bi[i]) : 0ull;
+    key = rowgroup_max16(key);
+    if (r16 == 0) sk[wave][4 * grp + i] = key;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const unsigned long long key = umax64(umax64(sk[0][threadIdx.x], sk[1][threadIdx.x]),
+                                          umax64(sk[2][threadIdx.x], sk[3][threadIdx.x]));
+    const int64_t b = b0 + threadIdx.x;
+    const int64_t slot = (static_cast<int64_t>(pos) * kArriveGroups + blockIdx.x % kArriveGroups) * g.B;
+    if (b < g.B && key != 0ull) atomicMax(&g.keys[slot + b], key);
+  }
+  BDR_WAIT_ALL_MEM();  // the key updates are performed before this workgroup arrives
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------------------
+// chain: persistent, all positions in one launch
+// ----------------------------------------------------------------------------
+
+// Poll `n` <= kChainSlots tagged slots (stride `stride` from `base`) with one
+// wave until all carry `tag`; returns their max (0 if the poll timed out, after
+// setting the error word).  Every lane issues its kChainSlots / 64 loads back
+// to back (addresses clamped into range, surplus lanes count as current), so
+// one attempt costs one round trip.  Called by all 64 lanes of one wave.
+__device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
+                                                       const unsigned long long* base,
+                                                       int64_t stride, int n, unsigned tag,
+                                                       int lane) {
+  constexpr int PL = kChainSlots / 64;
+  unsigned it = 0;
+  for (;;) {
+    unsigned long long t[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int i = lane + 64 * j;
+      t[j] = fetch_u64(base + static_cast<int64_t>(i < n ? i : n - 1) * stride);
+    }
+    unsigned long long m = 0ull;
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const bool cur = lane + 64 * j >= n || (t[j] & kTagMask) == tag;
+      ok = ok & cur;
+      m = umax64(m, t[j]);
+    }
+    if (__all(ok)) return wave_max64(m);
+    if (++it > kSpinLimit) {
+      if (lane == 0) atomicOr(g.err, 1u);
+      return 0ull;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not its global loads, so prefetched loads stay in flight across it.
+#define BDR_LDS_BARRIER()                              \
+  do {                                                 \
+    __builtin_amdgcn_s_waitcnt(0xC07F);  /* lgkmcnt(0) */ \
+    asm volatile("s_barrier" ::: "memory");            \
+    __builtin_amdgcn_sched_barrier(0);                 \
+  } while (0)
+
+constexpr int kChainWaves = 5;   // wave 0: hand-off; waves 1..4: vocabulary tiles
+
+template <typename S, int RKS, int MAXT, bool SAMPLE>
+__global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const MarkovArgs g) {
+  extern __shared__ u32x4_t w2s[];   // [tile][chunk][lane] operand chunks of markov_w2
+  constexpr int E = Elem<S>::PER16;
+  constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  constexpr int NC = RKS > 0 ? RKS : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int cw = wave - 1;           // compute wave index, -1 for the hand-off wave
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const unsigned G = gridDim.x;
+  const int64_t t_lo = static_cast<int64_t>(blockIdx.x) * g.vtiles / G;
+  const int64_t t_hi = static_cast<int64_t>(blockIdx.x + 1) * g.vtiles / G;
+  const int ntl = static_cast<int>(t_hi - t_lo);   // compute wave c owns tiles c, c+4, ... (< 4*MAXT)
+  const bool single = g.B <= kSinglePhaseB;
+
+  __shared__ unsigned long long sk[4][16];
+  __shared__ int32_t ctx[kChainMaxB];              // context token of every row
+  __shared__ int last_flag;
+
+  // stage this workgroup's markov_w2 rows in operand layout (lane l's 16 bytes
+  // of chunk q land at w2s[q*64 + l])
+  if constexpr (RKS > 0) {
+    const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
+    for (int q = wave; q < ntl * RKS; q += kChainWaves) {
+      const int tile = q / RKS;
+      const int c = q - tile * RKS;
+      const int64_t v = (t_lo + tile) * 16 + r16;
+      const int j = c * KS + grp * E;
+      const uint32_t off = (v < g.V && j < g.r) ? static_cast<uint32_t>((v * g.r + j) * ES) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r2, (__attribute__((address_space(3))) void*)(&w2s[q * 64]), 16, off, 0, 0, 0);
+    }
+  }
+  for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x) ctx[b] = g.prev[b];
+
+  // logits of position pos, row b0 + r16, vocabulary entries 16 * tile + 4 * grp
+  // .. + 3 of this compute wave's tiles: one 16-byte load per tile (entries
+  // past V are masked when compared).  Indices fit 32 bits (V <= 2^21, k <= 16,
+  // operands < 2^31 bytes).
+  const int V32 = static_cast<int>(g.V);
+  const int vbase = static_cast<int>(t_lo) * 16 + 4 * grp;   // + 16 * tile
+  const uint32_t zrow = static_cast<uint32_t>(g.k) * static_cast<uint32_t>(g.V) * 4u;
+  u32x4_t zv[MAXT];
+  u32x4_t gv[SAMPLE ? MAXT : 1];   // sampling: the draws' Gumbel noise, same layout
+  // bytes of the [nb rows][k][V] fp32 block a row group's position spans
+  auto block_bytes = [&](int64_t b0) {
+    const int nb = static_cast<int>(min<int64_t>(16, g.B - b0));
+    return static_cast<uint32_t>(nb - 1) * zrow + static_cast<uint32_t>(V32) * 4u;
+  };
+  // cwo / ntlo / vbo: this wave's first tile, the workgroup's tile count and
+  // the lane's first entry, passed in opaque per position (see below)
+  auto load_z = [&](int pos, int64_t b0, int cwo, int ntlo, int vbo) {
+    const int nb = static_cast<int>(min<int64_t>(16, g.B - b0));
+    const int64_t first = (b0 * g.k + pos) * g.V;
+    const rsrc_t rz = make_rsrc(g.logits + first, block_bytes(b0));
+    rsrc_t rg;
+    if constexpr (SAMPLE) rg = make_rsrc(g.noise + first, block_bytes(b0));
+    const uint32_t lane_off = static_cast<uint32_t>(r16) * zrow;
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int tile = cwo + 4 * u;
+      const int v0 = vbo + 16 * tile;
+      const uint32_t off = (tile < ntlo && v0 < V32 && r16 < nb)
+                               ? lane_off + static_cast<uint32_t>(v0) * 4u
+                               : kOOB;
+      zv[u] = bload16(rz, off);
+      if constexpr (SAMPLE) gv[u] = bload16(rg, off);
+    }
+  };
+  if (cw >= 0) load_z(0, 0, cw, ntl, vbase);
+  BDR_WAIT_VM(0);
+  __syncthreads();
+
+  for (int pos = 0; pos < g.k; ++pos) {
+    const unsigned tag = static_cast<unsigned>(pos) + 1;
+    for (int64_t b0 = 0; b0 < g.B; b0 += 16) {
+      const int64_t nb = min<int64_t>(16, g.B - b0);
+      const bool last_group = b0 + 16 >= g.B;
+      if (cw >= 0) {
+        // per-tile indices are recomputed each position from opaque copies
+        // instead of being kept live (in registers) across the whole chain
+        int cwo = cw, ntlo = ntl, vbo = vbase;
+        asm volatile("" : "+s"(cwo), "+s"(ntlo), "+v"(vbo));
+        if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
+        u32x4_t ef[NC];
+        context_frags<S, RKS>(g, b0 + r16 < g.B ? ctx[b0 + r16] : -1, grp, ef);
+        // bias tile D[vocab 4 * grp + i][row r16] = markov_w2 rows x context
+        // embeddings; each lane keeps the running maximum of its row r16 over
+        // the entries it visits in increasing order.  Reads past the
+        // workgroup's last tile repeat it (no branch) and are masked.
+        float bv = -INFINITY;
+        uint32_t bi = 0xFFFFFFFFu;
+        const bool row_ok = r16 < nb;
+        rsrc_t rx;
+        if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, block_bytes(b0));
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) {
+          const int tile = cwo + 4 * u;
+          const int tile_rd = tile < ntlo ? tile : ntlo - 1;
+          f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (RKS > 0) {
+#pragma unroll
+            for (int c = 0; c < RKS; ++c)
+              bias = mma16(w2s[(tile_rd * RKS + c) * 64 + lane], ef[c], bias, S());
+          }
+          const int v0 = vbo + 16 * tile;
+          const bool tok = row_ok && tile < ntlo;
+          f32x4_t xs;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float s = __uint_as_float(zv[u][i]) + bias[i];
+            float key = s;
+            if constexpr (SAMPLE) {
+              xs[i] = s;
+              key = s * g.inv_t + __uint_as_float(gv[u][i]);
+            }
+            if (tok && v0 + i < V32 && key > bv) {
+              bv = key;
+              bi = static_cast<uint32_t>(v0 + i);
+            }
+          }
+          if constexpr (SAMPLE) {
+            // x of the lane's four entries: one 16-byte store, element stores
+            // for the quad that straddles the end of the row
+            const uint32_t off = static_cast<uint32_t>(r16) * zrow + static_cast<uint32_t>(v0) * 4u;
+            const bool full = tok && v0 + 4 <= V32;
+            bstore16(xs, rx, full ? off : kOOB);
+            if (tok && !full) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) bstore_f32(xs[i], rx, v0 + i < V32 ? off + 4u * i : kOOB);
+            }
+          }
+        }
+        // the next position's first logits: independent of the hand-off below
+        // (kept after the compares so the two logits sets are never live together)
+        __builtin_amdgcn_sched_barrier(0);
+        if (last_group && pos + 1 < g.k) load_z(pos + 1, 0, cwo, ntlo, vbo);
+        // row r16's maximum over the four lane groups, then over the waves (LDS)
+        unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+        key = umax64(key, __shfl_xor(key, 16, 64));
+        key = umax64(key, __shfl_xor(key, 32, 64));
+        if (grp == 0) sk[cw][r16] = key;
+      }
+      BDR_LDS_BARRIER();
+      // this workgroup's maxima of rows b0.. -> its tagged slots
+      if (threadIdx.x < nb) {
+        const unsigned long long key = umax64(umax64(sk[0][threadIdx.x], sk[1][threadIdx.x]),
+                                              umax64(sk[2][threadIdx.x], sk[3][threadIdx.x]));
+        publish_u64(g.slots + (pos * g.B + b0 + threadIdx.x) * kChainSlots + blockIdx.x,
+                    tag_key(key, tag));
+      }
+      if (!last_group) BDR_LDS_BARRIER();   // sk is rewritten by the next row group
+    }
+    // contexts of the next position (and this position's tokens)
+    if (wave == 0) {
+      // row b's slots of this position are contiguous: [pos][b][workgroup]
+      const unsigned long long* pos_slots = g.slots + static_cast<int64_t>(pos) * g.B * kChainSlots;
+      if (single) {
+        for (int64_t b = 0; b < g.B; ++b) {
+          const int32_t tok =
+              tagged_index(poll_max(g, pos_slots + b * kChainSlots, 1, static_cast<int>(G), tag, lane));
+          if (lane == 0) {
+            ctx[b] = tok;
+            if (blockIdx.x == 0) g.draft[b * g.k + pos] = tok;
+          }
+        }
+      } else {
+        unsigned long long* toks = g.tokens + static_cast<int64_t>(pos) * g.B;
+        for (int64_t b = blockIdx.x; b < g.B; b += G) {   // rows this workgroup reduces
+          const unsigned long long t =
+              poll_max(g, pos_slots + b * kChainSlots, 1, static_cast<int>(G), tag, lane);
+          if (lane == 0) {
+            g.draft[b * g.k + pos] = tagged_index(t);
+            publish_u64(toks + b, (t & ~kTagMask) | tag);
+          }
+        }
+        for (int64_t b0 = 0; b0 < g.B; b0 += 64) {
+          const int n = static_cast<int>(min<int64_t>(64, g.B - b0));
+          unsigned it = 0;
+          for (;;) {
+            unsigned long long t = fetch_u64(toks + b0 + (lane < n ? lane : n - 1));
+            if (__all(lane >= n || (t & kTagMask) == tag)) {
+              if (lane < n) ctx[b0 + lane] = tagged_index(t);
+              break;
+            }
+            if (++it > kSpinLimit) {
+              if (lane == 0) atomicOr(g.err, 1u);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+    }
+    BDR_LDS_BARRIER();
+  }
+
+  // the last workgroup to finish returns the slots to zero (every other one has
+  // finished reading them)
+  if (threadIdx.x == 0) {
+    BDR_WAIT_ALL_MEM();
+    last_flag = atomicAdd(g.done, 1u) + 1 == G ? 1 : 0;
+  }
+  __syncthreads();
+  if (last_flag) {
+    const int64_t nslots = static_cast<int64_t>(g.k) * kChainSlots * g.B;
+    for (int64_t i = threadIdx.x; i < nslots; i += blockDim.x) g.slots[i] = 0ull;
+    if (!single)
+      for (int64_t i = threadIdx.x; i < static_cast<int64_t>(g.k) * g.B; i += blockDim.x)
+        g.tokens[i] = 0ull;
+    if (threadIdx.x == 0) *g.done = 0u;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// passes: one launch per position
+// ----------------------------------------------------------------------------
+template <typename S, int RKS, int TPW, bool SAMPLE>
+__global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, int pos) {
+  constexpr int E = Elem<S>::PER16;
+  constexpr int KS = Elem<S>::KSTEP;
+  constexpr int ES = static_cast<int>(sizeof(S));
+  constexpr int NC = RKS > 0 ? RKS : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int64_t nb = min<int64_t>(16, g.B - b0);
+  __shared__ unsigned long long sk[4][16];
+
+  if (pos > 0 && blockIdx.x == 0 && threadIdx.x < 16 && b0 + r16 < g.B)
+    g.draft[(b0 + r16) * g.k + (pos - 1)] = key_index(final_key(g, pos - 1, b0 + r16));
+  u32x4_t ef[NC];
+  context_frags<S, RKS>(g, pass_context(g, pos, b0 + r16), grp, ef);
+
+  const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
+  const uint32_t blk = static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4);
+  const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V, blk);
+  rsrc_t rn, rx;
+  if constexpr (SAMPLE) {
+    rn = make_rsrc(g.noise + (b0 * g.k + pos) * g.V, blk);
+    rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, blk);
+  }
+  uint32_t zrow[4];
+  bool bok[4];
+  float bv[4];
+  uint32_t bi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rb = 4 * grp + i;
+    bok[i] = rb < nb;
+    zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
+    bv[i] = -INFINITY;
+    bi[i] = 0xFFFFFFFFu;
+  }
+
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 4 + wave; base < g.vtiles;
+       base += nw * TPW) {
+    u32x4_t wf[TPW][NC];
+    float zv[TPW][4];
+    float gn[SAMPLE ? TPW : 1][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t v = (base + u * nw) * 16 + r16;
+      const bool vok = v < g.V;
+      if constexpr (RKS > 0) {
+#pragma unroll
+        for (int c = 0; c < RKS; ++c) {
+          const int j = c * KS + grp * E;
+          wf[u][c] = bload16(r2, (vok && j < g.r) ? static_cast<uint32_t>((v * g.r + j) * ES) : kOOB);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (vok && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB;
+        zv[u][i] = bload_f32(rz, off);
+        if constexpr (SAMPLE) gn[u][i] = bload_f32(rn, off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t v = (base + u * nw) * 16 + r16;
+      f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (RKS > 0) {
+#pragma unroll
+        for (int c = 0; c < RKS; ++c) bias = mma16(ef[c], wf[u][c], bias, S());
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = zv[u][i] + bias[i];
+        float key = s;
+        if constexpr (SAMPLE) {
+          key = s * g.inv_t + gn[u][i];
+          bstore_f32(s, rx, (v < g.V && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
+        }
+        if (v < g.V && bok[i] && key > bv[i]) {
+          bv[i] = key;
+          bi[i] = static_cast<uint32_t>(v);
+        }
+      }
+    }
+  }
+  publish_rows(g, b0, pos, wave, r16, grp, bv, bi, sk);
+}
+
+// last position's tokens; then the keys go back to zero
+static __global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs g) {
+  for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x)
+    g.draft[b * g.k + (g.k - 1)] = key_index(final_key(g, g.k - 1, b));
+  __syncthreads();
+  const int64_t nkeys = static_cast<int64_t>(g.k) * kArriveGroups * g.B;
+  for (int64_t i = threadIdx.x; i < nkeys; i += blockDim.x) g.keys[i] = 0ull;
+}
+
+constexpr size_t kChainLdsMax = 150 * 1024;
+
+template <typename S, int RKS, int MAXT, bool SAMPLE>
+static hipError_t launch_chain_t(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT, SAMPLE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kChainLdsMax));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT, SAMPLE>), dim3(G), dim3(64 * kChainWaves),
+                     lds, st, g);
+  return hipSuccess;
+}
+
+// MAXT: 16-entry vocabulary tiles per wave (the workgroup's tiles / 4, rounded up)
+template <typename S, int RKS, bool SAMPLE>
+static hipError_t launch_chain(const MarkovArgs& g, unsigned G, size_t lds, int64_t tiles_per_wg,
+                               hipStream_t st) {
+  const int64_t per_wave = (tiles_per_wg + 3) / 4;
+  if (per_wave <= 2) return launch_chain_t<S, RKS, 2, SAMPLE>(g, G, lds, st);
+  if (per_wave <= 4) return launch_chain_t<S, RKS, 4, SAMPLE>(g, G, lds, st);
+  if (per_wave <= 8) return launch_chain_t<S, RKS, 8, SAMPLE>(g, G, lds, st);
+  if (per_wave <= 10) return launch_chain_t<S, RKS, 10, SAMPLE>(g, G, lds, st);
+  if (per_wave <= 12) return launch_chain_t<S, RKS, 12, SAMPLE>(g, G, lds, st);
+  return launch_chain_t<S, RKS, 16, SAMPLE>(g, G, lds, st);
+}
+
+template <typename S, int RKS, bool SAMPLE>
+static void launch_passes(const MarkovArgs& g, hipStream_t st) {
+  constexpr int TPW = RKS <= 2 ? 8 : (RKS <= 4 ? 4 : 2);
+  const int64_t wgs = std::min<int64_t>((g.vtiles + 4 * TPW - 1) / (4 * TPW), 1024);
+  const dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>((g.B + 15) / 16));
+  for (int pos = 0; pos < g.k; ++pos)
+    hipLaunchKernelGGL((markov_pass_kernel<S, RKS, TPW, SAMPLE>), grid, dim3(256), 0, st, g, pos);
+  hipLaunchKernelGGL(markov_finalize_kernel, dim3(1), dim3(256), 0, st, g);
+}
+
+template <typename S, bool SAMPLE>
+static hipError_t launch_typed(const MarkovArgs& g, int rks, int n_cu, hipStream_t st) {
+  const unsigned G = static_cast<unsigned>(
+      std::min<int64_t>(std::min(std::max(n_cu, 1), kChainSlots), g.vtiles));
+  const int64_t tiles = (g.vtiles + G - 1) / G;
+  const size_t lds = static_cast<size_t>(tiles) * rks * 64 * 16;
+  if (lds <= kChainLdsMax && tiles <= 64 && g.B <= kChainMaxB) {
+    switch (rks) {
+      case 0: return launch_chain<S, 0, SAMPLE>(g, G, lds, tiles, st);
+      case 1: return launch_chain<S, 1, SAMPLE>(g, G, lds, tiles, st);
+      case 2: return launch_chain<S, 2, SAMPLE>(g, G, lds, tiles, st);
+      case 3: return launch_chain<S, 3, SAMPLE>(g, G, lds, tiles, st);
+      case 4: return launch_chain<S, 4, SAMPLE>(g, G, lds, tiles, st);
+      default: break;  // larger fp32 ranks: per-position launches
+    }
+  }
+  switch (rks) {
+    case 0: launch_passes<S, 0, SAMPLE>(g, st); break;
+    case 1: launch_passes<S, 1, SAMPLE>(g, st); break;
+    case 2: launch_passes<S, 2, SAMPLE>(g, st); break;
+    case 3: launch_passes<S, 3, SAMPLE>(g, st); break;
+    case 4: launch_passes<S, 4, SAMPLE>(g, st); break;
+    case 5: launch_passes<S, 5, SAMPLE>(g, st); break;
+    case 6: launch_passes<S, 6, SAMPLE>(g, st); break;
+    case 7: launch_passes<S, 7, SAMPLE>(g, st); break;
+    default: launch_passes<S, 8, SAMPLE>(g, st); break;
+  }
+  return hipSuccess;
+}
+
+// MarkovArgs over a workspace of markov_workspace(B, k) bytes (sampling fields unset).
+MarkovArgs markov_args(const float* logits, int64_t B, int k, int64_t V, const void* w1,
+                       const void* w2, int rank, const int32_t* prev, int32_t* draft,
+                       void* workspace);
+
+// Launch the schedule that fits (g.r already 0 when no Markov weights are given).
+template <bool SAMPLE>
+hipError_t markov_dispatch(const MarkovArgs& g, bdr_dtype wdt, int n_cu, hipStream_t stream) {
+  const int ks = wdt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
+  const int rks = (g.r + ks - 1) / ks;
+  hipError_t e = wdt == BDR_BF16 ? launch_typed<uint16_t, SAMPLE>(g, rks, n_cu, stream)
+                                 : launch_typed<float, SAMPLE>(g, rks, n_cu, stream);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+}  // namespace bdr

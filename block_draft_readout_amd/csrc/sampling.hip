@@ -1,0 +1,520 @@
+// Probabilistic drafting noise and rejection-sampling verification (gfx950).
+//
+// The serving recipe on the "Qwen3.8-27B-DSpark -- vLLM-ready" model card
+// ("Usage", "Tuning notes") draws the draft tokens probabilistically, and the
+// "Qwen4Exp DFlash drafter support" page ("Not covered") verifies speculative
+// decoding by rejection sampling.  Neither gives the arithmetic; this follows
+// the standard speculative-sampling rule (Leviathan, Kalman and Matias, ICML
+// 2023; Chen et al., 2023):
+//   q_i = softmax(x_i / T), x_i the Markov-biased draft logits of position i
+//         (the draft token d_i was drawn from q_i);
+//   p_i = softmax(y_i / T), y_i the target logits;
+//   d_i is accepted iff r_i * q_i(d_i) < p_i(d_i), r_i uniform, tested in
+//   order while accepted; at the first rejection the emitted token is drawn
+//   from max(0, p_i - q_i) (from p_i if that is zero everywhere); if the whole
+//   block is accepted the bonus token is drawn from p at the block's end.
+// Draws use the Gumbel-max rule, argmax_v log w_v + G_v, with noise from the
+// counter-based generator of bdr_device.h: G at vocabulary entry v of (row b,
+// position i, stream) is word v % 4 of Philox((v / 4, b, i, stream), seed).
+//
+// Kernels
+//   gumbel_noise_kernel  grid (row b*k+i, vocabulary chunk): the draft noise of
+//                        every (b, i, v), one Philox call per four entries.
+//   sample_lse_kernel    grid (row b*k+j, chunk), positions j < L_b only: the
+//                        (max, sum of exp) partials of y_j / T and x_j / T per
+//                        chunk.  The last workgroup to arrive folds them into
+//                        log-sum-exps, takes every row's accept decisions in
+//                        order (in the log domain: log r + log q < log p), and
+//                        records where and what the row still draws.
+//   sample_draw_kernel   grid (row b, chunk): the residual (or bonus) draw of
+//                        each row's recorded position; chunk keys are folded
+//                        with atomic max into eight slots per row, and the last
+//                        workgroup to arrive emits the tokens and clears slots
+//                        and counters.
+//
+// Workspace: LSE partials | per-row decisions | draw slots | LSE-pass counters
+// | draw-pass counters.  Slots and counters must be zero before the first call
+// and every call leaves them zero; partials and decisions are scratch.
+
+#include <algorithm>
+#include <cmath>
+
+#include "bdr_device.h"
+#include "bdr_internal.h"
+
+namespace bdr {
+
+// ----------------------------------------------------------------------------
+// draft noise
+// ----------------------------------------------------------------------------
+constexpr int kNoiseQuadsPerThread = 2;
+
+// noise[(b * k + i) * V + v]; blockIdx.x is the row, blockIdx.y the chunk of
+// 256 * kNoiseQuadsPerThread quads
+__global__ __launch_bounds__(256) void gumbel_noise_kernel(float* noise, int k, int64_t V,
+                                                           uint32_t k0, uint32_t k1,
+                                                           uint32_t stream) {
+  const int64_t row = blockIdx.x;
+  const uint32_t b = static_cast<uint32_t>(row / k);
+  const uint32_t pos = static_cast<uint32_t>(row - static_cast<int64_t>(b) * k);
+  const uint32_t V32 = static_cast<uint32_t>(V);
+  const uint32_t quads = (V32 + 3u) / 4u;
+  const rsrc_t r = make_rsrc(noise + row * V, V32 * 4u);
+#pragma unroll
+  for (int u = 0; u < kNoiseQuadsPerThread; ++u) {
+    const uint32_t q = (blockIdx.y * kNoiseQuadsPerThread + u) * 256u + threadIdx.x;
+    if (q < quads) {
+      const u32x4_t x = philox4x32_10(u32x4_t{q, b, pos, stream}, k0, k1);
+      f32x4_t gq;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) gq[w] = gumbel_of(bits_to_uniform(x[w]));
+      const uint32_t v0 = 4u * q;
+      if (v0 + 4u <= V32) {
+        bstore16(gq, r, v0 * 4u);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) bstore_f32(gq[w], r, v0 + w < V32 ? (v0 + w) * 4u : kOOB);
+      }
+    }
+  }
+}
+
+hipError_t launch_gumbel_noise(float* noise, int64_t B, int k, int64_t V, uint64_t seed,
+                               uint32_t stream_id, hipStream_t stream) {
+  const int64_t quads = (V + 3) / 4;
+  const int64_t per_wg = 256 * kNoiseQuadsPerThread;
+  const dim3 grid(static_cast<unsigned>(B * k),
+                  static_cast<unsigned>((quads + per_wg - 1) / per_wg));
+  hipLaunchKernelGGL(gumbel_noise_kernel, grid, dim3(256), 0, stream, noise, k, V,
+                     static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// rejection-sampling verification
+// ----------------------------------------------------------------------------
+constexpr int kMaxLseChunks = 32;
+constexpr int kDrawSlots = 8;   // atomic-max slots per row and key kind
+
+struct SampleArgs {
+  const void* Y;                 // [B, k+1, V] target logits
+  const float* X;                // [B, k, V] draft-distribution logits
+  int64_t B, V;
+  int k;
+  const int32_t* draft;          // [B, k]
+  const float* conf;             // [B, k] or null
+  float th;
+  int use_conf;
+  float inv_t;
+  uint32_t k0, k1;               // seed
+  int chunks;                    // LSE pass: chunks per row
+  int64_t chunk_len;             // multiple of 8 entries
+  unsigned long long* part;      // [2][B][k][chunks] packed (max, sum) of y/T and x/T
+  int4* dec;                     // [B] (position, residual?, lse_p bits, lse_q bits)
+  unsigned* gcnt;                // LSE pass arrival counters
+  unsigned* tcnt;
+  int dchunks;                   // draw pass: chunks per row
+  int64_t dchunk_len;            // multiple of 4 entries
+  unsigned long long* dslots;    // [B][kDrawSlots][2] keys: draw from p (0), residual (1)
+  unsigned* dgcnt;               // draw pass arrival counters
+  unsigned* dtcnt;
+  int32_t* block_len;
+  int32_t* accepted;
+  int32_t* bonus;
+  int64_t* acc;                  // [k] or null
+  int64_t* prop;                 // [k] or null
+};
+
+// L_b: first position whose confidence is strictly below the threshold, else k.
+__device__ __forceinline__ int sample_block_length(const SampleArgs& g, int64_t b) {
+  if (!g.use_conf) return g.k;
+  for (int i = 0; i < g.k; ++i)
+    if (g.conf[b * g.k + i] < g.th) return i;
+  return g.k;
+}
+
+// Running log-sum-exp state: m = max, s = sum exp(v - m); s == 0 means empty.
+struct Lse {
+  float m, s;
+};
+
+__device__ __forceinline__ void lse_add(Lse& a, float f) {
+  const float d = f - a.m;                // +inf on the first entry
+  const float e = expf(-fabsf(d));
+  if (d > 0.f) {
+    a.s = a.s * e + 1.f;
+    a.m = f;
+  } else {
+    a.s += e;
+  }
+}
+
+__device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
+  if (b.s == 0.f) return a;
+  if (a.s == 0.f) return b;
+  const float m = fmaxf(a.m, b.m);
+  return Lse{m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
+}
+
+__device__ __forceinline__ Lse lse_wave(Lse a) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1)
+    a = lse_merge(a, Lse{__shfl_xor(a.m, off, 64), __shfl_xor(a.s, off, 64)});
+  return a;
+}
+
+__device__ __forceinline__ unsigned long long lse_pack(Lse a) {
+  return (static_cast<unsigned long long>(__float_as_uint(a.s)) << 32) | __float_as_uint(a.m);
+}
+__device__ __forceinline__ Lse lse_unpack(unsigned long long v) {
+  return Lse{__uint_as_float(static_cast<uint32_t>(v)),
+             __uint_as_float(static_cast<uint32_t>(v >> 32))};
+}
+
+// acceptance uniform of (row b, position j)
+__device__ __forceinline__ float accept_uniform(const SampleArgs& g, int64_t b, int j) {
+  const u32x4_t x = philox4x32_10(
+      u32x4_t{0u, static_cast<uint32_t>(b), static_cast<uint32_t>(j), kStreamAccept}, g.k0, g.k1);
+  return bits_to_uniform(x.x);
+}
+
+// Fold the LSE partials into log-sum-exps, then take every row's accept
+// decisions.  Called by the whole last workgroup of the LSE pass.
+template <typename S>
+__device__ void sample_scan(const SampleArgs& g) {
+  constexpr int GROUP = 64;
+  __shared__ int Ls[GROUP];
+  __shared__ float lse[2][GROUP * BDR_MAX_K];
+  __shared__ int cacc[BDR_MAX_K];
+  __shared__ int cprop[BDR_MAX_K];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int k = g.k;
+  const S* Y = static_cast<const S*>(g.Y);
+  if (tid < BDR_MAX_K) {
+    cacc[tid] = 0;
+    cprop[tid] = 0;
+  }
+  for (int64_t b0 = 0; b0 < g.B; b0 += GROUP) {
+    const int nb = static_cast<int>(min<int64_t>(GROUP, g.B - b0));
+    if (tid < nb) Ls[tid] = sample_block_length(g, b0 + tid);
+    __syncthreads();
+    // one thread per (row, position, p or q): all chunk partials at once
+    for (int t = tid; t < nb * k * 2; t += nthr) {
+      const int which = t & 1;
+      const int lb = (t >> 1) / k;
+      const int j = (t >> 1) - lb * k;
+      if (j >= Ls[lb]) continue;
+      const unsigned long long* p =
+          g.part + ((static_cast<int64_t>(which) * g.B + b0 + lb) * k + j) * g.chunks;
+      unsigned long long v[kMaxLseChunks];
+#pragma unroll
+      for (int c = 0; c < kMaxLseChunks; ++c)
+        v[c] = fetch_u64(p + (c < g.chunks ? c : g.chunks - 1));
+      Lse a{-INFINITY, 0.f};
+#pragma unroll
+      for (int c = 0; c < kMaxLseChunks; ++c)
+        if (c < g.chunks) a = lse_merge(a, lse_unpack(v[c]));
+      lse[which][lb * k + j] = a.m + logf(a.s);
+    }
+    __syncthreads();
+    // one thread per row: the drafted entries of every tested position, then
+    // the accept tests in order
+    for (int lb = tid; lb < nb; lb += nthr) {
+      const int64_t b = b0 + lb;
+      const int L = Ls[lb];
+      int dd[BDR_MAX_K];
+#pragma unroll
+      for (int j = 0; j < BDR_MAX_K; ++j) dd[j] = j < L ? g.draft[b * k + j] : -1;
+      float yd[BDR_MAX_K], xd[BDR_MAX_K];
+#pragma unroll
+      for (int j = 0; j < BDR_MAX_K; ++j) {
+        const bool ok = j < L && dd[j] >= 0 && dd[j] < g.V;
+        yd[j] = ok ? to_f32<S>(Y[(b * (k + 1) + j) * g.V + dd[j]]) : 0.f;
+        xd[j] = ok ? g.X[(b * k + j) * g.V + dd[j]] : 0.f;
+      }
+      int a = L;
+#pragma unroll
+      for (int j = BDR_MAX_K - 1; j >= 0; --j) {
+        if (j < L) {
+          const bool ok = dd[j] >= 0 && dd[j] < g.V;
+          const float lp = yd[j] * g.inv_t - lse[0][lb * k + j];
+          const float lq = xd[j] * g.inv_t - lse[1][lb * k + j];
+          const float r = accept_uniform(g, b, j);
+          if (!(ok && logf(r) + lq < lp)) a = j;   // the first rejection wins
+        }
+      }
+      const bool resid = a < L;
+      g.block_len[b] = L;
+      g.accepted[b] = a;
+      g.dec[b] = int4{a, resid ? 1 : 0, resid ? __float_as_int(lse[0][lb * k + a]) : 0,
+                      resid ? __float_as_int(lse[1][lb * k + a]) : 0};
+      for (int i = 0; i < a; ++i) atomicAdd(&cacc[i], 1);
+      for (int i = 0; i < L; ++i) atomicAdd(&cprop[i], 1);
+    }
+    __syncthreads();
+  }
+  if (tid < k) {
+    if (g.acc) g.acc[tid] += cacc[tid];
+    if (g.prop) g.prop[tid] += cprop[tid];
+  }
+}
+
+template <typename S, bool VEC>
+__global__ __launch_bounds__(256) void sample_lse_kernel(const SampleArgs g) {
+  const int64_t row = blockIdx.x;     // b * k + j
+  const int64_t b = row / g.k;
+  const int j = static_cast<int>(row - b * g.k);
+  __shared__ Lse red[2][4];
+  __shared__ int last;
+  if (j < sample_block_length(g, b)) {   // same decision for the whole workgroup
+    const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.chunk_len;
+    const int64_t c1 = std::min<int64_t>(g.V, c0 + g.chunk_len);
+    const S* y = static_cast<const S*>(g.Y) + (b * (g.k + 1) + j) * g.V;
+    const float* x = g.X + row * g.V;
+    Lse lp{-INFINITY, 0.f}, lq{-INFINITY, 0.f};
+    if constexpr (VEC) {
+      // eight entries per lane per step: 16 or 32 bytes of y, 32 bytes of x
+      for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * 8; v < c1; v += 256 * 8) {
+        u32x4_t yq[sizeof(S) / 2];
+#pragma unroll
+        for (int h = 0; h < static_cast<int>(sizeof(S) / 2); ++h) yq[h] = load16_stream(y + v + h * Elem<S>::PER16);
+        const u32x4_t xq0 = load16_stream(x + v);
+        const u32x4_t xq1 = load16_stream(x + v + 4);
+        const S* ye = reinterpret_cast<const S*>(yq);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) lse_add(lp, to_f32<S>(ye[t]) * g.inv_t);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) lse_add(lq, __uint_as_float(xq0[t]) * g.inv_t);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) lse_add(lq, __uint_as_float(xq1[t]) * g.inv_t);
+      }
+    } else {
+      for (int64_t v = c0 + threadIdx.x; v < c1; v += 256) {
+        lse_add(lp, to_f32<S>(y[v]) * g.inv_t);
+        lse_add(lq, x[v] * g.inv_t);
+      }
+    }
+    lp = lse_wave(lp);
+    lq = lse_wave(lq);
+    if ((threadIdx.x & 63) == 0) {
+      red[0][threadIdx.x >> 6] = lp;
+      red[1][threadIdx.x >> 6] = lq;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const int w = threadIdx.x;
+      const Lse s = lse_merge(lse_merge(red[w][0], red[w][1]), lse_merge(red[w][2], red[w][3]));
+      publish_u64(&g.part[((static_cast<int64_t>(w) * g.B + b) * g.k + j) * g.chunks + blockIdx.y],
+                  lse_pack(s));
+    }
+  }
+  // arrive (two-level); the last workgroup to arrive runs the scan
+  if (threadIdx.x < 2) BDR_WAIT_ALL_MEM();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned w = blockIdx.y * gridDim.x + blockIdx.x;
+    last = arrive_group(g.gcnt, w, total) && arrive_top(g.tcnt, total);
+  }
+  __syncthreads();
+  if (!last) return;
+  sample_scan<S>(g);
+  if (threadIdx.x < kArriveGroups) g.gcnt[threadIdx.x * kLineWords] = 0u;
+  if (threadIdx.x == 0) *g.tcnt = 0u;
+}
+
+// Draw of each row's recorded position: from max(0, p - q) after a rejection,
+// from p after a fully accepted block.  Both keys are kept for every entry of a
+// residual row: the draw falls back to p when max(0, p - q) is zero everywhere.
+template <typename S>
+__global__ __launch_bounds__(256) void sample_draw_kernel(const SampleArgs g) {
+  const int64_t b = blockIdx.x;
+  const int4 dd = g.dec[b];
+  const int s = dd.x;
+  const bool resid = dd.y != 0;
+  const float lse_p = __int_as_float(dd.z);
+  const float lse_q = __int_as_float(dd.w);
+  const S* y = static_cast<const S*>(g.Y) + (b * (g.k + 1) + s) * g.V;
+  const float* x = g.X + (b * g.k + (resid ? s : 0)) * g.V;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.dchunk_len;
+  const int64_t c1 = std::min<int64_t>(g.V, c0 + g.dchunk_len);
+  __shared__ unsigned long long sk[2][4];
+  __shared__ int last;
+  float bp = -INFINITY, br = -INFINITY;
+  uint32_t ip = 0xFFFFFFFFu, ir = 0xFFFFFFFFu;
+  for (int64_t v0 = c0 + static_cast<int64_t>(threadIdx.x) * 4; v0 < c1; v0 += 256 * 4) {
+    const u32x4_t u = philox4x32_10(
+        u32x4_t{static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(b), static_cast<uint32_t>(s),
+                kStreamResample},
+        g.k0, g.k1);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t v = v0 + w;
+      if (v < c1) {
+        const float G = gumbel_of(bits_to_uniform(u[w]));
+        const float fy = to_f32<S>(y[v]) * g.inv_t;
+        const float kp = fy + G;
+        if (kp > bp) {
+          bp = kp;
+          ip = static_cast<uint32_t>(v);
+        }
+        if (resid) {
+          const float wv = expf(fy - lse_p) - expf(x[v] * g.inv_t - lse_q);
+          if (wv > 0.f) {
+            const float kr = logf(wv) + G;
+            if (kr > br) {
+              br = kr;
+              ir = static_cast<uint32_t>(v);
+            }
+          }
+        }
+      }
+    }
+  }
+  unsigned long long kp = ip != 0xFFFFFFFFu ? pack_key(bp, ip) : 0ull;
+  unsigned long long kr = ir != 0xFFFFFFFFu ? pack_key(br, ir) : 0ull;
+  kp = wave_max64(kp);
+  kr = wave_max64(kr);
+  if ((threadIdx.x & 63) == 0) {
+    sk[0][threadIdx.x >> 6] = kp;
+    sk[1][threadIdx.x >> 6] = kr;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int w = threadIdx.x;
+    const unsigned long long key = umax64(umax64(sk[w][0], sk[w][1]), umax64(sk[w][2], sk[w][3]));
+    if (key != 0ull)
+      atomicMax(&g.dslots[(b * kDrawSlots + blockIdx.y % kDrawSlots) * 2 + w], key);
+    BDR_WAIT_ALL_MEM();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned w = blockIdx.y * gridDim.x + blockIdx.x;
+    last = arrive_group(g.dgcnt, w, total) && arrive_top(g.dtcnt, total);
+  }
+  __syncthreads();
+  if (!last) return;
+  // one thread per row: fold the slots, emit the token, clear the slots
+  for (int64_t r = threadIdx.x; r < g.B; r += blockDim.x) {
+    unsigned long long* sl = g.dslots + r * kDrawSlots * 2;
+    unsigned long long t[kDrawSlots * 2];
+#pragma unroll
+    for (int i = 0; i < kDrawSlots * 2; ++i) t[i] = fetch_u64(sl + i);
+    unsigned long long mp = 0ull, mr = 0ull;
+#pragma unroll
+    for (int i = 0; i < kDrawSlots; ++i) {
+      mp = umax64(mp, t[2 * i]);
+      mr = umax64(mr, t[2 * i + 1]);
+    }
+    const bool rr = g.dec[r].y != 0;
+    g.bonus[r] = key_index(rr && mr != 0ull ? mr : mp);
+#pragma unroll
+    for (int i = 0; i < kDrawSlots * 2; ++i) publish_u64(sl + i, 0ull);
+  }
+  if (threadIdx.x < kArriveGroups) g.dgcnt[threadIdx.x * kLineWords] = 0u;
+  if (threadIdx.x == 0) *g.dtcnt = 0u;
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+// LSE pass: about 2048 workgroups, at most kMaxLseChunks chunks of >= 2048 entries per row
+static void lse_plan(int64_t B, int k, int64_t V, int* chunks, int64_t* len) {
+  const int64_t rows = std::max<int64_t>(1, B * k);
+  int64_t c = std::max<int64_t>(1, (2048 + rows - 1) / rows);
+  c = std::min<int64_t>(c, std::max<int64_t>(1, (V + 2047) / 2048));
+  c = std::min<int64_t>(c, kMaxLseChunks);
+  int64_t l = (V + c - 1) / c;
+  l = (l + 7) / 8 * 8;
+  *len = l;
+  *chunks = static_cast<int>((V + l - 1) / l);
+}
+
+// draw pass: about 2048 workgroups, chunks of >= 1024 entries
+static void draw_plan(int64_t B, int64_t V, int* chunks, int64_t* len) {
+  const int64_t rows = std::max<int64_t>(1, B);
+  int64_t c = std::max<int64_t>(1, (2048 + rows - 1) / rows);
+  c = std::min<int64_t>(c, std::max<int64_t>(1, (V + 1023) / 1024));
+  c = std::min<int64_t>(c, 4096);
+  int64_t l = (V + c - 1) / c;
+  l = (l + 3) / 4 * 4;
+  *len = l;
+  *chunks = static_cast<int>((V + l - 1) / l);
+}
+
+struct SampleLayout {
+  size_t part, dec, slots, cnt1, cnt2, total;
+};
+
+static SampleLayout sample_layout(int64_t B, int k, int64_t V) {
+  int c;
+  int64_t l;
+  lse_plan(B, k, V, &c, &l);
+  SampleLayout s{};
+  s.part = 0;
+  s.dec = s.part + align256(static_cast<size_t>(2) * B * k * c * 8);
+  s.slots = s.dec + align256(static_cast<size_t>(B) * 16);
+  s.cnt1 = s.slots + align256(static_cast<size_t>(B) * kDrawSlots * 2 * 8);
+  s.cnt2 = s.cnt1 + kArriveGroups * 128 + 256;
+  s.total = s.cnt2 + kArriveGroups * 128 + 256;
+  return s;
+}
+
+size_t sample_verify_workspace(int64_t B, int k, int64_t V) { return sample_layout(B, k, V).total; }
+
+hipError_t launch_verify_sample(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
+                                const int32_t* draft, const float* X, const float* conf,
+                                float threshold, float inv_t, uint64_t seed, int32_t* block_len,
+                                int32_t* accepted, int32_t* bonus, int64_t* acc, int64_t* prop,
+                                void* workspace, hipStream_t stream) {
+  SampleArgs g{};
+  g.Y = Y;
+  g.X = X;
+  g.B = B;
+  g.V = V;
+  g.k = k;
+  g.draft = draft;
+  g.conf = conf;
+  g.th = threshold;
+  g.use_conf = (conf != nullptr && !std::isnan(threshold)) ? 1 : 0;
+  g.inv_t = inv_t;
+  g.k0 = static_cast<uint32_t>(seed);
+  g.k1 = static_cast<uint32_t>(seed >> 32);
+  lse_plan(B, k, V, &g.chunks, &g.chunk_len);
+  draw_plan(B, V, &g.dchunks, &g.dchunk_len);
+  const SampleLayout lay = sample_layout(B, k, V);
+  char* ws = static_cast<char*>(workspace);
+  g.part = reinterpret_cast<unsigned long long*>(ws + lay.part);
+  g.dec = reinterpret_cast<int4*>(ws + lay.dec);
+  g.dslots = reinterpret_cast<unsigned long long*>(ws + lay.slots);
+  g.gcnt = reinterpret_cast<unsigned*>(ws + lay.cnt1);
+  g.tcnt = reinterpret_cast<unsigned*>(ws + lay.cnt1 + kArriveGroups * 128);
+  g.dgcnt = reinterpret_cast<unsigned*>(ws + lay.cnt2);
+  g.dtcnt = reinterpret_cast<unsigned*>(ws + lay.cnt2 + kArriveGroups * 128);
+  g.block_len = block_len;
+  g.accepted = accepted;
+  g.bonus = bonus;
+  g.acc = acc;
+  g.prop = prop;
+  const dim3 grid1(static_cast<unsigned>(B * k), static_cast<unsigned>(g.chunks));
+  const dim3 grid2(static_cast<unsigned>(B), static_cast<unsigned>(g.dchunks));
+  if (dt == BDR_BF16) {
+    if (V % 8 == 0)
+      hipLaunchKernelGGL((sample_lse_kernel<uint16_t, true>), grid1, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((sample_lse_kernel<uint16_t, false>), grid1, dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((sample_draw_kernel<uint16_t>), grid2, dim3(256), 0, stream, g);
+  } else {
+    if (V % 8 == 0)
+      hipLaunchKernelGGL((sample_lse_kernel<float, true>), grid1, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((sample_lse_kernel<float, false>), grid1, dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((sample_draw_kernel<float>), grid2, dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bdr

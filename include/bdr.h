@@ -208,6 +208,87 @@ int spec_verify_greedy(const void* target_logits, bdr_dtype dt, int64_t batch,
                        int64_t* proposed_counts, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Probabilistic drafting and rejection-sampling verification.
+ *
+ * The model card's recommended serving mode draws the draft tokens
+ * probabilistically ([card] "Usage", "Tuning notes"), and speculative decoding
+ * there is verified by rejection sampling ([pr128] "Not covered").  The pages
+ * give no further arithmetic; the standard speculative-sampling rule is used
+ * (Leviathan, Kalman and Matias, ICML 2023; Chen et al., 2023), which makes
+ * the emitted tokens distributed exactly as tokens sampled from the target.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC 2011) keyed by the 64-bit
+ * `seed` (low word = key word 0).  The uniform of vocabulary entry v at (row
+ * b, position i) of a stream is word v % 4 of Philox((v / 4, b, i, stream)),
+ * u = ((x >> 9) + 0.5) * 2^-23; Gumbel noise is -log(-log u).  Streams: 0 the
+ * draft draws, 1 the acceptance tests (v = 0), 2 the residual / bonus draws.
+ * Callers pass a fresh seed per step (the counters do not include a step).
+ * temperature T must be finite and > 0 (T -> 0 is the greedy path above).
+ * ------------------------------------------------------------------------- */
+
+/* noise[b, i, v] = Gumbel noise of `stream_id` at (b, i, v): [B, k, V] fp32.
+ * 1 <= k <= BDR_MAX_K, 0 < V <= 2^21, 0 <= stream_id. */
+int dspark_gumbel_noise(int64_t batch, int k, int64_t vocab, uint64_t seed,
+                        int stream_id, float* noise, void* stream);
+
+/* dspark_markov_sample -- S3 with probabilistic drafting.
+ *
+ * As dspark_markov_argmax, except that position i's token is drawn from
+ *     q_i = softmax(x_i / T),  x_i[v] = logits[b, i, v] + bias(context)[v]
+ * by the Gumbel-max rule with stream-0 noise:
+ *     d[b, i] = min{ v : x_i[v] / T + G[b, i, v] is maximal }
+ * and the drawn token is the next position's context.  x is written out: it
+ * is the draft distribution that spec_verify_sample needs.
+ *
+ *   logits, batch, k, vocab, wdt, markov_w1/w2, rank, prev_token: as S3
+ *   temperature T > 0; seed as above
+ *   draft_tokens [B, k] int32 out
+ *   draft_logits [B, k, V] fp32 out (x, before the division by T)
+ *   workspace    >= dspark_markov_sample_workspace_bytes(B, k, V): the draw
+ *                noise, then a Markov workspace (same rules as S3; its error
+ *                word is in the last 256 bytes of this size)
+ * ------------------------------------------------------------------------- */
+size_t dspark_markov_sample_workspace_bytes(int64_t batch, int k, int64_t vocab);
+int dspark_markov_sample(const float* logits, int64_t batch, int k,
+                         int64_t vocab, bdr_dtype wdt, const void* markov_w1,
+                         const void* markov_w2, int rank,
+                         const int32_t* prev_token, float temperature,
+                         uint64_t seed, int32_t* draft_tokens,
+                         float* draft_logits, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* spec_verify_sample -- S4 by rejection sampling.
+ *
+ *   L_b as in spec_verify_greedy;  p_j = softmax(Y[b, j] / T),
+ *   q_j = softmax(draft_logits[b, j] / T), r_j the stream-1 uniform of (b, j)
+ *   a_b   = first j < L_b with NOT (r_j * q_j(d_j) < p_j(d_j)), else L_b
+ *           (a draft token outside [0, V) is rejected)
+ *   bonus = a_b < L_b: drawn from max(0, p_a - q_a) (from p_a if that is
+ *                      zero everywhere);  a_b == L_b: drawn from p_{L_b};
+ *           by the Gumbel-max rule with the stream-2 noise of (b, a_b)
+ *   accept_counts / proposed_counts as in spec_verify_greedy
+ * Decisions are taken in fp32 (log domain for the acceptance test); they
+ * agree with an exact evaluation except within rounding of a tie.
+ *
+ *   target_logits [B, k+1, V] dtype (finite); draft_tokens [B, k] int32
+ *   draft_logits  [B, k, V] fp32 (finite), as written by dspark_markov_sample
+ *   confidence    [B, k] fp32 or NULL; threshold as in spec_verify_greedy
+ *   temperature   T > 0, seed: the same conventions as dspark_markov_sample
+ *                 (the streams differ, so the drafting seed may be reused)
+ *   block_len, accepted, bonus [B] int32 out
+ *   accept_counts, proposed_counts [k] int64, ACCUMULATED (+=), optional
+ *   workspace     >= spec_verify_sample_workspace_bytes(B, k, V)
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_sample_workspace_bytes(int64_t batch, int k, int64_t vocab);
+int spec_verify_sample(const void* target_logits, bdr_dtype dt, int64_t batch,
+                       int k, int64_t vocab, const int32_t* draft_tokens,
+                       const float* draft_logits, const float* confidence,
+                       float threshold, float temperature, uint64_t seed,
+                       int32_t* block_len, int32_t* accepted, int32_t* bonus,
+                       int64_t* accept_counts, int64_t* proposed_counts,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

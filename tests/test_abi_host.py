@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 1
+    assert L.bdr_abi_version() == 2
 
 
 def test_workspace_sizes(L):
@@ -158,6 +158,53 @@ def test_verify_validation(L):
     assert f(V=0) == A.BDR_EINVAL
     assert f() == A.BDR_EWORKSPACE
     assert f(B=0) == A.BDR_OK
+
+
+def test_sampling_workspace_sizes(L):
+    a256 = lambda x: (x + 255) // 256 * 256
+    markov = lambda B, k: a256(8 * 16 * B * k) + a256(8 * 256 * B * k) + a256(8 * B * k) + 256 + 256
+    V = 151936
+    # the draw noise [B, k, V] fp32 in front of a greedy Markov workspace
+    assert L.dspark_markov_sample_workspace_bytes(1, 7, V) == a256(7 * V * 4) + markov(1, 7)
+    assert L.dspark_markov_sample_workspace_bytes(16, 8, 1000) == a256(16 * 8 * 1000 * 4) + markov(16, 8)
+    assert L.dspark_markov_sample_workspace_bytes(1, 7, (1 << 21) + 1) == 0
+    v = L.spec_verify_sample_workspace_bytes(16, 8, V)
+    assert v > 0 and v % 256 == 0
+    assert L.spec_verify_sample_workspace_bytes(1, 17, V) == 0
+
+
+def test_sampling_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    ws = C.c_void_p(4096)
+    m = lambda T=1.0, B=4, k=8, V=1000, r=64, x=P, prev=P, wp=ws, wn=4096: \
+        L.dspark_markov_sample(P, B, k, V, A.BDR_BF16, P, P, r, prev, T, 7, P, x, wp, wn, None)
+    assert m(T=0.0) == A.BDR_EINVAL
+    assert m(T=-1.0) == A.BDR_EINVAL
+    assert m(T=float("nan")) == A.BDR_EINVAL
+    assert m(T=float("inf")) == A.BDR_EINVAL
+    assert m(T=1e-45) == A.BDR_EUNSUPPORTED           # 1 / T overflows
+    assert m(x=None) == A.BDR_EINVAL                   # draft_logits are an output
+    assert m(prev=None) == A.BDR_EINVAL
+    assert m(k=17) == A.BDR_EUNSUPPORTED
+    assert m(r=60) == A.BDR_EUNSUPPORTED
+    assert m(wn=8) == A.BDR_EWORKSPACE
+    assert m(B=0) == A.BDR_OK
+    assert m(B=0, T=0.0) == A.BDR_EINVAL                # scalars are checked first
+    v = lambda T=1.0, y=P, x=P, dt=A.BDR_BF16, B=4, wp=None, wn=0: \
+        L.spec_verify_sample(y, dt, B, 8, 1000, P, x, None, 0.3, T, 7, P, P, P, None, None, wp, wn,
+                             None)
+    assert v(T=0.0) == A.BDR_EINVAL
+    assert v(y=None) == A.BDR_EINVAL
+    assert v(x=None) == A.BDR_EINVAL
+    assert v(dt=3) == A.BDR_EINVAL
+    assert v() == A.BDR_EWORKSPACE
+    assert v(B=0) == A.BDR_OK
+    n = lambda B=2, k=3, V=1000, sid=0, out=P: L.dspark_gumbel_noise(B, k, V, 1, sid, out, None)
+    assert n(sid=-1) == A.BDR_EINVAL
+    assert n(out=None) == A.BDR_EINVAL
+    assert n(V=(1 << 21) + 1) == A.BDR_EUNSUPPORTED
+    assert n(B=0) == A.BDR_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

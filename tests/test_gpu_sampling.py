@@ -1,0 +1,284 @@
+"""GPU parity of probabilistic drafting and rejection-sampling verification.
+
+Expected values come only from the CPU oracle (oracle.sampling) on the same
+seeded inputs; both sides run their own Philox4x32-10.  Integer results
+(tokens, accept lengths, counts) must match exactly wherever the oracle's
+decision is not within rounding of a tie:
+  * draft draws: the oracle's top-2 Gumbel-key gap below NEAR_TIE starts the
+    usual cascade (later positions of the row depend on that token);
+  * acceptance tests: relative margin |r q - p| / max(p, q) below 1e-3;
+  * residual / bonus draws: key gap below NEAR_TIE.
+Rows that hit one of these are reported and left out; the tests assert that
+only a few are.  A statistical test checks losslessness on the GPU alone
+against closed forms.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import sampling as S
+from workloads import synth
+from gpu_util import NEAR_TIE, dev, first_near_tie, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MARGIN_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_draft_readout_amd as bdr
+    bdr.lib()
+
+
+def bdr():
+    import block_draft_readout_amd as m
+    return m
+
+
+def _markov(cid, V, r, dtype):
+    w1 = synth.store(synth.normal_f32((V, r), (cid, 0, 0, 2), 1.0), dtype)
+    w2 = synth.store(synth.normal_f32((V, r), (cid, 0, 0, 3), np.sqrt(0.1)), dtype)
+    return w1, w2
+
+
+def _logits(cid, B, k, V, std):
+    return synth.normal_f32((B, k, V), (cid, 1, 0, 1), std)
+
+
+# ----------------------------------------------------------------------------- generator
+@pytest.mark.parametrize("stream", [0, 2])
+def test_gumbel_noise_matches_the_generator(stream):
+    B, k, V, seed = 3, 4, 1003, 0x0123456789ABCDEF
+    log(f"noise B={B} k={k} V={V} stream={stream}")
+    got = bdr().dspark_gumbel_noise(B, k, V, seed, stream).cpu().numpy().astype(np.float64)
+    ref = np.stack([np.stack([S.gumbel(S.uniforms(seed, stream, b, i, V)) for i in range(k)])
+                    for b in range(B)])
+    err = np.abs(got - ref)
+    log(f"  max abs err {err.max():.3e}")
+    assert np.all(err <= 1e-6 + 1e-6 * np.abs(ref))
+    # the uniforms recovered from the noise sit on the generator's own grid points
+    m_ref = np.round(np.exp(-np.exp(-ref)) * 2.0 ** 23 - 0.5)
+    m_got = np.round(np.exp(-np.exp(-got)) * 2.0 ** 23 - 0.5)
+    assert np.mean(m_ref == m_got) > 0.95
+
+
+def test_gumbel_noise_seeds_and_streams_differ():
+    a = bdr().dspark_gumbel_noise(1, 2, 4096, 5, 0)
+    b = bdr().dspark_gumbel_noise(1, 2, 4096, 6, 0)
+    c = bdr().dspark_gumbel_noise(1, 2, 4096, 5, 2)
+    assert not torch.equal(a, b) and not torch.equal(a, c)
+    assert torch.equal(a, bdr().dspark_gumbel_noise(1, 2, 4096, 5, 0))
+
+
+# ----------------------------------------------------------------------------- drafting
+DRAFT_CASES = {
+    # name: (B, k, V, rank, dtype, logit std, temperature)
+    "tiny_f32": (1, 4, 1000, 8, "f32", 2.0, 1.0),
+    "f32_ragged": (5, 6, 2053, 12, "f32", 3.0, 0.7),
+    "bf16_b5": (5, 7, 5003, 64, "bf16", 2.5, 1.0),
+    "bf16_b20": (20, 3, 1031, 8, "bf16", 2.0, 1.3),
+    "no_bias": (3, 5, 4099, 0, "bf16", 2.0, 0.8),
+    "f32_r128_passes": (2, 3, 3001, 128, "f32", 2.0, 1.0),   # per-position launches
+    "qwen_vocab": (1, 7, 151936, 32, "bf16", 3.0, 1.0),
+    "b16_vocab": (16, 7, 151936, 64, "bf16", 3.0, 0.9),
+}
+
+
+@pytest.mark.parametrize("name", list(DRAFT_CASES))
+def test_markov_sample_parity(name):
+    B, k, V, r, dtype, std, T = DRAFT_CASES[name]
+    cid = 70 + list(DRAFT_CASES).index(name)
+    seed = 1000 + cid
+    Z = _logits(cid, B, k, V, std)
+    w1, w2 = _markov(cid, V, r, dtype) if r else (None, None)
+    prev = np.random.default_rng(cid).integers(0, V, B).astype(np.int32)
+    log(f"markov sample {name}: B={B} k={k} V={V} r={r} {dtype} T={T}")
+    d_ref, gap, x_ref = S.semi_ar_sample(Z, w1, w2, prev, dtype, T, seed)
+    d, x = bdr().dspark_markov_sample(dev(Z), dev(w1) if r else None, dev(w2) if r else None,
+                                      dev(prev), T, seed)
+    d, x = d.cpu().numpy(), x.cpu().numpy()
+    istar = first_near_tie(gap)
+    n_cmp = 0
+    for b in range(B):
+        m = int(istar[b])
+        assert np.array_equal(d[b, :m], d_ref[b, :m]), (b, d[b], d_ref[b], gap[b])
+        n_cmp += m
+        # x of every position whose context agrees (through the first near-tie)
+        top = min(m + 1, k)
+        diff = np.abs(x[b, :top].astype(np.float64) - x_ref[b, :top])
+        assert np.all(diff <= 1e-4 * (1 + np.abs(x_ref[b, :top]))), (b, diff.max())
+    log(f"  {n_cmp}/{B * k} draws compared, {B * k - n_cmp} after a near-tie")
+    assert n_cmp >= 0.9 * B * k
+
+
+def test_small_temperature_is_the_greedy_chain():
+    B, k, V, r = 4, 6, 5003, 64
+    Z = _logits(90, B, k, V, 3.0)
+    w1, w2 = _markov(90, V, r, "bf16")
+    prev = np.arange(B, dtype=np.int32) * 7
+    dg = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+    ds, _ = bdr().dspark_markov_sample(dev(Z), dev(w1), dev(w2), dev(prev), 1e-6, 3)
+    d_ref, gap = oracle.semi_ar_argmax(Z, w1, w2, prev, "bf16")
+    istar = first_near_tie(gap)
+    for b in range(B):
+        m = int(istar[b])
+        assert np.array_equal(ds.cpu().numpy()[b, :m], dg[b, :m])
+
+
+def test_markov_sample_repeat_and_workspace_reuse():
+    B, k, V, r = 3, 5, 7001, 32
+    Z = dev(_logits(91, B, k, V, 2.0))
+    w1, w2 = (dev(t) for t in _markov(91, V, r, "bf16"))
+    prev = dev(np.array([1, 2, 3], dtype=np.int32))
+    L = bdr().lib()
+    ws = torch.zeros(L.dspark_markov_sample_workspace_bytes(B, k, V) + 256, dtype=torch.uint8,
+                     device="cuda")
+    a = bdr().dspark_markov_sample(Z, w1, w2, prev, 1.0, 11, workspace=ws)
+    b = bdr().dspark_markov_sample(Z, w1, w2, prev, 1.0, 11, workspace=ws)
+    c = bdr().dspark_markov_sample(Z, w1, w2, prev, 1.0, 12, workspace=ws)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert not torch.equal(a[0], c[0])
+    # the error word (first 4 of the last 256 bytes) stays clear
+    n = L.dspark_markov_sample_workspace_bytes(B, k, V)
+    base = (ws.data_ptr() + 255) // 256 * 256 - ws.data_ptr()
+    assert int(ws[base + n - 256: base + n - 252].sum()) == 0
+
+
+# ----------------------------------------------------------------------------- verification
+def _verify_inputs(cid, B, k, V, std, T, dtype, corr):
+    """Oracle-drafted block and target logits y = corr * x + noise (acceptance
+    rates between the extremes)."""
+    Z = _logits(cid, B, k, V, std)
+    d, _, x = S.semi_ar_sample(Z, None, None, np.zeros(B, np.int32), "f32", T, cid)
+    noise = synth.normal_f32((B, k + 1, V), (cid, 1, 0, 3), std)
+    y = noise.copy()
+    y[:, :k] = corr * x + (1 - corr) * noise[:, :k]
+    return d.astype(np.int32), x, synth.store(y, dtype)
+
+
+def _clean_rows(ref, B):
+    ok = np.ones(B, dtype=bool)
+    for b in range(B):
+        a = int(ref["accepted"][b])
+        tested = ref["margin"][b, :min(a + 1, ref["margin"].shape[1])]
+        if np.any(tested < MARGIN_TOL) or ref["draw_gap"][b] < NEAR_TIE:
+            ok[b] = False
+    return ok
+
+
+VERIFY_CASES = {
+    # name: (B, k, V, dtype, std, T, corr, threshold)
+    "tiny_f32": (6, 4, 1000, "f32", 2.0, 1.0, 0.8, None),
+    "bf16_ragged": (9, 5, 4099, "bf16", 2.0, 0.8, 0.9, None),     # scalar LSE path
+    "bf16_adaptive": (16, 8, 5000, "bf16", 2.0, 1.0, 0.85, 0.3),  # truncated blocks, L = 0 rows
+    "f32_low_accept": (7, 6, 2048, "f32", 3.0, 1.2, 0.3, None),
+    "bf16_b64": (64, 3, 1536, "bf16", 2.0, 1.0, 0.9, None),
+    "qwen_vocab": (1, 7, 151936, "bf16", 3.0, 1.0, 0.95, None),
+    "b16_vocab": (16, 7, 151936, "bf16", 3.0, 1.0, 0.9, None),
+}
+
+
+@pytest.mark.parametrize("name", list(VERIFY_CASES))
+def test_verify_sample_parity(name):
+    B, k, V, dtype, std, T, corr, th = VERIFY_CASES[name]
+    cid = 100 + list(VERIFY_CASES).index(name)
+    seed = 5000 + cid
+    d, x, Y = _verify_inputs(cid, B, k, V, std, T, dtype, corr)
+    conf = None
+    if th is not None:
+        conf = np.random.default_rng(cid).random((B, k), dtype=np.float32)
+        conf[0, 0] = 0.0                       # row 0: empty block
+    L = oracle.truncate_by_confidence(conf, th, B, k)
+    log(f"verify sample {name}: B={B} k={k} V={V} {dtype} T={T}")
+    ref = S.verify_sample(d, x, Y, dtype, L, T, seed)
+    acc = torch.zeros(k, dtype=torch.int64, device="cuda")
+    prop = torch.zeros(k, dtype=torch.int64, device="cuda")
+    out = bdr().spec_verify_sample(dev(Y), dev(d), dev(x), T, seed,
+                                   confidence=dev(conf) if conf is not None else None,
+                                   threshold=th if th is not None else float("nan"),
+                                   accept_counts=acc, proposed_counts=prop)
+    got = {n: t.cpu().numpy() for n, t in out.items()}
+    assert np.array_equal(got["block_len"], L)
+    clean = _clean_rows(ref, B)
+    log(f"  accepted {ref['accepted'].tolist()[:16]}; {int((~clean).sum())} rows near a tie")
+    assert clean.sum() >= B - max(1, B // 10)
+    assert np.array_equal(got["accepted"][clean], ref["accepted"][clean])
+    assert np.array_equal(got["bonus"][clean], ref["bonus"][clean])
+    if clean.all():
+        assert np.array_equal(acc.cpu().numpy(), ref["accept_counts"])
+        assert np.array_equal(prop.cpu().numpy(), ref["proposed_counts"])
+
+
+def test_out_of_range_draft_token_is_rejected():
+    B, k, V = 2, 3, 1000
+    d, x, Y = _verify_inputs(120, B, k, V, 2.0, 1.0, "f32", 1.0)
+    d[0, 0] = V + 5
+    d[1, 1] = -1
+    out = bdr().spec_verify_sample(dev(Y), dev(d), dev(x), 1.0, 9)
+    a = out["accepted"].cpu().numpy()
+    assert a[0] == 0 and a[1] <= 1
+
+
+def test_identical_distributions_accept_everything():
+    B, k, V = 32, 5, 3000
+    d, x, _ = _verify_inputs(121, B, k, V, 2.0, 1.0, "f32", 1.0)
+    Y = np.concatenate([x, x[:, :1]], axis=1)
+    out = bdr().spec_verify_sample(dev(Y), dev(d), dev(x), 1.0, 4)
+    assert np.all(out["accepted"].cpu().numpy() == k)
+
+
+def test_sampling_is_lossless_on_the_gpu():
+    """Many independent rows of one tiny case: the first emitted token follows
+    p_0 and position 0 is accepted with probability sum_v min(p_0, q_0)
+    (5 standard deviations)."""
+    B, k, V, T = 8192, 2, 8, 1.0
+    rng = np.random.default_rng(7)
+    z = (rng.standard_normal((1, k, V)) * 1.5).astype(np.float32)
+    yrow = (rng.standard_normal((1, k + 1, V)) * 1.5).astype(np.float32)
+    Z = np.repeat(z, B, axis=0)
+    Y = np.repeat(yrow, B, axis=0)
+    prev = np.zeros(B, dtype=np.int32)
+    d, x = bdr().dspark_markov_sample(dev(Z), None, None, dev(prev), T, 77)
+    out = bdr().spec_verify_sample(dev(Y), d, x, T, 78)
+    d = d.cpu().numpy()
+    a = out["accepted"].cpu().numpy()
+    bonus = out["bonus"].cpu().numpy()
+    first = np.where(a >= 1, d[:, 0], bonus)
+    p0 = np.exp(yrow[0, 0] - yrow[0, 0].max()).astype(np.float64)
+    p0 /= p0.sum()
+    q0 = np.exp(z[0, 0] - z[0, 0].max()).astype(np.float64)
+    q0 /= q0.sum()
+    # the draft draws themselves follow q_0
+    for v in range(V):
+        c = np.sum(d[:, 0] == v)
+        assert abs(c - B * q0[v]) <= 5 * np.sqrt(B * q0[v] * (1 - q0[v])) + 1, ("q", v)
+        c = np.sum(first == v)
+        assert abs(c - B * p0[v]) <= 5 * np.sqrt(B * p0[v] * (1 - p0[v])) + 1, ("p", v)
+    pa = float(np.minimum(p0, q0).sum())
+    assert abs(np.sum(a >= 1) - B * pa) <= 5 * np.sqrt(B * pa * (1 - pa)) + 1
+
+
+def test_end_to_end_block_matches_oracle_on_gpu_draft():
+    """Drafting and verification chained on the device; the oracle verifies the
+    GPU's own draft (tokens and draft logits) with the same seed."""
+    B, k, V, r, T = 4, 6, 9001, 32, 1.0
+    Z = _logits(130, B, k, V, 2.5)
+    w1, w2 = _markov(130, V, r, "bf16")
+    prev = np.array([5, 6, 7, 8], dtype=np.int32)
+    noise = synth.normal_f32((B, k + 1, V), (130, 1, 0, 3), 2.5)
+    d, x = bdr().dspark_markov_sample(dev(Z), dev(w1), dev(w2), dev(prev), T, 131)
+    xh = x.cpu().numpy()
+    Y = noise.copy()
+    Y[:, :k] = 0.9 * xh + 0.1 * noise[:, :k]
+    Yb = synth.store(Y, "bf16")
+    out = bdr().spec_verify_sample(dev(Yb), d, x, T, 132)
+    ref = S.verify_sample(d.cpu().numpy(), xh, Yb, "bf16", np.full(B, k), T, 132)
+    clean = _clean_rows(ref, B)
+    assert clean.sum() >= B - 1
+    assert np.array_equal(out["accepted"].cpu().numpy()[clean], ref["accepted"][clean])
+    assert np.array_equal(out["bonus"].cpu().numpy()[clean], ref["bonus"][clean])
