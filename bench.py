@@ -68,8 +68,9 @@ def recorded_traffic(workload: str):
 class Step:
     """Pre-bound C-ABI calls of one pool slot (pointers resolved once)."""
 
-    def __init__(self, L, w, dt, g, slot, bufs, stream):
+    def __init__(self, L, w, dt, g, slot, bufs, stream, sample=None):
         self.L, self.w, self.dt, self.g, self.s, self.b = L, w, dt, g, slot, bufs
+        self.sample = sample      # None: greedy; else (temperature, seed)
         self.stream = stream
         self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
@@ -88,6 +89,12 @@ class Step:
 
     def markov(self):
         w, b = self.w, self.b
+        if self.sample is not None:
+            T, seed = self.sample
+            return self.L.dspark_markov_sample(
+                b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt, self.g["w1"].data_ptr(),
+                self.g["w2"].data_ptr(), w.rank, self.s["prev0"].data_ptr(), T, seed,
+                b["d"].data_ptr(), b["x"].data_ptr(), b["ws_ms"], b["ws_ms_n"], self.stream)
         return self.L.dspark_markov_argmax(b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt,
                                            self.g["w1"].data_ptr(), self.g["w2"].data_ptr(),
                                            w.rank, self.s["prev0"].data_ptr(), b["d"].data_ptr(),
@@ -106,6 +113,13 @@ class Step:
         w, b = self.w, self.b
         conf = self.s.get("conf")
         th = float("nan") if w.threshold is None else w.threshold
+        if self.sample is not None:
+            T, seed = self.sample
+            return self.L.spec_verify_sample(
+                self.s["Y"].data_ptr(), self.dt, w.batch, w.k, w.vocab, b["d"].data_ptr(),
+                b["x"].data_ptr(), None if conf is None else conf.data_ptr(), th, T, seed,
+                b["bl"].data_ptr(), b["acc_len"].data_ptr(), b["bonus"].data_ptr(),
+                b["acc"].data_ptr(), b["prop"].data_ptr(), b["ws_vs"], b["ws_vs_n"], self.stream)
         return self.L.spec_verify_greedy(
             self.s["Y"].data_ptr(), self.dt, w.batch, w.k, w.vocab, b["d"].data_ptr(),
             None if conf is None else conf.data_ptr(), th, b["bl"].data_ptr(),
@@ -119,10 +133,12 @@ def check(rc, what):
         raise RuntimeError(f"{what} failed ({rc}): {bdr.lib().bdr_last_error().decode()}")
 
 
-def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30):
+def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None):
     """The oracle, as it stands, on whole block-steps of the workload: repeats
-    the step of pool slot 0 until about ``budget_s`` seconds of CPU work."""
+    the step of pool slot 0 until about ``budget_s`` seconds of CPU work.
+    ``sample`` = (temperature, seed) times the probabilistic path instead."""
     import oracle
+    from oracle import sampling
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -131,16 +147,24 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30):
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.block_step(w.dtype, slot_host["taps"], W["fc_w"], slot_host["draft_hidden"],
-                          W["lm_w"], W["w1"], W["w2"], slot_host["prev0"],
-                          target_logits=slot_host["Y"], confidence=slot_host["conf"],
-                          threshold=w.threshold)
+        if sample is None:
+            oracle.block_step(w.dtype, slot_host["taps"], W["fc_w"], slot_host["draft_hidden"],
+                              W["lm_w"], W["w1"], W["w2"], slot_host["prev0"],
+                              target_logits=slot_host["Y"], confidence=slot_host["conf"],
+                              threshold=w.threshold)
+        else:
+            oracle.fuse_fc(slot_host["taps"], W["fc_w"], w.dtype)
+            Z = oracle.lm_head(slot_host["draft_hidden"], W["lm_w"], w.dtype)
+            sampling.block_step_sample(w.dtype, Z, W["w1"], W["w2"], slot_host["prev0"],
+                                       slot_host["Y"], sample[0], sample[1],
+                                       confidence=slot_host["conf"], threshold=w.threshold)
         n += 1
         dt = time.perf_counter() - t0
         if dt >= budget_s or n >= max_steps:
             break
     return {"value": n / dt, "unit": "block-steps/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{n} full block-steps of {w.name} (S1-S4, all {w.batch} rows) in "
+            "sample": f"{n} full {'probabilistic' if sample else 'greedy'} block-steps of "
+                      f"{w.name} (S1-S4, all {w.batch} rows) in "
                       f"{dt:.1f} s on the host; numpy float64 with BLAS threads={blas}, "
                       f"affinity cores={len(os.sched_getaffinity(0))}"}
 
@@ -157,6 +181,10 @@ def main():
                     help="run the fc on a second stream, concurrently with the LM head "
                          "(lm) or with the Markov chain and verification (chain); the fc "
                          "output feeds the next step's drafter, not S2-S4 of this step")
+    ap.add_argument("--draft", choices=("greedy", "sample"), default="greedy",
+                    help="greedy drafting + exact-match verification, or probabilistic "
+                         "drafting + rejection-sampling verification")
+    ap.add_argument("--temperature", type=float, default=1.0, help="sampling temperature")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
@@ -210,9 +238,14 @@ def main():
             "targ": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
             "acc": torch.zeros(k, dtype=torch.int64, device=dev),
             "prop": torch.zeros(k, dtype=torch.int64, device=dev)}
+    sampling = args.draft == "sample"
+    if sampling:
+        bufs["x"] = torch.empty((B, k, V), dtype=torch.float32, device=dev)
     for key, n in (("ws_fc", L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
                    ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
-                   ("ws_v", L.spec_verify_workspace_bytes(B, k, V))):
+                   ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
+                   ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
+                   ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0)):
         p, n2, t = ws(n)
         bufs[key], bufs[key + "_n"] = p, n2
         keep.append(t)
@@ -226,8 +259,11 @@ def main():
                 "prev0": up(s["prev0"])}
         conf = synth.make_confidence(w, p)
         slot["conf"] = None if conf is None else up(conf)
-        st = Step(L, w, dt, g, slot, bufs, sptr)
+        st = Step(L, w, dt, g, slot, bufs, sptr,
+                  sample=(args.temperature, 0x5EED0000 + p) if sampling else None)
         check(st.draft_block(), "dspark_draft_block")
+        if sampling:   # plant the targets on this step's sampled draft
+            check(st.markov(), "dspark_markov_sample")
         torch.cuda.synchronize()
         d_host = bufs["d"].cpu().numpy()
         Y = synth.plant_targets(w, p, s["noise"], d_host)["target_logits"]
@@ -247,8 +283,8 @@ def main():
         if args.overlap == "none":
             check(st.fc(), "dflash_fuse_fc")
             check(st.lm_head(), "dspark_lm_head")
-            check(st.markov(), "dspark_markov_argmax")
-            check(st.verify(), "spec_verify_greedy")
+            check(st.markov(), "drafting")
+            check(st.verify(), "verification")
             return
         main = torch.cuda.current_stream(dev)
         fc_ptr = st.fc_stream
@@ -261,8 +297,8 @@ def main():
         ev_join.record(stream2)
         if args.overlap == "lm":
             check(st.lm_head(), "dspark_lm_head")
-        check(st.markov(), "dspark_markov_argmax")
-        check(st.verify(), "spec_verify_greedy")
+        check(st.markov(), "drafting")
+        check(st.verify(), "verification")
         main.wait_event(ev_join)
         st.fc_stream = fc_ptr
 
@@ -312,8 +348,8 @@ def main():
         evs[i][0].record(stream)
         check(st.lm_head(), "dspark_lm_head")
         evs[i][1].record(stream)
-        check(st.markov(), "dspark_markov_argmax")
-        check(st.verify(), "spec_verify_greedy")
+        check(st.markov(), "drafting")
+        check(st.verify(), "verification")
     torch.cuda.synchronize()
     lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
@@ -352,7 +388,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one block-step ...")
-        cpu = cpu_baseline(w, W, host0)
+        cpu = cpu_baseline(w, W, host0,
+                           sample=(args.temperature, 0x5EED0000) if sampling else None)
         log(f"cpu oracle: {1.0 / cpu['value']:.1f} s per block-step")
 
     out = {
@@ -372,6 +409,8 @@ def main():
                    "rank": w.rank, "n_taps": w.n_taps,
                    "launch": "hip-graph" if graphs is not None else "eager",
                    "fc_overlap": args.overlap,
+                   "draft": args.draft,
+                   **({"temperature": args.temperature} if sampling else {}),
                    "pool_steps": args.pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,

@@ -298,6 +298,8 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
         uint32_t bi = 0xFFFFFFFFu;
         const bool row_ok = r16 < nb;
         rsrc_t rx;
+        f32x4_t xt = {0.f, 0.f, 0.f, 0.f};
+        uint32_t toff = kOOB;
         if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, block_bytes(b0));
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
@@ -310,7 +312,9 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
               bias = mma16(w2s[(tile_rd * RKS + c) * 64 + lane], ef[c], bias, S());
           }
           const int v0 = vbo + 16 * tile;
-          const bool tok = row_ok && tile < ntlo;
+          // entries of the lane's quad that exist (<= 0: none); a missing
+          // entry's key is -inf and never wins
+          const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
           f32x4_t xs;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -320,21 +324,28 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
               xs[i] = s;
               key = s * g.inv_t + __uint_as_float(gv[u][i]);
             }
-            if (tok && v0 + i < V32 && key > bv) {
+            key = i < lim ? key : -INFINITY;
+            if (key > bv) {
               bv = key;
               bi = static_cast<uint32_t>(v0 + i);
             }
           }
           if constexpr (SAMPLE) {
-            // x of the lane's four entries: one 16-byte store, element stores
-            // for the quad that straddles the end of the row
+            // x of the lane's four entries in one 16-byte store; the quad that
+            // straddles the end of the row (at most one per lane) is kept for
+            // element stores after the loop
             const uint32_t off = static_cast<uint32_t>(r16) * zrow + static_cast<uint32_t>(v0) * 4u;
-            const bool full = tok && v0 + 4 <= V32;
-            bstore16(xs, rx, full ? off : kOOB);
-            if (tok && !full) {
+            bstore16(xs, rx, lim >= 4 ? off : kOOB);
+            const bool part = lim > 0 && lim < 4;
+            xt = part ? xs : xt;
+            toff = part ? off : toff;
+          }
+        }
+        if constexpr (SAMPLE) {
+          const int tn = V32 & 3;   // entries of a straddling quad
+          if (toff != kOOB) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) bstore_f32(xs[i], rx, v0 + i < V32 ? off + 4u * i : kOOB);
-            }
+            for (int i = 0; i < 3; ++i) bstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
           }
         }
         // the next position's first logits: independent of the hand-off below

@@ -22,10 +22,13 @@
 //                        every (b, i, v), one Philox call per four entries.
 //   sample_lse_kernel    grid (row b*k+j, chunk), positions j < L_b only: the
 //                        (max, sum of exp) partials of y_j / T and x_j / T per
-//                        chunk.  The last workgroup to arrive folds them into
-//                        log-sum-exps, takes every row's accept decisions in
-//                        order (in the log domain: log r + log q < log p), and
-//                        records where and what the row still draws.
+//                        chunk, in base 2 (v_exp_f32 / v_log_f32 on values
+//                        scaled by log2(e) / T).  The last workgroup to arrive
+//                        folds them into log-sum-exps, tests every drafted
+//                        position (one thread each, in the log domain:
+//                        log r + log q < log p), takes each row's first
+//                        rejection, and records where and what the row still
+//                        draws.
 //   sample_draw_kernel   grid (row b, chunk): the residual (or bonus) draw of
 //                        each row's recorded position; chunk keys are folded
 //                        with atomic max into eight slots per row, and the last
@@ -133,14 +136,18 @@ __device__ __forceinline__ int sample_block_length(const SampleArgs& g, int64_t 
   return g.k;
 }
 
-// Running log-sum-exp state: m = max, s = sum exp(v - m); s == 0 means empty.
+// Running base-2 log-sum-exp state: m = max, s = sum 2^(v - m); s == 0 means
+// empty.  Values are natural logits scaled by log2(e) / T.
 struct Lse {
   float m, s;
 };
 
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ void lse_add(Lse& a, float f) {
   const float d = f - a.m;                // +inf on the first entry
-  const float e = expf(-fabsf(d));
+  const float e = exp2_hw(-fabsf(d));
   if (d > 0.f) {
     a.s = a.s * e + 1.f;
     a.m = f;
@@ -153,7 +160,7 @@ __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
   if (b.s == 0.f) return a;
   if (a.s == 0.f) return b;
   const float m = fmaxf(a.m, b.m);
-  return Lse{m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
+  return Lse{m, a.s * exp2_hw(a.m - m) + b.s * exp2_hw(b.m - m)};
 }
 
 __device__ __forceinline__ Lse lse_wave(Lse a) {
@@ -178,18 +185,21 @@ __device__ __forceinline__ float accept_uniform(const SampleArgs& g, int64_t b, 
   return bits_to_uniform(x.x);
 }
 
-// Fold the LSE partials into log-sum-exps, then take every row's accept
-// decisions.  Called by the whole last workgroup of the LSE pass.
+// Fold the LSE partials into log-sum-exps, test every drafted position, then
+// take each row's first rejection.  Called by the whole last workgroup of the
+// LSE pass.
 template <typename S>
 __device__ void sample_scan(const SampleArgs& g) {
   constexpr int GROUP = 64;
   __shared__ int Ls[GROUP];
-  __shared__ float lse[2][GROUP * BDR_MAX_K];
+  __shared__ float lse[2][GROUP * BDR_MAX_K];     // base 2
+  __shared__ unsigned char ok[GROUP * BDR_MAX_K];
   __shared__ int cacc[BDR_MAX_K];
   __shared__ int cprop[BDR_MAX_K];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int k = g.k;
+  const float c2 = g.inv_t * kLog2e;
   const S* Y = static_cast<const S*>(g.Y);
   if (tid < BDR_MAX_K) {
     cacc[tid] = 0;
@@ -215,35 +225,33 @@ __device__ void sample_scan(const SampleArgs& g) {
 #pragma unroll
       for (int c = 0; c < kMaxLseChunks; ++c)
         if (c < g.chunks) a = lse_merge(a, lse_unpack(v[c]));
-      lse[which][lb * k + j] = a.m + logf(a.s);
+      lse[which][lb * k + j] = a.m + log2_hw(a.s);
     }
     __syncthreads();
-    // one thread per row: the drafted entries of every tested position, then
-    // the accept tests in order
+    // one thread per (row, position < L): the acceptance test
+    for (int t = tid; t < nb * k; t += nthr) {
+      const int lb = t / k;
+      const int j = t - lb * k;
+      if (j >= Ls[lb]) continue;
+      const int64_t b = b0 + lb;
+      const int32_t d = g.draft[b * k + j];
+      bool acc = false;
+      if (d >= 0 && d < g.V) {
+        const float yd = to_f32<S>(Y[(b * (k + 1) + j) * g.V + d]);
+        const float xd = g.X[(b * k + j) * g.V + d];
+        const float lp = yd * c2 - lse[0][t];
+        const float lq = xd * c2 - lse[1][t];
+        acc = log2_hw(accept_uniform(g, b, j)) + lq < lp;
+      }
+      ok[t] = acc ? 1 : 0;
+    }
+    __syncthreads();
+    // one thread per row: the first rejection
     for (int lb = tid; lb < nb; lb += nthr) {
       const int64_t b = b0 + lb;
       const int L = Ls[lb];
-      int dd[BDR_MAX_K];
-#pragma unroll
-      for (int j = 0; j < BDR_MAX_K; ++j) dd[j] = j < L ? g.draft[b * k + j] : -1;
-      float yd[BDR_MAX_K], xd[BDR_MAX_K];
-#pragma unroll
-      for (int j = 0; j < BDR_MAX_K; ++j) {
-        const bool ok = j < L && dd[j] >= 0 && dd[j] < g.V;
-        yd[j] = ok ? to_f32<S>(Y[(b * (k + 1) + j) * g.V + dd[j]]) : 0.f;
-        xd[j] = ok ? g.X[(b * k + j) * g.V + dd[j]] : 0.f;
-      }
-      int a = L;
-#pragma unroll
-      for (int j = BDR_MAX_K - 1; j >= 0; --j) {
-        if (j < L) {
-          const bool ok = dd[j] >= 0 && dd[j] < g.V;
-          const float lp = yd[j] * g.inv_t - lse[0][lb * k + j];
-          const float lq = xd[j] * g.inv_t - lse[1][lb * k + j];
-          const float r = accept_uniform(g, b, j);
-          if (!(ok && logf(r) + lq < lp)) a = j;   // the first rejection wins
-        }
-      }
+      int a = 0;
+      while (a < L && ok[lb * k + a]) ++a;
       const bool resid = a < L;
       g.block_len[b] = L;
       g.accepted[b] = a;
@@ -272,27 +280,38 @@ __global__ __launch_bounds__(256) void sample_lse_kernel(const SampleArgs g) {
     const int64_t c1 = std::min<int64_t>(g.V, c0 + g.chunk_len);
     const S* y = static_cast<const S*>(g.Y) + (b * (g.k + 1) + j) * g.V;
     const float* x = g.X + row * g.V;
+    const float c2 = g.inv_t * kLog2e;
     Lse lp{-INFINITY, 0.f}, lq{-INFINITY, 0.f};
     if constexpr (VEC) {
-      // eight entries per lane per step: 16 or 32 bytes of y, 32 bytes of x
-      for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * 8; v < c1; v += 256 * 8) {
-        u32x4_t yq[sizeof(S) / 2];
+      // eight entries per lane per step (16 or 32 bytes of y, 32 bytes of x);
+      // the loads of U steps are issued before any of them is used
+      constexpr int U = 4;
+      constexpr int YQ = static_cast<int>(sizeof(S)) / 2;
+      for (int64_t v0 = c0 + static_cast<int64_t>(threadIdx.x) * 8; v0 < c1; v0 += 256 * 8 * U) {
+        u32x4_t yq[U][YQ], xq[U][2];
 #pragma unroll
-        for (int h = 0; h < static_cast<int>(sizeof(S) / 2); ++h) yq[h] = load16_stream(y + v + h * Elem<S>::PER16);
-        const u32x4_t xq0 = load16_stream(x + v);
-        const u32x4_t xq1 = load16_stream(x + v + 4);
-        const S* ye = reinterpret_cast<const S*>(yq);
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 2048 < c1 ? v0 + u * 2048 : c0;   // clamped: always readable
 #pragma unroll
-        for (int t = 0; t < 8; ++t) lse_add(lp, to_f32<S>(ye[t]) * g.inv_t);
+          for (int h = 0; h < YQ; ++h) yq[u][h] = load16_stream(y + v + h * Elem<S>::PER16);
+          xq[u][0] = load16_stream(x + v);
+          xq[u][1] = load16_stream(x + v + 4);
+        }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) lse_add(lq, __uint_as_float(xq0[t]) * g.inv_t);
+        for (int u = 0; u < U; ++u) {
+          if (v0 + u * 2048 < c1) {
+            const S* ye = reinterpret_cast<const S*>(yq[u]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) lse_add(lq, __uint_as_float(xq1[t]) * g.inv_t);
+            for (int t = 0; t < 8; ++t) lse_add(lp, to_f32<S>(ye[t]) * c2);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) lse_add(lq, __uint_as_float(xq[u][t >> 2][t & 3]) * c2);
+          }
+        }
       }
     } else {
       for (int64_t v = c0 + threadIdx.x; v < c1; v += 256) {
-        lse_add(lp, to_f32<S>(y[v]) * g.inv_t);
-        lse_add(lq, x[v] * g.inv_t);
+        lse_add(lp, to_f32<S>(y[v]) * c2);
+        lse_add(lq, x[v] * c2);
       }
     }
     lp = lse_wave(lp);
@@ -333,8 +352,9 @@ __global__ __launch_bounds__(256) void sample_draw_kernel(const SampleArgs g) {
   const int4 dd = g.dec[b];
   const int s = dd.x;
   const bool resid = dd.y != 0;
-  const float lse_p = __int_as_float(dd.z);
+  const float lse_p = __int_as_float(dd.z);   // base 2
   const float lse_q = __int_as_float(dd.w);
+  const float c2 = g.inv_t * kLog2e;
   const S* y = static_cast<const S*>(g.Y) + (b * (g.k + 1) + s) * g.V;
   const float* x = g.X + (b * g.k + (resid ? s : 0)) * g.V;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * g.dchunk_len;
@@ -353,16 +373,16 @@ __global__ __launch_bounds__(256) void sample_draw_kernel(const SampleArgs g) {
       const int64_t v = v0 + w;
       if (v < c1) {
         const float G = gumbel_of(bits_to_uniform(u[w]));
-        const float fy = to_f32<S>(y[v]) * g.inv_t;
-        const float kp = fy + G;
+        const float yv = to_f32<S>(y[v]);
+        const float kp = yv * g.inv_t + G;
         if (kp > bp) {
           bp = kp;
           ip = static_cast<uint32_t>(v);
         }
         if (resid) {
-          const float wv = expf(fy - lse_p) - expf(x[v] * g.inv_t - lse_q);
+          const float wv = exp2_hw(yv * c2 - lse_p) - exp2_hw(x[v] * c2 - lse_q);
           if (wv > 0.f) {
-            const float kr = logf(wv) + G;
+            const float kr = log2_hw(wv) * kLn2 + G;
             if (kr > br) {
               br = kr;
               ir = static_cast<uint32_t>(v);

@@ -67,6 +67,19 @@ def test_gumbel_noise_matches_the_generator(stream):
     assert np.mean(m_ref == m_got) > 0.95
 
 
+def test_gumbel_noise_over_a_large_sample_of_the_grid():
+    """16.7M variates (most of the 2^23 uniforms of the grid): every one within
+    2e-6 of the exact -log(-log u)."""
+    k, V, seed = 8, 1 << 21, 99
+    got = bdr().dspark_gumbel_noise(1, k, V, seed, 0).cpu().numpy()
+    worst = 0.0
+    for i in range(k):
+        ref = S.gumbel(S.uniforms(seed, 0, 0, i, V))
+        worst = max(worst, float(np.max(np.abs(got[0, i].astype(np.float64) - ref))))
+    log(f"  max abs err {worst:.3e}")
+    assert worst <= 2e-6
+
+
 def test_gumbel_noise_seeds_and_streams_differ():
     a = bdr().dspark_gumbel_noise(1, 2, 4096, 5, 0)
     b = bdr().dspark_gumbel_noise(1, 2, 4096, 6, 0)
