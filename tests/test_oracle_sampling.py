@@ -1,7 +1,9 @@
 """Pins of the sampling oracle (oracle.sampling) against what the mathematics
 fixes, not against itself:
-  * the generator's uniforms are uniform, 23-bit exact, and every counter and
-    key bit diffuses over the output (Philox4x32-10 diffusion);
+  * the generator equals rocRAND's Philox4x32-10 (an independent
+    implementation, compiled here from the ROCm headers) bit for bit; its
+    uniforms are uniform and 23-bit exact, and every counter and key bit
+    diffuses over the output;
   * Gumbel-max draws reproduce softmax frequencies;
   * at vanishing temperature probabilistic drafting is the greedy chain;
   * speculative sampling is lossless: the first emitted token is distributed
@@ -9,6 +11,9 @@ fixes, not against itself:
     identical distributions are always accepted, and a draft token the target
     gives no mass to is always rejected and replaced by a draw from p.
 Frequencies are checked within 5 binomial standard deviations."""
+import os
+import subprocess
+
 import numpy as np
 import pytest
 
@@ -62,6 +67,38 @@ def test_philox_counter_and_key_bits_diffuse():
     c2[:, 1] ^= np.uint32(1)
     f1 = flipped_bits(S.philox4x32(ctr, key, rounds=1), S.philox4x32(c2, key, rounds=1)).mean()
     assert f1 < 8.0
+
+
+def _hipcc():
+    import shutil
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    return cand if os.path.exists(cand) else shutil.which("hipcc")
+
+
+def test_philox_matches_rocrand(tmp_path):
+    """The oracle's Philox4x32-10 against rocRAND's independent implementation
+    (its host-callable engine, built here from the ROCm headers) on random and
+    extreme counters and keys."""
+    cc = _hipcc()
+    if cc is None:
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "philox_rocrand")
+    src = os.path.join(os.path.dirname(__file__), "philox_rocrand.cpp")
+    r = subprocess.run([cc, "-O1", src, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    rng = np.random.default_rng(17)
+    ctr = rng.integers(0, 1 << 32, size=(2000, 4), dtype=np.uint64).astype(np.uint32)
+    key = rng.integers(0, 1 << 32, size=(2000, 2), dtype=np.uint64).astype(np.uint32)
+    ctr[0], key[0] = 0, 0
+    ctr[1], key[1] = 0xFFFFFFFF, 0xFFFFFFFF
+    ctr[2] = (7, 3, 2, S.STREAM_RESAMPLE)          # a counter of the sampling layout
+    lines = "\n".join(" ".join(str(int(v)) for v in (*c, *k)) for c, k in zip(ctr, key))
+    out = subprocess.run([exe], input=lines, capture_output=True, text=True, check=True).stdout
+    ref = np.array([[int(t) for t in l.split()] for l in out.strip().splitlines()], dtype=np.uint64)
+    got = np.stack([S.philox4x32(c[None], (int(k[0]), int(k[1])))[0] for c, k in zip(ctr, key)])
+    assert ref.shape == (2000, 4)
+    assert np.array_equal(got.astype(np.uint64), ref)
 
 
 def test_streams_rows_and_positions_are_uncorrelated():
