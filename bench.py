@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -169,6 +170,70 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None):
                       f"affinity cores={len(os.sched_getaffinity(0))}"}
 
 
+def fc_only(args, w, L, bdr, synth, torch, dev):
+    """Times dflash_fuse_fc alone on args.fc_rows rows (taps and fc_w of the
+    workload's shape, synthetic N(0, 1) / N(0, 1/fan_in)); one JSON line."""
+    rows, H, T = args.fc_rows, w.hidden, w.n_taps
+    dt = bdr.BDR_BF16 if w.dtype == "bf16" else bdr.BDR_F32
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    taps = [up(synth.store(synth.normal_f32((rows, H), (w.cid, 5, 0, t)), w.dtype))
+            for t in range(T)]
+    fc_w = up(synth.store(synth.normal_f32((H, T * H), (w.cid, 0, 0, 0), math.sqrt(1.0 / (T * H))),
+                          w.dtype))
+    out = torch.empty((rows, H), dtype=fc_w.dtype, device=dev)
+    nws = L.dflash_fuse_fc_workspace_bytes(rows, H, T, dt)
+    wst = torch.zeros(nws + 256, dtype=torch.uint8, device=dev)
+    wsp = C.c_void_p((wst.data_ptr() + 255) & ~255)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    stream = torch.cuda.current_stream(dev)
+    sp = C.c_void_p(stream.cuda_stream)
+
+    def run():
+        check(L.dflash_fuse_fc(arr, T, rows, H, dt, fc_w.data_ptr(), out.data_ptr(), wsp, nws, sp),
+              "dflash_fuse_fc")
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        run()
+        b.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 2.0 * rows * H * T * H
+    tflops = flops / (per * 1e-3) / 1e12
+    esz = 2 if w.dtype == "bf16" else 4
+    nbytes = (rows * T * H + H * T * H + rows * H) * esz
+    log(f"fc rows={rows} H={H} T={T}: {per * 1e3:.1f} us per launch, {tflops:.0f} TFLOP/s")
+    print(json.dumps({
+        "metric": "drafter fc TFLOP/s (prefill-shaped rows)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"fc {rows} x {T}x{H} -> {H} ({w.name} shape)", "rows": rows,
+                   "hidden": H, "n_taps": T},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "tiled GEMM (dflash_fuse_fc)", "avg_launch_us": per * 1e3,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +250,9 @@ def main():
                     help="greedy drafting + exact-match verification, or probabilistic "
                          "drafting + rejection-sampling verification")
     ap.add_argument("--temperature", type=float, default=1.0, help="sampling temperature")
+    ap.add_argument("--fc-rows", type=int, default=0,
+                    help="time the drafter fc alone on this many rows (the prefill-shaped, "
+                         "MFMA-bound fc) with the workload's H and taps, instead of block-steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
@@ -203,6 +271,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = bdr.lib()
+    if args.fc_rows > 0:
+        fc_only(args, w, L, bdr, synth, torch, dev)
+        return
     dt = bdr.BDR_BF16 if w.dtype == "bf16" else bdr.BDR_F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 

@@ -32,6 +32,10 @@ struct GemmPlan {
   int64_t n_waves = 0;    // row ranges (workgroups along N)
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;
+  // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
+  // K steps of 64 (kblocks / kb_per_split count steps)
+  bool tile = false;
+  int tiles_m = 0, tiles_n = 0;
 };
 
 // Compute units of a gfx950 part (MI350X / MI355X); fixed so that workspace

@@ -409,6 +409,37 @@ static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allo
   return p->nt > 0;
 }
 
+// bounds keeping the tiled variant's tile count and indices in 32 bits
+constexpr int64_t kMaxTileRows = int64_t(1) << 22;
+constexpr int64_t kMaxTileCols = int64_t(1) << 22;
+
+// Tiled variant (gemm_tile.hip) for bf16 with more rows than the streaming
+// kernels take: 256 x 160 tiles, K steps of 64 that never straddle a segment,
+// output columns in whole groups of four.  Split K only when the tiles alone
+// leave compute units idle, each split keeping >= 16 steps.
+static bool plan_tile(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
+                      GemmPlan* out) {
+  const int64_t seg = K / std::max(n_seg, 1);
+  if (esize != 2 || M <= 160 || seg % 64 != 0 || N % 4 != 0) return false;
+  if (N > kMaxTileCols || M > kMaxTileRows) return false;
+  GemmPlan p;
+  p.tile = true;
+  p.tiles_m = static_cast<int>((M + 255) / 256);
+  p.tiles_n = static_cast<int>((N + 159) / 160);
+  p.kblocks = K / 64;
+  const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+  int64_t split = 1;
+  if (allow_split && tiles < kNumCU) {
+    split = std::min<int64_t>(kNumCU / tiles, std::max<int64_t>(1, p.kblocks / 16));
+    split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
+  }
+  p.kb_per_split = (p.kblocks + split - 1) / split;
+  p.ksplit = static_cast<int>((p.kblocks + p.kb_per_split - 1) / p.kb_per_split);
+  p.workspace = p.ksplit > 1 ? align256(static_cast<size_t>(p.ksplit) * M * N * 4) : 0;
+  *out = p;
+  return true;
+}
+
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split, int n_seg) {
   GemmPlan p;
   const int ks = dt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
@@ -417,6 +448,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
   {
     GemmPlan q;
     if (plan_stream_wg(M, N, K, esize, allow_split, n_seg, &q)) return q;
+    if (plan_tile(M, N, K, esize, allow_split, n_seg, &q)) return q;
   }
   const int64_t mtiles = std::max<int64_t>(1, (M + 15) / 16);
   if (mtiles <= 9) {
@@ -505,7 +537,10 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   const bool split = p.ksplit > 1;
   g.partial = split ? 1 : 0;
   g.out = split ? workspace : out;
-  if (p.wg) {
+  if (p.tile) {
+    const hipError_t le = launch_gemm_tile(p, g, stream);
+    if (le != hipSuccess) return le;
+  } else if (p.wg) {
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
     const bool bf16 = dt == BDR_BF16;
     const hipError_t le = p.mtw == 1   ? launch_wg_mtw1(p, sa, bf16, stream)

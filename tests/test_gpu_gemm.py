@@ -54,6 +54,16 @@ SHAPES = {
     # fp32: LM M=140 (3 tiles / wave) with a partial K block; fc falls back (256-byte segments)
     "f32_m140": _w("f32_m140", 46, "tiny", batch=20, k=7, hidden=64, n_taps=2, vocab=1500,
                    rank=8),
+    # tiled kernel (M > 160): fc M=300 (ragged row tile, ragged 160-column tile, split K over
+    # 3 taps); LM M=275 over V=4100 (26 column tiles, the last ragged)
+    "tile_m300": _w("tile_m300", 51, "b16", batch=25, k=11, hidden=512, n_taps=3, vocab=4100,
+                    rank=8),
+    # tiled kernel: fc M=1040 on H=2560 x 5 taps (5 row tiles x 16 column tiles, split K);
+    # LM M=1000 over V=2000; LM head with V % 4 != 0 falls back to the register kernel
+    "tile_m1040": _w("tile_m1040", 52, "flashnext_b4", batch=40, k=25, hidden=2560, n_taps=5,
+                     vocab=2000, rank=8),
+    "tile_fallback_v": _w("tile_fallback_v", 53, "b16", batch=20, k=9, hidden=256, n_taps=2,
+                          vocab=1003, rank=8),
 }
 
 
@@ -96,3 +106,24 @@ def test_lm_head_repeat_is_bitwise_identical():
     a = bdr.dspark_lm_head(h, lw).cpu().numpy()
     b = bdr.dspark_lm_head(h, lw).cpu().numpy()
     assert (a.view("u4") == b.view("u4")).all()
+
+
+@pytest.mark.parametrize("hidden", [2560, 5120])
+def test_prefill_fc_parity_on_sampled_rows(hidden):
+    """The prefill-shaped fc (4096 rows, five taps) through the tiled kernel,
+    every output column of 96 sampled rows against the oracle."""
+    import block_draft_readout_amd as bdr
+    import numpy as np
+    rows, T = 4096, 5
+    cid = 60 + hidden // 2560
+    taps = [synth.store(synth.normal_f32((rows, hidden), (cid, 1, 0, t)), "bf16") for t in range(T)]
+    fc_w = synth.store(synth.normal_f32((hidden, T * hidden), (cid, 0, 0, 0),
+                                        (1.0 / (T * hidden)) ** 0.5), "bf16")
+    log(f"prefill fc rows={rows} H={hidden} T={T}")
+    out = bdr.dflash_fuse_fc([dev(t) for t in taps], dev(fc_w))
+    got = host_bits(out)
+    sample = np.unique(np.concatenate([np.arange(0, rows, 43), [rows - 1, 255, 256, 4095 - 160]]))
+    ref = oracle.fuse_fc([t[sample] for t in taps], fc_w, "bf16")
+    err = max_rel_err(oracle.widen(got[sample], "bf16"), ref)
+    log(f"  {sample.size} rows, max rel err {err:.3e}")
+    assert err <= 4e-3
