@@ -35,6 +35,7 @@ struct GemmPlan {
   // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
   // K steps of 64 (kblocks / kb_per_split count steps)
   bool tile = false;
+  int tile_shape = 0;     // 0: 256 x 160 tiles, 3 LDS stages; 1: 256 x 320, 2 stages
   int tiles_m = 0, tiles_n = 0;
 };
 

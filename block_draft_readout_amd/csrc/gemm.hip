@@ -22,6 +22,7 @@
 // (v_mfma_f32_16x16x4_f32); accumulation is fp32.
 
 #include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "gemm_kernels.h"
@@ -414,28 +415,50 @@ constexpr int64_t kMaxTileRows = int64_t(1) << 22;
 constexpr int64_t kMaxTileCols = int64_t(1) << 22;
 
 // Tiled variant (gemm_tile.hip) for bf16 with more rows than the streaming
-// kernels take: 256 x 160 tiles, K steps of 64 that never straddle a segment,
-// output columns in whole groups of four.  Split K only when the tiles alone
-// leave compute units idle, each split keeping >= 16 steps.
+// kernels take: 256 x 160 or 256 x 320 tiles, K steps of 64 that never
+// straddle a segment, output columns in whole groups of four.  Split K only
+// when the tiles alone leave compute units idle, each split keeping >= 16
+// steps.
 static bool plan_tile(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
                       GemmPlan* out) {
   const int64_t seg = K / std::max(n_seg, 1);
   if (esize != 2 || M <= 160 || seg % 64 != 0 || N % 4 != 0) return false;
   if (N > kMaxTileCols || M > kMaxTileRows) return false;
+  // Shape 1 (256 x 320, eight waves) reached ~0.49 of the MFMA peak on the
+  // 4096-row fc, shape 0 (256 x 160, four waves) ~0.35; pick the shape (and a
+  // K split that fills the compute units) with the lower estimated time,
+  // counting rounds of workgroups and the fp32 partials' round trip.
+  const double eff[2] = {0.35, 0.49};
+  const double cu_flops = 2.5e15 / kNumCU;
+  const double bw = 5e12;
+  const int64_t kblocks = K / 64;
+  const int64_t tiles_m = (M + 255) / 256;
+  double best = 1e30;
   GemmPlan p;
-  p.tile = true;
-  p.tiles_m = static_cast<int>((M + 255) / 256);
-  p.tiles_n = static_cast<int>((N + 159) / 160);
-  p.kblocks = K / 64;
-  const int64_t tiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
-  int64_t split = 1;
-  if (allow_split && tiles < kNumCU) {
-    split = std::min<int64_t>(kNumCU / tiles, std::max<int64_t>(1, p.kblocks / 16));
-    split = std::max<int64_t>(1, std::min<int64_t>(split, 16));
+  for (int shape = 0; shape < 2; ++shape) {
+    const int64_t cols = tile_cols(shape);
+    const int64_t tiles = tiles_m * ((N + cols - 1) / cols);
+    int64_t split = 1;
+    if (allow_split && tiles < kNumCU)
+      split = std::max<int64_t>(1, std::min<int64_t>({kNumCU / tiles, kblocks / 16, 16}));
+    const int64_t kps = (kblocks + split - 1) / split;
+    split = (kblocks + kps - 1) / kps;
+    const double rounds = std::ceil(static_cast<double>(tiles * split) / kNumCU);
+    double t = rounds * 2.0 * 256 * cols * 64.0 * kps / (eff[shape] * cu_flops);
+    if (split > 1) t += (static_cast<double>(split) * M * N * 8 + static_cast<double>(M) * N * 2) / bw;
+    if (t < best) {
+      best = t;
+      p = GemmPlan{};
+      p.tile = true;
+      p.tile_shape = shape;
+      p.tiles_m = static_cast<int>(tiles_m);
+      p.tiles_n = static_cast<int>((N + cols - 1) / cols);
+      p.kblocks = kblocks;
+      p.kb_per_split = kps;
+      p.ksplit = static_cast<int>(split);
+      p.workspace = split > 1 ? align256(static_cast<size_t>(split) * M * N * 4) : 0;
+    }
   }
-  p.kb_per_split = (p.kblocks + split - 1) / split;
-  p.ksplit = static_cast<int>((p.kblocks + p.kb_per_split - 1) / p.kb_per_split);
-  p.workspace = p.ksplit > 1 ? align256(static_cast<size_t>(p.ksplit) * M * N * 4) : 0;
   *out = p;
   return true;
 }

@@ -419,6 +419,7 @@ hipError_t launch_wg_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
 // of A tiles a wave holds (p.mtw), so the instantiations compile in parallel;
 // each returns hipErrorInvalidValue for a tile count it does not instantiate.
 hipError_t launch_gemm_tile(const GemmPlan& p, const GemmArgs& g, hipStream_t stream);
+int tile_cols(int shape);   // output columns of a tiled-variant workgroup tile
 hipError_t launch_wg_mtw1(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
 hipError_t launch_wg_mtw2(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
 hipError_t launch_wg_mtw3(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);

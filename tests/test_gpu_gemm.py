@@ -64,6 +64,13 @@ SHAPES = {
                      vocab=2000, rank=8),
     "tile_fallback_v": _w("tile_fallback_v", 53, "b16", batch=20, k=9, hidden=256, n_taps=2,
                           vocab=1003, rank=8),
+    # the wide (256 x 320, eight-wave) tile: LM M=4000 over V=5000 (ragged last row and column
+    # tiles); fc M=4400 on the narrow tile
+    "tile_wide_m4000": _w("tile_wide_m4000", 54, "b16", batch=400, k=10, hidden=512, n_taps=2,
+                          vocab=5000, rank=8),
+    # narrow tile with split K: fc M=520 over 4 taps of 1024 (21 tiles x 4 splits)
+    "tile_split_m520": _w("tile_split_m520", 55, "b16", batch=40, k=12, hidden=1024, n_taps=4,
+                          vocab=3000, rank=8),
 }
 
 
