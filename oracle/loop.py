@@ -1,0 +1,106 @@
+"""The closed multi-step drafting loop (plain CPU definitions).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke entry point and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+Sources (web pages; cited by title and section):
+  * "docs(vllm): Qwen3.8-27B DFlash drafter recipe" (intel/llm-scaler PR #620),
+    DSpark port notes: propose() keeps the accepted bonus token as the Markov
+    previous-token context of the next draft; the adaptive block path needs
+    list-type draft_token_ids with padding (rows of different lengths).
+  * "Qwen4Exp DFlash drafter support" (wtdcode/vllm-backport PR #128), "What was
+    missing" item 1: the drafter consumes the target's hidden states captured at
+    its target layers for the positions the target just processed.
+
+Readings (the pages do not spell these out):
+  * After verification of row b, the tokens committed to the sequence are the
+    accepted draft prefix d[b, :a_b] followed by the bonus token; they are
+    returned as a [B, k+1] list padded with -1.
+  * The next draft's Markov context of row b is its bonus token.
+  * Of the k+1 verified positions of row b (the bonus input of the previous
+    step and the k draft tokens), the first a_b + 1 were accepted into the
+    sequence; their tapped target hidden states are the rows the drafter fc
+    consumes next: row b*(k+1) + j for j <= a_b, concatenated in row order
+    (sum_b (a_b + 1) rows).
+  * The draft block of row b as a list is d[b, :L_b] padded with -1.
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .reference import (fuse_fc, lm_head, semi_ar_argmax, target_argmax,
+                        truncate_by_confidence, verify_greedy)
+
+PAD = -1
+
+
+def commit_step(d: np.ndarray, accepted: np.ndarray, bonus: np.ndarray,
+                block_len: np.ndarray) -> Dict[str, np.ndarray]:
+    """Committed tokens, next Markov contexts, the accepted rows whose taps feed
+    the fc next, and the padded draft lists of one verified block."""
+    d = np.asarray(d, dtype=np.int64)
+    B, k = d.shape
+    emitted = np.full((B, k + 1), PAD, dtype=np.int64)
+    n_emitted = np.zeros(B, dtype=np.int64)
+    draft_list = np.full((B, k), PAD, dtype=np.int64)
+    rows: List[int] = []
+    offsets = np.zeros(B + 1, dtype=np.int64)
+    for b in range(B):
+        a = int(accepted[b])
+        for j in range(a):
+            emitted[b, j] = d[b, j]
+        emitted[b, a] = int(bonus[b])
+        n_emitted[b] = a + 1
+        for i in range(int(block_len[b])):
+            draft_list[b, i] = d[b, i]
+        for j in range(a + 1):
+            rows.append(b * (k + 1) + j)
+        offsets[b + 1] = len(rows)
+    return dict(emitted=emitted, n_emitted=n_emitted,
+                next_prev=np.asarray(bonus, dtype=np.int64).copy(),
+                row_index=np.asarray(rows, dtype=np.int64), row_count=len(rows),
+                row_offsets=offsets, draft_list=draft_list)
+
+
+def fuse_fc_rows(taps: Sequence[np.ndarray], row_index: np.ndarray, fc_w: np.ndarray,
+                 dtype: str) -> np.ndarray:
+    """The drafter fc on the selected rows of the taps, in the order given."""
+    idx = np.asarray(row_index, dtype=np.int64)
+    return fuse_fc([np.asarray(t)[idx] for t in taps], fc_w, dtype)
+
+
+def closed_loop(dtype: str, steps: int, prev0: np.ndarray, fc_w, lm_w, w1, w2,
+                step_inputs: Callable[[int], Dict[str, object]],
+                target_logits: Callable[[int, np.ndarray], np.ndarray],
+                threshold: Optional[float] = None) -> List[Dict[str, object]]:
+    """`steps` block-steps where each step's Markov context is the previous
+    step's bonus token and the fc runs on the previous verification's accepted
+    rows.
+
+    Per step s: step_inputs(s) gives the drafter's block hidden states
+    ``draft_hidden`` [B, k, H], the target's tapped hidden states ``taps`` (T
+    arrays [B*(k+1), H]) of the positions it verifies at this step, and
+    optional ``confidence`` [B, k]; target_logits(s, d) gives the target logits
+    [B, k+1, V] once the draft d is known.  Order: S2 LM head, S3 Markov draft,
+    (target), S4 verification, commit, S1 fc on the accepted rows.
+    """
+    prev = np.asarray(prev0, dtype=np.int64).copy()
+    out = []
+    for s in range(steps):
+        inp = step_inputs(s)
+        Z = lm_head(inp["draft_hidden"], lm_w, dtype)
+        d, gap = semi_ar_argmax(Z, w1, w2, prev, dtype)
+        B, k = d.shape
+        Y = target_logits(s, d)
+        L = truncate_by_confidence(inp.get("confidence"), threshold, B, k)
+        t = target_argmax(Y, dtype, L)
+        a, bonus, acc, prop = verify_greedy(d, t, L)
+        c = commit_step(d, a, bonus, L)
+        F = fuse_fc_rows(inp["taps"], c["row_index"], fc_w, dtype)
+        out.append(dict(prev=prev.copy(), logits=Z, draft_tokens=d, gap=gap, target_logits=Y,
+                        block_len=L, accepted=a, bonus=bonus, accept_counts=acc,
+                        proposed_counts=prop, fc_out=F, **c))
+        prev = c["next_prev"]
+    return out
