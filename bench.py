@@ -75,6 +75,7 @@ class Step:
         self.stream = stream
         self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
+        self.prev = slot["prev0"].data_ptr()   # Markov context of position 0 (see --closed-loop)
 
     def fc(self):
         w, b = self.w, self.b
@@ -94,11 +95,11 @@ class Step:
             T, seed = self.sample
             return self.L.dspark_markov_sample(
                 b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt, self.g["w1"].data_ptr(),
-                self.g["w2"].data_ptr(), w.rank, self.s["prev0"].data_ptr(), T, seed,
+                self.g["w2"].data_ptr(), w.rank, self.prev, T, seed,
                 b["d"].data_ptr(), b["x"].data_ptr(), b["ws_ms"], b["ws_ms_n"], self.stream)
         return self.L.dspark_markov_argmax(b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt,
                                            self.g["w1"].data_ptr(), self.g["w2"].data_ptr(),
-                                           w.rank, self.s["prev0"].data_ptr(), b["d"].data_ptr(),
+                                           w.rank, self.prev, b["d"].data_ptr(),
                                            b["ws_m"], b["ws_m_n"], self.stream)
 
     def draft_block(self):
@@ -126,6 +127,22 @@ class Step:
             None if conf is None else conf.data_ptr(), th, b["bl"].data_ptr(),
             b["acc_len"].data_ptr(), b["bonus"].data_ptr(), b["targ"].data_ptr(),
             b["acc"].data_ptr(), b["prop"].data_ptr(), b["ws_v"], b["ws_v_n"], self.stream)
+
+
+    def commit(self, next_prev):
+        w, b = self.w, self.b
+        return self.L.spec_commit(b["d"].data_ptr(), b["acc_len"].data_ptr(), b["bonus"].data_ptr(),
+                                  b["bl"].data_ptr(), w.batch, w.k, next_prev,
+                                  b["emitted"].data_ptr(), b["draft_list"].data_ptr(),
+                                  b["row_index"].data_ptr(), b["row_count"].data_ptr(),
+                                  b["row_offsets"].data_ptr(), self.stream)
+
+    def fc_rows(self):
+        w, b = self.w, self.b
+        return self.L.dflash_fuse_fc_rows(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+                                          b["row_index"].data_ptr(), b["row_count"].data_ptr(),
+                                          w.rows, self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
+                                          b["ws_fcr"], b["ws_fcr_n"], self.stream)
 
 
 def check(rc, what):
@@ -250,6 +267,10 @@ def main():
                     help="greedy drafting + exact-match verification, or probabilistic "
                          "drafting + rejection-sampling verification")
     ap.add_argument("--temperature", type=float, default=1.0, help="sampling temperature")
+    ap.add_argument("--closed-loop", action="store_true",
+                    help="chain the steps on the device: each step's Markov context is the previous "
+                         "step's bonus token, and the fc runs after verification on the accepted "
+                         "rows only (LM head, draft, verify, commit, fc in order)")
     ap.add_argument("--fc-rows", type=int, default=0,
                     help="time the drafter fc alone on this many rows (the prefill-shaped, "
                          "MFMA-bound fc) with the workload's H and taps, instead of block-steps")
@@ -258,6 +279,9 @@ def main():
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
     args = ap.parse_args()
 
+    if args.closed_loop and args.graph:
+        print(json.dumps({"error": "--closed-loop runs eagerly (no --graph)"}))
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -312,11 +336,18 @@ def main():
     sampling = args.draft == "sample"
     if sampling:
         bufs["x"] = torch.empty((B, k, V), dtype=torch.float32, device=dev)
+    if args.closed_loop:
+        for name, shp in (("prev_a", (B,)), ("prev_b", (B,)), ("emitted", (B, k + 1)),
+                          ("draft_list", (B, k)), ("row_index", (B * (k + 1),)), ("row_count", (1,)),
+                          ("row_offsets", (B + 1,))):
+            bufs[name] = torch.zeros(shp, dtype=torch.int32, device=dev)
     for key, n in (("ws_fc", L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
                    ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
                    ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
                    ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
-                   ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0)):
+                   ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0),
+                   ("ws_fcr", L.dflash_fuse_fc_rows_workspace_bytes(w.rows, H, w.n_taps, dt)
+                    if args.closed_loop else 0)):
         p, n2, t = ws(n)
         bufs[key], bufs[key + "_n"] = p, n2
         keep.append(t)
@@ -350,7 +381,24 @@ def main():
     ev_fork = torch.cuda.Event()
     ev_join = torch.cuda.Event()
 
+    loop_state = {"cur": "prev_a"}
+    if args.closed_loop:
+        bufs["prev_a"].copy_(slots[0].s["prev0"])
+        torch.cuda.synchronize()
+
     def run_step(st):
+        if args.closed_loop:
+            cur = loop_state["cur"]
+            nxt = "prev_b" if cur == "prev_a" else "prev_a"
+            st.prev = bufs[cur].data_ptr()
+            check(st.lm_head(), "dspark_lm_head")
+            check(st.markov(), "drafting")
+            check(st.verify(), "verification")
+            check(st.commit(bufs[nxt].data_ptr()), "spec_commit")
+            check(st.fc_rows(), "dflash_fuse_fc_rows")
+            st.prev = st.s["prev0"].data_ptr()
+            loop_state["cur"] = nxt
+            return
         if args.overlap == "none":
             check(st.fc(), "dflash_fuse_fc")
             check(st.lm_head(), "dspark_lm_head")
@@ -479,7 +527,8 @@ def main():
         "config": {"workload": w.describe(), "batch": B, "k": k, "hidden": H, "vocab": V,
                    "rank": w.rank, "n_taps": w.n_taps,
                    "launch": "hip-graph" if graphs is not None else "eager",
-                   "fc_overlap": args.overlap,
+                   "fc_overlap": "none (closed loop)" if args.closed_loop else args.overlap,
+                   "loop": "closed" if args.closed_loop else "independent steps",
                    "draft": args.draft,
                    **({"temperature": args.temperature} if sampling else {}),
                    "pool_steps": args.pool},

@@ -21,7 +21,7 @@ from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
-    "workspace_bytes", "lib", "BdrError",
+    "spec_commit", "dflash_fuse_fc_rows", "workspace_bytes", "lib", "BdrError",
 ]
 
 
@@ -365,3 +365,63 @@ def spec_verify_sample(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
                                     _ptr(res["bonus"]), _ptr(accept_counts),
                                     _ptr(proposed_counts), wp, wn, _stream(dev)))
     return res
+
+
+# ----------------------------------------------------------------------------- loop
+def spec_commit(draft_tokens: torch.Tensor, accepted: torch.Tensor, bonus: torch.Tensor,
+                block_len: Optional[torch.Tensor] = None,
+                out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Commit a verified block: next_prev [B], emitted [B, k+1] (-1 padded),
+    draft_list [B, k] (-1 padded), row_index [B*(k+1)] (first row_count valid),
+    row_count [1], row_offsets [B+1] -- all int32 on the device."""
+    L = lib()
+    _dev(draft_tokens, "draft_tokens")
+    B, k = draft_tokens.shape
+    for name, t in (("accepted", accepted), ("bonus", bonus), ("block_len", block_len)):
+        if t is not None:
+            _dev(t, name)
+            if t.dtype != torch.int32 or t.numel() != B:
+                raise ValueError(f"{name} must be int32 [B]")
+    dev = draft_tokens.device
+    res = dict(out) if out is not None else {}
+    shapes = {"next_prev": (B,), "emitted": (B, k + 1), "draft_list": (B, k),
+              "row_index": (B * (k + 1),), "row_count": (1,), "row_offsets": (B + 1,)}
+    for name, shp in shapes.items():
+        if name not in res:
+            res[name] = torch.empty(shp, dtype=torch.int32, device=dev)
+    _abi.check("spec_commit",
+               L.spec_commit(_ptr(draft_tokens), _ptr(accepted), _ptr(bonus), _ptr(block_len), B, k,
+                             _ptr(res["next_prev"]), _ptr(res["emitted"]), _ptr(res["draft_list"]),
+                             _ptr(res["row_index"]), _ptr(res["row_count"]),
+                             _ptr(res["row_offsets"]), _stream(dev)))
+    return res
+
+
+def dflash_fuse_fc_rows(taps: Sequence[torch.Tensor], fc_w: torch.Tensor, row_index: torch.Tensor,
+                        row_count: torch.Tensor, max_rows: Optional[int] = None,
+                        out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[r] = fc(concat(taps)[row_index[r]]) for r < row_count[0], zeros after (out [max_rows, H])."""
+    L = lib()
+    T = len(taps)
+    rows, H = taps[0].shape
+    for i, t in enumerate(taps):
+        _dev(t, f"taps[{i}]")
+        if t.shape != (rows, H) or t.dtype != fc_w.dtype:
+            raise ValueError("taps must all be [rows, H] with fc_w's dtype")
+    _dev(fc_w, "fc_w")
+    _dev(row_index, "row_index")
+    _dev(row_count, "row_count")
+    if max_rows is None:
+        max_rows = row_index.numel()
+    dt = _dt(fc_w)
+    if out is None:
+        out = torch.empty((max_rows, H), dtype=fc_w.dtype, device=fc_w.device)
+    _dev(out, "out")
+    ws = _workspace(L.dflash_fuse_fc_rows_workspace_bytes(max_rows, H, T, dt), fc_w.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    _abi.check("dflash_fuse_fc_rows",
+               L.dflash_fuse_fc_rows(arr, T, rows, H, dt, _ptr(row_index), _ptr(row_count), max_rows,
+                                     _ptr(fc_w), _ptr(out), wp, wn, _stream(fc_w.device)))
+    return out

@@ -49,6 +49,10 @@ SIGNATURES = {
     "spec_verify_sample_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "spec_verify_sample": (_int, [_vp, _int, _i64, _int, _i64, _vp, _vp, _vp, C.c_float,
                                   C.c_float, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "spec_commit": (_int, [_vp, _vp, _vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "dflash_fuse_fc_rows_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
+    "dflash_fuse_fc_rows": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _i64, _vp,
+                                   _vp, _vp, _sz, _vp]),
 }
 
 _lib = None

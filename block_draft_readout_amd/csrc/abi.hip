@@ -386,4 +386,61 @@ int spec_verify_sample(const void* target_logits, bdr_dtype dt, int64_t batch, i
   return BDR_OK;
 }
 
+// ---------------------------------------------------------------------------- loop
+int spec_commit(const int32_t* draft_tokens, const int32_t* accepted, const int32_t* bonus,
+                const int32_t* block_len, int64_t batch, int k, int32_t* next_prev,
+                int32_t* emitted, int32_t* draft_list, int32_t* row_index, int32_t* row_count,
+                int32_t* row_offsets, void* stream) {
+  if (batch < 0) return fail(BDR_EINVAL, "batch must be >= 0");
+  if (k < 1) return fail(BDR_EINVAL, "k must be >= 1, got %d", k);
+  if (k > BDR_MAX_K) return fail(BDR_EUNSUPPORTED, "k %d > %d", k, BDR_MAX_K);
+  if (batch > 0x7FFFFFFFLL / (k + 1)) return fail(BDR_EUNSUPPORTED, "batch too large");
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  BDR_TRY(need_ptr(accepted, "accepted", 4));
+  BDR_TRY(need_ptr(bonus, "bonus", 4));
+  if (block_len) BDR_TRY(need_ptr(block_len, "block_len", 4));
+  BDR_TRY(need_ptr(next_prev, "next_prev", 4));
+  for (const int32_t* p : {static_cast<const int32_t*>(emitted), static_cast<const int32_t*>(draft_list),
+                           static_cast<const int32_t*>(row_index), static_cast<const int32_t*>(row_count),
+                           static_cast<const int32_t*>(row_offsets)})
+    if (p) BDR_TRY(need_ptr(p, "output", 4));
+  BDR_TRY(check_device());
+  hipError_t e = launch_commit(draft_tokens, accepted, bonus, block_len, batch, k, next_prev,
+                               emitted, draft_list, row_index, row_count, row_offsets,
+                               as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "spec_commit launch");
+  return BDR_OK;
+}
+
+size_t dflash_fuse_fc_rows_workspace_bytes(int64_t max_rows, int64_t hidden, int n_taps,
+                                           bdr_dtype dt) {
+  if (fc_shape(max_rows, hidden, n_taps, dt) != BDR_OK) return 0;
+  return fc_rows_workspace(max_rows, hidden, n_taps, dt);
+}
+
+int dflash_fuse_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                        bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
+                        int64_t max_rows, const void* fc_w, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  BDR_TRY(fc_shape(max_rows, hidden, n_taps, dt));
+  BDR_TRY(fc_shape(rows, hidden, n_taps, dt));
+  if (max_rows == 0) return BDR_OK;
+  if (!taps) return fail(BDR_EINVAL, "taps must not be NULL");
+  for (int t = 0; t < n_taps; ++t) {
+    if (rows > 0 && !taps[t]) return fail(BDR_EINVAL, "taps[%d] must not be NULL", t);
+    if (!aligned(taps[t], 16)) return fail(BDR_EINVAL, "taps[%d] must be 16-byte aligned", t);
+  }
+  BDR_TRY(need_ptr(row_index, "row_index", 4));
+  BDR_TRY(need_ptr(row_count, "row_count", 4));
+  BDR_TRY(need_ptr(fc_w, "fc_w"));
+  BDR_TRY(need_ptr(out, "out"));
+  BDR_TRY(need_ws(workspace, workspace_bytes, fc_rows_workspace(max_rows, hidden, n_taps, dt)));
+  BDR_TRY(check_device());
+  hipError_t e = launch_fc_rows(taps, n_taps, rows, hidden, dt, row_index, row_count, max_rows,
+                                fc_w, out, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_rows launch");
+  return BDR_OK;
+}
+
 }  // extern "C"

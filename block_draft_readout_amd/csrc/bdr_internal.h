@@ -89,6 +89,19 @@ hipError_t launch_verify_sample(const void* Y, bdr_dtype dt, int64_t B, int k, i
                                 int32_t* accepted, int32_t* bonus, int64_t* acc, int64_t* prop,
                                 void* workspace, hipStream_t stream);
 
+// ----------------------------------------------------------------------------
+// Closing the loop: commit a verified block; the fc on gathered rows.
+// ----------------------------------------------------------------------------
+hipError_t launch_commit(const int32_t* draft, const int32_t* accepted, const int32_t* bonus,
+                         const int32_t* block_len, int64_t B, int k, int32_t* next_prev,
+                         int32_t* emitted, int32_t* draft_list, int32_t* row_index,
+                         int32_t* row_count, int32_t* row_offsets, hipStream_t stream);
+size_t fc_rows_workspace(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt);
+hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                          bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
+                          int64_t max_rows, const void* fc_w, void* out, void* workspace,
+                          hipStream_t stream);
+
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace bdr

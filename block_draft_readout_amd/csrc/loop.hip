@@ -1,0 +1,178 @@
+// Closing the drafting loop between block-steps (gfx950): committing a
+// verified block and running the drafter fc on the accepted rows only.
+//
+// The DSpark proposer keeps the accepted bonus token as the next draft's
+// Markov context, and the adaptive block path hands draft token lists of
+// different lengths around padded (llm-scaler PR #620, DSpark port notes); the
+// drafter consumes the target's tapped hidden states of the positions that
+// were accepted (vllm-backport PR #128, "What was missing" item 1).
+//
+//   commit_kernel   one workgroup: per row b the committed tokens d[b, :a_b] ++
+//                   [bonus_b] (padded with -1), the next Markov context
+//                   (bonus_b), the padded draft list d[b, :L_b], and the rows
+//                   b*(k+1) + j, j <= a_b, of the accepted positions, placed by
+//                   an exclusive prefix sum of a_b + 1 over the rows (LDS scan
+//                   of 256 rows at a time, running base across chunks).
+//   gather_kernel   grid (row, tap): copies tap row row_index[r] into row r of
+//                   a dense buffer (zeros for r >= the device-side row count);
+//                   the fc then runs on that buffer with the usual GEMM plans
+//                   (its cost is the weight stream, whatever the row count).
+
+#include <algorithm>
+
+#include "bdr_device.h"
+#include "bdr_internal.h"
+
+namespace bdr {
+
+struct CommitArgs {
+  const int32_t* draft;      // [B, k]
+  const int32_t* accepted;   // [B]
+  const int32_t* bonus;      // [B]
+  const int32_t* block_len;  // [B] or null (full blocks)
+  int64_t B;
+  int k;
+  int32_t* next_prev;        // [B]
+  int32_t* emitted;          // [B, k+1] or null
+  int32_t* draft_list;       // [B, k] or null
+  int32_t* row_index;        // [B*(k+1)] or null
+  int32_t* row_count;        // [1] or null
+  int32_t* row_offsets;      // [B+1] or null
+};
+
+__global__ __launch_bounds__(256) void commit_kernel(const CommitArgs g) {
+  __shared__ int32_t scan[256];
+  __shared__ int32_t base_s;
+  const int tid = threadIdx.x;
+  const int k1 = g.k + 1;
+  if (tid == 0) base_s = 0;
+  __syncthreads();
+  for (int64_t b0 = 0; b0 < g.B; b0 += 256) {
+    const int64_t b = b0 + tid;
+    const bool live = b < g.B;
+    int32_t a = 0, L = g.k;
+    if (live) {
+      a = min(max(g.accepted[b], 0), g.k);   // device values: kept in range
+      if (g.block_len) L = min(max(g.block_len[b], 0), g.k);
+      const int32_t bon = g.bonus[b];
+      g.next_prev[b] = bon;
+      if (g.emitted)
+        for (int j = 0; j < k1; ++j)
+          g.emitted[b * k1 + j] = j < a ? g.draft[b * g.k + j] : (j == a ? bon : -1);
+      if (g.draft_list)
+        for (int i = 0; i < g.k; ++i) g.draft_list[b * g.k + i] = i < L ? g.draft[b * g.k + i] : -1;
+    }
+    // inclusive scan of the accepted-row counts of this chunk
+    scan[tid] = live ? a + 1 : 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int32_t v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int32_t base = base_s;
+    const int32_t excl = base + scan[tid] - (live ? a + 1 : 0);
+    if (live) {
+      if (g.row_offsets) g.row_offsets[b] = excl;
+      if (g.row_index)
+        for (int j = 0; j <= a; ++j) g.row_index[excl + j] = static_cast<int32_t>(b * k1 + j);
+    }
+    __syncthreads();
+    if (tid == 255) base_s = base + scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (g.row_count) *g.row_count = base_s;
+    if (g.row_offsets) g.row_offsets[g.B] = base_s;
+  }
+}
+
+hipError_t launch_commit(const int32_t* draft, const int32_t* accepted, const int32_t* bonus,
+                         const int32_t* block_len, int64_t B, int k, int32_t* next_prev,
+                         int32_t* emitted, int32_t* draft_list, int32_t* row_index,
+                         int32_t* row_count, int32_t* row_offsets, hipStream_t stream) {
+  CommitArgs g{draft, accepted, bonus, block_len, B, k, next_prev, emitted, draft_list,
+               row_index, row_count, row_offsets};
+  hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+// dst[t][r][:] = taps[t][row_index[r]][:] for r < *row_count, zeros otherwise
+// (also for an index outside [0, rows)).  One workgroup per (row, tap).
+struct GatherArgs {
+  const void* taps[BDR_MAX_TAPS];
+  void* dst[BDR_MAX_TAPS];
+  int64_t rows, max_rows;
+  int64_t row_bytes;             // multiple of 16
+  const int32_t* row_index;
+  const int32_t* row_count;
+};
+
+__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs g) {
+  const int64_t r = blockIdx.x;
+  const int t = blockIdx.y;
+  const void* src_base = g.taps[0];
+  void* dst_base = g.dst[0];
+#pragma unroll
+  for (int c = 1; c < BDR_MAX_TAPS; ++c)
+    if (t == c) {
+      src_base = g.taps[c];
+      dst_base = g.dst[c];
+    }
+  int64_t src_row = -1;
+  if (r < *g.row_count) {
+    const int64_t i = g.row_index[r];
+    if (i >= 0 && i < g.rows) src_row = i;
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<char*>(dst_base) + r * g.row_bytes);
+  const int64_t n16 = g.row_bytes / 16;
+  if (src_row < 0) {
+    for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+  } else {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(src_base) +
+                                                          src_row * g.row_bytes);
+    for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = src[i];
+  }
+}
+
+// gathered taps (n_taps x [max_rows, H]) | fc workspace
+static size_t gathered_bytes(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {
+  return align256(static_cast<size_t>(max_rows) * hidden * (dt == BDR_BF16 ? 2 : 4)) * n_taps;
+}
+
+size_t fc_rows_workspace(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {
+  if (max_rows == 0) return 0;
+  return gathered_bytes(max_rows, hidden, n_taps, dt) +
+         plan_gemm(max_rows, hidden, hidden * n_taps, dt, true, n_taps).workspace;
+}
+
+hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                          bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
+                          int64_t max_rows, const void* fc_w, void* out, void* workspace,
+                          hipStream_t stream) {
+  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+  GatherArgs ga{};
+  char* ws = static_cast<char*>(workspace);
+  const size_t per_tap = align256(static_cast<size_t>(max_rows) * hidden * es);
+  const void* gathered[BDR_MAX_TAPS] = {};
+  for (int t = 0; t < n_taps; ++t) {
+    ga.taps[t] = taps[t];
+    ga.dst[t] = ws + t * per_tap;
+    gathered[t] = ga.dst[t];
+  }
+  ga.rows = rows;
+  ga.max_rows = max_rows;
+  ga.row_bytes = hidden * es;
+  ga.row_index = row_index;
+  ga.row_count = row_count;
+  hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(max_rows), static_cast<unsigned>(n_taps)),
+                     dim3(256), 0, stream, ga);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const GemmPlan p = plan_gemm(max_rows, hidden, hidden * n_taps, dt, true, n_taps);
+  return launch_gemm(p, dt, gathered, n_taps, hidden, max_rows, hidden, fc_w, out,
+                     dt == BDR_BF16 ? OUT_BF16 : OUT_F32, ws + n_taps * per_tap, stream);
+}
+
+}  // namespace bdr

@@ -289,6 +289,51 @@ int spec_verify_sample(const void* target_logits, bdr_dtype dt, int64_t batch,
                        int64_t* accept_counts, int64_t* proposed_counts,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Closing the loop between block-steps.
+ *
+ * The proposer keeps the accepted bonus token as the next draft's Markov
+ * context, and the adaptive block path hands draft token lists of different
+ * lengths around padded ([recipe] DSpark port notes, dflash.py); the drafter
+ * consumes the target's tapped hidden states of the positions it just
+ * processed ([pr128] "What was missing" item 1), of which the accepted ones
+ * continue the sequence.
+ *
+ * spec_commit -- after verification of a block (device values from
+ * spec_verify_greedy or spec_verify_sample; accepted is clamped to [0, k]):
+ *   next_prev[b]          = bonus[b]              (the next draft's context)
+ *   emitted[b, :]         = d[b, :a_b] ++ [bonus[b]], padded with -1  [B, k+1]
+ *   draft_list[b, :]      = d[b, :L_b], padded with -1                [B, k]
+ *   row_index[0 .. n)     = b*(k+1) + j for j <= a_b, rows in order   [B*(k+1)]
+ *   row_count[0]          = n = sum_b (a_b + 1)
+ *   row_offsets[b]        = sum_{c<b} (a_c + 1), row_offsets[B] = n     [B+1]
+ * block_len may be NULL (L_b = k); every output except next_prev may be NULL.
+ * Entries of row_index from n on are not written.  One workgroup; no
+ * workspace.
+ * ------------------------------------------------------------------------- */
+int spec_commit(const int32_t* draft_tokens, const int32_t* accepted,
+                const int32_t* bonus, const int32_t* block_len, int64_t batch,
+                int k, int32_t* next_prev, int32_t* emitted,
+                int32_t* draft_list, int32_t* row_index, int32_t* row_count,
+                int32_t* row_offsets, void* stream);
+
+/* dflash_fuse_fc_rows -- S1 on selected rows (the accepted positions):
+ *   out[r, :] = concat_t(taps[t][row_index[r], :]) . fc_w^T   for r < *row_count
+ *   out[r, :] = 0                                             for r >= *row_count
+ * row_index and row_count live on the device (as written by spec_commit);
+ * an index outside [0, rows) reads a zero row.  Taps [rows, H] as in
+ * dflash_fuse_fc; out [max_rows, H] (dtype).  The rows are gathered into the
+ * workspace, then the fc runs on max_rows rows (its cost is the weight stream).
+ *   workspace >= dflash_fuse_fc_rows_workspace_bytes(max_rows, H, n_taps, dt)
+ * ------------------------------------------------------------------------- */
+size_t dflash_fuse_fc_rows_workspace_bytes(int64_t max_rows, int64_t hidden,
+                                           int n_taps, bdr_dtype dt);
+int dflash_fuse_fc_rows(const void* const* taps, int n_taps, int64_t rows,
+                        int64_t hidden, bdr_dtype dt, const int32_t* row_index,
+                        const int32_t* row_count, int64_t max_rows,
+                        const void* fc_w, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

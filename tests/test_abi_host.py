@@ -207,6 +207,32 @@ def test_sampling_validation(L):
     assert n(B=0) == A.BDR_OK
 
 
+def test_loop_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    c = lambda B=4, k=7, nxt=P, acc=P, em=None: L.spec_commit(P, acc, P, None, B, k, nxt, em, None,
+                                                              None, None, None, None)
+    assert c(k=0) == A.BDR_EINVAL
+    assert c(k=17) == A.BDR_EUNSUPPORTED
+    assert c(B=-1) == A.BDR_EINVAL
+    assert c(nxt=None) == A.BDR_EINVAL
+    assert c(acc=None) == A.BDR_EINVAL
+    assert c(em=C.c_void_p(4098)) == A.BDR_EINVAL        # int32 outputs 4-byte aligned
+    assert c(B=0) == A.BDR_OK
+    taps = (C.c_void_p * 2)(*([4096] * 2))
+    f = lambda mr=8, rows=8, H=512, ri=P, rc=P, wn=0: L.dflash_fuse_fc_rows(
+        taps, 2, rows, H, A.BDR_BF16, ri, rc, mr, P, P, None, wn, None)
+    assert f(H=500) == A.BDR_EUNSUPPORTED
+    assert f(ri=None) == A.BDR_EINVAL
+    assert f(rc=None) == A.BDR_EINVAL
+    assert f(mr=-1) == A.BDR_EINVAL
+    assert f(mr=0) == A.BDR_OK
+    need = L.dflash_fuse_fc_rows_workspace_bytes(8, 512, 2, A.BDR_BF16)
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert need >= 2 * a256(8 * 512 * 2)
+    assert f() == A.BDR_EWORKSPACE
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     from block_draft_readout_amd import _abi
     saved = _abi._lib
