@@ -1,0 +1,120 @@
+"""fp8 weight streaming of the drafter fc and the LM head (plain CPU definitions).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke entry point and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+Sources (web pages; cited by title and section):
+  * "docs(vllm): Qwen3.8-27B DFlash drafter recipe" (intel/llm-scaler PR #620),
+    summary and "Published artifacts": the drafter checkpoints are published
+    under fp8 names (drafter-fp8-v5, qwen3.8-27b-dflash-drafter-fp8-b70).
+  * "Qwen3.8-27B-DSpark -- vLLM-ready" model card, "Target quantisation": the
+    tapped hidden states are bf16 activations whatever the weights' storage.
+
+Readings (the pages name the checkpoints fp8 but give no format):
+  * Weights are OCP 8-bit floating point E4M3 in its finite-only form: one sign
+    bit, four exponent bits with bias 7, three mantissa bits; exponent field 0
+    holds the subnormals m/8 * 2^-6; there are no infinities, the two codes
+    with every exponent and mantissa bit set are NaN, and 448 is the largest
+    magnitude.
+  * One float32 scale per output row: W[n, k] = scale[n] * e4m3(code[n, k]).
+  * Activations stay in their storage dtype (bf16); products are summed
+    exactly (float64 here), the row scale multiplies the sum, and the result
+    is rounded once to float32.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+from .reference import LM_HEAD_SLICE, round_to_f32, widen
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 code, straight from the field definition."""
+    code = int(code)
+    if not 0 <= code <= 255:
+        raise ValueError("an fp8 code is a byte")
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        mag = (m / 8.0) * 2.0 ** -6
+    else:
+        mag = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return sign * mag
+
+
+# the 256 values, built from the definition above
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Exact float64 values of an array of E4M3 codes (uint8)."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise ValueError("fp8 weights are stored as uint8 codes")
+    return E4M3_TABLE[c]
+
+
+def _scaled_weights(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    W = decode_e4m3(codes)
+    if not np.all(np.isfinite(W)):
+        raise ValueError("fp8 weights must not hold NaN codes")
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    if s.shape != (W.shape[0],) or not np.all(np.isfinite(s)):
+        raise ValueError("one finite float32 scale per output row is required")
+    return W, s
+
+
+def lm_head_fp8(hidden: np.ndarray, lm_q: np.ndarray, lm_scale: np.ndarray,
+                dtype: str) -> np.ndarray:
+    """Z[..., v] = lm_scale[v] * sum_h hidden[..., h] * e4m3(lm_q[v, h]); float32.
+
+    The LM head of the DSpark greedy sample (llm-scaler PR #620, DSpark port
+    notes) with its [V, H] weight held as E4M3 codes and per-row scales.
+    """
+    hid = widen(hidden, dtype)
+    if not np.all(np.isfinite(hid)):
+        raise ValueError("hidden must be finite")
+    lead, H = hid.shape[:-1], hid.shape[-1]
+    V, H2 = np.shape(lm_q)
+    if H2 != H:
+        raise ValueError("lm head must be [V, H]")
+    if np.shape(lm_scale) != (V,):
+        raise ValueError("lm head scales must be [V]")
+    h2 = hid.reshape(-1, H)
+    Z = np.empty((h2.shape[0], V), dtype=np.float32)
+    for v0 in range(0, V, LM_HEAD_SLICE):
+        v1 = min(V, v0 + LM_HEAD_SLICE)
+        W, s = _scaled_weights(lm_q[v0:v1], lm_scale[v0:v1])
+        Z[:, v0:v1] = round_to_f32((h2 @ W.T) * s[None, :])
+    return Z.reshape(*lead, V)
+
+
+def fuse_fc_fp8(taps: Sequence[np.ndarray], fc_q: np.ndarray, fc_scale: np.ndarray,
+                dtype: str) -> np.ndarray:
+    """F[m, o] = fc_scale[o] * sum_t sum_h taps[t][m, h] * e4m3(fc_q[o, t*H + h]).
+
+    The drafter fc on the feature-wise concatenation of the taps (vllm-backport
+    PR #128, "What was missing" item 1), weight [H, T*H] as E4M3 codes with one
+    scale per output row; float32 result of the exact sum times the scale.
+    """
+    T = len(taps)
+    if T < 1:
+        raise ValueError("at least one tap is required")
+    rows, H = np.shape(taps[0])
+    for t in taps:
+        if np.shape(t) != (rows, H):
+            raise ValueError("all taps must be [rows, H]")
+    if np.shape(fc_q) != (H, T * H):
+        raise ValueError(f"fc weight must be [H, T*H] = [{H}, {T * H}], got {np.shape(fc_q)}")
+    X = np.concatenate([widen(t, dtype) for t in taps], axis=1)
+    if not np.all(np.isfinite(X)):
+        raise ValueError("taps must be finite")
+    W, s = _scaled_weights(fc_q, fc_scale)
+    return round_to_f32((X @ W.T) * s[None, :])

@@ -100,6 +100,45 @@ def make_weights(w: Workload) -> Dict[str, np.ndarray]:
     return out
 
 
+def quantize_e4m3_rows(x: np.ndarray, rows_at_once: int = 8192):
+    """float32 [N, K] -> (E4M3 codes uint8 [N, K], float32 scales [N]).
+
+    The synthetic fp8 checkpoint recipe: scale[n] = max_k |x[n, k]| / 448 (1 for
+    an all-zero row) and code = x / scale rounded to nearest even by torch's CPU
+    float8_e4m3fn conversion, so every row uses the full E4M3 range.  This makes
+    inputs for the fp8 weight path; that path only reads codes and scales.
+    """
+    import torch
+    x = np.asarray(x, dtype=np.float32)
+    N, K = x.shape
+    codes = np.empty((N, K), dtype=np.uint8)
+    amax = np.abs(x).max(axis=1) if K else np.zeros(N, dtype=np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    for r0 in range(0, N, rows_at_once):
+        r1 = min(N, r0 + rows_at_once)
+        t = torch.from_numpy(x[r0:r1]) / torch.from_numpy(scale[r0:r1])[:, None]
+        codes[r0:r1] = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def make_weights_fp8(w: Workload) -> Dict[str, np.ndarray]:
+    """The weights of make_weights with fc_w and lm_w as E4M3 codes + row scales.
+
+    fc_q [H, T*H] / fc_scale [H] and lm_q [V, H] / lm_scale [V] quantise the
+    same float32 draws that make_weights stores; markov_w1 / markov_w2 keep the
+    workload's storage dtype.
+    """
+    H, V, r, K = w.hidden, w.vocab, w.rank, w.fc_in
+    out = {}
+    out["fc_q"], out["fc_scale"] = quantize_e4m3_rows(
+        normal_f32((H, K), (w.cid, 0, 0, _W_FC), math.sqrt(1.0 / K)))
+    out["lm_q"], out["lm_scale"] = quantize_e4m3_rows(
+        normal_f32((V, H), (w.cid, 0, 0, _W_LM), math.sqrt(1.0 / H)))
+    out["w1"] = store(normal_f32((V, r), (w.cid, 0, 0, _W_W1), 1.0), w.dtype)
+    out["w2"] = store(normal_f32((V, r), (w.cid, 0, 0, _W_W2), math.sqrt(0.1)), w.dtype)
+    return out
+
+
 def make_step(w: Workload, step: int, noise: bool = True,
               noise_step: Optional[int] = None) -> Dict[str, object]:
     """Per-step activations.
