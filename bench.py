@@ -37,13 +37,14 @@ def log(msg):
 
 GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "gemm_wg3.hip",
                 "bdr_device.h", "bdr_internal.h")
+GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_kernels.h", "bdr_device.h", "bdr_internal.h")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=GEMM_SOURCES) -> str:
     """Hash of the code (comments and whitespace removed) of the sources that
     define the LM-head GEMM kernels."""
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "block_draft_readout_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -52,16 +53,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, fp8: bool = False):
     """HBM bytes per LM-head launch from the committed rocprofv3 counter summary,
     or None when the summary is missing or the kernel has changed since."""
-    path = os.path.join(PROFILES, f"lm_head_gemm_{workload}_pmc.md")
+    name = f"lm_head_gemm_fp8_{workload}_pmc.md" if fp8 else f"lm_head_gemm_{workload}_pmc.md"
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    want = kernel_source_hash(GEMM_FP8_SOURCES if fp8 else GEMM_SOURCES)
+    if not m_hash or not m_bytes or m_hash.group(1) != want:
         return None
     return float(m_bytes.group(1))
 
@@ -69,9 +72,10 @@ def recorded_traffic(workload: str):
 class Step:
     """Pre-bound C-ABI calls of one pool slot (pointers resolved once)."""
 
-    def __init__(self, L, w, dt, g, slot, bufs, stream, sample=None):
+    def __init__(self, L, w, dt, g, slot, bufs, stream, sample=None, fp8=False):
         self.L, self.w, self.dt, self.g, self.s, self.b = L, w, dt, g, slot, bufs
         self.sample = sample      # None: greedy; else (temperature, seed)
+        self.fp8 = fp8            # fc and LM head weights as E4M3 codes + row scales
         self.stream = stream
         self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
@@ -79,12 +83,22 @@ class Step:
 
     def fc(self):
         w, b = self.w, self.b
+        if self.fp8:
+            return self.L.dflash_fuse_fc_fp8(self.taps, w.n_taps, w.rows, w.hidden,
+                                             self.g["fc_q"].data_ptr(), self.g["fc_scale"].data_ptr(),
+                                             b["F"].data_ptr(), b["ws_fc"], b["ws_fc_n"],
+                                             self.fc_stream)
         return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
                                      self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
                                      b["ws_fc"], b["ws_fc_n"], self.fc_stream)
 
     def lm_head(self):
         w = self.w
+        if self.fp8:
+            return self.L.dspark_lm_head_fp8(self.s["draft_hidden"].data_ptr(), w.batch * w.k,
+                                             w.hidden, w.vocab, self.g["lm_q"].data_ptr(),
+                                             self.g["lm_scale"].data_ptr(),
+                                             self.b["logits"].data_ptr(), self.stream)
         return self.L.dspark_lm_head(self.s["draft_hidden"].data_ptr(), w.batch * w.k, w.hidden,
                                      w.vocab, self.dt, self.g["lm_w"].data_ptr(),
                                      self.b["logits"].data_ptr(), self.stream)
@@ -104,6 +118,9 @@ class Step:
 
     def draft_block(self):
         w, b = self.w, self.b
+        if self.fp8:     # the same two calls with the fp8 LM head
+            rc = self.lm_head()
+            return rc if rc != 0 else self.markov()
         return self.L.dspark_draft_block(self.s["draft_hidden"].data_ptr(), w.batch, w.k,
                                          w.hidden, w.vocab, self.dt, self.g["lm_w"].data_ptr(),
                                          self.g["w1"].data_ptr(), self.g["w2"].data_ptr(), w.rank,
@@ -151,11 +168,13 @@ def check(rc, what):
         raise RuntimeError(f"{what} failed ({rc}): {bdr.lib().bdr_last_error().decode()}")
 
 
-def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None):
+def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None, fp8=False):
     """The oracle, as it stands, on whole block-steps of the workload: repeats
     the step of pool slot 0 until about ``budget_s`` seconds of CPU work.
-    ``sample`` = (temperature, seed) times the probabilistic path instead."""
+    ``sample`` = (temperature, seed) times the probabilistic path instead;
+    ``fp8`` times the fp8-weight fc and LM head."""
     import oracle
+    from oracle import fp8 as ofp8
     from oracle import sampling
     try:
         from threadpoolctl import threadpool_info
@@ -165,7 +184,13 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None):
     n = 0
     t0 = time.perf_counter()
     while True:
-        if sample is None:
+        if fp8:
+            ofp8.fuse_fc_fp8(slot_host["taps"], W["fc_q"], W["fc_scale"], w.dtype)
+            Z = ofp8.lm_head_fp8(slot_host["draft_hidden"], W["lm_q"], W["lm_scale"], w.dtype)
+            d, _ = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], slot_host["prev0"], w.dtype)
+            Lb = oracle.truncate_by_confidence(slot_host["conf"], w.threshold, w.batch, w.k)
+            oracle.verify_greedy(d, oracle.target_argmax(slot_host["Y"], w.dtype, Lb), Lb)
+        elif sample is None:
             oracle.block_step(w.dtype, slot_host["taps"], W["fc_w"], slot_host["draft_hidden"],
                               W["lm_w"], W["w1"], W["w2"], slot_host["prev0"],
                               target_logits=slot_host["Y"], confidence=slot_host["conf"],
@@ -182,6 +207,7 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None):
             break
     return {"value": n / dt, "unit": "block-steps/s", "cores": int(blas), "kind": "oracle",
             "sample": f"{n} full {'probabilistic' if sample else 'greedy'} block-steps of "
+                      f"{'(fp8 weights) ' if fp8 else ''}"
                       f"{w.name} (S1-S4, all {w.batch} rows) in "
                       f"{dt:.1f} s on the host; numpy float64 with BLAS threads={blas}, "
                       f"affinity cores={len(os.sched_getaffinity(0))}"}
@@ -274,6 +300,9 @@ def main():
     ap.add_argument("--fc-rows", type=int, default=0,
                     help="time the drafter fc alone on this many rows (the prefill-shaped, "
                          "MFMA-bound fc) with the workload's H and taps, instead of block-steps")
+    ap.add_argument("--weights", choices=("native", "fp8"), default="native",
+                    help="native: fc and LM head weights in the workload's dtype; fp8: E4M3 "
+                         "codes with one fp32 scale per row (bf16 workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
@@ -281,6 +310,10 @@ def main():
 
     if args.closed_loop and args.graph:
         print(json.dumps({"error": "--closed-loop runs eagerly (no --graph)"}))
+        sys.exit(2)
+    fp8 = args.weights == "fp8"
+    if fp8 and (args.closed_loop or args.draft != "greedy" or args.fc_rows > 0):
+        print(json.dumps({"error": "--weights fp8 times greedy independent block-steps only"}))
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -307,8 +340,11 @@ def main():
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
+    if fp8 and w.dtype != "bf16":
+        print(json.dumps({"error": "--weights fp8 needs a bf16 workload"}))
+        sys.exit(2)
     t0 = time.time()
-    W = synth.make_weights(w)
+    W = synth.make_weights_fp8(w) if fp8 else synth.make_weights(w)
     g = {k: up(v) for k, v in W.items()}
     log(f"{w.describe()}: weights ready in {time.time() - t0:.1f}s")
 
@@ -341,7 +377,8 @@ def main():
                           ("draft_list", (B, k)), ("row_index", (B * (k + 1),)), ("row_count", (1,)),
                           ("row_offsets", (B + 1,))):
             bufs[name] = torch.zeros(shp, dtype=torch.int32, device=dev)
-    for key, n in (("ws_fc", L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
+    for key, n in (("ws_fc", L.dflash_fuse_fc_fp8_workspace_bytes(w.rows, H, w.n_taps) if fp8
+                     else L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
                    ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
                    ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
                    ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
@@ -362,7 +399,7 @@ def main():
         conf = synth.make_confidence(w, p)
         slot["conf"] = None if conf is None else up(conf)
         st = Step(L, w, dt, g, slot, bufs, sptr,
-                  sample=(args.temperature, 0x5EED0000 + p) if sampling else None)
+                  sample=(args.temperature, 0x5EED0000 + p) if sampling else None, fp8=fp8)
         check(st.draft_block(), "dspark_draft_block")
         if sampling:   # plant the targets on this step's sampled draft
             check(st.markov(), "dspark_markov_sample")
@@ -489,10 +526,13 @@ def main():
                  for j, (name, _) in enumerate(stage_fns)}
     log(f"stages (us): {stages_us}")
 
-    lm_bytes = V * H * (2 if w.dtype == "bf16" else 4) + B * k * H * (2 if w.dtype == "bf16" else 4) \
-        + B * k * V * 4
+    es = 2 if w.dtype == "bf16" else 4
+    if fp8:      # codes + row scales, bf16 hidden states, fp32 logits
+        lm_bytes = V * H + V * 4 + B * k * H * es + B * k * V * 4
+    else:
+        lm_bytes = V * H * es + B * k * H * es + B * k * V * 4
     achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(w.name)
+    traffic = recorded_traffic(w.name, fp8)
     log(f"step {ms_step * 1e3:.1f} us; LM head {lm_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
 
     if args.calib_copy:
@@ -508,7 +548,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one block-step ...")
         cpu = cpu_baseline(w, W, host0,
-                           sample=(args.temperature, 0x5EED0000) if sampling else None)
+                           sample=(args.temperature, 0x5EED0000) if sampling else None, fp8=fp8)
         log(f"cpu oracle: {1.0 / cpu['value']:.1f} s per block-step")
 
     out = {
@@ -530,12 +570,15 @@ def main():
                    "fc_overlap": "none (closed loop)" if args.closed_loop else args.overlap,
                    "loop": "closed" if args.closed_loop else "independent steps",
                    "draft": args.draft,
+                   "weights": "fp8-e4m3 codes + fp32 row scales (fc, LM head)" if fp8
+                   else w.dtype,
                    **({"temperature": args.temperature} if sampling else {}),
                    "pool_steps": args.pool},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "LM-head weight-streaming GEMM (dspark_lm_head)",
+                     "kernel": "LM-head weight-streaming GEMM (dspark_lm_head_fp8)" if fp8
+                     else "LM-head weight-streaming GEMM (dspark_lm_head)",
                      "avg_launch_us": lm_ms * 1e3,
                      "algorithmic_bytes_per_launch": lm_bytes},
         "stages_us": stages_us,

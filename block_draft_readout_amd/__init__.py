@@ -21,7 +21,8 @@ from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
-    "spec_commit", "dflash_fuse_fc_rows", "workspace_bytes", "lib", "BdrError",
+    "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
+    "workspace_bytes", "lib", "BdrError",
 ]
 
 
@@ -77,6 +78,8 @@ def workspace_bytes(kind: str, **kw) -> int:
     L = lib()
     if kind == "fc":
         return L.dflash_fuse_fc_workspace_bytes(kw["rows"], kw["hidden"], kw["n_taps"], kw["dtype"])
+    if kind == "fc_fp8":
+        return L.dflash_fuse_fc_fp8_workspace_bytes(kw["rows"], kw["hidden"], kw["n_taps"])
     if kind == "markov":
         return L.dspark_markov_workspace_bytes(kw["batch"], kw["k"])
     if kind == "draft":
@@ -136,6 +139,62 @@ def dspark_lm_head(hidden: torch.Tensor, lm_head_w: torch.Tensor,
     _abi.check("dspark_lm_head", L.dspark_lm_head(_ptr(hidden), rows, H, V, _dt(lm_head_w),
                                                   _ptr(lm_head_w), _ptr(logits),
                                                   _stream(hidden.device)))
+    return logits
+
+
+# ----------------------------------------------------------------------------- S1/S2, fp8 weights
+def _fp8_weight(q: torch.Tensor, scale: torch.Tensor, qname: str, sname: str):
+    _dev(q, qname)
+    _dev(scale, sname)
+    if q.dtype != torch.uint8 or q.dim() != 2:
+        raise ValueError(f"{qname} must be a 2-D uint8 tensor of E4M3 codes")
+    if scale.dtype != torch.float32 or tuple(scale.shape) != (q.shape[0],):
+        raise ValueError(f"{sname} must be fp32 [{q.shape[0]}]")
+
+
+def dflash_fuse_fc_fp8(taps: Sequence[torch.Tensor], fc_q: torch.Tensor, fc_scale: torch.Tensor,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 out[rows, H] = fc_scale * (concat(taps) @ e4m3(fc_q)^T)  (taps bf16 [rows, H])."""
+    L = lib()
+    T = len(taps)
+    rows, H = taps[0].shape
+    for i, t in enumerate(taps):
+        _dev(t, f"taps[{i}]")
+        if t.shape != (rows, H) or t.dtype != torch.bfloat16:
+            raise ValueError("taps must all be bf16 [rows, H]")
+    _fp8_weight(fc_q, fc_scale, "fc_q", "fc_scale")
+    if tuple(fc_q.shape) != (H, T * H):
+        raise ValueError(f"fc_q must be [{H}, {T * H}]")
+    if out is None:
+        out = torch.empty((rows, H), dtype=torch.bfloat16, device=fc_q.device)
+    _dev(out, "out")
+    need = L.dflash_fuse_fc_fp8_workspace_bytes(rows, H, T)
+    ws = _workspace(need, fc_q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    _abi.check("dflash_fuse_fc_fp8", L.dflash_fuse_fc_fp8(arr, T, rows, H, _ptr(fc_q),
+                                                          _ptr(fc_scale), _ptr(out), wp, wn,
+                                                          _stream(fc_q.device)))
+    return out
+
+
+def dspark_lm_head_fp8(hidden: torch.Tensor, lm_head_q: torch.Tensor, lm_head_scale: torch.Tensor,
+                       logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 logits [..., V] = lm_head_scale * (hidden[..., H] @ e4m3(lm_head_q)[V, H]^T)."""
+    L = lib()
+    _dev(hidden, "hidden")
+    _fp8_weight(lm_head_q, lm_head_scale, "lm_head_q", "lm_head_scale")
+    V, H = lm_head_q.shape
+    if hidden.shape[-1] != H or hidden.dtype != torch.bfloat16:
+        raise ValueError("hidden must be bf16 [..., H]")
+    rows = hidden.numel() // H
+    if logits is None:
+        logits = torch.empty((*hidden.shape[:-1], V), dtype=torch.float32, device=hidden.device)
+    _dev(logits, "logits")
+    _abi.check("dspark_lm_head_fp8", L.dspark_lm_head_fp8(_ptr(hidden), rows, H, V,
+                                                          _ptr(lm_head_q), _ptr(lm_head_scale),
+                                                          _ptr(logits), _stream(hidden.device)))
     return logits
 
 

@@ -155,7 +155,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int bdr_abi_version(void) { return 2; }
+int bdr_abi_version(void) { return 3; }
 
 const char* bdr_last_error(void) { return g_err; }
 
@@ -200,6 +200,76 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size, int64_
   hipError_t e = launch_gemm(p, dt, a, 1, hidden_size, rows, vocab, lm_head_w, logits, OUT_F32,
                              nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_lm_head launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S1/S2, fp8 weights
+namespace {
+
+// bf16 activations [rows, H] read against E4M3 weights [N, K] with K = n_seg * H
+int fp8_shape(int64_t rows, int64_t hidden, int n_seg, int64_t n_out) {
+  if (n_seg < 1) return fail(BDR_EINVAL, "n_taps must be >= 1, got %d", n_seg);
+  if (n_seg > BDR_MAX_TAPS) return fail(BDR_EUNSUPPORTED, "n_taps %d > %d", n_seg, BDR_MAX_TAPS);
+  if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
+  if (hidden <= 0) return fail(BDR_EINVAL, "hidden must be > 0");
+  if (n_out <= 0) return fail(BDR_EINVAL, "output width must be > 0");
+  if (n_out > kMaxVocab) return fail(BDR_EUNSUPPORTED, "output width must be < 2^31 - 1");
+  if (hidden % 64)
+    return fail(BDR_EUNSUPPORTED, "hidden %lld must be a multiple of 64 for fp8 weights",
+                static_cast<long long>(hidden));
+  // each activation tensor, and the W rows one workgroup streams (<= 192 rows), under 2^31 bytes
+  if (rows > kMaxBytes / (hidden * 2) || hidden * n_seg > kMaxBytes / 192 ||
+      n_out > kMaxElems / (hidden * n_seg) || rows > kMaxElems / n_out)
+    return fail(BDR_EUNSUPPORTED, "problem too large (per-operand byte limit 2^31)");
+  return BDR_OK;
+}
+
+}  // namespace
+
+size_t dflash_fuse_fc_fp8_workspace_bytes(int64_t rows, int64_t hidden, int n_taps) {
+  if (fp8_shape(rows, hidden, n_taps, hidden) != BDR_OK || rows == 0) return 0;
+  return plan_gemm_fp8(rows, hidden, hidden * n_taps, true, n_taps).workspace;
+}
+
+int dflash_fuse_fc_fp8(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                       const uint8_t* fc_q, const float* fc_scale, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  BDR_TRY(fp8_shape(rows, hidden, n_taps, hidden));
+  if (rows == 0) return BDR_OK;
+  if (!taps) return fail(BDR_EINVAL, "taps must not be NULL");
+  for (int t = 0; t < n_taps; ++t) {
+    if (!taps[t]) return fail(BDR_EINVAL, "taps[%d] must not be NULL", t);
+    if (!aligned(taps[t], 16)) return fail(BDR_EINVAL, "taps[%d] must be 16-byte aligned", t);
+  }
+  BDR_TRY(need_ptr(fc_q, "fc_q"));
+  BDR_TRY(need_ptr(fc_scale, "fc_scale", 4));
+  BDR_TRY(need_ptr(out, "out"));
+  const GemmPlan p = plan_gemm_fp8(rows, hidden, hidden * n_taps, true, n_taps);
+  if (!p.stream) return fail(BDR_EUNSUPPORTED, "fc shape not supported with fp8 weights");
+  BDR_TRY(need_ws(workspace, workspace_bytes, p.workspace));
+  BDR_TRY(check_device());
+  hipError_t e = launch_gemm_fp8(p, taps, n_taps, hidden, rows, hidden, fc_q, fc_scale, out,
+                                 OUT_BF16, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_fp8 launch");
+  return BDR_OK;
+}
+
+int dspark_lm_head_fp8(const void* hidden, int64_t rows, int64_t hidden_size, int64_t vocab,
+                       const uint8_t* lm_head_q, const float* lm_head_scale, float* logits,
+                       void* stream) {
+  BDR_TRY(fp8_shape(rows, hidden_size, 1, vocab));
+  if (rows == 0) return BDR_OK;
+  BDR_TRY(need_ptr(hidden, "hidden"));
+  BDR_TRY(need_ptr(lm_head_q, "lm_head_q"));
+  BDR_TRY(need_ptr(lm_head_scale, "lm_head_scale", 4));
+  BDR_TRY(need_ptr(logits, "logits"));
+  const GemmPlan p = plan_gemm_fp8(rows, vocab, hidden_size, false);
+  if (!p.stream) return fail(BDR_EUNSUPPORTED, "LM-head shape not supported with fp8 weights");
+  BDR_TRY(check_device());
+  const void* a[1] = {hidden};
+  hipError_t e = launch_gemm_fp8(p, a, 1, hidden_size, rows, vocab, lm_head_q, lm_head_scale,
+                                 logits, OUT_F32, nullptr, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dspark_lm_head_fp8 launch");
   return BDR_OK;
 }
 

@@ -52,6 +52,14 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,
                        OutKind out_kind, void* workspace, hipStream_t stream);
 
+// fp8 (E4M3) weights [N, K] with one fp32 scale per row, bf16 A segments
+// (multiples of 64 elements); plan.stream == false means the shape is not
+// supported.
+GemmPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split, int n_seg = 1);
+hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, int64_t seg,
+                           int64_t M, int64_t N, const uint8_t* w_q, const float* w_scale,
+                           void* out, OutKind out_kind, void* workspace, hipStream_t stream);
+
 // ----------------------------------------------------------------------------
 // Markov bias + semi-autoregressive argmax over k positions.
 // ----------------------------------------------------------------------------

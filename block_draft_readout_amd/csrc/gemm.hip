@@ -149,6 +149,7 @@ __global__ __launch_bounds__(64) void ws_gemm_kernel(const GemmArgs g) {
 constexpr int kKBB = 1024;            // bytes of each W row per visit
 constexpr int kPadRow = kKBB + 16;    // LDS row stride (breaks bank aliasing)
 constexpr int kStreamTiles = 16;      // max 16-row tiles per workgroup
+constexpr int kStreamTilesFp8 = 12;   // the same for fp8 weights (register budget)
 
 
 
@@ -306,17 +307,21 @@ static int pick_jn(int mt) { return mt <= 2 ? 4 : 2; }
 // Streaming plan: balanced row ranges (at most kStreamTiles tiles each) and a
 // K split chosen to minimise per-wave cost = W bytes + a quarter of the A bytes
 // it re-reads from L2 (+ the partial-sum round trip and a second launch).
+// fp8 weights (esize 1): visits of 1 KB of codes, A segments in multiples of 64
+// elements (the fp8 kernel loads A step by step from the segment of each step).
 static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
                         GemmPlan* p) {
   const int64_t kbytes = K * esize;
   const int64_t segbytes = kbytes / n_seg;
-  if (M > 16 || kbytes % 64 != 0 || (n_seg > 1 && segbytes % kKBB != 0)) return false;
+  if (M > 16 || kbytes % 64 != 0) return false;
+  if (n_seg > 1 && segbytes % (esize == 1 ? 64 : kKBB) != 0) return false;
+  const int64_t max_tiles = esize == 1 ? kStreamTilesFp8 : kStreamTiles;
   const int64_t waves = 4 * static_cast<int64_t>(kNumCU);
   const int64_t kblocks = (kbytes + kKBB - 1) / kKBB;
   double best = 1e300;
   for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
     int64_t nw = std::max<int64_t>(1, waves / ks);
-    nw = std::max<int64_t>(nw, (N + 16 * kStreamTiles - 1) / (16 * kStreamTiles));
+    nw = std::max<int64_t>(nw, (N + 16 * max_tiles - 1) / (16 * max_tiles));
     nw = std::min<int64_t>(nw, N);
     const int64_t kbps = (kblocks + ks - 1) / ks;
     const int64_t ks_eff = (kblocks + kbps - 1) / kbps;
@@ -371,9 +376,10 @@ static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allo
   const int64_t mtiles = (M + 15) / 16;
   if (M <= 16 || mtiles > kWgMaxTiles || kbytes % 64 != 0) return false;
   const int mtw = static_cast<int>((mtiles + kWgWaves - 1) / kWgWaves);
-  const int kbb = kWgKBB;
+  // fp8 weights (esize 1): K blocks of 256 elements (256 bytes of codes per row)
+  const int kbb = esize == 1 ? 256 : kWgKBB;
   if (n_seg > 1 && segbytes % kbb != 0) return false;
-  const bool bf16 = esize == 2;
+  const bool bf16 = esize <= 2;      // accumulator budget as for bf16
   const int ntmax = wg_nt_max(mtw, bf16);
   const int64_t kblocks = (kbytes + kbb - 1) / kbb;
   double best = 1e300;
@@ -503,6 +509,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
   return p;
 }
 
+// fp8 plans cover one slab of at most 16 rows; launch_gemm_fp8 runs the
+// slabs of a taller A one after another on the stream (sharing the workspace).
+GemmPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split, int n_seg) {
+  GemmPlan p;
+  if (M > 16) {
+    GemmPlan q;
+    if (plan_stream_wg(M, N, K, 1, allow_split, n_seg, &q)) return q;
+  }
+  if (!plan_stream(std::min<int64_t>(M, 16), N, K, 1, allow_split, n_seg, &p)) p.stream = false;
+  return p;
+}
+
 template <typename S, int MT>
 static void launch_mt(const GemmPlan& p, const GemmArgs& g, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.n_wg), static_cast<unsigned>(p.ksplit),
@@ -545,6 +563,17 @@ static void launch_stream(const GemmPlan& p, const GemmArgs& g, hipStream_t st) 
   else hipLaunchKernelGGL((ws_gemm_stream_kernel<S, 16>), grid, dim3(64), 0, st, sa);
 }
 
+// out = ordered sum of the ksplit fp32 partials in the workspace
+static hipError_t launch_splitk_reduce(const GemmPlan& p, int64_t M, int64_t N, void* out,
+                                       OutKind out_kind, void* workspace, hipStream_t stream) {
+  const int64_t mn = M * N;
+  const int64_t blocks = (mn + 1023) / 1024;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, static_cast<const float*>(workspace), p.ksplit, mn, out,
+                     static_cast<int>(out_kind));
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,
                        OutKind out_kind, void* workspace, hipStream_t stream) {
@@ -582,12 +611,53 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  const int64_t mn = M * N;
-  const int64_t blocks = (mn + 1023) / 1024;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, static_cast<const float*>(workspace), p.ksplit, mn, out,
-                     static_cast<int>(out_kind));
-  return hipGetLastError();
+  return launch_splitk_reduce(p, M, N, out, out_kind, workspace, stream);
+}
+
+hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, int64_t seg,
+                           int64_t M, int64_t N, const uint8_t* w_q, const float* w_scale,
+                           void* out, OutKind out_kind, void* workspace, hipStream_t stream) {
+  if (!p.stream) return hipErrorInvalidValue;
+  if (p.wg) {     // all rows in one launch of the workgroup kernel
+    GemmArgs g{};
+    for (int t = 0; t < n_seg; ++t) g.a[t] = a[t];
+    g.seg = seg;
+    g.M = M;
+    g.N = N;
+    g.K = seg * n_seg;
+    g.w = w_q;
+    g.w_scale = w_scale;
+    g.out_kind = out_kind;
+    const bool split = p.ksplit > 1;
+    g.partial = split ? 1 : 0;
+    g.out = split ? workspace : out;
+    const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
+    hipError_t e = launch_wg_fp8(p, sa, stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess && split) e = launch_splitk_reduce(p, M, N, out, out_kind, workspace, stream);
+    return e;
+  }
+  const int64_t out_es = out_kind == OUT_BF16 ? 2 : 4;
+  for (int64_t m0 = 0; m0 < M; m0 += 16) {
+    const int64_t ms = std::min<int64_t>(16, M - m0);
+    GemmArgs g{};
+    for (int t = 0; t < n_seg; ++t) g.a[t] = static_cast<const uint16_t*>(a[t]) + m0 * seg;
+    g.seg = seg;
+    g.M = ms;
+    g.N = N;
+    g.K = seg * n_seg;
+    g.w = w_q;
+    g.w_scale = w_scale;
+    g.out_kind = out_kind;
+    const bool split = p.ksplit > 1;
+    void* out_s = static_cast<char*>(out) + m0 * N * out_es;
+    g.partial = split ? 1 : 0;
+    g.out = split ? workspace : out_s;
+    hipError_t e = launch_stream_fp8(p, g, stream);
+    if (e == hipSuccess && split) e = launch_splitk_reduce(p, ms, N, out_s, out_kind, workspace, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace bdr

@@ -21,6 +21,7 @@ struct GemmArgs {
   int out_kind;                 // OutKind of a final output
   int partial;                  // 1: write fp32 partials indexed by blockIdx.y
   int64_t steps_per_split;      // K steps handled by one workgroup along K
+  const float* w_scale;         // fp8 weights: one scale per W row [N]; else unused
 };
 
 // Segment base pointer chosen with scalar selects (t is uniform), so the
@@ -161,18 +162,41 @@ __device__ __forceinline__ void wait_vm_visit(int n) {
   BDR_WAIT_VM_LGKM(BASE + PER * N, 0);
 }
 
+// fp8 weights: S = uint8_t means E4M3 codes with one fp32 scale per W row and
+// bf16 A.  A K block is then 256 elements: a W visit row holds 256 codes (256
+// bytes) and the A slice is the same 512 bytes per row as for bf16.
+template <typename S> constexpr bool kIsFp8 = std::is_same_v<S, uint8_t>;
+template <typename S> constexpr int kWgKbbW = kIsFp8<S> ? 256 : kWgKBB;   // W bytes per row per visit
+template <typename S> constexpr int kAElem = kIsFp8<S> ? 2 : static_cast<int>(sizeof(S));
+
 // LDS bytes of the workgroup kernel: R visits of VT tiles + one staging tile per A tile
-inline size_t wg_lds_bytes(int ring, int vt, int mtiles) {
-  return static_cast<size_t>(ring * vt + mtiles) * VisitShape<kWgKBB>::SLOT;
+inline size_t wg_lds_bytes(int ring, int vt, int mtiles, int kbb_w = kWgKBB) {
+  const size_t wslot = kbb_w == 256 ? VisitShape<256>::SLOT : VisitShape<kWgKBB>::SLOT;
+  return static_cast<size_t>(ring * vt) * wslot + static_cast<size_t>(mtiles) * VisitShape<kWgKBB>::SLOT;
+}
+
+// 16 E4M3 codes (little-endian bytes of q) -> bf16 operands of elements 0..7 (lo)
+// and 8..15 (hi); exact, every E4M3 value being a bf16 value
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t q, u32x4_t& lo, u32x4_t& hi) {
+  lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false));
+  lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true));
+  lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false));
+  lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true));
+  hi.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.z, 1.0f, false));
+  hi.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.z, 1.0f, true));
+  hi.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.w, 1.0f, false));
+  hi.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.w, 1.0f, true));
 }
 
 template <typename S, int MTW, int NT, int VT, int R>
 __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs sa) {
-  constexpr int KBB = kWgKBB;
-  using VS = VisitShape<KBB>;
-  constexpr int STEPS = VS::STEPS;
+  constexpr bool F8 = kIsFp8<S>;
+  constexpr int KBB = kWgKbbW<S>;        // W bytes per row per visit
+  using VS = VisitShape<KBB>;            // W visit geometry
+  using VA = VisitShape<kWgKBB>;         // A staging geometry (512 bytes per row)
+  constexpr int STEPS = VA::STEPS;       // 16-byte A operands per row and block
   constexpr int NI = VT * VS::NI;        // W loads per wave per visit
-  constexpr int NA = MTW * VS::NIA;      // A loads per wave per K block
+  constexpr int NA = MTW * VA::NIA;      // A loads per wave per K block
   constexpr int NV = NT / VT;            // visits per K block and pass (compile-time bound)
   constexpr int kAhead = R - 2;
   static_assert(NT % VT == 0, "tiles per pass must be whole visits");
@@ -198,7 +222,8 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   const int nkb = static_cast<int>(kb_hi - kb_lo);
   const OutRef out(g, blockIdx.y);
   const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
-  const uint32_t segbytes = static_cast<uint32_t>(g.seg * static_cast<int64_t>(sizeof(S)));
+  const uint32_t akbytes = static_cast<uint32_t>(g.K * kAElem<S>);      // A row bytes
+  const uint32_t segbytes = static_cast<uint32_t>(g.seg * kAElem<S>);
   const int mtiles = static_cast<int>((g.M + 15) / 16);
 
   // rows past the range (also those of a last visit's missing tile) read zeros
@@ -208,11 +233,15 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   // buffer-to-LDS lane mapping: row (lane % RPI) of the load, 16-byte chunk lane / RPI
   const uint32_t dma_chunk = static_cast<uint32_t>(lane / VS::RPI) * 16;
   const uint32_t dma_row = static_cast<uint32_t>(lane % VS::RPI);
-  // operand read of row r16, chunk grp + 4 * step inside a tile
+  const uint32_t dma_chunk_a = static_cast<uint32_t>(lane / VA::RPI) * 16;
+  const uint32_t dma_row_a = static_cast<uint32_t>(lane % VA::RPI);
+  // operand read of row r16, chunk grp + 4 * step inside a W tile
   const uint32_t rd = static_cast<uint32_t>((r16 / VS::RPI) * VS::GROUP +
                                             (grp * VS::RPI + r16 % VS::RPI) * 16);
+  // chunk c of row r16 inside an A staging tile: rd_a + c * 16 * VA::RPI
+  const uint32_t rd_a = static_cast<uint32_t>((r16 / VA::RPI) * VA::GROUP + (r16 % VA::RPI) * 16);
   constexpr int VSLOT = VT * VS::SLOT;        // one visit
-  char* const stage = lds + R * VSLOT;        // A staging, one SLOT per A tile
+  char* const stage = lds + R * VSLOT;        // A staging, one VA::SLOT per A tile
 
   f32x4_t acc[NT][MTW];
   auto zero_acc = [&]() {
@@ -245,31 +274,35 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   // this wave's A tiles of K block kb -> staging (rows >= M and bytes past K
   // read zeros; K blocks never straddle A segments); tiles_w * NIA loads
   auto dma_a = [&](uint32_t kb) {
-    const uint32_t k0 = kb * KBB;
+    const uint32_t k0 = kb * kWgKBB;          // A bytes
     const uint32_t ts = k0 / segbytes;
     const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
-    const uint32_t lo = k0 + dma_chunk < kbytes ? (k0 - ts * segbytes) + dma_chunk : kOOB;
+    const uint32_t lo = k0 + dma_chunk_a < akbytes ? (k0 - ts * segbytes) + dma_chunk_a : kOOB;
     static_for<MTW>([&](auto mw) {
       const int mt = wave + kWgWaves * mw;
       if (mt < mtiles) {
-        char* dst = stage + mt * VS::SLOT;
+        char* dst = stage + mt * VA::SLOT;
 #pragma unroll
-        for (int j = 0; j < VS::NIA; ++j) {
-          const uint32_t row = static_cast<uint32_t>(16 * mt + j * VS::RPI) + dma_row;
+        for (int j = 0; j < VA::NIA; ++j) {
+          const uint32_t row = static_cast<uint32_t>(16 * mt + j * VA::RPI) + dma_row_a;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              ra, (__attribute__((address_space(3))) void*)(dst + j * VS::GROUP), 16,
+              ra, (__attribute__((address_space(3))) void*)(dst + j * VA::GROUP), 16,
               lo + row * segbytes, 0, 0, 0);
         }
       }
     });
   };
+  // A operand i of row r16: bf16/fp32 W -> chunk 4i + grp (elements of MFMA
+  // step i); fp8 W -> chunk 8(i/2) + 2grp + i%2, i.e. elements 64(i/2) + 16grp
+  // + 8(i%2) + [0, 8), matching the 16 codes a lane reads per 64-element step
   auto stage_to_regs = [&]() {
     static_for<MTW>([&](auto mw) {
       const int mt = wave + kWgWaves * mw;
       if (mt < mtiles) {
-        const char* src = stage + mt * VS::SLOT + rd;
+        const char* src = stage + mt * VA::SLOT + rd_a;
         static_for<STEPS>([&](auto st) {
-          a[mw][st] = *reinterpret_cast<const u32x4_t*>(src + st * 64 * VS::RPI);
+          const int c = F8 ? 8 * (st / 2) + 2 * grp + st % 2 : 4 * st + grp;
+          a[mw][st] = *reinterpret_cast<const u32x4_t*>(src + c * 16 * VA::RPI);
         });
       }
     });
@@ -277,23 +310,47 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   // all VT tiles of visit vt (compile-time) of the current pass, from a ring slot
   auto compute = [&](auto vt, int slot) {
     const char* src = lds + slot * VSLOT + rd;
-    u32x4_t bv[VT][STEPS];
-    static_for<VT>([&](auto u) {
-      static_for<STEPS>([&](auto st) {
-        bv[u][st] = *reinterpret_cast<const u32x4_t*>(src + u * VS::SLOT + st * 64 * VS::RPI);
-      });
-    });
-    static_for<VT>([&](auto u) {
-      constexpr int t = VT * decltype(vt)::value + decltype(u)::value;
-      static_for<STEPS>([&](auto st) {
-        static_for<MTW>([&](auto mw) {
-          acc[t][mw] = mma16(a[mw][st], bv[u][st], acc[t][mw], S());
+    if constexpr (F8) {
+      // per 64-element step: 16 codes of row r16 -> two bf16 operands
+      constexpr int WS = VS::STEPS;
+      u32x4_t q[VT][WS];
+      static_for<VT>([&](auto u) {
+        static_for<WS>([&](auto st) {
+          q[u][st] = *reinterpret_cast<const u32x4_t*>(src + u * VS::SLOT + st * 64 * VS::RPI);
         });
       });
-    });
-    // issue all of the visit's LDS reads before its MFMAs (one latency per visit)
-    __builtin_amdgcn_sched_group_barrier(0x100, VT * STEPS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, VT * STEPS * MTW * Elem<S>::MFMA_PER16, 0);
+      static_for<VT>([&](auto u) {
+        constexpr int t = VT * decltype(vt)::value + decltype(u)::value;
+        static_for<WS>([&](auto st) {
+          u32x4_t lo, hi;
+          e4m3x16_to_bf16(q[u][st], lo, hi);
+          static_for<MTW>([&](auto mw) {
+            acc[t][mw] = mma16(a[mw][2 * st], lo, acc[t][mw], uint16_t());
+            acc[t][mw] = mma16(a[mw][2 * st + 1], hi, acc[t][mw], uint16_t());
+          });
+        });
+      });
+      __builtin_amdgcn_sched_group_barrier(0x100, VT * WS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, VT * WS * MTW * 2, 0);
+    } else {
+      u32x4_t bv[VT][STEPS];
+      static_for<VT>([&](auto u) {
+        static_for<STEPS>([&](auto st) {
+          bv[u][st] = *reinterpret_cast<const u32x4_t*>(src + u * VS::SLOT + st * 64 * VS::RPI);
+        });
+      });
+      static_for<VT>([&](auto u) {
+        constexpr int t = VT * decltype(vt)::value + decltype(u)::value;
+        static_for<STEPS>([&](auto st) {
+          static_for<MTW>([&](auto mw) {
+            acc[t][mw] = mma16(a[mw][st], bv[u][st], acc[t][mw], S());
+          });
+        });
+      });
+      // issue all of the visit's LDS reads before its MFMAs (one latency per visit)
+      __builtin_amdgcn_sched_group_barrier(0x100, VT * STEPS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, VT * STEPS * MTW * Elem<S>::MFMA_PER16, 0);
+    }
   };
 
   int nvis = 0;
@@ -346,7 +403,7 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
         }
         if (full) {
           if (vt <= kAhead && more)
-            wait_vm_visit<NI * kAhead, VS::NIA, MTW>(tiles_w);
+            wait_vm_visit<NI * kAhead, VA::NIA, MTW>(tiles_w);
           else
             BDR_WAIT_VM_LGKM(NI * kAhead, 0);
         } else {
@@ -374,7 +431,12 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t m = 16 * mt + 4 * grp + i;
-          if (t < ntp && m < out.M && n < n_hi) out.put(m, n, acc[t][mw][i]);
+          if (t < ntp && m < out.M && n < n_hi) {
+            if constexpr (F8)
+              out.put(m, n, acc[t][mw][i] * g.w_scale[n]);
+            else
+              out.put(m, n, acc[t][mw][i]);
+          }
         }
       });
     });
@@ -390,28 +452,31 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
 // Visit width and ring depth by A tiles per wave: one-tile visits (the
 // fewest operand registers), and as deep a ring as LDS holds next to the A
 // staging of 4 * MTW tiles.
-template <int MTW> struct WgShape {
+template <int MTW, bool F8 = false> struct WgShape {
   static constexpr int VT = 1;
-  static constexpr int R = MTW == 1 ? 12 : MTW == 2 ? 10 : 9;
+  // fp8 visits are half the bytes: twice the ring depth keeps as many bytes in flight
+  static constexpr int R = F8 ? (MTW == 1 ? 22 : MTW == 2 ? 18 : 16)
+                              : (MTW == 1 ? 12 : MTW == 2 ? 10 : 9);
 };
 
 // Launch one instantiation with its dynamic LDS (ring + staging for mt tiles).
 template <typename S, int MTW, int NT>
 hipError_t launch_wg_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  constexpr int VT = WgShape<MTW>::VT;
-  constexpr int R = WgShape<MTW>::R;
+  constexpr int VT = WgShape<MTW, kIsFp8<S>>::VT;
+  constexpr int R = WgShape<MTW, kIsFp8<S>>::R;
+  constexpr int KW = kWgKbbW<S>;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&ws_gemm_stream_wg_kernel<S, MTW, NT, VT, R>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(wg_lds_bytes(R, VT, std::min(kWgWaves * MTW, kWgMaxTiles))));
+        static_cast<int>(wg_lds_bytes(R, VT, std::min(kWgWaves * MTW, kWgMaxTiles), KW)));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
   hipLaunchKernelGGL((ws_gemm_stream_wg_kernel<S, MTW, NT, VT, R>), grid, dim3(64 * kWgWaves),
-                     wg_lds_bytes(R, VT, p.mt), st, sa);
+                     wg_lds_bytes(R, VT, p.mt, KW), st, sa);
   return hipSuccess;
 }
 
@@ -423,5 +488,9 @@ int tile_cols(int shape);   // output columns of a tiled-variant workgroup tile
 hipError_t launch_wg_mtw1(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
 hipError_t launch_wg_mtw2(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
 hipError_t launch_wg_mtw3(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
+// fp8 (E4M3) weights with per-row scales, bf16 A: one-wave streaming kernel
+// (gemm_fp8.hip) and the workgroup kernel's fp8 instantiations (gemm_wg_fp8.hip)
+hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t st);
+hipError_t launch_wg_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 
 }  // namespace bdr

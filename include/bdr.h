@@ -111,6 +111,52 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size,
                    float* logits, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * S1/S2 with fp8 weights -- the fc and the LM head streaming one byte per
+ * weight.
+ *
+ * out[m, n] = scale[n] * sum_k x[m, k] * e4m3(q[n, k])
+ *
+ * The drafter checkpoints are published under fp8 names ([recipe] summary
+ * and "Published artifacts": drafter-fp8-v5, qwen3.8-27b-dflash-drafter-fp8-
+ * b70) without a stated format.  Read here as: OCP 8-bit floating point E4M3
+ * in its finite-only form (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * exponent 0 holds the subnormals; no infinities; codes 0x7F and 0xFF are
+ * NaN; largest magnitude 448), one fp32 scale per output row.  Activations
+ * stay bf16: the taps are bf16 whatever the weights' storage ([card] "Target
+ * quantisation").  Every E4M3 value is a bf16 value, so the products are
+ * exact; sums are fp32 and the row scale multiplies each sum once (each
+ * split-K partial, before the ordered reduction).  Weights must hold no NaN
+ * codes, and scales must be finite.
+ *
+ * dflash_fuse_fc_fp8: the S1 fc.
+ *   taps      HOST array of n_taps device pointers, each [rows, H] bf16
+ *   n_taps    1..BDR_MAX_TAPS; rows >= 0; H > 0 with H % 64 == 0
+ *   fc_q      [H, n_taps*H] uint8 E4M3 codes (out x in), 16-byte aligned
+ *   fc_scale  [H] fp32
+ *   out       [rows, H] bf16 (rounded to nearest even from the fp32 result)
+ *   workspace split-K partial sums; size from dflash_fuse_fc_fp8_workspace_bytes
+ *             (may be NULL when that returns 0)
+ *
+ * dspark_lm_head_fp8: the S2 LM head.
+ *   hidden        [rows, H] bf16; rows >= 0; H > 0 with H % 64 == 0
+ *   lm_head_q     [V, H] uint8 E4M3 codes, 16-byte aligned; 0 < V < 2^31 - 1
+ *   lm_head_scale [V] fp32
+ *   logits        [rows, V] fp32
+ *
+ * Up to 16 rows, and up to 160 rows when H % 256 == 0, the weights are
+ * streamed once; other row counts are processed in slabs of 16 rows, each
+ * streaming the weights again (these entry points serve decode-sized blocks).
+ * ------------------------------------------------------------------------- */
+size_t dflash_fuse_fc_fp8_workspace_bytes(int64_t rows, int64_t hidden, int n_taps);
+int dflash_fuse_fc_fp8(const void* const* taps, int n_taps, int64_t rows,
+                       int64_t hidden, const uint8_t* fc_q, const float* fc_scale,
+                       void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int dspark_lm_head_fp8(const void* hidden, int64_t rows, int64_t hidden_size,
+                       int64_t vocab, const uint8_t* lm_head_q,
+                       const float* lm_head_scale, float* logits, void* stream);
+
+/* ---------------------------------------------------------------------------
  * S3  dspark_markov_argmax -- Markov bigram bias + semi-autoregressive argmax.
  *
  * For each row b: p = prev_token[b]; for i = 0..k-1:

@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 2
+    assert L.bdr_abi_version() == 3
 
 
 def test_workspace_sizes(L):
@@ -106,6 +106,41 @@ def test_lm_head_validation(L):
     assert L.dspark_lm_head(P, 7, 5124, 1000, A.BDR_BF16, P, P, None) == A.BDR_EUNSUPPORTED
     assert L.dspark_lm_head(None, 7, 5120, 1000, A.BDR_BF16, P, P, None) == A.BDR_EINVAL
     assert L.dspark_lm_head(P, 0, 5120, 1000, A.BDR_BF16, P, P, None) == A.BDR_OK
+
+
+def test_fp8_workspace_and_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    taps = (C.c_void_p * 5)(*([4096] * 5))
+    # split-K partials: of all rows (one pass, <= 160 rows) or of one 16-row slab
+    ws = L.dflash_fuse_fc_fp8_workspace_bytes(8, 5120, 5)
+    assert ws > 0 and ws % 256 == 0
+    assert L.dflash_fuse_fc_fp8_workspace_bytes(128, 5120, 5) % 256 == 0
+    assert (L.dflash_fuse_fc_fp8_workspace_bytes(400, 192, 3)
+            == L.dflash_fuse_fc_fp8_workspace_bytes(16, 192, 3))
+    assert L.dflash_fuse_fc_fp8_workspace_bytes(0, 5120, 5) == 0
+    assert L.dflash_fuse_fc_fp8_workspace_bytes(8, 5120, 9) == 0
+    assert L.dflash_fuse_fc_fp8_workspace_bytes(8, 5130, 5) == 0
+    fc = L.dflash_fuse_fc_fp8
+    assert fc(None, 5, 8, 5120, P, P, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 0, 8, 5120, P, P, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 9, 8, 5120, P, P, P, None, 0, None) == A.BDR_EUNSUPPORTED
+    assert fc(taps, 5, 8, 5088, P, P, P, None, 0, None) == A.BDR_EUNSUPPORTED   # H % 64
+    assert fc(taps, 5, -1, 5120, P, P, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 5, 8, 5120, None, P, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 5, 8, 5120, C.c_void_p(4104), P, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 5, 8, 5120, P, None, P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 5, 8, 5120, P, C.c_void_p(4098), P, None, 0, None) == A.BDR_EINVAL
+    assert fc(taps, 5, 8, 5120, P, P, P, None, 0, None) == A.BDR_EWORKSPACE
+    assert fc(taps, 5, 0, 5120, P, P, P, None, 0, None) == A.BDR_OK
+    lm = L.dspark_lm_head_fp8
+    assert lm(P, 7, 5120, 0, P, P, P, None) == A.BDR_EINVAL
+    assert lm(P, 7, 5120, 1 << 31, P, P, P, None) == A.BDR_EUNSUPPORTED
+    assert lm(P, 7, 5100, 1000, P, P, P, None) == A.BDR_EUNSUPPORTED
+    assert lm(None, 7, 5120, 1000, P, P, P, None) == A.BDR_EINVAL
+    assert lm(P, 7, 5120, 1000, P, None, P, None) == A.BDR_EINVAL
+    assert lm(P, 7, 5120, 1000, P, P, None, None) == A.BDR_EINVAL
+    assert lm(P, 0, 5120, 1000, P, P, P, None) == A.BDR_OK
 
 
 def test_markov_validation(L):
