@@ -452,11 +452,12 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
 // Visit width and ring depth by A tiles per wave: one-tile visits (the
 // fewest operand registers), and as deep a ring as LDS holds next to the A
 // staging of 4 * MTW tiles.
+// fp8 tiles are half the bytes: two tiles per visit keep the bytes per visit
+// (and per barrier) of the bf16 kernel and give each wave two independent
+// accumulator chains per visit.
 template <int MTW, bool F8 = false> struct WgShape {
-  static constexpr int VT = 1;
-  // fp8 visits are half the bytes: twice the ring depth keeps as many bytes in flight
-  static constexpr int R = F8 ? (MTW == 1 ? 22 : MTW == 2 ? 18 : 16)
-                              : (MTW == 1 ? 12 : MTW == 2 ? 10 : 9);
+  static constexpr int VT = F8 ? 2 : 1;
+  static constexpr int R = MTW == 1 ? 12 : MTW == 2 ? 10 : 9;
 };
 
 // Launch one instantiation with its dynamic LDS (ring + staging for mt tiles).
