@@ -1,0 +1,74 @@
+"""Averaging a captured layer output over its hyper-connection streams
+(plain CPU definition).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke entry point and the
+CPU-baseline leg of the benchmark, never by the product path.
+
+Source (web page; cited by title and section): "Qwen4Exp DFlash drafter
+support" (wtdcode/vllm-backport PR #128), "What was missing" item 1: the layer
+loop materialises the completed output of each requested layer (its pending
+hyper-connection combine) and averages it over the hc_count streams; that
+average is the feature the drafter's fc consumes.
+
+Readings (the page gives no shapes or precision):
+  * A captured layer output is hc_count streams of [rows, H] in the storage
+    dtype (the combine that completes them belongs to the target model and
+    is an input here).
+  * tap[r, h] = (1/hc) * sum_s stream_s[r, h]: the streams are added in stream
+    order in float64, the sum is divided by hc in float64 (one IEEE rounding),
+    and the quotient is rounded once to the storage dtype, to nearest with
+    ties to even.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+from .reference import f32_to_bf16_bits, widen
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+
+    Goes through float32 rounded to odd: truncate toward zero to float32 and
+    set the last bit when anything was dropped.  float32 keeps 16 more bits than
+    bfloat16, so the odd bit stands for the dropped part and the final round to
+    nearest even is the correctly rounded result (Boldo and Melquiond, "When
+    double rounding is odd", 2005).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16 rounding is defined here for finite values only")
+    rn = x.astype(np.float32)                       # round to nearest
+    back = rn.astype(np.float64)
+    bits = rn.view(np.uint32).astype(np.int64)
+    # one float32 step toward zero where rounding went away from zero
+    away = np.abs(back) > np.abs(x)
+    bits = np.where(away, bits - 1, bits)
+    inexact = back != x
+    bits = np.where(inexact, bits | 1, bits)
+    rz_odd = bits.astype(np.uint32).view(np.float32)
+    return f32_to_bf16_bits(rz_odd)
+
+
+def hc_average(streams: Sequence[np.ndarray], dtype: str) -> np.ndarray:
+    """The tap of one layer: the mean of its hc_count streams, in the storage dtype."""
+    hc = len(streams)
+    if hc < 1:
+        raise ValueError("at least one stream is required")
+    shape = np.shape(streams[0])
+    acc = np.zeros(shape, dtype=np.float64)
+    for s in streams:                               # stream order
+        if np.shape(s) != shape:
+            raise ValueError("all streams must have one shape")
+        v = widen(s, dtype)
+        if not np.all(np.isfinite(v)):
+            raise ValueError("streams must be finite")
+        acc = acc + v
+    mean = acc / np.float64(hc)
+    if dtype == "f32":
+        return mean.astype(np.float32)
+    if dtype == "bf16":
+        return f64_to_bf16_bits(mean)
+    raise ValueError(f"unknown dtype {dtype!r}")
