@@ -225,8 +225,18 @@ def fc_only(args, w, L, bdr, synth, torch, dev):
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
-    taps = [up(synth.store(synth.normal_f32((rows, H), (w.cid, 5, 0, t)), w.dtype))
-            for t in range(T)]
+    hc = args.hc
+    if hc > 1:
+        # captured layer outputs with hc streams, memory [rows, hc, H]; the taps
+        # are their averages (dflash_hc_average), then the fc runs on them
+        cap = [up(synth.store(synth.normal_f32((rows, hc, H), (w.cid, 6, 0, t)), w.dtype))
+               for t in range(T)]
+        taps = [torch.empty((rows, H), dtype=cap[0].dtype, device=dev) for _ in range(T)]
+        cap_arr = (C.c_void_p * T)(*[c.data_ptr() for c in cap])
+        tap_arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    else:
+        taps = [up(synth.store(synth.normal_f32((rows, H), (w.cid, 5, 0, t)), w.dtype))
+                for t in range(T)]
     fc_w = up(synth.store(synth.normal_f32((H, T * H), (w.cid, 0, 0, 0), math.sqrt(1.0 / (T * H))),
                           w.dtype))
     out = torch.empty((rows, H), dtype=fc_w.dtype, device=dev)
@@ -237,19 +247,31 @@ def fc_only(args, w, L, bdr, synth, torch, dev):
     stream = torch.cuda.current_stream(dev)
     sp = C.c_void_p(stream.cuda_stream)
 
+    def average():
+        check(L.dflash_hc_average(cap_arr, T, hc, rows, H, H, hc * H, dt, tap_arr, sp),
+              "dflash_hc_average")
+
     def run():
         check(L.dflash_fuse_fc(arr, T, rows, H, dt, fc_w.data_ptr(), out.data_ptr(), wsp, nws, sp),
               "dflash_fuse_fc")
 
     for _ in range(args.warmup):
+        if hc > 1:
+            average()
         run()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    hevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for a, b in evs:
+    for (a, b), (ha, hb) in zip(evs, hevs):
+        if hc > 1:
+            ha.record(stream)
+            average()
+            hb.record(stream)
         a.record(stream)
         run()
         b.record(stream)
@@ -257,6 +279,15 @@ def fc_only(args, w, L, bdr, synth, torch, dev):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     per = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    hc_info = None
+    if hc > 1:
+        hper = float(np.mean([a.elapsed_time(b) for a, b in hevs]))
+        hbytes = T * rows * H * (hc + 1) * (2 if w.dtype == "bf16" else 4)
+        hgbs = hbytes / (hper * 1e-3) / 1e9
+        log(f"hc average ({hc} streams, {T} taps): {hper * 1e3:.1f} us = {hgbs:.0f} GB/s")
+        hc_info = {"streams": hc, "layout": "[rows, hc, H]", "avg_launch_us": hper * 1e3,
+                   "algorithmic_bytes_per_launch": hbytes, "achieved_GBs": hgbs,
+                   "frac_of_hbm_peak": hgbs / HBM_PEAK_GBS}
     flops = 2.0 * rows * H * T * H
     tflops = flops / (per * 1e-3) / 1e12
     esz = 2 if w.dtype == "bf16" else 4
@@ -267,13 +298,15 @@ def fc_only(args, w, L, bdr, synth, torch, dev):
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"fc {rows} x {T}x{H} -> {H} ({w.name} shape)", "rows": rows,
-                   "hidden": H, "n_taps": T},
+        "config": {"workload": f"fc {rows} x {T}x{H} -> {H} ({w.name} shape)"
+                               + (f", taps averaged over {hc} hc streams" if hc > 1 else ""),
+                   "rows": rows, "hidden": H, "n_taps": T, "hc_streams": hc},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "tiled GEMM (dflash_fuse_fc)", "avg_launch_us": per * 1e3,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes},
+        "hc_average": hc_info,
         "cpu_baseline": None}), flush=True)
 
 
@@ -303,6 +336,9 @@ def main():
     ap.add_argument("--weights", choices=("native", "fp8"), default="native",
                     help="native: fc and LM head weights in the workload's dtype; fp8: E4M3 "
                          "codes with one fp32 scale per row (bf16 workloads)")
+    ap.add_argument("--hc", type=int, default=1,
+                    help="with --fc-rows: average each tap over this many hyper-connection "
+                         "streams (dflash_hc_average) before the fc; both are timed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")

@@ -22,6 +22,7 @@ __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
+    "dflash_hc_average",
     "workspace_bytes", "lib", "BdrError",
 ]
 
@@ -140,6 +141,38 @@ def dspark_lm_head(hidden: torch.Tensor, lm_head_w: torch.Tensor,
                                                   _ptr(lm_head_w), _ptr(logits),
                                                   _stream(hidden.device)))
     return logits
+
+
+# ----------------------------------------------------------------------------- S1 input: hc average
+def dflash_hc_average(captured: Sequence[torch.Tensor],
+                      out: Optional[Sequence[torch.Tensor]] = None):
+    """taps[t][rows, H] = mean over s of captured[t][s, rows, H] (hyper-connection
+    streams).  Each captured tensor is a [hc, rows, H] view with a unit last
+    stride (any stream/row strides, the same for every tap)."""
+    L = lib()
+    T = len(captured)
+    c0 = captured[0]
+    if c0.dim() != 3:
+        raise ValueError("captured tensors must be [hc, rows, H]")
+    hc, rows, H = c0.shape
+    ss, rs, es = c0.stride()
+    for i, c in enumerate(captured):
+        if not c.is_cuda:
+            raise ValueError(f"captured[{i}] must be a device tensor")
+        if c.shape != c0.shape or c.stride() != c0.stride() or c.dtype != c0.dtype:
+            raise ValueError("captured tensors must share shape, strides and dtype")
+    if es != 1:
+        raise ValueError("captured tensors need a unit stride along H")
+    dt = _dt(c0)
+    if out is None:
+        out = [torch.empty((rows, H), dtype=c0.dtype, device=c0.device) for _ in range(T)]
+    for i, o in enumerate(out):
+        _dev(o, f"out[{i}]")
+    src = (C.c_void_p * T)(*[c.data_ptr() for c in captured])
+    dst = (C.c_void_p * T)(*[o.data_ptr() for o in out])
+    _abi.check("dflash_hc_average", L.dflash_hc_average(src, T, hc, rows, H, ss, rs, dt, dst,
+                                                        _stream(c0.device)))
+    return list(out)
 
 
 # ----------------------------------------------------------------------------- S1/S2, fp8 weights

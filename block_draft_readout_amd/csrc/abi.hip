@@ -155,7 +155,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int bdr_abi_version(void) { return 3; }
+int bdr_abi_version(void) { return 4; }
 
 const char* bdr_last_error(void) { return g_err; }
 
@@ -200,6 +200,37 @@ int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size, int64_
   hipError_t e = launch_gemm(p, dt, a, 1, hidden_size, rows, vocab, lm_head_w, logits, OUT_F32,
                              nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_lm_head launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S1 taps: hc average
+int dflash_hc_average(const void* const* captured, int n_taps, int hc, int64_t rows,
+                      int64_t hidden, int64_t stream_stride, int64_t row_stride, bdr_dtype dt,
+                      void* const* taps_out, void* stream) {
+  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+  if (n_taps < 1) return fail(BDR_EINVAL, "n_taps must be >= 1, got %d", n_taps);
+  if (n_taps > BDR_MAX_TAPS) return fail(BDR_EUNSUPPORTED, "n_taps %d > %d", n_taps, BDR_MAX_TAPS);
+  if (hc < 1) return fail(BDR_EINVAL, "hc must be >= 1, got %d", hc);
+  if (hc > BDR_MAX_HC) return fail(BDR_EUNSUPPORTED, "hc %d > %d", hc, BDR_MAX_HC);
+  if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
+  if (hidden <= 0) return fail(BDR_EINVAL, "hidden must be > 0");
+  if (hidden % 8) return fail(BDR_EUNSUPPORTED, "hidden must be a multiple of 8");
+  if (stream_stride < 0 || row_stride < hidden || stream_stride % 8 || row_stride % 8)
+    return fail(BDR_EINVAL, "strides must be multiples of 8 elements, row_stride >= hidden, "
+                "stream_stride >= 0");
+  if (rows > kMaxElems / hidden || rows > kMaxElems / row_stride || hc > kMaxElems / (stream_stride + 1))
+    return fail(BDR_EUNSUPPORTED, "problem too large");
+  if (rows == 0) return BDR_OK;
+  if (!captured || !taps_out) return fail(BDR_EINVAL, "captured and taps_out must not be NULL");
+  for (int t = 0; t < n_taps; ++t) {
+    if (!captured[t] || !taps_out[t]) return fail(BDR_EINVAL, "tap %d pointer is NULL", t);
+    if (!aligned(captured[t], 16) || !aligned(taps_out[t], 16))
+      return fail(BDR_EINVAL, "tap %d pointers must be 16-byte aligned", t);
+  }
+  BDR_TRY(check_device());
+  hipError_t e = launch_hc_average(captured, taps_out, n_taps, hc, rows, hidden, stream_stride,
+                                   row_stride, dt, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dflash_hc_average launch");
   return BDR_OK;
 }
 

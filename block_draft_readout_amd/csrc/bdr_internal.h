@@ -52,6 +52,11 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,
                        OutKind out_kind, void* workspace, hipStream_t stream);
 
+// hyper-connection stream average of each tap: dst[t][r, h] = mean_s src[t][s*ss + r*rs + h]
+hipError_t launch_hc_average(const void* const* src, void* const* dst, int n_taps, int hc,
+                             int64_t rows, int64_t hidden, int64_t stream_stride,
+                             int64_t row_stride, bdr_dtype dt, hipStream_t stream);
+
 // fp8 (E4M3) weights [N, K] with one fp32 scale per row, bf16 A segments
 // (multiples of 64 elements); plan.stream == false means the shape is not
 // supported.

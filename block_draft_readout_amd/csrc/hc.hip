@@ -1,0 +1,129 @@
+// Averaging captured layer outputs over their hyper-connection streams (gfx950).
+//
+// On a target with hyper-connections each drafted layer's completed output is
+// hc_count streams, and the feature the drafter's fc reads is their average
+// ("Qwen4Exp DFlash drafter support", "What was missing" item 1).  One launch
+// averages every tap: grid (chunk, tap), each thread owns 8 consecutive
+// elements of one row, reads them from every stream (16-byte loads for bf16),
+// adds them in stream order in fp64 (exact for bf16 inputs of moderate range),
+// divides once by hc in fp64 (IEEE division; a product by 1/hc, also exact, for
+// a power-of-two hc) and rounds the quotient once to
+// the storage dtype: to bf16 through fp32 rounded to odd, which makes the two
+// roundings equal the single correct one.  The work is a few flops per byte;
+// the launch moves (hc + 1) * rows * H elements per tap at HBM speed.
+
+#include <hip/hip_runtime.h>
+
+#include "bdr_device.h"
+#include "bdr_internal.h"
+
+namespace bdr {
+
+struct HcArgs {
+  const void* src[BDR_MAX_TAPS];   // per tap: element (s, r, h) at src + s*stream_stride + r*row_stride + h
+  void* dst[BDR_MAX_TAPS];         // per tap: [rows, H] contiguous
+  int hc;
+  int64_t rows, hidden;
+  int64_t stream_stride, row_stride;
+};
+
+// fp64 -> fp32 rounded to odd: truncate toward zero, set the last bit if inexact
+__device__ __forceinline__ float f64_to_f32_odd(double q) {
+  const float rn = static_cast<float>(q);
+  const double back = static_cast<double>(rn);
+  uint32_t b = __float_as_uint(rn);
+  if (fabs(back) > fabs(q)) b -= 1u;
+  if (back != q) b |= 1u;
+  return __uint_as_float(b);
+}
+
+template <typename S>
+__global__ __launch_bounds__(256) void hc_average_kernel(const HcArgs g) {
+  const int t = blockIdx.y;
+  const void* src_base = g.src[0];
+  void* dst_base = g.dst[0];
+#pragma unroll
+  for (int c = 1; c < BDR_MAX_TAPS; ++c)
+    if (t == c) {
+      src_base = g.src[c];
+      dst_base = g.dst[c];
+    }
+  const int64_t per_row = g.hidden / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= g.rows * per_row) return;
+  const int64_t r = i / per_row;
+  const int64_t h = (i - r * per_row) * 8;
+  const S* src = static_cast<const S*>(src_base) + r * g.row_stride + h;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int s = 0; s < g.hc; ++s) {
+    const S* p = src + static_cast<int64_t>(s) * g.stream_stride;
+    if constexpr (sizeof(S) == 2) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += static_cast<double>(__uint_as_float(v[e] << 16));
+        acc[2 * e + 1] += static_cast<double>(__uint_as_float(v[e] & 0xFFFF0000u));
+      }
+    } else {
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(p);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += static_cast<double>(v0[e]);
+        acc[4 + e] += static_cast<double>(v1[e]);
+      }
+    }
+  }
+  // a power-of-two count divides exactly as a product (the common case, and
+  // far cheaper than the correctly rounded fp64 division sequence)
+  const double n = static_cast<double>(g.hc);
+  const bool pow2 = (g.hc & (g.hc - 1)) == 0;
+  const double inv = 1.0 / n;
+  auto mean = [&](double a) { return pow2 ? a * inv : a / n; };
+  S* dst = static_cast<S*>(dst_base) + r * g.hidden + h;
+  if constexpr (sizeof(S) == 2) {
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = f32_to_bf16(f64_to_f32_odd(mean(acc[2 * e])));
+      const uint32_t hi = f32_to_bf16(f64_to_f32_odd(mean(acc[2 * e + 1])));
+      o[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(dst) = o;
+  } else {
+    f32x4_t o0, o1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = static_cast<float>(mean(acc[e]));
+      o1[e] = static_cast<float>(mean(acc[4 + e]));
+    }
+    *reinterpret_cast<f32x4_t*>(dst) = o0;
+    *reinterpret_cast<f32x4_t*>(dst + 4) = o1;
+  }
+}
+
+hipError_t launch_hc_average(const void* const* src, void* const* dst, int n_taps, int hc,
+                             int64_t rows, int64_t hidden, int64_t stream_stride,
+                             int64_t row_stride, bdr_dtype dt, hipStream_t stream) {
+  HcArgs g{};
+  for (int t = 0; t < n_taps; ++t) {
+    g.src[t] = src[t];
+    g.dst[t] = dst[t];
+  }
+  g.hc = hc;
+  g.rows = rows;
+  g.hidden = hidden;
+  g.stream_stride = stream_stride;
+  g.row_stride = row_stride;
+  const int64_t blocks = (rows * (hidden / 8) + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(n_taps));
+  if (dt == BDR_BF16)
+    hipLaunchKernelGGL(hc_average_kernel<uint16_t>, grid, dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL(hc_average_kernel<float>, grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace bdr

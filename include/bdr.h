@@ -58,6 +58,7 @@ typedef enum bdr_dtype { BDR_F32 = 0, BDR_BF16 = 1 } bdr_dtype;
 #define BDR_MAX_TAPS   8
 #define BDR_MAX_K      16
 #define BDR_MAX_RANK   128
+#define BDR_MAX_HC     16
 
 /* Version of this interface (incremented on any signature change). */
 int bdr_abi_version(void);
@@ -92,6 +93,32 @@ size_t dflash_fuse_fc_workspace_bytes(int64_t rows, int64_t hidden, int n_taps,
 int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows,
                    int64_t hidden, bdr_dtype dt, const void* fc_w, void* out,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * S1 input  dflash_hc_average -- average each captured layer output over its
+ * hyper-connection streams.
+ *
+ * taps_out[t][r, h] = (1/hc) * sum_{s < hc} captured[t][s*stream_stride + r*row_stride + h]
+ *
+ * On a target with hyper-connections the completed output of each drafted
+ * layer (its pending combine materialised) is hc_count streams, and the
+ * drafter's feature is their average ([pr128] "What was missing" item 1).  The
+ * streams are added in stream order in fp64, the sum is divided by hc in fp64
+ * and the quotient is rounded once to the dtype (bf16: to nearest even, equal
+ * to the correctly rounded mean whenever the fp64 sum is exact).
+ *
+ *   captured      HOST array of n_taps device pointers; element (s, r, h) at
+ *                 the given element strides (e.g. [hc, rows, H]: stream_stride
+ *                 = rows*H, row_stride = H; [rows, hc, H]: H and hc*H)
+ *   n_taps        1..BDR_MAX_TAPS; hc 1..BDR_MAX_HC; rows >= 0
+ *   hidden        H > 0, H % 8 == 0; strides multiples of 8, row_stride >= H
+ *   dt            storage of captured and taps_out (BDR_BF16 or BDR_F32)
+ *   taps_out      HOST array of n_taps device pointers, each [rows, H]
+ *                 contiguous; must not overlap the captured tensors
+ * ------------------------------------------------------------------------- */
+int dflash_hc_average(const void* const* captured, int n_taps, int hc, int64_t rows,
+                      int64_t hidden, int64_t stream_stride, int64_t row_stride,
+                      bdr_dtype dt, void* const* taps_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * S2  dspark_lm_head -- full-vocabulary logits of the drafted positions.

@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 3
+    assert L.bdr_abi_version() == 4
 
 
 def test_workspace_sizes(L):
@@ -141,6 +141,27 @@ def test_fp8_workspace_and_validation(L):
     assert lm(P, 7, 5120, 1000, P, None, P, None) == A.BDR_EINVAL
     assert lm(P, 7, 5120, 1000, P, P, None, None) == A.BDR_EINVAL
     assert lm(P, 0, 5120, 1000, P, P, P, None) == A.BDR_OK
+
+
+def test_hc_average_validation(L):
+    from block_draft_readout_amd import _abi as A
+    src = (C.c_void_p * 5)(*([4096] * 5))
+    dst = (C.c_void_p * 5)(*([8192] * 5))
+    f = L.dflash_hc_average
+    ok = (8 * 5120, 5120)          # [hc, rows, H] strides for rows = 8
+    assert f(src, 5, 4, 8, 5120, *ok, 7, dst, None) == A.BDR_EINVAL                 # dtype
+    assert f(src, 0, 4, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    assert f(src, 9, 4, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EUNSUPPORTED
+    assert f(src, 5, 0, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    assert f(src, 5, 17, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EUNSUPPORTED
+    assert f(src, 5, 4, -1, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    assert f(src, 5, 4, 8, 5124, 8 * 5124, 5124, A.BDR_BF16, dst, None) == A.BDR_EUNSUPPORTED
+    assert f(src, 5, 4, 8, 5120, 8 * 5120, 5112, A.BDR_BF16, dst, None) == A.BDR_EINVAL  # row stride < H
+    assert f(src, 5, 4, 8, 5120, 8 * 5120 + 4, 5120, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    assert f(None, 5, 4, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    bad = (C.c_void_p * 5)(4096, 4096, 4100, 4096, 4096)
+    assert f(bad, 5, 4, 8, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_EINVAL
+    assert f(src, 5, 4, 0, 5120, *ok, A.BDR_BF16, dst, None) == A.BDR_OK
 
 
 def test_markov_validation(L):
