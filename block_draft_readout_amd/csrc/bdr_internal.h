@@ -26,6 +26,7 @@ struct GemmPlan {
   // range (M <= 16) or a four-wave workgroup per range (wg, 16 < M <= 192)
   bool stream = false;
   bool wg = false;
+  bool ns = false;        // row-split workgroup kernel (gemm_ns.h), mt = A row tiles
   int kbb = 1024;         // W bytes per row per visit
   int mtw = 1;            // A row tiles per wave (wg)
   int nt = 1;             // 16-row W tiles per range (compile-time bound)

@@ -416,6 +416,57 @@ static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allo
   return p->nt > 0;
 }
 
+// Row-split workgroup plan (gemm_ns.h; bf16 or fp8 weights, bf16 A, 16 < M <=
+// 160): K blocks of 128 elements that never straddle a tap segment; one
+// workgroup per compute unit and K split, its rows split over four waves, each
+// walking its tiles in passes of ns_tiles(mt).  The K split minimises the
+// per-compute-unit cost W bytes + a quarter of the A bytes staged per pass (+
+// the partial-sum round trip).
+static int ns_tiles(int mt) {      // NsTiles<MT>::NTW
+  return mt <= 3 ? 16 : mt == 4 ? 12 : mt == 5 ? 9 : mt == 6 ? 8 : mt == 7 ? 6 : mt == 8 ? 5
+         : mt == 9 ? 4 : 3;
+}
+
+static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
+                    GemmPlan* p) {
+  constexpr int KE = 128;
+  const int64_t mtiles = (M + 15) / 16;
+  if (esize > 2 || M <= 16 || mtiles > 10 || K % (esize == 1 ? 16 : 8) != 0) return false;
+  if (n_seg > 1 && (K / n_seg) % KE != 0) return false;
+  const int ntw = ns_tiles(static_cast<int>(mtiles));
+  const int64_t kblocks = (K + KE - 1) / KE;
+  double best = 1e300;
+  for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
+    const int64_t kbps = (kblocks + ks - 1) / ks;
+    const int64_t ks_eff = (kblocks + kbps - 1) / kbps;
+    if (ks_eff > kNumCU) continue;
+    int64_t nwg = std::max<int64_t>(1, kNumCU / ks_eff);
+    nwg = std::min<int64_t>(nwg, (N + 63) / 64);
+    const int64_t rows = (N + nwg - 1) / nwg;
+    const int64_t tiles_w = ((rows + 3) / 4 + 15) / 16;
+    const int64_t npass = (tiles_w + ntw - 1) / ntw;
+    double cost = static_cast<double>(kbps) * KE * (esize * rows + 0.5 * M * npass);
+    if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / kNumCU;
+    if (cost < best) {
+      best = cost;
+      p->n_waves = nwg;
+      p->kb_per_split = kbps;
+      p->ksplit = static_cast<int>(ks_eff);
+    }
+  }
+  // a wave's rows x row bytes are addressed with 32-bit offsets
+  const int64_t rows_w = ((N + p->n_waves - 1) / p->n_waves + 3) / 4;
+  if ((rows_w + 16) * K * esize >= (int64_t(1) << 31)) return false;
+  p->stream = true;
+  p->ns = true;
+  p->mt = static_cast<int>(mtiles);
+  p->kblocks = kblocks;
+  p->m_groups = 1;
+  p->n_wg = p->n_waves;
+  p->workspace = p->ksplit > 1 ? align256(static_cast<size_t>(p->ksplit) * M * N * 4) : 0;
+  return true;
+}
+
 // bounds keeping the tiled variant's tile count and indices in 32 bits
 constexpr int64_t kMaxTileRows = int64_t(1) << 22;
 constexpr int64_t kMaxTileCols = int64_t(1) << 22;
@@ -476,6 +527,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
   if (plan_stream(M, N, K, esize, allow_split, n_seg, &p)) return p;
   {
     GemmPlan q;
+    if (plan_ns(M, N, K, esize, allow_split, n_seg, &q)) return q;
+    q = GemmPlan{};
     if (plan_stream_wg(M, N, K, esize, allow_split, n_seg, &q)) return q;
     if (plan_tile(M, N, K, esize, allow_split, n_seg, &q)) return q;
   }
@@ -515,6 +568,8 @@ GemmPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split, int n_
   GemmPlan p;
   if (M > 16) {
     GemmPlan q;
+    if (plan_ns(M, N, K, 1, allow_split, n_seg, &q)) return q;
+    q = GemmPlan{};
     if (plan_stream_wg(M, N, K, 1, allow_split, n_seg, &q)) return q;
   }
   if (!plan_stream(std::min<int64_t>(M, 16), N, K, 1, allow_split, n_seg, &p)) p.stream = false;
@@ -592,6 +647,10 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   if (p.tile) {
     const hipError_t le = launch_gemm_tile(p, g, stream);
     if (le != hipSuccess) return le;
+  } else if (p.ns) {
+    const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
+    const hipError_t le = launch_ns_bf16(p, sa, stream);
+    if (le != hipSuccess) return le;
   } else if (p.wg) {
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
     const bool bf16 = dt == BDR_BF16;
@@ -618,7 +677,7 @@ hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, i
                            int64_t M, int64_t N, const uint8_t* w_q, const float* w_scale,
                            void* out, OutKind out_kind, void* workspace, hipStream_t stream) {
   if (!p.stream) return hipErrorInvalidValue;
-  if (p.wg) {     // all rows in one launch of the workgroup kernel
+  if (p.wg || p.ns) {     // all rows in one launch of a workgroup kernel
     GemmArgs g{};
     for (int t = 0; t < n_seg; ++t) g.a[t] = a[t];
     g.seg = seg;
@@ -632,7 +691,7 @@ hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, i
     g.partial = split ? 1 : 0;
     g.out = split ? workspace : out;
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
-    hipError_t e = launch_wg_fp8(p, sa, stream);
+    hipError_t e = p.ns ? launch_ns_fp8(p, sa, stream) : launch_wg_fp8(p, sa, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess && split) e = launch_splitk_reduce(p, M, N, out, out_kind, workspace, stream);
     return e;

@@ -495,5 +495,8 @@ hipError_t launch_wg_mtw3(const GemmPlan& p, const StreamArgs& sa, bool bf16, hi
 // (gemm_fp8.hip) and the workgroup kernel's fp8 instantiations (gemm_wg_fp8.hip)
 hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t st);
 hipError_t launch_wg_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+// row-split workgroup kernel (gemm_ns.h): bf16 and fp8 weights, bf16 A
+hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 
 }  // namespace bdr

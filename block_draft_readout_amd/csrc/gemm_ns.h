@@ -1,0 +1,326 @@
+// Row-split workgroup GEMM for 16 < M <= 160 (gfx950): C[M, N] = A[M, K] * W[N, K]^T,
+// W in bf16, or in fp8 (E4M3 codes, one fp32 scale per row) against bf16 A.
+//
+// Four waves per workgroup; the workgroup owns a balanced range of W rows and
+// each wave a quarter of it.  Every wave streams its own rows through a
+// private LDS ring with buffer-to-LDS loads (no workgroup barrier per visit,
+// and each fp8 code is widened once), while the A slice of the current K
+// block is shared: staged once per workgroup into LDS (double-buffered, one
+// barrier per K block) and held in every wave's registers for all the A row
+// tiles, so one W visit (16 rows x 128 reduction elements) feeds MT
+// independent accumulator chains.
+//
+//   K block   128 reduction elements: W visit rows of 256 bytes (bf16) or 128
+//             bytes (fp8), A slice rows of 256 bytes (never straddling a tap
+//             segment: segments are multiples of 128 elements);
+//   passes    a wave walks its tiles in passes of at most NTW (accumulator
+//             budget NTW * MT * 4 <= 256); every wave runs the same number of
+//             passes and K blocks, so the barriers match;
+//   order     visits run pass by pass, K block by K block, tile by tile, and
+//             each wave's loads stream on across block and pass boundaries,
+//             kAhead = R - 1 visits ahead (a ring slot is refilled only after
+//             this wave multiplied the visit it held);
+//   A stage   the slice of the next block is copied (each wave a quarter of
+//             the loads) right after the barrier of the current one; the
+//             buffer it overwrites was last read before that barrier.
+//
+// Loads to LDS are not tracked by the compiler, so the waits are explicit and
+// count what this wave issued afterwards (vmcnt retires in issue order):
+//   * before multiplying visit v: vmcnt <= kAhead * NI when the loads of v+1
+//     .. v+kAhead were issued (A loads issued after v only make this stricter),
+//     else vmcnt(0);
+//   * before the barrier of a block: this wave's share of its A slice is
+//     followed by the W loads of the visits it issued since, at least
+//     min(visits of the previous block, kAhead) of them: vmcnt <= NI times that.
+#pragma once
+
+#include "gemm_kernels.h"
+
+namespace bdr {
+
+constexpr int kNsWaves = 4;
+constexpr int kNsKE = 128;             // reduction elements per K block
+
+template <typename S>
+struct NsShape {
+  static constexpr bool F8 = kIsFp8<S>;
+  static constexpr int WROW = F8 ? 128 : 256;       // W bytes per row per visit
+  static constexpr int RPI = 1024 / WROW;           // rows per 1 KB load
+  static constexpr int GROUP = 1024 + 16 * RPI;     // padded LDS bytes per load
+  static constexpr int NI = 16 / RPI;               // loads per visit
+  static constexpr int SLOT = NI * GROUP;           // one visit
+  static constexpr int ASLOT = 4 * (1024 + 64);     // one A tile: 16 rows x 256 B, 4 rows per load
+  static constexpr int WSTEPS = F8 ? 2 : 4;         // 16-byte W reads per row per visit
+};
+
+// ring slots per wave: as many as LDS holds beside two A stagings of MT tiles
+template <typename S, int MT>
+constexpr int ns_ring() { return kIsFp8<S> ? 8 : (MT >= 9 ? 4 : 5); }
+
+// LDS bytes: four rings + two A stagings of MT tiles
+template <typename S, int MT>
+constexpr size_t ns_lds_bytes() {
+  return static_cast<size_t>(kNsWaves * ns_ring<S, MT>() * NsShape<S>::SLOT) +
+         static_cast<size_t>(2 * MT) * NsShape<S>::ASLOT;
+}
+
+// wait until at most NI * c loads are outstanding, c in 0..C
+template <int NI, int C>
+__device__ __forceinline__ void ns_wait(int c) {
+  if constexpr (C > 0) {
+    if (c < C) {
+      ns_wait<NI, C - 1>(c);
+      return;
+    }
+  }
+  BDR_WAIT_VM_LGKM(NI * C, 15);
+}
+
+template <typename S, int MT, int NTW>
+__global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
+  using SH = NsShape<S>;
+  constexpr bool F8 = SH::F8;
+  constexpr int NI = SH::NI;
+  constexpr int R = ns_ring<S, MT>();
+  constexpr int kAhead = R - 1;
+  static_assert(ns_lds_bytes<S, MT>() <= 160 * 1024, "LDS budget");
+  constexpr int NA = MT;                    // A loads per wave per block (4 * MT in all)
+  static_assert(NI * kAhead + NA <= 63, "vmcnt range");
+  const GemmArgs& g = sa.g;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // the workgroup's rows, then this wave's quarter
+  const int64_t g_lo = static_cast<int64_t>(blockIdx.x) * g.N / sa.n_waves;
+  const int64_t g_hi = static_cast<int64_t>(blockIdx.x + 1) * g.N / sa.n_waves;
+  // (row indices fit 31 bits; readfirstlane keeps everything derived from the
+  // wave index in scalar registers, so the load descriptors stay uniform)
+  const int n_lo = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(g_lo + (g_hi - g_lo) * wave / kNsWaves));
+  const int n_hi = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(g_lo + (g_hi - g_lo) * (wave + 1) / kNsWaves));
+  const int ntiles = (n_hi - n_lo + 15) / 16;
+  // passes: the same count on every wave (from the largest quarter); pass p
+  // holds base (+1 for the first rem passes) of this wave's tiles
+  const int max_tiles = static_cast<int>(((g_hi - g_lo + kNsWaves - 1) / kNsWaves + 15) / 16);
+  const int npass = max(1, (max_tiles + NTW - 1) / NTW);
+  const int pbase = ntiles / npass, prem = ntiles - pbase * npass;
+  auto pass_lo = [&](int p) { return p * pbase + min(p, prem); };
+  const uint32_t kb_lo = static_cast<uint32_t>(blockIdx.y * sa.kb_per_split);
+  const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
+  if (g_hi <= g_lo || kb_lo >= kb_hi) return;   // whole workgroup
+  const int nkb = static_cast<int>(kb_hi - kb_lo);
+  const OutRef out(g, blockIdx.y);
+  const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
+  const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
+  const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
+  const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
+  const int mtiles = static_cast<int>((g.M + 15) / 16);
+
+  // this wave's rows (a missing tile of a visit reads zeros)
+  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
+                              static_cast<uint32_t>(n_hi - n_lo) * kbytes);
+  char* const ring = lds + wave * (R * SH::SLOT);
+  char* const stage = lds + kNsWaves * R * SH::SLOT;          // [2][MT][ASLOT]
+  // W load lane mapping: row lane % RPI of the load, 16-byte chunk lane / RPI
+  const uint32_t w_chunk = static_cast<uint32_t>(lane / SH::RPI) * 16;
+  const uint32_t w_row = static_cast<uint32_t>(lane % SH::RPI);
+  // A load lane mapping (4 rows of 256 bytes per load)
+  const uint32_t a_chunk = static_cast<uint32_t>(lane / 4) * 16;
+  const uint32_t a_row = static_cast<uint32_t>(lane % 4);
+  // operand reads: chunk c of row r16 at rd + c * 16 * RPI (W) / rd_a + c * 64 (A)
+  const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * 16);
+  const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 16);
+
+  f32x4_t acc[NTW][MT];
+  auto zero_acc = [&]() {
+    static_for<NTW>([&](auto t) {
+      static_for<MT>([&](auto m) { acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; });
+    });
+  };
+  zero_acc();
+  u32x4_t a[MT][4];
+
+  // W visit (tile t of this wave, block kb) -> ring slot
+  auto dma_w = [&](uint32_t kb, int t, int slot) {
+    const uint32_t k0 = kb * SH::WROW;
+    const uint32_t lo = k0 + w_chunk < kbytes ? w_chunk : kOOB;
+    char* dst = ring + slot * SH::SLOT;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t row = static_cast<uint32_t>(16 * t + j * SH::RPI) + w_row;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16,
+          lo + row * kbytes + k0, 0, 0, 2);
+    }
+  };
+  // this wave's share of the A slice of block kb -> staging buffer b: loads
+  // j = wave, wave + 4, ... of the 4 * MT (tile j / 4, rows 4 * (j % 4) ..)
+  auto dma_a = [&](uint32_t kb, int b) {
+    const uint32_t k0 = kb * (kNsKE * 2);
+    const uint32_t ts = k0 / segbytes;
+    const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
+    const uint32_t lo = k0 + a_chunk < akbytes ? (k0 - ts * segbytes) + a_chunk : kOOB;
+    char* dst = stage + b * (MT * SH::ASLOT);
+    static_for<MT>([&](auto i) {
+      const int j = wave + kNsWaves * i;
+      const int mt = j / 4;
+      if (mt < mtiles) {
+        const uint32_t row = static_cast<uint32_t>(16 * mt + 4 * (j % 4)) + a_row;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(dst + mt * SH::ASLOT + (j % 4) * (1024 + 64)),
+            16, lo + row * segbytes, 0, 0, 0);
+      }
+    });
+  };
+  // A operands of every tile from staging buffer b: bf16 W -> chunk 4s + grp
+  // (elements 32s + 8grp ..); fp8 W -> chunk 8(i/2) + 2grp + i%2 (elements
+  // 64(i/2) + 16grp + 8(i%2) .., the order of the 16 codes a lane reads)
+  auto stage_to_regs = [&](int b) {
+    const char* src = stage + b * (MT * SH::ASLOT) + rd_a;
+    static_for<MT>([&](auto m) {
+      static_for<4>([&](auto i) {
+        const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
+        a[m][i] = (m < mtiles) ? *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + c * 64)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+      });
+    });
+  };
+  // one visit from ring slot `slot` into the accumulators of tile t (compile time)
+  auto compute = [&](auto t, int slot) {
+    const char* src = ring + slot * SH::SLOT + rd;
+    u32x4_t q[SH::WSTEPS];
+    static_for<SH::WSTEPS>([&](auto s) {
+      q[s] = *reinterpret_cast<const u32x4_t*>(src + (4 * s) * 16 * SH::RPI + grp * 16 * SH::RPI);
+    });
+    if constexpr (F8) {
+      static_for<SH::WSTEPS>([&](auto s) {
+        u32x4_t lo, hi;
+        e4m3x16_to_bf16(q[s], lo, hi);
+        static_for<MT>([&](auto m) {
+          acc[t][m] = mma16(a[m][2 * s], lo, acc[t][m], uint16_t());
+          acc[t][m] = mma16(a[m][2 * s + 1], hi, acc[t][m], uint16_t());
+        });
+      });
+    } else {
+      static_for<SH::WSTEPS>([&](auto s) {
+        static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
+      });
+    }
+    // all of the visit's LDS reads ahead of its MFMAs (one latency per visit)
+    __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, SH::WSTEPS * MT * (F8 ? 2 : 1), 0);
+  };
+
+  // visit cursor for the loads: pass ip, block ikb, tile it of the pass
+  int nvis = 0;
+  for (int p = 0; p < npass; ++p) nvis += (pass_lo(p + 1) - pass_lo(p)) * nkb;
+  // (the pass bounds are recomputed only when the cursor changes pass)
+  int iv = 0, ip = 0, it = 0, slot = 0;
+  int ip_lo = 0, ip_n = pass_lo(1);
+  uint32_t ikb = kb_lo;
+  auto issue_next = [&]() {
+    while (ip_n == 0) {      // passes with no tiles on this wave
+      ++ip;
+      ip_lo = pass_lo(ip);
+      ip_n = pass_lo(ip + 1) - ip_lo;
+    }
+    dma_w(ikb, ip_lo + it, slot);
+    ++iv;
+    slot = slot + 1 == R ? 0 : slot + 1;
+    if (++it == ip_n) {
+      it = 0;
+      if (++ikb == kb_hi) {
+        ikb = kb_lo;
+        ++ip;
+        ip_lo = pass_lo(ip);
+        ip_n = pass_lo(ip + 1) - ip_lo;
+      }
+    }
+  };
+
+  dma_a(kb_lo, 0);
+  for (int d = 0; d < kAhead && iv < nvis; ++d) issue_next();
+  int v = 0;                 // visit multiplied next
+  int vslot = 0;             // its ring slot (v % R)
+  int prev_vis = iv;         // visits whose loads followed the current A slice's
+  int blk = 0;
+  for (int p = 0; p < npass; ++p) {
+    const int tp = pass_lo(p);
+    const int ntp = pass_lo(p + 1) - tp;
+    for (uint32_t kb = kb_lo; kb < kb_hi; ++kb, ++blk) {
+      // this block's A slice: own share complete, then everyone's
+      ns_wait<NI, kAhead>(min(prev_vis, kAhead));
+      BDR_WG_BARRIER();
+      stage_to_regs(blk & 1);
+      const bool more = blk + 1 < npass * nkb;
+      if (more) dma_a(kb + 1 < kb_hi ? kb + 1 : kb_lo, (blk + 1) & 1);
+      int issued = 0;
+      static_for<NTW>([&](auto t) {
+        if (t < ntp) {
+          const bool full = v + kAhead < nvis;
+          if (full) {
+            issue_next();
+            ++issued;
+            BDR_WAIT_VM_LGKM(NI * kAhead, 15);
+          } else {
+            BDR_WAIT_VM_LGKM(0, 15);
+          }
+          compute(t, vslot);
+          ++v;
+          vslot = vslot + 1 == R ? 0 : vslot + 1;
+        }
+      });
+      // loads issued after the next A slice: the W loads of this block's visits
+      prev_vis = issued;
+    }
+    // pass p complete: scale (fp8) and store, then clear.  The row base is
+    // opaque so that no part of the store addresses is kept live across the loop.
+    int64_t nbase = static_cast<int64_t>(n_lo) + 16 * tp + r16;
+    asm volatile("" : "+v"(nbase));
+    static_for<NTW>([&](auto t) {
+      const int64_t n = nbase + 16 * t;
+      if (t < ntp && n < n_hi) {
+        float s = 1.f;
+        if constexpr (F8) s = g.w_scale[n];
+        static_for<MT>([&](auto m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = 16 * m + 4 * grp + i;
+            if (row < out.M) out.put(row, n, acc[t][m][i] * s);
+          }
+        });
+      }
+    });
+    zero_acc();
+  }
+}
+
+// accumulator tiles per pass by A tiles: NTW * MT * 4 accumulators next to
+// MT * 16 operand registers (the largest counts that compile without spills)
+template <int MT> struct NsTiles {
+  static constexpr int NTW = MT <= 3 ? 16 : MT == 4 ? 12 : MT == 5 ? 9 : MT == 6 ? 8
+                           : MT == 7 ? 6 : MT == 8 ? 5 : MT == 9 ? 4 : 3;
+};
+
+template <typename S, int MT>
+hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
+  constexpr int NTW = NsTiles<MT>::NTW;
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, NTW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ns_lds_bytes<S, MT>()));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
+  hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, NTW>), grid, dim3(64 * kNsWaves),
+                     (ns_lds_bytes<S, MT>()), st, sa);
+  return hipGetLastError();
+}
+
+}  // namespace bdr
