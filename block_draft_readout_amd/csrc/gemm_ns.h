@@ -125,15 +125,21 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
                               static_cast<uint32_t>(n_hi - n_lo) * kbytes);
   char* const ring = lds + wave * (R * SH::SLOT);
   char* const stage = lds + kNsWaves * R * SH::SLOT;          // [2][MT][ASLOT]
-  // W load lane mapping: row lane % RPI of the load, 16-byte chunk lane / RPI
-  const uint32_t w_chunk = static_cast<uint32_t>(lane / SH::RPI) * 16;
-  const uint32_t w_row = static_cast<uint32_t>(lane % SH::RPI);
-  // A load lane mapping (4 rows of 256 bytes per load)
-  const uint32_t a_chunk = static_cast<uint32_t>(lane / 4) * 16;
-  const uint32_t a_row = static_cast<uint32_t>(lane % 4);
-  // operand reads: chunk c of row r16 at rd + c * 16 * RPI (W) / rd_a + c * 64 (A)
-  const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * 16);
-  const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 16);
+  // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
+  // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
+  // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
+  // (chunk c at position c ^ row-in-load): with the padded groups, the 16
+  // rows a step reads then fall on 16 different bank groups.
+  constexpr int CPR = SH::WROW / 16;
+  const uint32_t w_row = static_cast<uint32_t>(lane / CPR);
+  const uint32_t w_chunk = static_cast<uint32_t>((lane % CPR) ^ (lane / CPR)) * 16;
+  const uint32_t a_row = static_cast<uint32_t>(lane / 16);
+  const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ (lane / 16)) * 16;
+  // operand reads: chunk c of row r16 at rd + ((c ^ rs) * 16) (W) / rd_a + ((c ^ rs_a) * 16) (A)
+  const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
+  const int rs = r16 % SH::RPI;
+  const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
+  const int rs_a = r16 % 4;
 
   f32x4_t acc[NTW][MT];
   auto zero_acc = [&]() {
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
     static_for<MT>([&](auto m) {
       static_for<4>([&](auto i) {
         const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
-        a[m][i] = (m < mtiles) ? *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + c * 64)
+        a[m][i] = (m < mtiles) ? *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + (c ^ rs_a) * 16)
                                : u32x4_t{0u, 0u, 0u, 0u};
       });
     });
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
     const char* src = ring + slot * SH::SLOT + rd;
     u32x4_t q[SH::WSTEPS];
     static_for<SH::WSTEPS>([&](auto s) {
-      q[s] = *reinterpret_cast<const u32x4_t*>(src + (4 * s) * 16 * SH::RPI + grp * 16 * SH::RPI);
+      q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
     });
     if constexpr (F8) {
       static_for<SH::WSTEPS>([&](auto s) {
