@@ -36,8 +36,9 @@ def log(msg):
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "gemm_wg3.hip",
-                "bdr_device.h", "bdr_internal.h")
-GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_kernels.h", "bdr_device.h", "bdr_internal.h")
+                "gemm_ns.h", "gemm_ns_bf16.hip", "bdr_device.h", "bdr_internal.h")
+GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_kernels.h",
+                    "bdr_device.h", "bdr_internal.h")
 
 
 def kernel_source_hash(sources=GEMM_SOURCES) -> str:
