@@ -266,35 +266,28 @@ __global__ __launch_bounds__(64) void ws_gemm_stream_kernel(const StreamArgs sa)
 }
 
 
-// out[i] = sum_p part[p][i] in order p = 0, 1, ...; four outputs per thread,
-// all splits' loads issued before the (ordered) sums.
+// out[i] = sum_p part[p][i] in order p = 0, 1, ...; one output per thread (the
+// partials are a few MB at most: a wide grid keeps enough loads in flight),
+// the loads of up to 16 splits issued before their ordered sums.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int ksplit, int64_t mn, void* out,
                                                             int out_kind) {
   constexpr int PMAX = 16;
-  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i0 >= mn) return;
-  const int n = static_cast<int>(min<int64_t>(4, mn - i0));
-  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float sum = 0.f;
   for (int p0 = 0; p0 < ksplit; p0 += PMAX) {
-    float v[PMAX][4];
+    float v[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) v[p] = p0 + p < ksplit ? part[(p0 + p) * mn + i] : 0.f;
 #pragma unroll
     for (int p = 0; p < PMAX; ++p)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[p][e] = (p0 + p < ksplit && e < n) ? part[(p0 + p) * mn + i0 + e] : 0.f;
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (p0 + p < ksplit) sum[e] += v[p][e];
+      if (p0 + p < ksplit) sum += v[p];
   }
-  for (int e = 0; e < n; ++e) {
-    if (out_kind == OUT_BF16)
-      static_cast<uint16_t*>(out)[i0 + e] = f32_to_bf16(sum[e]);
-    else
-      static_cast<float*>(out)[i0 + e] = sum[e];
-  }
+  if (out_kind == OUT_BF16)
+    static_cast<uint16_t*>(out)[i] = f32_to_bf16(sum);
+  else
+    static_cast<float*>(out)[i] = sum;
 }
 
 // ----------------------------------------------------------------------------
@@ -622,7 +615,7 @@ static void launch_stream(const GemmPlan& p, const GemmArgs& g, hipStream_t st) 
 static hipError_t launch_splitk_reduce(const GemmPlan& p, int64_t M, int64_t N, void* out,
                                        OutKind out_kind, void* workspace, hipStream_t stream) {
   const int64_t mn = M * N;
-  const int64_t blocks = (mn + 1023) / 1024;
+  const int64_t blocks = (mn + 255) / 256;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const float*>(workspace), p.ksplit, mn, out,
                      static_cast<int>(out_kind));
