@@ -8,11 +8,14 @@
 //   * ws_gemm_stream_kernel (M <= 16): one-wave workgroups, each streaming a
 //     balanced range of W rows through LDS with buffer-to-LDS loads while
 //     holding A in registers (this file);
-//   * ws_gemm_stream_wg_kernel (16 < M <= 160): four-wave workgroups sharing
-//     each W visit, A staged once per workgroup (gemm_kernels.h, instantiated
-//     in gemm_wg1/2/3.hip);
-//   * ws_gemm_kernel: a register-only fallback for the shapes the streaming
-//     kernels do not take (tap segments not a multiple of 512 bytes, M > 160);
+//   * ws_gemm_ns_kernel (16 < M <= 160, bf16 or fp8 weights): four-wave
+//     workgroups, each wave streaming its own W rows, the A slice staged once
+//     per workgroup and K block (gemm_ns.h, instantiated in gemm_ns_*.hip);
+//   * ws_gemm_stream_wg_kernel (16 < M <= 160, fp32): four-wave workgroups
+//     sharing each W visit (gemm_kernels.h, instantiated in gemm_wg1/2/3.hip);
+//   * gemm_tile_kernel (bf16, M > 160): LDS-tiled MFMA GEMM (gemm_tile.hip);
+//   * ws_gemm_kernel: a register-only fallback for the shapes the others do
+//     not take (tap segments not a multiple of 128 elements, fp32 M > 160);
 //   * when N alone gives too few workgroups (the fc: N = H), K is split too;
 //     partials are summed in a fixed order by splitk_reduce_kernel, so the
 //     result is deterministic.
@@ -338,42 +341,21 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
   return true;
 }
 
-// Workgroup streaming plan (16 < M <= 160): one workgroup per compute unit
-// and K split (a single round), each walking its row range in passes of at
-// most wg_nt_max tiles (accumulator budget), rounded up to an instantiated
-// tile count.  The K split minimises the per-compute-unit cost W bytes + a
-// quarter of the A bytes re-read per pass (+ the partial-sum round trip).
-static int wg_nt_max(int mtw, bool bf16) {
-  if (!bf16) return 8;
-  return mtw == 1 ? 40 : mtw == 2 ? 20 : 12;
-}
-static int wg_nt_round(int tiles, int mtw, bool bf16) {
-  static const int kSet1[] = {8, 16, 24, 32, 40};
-  static const int kSet2[] = {8, 16, 20};
-  static const int kSet3[] = {8, 12};
-  if (!bf16) return tiles <= 8 ? 8 : 0;
-  if (mtw == 1) {
-    for (int v : kSet1) if (tiles <= v) return v;
-  } else if (mtw == 2) {
-    for (int v : kSet2) if (tiles <= v) return v;
-  } else {
-    for (int v : kSet3) if (tiles <= v) return v;
-  }
-  return 0;
-}
-
+// Shared-visit workgroup plan (fp32, 16 < M <= 160): one workgroup per
+// compute unit and K split (a single round), each walking its row range in
+// passes of at most 8 tiles (accumulator budget).  The K split minimises the
+// per-compute-unit cost W bytes + a quarter of the A bytes re-read per pass
+// (+ the partial-sum round trip).
 static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allow_split,
                            int n_seg, GemmPlan* p) {
   const int64_t kbytes = K * esize;
   const int64_t segbytes = kbytes / n_seg;
   const int64_t mtiles = (M + 15) / 16;
-  if (M <= 16 || mtiles > kWgMaxTiles || kbytes % 64 != 0) return false;
+  if (esize != 4 || M <= 16 || mtiles > kWgMaxTiles || kbytes % 64 != 0) return false;
   const int mtw = static_cast<int>((mtiles + kWgWaves - 1) / kWgWaves);
-  // fp8 weights (esize 1): K blocks of 256 elements (256 bytes of codes per row)
-  const int kbb = esize == 1 ? 256 : kWgKBB;
+  const int kbb = kWgKBB;
   if (n_seg > 1 && segbytes % kbb != 0) return false;
-  const bool bf16 = esize <= 2;      // accumulator budget as for bf16
-  const int ntmax = wg_nt_max(mtw, bf16);
+  const int ntmax = 8;
   const int64_t kblocks = (kbytes + kbb - 1) / kbb;
   double best = 1e300;
   int64_t best_tiles = 0;
@@ -401,7 +383,7 @@ static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allo
   p->kbb = kbb;
   p->mtw = mtw;
   p->kblocks = kblocks;
-  p->nt = wg_nt_round(static_cast<int>(best_tiles), mtw, bf16);
+  p->nt = best_tiles <= 8 ? 8 : 0;
   p->mt = static_cast<int>(mtiles);
   p->m_groups = 1;
   p->n_wg = p->n_waves;
@@ -562,8 +544,6 @@ GemmPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split, int n_
   if (M > 16) {
     GemmPlan q;
     if (plan_ns(M, N, K, 1, allow_split, n_seg, &q)) return q;
-    q = GemmPlan{};
-    if (plan_stream_wg(M, N, K, 1, allow_split, n_seg, &q)) return q;
   }
   if (!plan_stream(std::min<int64_t>(M, 16), N, K, 1, allow_split, n_seg, &p)) p.stream = false;
   return p;
@@ -646,10 +626,9 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
     if (le != hipSuccess) return le;
   } else if (p.wg) {
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
-    const bool bf16 = dt == BDR_BF16;
-    const hipError_t le = p.mtw == 1   ? launch_wg_mtw1(p, sa, bf16, stream)
-                          : p.mtw == 2 ? launch_wg_mtw2(p, sa, bf16, stream)
-                                       : launch_wg_mtw3(p, sa, bf16, stream);
+    const hipError_t le = p.mtw == 1   ? launch_wg_mtw1(p, sa, stream)
+                          : p.mtw == 2 ? launch_wg_mtw2(p, sa, stream)
+                                       : launch_wg_mtw3(p, sa, stream);
     if (le != hipSuccess) return le;
   } else if (p.stream) {
     if (dt == BDR_BF16)
@@ -670,7 +649,7 @@ hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, i
                            int64_t M, int64_t N, const uint8_t* w_q, const float* w_scale,
                            void* out, OutKind out_kind, void* workspace, hipStream_t stream) {
   if (!p.stream) return hipErrorInvalidValue;
-  if (p.wg || p.ns) {     // all rows in one launch of a workgroup kernel
+  if (p.ns) {     // all rows in one launch of the row-split kernel
     GemmArgs g{};
     for (int t = 0; t < n_seg; ++t) g.a[t] = a[t];
     g.seg = seg;
@@ -684,7 +663,7 @@ hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, i
     g.partial = split ? 1 : 0;
     g.out = split ? workspace : out;
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
-    hipError_t e = p.ns ? launch_ns_fp8(p, sa, stream) : launch_wg_fp8(p, sa, stream);
+    hipError_t e = launch_ns_fp8(p, sa, stream);
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess && split) e = launch_splitk_reduce(p, M, N, out, out_kind, workspace, stream);
     return e;

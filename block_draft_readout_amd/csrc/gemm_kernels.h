@@ -78,7 +78,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // ----------------------------------------------------------------------------
-// Streaming variant for 16 < M <= 160 (2..10 tiles of A rows).
+// Shared-visit streaming variant for 16 < M <= 160 with fp32 operands (bf16
+// and fp8 weights take the row-split kernel of gemm_ns.h).
 //
 // A workgroup of four waves owns a balanced contiguous range of W rows, walked
 // in passes of at most NT 16-row tiles (the accumulators of one pass live in
@@ -162,17 +163,13 @@ __device__ __forceinline__ void wait_vm_visit(int n) {
   BDR_WAIT_VM_LGKM(BASE + PER * N, 0);
 }
 
-// fp8 weights: S = uint8_t means E4M3 codes with one fp32 scale per W row and
-// bf16 A.  A K block is then 256 elements: a W visit row holds 256 codes (256
-// bytes) and the A slice is the same 512 bytes per row as for bf16.
+// fp8 weights (row-split kernel): S = uint8_t means E4M3 codes with one fp32
+// scale per W row against bf16 A
 template <typename S> constexpr bool kIsFp8 = std::is_same_v<S, uint8_t>;
-template <typename S> constexpr int kWgKbbW = kIsFp8<S> ? 256 : kWgKBB;   // W bytes per row per visit
-template <typename S> constexpr int kAElem = kIsFp8<S> ? 2 : static_cast<int>(sizeof(S));
 
 // LDS bytes of the workgroup kernel: R visits of VT tiles + one staging tile per A tile
-inline size_t wg_lds_bytes(int ring, int vt, int mtiles, int kbb_w = kWgKBB) {
-  const size_t wslot = kbb_w == 256 ? VisitShape<256>::SLOT : VisitShape<kWgKBB>::SLOT;
-  return static_cast<size_t>(ring * vt) * wslot + static_cast<size_t>(mtiles) * VisitShape<kWgKBB>::SLOT;
+inline size_t wg_lds_bytes(int ring, int vt, int mtiles) {
+  return static_cast<size_t>(ring * vt + mtiles) * VisitShape<kWgKBB>::SLOT;
 }
 
 // 16 E4M3 codes (little-endian bytes of q) -> bf16 operands of elements 0..7 (lo)
@@ -190,10 +187,9 @@ __device__ __forceinline__ void e4m3x16_to_bf16(u32x4_t q, u32x4_t& lo, u32x4_t&
 
 template <typename S, int MTW, int NT, int VT, int R>
 __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs sa) {
-  constexpr bool F8 = kIsFp8<S>;
-  constexpr int KBB = kWgKbbW<S>;        // W bytes per row per visit
+  constexpr int KBB = kWgKBB;            // bytes per row per visit (W and A)
   using VS = VisitShape<KBB>;            // W visit geometry
-  using VA = VisitShape<kWgKBB>;         // A staging geometry (512 bytes per row)
+  using VA = VS;                         // A staging geometry
   constexpr int STEPS = VA::STEPS;       // 16-byte A operands per row and block
   constexpr int NI = VT * VS::NI;        // W loads per wave per visit
   constexpr int NA = MTW * VA::NIA;      // A loads per wave per K block
@@ -222,8 +218,8 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   const int nkb = static_cast<int>(kb_hi - kb_lo);
   const OutRef out(g, blockIdx.y);
   const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
-  const uint32_t akbytes = static_cast<uint32_t>(g.K * kAElem<S>);      // A row bytes
-  const uint32_t segbytes = static_cast<uint32_t>(g.seg * kAElem<S>);
+  const uint32_t akbytes = kbytes;                                      // A row bytes
+  const uint32_t segbytes = static_cast<uint32_t>(g.seg * static_cast<int64_t>(sizeof(S)));
   const int mtiles = static_cast<int>((g.M + 15) / 16);
 
   // rows past the range (also those of a last visit's missing tile) read zeros
@@ -292,17 +288,14 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
       }
     });
   };
-  // A operand i of row r16: bf16/fp32 W -> chunk 4i + grp (elements of MFMA
-  // step i); fp8 W -> chunk 8(i/2) + 2grp + i%2, i.e. elements 64(i/2) + 16grp
-  // + 8(i%2) + [0, 8), matching the 16 codes a lane reads per 64-element step
+  // A operand i of row r16: chunk 4i + grp (elements of MFMA step i)
   auto stage_to_regs = [&]() {
     static_for<MTW>([&](auto mw) {
       const int mt = wave + kWgWaves * mw;
       if (mt < mtiles) {
         const char* src = stage + mt * VA::SLOT + rd_a;
         static_for<STEPS>([&](auto st) {
-          const int c = F8 ? 8 * (st / 2) + 2 * grp + st % 2 : 4 * st + grp;
-          a[mw][st] = *reinterpret_cast<const u32x4_t*>(src + c * 16 * VA::RPI);
+          a[mw][st] = *reinterpret_cast<const u32x4_t*>(src + (4 * st + grp) * 16 * VA::RPI);
         });
       }
     });
@@ -310,29 +303,7 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
   // all VT tiles of visit vt (compile-time) of the current pass, from a ring slot
   auto compute = [&](auto vt, int slot) {
     const char* src = lds + slot * VSLOT + rd;
-    if constexpr (F8) {
-      // per 64-element step: 16 codes of row r16 -> two bf16 operands
-      constexpr int WS = VS::STEPS;
-      u32x4_t q[VT][WS];
-      static_for<VT>([&](auto u) {
-        static_for<WS>([&](auto st) {
-          q[u][st] = *reinterpret_cast<const u32x4_t*>(src + u * VS::SLOT + st * 64 * VS::RPI);
-        });
-      });
-      static_for<VT>([&](auto u) {
-        constexpr int t = VT * decltype(vt)::value + decltype(u)::value;
-        static_for<WS>([&](auto st) {
-          u32x4_t lo, hi;
-          e4m3x16_to_bf16(q[u][st], lo, hi);
-          static_for<MTW>([&](auto mw) {
-            acc[t][mw] = mma16(a[mw][2 * st], lo, acc[t][mw], uint16_t());
-            acc[t][mw] = mma16(a[mw][2 * st + 1], hi, acc[t][mw], uint16_t());
-          });
-        });
-      });
-      __builtin_amdgcn_sched_group_barrier(0x100, VT * WS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, VT * WS * MTW * 2, 0);
-    } else {
+    {
       u32x4_t bv[VT][STEPS];
       static_for<VT>([&](auto u) {
         static_for<STEPS>([&](auto st) {
@@ -431,12 +402,7 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t m = 16 * mt + 4 * grp + i;
-          if (t < ntp && m < out.M && n < n_hi) {
-            if constexpr (F8)
-              out.put(m, n, acc[t][mw][i] * g.w_scale[n]);
-            else
-              out.put(m, n, acc[t][mw][i]);
-          }
+          if (t < ntp && m < out.M && n < n_hi) out.put(m, n, acc[t][mw][i]);
         }
       });
     });
@@ -451,35 +417,32 @@ __global__ __launch_bounds__(256) void ws_gemm_stream_wg_kernel(const StreamArgs
 
 // Visit width and ring depth by A tiles per wave.  Two tiles per visit halve
 // the barriers per byte and give each wave twice the independent accumulator
-// chains per visit (bf16 with one or two A tiles per wave: 4-5 % faster on the
-// LM head than one-tile visits; fp8 tiles are half the bytes, so two of them
-// make the bf16 kernel's bytes per visit).  With three A tiles per wave the A
-// staging leaves room for too shallow a ring of two-tile visits, so visits
-// keep one tile there.  The ring is as deep as LDS holds next to the staging
-// of 4 * MTW tiles.
-template <int MTW, bool F8 = false> struct WgShape {
-  static constexpr int VT = F8 || MTW < 3 ? 2 : 1;
-  static constexpr int R = F8 ? (MTW == 1 ? 12 : MTW == 2 ? 10 : 9) : (MTW == 1 ? 6 : MTW == 2 ? 5 : 9);
+// chains per visit (4-5 % faster on a bf16 LM head than one-tile visits when
+// this kernel served bf16).  With three A tiles per wave the A staging leaves
+// room for too shallow a ring of two-tile visits, so visits keep one tile
+// there.  The ring is as deep as LDS holds next to the staging of 4 * MTW tiles.
+template <int MTW> struct WgShape {
+  static constexpr int VT = MTW < 3 ? 2 : 1;
+  static constexpr int R = MTW == 1 ? 6 : MTW == 2 ? 5 : 9;
 };
 
 // Launch one instantiation with its dynamic LDS (ring + staging for mt tiles).
 template <typename S, int MTW, int NT>
 hipError_t launch_wg_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  constexpr int VT = WgShape<MTW, kIsFp8<S>>::VT;
-  constexpr int R = WgShape<MTW, kIsFp8<S>>::R;
-  constexpr int KW = kWgKbbW<S>;
+  constexpr int VT = WgShape<MTW>::VT;
+  constexpr int R = WgShape<MTW>::R;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&ws_gemm_stream_wg_kernel<S, MTW, NT, VT, R>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        static_cast<int>(wg_lds_bytes(R, VT, std::min(kWgWaves * MTW, kWgMaxTiles), KW)));
+        static_cast<int>(wg_lds_bytes(R, VT, std::min(kWgWaves * MTW, kWgMaxTiles))));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
   hipLaunchKernelGGL((ws_gemm_stream_wg_kernel<S, MTW, NT, VT, R>), grid, dim3(64 * kWgWaves),
-                     wg_lds_bytes(R, VT, p.mt, KW), st, sa);
+                     wg_lds_bytes(R, VT, p.mt), st, sa);
   return hipSuccess;
 }
 
@@ -488,13 +451,12 @@ hipError_t launch_wg_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
 // each returns hipErrorInvalidValue for a tile count it does not instantiate.
 hipError_t launch_gemm_tile(const GemmPlan& p, const GemmArgs& g, hipStream_t stream);
 int tile_cols(int shape);   // output columns of a tiled-variant workgroup tile
-hipError_t launch_wg_mtw1(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
-hipError_t launch_wg_mtw2(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
-hipError_t launch_wg_mtw3(const GemmPlan& p, const StreamArgs& sa, bool bf16, hipStream_t st);
+hipError_t launch_wg_mtw1(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_wg_mtw2(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_wg_mtw3(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 // fp8 (E4M3) weights with per-row scales, bf16 A: one-wave streaming kernel
-// (gemm_fp8.hip) and the workgroup kernel's fp8 instantiations (gemm_wg_fp8.hip)
+// (gemm_fp8.hip)
 hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t st);
-hipError_t launch_wg_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 // row-split workgroup kernel (gemm_ns.h): bf16 and fp8 weights, bf16 A
 hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);

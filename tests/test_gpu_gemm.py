@@ -1,8 +1,9 @@
 """GPU parity of the weight-streaming GEMM (drafter fc and LM head) across the
-shapes that select each kernel variant: one to three A row tiles per wave of
-the four-wave streaming kernel, tap segments, ragged M / N / K, split K, the
-fp32 path, and the fallbacks just outside those shapes.  Compared with the
-oracle's float64 products."""
+shapes that select each kernel variant: the row-split workgroup kernel for
+bf16 with 2 to 10 A row tiles (tap segments, ranges walked in several passes,
+ragged M / N / K, split K), the shared-visit kernel for fp32, the tiled kernel
+above 160 rows, and the fallbacks just outside those shapes.  Compared with
+the oracle's float64 products."""
 import dataclasses
 
 import pytest
