@@ -53,14 +53,35 @@ struct NsShape {
   static constexpr int WSTEPS = F8 ? 2 : 4;         // 16-byte W reads per row per visit
 };
 
-// ring slots per wave: as many as LDS holds beside two A stagings of MT tiles
+// accumulator tiles per pass by A tiles: NTW * MT * 4 accumulators next to
+// MT * 16 operand registers (the largest counts that compile without spills)
+template <int MT> struct NsTiles {
+  static constexpr int NTW = MT <= 3 ? 16 : MT == 4 ? 12 : MT == 5 ? 9 : MT == 6 ? 8
+                           : MT == 7 ? 6 : MT == 8 ? 5 : MT == 9 ? 4 : 3;
+};
+
+// tiles per visit: one visit carries VT 16-row tiles (one load batch, one
+// wait).  Two fp8 tiles per visit measured ~7 % faster with 2..3 A tiles (the
+// codes of one tile are few bytes per visit); with more A tiles, and for
+// bf16, one tile per visit is faster.
 template <typename S, int MT>
-constexpr int ns_ring() { return kIsFp8<S> ? 8 : (MT >= 9 ? 4 : 5); }
+constexpr int ns_vt() { return kIsFp8<S> && MT <= 3 ? 2 : 1; }
+
+// ring slots per wave (of VT tiles each): as many as LDS holds beside two A
+// stagings of MT tiles, and as vmcnt can count (NI * VT * (R - 1) + MT <= 63)
+template <typename S, int MT>
+constexpr int ns_ring() {
+  constexpr int vt = ns_vt<S, MT>();
+  constexpr int fit = (160 * 1024 - 2 * MT * NsShape<S>::ASLOT) / (kNsWaves * vt * NsShape<S>::SLOT);
+  constexpr int cnt = (63 - MT) / (NsShape<S>::NI * vt) + 1;
+  constexpr int r = fit < cnt ? fit : cnt;
+  return r > 16 ? 16 : r;
+}
 
 // LDS bytes: four rings + two A stagings of MT tiles
 template <typename S, int MT>
 constexpr size_t ns_lds_bytes() {
-  return static_cast<size_t>(kNsWaves * ns_ring<S, MT>() * NsShape<S>::SLOT) +
+  return static_cast<size_t>(kNsWaves * ns_ring<S, MT>() * ns_vt<S, MT>() * NsShape<S>::SLOT) +
          static_cast<size_t>(2 * MT) * NsShape<S>::ASLOT;
 }
 
@@ -80,7 +101,10 @@ template <typename S, int MT, int NTW>
 __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   using SH = NsShape<S>;
   constexpr bool F8 = SH::F8;
-  constexpr int NI = SH::NI;
+  constexpr int VT = ns_vt<S, MT>();
+  static_assert(NTW % VT == 0, "whole visits per pass");
+  constexpr int NI = SH::NI * VT;            // loads per visit
+  constexpr int SLOTV = VT * SH::SLOT;       // one visit in the ring
   constexpr int R = ns_ring<S, MT>();
   constexpr int kAhead = R - 1;
   static_assert(ns_lds_bytes<S, MT>() <= 160 * 1024, "LDS budget");
@@ -123,8 +147,8 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   // this wave's rows (a missing tile of a visit reads zeros)
   const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
                               static_cast<uint32_t>(n_hi - n_lo) * kbytes);
-  char* const ring = lds + wave * (R * SH::SLOT);
-  char* const stage = lds + kNsWaves * R * SH::SLOT;          // [2][MT][ASLOT]
+  char* const ring = lds + wave * (R * SLOTV);
+  char* const stage = lds + kNsWaves * R * SLOTV;             // [2][MT][ASLOT]
   // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
   // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
   // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
@@ -150,17 +174,23 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   zero_acc();
   u32x4_t a[MT][4];
 
-  // W visit (tile t of this wave, block kb) -> ring slot
-  auto dma_w = [&](uint32_t kb, int t, int slot) {
+  // W visit (tiles t .. t+VT-1 of this wave, block kb) -> ring slot; a tile at
+  // or past `t_end` (the end of the pass) is not read (out-of-range loads,
+  // still counted by vmcnt)
+  auto dma_w = [&](uint32_t kb, int t, int t_end, int slot) {
     const uint32_t k0 = kb * SH::WROW;
     const uint32_t lo = k0 + w_chunk < kbytes ? w_chunk : kOOB;
-    char* dst = ring + slot * SH::SLOT;
+    char* dst = ring + slot * SLOTV;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint32_t row = static_cast<uint32_t>(16 * t + j * SH::RPI) + w_row;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16,
-          lo + row * kbytes + k0, 0, 0, 2);
+    for (int u = 0; u < VT; ++u) {
+      const uint32_t lou = t + u < t_end ? lo : kOOB;
+#pragma unroll
+      for (int j = 0; j < SH::NI; ++j) {
+        const uint32_t row = static_cast<uint32_t>(16 * (t + u) + j * SH::RPI) + w_row;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void*)(dst + u * SH::SLOT + j * SH::GROUP), 16,
+            lou + row * kbytes + k0, 0, 0, 2);
+      }
     }
   };
   // this wave's share of the A slice of block kb -> staging buffer b: loads
@@ -195,9 +225,9 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
       });
     });
   };
-  // one visit from ring slot `slot` into the accumulators of tile t (compile time)
-  auto compute = [&](auto t, int slot) {
-    const char* src = ring + slot * SH::SLOT + rd;
+  // one tile of a visit (ring slot `slot`, tile u) into the accumulators of tile t
+  auto compute = [&](auto t, int slot, int u) {
+    const char* src = ring + slot * SLOTV + u * SH::SLOT + rd;
     u32x4_t q[SH::WSTEPS];
     static_for<SH::WSTEPS>([&](auto s) {
       q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
@@ -216,14 +246,11 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
         static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
       });
     }
-    // all of the visit's LDS reads ahead of its MFMAs (one latency per visit)
-    __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, SH::WSTEPS * MT * (F8 ? 2 : 1), 0);
   };
 
   // visit cursor for the loads: pass ip, block ikb, tile it of the pass
   int nvis = 0;
-  for (int p = 0; p < npass; ++p) nvis += (pass_lo(p + 1) - pass_lo(p)) * nkb;
+  for (int p = 0; p < npass; ++p) nvis += (pass_lo(p + 1) - pass_lo(p) + VT - 1) / VT * nkb;
   // (the pass bounds are recomputed only when the cursor changes pass)
   int iv = 0, ip = 0, it = 0, slot = 0;
   int ip_lo = 0, ip_n = pass_lo(1);
@@ -234,10 +261,11 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
       ip_lo = pass_lo(ip);
       ip_n = pass_lo(ip + 1) - ip_lo;
     }
-    dma_w(ikb, ip_lo + it, slot);
+    dma_w(ikb, ip_lo + it, ip_lo + ip_n, slot);
     ++iv;
     slot = slot + 1 == R ? 0 : slot + 1;
-    if (++it == ip_n) {
+    it += VT;
+    if (it >= ip_n) {
       it = 0;
       if (++ikb == kb_hi) {
         ikb = kb_lo;
@@ -265,8 +293,8 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
       const bool more = blk + 1 < npass * nkb;
       if (more) dma_a(kb + 1 < kb_hi ? kb + 1 : kb_lo, (blk + 1) & 1);
       int issued = 0;
-      static_for<NTW>([&](auto t) {
-        if (t < ntp) {
+      static_for<NTW / VT>([&](auto vt) {
+        if (VT * vt < ntp) {
           const bool full = v + kAhead < nvis;
           if (full) {
             issue_next();
@@ -275,7 +303,13 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
           } else {
             BDR_WAIT_VM_LGKM(0, 15);
           }
-          compute(t, vslot);
+          static_for<VT>([&](auto u) {
+            compute(std::integral_constant<int, VT * decltype(vt)::value + decltype(u)::value>{},
+                    vslot, u);
+          });
+          // all of the visit's LDS reads ahead of its MFMAs (one latency per visit)
+          __builtin_amdgcn_sched_group_barrier(0x100, VT * SH::WSTEPS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, VT * SH::WSTEPS * MT * (F8 ? 2 : 1), 0);
           ++v;
           vslot = vslot + 1 == R ? 0 : vslot + 1;
         }
@@ -304,13 +338,6 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
     zero_acc();
   }
 }
-
-// accumulator tiles per pass by A tiles: NTW * MT * 4 accumulators next to
-// MT * 16 operand registers (the largest counts that compile without spills)
-template <int MT> struct NsTiles {
-  static constexpr int NTW = MT <= 3 ? 16 : MT == 4 ? 12 : MT == 5 ? 9 : MT == 6 ? 8
-                           : MT == 7 ? 6 : MT == 8 ? 5 : MT == 9 ? 4 : 3;
-};
 
 template <typename S, int MT>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
