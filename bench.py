@@ -157,6 +157,12 @@ class Step:
 
     def fc_rows(self):
         w, b = self.w, self.b
+        if self.fp8:
+            return self.L.dflash_fuse_fc_rows_fp8(
+                self.taps, w.n_taps, w.rows, w.hidden, b["row_index"].data_ptr(),
+                b["row_count"].data_ptr(), w.rows, self.g["fc_q"].data_ptr(),
+                self.g["fc_scale"].data_ptr(), b["F"].data_ptr(), b["ws_fcr"], b["ws_fcr_n"],
+                self.stream)
         return self.L.dflash_fuse_fc_rows(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
                                           b["row_index"].data_ptr(), b["row_count"].data_ptr(),
                                           w.rows, self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
@@ -188,9 +194,14 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None, fp8=
         if fp8:
             ofp8.fuse_fc_fp8(slot_host["taps"], W["fc_q"], W["fc_scale"], w.dtype)
             Z = ofp8.lm_head_fp8(slot_host["draft_hidden"], W["lm_q"], W["lm_scale"], w.dtype)
-            d, _ = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], slot_host["prev0"], w.dtype)
-            Lb = oracle.truncate_by_confidence(slot_host["conf"], w.threshold, w.batch, w.k)
-            oracle.verify_greedy(d, oracle.target_argmax(slot_host["Y"], w.dtype, Lb), Lb)
+            if sample is None:
+                d, _ = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], slot_host["prev0"], w.dtype)
+                Lb = oracle.truncate_by_confidence(slot_host["conf"], w.threshold, w.batch, w.k)
+                oracle.verify_greedy(d, oracle.target_argmax(slot_host["Y"], w.dtype, Lb), Lb)
+            else:
+                sampling.block_step_sample(w.dtype, Z, W["w1"], W["w2"], slot_host["prev0"],
+                                           slot_host["Y"], sample[0], sample[1],
+                                           confidence=slot_host["conf"], threshold=w.threshold)
         elif sample is None:
             oracle.block_step(w.dtype, slot_host["taps"], W["fc_w"], slot_host["draft_hidden"],
                               W["lm_w"], W["w1"], W["w2"], slot_host["prev0"],
@@ -349,8 +360,8 @@ def main():
         print(json.dumps({"error": "--closed-loop runs eagerly (no --graph)"}))
         sys.exit(2)
     fp8 = args.weights == "fp8"
-    if fp8 and (args.closed_loop or args.draft != "greedy" or args.fc_rows > 0):
-        print(json.dumps({"error": "--weights fp8 times greedy independent block-steps only"}))
+    if fp8 and args.fc_rows > 0:
+        print(json.dumps({"error": "--weights fp8 times block-steps (not --fc-rows)"}))
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -420,7 +431,8 @@ def main():
                    ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
                    ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
                    ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0),
-                   ("ws_fcr", L.dflash_fuse_fc_rows_workspace_bytes(w.rows, H, w.n_taps, dt)
+                   ("ws_fcr", (L.dflash_fuse_fc_rows_fp8_workspace_bytes(w.rows, H, w.n_taps) if fp8
+                               else L.dflash_fuse_fc_rows_workspace_bytes(w.rows, H, w.n_taps, dt))
                     if args.closed_loop else 0)):
         p, n2, t = ws(n)
         bufs[key], bufs[key + "_n"] = p, n2

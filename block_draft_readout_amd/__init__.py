@@ -22,7 +22,7 @@ __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
-    "dflash_hc_average",
+    "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
     "workspace_bytes", "lib", "BdrError",
 ]
 
@@ -517,3 +517,34 @@ def dflash_fuse_fc_rows(taps: Sequence[torch.Tensor], fc_w: torch.Tensor, row_in
                L.dflash_fuse_fc_rows(arr, T, rows, H, dt, _ptr(row_index), _ptr(row_count), max_rows,
                                      _ptr(fc_w), _ptr(out), wp, wn, _stream(fc_w.device)))
     return out
+
+
+def dflash_fuse_fc_rows_fp8(taps: Sequence[torch.Tensor], fc_q: torch.Tensor, fc_scale: torch.Tensor,
+                            row_index: torch.Tensor, row_count: torch.Tensor,
+                            max_rows: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dflash_fuse_fc_rows with fp8 weights (E4M3 fc_q [H, T*H] + fp32 fc_scale [H]); bf16 taps/out."""
+    L = lib()
+    T = len(taps)
+    rows, H = taps[0].shape
+    for i, t in enumerate(taps):
+        _dev(t, f"taps[{i}]")
+        if t.shape != (rows, H) or t.dtype != torch.bfloat16:
+            raise ValueError("taps must all be bf16 [rows, H]")
+    _fp8_weight(fc_q, fc_scale, "fc_q", "fc_scale")
+    _dev(row_index, "row_index")
+    _dev(row_count, "row_count")
+    if max_rows is None:
+        max_rows = row_index.numel()
+    if out is None:
+        out = torch.empty((max_rows, H), dtype=torch.bfloat16, device=fc_q.device)
+    _dev(out, "out")
+    ws = _workspace(L.dflash_fuse_fc_rows_fp8_workspace_bytes(max_rows, H, T), fc_q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    _abi.check("dflash_fuse_fc_rows_fp8",
+               L.dflash_fuse_fc_rows_fp8(arr, T, rows, H, _ptr(row_index), _ptr(row_count), max_rows,
+                                         _ptr(fc_q), _ptr(fc_scale), _ptr(out), wp, wn,
+                                         _stream(fc_q.device)))
+    return out
+

@@ -36,6 +36,9 @@ SIGNATURES = {
     "dflash_hc_average": (_int, [C.POINTER(_vp), _int, _int, _i64, _i64, _i64, _i64, _int,
                                  C.POINTER(_vp), _vp]),
     "dflash_fuse_fc_fp8_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "dflash_fuse_fc_rows_fp8_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "dflash_fuse_fc_rows_fp8": (_int, [C.POINTER(_vp), _int, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
+                                       _vp, _vp, _sz, _vp]),
     "dflash_fuse_fc_fp8": (_int, [C.POINTER(_vp), _int, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_lm_head_fp8": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "dspark_markov_workspace_bytes": (_sz, [_i64, _int]),

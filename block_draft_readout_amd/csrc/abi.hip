@@ -155,7 +155,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int bdr_abi_version(void) { return 4; }
+int bdr_abi_version(void) { return 5; }
 
 const char* bdr_last_error(void) { return g_err; }
 
@@ -541,6 +541,38 @@ int dflash_fuse_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64
   hipError_t e = launch_fc_rows(taps, n_taps, rows, hidden, dt, row_index, row_count, max_rows,
                                 fc_w, out, workspace, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_rows launch");
+  return BDR_OK;
+}
+
+size_t dflash_fuse_fc_rows_fp8_workspace_bytes(int64_t max_rows, int64_t hidden, int n_taps) {
+  if (fp8_shape(max_rows, hidden, n_taps, hidden) != BDR_OK) return 0;
+  return fc_rows_fp8_workspace(max_rows, hidden, n_taps);
+}
+
+int dflash_fuse_fc_rows_fp8(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                            const int32_t* row_index, const int32_t* row_count, int64_t max_rows,
+                            const uint8_t* fc_q, const float* fc_scale, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  BDR_TRY(fp8_shape(max_rows, hidden, n_taps, hidden));
+  BDR_TRY(fp8_shape(rows, hidden, n_taps, hidden));
+  if (max_rows == 0) return BDR_OK;
+  if (!taps) return fail(BDR_EINVAL, "taps must not be NULL");
+  for (int t = 0; t < n_taps; ++t) {
+    if (rows > 0 && !taps[t]) return fail(BDR_EINVAL, "taps[%d] must not be NULL", t);
+    if (!aligned(taps[t], 16)) return fail(BDR_EINVAL, "taps[%d] must be 16-byte aligned", t);
+  }
+  BDR_TRY(need_ptr(row_index, "row_index", 4));
+  BDR_TRY(need_ptr(row_count, "row_count", 4));
+  BDR_TRY(need_ptr(fc_q, "fc_q"));
+  BDR_TRY(need_ptr(fc_scale, "fc_scale", 4));
+  BDR_TRY(need_ptr(out, "out"));
+  if (!plan_gemm_fp8(max_rows, hidden, hidden * n_taps, true, n_taps).stream)
+    return fail(BDR_EUNSUPPORTED, "fc shape not supported with fp8 weights");
+  BDR_TRY(need_ws(workspace, workspace_bytes, fc_rows_fp8_workspace(max_rows, hidden, n_taps)));
+  BDR_TRY(check_device());
+  hipError_t e = launch_fc_rows_fp8(taps, n_taps, rows, hidden, row_index, row_count, max_rows,
+                                    fc_q, fc_scale, out, workspace, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_rows_fp8 launch");
   return BDR_OK;
 }
 

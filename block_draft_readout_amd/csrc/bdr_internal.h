@@ -115,6 +115,11 @@ hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int
                           bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
                           int64_t max_rows, const void* fc_w, void* out, void* workspace,
                           hipStream_t stream);
+size_t fc_rows_fp8_workspace(int64_t max_rows, int64_t hidden, int n_taps);
+hipError_t launch_fc_rows_fp8(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                              const int32_t* row_index, const int32_t* row_count,
+                              int64_t max_rows, const uint8_t* fc_q, const float* fc_scale,
+                              void* out, void* workspace, hipStream_t stream);
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

@@ -147,15 +147,14 @@ size_t fc_rows_workspace(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype
          plan_gemm(max_rows, hidden, hidden * n_taps, dt, true, n_taps).workspace;
 }
 
-hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
-                          bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
-                          int64_t max_rows, const void* fc_w, void* out, void* workspace,
-                          hipStream_t stream) {
-  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+// gather the selected rows of every tap into the workspace (n_taps x
+// [max_rows, H]); gathered[t] receives the dense tap t
+static hipError_t launch_gather(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                                int64_t es, const int32_t* row_index, const int32_t* row_count,
+                                int64_t max_rows, char* ws, const void** gathered,
+                                hipStream_t stream) {
   GatherArgs ga{};
-  char* ws = static_cast<char*>(workspace);
   const size_t per_tap = align256(static_cast<size_t>(max_rows) * hidden * es);
-  const void* gathered[BDR_MAX_TAPS] = {};
   for (int t = 0; t < n_taps; ++t) {
     ga.taps[t] = taps[t];
     ga.dst[t] = ws + t * per_tap;
@@ -168,11 +167,43 @@ hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int
   ga.row_count = row_count;
   hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(max_rows), static_cast<unsigned>(n_taps)),
                      dim3(256), 0, stream, ga);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                          bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
+                          int64_t max_rows, const void* fc_w, void* out, void* workspace,
+                          hipStream_t stream) {
+  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+  char* ws = static_cast<char*>(workspace);
+  const void* gathered[BDR_MAX_TAPS] = {};
+  hipError_t e = launch_gather(taps, n_taps, rows, hidden, es, row_index, row_count, max_rows, ws,
+                               gathered, stream);
   if (e != hipSuccess) return e;
   const GemmPlan p = plan_gemm(max_rows, hidden, hidden * n_taps, dt, true, n_taps);
   return launch_gemm(p, dt, gathered, n_taps, hidden, max_rows, hidden, fc_w, out,
-                     dt == BDR_BF16 ? OUT_BF16 : OUT_F32, ws + n_taps * per_tap, stream);
+                     dt == BDR_BF16 ? OUT_BF16 : OUT_F32,
+                     ws + gathered_bytes(max_rows, hidden, n_taps, dt), stream);
+}
+
+size_t fc_rows_fp8_workspace(int64_t max_rows, int64_t hidden, int n_taps) {
+  if (max_rows == 0) return 0;
+  return gathered_bytes(max_rows, hidden, n_taps, BDR_BF16) +
+         plan_gemm_fp8(max_rows, hidden, hidden * n_taps, true, n_taps).workspace;
+}
+
+hipError_t launch_fc_rows_fp8(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                              const int32_t* row_index, const int32_t* row_count,
+                              int64_t max_rows, const uint8_t* fc_q, const float* fc_scale,
+                              void* out, void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  const void* gathered[BDR_MAX_TAPS] = {};
+  hipError_t e = launch_gather(taps, n_taps, rows, hidden, 2, row_index, row_count, max_rows, ws,
+                               gathered, stream);
+  if (e != hipSuccess) return e;
+  const GemmPlan p = plan_gemm_fp8(max_rows, hidden, hidden * n_taps, true, n_taps);
+  return launch_gemm_fp8(p, gathered, n_taps, hidden, max_rows, hidden, fc_q, fc_scale, out,
+                         OUT_BF16, ws + gathered_bytes(max_rows, hidden, n_taps, BDR_BF16), stream);
 }
 
 }  // namespace bdr

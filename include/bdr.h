@@ -407,6 +407,18 @@ int dflash_fuse_fc_rows(const void* const* taps, int n_taps, int64_t rows,
                         const void* fc_w, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* dflash_fuse_fc_rows_fp8 -- the same on fp8 weights (E4M3 codes fc_q [H, n_taps*H]
+ * with fp32 row scales fc_scale [H], as dflash_fuse_fc_fp8); taps and out bf16.
+ *   workspace >= dflash_fuse_fc_rows_fp8_workspace_bytes(max_rows, H, n_taps)
+ * ------------------------------------------------------------------------- */
+size_t dflash_fuse_fc_rows_fp8_workspace_bytes(int64_t max_rows, int64_t hidden,
+                                               int n_taps);
+int dflash_fuse_fc_rows_fp8(const void* const* taps, int n_taps, int64_t rows,
+                            int64_t hidden, const int32_t* row_index,
+                            const int32_t* row_count, int64_t max_rows,
+                            const uint8_t* fc_q, const float* fc_scale, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 4
+    assert L.bdr_abi_version() == 5
 
 
 def test_workspace_sizes(L):
@@ -141,6 +141,13 @@ def test_fp8_workspace_and_validation(L):
     assert lm(P, 7, 5120, 1000, P, None, P, None) == A.BDR_EINVAL
     assert lm(P, 7, 5120, 1000, P, P, None, None) == A.BDR_EINVAL
     assert lm(P, 0, 5120, 1000, P, P, P, None) == A.BDR_OK
+    rws = L.dflash_fuse_fc_rows_fp8_workspace_bytes(64, 5120, 5)
+    assert rws > 5 * 64 * 5120 * 2 and rws % 256 == 0
+    fr = L.dflash_fuse_fc_rows_fp8
+    assert fr(taps, 5, 8, 5120, P, P, 64, P, P, P, None, 0, None) == A.BDR_EWORKSPACE
+    assert fr(taps, 5, 8, 5120, None, P, 64, P, P, P, None, 0, None) == A.BDR_EINVAL
+    assert fr(taps, 5, 8, 5100, P, P, 64, P, P, P, None, 0, None) == A.BDR_EUNSUPPORTED
+    assert fr(taps, 5, 8, 5120, P, P, 0, P, P, P, None, 0, None) == A.BDR_OK
 
 
 def test_hc_average_validation(L):

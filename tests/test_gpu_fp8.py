@@ -196,3 +196,81 @@ def test_b16_fp8_full_size_sampled():
     assert err <= LM_TOL
     assert errf <= FC_TOL
 
+
+
+def test_fc_rows_fp8_on_gathered_rows():
+    rng = np.random.default_rng(6)
+    T, rows, H = 5, 40, 512
+    taps = [_bf16(rng, (rows, H)) for _ in range(T)]
+    q, s = synth.quantize_e4m3_rows(rng.standard_normal((H, T * H)).astype(np.float32) / np.sqrt(T * H))
+    idx = np.sort(rng.choice(rows, size=13, replace=False)).astype(np.int32)
+    row_index = np.full(rows, -3, dtype=np.int32)
+    row_index[:idx.size] = idx
+    count = np.array([idx.size], dtype=np.int32)
+    out = bdr().dflash_fuse_fc_rows_fp8([dev(t) for t in taps], dev(q), dev(s), dev(row_index),
+                                        dev(count))
+    got = oracle.widen(host_bits(out), "bf16")
+    ref = fp8.fuse_fc_fp8([t[idx] for t in taps], q, s, "bf16")
+    err = max_rel_err(got[:idx.size], ref)
+    log(f"fc rows fp8: {idx.size}/{rows} rows, max rel err {err:.3e}")
+    assert err <= FC_TOL
+    assert np.all(got[idx.size:] == 0)
+
+
+def test_closed_loop_fp8_on_device():
+    """Three block-steps chained on the device with fp8 weights (LM head, draft,
+    verify, commit, fc on the accepted rows), each against the oracle's step
+    from the same context; rows whose acceptance meets a near-tie leave the
+    comparison."""
+    import dataclasses
+    from oracle import loop
+    from gpu_util import first_near_tie
+    w = dataclasses.replace(workloads.get("b16"), cid=96, name="loop_fp8", batch=3, hidden=256,
+                            n_taps=3, k=5, vocab=4099, rank=16)
+    W = synth.make_weights_fp8(w)
+    steps = 3
+    inputs = [synth.make_step(w, s) for s in range(steps)]
+    g = {n: dev(W[n]) for n in ("fc_q", "fc_scale", "lm_q", "lm_scale", "w1", "w2")}
+    prev = dev(inputs[0]["prev0"])
+    live = np.ones(w.batch, dtype=bool)
+    prev_ref = inputs[0]["prev0"].astype(np.int64)
+    for s in range(steps):
+        inp = inputs[s]
+        Z = fp8.lm_head_fp8(inp["draft_hidden"], W["lm_q"], W["lm_scale"], "bf16")
+        d_ref, gap = oracle.semi_ar_argmax(Z, W["w1"], W["w2"], prev_ref, "bf16")
+        Y = synth.plant_targets(w, s, inp["noise"], d_ref)["target_logits"]
+        L = np.full(w.batch, w.k)
+        t_ref = oracle.target_argmax(Y, "bf16", L)
+        a_ref, bonus_ref, _, _ = oracle.verify_greedy(d_ref, t_ref, L)
+        c_ref = loop.commit_step(d_ref, a_ref, bonus_ref, L)
+        F_ref = fp8.fuse_fc_fp8([t[c_ref["row_index"]] for t in inp["taps"]], W["fc_q"],
+                                W["fc_scale"], "bf16")
+        Zg = bdr().dspark_lm_head_fp8(dev(inp["draft_hidden"]), g["lm_q"], g["lm_scale"])
+        d = bdr().dspark_markov_argmax(Zg, g["w1"], g["w2"], prev)
+        v = bdr().spec_verify_greedy(dev(Y), d, target_argmax=False)
+        c = bdr().spec_commit(d, v["accepted"], v["bonus"], v["block_len"])
+        F = bdr().dflash_fuse_fc_rows_fp8([dev(t) for t in inp["taps"]], g["fc_q"], g["fc_scale"],
+                                          c["row_index"], c["row_count"])
+        torch.cuda.synchronize()
+        istar = first_near_tie(gap)
+        r = {n: host_bits(x) for n, x in dict(d=d, F=F, **c, **v).items()}
+        got_F = oracle.widen(r["F"], "bf16")
+        for b in range(w.batch):
+            if not live[b]:
+                continue
+            m = int(istar[b])
+            assert np.array_equal(r["d"][b, :m], d_ref[b, :m]), (s, b)
+            if m <= min(int(a_ref[b]), w.k - 1):
+                live[b] = False
+                log(f"  step {s} row {b}: near-tie at {m}, row left out from here")
+                continue
+            a = int(a_ref[b])
+            assert r["accepted"][b] == a and r["bonus"][b] == bonus_ref[b], (s, b)
+            assert np.array_equal(r["emitted"][b], c_ref["emitted"][b]), (s, b)
+            g0, o0 = int(r["row_offsets"][b]), int(c_ref["row_offsets"][b])
+            err = max_rel_err(got_F[g0:g0 + a + 1], F_ref[o0:o0 + a + 1])
+            assert err <= FC_TOL, (s, b, err)
+        prev = c["next_prev"]
+        prev_ref = np.where(live, bonus_ref, r["next_prev"]).astype(np.int64)
+    log(f"fp8 closed loop: rows compared to the end {int(live.sum())}/{w.batch}")
+    assert live.sum() >= w.batch - 1
