@@ -274,3 +274,14 @@ def test_closed_loop_fp8_on_device():
         prev_ref = np.where(live, bonus_ref, r["next_prev"]).astype(np.int64)
     log(f"fp8 closed loop: rows compared to the end {int(live.sum())}/{w.batch}")
     assert live.sum() >= w.batch - 1
+
+
+@pytest.mark.parametrize("M,N,H", [(17, 1, 128), (33, 3, 256), (160, 17, 64), (48, 300, 192)])
+def test_fp8_row_split_edge_shapes(M, N, H):
+    rng = np.random.default_rng(M * 1000 + N + 7)
+    hid = _bf16(rng, (M, H))
+    q, s = synth.quantize_e4m3_rows(rng.standard_normal((N, H)).astype(np.float32) / np.sqrt(H))
+    got = bdr().dspark_lm_head_fp8(dev(hid), dev(q), dev(s)).cpu().numpy()
+    err = max_rel_err(got, fp8.lm_head_fp8(hid, q, s, "bf16"))
+    log(f"fp8 row-split edge M={M} N={N} H={H}: max rel err {err:.3e}")
+    assert err <= LM_TOL

@@ -135,3 +135,20 @@ def test_prefill_fc_parity_on_sampled_rows(hidden):
     err = max_rel_err(oracle.widen(got[sample], "bf16"), ref)
     log(f"  {sample.size} rows, max rel err {err:.3e}")
     assert err <= 4e-3
+
+
+@pytest.mark.parametrize("M,N,H", [(17, 1, 128), (160, 17, 128), (33, 3, 256), (100, 65, 8),
+                                   (48, 300, 136)])
+def test_row_split_edge_shapes(M, N, H):
+    """Row-split kernel at the edges: workgroups whose waves own no rows, a
+    partial last K block (H = 136, 8), row counts just above a tile."""
+    import block_draft_readout_amd as bdr
+    import numpy as np
+    rng = np.random.default_rng(M * 1000 + N)
+    hid = synth.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    lm_w = synth.to_bf16_bits((rng.standard_normal((N, H)) / np.sqrt(H)).astype(np.float32))
+    got = bdr.dspark_lm_head(dev(hid), dev(lm_w)).cpu().numpy()
+    ref = oracle.lm_head(hid, lm_w, "bf16")
+    err = max_rel_err(got, ref)
+    log(f"row-split edge M={M} N={N} H={H}: max rel err {err:.3e}")
+    assert err <= 1e-3
