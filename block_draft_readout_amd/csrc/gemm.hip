@@ -312,7 +312,12 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
   if (M > 16 || kbytes % 64 != 0) return false;
   if (n_seg > 1 && segbytes % (esize == 1 ? 64 : kKBB) != 0) return false;
   const int64_t max_tiles = esize == 1 ? kStreamTilesFp8 : kStreamTiles;
-  const int64_t waves = 4 * static_cast<int64_t>(kNumCU);
+  // bf16 split-K plans (the fc) use two one-wave workgroups per compute unit
+  // rather than four: alone the fc barely slows (48 -> 49 us on the 27B shape),
+  // and it leaves LDS for the Markov chain that runs beside it on another
+  // stream (block-step 308.5 -> 303.3 us).  One per CU made the fc itself too
+  // slow, and the fp8 fc (half the K blocks) loses more than the chain gains.
+  const int64_t waves = (allow_split && esize == 2 ? 2 : 4) * static_cast<int64_t>(kNumCU);
   const int64_t kblocks = (kbytes + kKBB - 1) / kKBB;
   double best = 1e300;
   for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
