@@ -201,7 +201,7 @@ __device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
 
 constexpr int kChainWaves = 5;   // wave 0: hand-off; waves 1..4: vocabulary tiles
 
-template <typename S, int RKS, int MAXT, bool SAMPLE>
+template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE>
 __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const MarkovArgs g) {
   extern __shared__ u32x4_t w2s[];   // [tile][chunk][lane] operand chunks of markov_w2
   constexpr int E = Elem<S>::PER16;
@@ -273,7 +273,35 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
       if constexpr (SAMPLE) gv[u] = bload16(rg, off);
     }
   };
-  if (cw >= 0) load_z(0, 0, cw, ntl, vbase);
+  // One row (B == 1): the product is taken the other way round, D[row][entry]
+  // = context embeddings x markov_w2 rows, so lane (r16, grp) holds entry
+  // 16 * tile + r16 of row 4 * grp (the batch's row in grp 0 lanes) and each
+  // tile costs one compare per lane instead of four.  z1 / n1: the lane's
+  // logit and noise of each of its tiles.
+  float z1[ONE ? MAXT : 1];
+  float n1[ONE && SAMPLE ? MAXT : 1];
+  const int vbase1 = static_cast<int>(t_lo) * 16 + r16;   // + 16 * tile
+  auto load_z1 = [&](int pos, int cwo, int ntlo, int vbo) {
+    const int64_t first = static_cast<int64_t>(pos) * g.V;
+    const uint32_t bytes = static_cast<uint32_t>(V32) * 4u;
+    const rsrc_t rz = make_rsrc(g.logits + first, bytes);
+    rsrc_t rg;
+    if constexpr (SAMPLE) rg = make_rsrc(g.noise + first, bytes);
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int tile = cwo + 4 * u;
+      const int v = vbo + 16 * tile;
+      const uint32_t off = (grp == 0 && tile < ntlo && v < V32) ? static_cast<uint32_t>(v) * 4u : kOOB;
+      z1[u] = bload_f32(rz, off);
+      if constexpr (SAMPLE) n1[u] = bload_f32(rg, off);
+    }
+  };
+  if (cw >= 0) {
+    if constexpr (ONE)
+      load_z1(0, cw, ntl, vbase1);
+    else
+      load_z(0, 0, cw, ntl, vbase);
+  }
   BDR_WAIT_VM(0);
   __syncthreads();
 
@@ -285,78 +313,118 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
       if (cw >= 0) {
         // per-tile indices are recomputed each position from opaque copies
         // instead of being kept live (in registers) across the whole chain
-        int cwo = cw, ntlo = ntl, vbo = vbase;
+        int cwo = cw, ntlo = ntl, vbo = ONE ? vbase1 : vbase;
         asm volatile("" : "+s"(cwo), "+s"(ntlo), "+v"(vbo));
-        if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
-        u32x4_t ef[NC];
-        context_frags<S, RKS>(g, b0 + r16 < g.B ? ctx[b0 + r16] : -1, grp, ef);
-        // bias tile D[vocab 4 * grp + i][row r16] = markov_w2 rows x context
-        // embeddings; each lane keeps the running maximum of its row r16 over
-        // the entries it visits in increasing order.  Reads past the
-        // workgroup's last tile repeat it (no branch) and are masked.
-        float bv = -INFINITY;
-        uint32_t bi = 0xFFFFFFFFu;
-        const bool row_ok = r16 < nb;
-        rsrc_t rx;
-        f32x4_t xt = {0.f, 0.f, 0.f, 0.f};
-        uint32_t toff = kOOB;
-        if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, block_bytes(b0));
+        if constexpr (ONE) {
+          u32x4_t ef[NC];
+          context_frags<S, RKS>(g, r16 == 0 ? ctx[0] : -1, grp, ef);
+          float bv = -INFINITY;
+          uint32_t bi = 0xFFFFFFFFu;
+          rsrc_t rx;
+          if constexpr (SAMPLE)
+            rx = make_rsrc(g.xout + static_cast<int64_t>(pos) * g.V, static_cast<uint32_t>(V32) * 4u);
 #pragma unroll
-        for (int u = 0; u < MAXT; ++u) {
-          const int tile = cwo + 4 * u;
-          const int tile_rd = tile < ntlo ? tile : ntlo - 1;
-          f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (RKS > 0) {
+          for (int u = 0; u < MAXT; ++u) {
+            const int tile = cwo + 4 * u;
+            const int tile_rd = tile < ntlo ? tile : ntlo - 1;
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (RKS > 0) {
 #pragma unroll
-            for (int c = 0; c < RKS; ++c)
-              bias = mma16(w2s[(tile_rd * RKS + c) * 64 + lane], ef[c], bias, S());
-          }
-          const int v0 = vbo + 16 * tile;
-          // entries of the lane's quad that exist (<= 0: none); a missing
-          // entry's key is -inf and never wins
-          const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
-          f32x4_t xs;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float s = __uint_as_float(zv[u][i]) + bias[i];
-            float key = s;
-            if constexpr (SAMPLE) {
-              xs[i] = s;
-              key = s * g.inv_t + __uint_as_float(gv[u][i]);
+              for (int c = 0; c < RKS; ++c)
+                d = mma16(ef[c], w2s[(tile_rd * RKS + c) * 64 + lane], d, S());
             }
-            key = i < lim ? key : -INFINITY;
+            const int v = vbo + 16 * tile;
+            const bool ok = tile < ntlo && v < V32;
+            const float sv = z1[u] + d[0];
+            float key = sv;
+            if constexpr (SAMPLE) {
+              key = sv * g.inv_t + n1[u];
+              bstore_f32(sv, rx, (ok && grp == 0) ? static_cast<uint32_t>(v) * 4u : kOOB);
+            }
+            key = ok ? key : -INFINITY;
             if (key > bv) {
               bv = key;
-              bi = static_cast<uint32_t>(v0 + i);
+              bi = static_cast<uint32_t>(v);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (pos + 1 < g.k) load_z1(pos + 1, cwo, ntlo, vbo);
+          // the row's maximum over the 16 lanes of grp 0, then over the waves
+          unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+          key = rowgroup_max16(key);
+          if (lane == 0) sk[cw][0] = key;
+        } else {
+          if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
+          u32x4_t ef[NC];
+          context_frags<S, RKS>(g, b0 + r16 < g.B ? ctx[b0 + r16] : -1, grp, ef);
+          // bias tile D[vocab 4 * grp + i][row r16] = markov_w2 rows x context
+          // embeddings; each lane keeps the running maximum of its row r16 over
+          // the entries it visits in increasing order.  Reads past the
+          // workgroup's last tile repeat it (no branch) and are masked.
+          float bv = -INFINITY;
+          uint32_t bi = 0xFFFFFFFFu;
+          const bool row_ok = r16 < nb;
+          rsrc_t rx;
+          f32x4_t xt = {0.f, 0.f, 0.f, 0.f};
+          uint32_t toff = kOOB;
+          if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, block_bytes(b0));
+  #pragma unroll
+          for (int u = 0; u < MAXT; ++u) {
+            const int tile = cwo + 4 * u;
+            const int tile_rd = tile < ntlo ? tile : ntlo - 1;
+            f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (RKS > 0) {
+  #pragma unroll
+              for (int c = 0; c < RKS; ++c)
+                bias = mma16(w2s[(tile_rd * RKS + c) * 64 + lane], ef[c], bias, S());
+            }
+            const int v0 = vbo + 16 * tile;
+            // entries of the lane's quad that exist (<= 0: none); a missing
+            // entry's key is -inf and never wins
+            const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
+            f32x4_t xs;
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float s = __uint_as_float(zv[u][i]) + bias[i];
+              float key = s;
+              if constexpr (SAMPLE) {
+                xs[i] = s;
+                key = s * g.inv_t + __uint_as_float(gv[u][i]);
+              }
+              key = i < lim ? key : -INFINITY;
+              if (key > bv) {
+                bv = key;
+                bi = static_cast<uint32_t>(v0 + i);
+              }
+            }
+            if constexpr (SAMPLE) {
+              // x of the lane's four entries in one 16-byte store; the quad that
+              // straddles the end of the row (at most one per lane) is kept for
+              // element stores after the loop
+              const uint32_t off = static_cast<uint32_t>(r16) * zrow + static_cast<uint32_t>(v0) * 4u;
+              bstore16(xs, rx, lim >= 4 ? off : kOOB);
+              const bool part = lim > 0 && lim < 4;
+              xt = part ? xs : xt;
+              toff = part ? off : toff;
             }
           }
           if constexpr (SAMPLE) {
-            // x of the lane's four entries in one 16-byte store; the quad that
-            // straddles the end of the row (at most one per lane) is kept for
-            // element stores after the loop
-            const uint32_t off = static_cast<uint32_t>(r16) * zrow + static_cast<uint32_t>(v0) * 4u;
-            bstore16(xs, rx, lim >= 4 ? off : kOOB);
-            const bool part = lim > 0 && lim < 4;
-            xt = part ? xs : xt;
-            toff = part ? off : toff;
+            const int tn = V32 & 3;   // entries of a straddling quad
+            if (toff != kOOB) {
+  #pragma unroll
+              for (int i = 0; i < 3; ++i) bstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
+            }
           }
+          // the next position's first logits: independent of the hand-off below
+          // (kept after the compares so the two logits sets are never live together)
+          __builtin_amdgcn_sched_barrier(0);
+          if (last_group && pos + 1 < g.k) load_z(pos + 1, 0, cwo, ntlo, vbo);
+          // row r16's maximum over the four lane groups, then over the waves (LDS)
+          unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+          key = umax64(key, __shfl_xor(key, 16, 64));
+          key = umax64(key, __shfl_xor(key, 32, 64));
+          if (grp == 0) sk[cw][r16] = key;
         }
-        if constexpr (SAMPLE) {
-          const int tn = V32 & 3;   // entries of a straddling quad
-          if (toff != kOOB) {
-#pragma unroll
-            for (int i = 0; i < 3; ++i) bstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
-          }
-        }
-        // the next position's first logits: independent of the hand-off below
-        // (kept after the compares so the two logits sets are never live together)
-        __builtin_amdgcn_sched_barrier(0);
-        if (last_group && pos + 1 < g.k) load_z(pos + 1, 0, cwo, ntlo, vbo);
-        // row r16's maximum over the four lane groups, then over the waves (LDS)
-        unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
-        key = umax64(key, __shfl_xor(key, 16, 64));
-        key = umax64(key, __shfl_xor(key, 32, 64));
-        if (grp == 0) sk[cw][r16] = key;
       }
       BDR_LDS_BARRIER();
       // this workgroup's maxima of rows b0.. -> its tagged slots
@@ -533,19 +601,25 @@ static __global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs 
 
 constexpr size_t kChainLdsMax = 150 * 1024;
 
-template <typename S, int RKS, int MAXT, bool SAMPLE>
-static hipError_t launch_chain_t(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
+template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE>
+static hipError_t launch_chain_r(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT, SAMPLE>),
+        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kChainLdsMax));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT, SAMPLE>), dim3(G), dim3(64 * kChainWaves),
-                     lds, st, g);
+  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE>), dim3(G),
+                     dim3(64 * kChainWaves), lds, st, g);
   return hipSuccess;
+}
+
+template <typename S, int RKS, int MAXT, bool SAMPLE>
+static hipError_t launch_chain_t(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
+  return g.B == 1 ? launch_chain_r<S, RKS, MAXT, SAMPLE, true>(g, G, lds, st)
+                  : launch_chain_r<S, RKS, MAXT, SAMPLE, false>(g, G, lds, st);
 }
 
 // MAXT: 16-entry vocabulary tiles per wave (the workgroup's tiles / 4, rounded up)

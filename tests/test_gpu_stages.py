@@ -43,6 +43,10 @@ MID = {
                                    plant_p=(0.76, 0.45, 0.31, 0.14, 0.10, 0.02)),
     "mid_bf16_b20": dataclasses.replace(workloads.get("b16"), cid=22, name="mid_bf16_b20",
                                         batch=20, hidden=64, n_taps=2, k=3, vocab=1031, rank=8),
+    # the chain's [B, k] logits do not fit in LDS: prefetched into registers
+    # position by position instead of staged once
+    "mid_bf16_b40": dataclasses.replace(workloads.get("b16"), cid=23, name="mid_bf16_b40",
+                                        batch=40, hidden=64, n_taps=2, k=7, vocab=3001, rank=24),
 }
 
 
