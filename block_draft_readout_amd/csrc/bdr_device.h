@@ -173,18 +173,47 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
   return a > b ? a : b;
 }
 
-// max over the 16 lanes of a row group (lanes with equal l >> 4)
+// Data-parallel-primitive (DPP) moves inside rows of 16 lanes, 64 bits as two
+// 32-bit moves: quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, xor 2),
+// row_half_mirror (lane i of each 8 <- 7 - i) and row_mirror (lane i of each
+// 16 <- 15 - i).  No LDS traffic, unlike a general lane shuffle.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long k) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(k)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      0, static_cast<int>(static_cast<uint32_t>(k >> 32)), CTRL, 0xF, 0xF, false));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// max over the 16 lanes of a row group (lanes with equal l >> 4), in every
+// lane of the group: quads, then halves, then the row.  Called by whole waves.
 __device__ __forceinline__ unsigned long long rowgroup_max16(unsigned long long k) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) k = umax64(k, __shfl_xor(k, off, 64));
+  k = umax64(k, dpp_u64<kDppQuadXor1>(k));
+  k = umax64(k, dpp_u64<kDppQuadXor2>(k));
+  k = umax64(k, dpp_u64<kDppRowHalfMirror>(k));
+  k = umax64(k, dpp_u64<kDppRowMirror>(k));
   return k;
 }
 
-// max over a whole 64-lane wave
+// max over a whole 64-lane wave, in every lane: the row maxima, then the four
+// rows' values read from lanes 0, 16, 32 and 48.  Called by whole waves.
 __device__ __forceinline__ unsigned long long wave_max64(unsigned long long k) {
+  k = rowgroup_max16(k);
+  const uint32_t lo = static_cast<uint32_t>(k);
+  const uint32_t hi = static_cast<uint32_t>(k >> 32);
+  unsigned long long m = 0ull;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) k = umax64(k, __shfl_xor(k, off, 64));
-  return k;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 16 * r));
+    const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 16 * r));
+    m = umax64(m, (static_cast<unsigned long long>(h) << 32) | l);
+  }
+  return m;
 }
 
 // ---------------------------------------------------------------------------

@@ -219,7 +219,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
   const int ntl = static_cast<int>(t_hi - t_lo);   // compute wave c owns tiles c, c+4, ... (< 4*MAXT)
   const bool single = g.B <= kSinglePhaseB;
 
-  __shared__ unsigned long long sk[4][16];
+  __shared__ unsigned long long sk[4][4][16];      // [compute wave][lane group][row]
   __shared__ int32_t ctx[kChainMaxB];              // context token of every row
   __shared__ int last_flag;
 
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           // the row's maximum over the 16 lanes of grp 0, then over the waves
           unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
           key = rowgroup_max16(key);
-          if (lane == 0) sk[cw][0] = key;
+          if (lane == 0) sk[cw][0][0] = key;
         } else {
           if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
           u32x4_t ef[NC];
@@ -419,18 +419,18 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           // (kept after the compares so the two logits sets are never live together)
           __builtin_amdgcn_sched_barrier(0);
           if (last_group && pos + 1 < g.k) load_z(pos + 1, 0, cwo, ntlo, vbo);
-          // row r16's maximum over the four lane groups, then over the waves (LDS)
-          unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
-          key = umax64(key, __shfl_xor(key, 16, 64));
-          key = umax64(key, __shfl_xor(key, 32, 64));
-          if (grp == 0) sk[cw][r16] = key;
+          // row r16's maximum over the lane groups and waves, taken from LDS
+          sk[cw][grp][r16] = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
         }
       }
       BDR_LDS_BARRIER();
       // this workgroup's maxima of rows b0.. -> its tagged slots
       if (threadIdx.x < nb) {
-        const unsigned long long key = umax64(umax64(sk[0][threadIdx.x], sk[1][threadIdx.x]),
-                                              umax64(sk[2][threadIdx.x], sk[3][threadIdx.x]));
+        unsigned long long key = 0ull;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+          for (int q = 0; q < (ONE ? 1 : 4); ++q) key = umax64(key, sk[w][q][threadIdx.x]);
         publish_u64(g.slots + (pos * g.B + b0 + threadIdx.x) * kChainSlots + blockIdx.x,
                     tag_key(key, tag));
       }
