@@ -173,6 +173,34 @@ __device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsig
   return a > b ? a : b;
 }
 
+// The k <= N int32 / fp32 values of a block row, all loaded before any is
+// used (one memory round trip rather than one per element); entries past k
+// read as `fill`.
+template <typename T, int N>
+__device__ __forceinline__ void load_block_row(const T* row, int k, T fill, T (&out)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) out[i] = i < k ? row[i] : fill;
+}
+
+// Block length by confidence (k <= N positions): the first position whose
+// confidence is strictly below th, else k (a NaN confidence never truncates).
+template <int N>
+__device__ __forceinline__ int truncated_length(const float* conf_row, float th, int k) {
+  float c[N];
+  load_block_row(conf_row, k, 0.f, c);
+  int L = k;
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i)
+    if (i < k && c[i] < th) L = i;
+  return L;
+}
+
+// acc[i] += v with a device atomic that returns nothing (no round trip waited on)
+__device__ __forceinline__ void add_count(int64_t* acc, int v) {
+  if (v != 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(acc), static_cast<unsigned long long>(static_cast<int64_t>(v)));
+}
+
 // Data-parallel-primitive (DPP) moves inside rows of 16 lanes, 64 bits as two
 // 32-bit moves: quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, xor 2),
 // row_half_mirror (lane i of each 8 <- 7 - i) and row_mirror (lane i of each

@@ -55,12 +55,20 @@ __global__ __launch_bounds__(256) void commit_kernel(const CommitArgs g) {
       a = min(max(g.accepted[b], 0), g.k);   // device values: kept in range
       if (g.block_len) L = min(max(g.block_len[b], 0), g.k);
       const int32_t bon = g.bonus[b];
+      // the row's draft tokens, loaded once before the stores (which may alias)
+      int32_t dr[BDR_MAX_K];
+      if (g.emitted || g.draft_list) load_block_row(g.draft + b * g.k, g.k, int32_t{-1}, dr);
       g.next_prev[b] = bon;
-      if (g.emitted)
-        for (int j = 0; j < k1; ++j)
-          g.emitted[b * k1 + j] = j < a ? g.draft[b * g.k + j] : (j == a ? bon : -1);
-      if (g.draft_list)
-        for (int i = 0; i < g.k; ++i) g.draft_list[b * g.k + i] = i < L ? g.draft[b * g.k + i] : -1;
+      if (g.emitted) {
+#pragma unroll
+        for (int j = 0; j <= BDR_MAX_K; ++j)
+          if (j < k1) g.emitted[b * k1 + j] = j < a ? dr[j < BDR_MAX_K ? j : 0] : (j == a ? bon : -1);
+      }
+      if (g.draft_list) {
+#pragma unroll
+        for (int i = 0; i < BDR_MAX_K; ++i)
+          if (i < g.k) g.draft_list[b * g.k + i] = i < L ? dr[i] : -1;
+      }
     }
     // inclusive scan of the accepted-row counts of this chunk
     scan[tid] = live ? a + 1 : 0;

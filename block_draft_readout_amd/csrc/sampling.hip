@@ -130,10 +130,7 @@ struct SampleArgs {
 
 // L_b: first position whose confidence is strictly below the threshold, else k.
 __device__ __forceinline__ int sample_block_length(const SampleArgs& g, int64_t b) {
-  if (!g.use_conf) return g.k;
-  for (int i = 0; i < g.k; ++i)
-    if (g.conf[b * g.k + i] < g.th) return i;
-  return g.k;
+  return g.use_conf ? truncated_length<BDR_MAX_K>(g.conf + b * g.k, g.th, g.k) : g.k;
 }
 
 // Running base-2 log-sum-exp state: m = max, s = sum 2^(v - m); s == 0 means
@@ -263,8 +260,8 @@ __device__ void sample_scan(const SampleArgs& g) {
     __syncthreads();
   }
   if (tid < k) {
-    if (g.acc) g.acc[tid] += cacc[tid];
-    if (g.prop) g.prop[tid] += cprop[tid];
+    if (g.acc) add_count(g.acc + tid, cacc[tid]);
+    if (g.prop) add_count(g.prop + tid, cprop[tid]);
   }
 }
 

@@ -51,10 +51,7 @@ struct VerifyArgs {
 
 // L_b: first position whose confidence is strictly below the threshold, else k.
 __device__ __forceinline__ int block_length(const VerifyArgs& g, int64_t b) {
-  if (!g.use_conf) return g.k;
-  for (int i = 0; i < g.k; ++i)
-    if (g.conf[b * g.k + i] < g.th) return i;
-  return g.k;
+  return g.use_conf ? truncated_length<BDR_MAX_K>(g.conf + b * g.k, g.th, g.k) : g.k;
 }
 
 // Fold the chunk keys into target argmaxes and scan every row's block.
@@ -79,6 +76,10 @@ __device__ void verify_scan(const VerifyArgs& g) {
     const int nb = static_cast<int>(min<int64_t>(GROUP, g.B - b0));
     if (tid < nb) Ls[tid] = block_length(g, b0 + tid);
     for (int r = tid; r < nb * k1; r += nthr) tk[r] = 0ull;
+    // the draft row of the sequence this thread scans, in flight during the
+    // key fetch below (GROUP <= blockDim: one sequence per thread)
+    int32_t dr[BDR_MAX_K];
+    if (tid < nb) load_block_row(g.draft + (b0 + tid) * g.k, g.k, int32_t{-1}, dr);
     __syncthreads();
     const int total = nb * k1 * g.chunks;   // (row, chunk) pairs of this group
     const unsigned long long* base = g.part + b0 * k1 * g.chunks;
@@ -98,12 +99,16 @@ __device__ void verify_scan(const VerifyArgs& g) {
       }
     }
     __syncthreads();
-    for (int lb = tid; lb < nb; lb += nthr) {
+    if (tid < nb) {
+      const int lb = tid;
       const int64_t b = b0 + lb;
       const int L = Ls[lb];
       auto tok = [&](int j) { return j <= L ? key_index(tk[lb * k1 + j]) : -1; };
-      int a = 0;
-      while (a < L && g.draft[b * g.k + a] == tok(a)) ++a;
+      // accepted prefix: the first position below L whose draft differs
+      int a = L;
+#pragma unroll
+      for (int i = BDR_MAX_K - 1; i >= 0; --i)
+        if (i < L && dr[i] != tok(i)) a = i;
       g.block_len[b] = L;
       g.accepted[b] = a;
       g.bonus[b] = tok(a);
@@ -115,8 +120,8 @@ __device__ void verify_scan(const VerifyArgs& g) {
     __syncthreads();
   }
   if (tid < g.k) {
-    if (g.acc) g.acc[tid] += cacc[tid];
-    if (g.prop) g.prop[tid] += cprop[tid];
+    if (g.acc) add_count(g.acc + tid, cacc[tid]);
+    if (g.prop) add_count(g.prop + tid, cprop[tid]);
   }
 }
 
