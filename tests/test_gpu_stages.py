@@ -215,6 +215,48 @@ def test_exact_ties_across_tiles_and_tail():
     assert np.array_equal(r["target_argmax"].cpu().numpy(), t_ref)
 
 
+def test_single_row_chain_ties_and_edges():
+    """B = 1 takes its own chain path (the bias product transposed, one
+    vocabulary entry per lane): exact ties across workgroups and at V-1,
+    -0.0 against +0.0 and all-equal rows, with no Markov head and with zero
+    bf16 Markov weights (bias exactly 0 through the MFMAs); k = 1 with tiny
+    vocabularies; zero weights against the plain argmax."""
+    V, k = 151936, 4
+    Z = np.full((3, k, V), -3.0, np.float32)
+    Z[0, 0, [150000, 77, 151935]] = 5.0
+    Z[0, 1, [151935, 151934]] = 5.0
+    Z[0, 2, [40000, 120000]] = 5.0
+    Z[0, 3, 3] = -0.0
+    Z[0, 3, 9] = 0.0
+    Z[0, 3, :3] = -4.0
+    Z[1] = Z[0, ::-1]
+    Z[2, :, :] = 1.0
+    zeros = np.zeros((V, 32), np.uint16)
+    for b in range(3):
+        Zb = np.ascontiguousarray(Z[b:b + 1])
+        prev = np.array([b * 1000 + 5], np.int32)
+        d_ref, _ = oracle.semi_ar_argmax(Zb, None, None, prev, "f32")
+        d = bdr().dspark_markov_argmax(dev(Zb), None, None, dev(prev)).cpu().numpy()
+        assert np.array_equal(d, d_ref), (b, d, d_ref)
+        d = bdr().dspark_markov_argmax(dev(Zb), dev(zeros), dev(zeros), dev(prev)).cpu().numpy()
+        assert np.array_equal(d, d_ref), (b, d, d_ref)
+    g = np.random.default_rng(12)
+    for V in (1, 17, 64, 1000):
+        Zs = g.standard_normal((1, 1, V)).astype(np.float32)
+        w1 = synth.to_bf16_bits(g.standard_normal((V, 8)).astype(np.float32))
+        w2 = synth.to_bf16_bits(g.standard_normal((V, 8)).astype(np.float32))
+        prev = g.integers(0, V, 1).astype(np.int32)
+        d_ref, gap = oracle.semi_ar_argmax(Zs, w1, w2, prev, "bf16")
+        d = bdr().dspark_markov_argmax(dev(Zs), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+        compare_drafts(d, d_ref, gap)
+    Z1 = g.standard_normal((1, 6, 3001)).astype(np.float32)
+    w = synth.to_bf16_bits(g.standard_normal((3001, 32)).astype(np.float32))
+    z32 = np.zeros((3001, 32), np.uint16)
+    for w1, w2 in ((z32, w), (w, z32)):
+        d = bdr().dspark_markov_argmax(dev(Z1), dev(w1), dev(w2), dev(np.array([7], np.int32)))
+        assert np.array_equal(d.cpu().numpy(), np.argmax(Z1, axis=-1))
+
+
 def test_zero_markov_equals_plain_argmax():
     g = np.random.default_rng(4)
     B, k, V, r = 4, 6, 3001, 32
