@@ -139,16 +139,31 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs g) {
     float bv = -INFINITY;
     uint32_t bi = 0xFFFFFFFFu;
     if constexpr (VEC) {
+      // U steps of 16 bytes per lane issued before any is compared (a step
+      // past the chunk reloads its first bytes and is skipped); entries are
+      // visited in increasing order within a lane
       constexpr int E = Elem<S>::PER16;
-      for (int64_t v = c0 + static_cast<int64_t>(threadIdx.x) * E; v < c1; v += 256 * E) {
-        const u32x4_t q = load16_stream(y + v);
-        const S* e = reinterpret_cast<const S*>(&q);
+      constexpr int U = 4;
+      for (int64_t v0 = c0 + static_cast<int64_t>(threadIdx.x) * E; v0 < c1; v0 += 256 * E * U) {
+        u32x4_t q[U];
 #pragma unroll
-        for (int t = 0; t < E; ++t) {
-          const float f = to_f32<S>(e[t]);
-          if (f > bv) {
-            bv = f;
-            bi = static_cast<uint32_t>(v + t);
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 256 * E;
+          q[u] = load16_stream(y + (v < c1 ? v : c0));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = v0 + u * 256 * E;
+          if (v < c1) {
+            const S* e = reinterpret_cast<const S*>(&q[u]);
+#pragma unroll
+            for (int t = 0; t < E; ++t) {
+              const float f = to_f32<S>(e[t]);
+              if (f > bv) {
+                bv = f;
+                bi = static_cast<uint32_t>(v + t);
+              }
+            }
           }
         }
       }
@@ -187,9 +202,11 @@ __global__ __launch_bounds__(256) void verify_kernel(const VerifyArgs g) {
 // host side
 // ----------------------------------------------------------------------------
 
+// About 1024 workgroups (each lane keeps four 16-byte loads in flight), chunks
+// of >= 2048 entries, at most 256 per row.
 static void chunk_plan(int64_t B, int k, int64_t V, int* chunks, int64_t* len) {
   const int64_t rows = std::max<int64_t>(1, B * (k + 1));
-  int64_t c = std::max<int64_t>(1, (2048 + rows - 1) / rows);
+  int64_t c = std::max<int64_t>(1, (1024 + rows - 1) / rows);
   c = std::min<int64_t>(c, std::max<int64_t>(1, (V + 2047) / 2048));
   c = std::min<int64_t>(c, 256);
   int64_t l = (V + c - 1) / c;
