@@ -95,6 +95,7 @@ DRAFT_CASES = {
     "f32_ragged": (5, 6, 2053, 12, "f32", 3.0, 0.7),
     "bf16_b5": (5, 7, 5003, 64, "bf16", 2.5, 1.0),
     "bf16_b20": (20, 3, 1031, 8, "bf16", 2.0, 1.3),
+    "bf16_b256": (256, 3, 3001, 16, "bf16", 2.0, 1.0),   # the chain's largest batch
     "no_bias": (3, 5, 4099, 0, "bf16", 2.0, 0.8),
     "f32_r128_passes": (2, 3, 3001, 128, "f32", 2.0, 1.0),   # per-position launches
     "qwen_vocab": (1, 7, 151936, 32, "bf16", 3.0, 1.0),

@@ -313,6 +313,25 @@ def test_block_truncated_to_zero_and_max_sizes():
     compare_drafts(dg.cpu().numpy(), d_ref, gap)
 
 
+@pytest.mark.parametrize("B", [17, 256, 257])
+def test_markov_row_count_limits(B):
+    """Row counts at the chain's limits: a second row group holding one row
+    (17); the most rows whose contexts the chain keeps in LDS (256), where some
+    workgroups reduce two rows (3001 entries: 188 workgroups); one row more
+    (257), which takes one launch per position."""
+    g = np.random.default_rng(100 + B)
+    k, V, r = 3, 3001, 16
+    Z = (g.standard_normal((B, k, V)) * 4.0).astype(np.float32)
+    w1 = synth.to_bf16_bits((g.standard_normal((V, r)) * 0.5).astype(np.float32))
+    w2 = synth.to_bf16_bits((g.standard_normal((V, r)) * 0.5).astype(np.float32))
+    prev = g.integers(0, V, B).astype(np.int32)
+    d_ref, gap = oracle.semi_ar_argmax(Z, w1, w2, prev, "bf16")
+    d = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+    n_cmp, n_ex = compare_drafts(d, d_ref, gap)
+    log(f"markov B={B}: compared {n_cmp}, excluded {n_ex}")
+    assert n_cmp >= 0.8 * B * k
+
+
 def test_sentinel_outputs_all_written_and_deterministic():
     w = MID["mid_bf16"]
     W, s = _data(w)
