@@ -14,9 +14,11 @@ static size_t keys_bytes(int64_t B, int k) {
   return align256(static_cast<size_t>(B) * k * kArriveGroups * 8);
 }
 static size_t slots_bytes(int64_t B, int k) {
-  return align256(static_cast<size_t>(B) * k * kChainSlots * 8);
+  return align256(static_cast<size_t>(B) * k * kChainSlots * kSlotStride * 8);
 }
-static size_t tokens_bytes(int64_t B, int k) { return align256(static_cast<size_t>(B) * k * 8); }
+static size_t tokens_bytes(int64_t B, int k) {
+  return align256(static_cast<size_t>(B) * k * kTokenStride * 8);
+}
 
 size_t markov_workspace(int64_t B, int k) {
   return keys_bytes(B, k) + slots_bytes(B, k) + tokens_bytes(B, k) + 256 + 256;

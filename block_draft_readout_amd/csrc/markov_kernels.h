@@ -39,8 +39,10 @@
 //
 // Workspace (zero-filled before first use; every call leaves it zeroed):
 //   keys[k][16][B] uint64 (passes) | slots[k][B][256] uint64 (chain, per
-//   workgroup) | tokens[k][B] uint64 (chain, B > 2) | completion counter
-//   (128 bytes) | error uint32 (the last 256 bytes)
+//   workgroup, kSlotStride words apart) | tokens[k][B] uint64, each on its
+//   own 128-byte line (chain,
+//   B > 2) | completion counter (128 bytes) | error uint32 (the last 256
+//   bytes)
 
 #include <algorithm>
 
@@ -57,8 +59,8 @@ struct MarkovArgs {
   const void* w2;                // [V, r] projection to the vocabulary
   const int32_t* prev;           // [B] context of position 0
   unsigned long long* keys;      // passes: [k, 16, B] per-position argmax keys per group
-  unsigned long long* slots;     // chain: [k, B, kChainSlots] tagged local maxima
-  unsigned long long* tokens;    // chain: [k, B] tagged tokens (B > 2)
+  unsigned long long* slots;     // chain: [k, B, kChainSlots] tagged local maxima, kSlotStride apart
+  unsigned long long* tokens;    // chain: [k, B] tagged tokens (B > 2), kTokenStride apart
   unsigned* done;                // chain: completion counter
   unsigned* err;                 // error word
   int32_t* draft;                // [B, k]
@@ -73,6 +75,14 @@ struct MarkovArgs {
 constexpr int kChainSlots = kNumCU;   // workgroups of the chain (at most)
 constexpr int kChainMaxB = 256;       // rows the chain keeps contexts of in LDS
 constexpr int kSinglePhaseB = 2;      // up to this many rows every workgroup reduces all slots
+// Tokens sit one per 128-byte line: stores from many workgroups into one line
+// are merged one after another at the memory side, which had made the token
+// hand-off of 16 rows ~0.9 us slower per position.
+constexpr int kTokenStride = 16;      // uint64 words
+// Slots two words apart: eight writers per line instead of sixteen, at twice
+// the bytes per poll (measured: one word 27.4 us for the B = 1 chain, two 26.4,
+// four 26.8, sixteen 29.1; no change at B = 16 for two, worse for more).
+constexpr int kSlotStride = 2;        // uint64 words
 
 constexpr unsigned kSpinLimit = 1u << 22;   // ~0.2 s of polling before giving up
 
@@ -431,39 +441,42 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
         for (int w = 0; w < 4; ++w)
 #pragma unroll
           for (int q = 0; q < (ONE ? 1 : 4); ++q) key = umax64(key, sk[w][q][threadIdx.x]);
-        publish_u64(g.slots + (pos * g.B + b0 + threadIdx.x) * kChainSlots + blockIdx.x,
+        publish_u64(g.slots + ((pos * g.B + b0 + threadIdx.x) * kChainSlots + blockIdx.x) * kSlotStride,
                     tag_key(key, tag));
       }
       if (!last_group) BDR_LDS_BARRIER();   // sk is rewritten by the next row group
     }
     // contexts of the next position (and this position's tokens)
     if (wave == 0) {
-      // row b's slots of this position are contiguous: [pos][b][workgroup]
-      const unsigned long long* pos_slots = g.slots + static_cast<int64_t>(pos) * g.B * kChainSlots;
+      // row b's slots of this position are adjacent: [pos][b][workgroup]
+      const unsigned long long* pos_slots =
+          g.slots + static_cast<int64_t>(pos) * g.B * kChainSlots * kSlotStride;
       if (single) {
         for (int64_t b = 0; b < g.B; ++b) {
           const int32_t tok =
-              tagged_index(poll_max(g, pos_slots + b * kChainSlots, 1, static_cast<int>(G), tag, lane));
+              tagged_index(poll_max(g, pos_slots + b * kChainSlots * kSlotStride, kSlotStride,
+                                    static_cast<int>(G), tag, lane));
           if (lane == 0) {
             ctx[b] = tok;
             if (blockIdx.x == 0) g.draft[b * g.k + pos] = tok;
           }
         }
       } else {
-        unsigned long long* toks = g.tokens + static_cast<int64_t>(pos) * g.B;
+        unsigned long long* toks = g.tokens + static_cast<int64_t>(pos) * g.B * kTokenStride;
         for (int64_t b = blockIdx.x; b < g.B; b += G) {   // rows this workgroup reduces
           const unsigned long long t =
-              poll_max(g, pos_slots + b * kChainSlots, 1, static_cast<int>(G), tag, lane);
+              poll_max(g, pos_slots + b * kChainSlots * kSlotStride, kSlotStride,
+                       static_cast<int>(G), tag, lane);
           if (lane == 0) {
             g.draft[b * g.k + pos] = tagged_index(t);
-            publish_u64(toks + b, (t & ~kTagMask) | tag);
+            publish_u64(toks + b * kTokenStride, (t & ~kTagMask) | tag);
           }
         }
         for (int64_t b0 = 0; b0 < g.B; b0 += 64) {
           const int n = static_cast<int>(min<int64_t>(64, g.B - b0));
           unsigned it = 0;
           for (;;) {
-            unsigned long long t = fetch_u64(toks + b0 + (lane < n ? lane : n - 1));
+            unsigned long long t = fetch_u64(toks + (b0 + (lane < n ? lane : n - 1)) * kTokenStride);
             if (__all(lane >= n || (t & kTagMask) == tag)) {
               if (lane < n) ctx[b0 + lane] = tagged_index(t);
               break;
@@ -489,10 +502,10 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
   __syncthreads();
   if (last_flag) {
     const int64_t nslots = static_cast<int64_t>(g.k) * kChainSlots * g.B;
-    for (int64_t i = threadIdx.x; i < nslots; i += blockDim.x) g.slots[i] = 0ull;
+    for (int64_t i = threadIdx.x; i < nslots; i += blockDim.x) g.slots[i * kSlotStride] = 0ull;
     if (!single)
       for (int64_t i = threadIdx.x; i < static_cast<int64_t>(g.k) * g.B; i += blockDim.x)
-        g.tokens[i] = 0ull;
+        g.tokens[i * kTokenStride] = 0ull;
     if (threadIdx.x == 0) *g.done = 0u;
   }
 }

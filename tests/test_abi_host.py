@@ -51,9 +51,10 @@ def test_version(L):
 def test_workspace_sizes(L):
     from block_draft_readout_amd import _abi
     a256 = lambda x: (x + 255) // 256 * 256
-    # per-position keys [k][16 groups][B] | per-workgroup slots [k][256][B] |
-    # tokens [k][B] (all uint64) | a completion-counter block | an error block
-    markov = lambda B, k: a256(8 * 16 * B * k) + a256(8 * 256 * B * k) + a256(8 * B * k) + 256 + 256
+    # per-position keys [k][16 groups][B] | per-workgroup slots [k][256][B]
+    # two words apart | tokens [k][B] one per 128-byte line (all uint64) | a
+    # completion-counter block | an error block
+    markov = lambda B, k: a256(8 * 16 * B * k) + a256(16 * 256 * B * k) + a256(128 * B * k) + 256 + 256
     assert L.dspark_markov_workspace_bytes(16, 8) == markov(16, 8)
     assert L.dspark_markov_workspace_bytes(1, 7) == markov(1, 7)
     V = 151936
@@ -225,7 +226,7 @@ def test_verify_validation(L):
 
 def test_sampling_workspace_sizes(L):
     a256 = lambda x: (x + 255) // 256 * 256
-    markov = lambda B, k: a256(8 * 16 * B * k) + a256(8 * 256 * B * k) + a256(8 * B * k) + 256 + 256
+    markov = lambda B, k: a256(8 * 16 * B * k) + a256(16 * 256 * B * k) + a256(128 * B * k) + 256 + 256
     V = 151936
     # the draw noise [B, k, V] fp32 in front of a greedy Markov workspace
     assert L.dspark_markov_sample_workspace_bytes(1, 7, V) == a256(7 * V * 4) + markov(1, 7)
