@@ -99,6 +99,8 @@ DRAFT_CASES = {
     "no_bias": (3, 5, 4099, 0, "bf16", 2.0, 0.8),
     "f32_r128_passes": (2, 3, 3001, 128, "f32", 2.0, 1.0),   # per-position launches
     "qwen_vocab": (1, 7, 151936, 32, "bf16", 3.0, 1.0),
+    "b1_bf16_r64": (1, 6, 20011, 64, "bf16", 3.0, 1.0),
+    "b1_f32_r48": (1, 6, 20011, 48, "f32", 3.0, 0.8),
     "b16_vocab": (16, 7, 151936, 64, "bf16", 3.0, 0.9),
 }
 

@@ -257,6 +257,22 @@ def test_single_row_chain_ties_and_edges():
         assert np.array_equal(d.cpu().numpy(), np.argmax(Z1, axis=-1))
 
 
+@pytest.mark.parametrize("dtype,r", [("bf16", 64), ("f32", 24), ("f32", 48), ("f32", 64)])
+def test_single_row_chain_ranks(dtype, r):
+    """B = 1 chain with two to four operand chunks of the Markov rank (bf16
+    r = 64; fp32 r = 24, 48, 64) over a ragged vocabulary."""
+    g = np.random.default_rng(r)
+    k, V = 6, 20011
+    Z = (g.standard_normal((1, k, V)) * 3.0).astype(np.float32)
+    w = [(g.standard_normal((V, r)) * 0.4).astype(np.float32) for _ in range(2)]
+    w1, w2 = [synth.store(x, dtype) for x in w]
+    prev = g.integers(0, V, 1).astype(np.int32)
+    d_ref, gap = oracle.semi_ar_argmax(Z, w1, w2, prev, dtype)
+    d = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+    n_cmp, _ = compare_drafts(d, d_ref, gap)
+    assert n_cmp >= 4
+
+
 def test_zero_markov_equals_plain_argmax():
     g = np.random.default_rng(4)
     B, k, V, r = 4, 6, 3001, 32
