@@ -328,8 +328,16 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
         if constexpr (ONE) {
           u32x4_t ef[NC];
           context_frags<S, RKS>(g, r16 == 0 ? ctx[0] : -1, grp, ef);
+          // entries past the workgroup's range or the vocabulary get logit
+          // -inf (their key is -inf or NaN, which never wins), set here while
+          // the context embedding is in flight rather than in the compare loop
+#pragma unroll
+          for (int u = 0; u < MAXT; ++u) {
+            const int tile = cwo + 4 * u;
+            if (!(tile < ntlo && vbo + 16 * tile < V32)) z1[u] = -INFINITY;
+          }
           float bv = -INFINITY;
-          uint32_t bi = 0xFFFFFFFFu;
+          int bu = -1;   // tile slot u of the lane's maximum
           rsrc_t rx;
           if constexpr (SAMPLE)
             rx = make_rsrc(g.xout + static_cast<int64_t>(pos) * g.V, static_cast<uint32_t>(V32) * 4u);
@@ -343,24 +351,24 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
               for (int c = 0; c < RKS; ++c)
                 d = mma16(ef[c], w2s[(tile_rd * RKS + c) * 64 + lane], d, S());
             }
-            const int v = vbo + 16 * tile;
-            const bool ok = tile < ntlo && v < V32;
             const float sv = z1[u] + d[0];
             float key = sv;
             if constexpr (SAMPLE) {
               key = sv * g.inv_t + n1[u];
+              const int v = vbo + 16 * tile;
+              const bool ok = tile < ntlo && v < V32;
               bstore_f32(sv, rx, (ok && grp == 0) ? static_cast<uint32_t>(v) * 4u : kOOB);
             }
-            key = ok ? key : -INFINITY;
             if (key > bv) {
               bv = key;
-              bi = static_cast<uint32_t>(v);
+              bu = u;
             }
           }
           __builtin_amdgcn_sched_barrier(0);
           if (pos + 1 < g.k) load_z1(pos + 1, cwo, ntlo, vbo);
           // the row's maximum over the 16 lanes of grp 0, then over the waves
-          unsigned long long key = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+          unsigned long long key =
+              bu >= 0 ? pack_key(bv, static_cast<uint32_t>(vbo + 16 * (cwo + 4 * bu))) : 0ull;
           key = rowgroup_max16(key);
           if (lane == 0) sk[cw][0][0] = key;
         } else {
