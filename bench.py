@@ -464,8 +464,28 @@ def main():
 
     stream2 = torch.cuda.Stream(dev)          # default priority
     s2ptr = C.c_void_p(stream2.cuda_stream)
-    ev_fork = torch.cuda.Event()
-    ev_join = torch.cuda.Event()
+    # fork / join events for the fc beside the chain: device-side ordering only
+    # (nothing the host reads crosses them), so they are created without the
+    # system-scope fence that a default event record carries (-4 us per step)
+    hip = C.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+    hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+    hip.hipStreamWaitEvent.argtypes = [C.c_void_p, C.c_void_p, C.c_uint]
+    HIP_EVENT_DISABLE_TIMING, HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x2, 0x20000000
+    ev_fork, ev_join = C.c_void_p(), C.c_void_p()
+    for ev in (ev_fork, ev_join):
+        rc = hip.hipEventCreateWithFlags(
+            C.byref(ev), HIP_EVENT_DISABLE_TIMING | HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(ev, stream_ptr):
+        if hip.hipEventRecord(ev, stream_ptr) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def wait(stream_ptr, ev):
+        if hip.hipStreamWaitEvent(stream_ptr, ev, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     loop_state = {"cur": "prev_a"}
     if args.closed_loop:
@@ -491,20 +511,20 @@ def main():
             check(st.markov(), "drafting")
             check(st.verify(), "verification")
             return
-        main = torch.cuda.current_stream(dev)
+        main = C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         fc_ptr = st.fc_stream
         st.fc_stream = s2ptr
         if args.overlap == "chain":
             check(st.lm_head(), "dspark_lm_head")
-        ev_fork.record(main)
-        stream2.wait_event(ev_fork)
+        record(ev_fork, main)
+        wait(s2ptr, ev_fork)
         check(st.fc(), "dflash_fuse_fc")
-        ev_join.record(stream2)
+        record(ev_join, s2ptr)
         if args.overlap == "lm":
             check(st.lm_head(), "dspark_lm_head")
         check(st.markov(), "drafting")
         check(st.verify(), "verification")
-        main.wait_event(ev_join)
+        wait(main, ev_join)
         st.fc_stream = fc_ptr
 
     graphs = None
