@@ -169,6 +169,58 @@ class Step:
                                           b["ws_fcr"], b["ws_fcr_n"], self.stream)
 
 
+_HIP = None
+
+
+def hip_runtime():
+    """The HIP runtime through ctypes (event calls torch does not expose)."""
+    global _HIP
+    if _HIP is None:
+        h = C.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        h.hipStreamWaitEvent.argtypes = [C.c_void_p, C.c_void_p, C.c_uint]
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        _HIP = h
+    return _HIP
+
+
+HIP_EVENT_DISABLE_TIMING = 0x2
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def hip_event(flags):
+    ev = C.c_void_p()
+    rc = hip_runtime().hipEventCreateWithFlags(C.byref(ev), flags)
+    if rc != 0:
+        raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+    return ev
+
+
+class LaunchTimer:
+    """Start/stop HIP events around launches on one stream, created without the
+    system-scope fence, so the stop stamp is not stretched by a flush for host
+    visibility (the default event record adds ~3 us to a 227 us kernel)."""
+
+    def __init__(self, n):
+        self.ev = [(hip_event(HIP_EVENT_DISABLE_SYSTEM_FENCE), hip_event(HIP_EVENT_DISABLE_SYSTEM_FENCE))
+                   for _ in range(n)]
+
+    def start(self, i, stream_ptr):
+        if hip_runtime().hipEventRecord(self.ev[i][0], stream_ptr) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def stop(self, i, stream_ptr):
+        if hip_runtime().hipEventRecord(self.ev[i][1], stream_ptr) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i):
+        out = C.c_float()
+        if hip_runtime().hipEventElapsedTime(C.byref(out), self.ev[i][0], self.ev[i][1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+
 def check(rc, what):
     if rc != 0:
         import block_draft_readout_amd as bdr
@@ -467,17 +519,9 @@ def main():
     # fork / join events for the fc beside the chain: device-side ordering only
     # (nothing the host reads crosses them), so they are created without the
     # system-scope fence that a default event record carries (-4 us per step)
-    hip = C.CDLL("libamdhip64.so")
-    hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
-    hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
-    hip.hipStreamWaitEvent.argtypes = [C.c_void_p, C.c_void_p, C.c_uint]
-    HIP_EVENT_DISABLE_TIMING, HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x2, 0x20000000
-    ev_fork, ev_join = C.c_void_p(), C.c_void_p()
-    for ev in (ev_fork, ev_join):
-        rc = hip.hipEventCreateWithFlags(
-            C.byref(ev), HIP_EVENT_DISABLE_TIMING | HIP_EVENT_DISABLE_SYSTEM_FENCE)
-        if rc != 0:
-            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+    hip = hip_runtime()
+    ev_fork = hip_event(HIP_EVENT_DISABLE_TIMING | HIP_EVENT_DISABLE_SYSTEM_FENCE)
+    ev_join = hip_event(HIP_EVENT_DISABLE_TIMING | HIP_EVENT_DISABLE_SYSTEM_FENCE)
 
     def record(ev, stream_ptr):
         if hip.hipEventRecord(ev, stream_ptr) != 0:
@@ -564,33 +608,32 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
 
     # phase 2: the same steps eagerly, with HIP events around each LM-head launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    sptr_now = C.c_void_p(stream.cuda_stream)
+    lm_t = LaunchTimer(args.steps)
     torch.cuda.synchronize()
     for i in range(args.steps):
         st = slots[i % len(slots)]
         check(st.fc(), "dflash_fuse_fc")
-        evs[i][0].record(stream)
+        lm_t.start(i, sptr_now)
         check(st.lm_head(), "dspark_lm_head")
-        evs[i][1].record(stream)
+        lm_t.stop(i, sptr_now)
         check(st.markov(), "drafting")
         check(st.verify(), "verification")
     torch.cuda.synchronize()
-    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    lm_ms = float(np.mean([lm_t.ms(i) for i in range(args.steps)]))
 
     # phase 3: per-stage times (one stage at a time, events on the launch stream)
     stage_fns = (("fc", "fc"), ("lm_head", "lm_head"), ("markov", "markov"), ("verify", "verify"))
-    sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in stage_fns] for _ in range(args.steps)]
+    st_t = LaunchTimer(args.steps * len(stage_fns))
     torch.cuda.synchronize()
     for i in range(args.steps):
         st = slots[i % len(slots)]
         for j, (_, fn) in enumerate(stage_fns):
-            sev[i][j][0].record(stream)
+            st_t.start(i * len(stage_fns) + j, sptr_now)
             check(getattr(st, fn)(), fn)
-            sev[i][j][1].record(stream)
+            st_t.stop(i * len(stage_fns) + j, sptr_now)
     torch.cuda.synchronize()
-    stages_us = {name: round(float(np.mean([sev[i][j][0].elapsed_time(sev[i][j][1])
+    stages_us = {name: round(float(np.mean([st_t.ms(i * len(stage_fns) + j)
                                             for i in range(args.steps)])) * 1e3, 1)
                  for j, (name, _) in enumerate(stage_fns)}
     log(f"stages (us): {stages_us}")
