@@ -375,33 +375,40 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
           u32x4_t ef[NC];
           context_frags<S, RKS>(g, b0 + r16 < g.B ? ctx[b0 + r16] : -1, grp, ef);
+          // entries past the workgroup's range or the vocabulary get logit
+          // -inf (never winning), set while the context embeddings are in
+          // flight; rows past the batch are never published and need no mask
+#pragma unroll
+          for (int u = 0; u < MAXT; ++u) {
+            const int tile = cwo + 4 * u;
+            const int lim = tile < ntlo ? V32 - (vbo + 16 * tile) : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (!(i < lim)) zv[u][i] = 0xFF800000u;
+          }
           // bias tile D[vocab 4 * grp + i][row r16] = markov_w2 rows x context
           // embeddings; each lane keeps the running maximum of its row r16 over
-          // the entries it visits in increasing order.  Reads past the
-          // workgroup's last tile repeat it (no branch) and are masked.
+          // the entries it visits in increasing order (bs: slot 4 u + i of it).
+          // Reads past the workgroup's last tile repeat it (no branch).
           float bv = -INFINITY;
-          uint32_t bi = 0xFFFFFFFFu;
+          int bs = -1;
           const bool row_ok = r16 < nb;
           rsrc_t rx;
           f32x4_t xt = {0.f, 0.f, 0.f, 0.f};
           uint32_t toff = kOOB;
           if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, block_bytes(b0));
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < MAXT; ++u) {
             const int tile = cwo + 4 * u;
             const int tile_rd = tile < ntlo ? tile : ntlo - 1;
             f32x4_t bias = {0.f, 0.f, 0.f, 0.f};
             if constexpr (RKS > 0) {
-  #pragma unroll
+#pragma unroll
               for (int c = 0; c < RKS; ++c)
                 bias = mma16(w2s[(tile_rd * RKS + c) * 64 + lane], ef[c], bias, S());
             }
-            const int v0 = vbo + 16 * tile;
-            // entries of the lane's quad that exist (<= 0: none); a missing
-            // entry's key is -inf and never wins
-            const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
             f32x4_t xs;
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float s = __uint_as_float(zv[u][i]) + bias[i];
               float key = s;
@@ -409,13 +416,15 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
                 xs[i] = s;
                 key = s * g.inv_t + __uint_as_float(gv[u][i]);
               }
-              key = i < lim ? key : -INFINITY;
               if (key > bv) {
                 bv = key;
-                bi = static_cast<uint32_t>(v0 + i);
+                bs = 4 * u + i;
               }
             }
             if constexpr (SAMPLE) {
+              // entries of the lane's quad that exist (<= 0: none)
+              const int v0 = vbo + 16 * tile;
+              const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
               // x of the lane's four entries in one 16-byte store; the quad that
               // straddles the end of the row (at most one per lane) is kept for
               // element stores after the loop
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           if constexpr (SAMPLE) {
             const int tn = V32 & 3;   // entries of a straddling quad
             if (toff != kOOB) {
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 3; ++i) bstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
             }
           }
@@ -438,7 +447,9 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           __builtin_amdgcn_sched_barrier(0);
           if (last_group && pos + 1 < g.k) load_z(pos + 1, 0, cwo, ntlo, vbo);
           // row r16's maximum over the lane groups and waves, taken from LDS
-          sk[cw][grp][r16] = bi != 0xFFFFFFFFu ? pack_key(bv, bi) : 0ull;
+          sk[cw][grp][r16] =
+              bs >= 0 ? pack_key(bv, static_cast<uint32_t>(vbo + 16 * (cwo + 4 * (bs >> 2)) + (bs & 3)))
+                      : 0ull;
         }
       }
       BDR_LDS_BARRIER();
