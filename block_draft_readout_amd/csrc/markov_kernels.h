@@ -290,6 +290,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
   // logit and noise of each of its tiles.
   float z1[ONE ? MAXT : 1];
   float n1[ONE && SAMPLE ? MAXT : 1];
+  uint32_t x1[ONE && SAMPLE ? MAXT : 1];   // where the lane stores x of the entry (kOOB: nowhere)
   const int vbase1 = static_cast<int>(t_lo) * 16 + r16;   // + 16 * tile
   auto load_z1 = [&](int pos, int cwo, int ntlo, int vbo) {
     const int64_t first = static_cast<int64_t>(pos) * g.V;
@@ -303,7 +304,10 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
       const int v = vbo + 16 * tile;
       const uint32_t off = (grp == 0 && tile < ntlo && v < V32) ? static_cast<uint32_t>(v) * 4u : kOOB;
       z1[u] = bload_f32(rz, off);
-      if constexpr (SAMPLE) n1[u] = bload_f32(rg, off);
+      if constexpr (SAMPLE) {
+        n1[u] = bload_f32(rg, off);
+        x1[u] = off;
+      }
     }
   };
   if (cw >= 0) {
@@ -355,9 +359,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
             float key = sv;
             if constexpr (SAMPLE) {
               key = sv * g.inv_t + n1[u];
-              const int v = vbo + 16 * tile;
-              const bool ok = tile < ntlo && v < V32;
-              bstore_f32(sv, rx, (ok && grp == 0) ? static_cast<uint32_t>(v) * 4u : kOOB);
+              bstore_f32(sv, rx, x1[u]);
             }
             if (key > bv) {
               bv = key;
