@@ -298,3 +298,46 @@ def test_end_to_end_block_matches_oracle_on_gpu_draft():
     assert clean.sum() >= B - 1
     assert np.array_equal(out["accepted"].cpu().numpy()[clean], ref["accepted"][clean])
     assert np.array_equal(out["bonus"].cpu().numpy()[clean], ref["bonus"][clean])
+
+
+# ----------------------------------------------------------------------------- randomized shapes
+def _random_shapes(n, seed):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(g.choice([1, 1, 2, 3, 5, 16, 17, 33]))
+        k = int(g.integers(1, 17))
+        V = int(g.integers(16, 9000))
+        dtype = str(g.choice(["bf16", "f32"]))
+        r = int(g.choice([0, 8, 16, 32, 48, 64])) if dtype == "f32" else int(g.choice([0, 8, 32, 64]))
+        out.append((B, k, V, r, dtype))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(12, 2026))
+def test_chain_random_shapes(shape):
+    """Greedy and sampled drafts over seeded random shapes (batch 1 to 33, k 1
+    to 16, ragged vocabularies, ranks 0 to 64, both dtypes) against the
+    oracle, through the first near-tie of each row."""
+    B, k, V, r, dtype = shape
+    cid = 300 + B * 7 + k * 13 + V % 97
+    Z = _logits(cid, B, k, V, 3.0)
+    w1, w2 = _markov(cid, V, r, dtype) if r else (None, None)
+    prev = np.random.default_rng(cid).integers(0, V, B).astype(np.int32)
+    log(f"random chain B={B} k={k} V={V} r={r} {dtype}")
+    d_ref, gap = oracle.semi_ar_argmax(Z, w1, w2, prev, dtype)
+    d = bdr().dspark_markov_argmax(dev(Z), dev(w1) if r else None, dev(w2) if r else None,
+                                   dev(prev)).cpu().numpy()
+    istar = first_near_tie(gap)
+    for b in range(B):
+        m = int(istar[b])
+        assert np.array_equal(d[b, :m], d_ref[b, :m]), (b, d[b], d_ref[b], gap[b])
+    T, seed = 0.9, 4000 + cid
+    ds_ref, sgap, _ = S.semi_ar_sample(Z, w1, w2, prev, dtype, T, seed)
+    ds, _ = bdr().dspark_markov_sample(dev(Z), dev(w1) if r else None, dev(w2) if r else None,
+                                       dev(prev), T, seed)
+    ds = ds.cpu().numpy()
+    istar = first_near_tie(sgap)
+    for b in range(B):
+        m = int(istar[b])
+        assert np.array_equal(ds[b, :m], ds_ref[b, :m]), (b, ds[b], ds_ref[b], sgap[b])
