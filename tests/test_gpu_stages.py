@@ -461,3 +461,41 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
     # counts: eager once + warm-up + 4 replays + 4 eager = 10 accumulations
     assert torch.equal(acc, acc_eager * 10)
+
+
+def _verify_random_shapes(n, seed):
+    g = np.random.default_rng(seed)
+    return [(int(g.choice([1, 2, 3, 8, 16, 17, 40])), int(g.integers(1, 17)), int(g.integers(8, 20000)),
+             str(g.choice(["bf16", "f32"])), bool(g.integers(0, 2))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("shape", _verify_random_shapes(12, 77))
+def test_verify_random_shapes(shape):
+    """Greedy verification over seeded random shapes (batch 1 to 40, k 1 to 16,
+    ragged vocabularies, bf16 and fp32 targets, with and without confidence
+    truncation), drafts planted to match the target on a random prefix:
+    block lengths, accepted counts, bonus tokens, target argmaxes and counts
+    bit-exact against the oracle."""
+    B, k, V, dtype, use_conf = shape
+    g = np.random.default_rng(B * 1000 + k * 37 + V)
+    Y = synth.store((g.standard_normal((B, k + 1, V)) * 2.0).astype(np.float32), dtype)
+    t_all = oracle.target_argmax(Y, dtype, np.full(B, k))
+    d = g.integers(0, V, (B, k)).astype(np.int32)
+    for b in range(B):
+        m = int(g.integers(0, k + 1))
+        d[b, :m] = t_all[b, :m]
+    conf = g.uniform(0.0, 1.0, (B, k)).astype(np.float32) if use_conf else None
+    th = 0.2 if use_conf else None
+    L = oracle.truncate_by_confidence(conf, th, B, k)
+    t = oracle.target_argmax(Y, dtype, L)
+    a, bonus, acc, prop = oracle.verify_greedy(d, t, L)
+    accd = torch.zeros(k, dtype=torch.int64, device="cuda")
+    propd = torch.zeros(k, dtype=torch.int64, device="cuda")
+    r = bdr().spec_verify_greedy(dev(Y), dev(d), None if conf is None else dev(conf),
+                                 math.nan if th is None else th, accd, propd)
+    log(f"verify B={B} k={k} V={V} {dtype} conf={use_conf}: accepted {int(a.sum())}")
+    assert np.array_equal(r["block_len"].cpu().numpy(), L)
+    assert np.array_equal(r["target_argmax"].cpu().numpy(), t)
+    assert np.array_equal(r["accepted"].cpu().numpy(), a)
+    assert np.array_equal(r["bonus"].cpu().numpy(), bonus)
+    assert np.array_equal(accd.cpu().numpy(), acc) and np.array_equal(propd.cpu().numpy(), prop)
