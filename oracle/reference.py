@@ -218,6 +218,52 @@ def semi_ar_argmax(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndar
     return d, gap
 
 
+def score_draft(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndarray],
+                prev0: np.ndarray, draft: np.ndarray, dtype: str):
+    """Position-by-position check of a GIVEN draft block against the chain's rule.
+
+    The chain conditions position i on the biased prediction made at position
+    i-1 (llm-scaler PR #620, DSpark port notes, _greedy_sample), and position 0
+    on the accepted bonus token.  Here that previous prediction is the given
+    draft's own token, whatever it is, so a block that took the other side of a
+    near-tie can still be checked at every later position.  For each (b, i),
+    with context c = prev0[b] (i = 0) or draft[b, i-1]:
+      s      = float32(Z[b, i] + bias(c))       (as in semi_ar_argmax)
+      best   = lowest-index argmax of s
+      gap    = top-2 gap of s
+      deficit = max(s) - s[draft[b, i]]          (inf for a token outside [0, V))
+    A draft is the chain's exact result iff every deficit is 0 and the draft
+    token is ``best`` everywhere.  A context outside [0, V) contributes no bias
+    (the chain it came from has already failed its check at that position).
+    """
+    Z = np.asarray(Z, dtype=np.float32)
+    B, k, V = Z.shape
+    draft = np.asarray(draft, dtype=np.int64).reshape(B, k)
+    prev0 = np.asarray(prev0).reshape(B)
+    use_bias = w1 is not None and w2 is not None and np.shape(w1)[-1] > 0
+    if use_bias:
+        W1 = widen(w1, dtype)
+        W2 = widen(w2, dtype)
+        if W1.shape != W2.shape or W1.shape[0] != V:
+            raise ValueError("markov weights must both be [V, r]")
+    best = np.zeros((B, k), dtype=np.int64)
+    gap = np.zeros((B, k), dtype=np.float64)
+    deficit = np.zeros((B, k), dtype=np.float64)
+    for b in range(B):
+        p = int(prev0[b])
+        for i in range(k):
+            if use_bias and 0 <= p < V:
+                s = Z[b, i] + markov_bias(W1, W2, p)
+            else:
+                s = Z[b, i].copy()
+            best[b, i] = first_argmax(s)
+            gap[b, i] = top2_gap(s)
+            g = int(draft[b, i])
+            deficit[b, i] = (float(s.max()) - float(s[g])) if 0 <= g < V else float("inf")
+            p = g
+    return best, gap, deficit
+
+
 # ----------------------------------------------------------------------------
 # S4: greedy exact-match verification
 # ----------------------------------------------------------------------------

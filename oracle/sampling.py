@@ -163,9 +163,81 @@ def semi_ar_sample(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndar
     return d, gap, x
 
 
+def score_sampled_draft(Z: np.ndarray, w1: Optional[np.ndarray], w2: Optional[np.ndarray],
+                        prev0: np.ndarray, draft: np.ndarray, dtype: str, temperature: float,
+                        seed: int):
+    """Position-by-position check of a GIVEN sampled draft block.
+
+    As ``semi_ar_sample``, except that the context of position i is the given
+    draft's token at i-1 (prev0 at i = 0) -- each position is conditioned on the
+    token actually drawn before it (llm-scaler PR #620, DSpark port notes).
+    Returns, per (b, i): the Gumbel-max draw under that context, the gap between
+    the two largest keys x/T + G, the key deficit max(keys) - keys[draft[b, i]]
+    (inf for a token outside [0, V)), and the biased logits x under that context.
+    """
+    if not temperature > 0:
+        raise ValueError("temperature must be positive")
+    Z = np.asarray(Z, dtype=np.float32)
+    B, k, V = Z.shape
+    draft = np.asarray(draft, dtype=np.int64).reshape(B, k)
+    prev0 = np.asarray(prev0).reshape(B)
+    use_bias = w1 is not None and w2 is not None and np.shape(w1)[-1] > 0
+    if use_bias:
+        W1, W2 = widen(w1, dtype), widen(w2, dtype)
+    best = np.zeros((B, k), dtype=np.int64)
+    gap = np.zeros((B, k), dtype=np.float64)
+    deficit = np.zeros((B, k), dtype=np.float64)
+    x = np.zeros((B, k, V), dtype=np.float32)
+    for b in range(B):
+        p = int(prev0[b])
+        for i in range(k):
+            s = Z[b, i] + markov_bias(W1, W2, p) if (use_bias and 0 <= p < V) else Z[b, i].copy()
+            _finite(s, "biased logits")
+            x[b, i] = s
+            u = uniforms(seed, STREAM_DRAFT, b, i, V)
+            keys = s.astype(np.float64) / temperature + gumbel(u)
+            best[b, i], gap[b, i] = gumbel_max(s.astype(np.float64) / temperature, u)
+            g = int(draft[b, i])
+            deficit[b, i] = float(keys.max() - keys[g]) if 0 <= g < V else float("inf")
+            p = g
+    return best, gap, deficit, x
+
+
 # ----------------------------------------------------------------------------
 # S4 (probabilistic): rejection-sampling verification
 # ----------------------------------------------------------------------------
+
+def _accept_test(d_bn: int, x_bn: np.ndarray, y_bn: np.ndarray, dtype: str, temperature: float,
+                 seed: int, b: int, n: int):
+    """The acceptance test of draft token d_bn at row b, position n: with r the
+    uniform of stream STREAM_ACCEPT, accept iff r * q(d) < p(d).  Returns
+    (accepted, margin |r q - p| / max(p, q)); a token outside [0, V) is rejected
+    (it has no probability under p)."""
+    V = np.shape(y_bn)[-1]
+    if not 0 <= d_bn < V:
+        return False, float("inf")
+    lp = log_softmax(widen(y_bn, dtype) / temperature)
+    lq = log_softmax(np.asarray(x_bn, dtype=np.float64) / temperature)
+    pd, qd = np.exp(lp[d_bn]), np.exp(lq[d_bn])
+    r = uniforms(seed, STREAM_ACCEPT, b, n, 1)[0]
+    return bool(r * qd < pd), float(abs(r * qd - pd) / max(pd, qd))
+
+
+def _final_logw(x_bn: Optional[np.ndarray], y_bn: np.ndarray, dtype: str, temperature: float,
+                rejected: bool) -> np.ndarray:
+    """Log-weights of the draw that ends a row: after a rejection the residual
+    max(0, p - q) (from p when it is zero everywhere); after a full block the
+    target distribution p itself (unnormalised log-weights y / T)."""
+    if not rejected:
+        return widen(y_bn, dtype) / temperature
+    lp = log_softmax(widen(y_bn, dtype) / temperature)
+    lq = log_softmax(np.asarray(x_bn, dtype=np.float64) / temperature)
+    w = np.maximum(np.exp(lp) - np.exp(lq), 0.0)
+    if w.max() > 0:
+        with np.errstate(divide="ignore"):
+            return np.log(w)          # log 0 = -inf: never drawn
+    return lp
+
 
 def verify_sample(d: np.ndarray, x: np.ndarray, Y: np.ndarray, dtype: str, L: np.ndarray,
                   temperature: float, seed: int):
@@ -201,34 +273,67 @@ def verify_sample(d: np.ndarray, x: np.ndarray, Y: np.ndarray, dtype: str, L: np
         Lb = int(L[b])
         n = 0
         while n < Lb:
-            lp = log_softmax(widen(Y[b, n], dtype) / temperature)
-            lq = log_softmax(np.asarray(x[b, n], dtype=np.float64) / temperature)
-            pd, qd = np.exp(lp[d[b, n]]), np.exp(lq[d[b, n]])
-            r = uniforms(seed, STREAM_ACCEPT, b, n, 1)[0]
-            margin[b, n] = abs(r * qd - pd) / max(pd, qd)
-            if r * qd < pd:
-                n += 1
-                continue
-            w = np.maximum(np.exp(lp) - np.exp(lq), 0.0)
-            if w.max() > 0:
-                with np.errstate(divide="ignore"):
-                    logw = np.log(w)          # log 0 = -inf: never drawn
-            else:
-                logw = lp
-            u = uniforms(seed, STREAM_RESAMPLE, b, n, V)
-            bonus[b], draw_gap[b] = gumbel_max(logw, u)
-            resampled[b] = True
-            break
+            ok, margin[b, n] = _accept_test(int(d[b, n]), x[b, n], Y[b, n], dtype, temperature,
+                                            seed, b, n)
+            if not ok:
+                resampled[b] = True
+                break
+            n += 1
         a[b] = n
-        if not resampled[b]:
-            lp = widen(Y[b, Lb], dtype) / temperature
-            u = uniforms(seed, STREAM_RESAMPLE, b, Lb, V)
-            bonus[b], draw_gap[b] = gumbel_max(lp, u)
+        logw = _final_logw(x[b, n] if resampled[b] else None, Y[b, n], dtype, temperature,
+                           bool(resampled[b]))
+        bonus[b], draw_gap[b] = gumbel_max(logw, uniforms(seed, STREAM_RESAMPLE, b, n, V))
         for i in range(k):
             acc[i] += n > i
             prop[i] += Lb > i
     return dict(accepted=a, bonus=bonus, accept_counts=acc, proposed_counts=prop,
                 margin=margin, draw_gap=draw_gap, resampled=resampled)
+
+
+def verify_sample_outcome(d: np.ndarray, x: np.ndarray, Y: np.ndarray, dtype: str,
+                          L: np.ndarray, temperature: float, seed: int,
+                          accepted: np.ndarray, bonus: np.ndarray):
+    """The rule's verdict on a GIVEN outcome (accepted a_b, bonus token) per row.
+
+    The rule's decisions along the path that outcome takes (same tests and draws
+    as ``verify_sample``): the acceptance test at every position n <= a_b with
+    n < L_b (``decision``: the rule's accept/reject there, ``margin``: how far
+    from its threshold; inf where untested), then the draw that ends the row --
+    the residual draw at a_b after a rejection (a_b < L_b) or the bonus draw from
+    p_{L_b} after a full block -- with the rule's token ``draw``, its top-2 key
+    gap ``draw_gap`` and ``bonus_deficit`` = max(keys) - keys[bonus_b] (inf for a
+    token with no weight or outside [0, V)).  The given outcome is the rule's
+    exact result iff every tested decision agrees with it (accept below a_b,
+    reject at a_b < L_b) and bonus_b = draw.  Rows with a_b outside [0, L_b] get
+    ``valid`` False.
+    """
+    d = np.asarray(d, dtype=np.int64)
+    B, k = d.shape
+    V = np.shape(Y)[-1]
+    decision = np.zeros((B, k), dtype=bool)
+    margin = np.full((B, k), np.inf)
+    draw = np.zeros(B, dtype=np.int64)
+    draw_gap = np.zeros(B)
+    deficit = np.zeros(B)
+    valid = np.ones(B, dtype=bool)
+    for b in range(B):
+        Lb, ab = int(L[b]), int(accepted[b])
+        if not 0 <= ab <= Lb:
+            valid[b] = False
+            continue
+        for n in range(min(ab + 1, Lb)):
+            decision[b, n], margin[b, n] = _accept_test(int(d[b, n]), x[b, n], Y[b, n], dtype,
+                                                        temperature, seed, b, n)
+        rejected = ab < Lb
+        logw = _final_logw(x[b, ab] if rejected else None, Y[b, ab], dtype, temperature, rejected)
+        u = uniforms(seed, STREAM_RESAMPLE, b, ab, V)
+        draw[b], draw_gap[b] = gumbel_max(logw, u)
+        keys = np.where(np.isneginf(logw), -np.inf, logw + gumbel(u))
+        g = int(bonus[b])
+        deficit[b] = float(keys.max() - keys[g]) if (0 <= g < V and np.isfinite(keys[g])) \
+            else float("inf")
+    return dict(decision=decision, margin=margin, draw=draw, draw_gap=draw_gap,
+                bonus_deficit=deficit, valid=valid)
 
 
 def block_step_sample(dtype: str, Z, w1, w2, prev0, target_logits, temperature: float,

@@ -1,5 +1,7 @@
 """Helpers of the GPU parity tests: device transfer, the error metric, the
-near-tie exclusion cascade, and cached per-workload oracle results."""
+position-by-position checks of GPU drafts and sampling outcomes against the
+oracle's rule (admissible picks at near-ties), and cached per-workload oracle
+results."""
 from __future__ import annotations
 
 import functools
@@ -61,17 +63,85 @@ def first_near_tie(gap: np.ndarray, thr: float = NEAR_TIE) -> np.ndarray:
     return out
 
 
-def compare_drafts(got: np.ndarray, ref: np.ndarray, gap: np.ndarray):
-    """Bit-exact comparison of draft tokens at positions before each row's first
-    near-tie; returns (n_compared, n_excluded)."""
-    istar = first_near_tie(gap)
-    B, k = ref.shape
-    n_cmp = 0
+def check_draft(got: np.ndarray, Z, w1, w2, prev0, dtype: str) -> dict:
+    """Every position of a GPU greedy draft against the oracle's rule.
+
+    Each position's Markov context is the GPU's own previous token (prev0 at
+    position 0), as the chain defines it, so a block that took the other side
+    of a near-tie is still checked at every later position.  Where the oracle's
+    top-2 gap under that context is >= NEAR_TIE the token must be the oracle's
+    argmax bit for bit; below it the GPU's token must be an admissible pick,
+    within NEAR_TIE of the maximum of the oracle's biased logits.
+    """
+    got = np.asarray(got).astype(np.int64)
+    best, gap, deficit = oracle.score_draft(Z, w1, w2, prev0, got, dtype)
+    clear = gap >= NEAR_TIE
+    bad = np.argwhere(clear & (got != best))
+    assert bad.size == 0, ("draft token differs at a clear position", bad[:4].tolist(),
+                           [(int(got[b, i]), int(best[b, i]), float(gap[b, i])) for b, i in bad[:4]])
+    near = ~clear
+    assert np.all(deficit[near] <= NEAR_TIE), ("inadmissible pick at a near-tie",
+                                                np.argwhere(near & (deficit > NEAR_TIE))[:4].tolist())
+    return dict(n=int(got.size), exact=int(clear.sum()), near=int(near.sum()),
+                other_side=int(np.sum(near & (got != best))),
+                max_near_deficit=float(deficit[near].max()) if near.any() else 0.0)
+
+
+def check_sampled_draft(got: np.ndarray, x_got, Z, w1, w2, prev0, dtype: str, T: float,
+                        seed: int) -> dict:
+    """Every position of a GPU sampled draft against the oracle's rule, each
+    position's context being the GPU's own previous draw: the draw bit for bit
+    where the oracle's top-2 Gumbel-key gap is >= NEAR_TIE, otherwise a key
+    within NEAR_TIE of the maximum; the written draft distribution (biased
+    logits under those contexts) within 1e-4 (1 + |x|)."""
+    from oracle import sampling as S
+    got = np.asarray(got).astype(np.int64)
+    best, gap, deficit, x = S.score_sampled_draft(Z, w1, w2, prev0, got, dtype, T, seed)
+    clear = gap >= NEAR_TIE
+    bad = np.argwhere(clear & (got != best))
+    assert bad.size == 0, ("sampled token differs at a clear position", bad[:4].tolist())
+    near = ~clear
+    assert np.all(deficit[near] <= NEAR_TIE), ("inadmissible draw at a near-tie",
+                                                np.argwhere(near & (deficit > NEAR_TIE))[:4].tolist())
+    if x_got is not None:
+        diff = np.abs(np.asarray(x_got, dtype=np.float64) - x)
+        assert np.all(diff <= 1e-4 * (1 + np.abs(x))), float(diff.max())
+    return dict(n=int(got.size), exact=int(clear.sum()), near=int(near.sum()),
+                other_side=int(np.sum(near & (got != best))))
+
+
+MARGIN_TOL = 1e-3
+
+
+def check_verify_sample(accepted, bonus, d, x, Y, dtype: str, L, T: float, seed: int) -> dict:
+    """A GPU rejection-sampling outcome (accepted, bonus per row) against the
+    oracle's rule along the path that outcome takes: every acceptance test
+    below a_b must accept and the test at a_b < L_b must reject, unless the
+    oracle's margin |r q - p| / max(p, q) there is below MARGIN_TOL (then
+    either outcome is admissible); the bonus must be the oracle's draw at the
+    end of that path, or within NEAR_TIE of its maximum key where the oracle's
+    draw gap is below NEAR_TIE.  Returns counts of the decisions taken at a
+    near-tie."""
+    from oracle import sampling as S
+    accepted = np.asarray(accepted).astype(np.int64)
+    bonus = np.asarray(bonus).astype(np.int64)
+    o = S.verify_sample_outcome(d, x, Y, dtype, L, T, seed, accepted, bonus)
+    assert o["valid"].all(), np.flatnonzero(~o["valid"]).tolist()
+    B = accepted.shape[0]
+    near_tests = near_draws = 0
     for b in range(B):
-        m = int(istar[b])
-        assert np.array_equal(got[b, :m], ref[b, :m]), (b, got[b], ref[b], gap[b])
-        n_cmp += m
-    return n_cmp, B * k - n_cmp
+        a, Lb = int(accepted[b]), int(L[b])
+        for n in range(min(a + 1, Lb)):
+            want = n < a
+            if bool(o["decision"][b, n]) != want:
+                assert o["margin"][b, n] < MARGIN_TOL, ("acceptance decision", b, n,
+                                                        float(o["margin"][b, n]))
+                near_tests += 1
+        if int(o["draw"][b]) != int(bonus[b]):
+            assert o["draw_gap"][b] < NEAR_TIE and o["bonus_deficit"][b] <= NEAR_TIE, (
+                "bonus draw", b, int(bonus[b]), int(o["draw"][b]), float(o["draw_gap"][b]))
+            near_draws += 1
+    return dict(rows=B, near_tests=near_tests, near_draws=near_draws)
 
 
 @functools.lru_cache(maxsize=2)
