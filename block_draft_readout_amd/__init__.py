@@ -23,7 +23,7 @@ __all__ = [
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
     "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
-    "workspace_bytes", "lib", "BdrError",
+    "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us", "MARKOV_TIMED_OUT",
 ]
 
 
@@ -232,6 +232,34 @@ def dspark_lm_head_fp8(hidden: torch.Tensor, lm_head_q: torch.Tensor, lm_head_sc
 
 
 # ----------------------------------------------------------------------------- S3
+# BdrError code of a Markov call whose status word reports a wait that gave up
+MARKOV_TIMED_OUT = -5
+
+
+def _status_in(status: Optional[torch.Tensor], check: bool, device) -> Optional[torch.Tensor]:
+    if status is not None:
+        _dev(status, "status")
+        if status.dtype != torch.int32 or status.numel() < 1:
+            raise ValueError("status must be an int32 device tensor")
+        return status
+    return torch.empty(1, dtype=torch.int32, device=device) if check else None
+
+
+def _status_out(fn: str, status: Optional[torch.Tensor], check: bool) -> None:
+    """With check: wait for the call and raise if one of its bounded waits gave up."""
+    if check and status is not None and int(status.view(-1)[0].item()) != 0:
+        raise BdrError(fn, MARKOV_TIMED_OUT,
+                       "a bounded wait of the persistent Markov chain gave up (its workgroups "
+                       "were not all resident, e.g. beside another chain launch); the draft "
+                       "is invalid")
+
+
+def set_markov_poll_timeout_us(us: float) -> None:
+    """Process-wide limit of the Markov chain's bounded waits for later launches
+    (negative: the default)."""
+    lib().bdr_set_markov_poll_timeout_us(float(us))
+
+
 def _markov_args(w1, w2, dt_ref):
     if w1 is None and w2 is None:
         return None, None, 0
@@ -245,8 +273,14 @@ def _markov_args(w1, w2, dt_ref):
 def dspark_markov_argmax(logits: torch.Tensor, markov_w1: Optional[torch.Tensor],
                          markov_w2: Optional[torch.Tensor], prev_token: torch.Tensor,
                          draft_tokens: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Draft tokens [B, k] (int32) from fp32 logits [B, k, V] and the Markov head."""
+                         workspace: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None,
+                         check: bool = True) -> torch.Tensor:
+    """Draft tokens [B, k] (int32) from fp32 logits [B, k, V] and the Markov head.
+
+    ``status`` (int32 device tensor) receives the call's status word; with
+    ``check`` (default) the call is waited for and BdrError is raised when one
+    of the chain's bounded waits gave up."""
     L = lib()
     _dev(logits, "logits")
     if logits.dtype != torch.float32 or logits.dim() != 3:
@@ -262,10 +296,12 @@ def dspark_markov_argmax(logits: torch.Tensor, markov_w1: Optional[torch.Tensor]
     _dev(draft_tokens, "draft_tokens")
     ws = _workspace(L.dspark_markov_workspace_bytes(B, k), logits.device, workspace)
     wp, wn = _ws_ptr(ws)
+    st = _status_in(status, check, logits.device)
     _abi.check("dspark_markov_argmax",
                L.dspark_markov_argmax(_ptr(logits), B, k, V, wdt, _ptr(w1), _ptr(w2), r,
-                                      _ptr(prev_token), _ptr(draft_tokens), wp, wn,
+                                      _ptr(prev_token), _ptr(draft_tokens), _ptr(st), wp, wn,
                                       _stream(logits.device)))
+    _status_out("dspark_markov_argmax", st, check and B > 0)
     return draft_tokens
 
 
@@ -274,8 +310,11 @@ def dspark_draft_block(draft_hidden: torch.Tensor, lm_head_w: torch.Tensor,
                        markov_w1: Optional[torch.Tensor], markov_w2: Optional[torch.Tensor],
                        prev_token: torch.Tensor, draft_tokens: Optional[torch.Tensor] = None,
                        logits_out: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Draft one block: LM head over draft_hidden [B, k, H], then the Markov argmax chain."""
+                       workspace: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None,
+                       check: bool = True) -> torch.Tensor:
+    """Draft one block: LM head over draft_hidden [B, k, H], then the Markov argmax chain
+    (``status`` / ``check`` as in dspark_markov_argmax)."""
     L = lib()
     _dev(draft_hidden, "draft_hidden")
     _dev(lm_head_w, "lm_head_w")
@@ -297,11 +336,13 @@ def dspark_draft_block(draft_hidden: torch.Tensor, lm_head_w: torch.Tensor,
     need = L.dspark_draft_workspace_bytes(B, k, V, int(logits_out is None))
     ws = _workspace(need, draft_hidden.device, workspace)
     wp, wn = _ws_ptr(ws)
+    st = _status_in(status, check, draft_hidden.device)
     _abi.check("dspark_draft_block",
                L.dspark_draft_block(_ptr(draft_hidden), B, k, H, V, _dt(lm_head_w),
                                     _ptr(lm_head_w), _ptr(w1), _ptr(w2), r, _ptr(prev_token),
-                                    _ptr(draft_tokens), _ptr(logits_out), wp, wn,
+                                    _ptr(draft_tokens), _ptr(logits_out), _ptr(st), wp, wn,
                                     _stream(draft_hidden.device)))
+    _status_out("dspark_draft_block", st, check and B > 0)
     return draft_tokens
 
 
@@ -376,8 +417,11 @@ def dspark_markov_sample(logits: torch.Tensor, markov_w1: Optional[torch.Tensor]
                          temperature: float, seed: int,
                          draft_tokens: Optional[torch.Tensor] = None,
                          draft_logits: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None):
-    """Probabilistic drafting: (draft_tokens [B, k] int32, draft_logits [B, k, V] fp32).
+                         workspace: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None,
+                         check: bool = True):
+    """Probabilistic drafting: (draft_tokens [B, k] int32, draft_logits [B, k, V] fp32)
+    (``status`` / ``check`` as in dspark_markov_argmax).
 
     Each position's token is drawn from softmax((logits + Markov bias) / T) and
     becomes the next position's Markov context; draft_logits holds the biased
@@ -401,11 +445,13 @@ def dspark_markov_sample(logits: torch.Tensor, markov_w1: Optional[torch.Tensor]
     _dev(draft_logits, "draft_logits")
     ws = _workspace(L.dspark_markov_sample_workspace_bytes(B, k, V), logits.device, workspace)
     wp, wn = _ws_ptr(ws)
+    st = _status_in(status, check, logits.device)
     _abi.check("dspark_markov_sample",
                L.dspark_markov_sample(_ptr(logits), B, k, V, wdt, _ptr(w1), _ptr(w2), r,
                                       _ptr(prev_token), float(temperature), int(seed),
-                                      _ptr(draft_tokens), _ptr(draft_logits), wp, wn,
+                                      _ptr(draft_tokens), _ptr(draft_logits), _ptr(st), wp, wn,
                                       _stream(logits.device)))
+    _status_out("dspark_markov_sample", st, check and B > 0)
     return draft_tokens, draft_logits
 
 

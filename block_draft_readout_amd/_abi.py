@@ -30,6 +30,7 @@ _u64 = C.c_uint64
 SIGNATURES = {
     "bdr_abi_version": (_int, []),
     "bdr_last_error": (C.c_char_p, []),
+    "bdr_set_markov_poll_timeout_us": (None, [C.c_double]),
     "dflash_fuse_fc_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
     "dflash_fuse_fc": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
     "dspark_lm_head": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
@@ -43,17 +44,17 @@ SIGNATURES = {
     "dspark_lm_head_fp8": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "dspark_markov_workspace_bytes": (_sz, [_i64, _int]),
     "dspark_markov_argmax": (_int, [_vp, _i64, _int, _i64, _int, _vp, _vp, _int, _vp, _vp,
-                                    _vp, _sz, _vp]),
+                                    _vp, _vp, _sz, _vp]),
     "dspark_draft_workspace_bytes": (_sz, [_i64, _int, _i64, _int]),
     "dspark_draft_block": (_int, [_vp, _i64, _int, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp,
-                                  _vp, _vp, _vp, _sz, _vp]),
+                                  _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "spec_verify_greedy": (_int, [_vp, _int, _i64, _int, _i64, _vp, _vp, C.c_float, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "dspark_gumbel_noise": (_int, [_i64, _int, _i64, _u64, _int, _vp, _vp]),
     "dspark_markov_sample_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "dspark_markov_sample": (_int, [_vp, _i64, _int, _i64, _int, _vp, _vp, _int, _vp, C.c_float,
-                                    _u64, _vp, _vp, _vp, _sz, _vp]),
+                                    _u64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "spec_verify_sample": (_int, [_vp, _int, _i64, _int, _i64, _vp, _vp, _vp, C.c_float,
                                   C.c_float, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -155,7 +155,9 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int bdr_abi_version(void) { return 5; }
+int bdr_abi_version(void) { return 6; }
+
+void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
 
 const char* bdr_last_error(void) { return g_err; }
 
@@ -312,19 +314,21 @@ size_t dspark_markov_workspace_bytes(int64_t batch, int k) {
 
 int dspark_markov_argmax(const float* logits, int64_t batch, int k, int64_t vocab,
                          bdr_dtype wdt, const void* markov_w1, const void* markov_w2, int rank,
-                         const int32_t* prev_token, int32_t* draft_tokens, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         const int32_t* prev_token, int32_t* draft_tokens, int32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank, vocab, k));
   if (batch == 0) return BDR_OK;
   BDR_TRY(need_ptr(logits, "logits"));
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
   BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  if (status) BDR_TRY(need_ptr(status, "status", 4));
   BDR_TRY(need_ws(workspace, workspace_bytes, markov_workspace(batch, k)));
   int cus = 0;
   BDR_TRY(check_device(&cus));
   hipError_t e = launch_markov(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
-                               prev_token, draft_tokens, workspace, cus, as_stream(stream));
+                               prev_token, draft_tokens, status, workspace, cus,
+                               as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_markov_argmax launch");
   return BDR_OK;
 }
@@ -340,8 +344,8 @@ size_t dspark_draft_workspace_bytes(int64_t batch, int k, int64_t vocab, int log
 int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t hidden,
                        int64_t vocab, bdr_dtype dt, const void* lm_head_w, const void* markov_w1,
                        const void* markov_w2, int rank, const int32_t* prev_token,
-                       int32_t* draft_tokens, float* logits_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       int32_t* draft_tokens, float* logits_out, int32_t* status,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
   BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank, vocab, k));
@@ -351,6 +355,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
   BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
   if (logits_out) BDR_TRY(need_ptr(logits_out, "logits_out"));
+  if (status) BDR_TRY(need_ptr(status, "status", 4));
   const size_t need = dspark_draft_workspace_bytes(batch, k, vocab, logits_out == nullptr);
   BDR_TRY(need_ws(workspace, workspace_bytes, need));
   int cus = 0;
@@ -367,7 +372,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
                              nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block LM-head launch");
   e = launch_markov(logits, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
-                    draft_tokens, ws, cus, as_stream(stream));
+                    draft_tokens, status, ws, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block Markov launch");
   return BDR_OK;
 }
@@ -433,8 +438,8 @@ size_t dspark_markov_sample_workspace_bytes(int64_t batch, int k, int64_t vocab)
 int dspark_markov_sample(const float* logits, int64_t batch, int k, int64_t vocab,
                          bdr_dtype wdt, const void* markov_w1, const void* markov_w2, int rank,
                          const int32_t* prev_token, float temperature, uint64_t seed,
-                         int32_t* draft_tokens, float* draft_logits, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         int32_t* draft_tokens, float* draft_logits, int32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank, vocab, k));
   BDR_TRY(need_temperature(temperature));
@@ -443,12 +448,13 @@ int dspark_markov_sample(const float* logits, int64_t batch, int k, int64_t voca
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
   BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
   BDR_TRY(need_ptr(draft_logits, "draft_logits"));
+  if (status) BDR_TRY(need_ptr(status, "status", 4));
   BDR_TRY(need_ws(workspace, workspace_bytes, markov_sample_workspace(batch, k, vocab)));
   int cus = 0;
   BDR_TRY(check_device(&cus));
   hipError_t e = launch_markov_sample(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
                                       prev_token, 1.0f / temperature, seed, draft_tokens,
-                                      draft_logits, workspace, cus, as_stream(stream));
+                                      draft_logits, status, workspace, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_markov_sample launch");
   return BDR_OK;
 }

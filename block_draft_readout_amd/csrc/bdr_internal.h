@@ -6,65 +6,9 @@
 #include <stdint.h>
 
 #include "../../include/bdr.h"
+#include "gemm_plan.h"
 
 namespace bdr {
-
-// ----------------------------------------------------------------------------
-// Weight-streaming GEMM: C[M, N] = A[M, K] * W[N, K]^T with fp32 accumulation.
-// A is given as n_seg row-major segments [M, seg] laid side by side along K
-// (the fc's tap concatenation; one segment for the LM head).
-// ----------------------------------------------------------------------------
-struct GemmPlan {
-  int mt = 1;             // 16-row tiles per workgroup (1..9)
-  int m_groups = 1;       // workgroups along M
-  int jn = 4;             // 16-column tiles per workgroup (one wave)
-  int64_t n_wg = 1;       // workgroups along N
-  int ksplit = 1;         // workgroups along K (partials reduced by a second kernel)
-  int64_t steps_per_split = 0;
-  size_t workspace = 0;   // bytes of split-K partials
-  // streaming variants: balanced row ranges x K-block ranges; one wave per
-  // range (M <= 16) or a four-wave workgroup per range (wg, 16 < M <= 192)
-  bool stream = false;
-  bool wg = false;
-  bool ns = false;        // row-split workgroup kernel (gemm_ns.h), mt = A row tiles
-  int kbb = 1024;         // W bytes per row per visit
-  int mtw = 1;            // A row tiles per wave (wg)
-  int nt = 1;             // 16-row W tiles per range (compile-time bound)
-  int64_t n_waves = 0;    // row ranges (workgroups along N)
-  int64_t kblocks = 0;
-  int64_t kb_per_split = 0;
-  // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
-  // K steps of 64 (kblocks / kb_per_split count steps)
-  bool tile = false;
-  int tile_shape = 0;     // 0: 256 x 160 tiles, 3 LDS stages; 1: 256 x 320, 2 stages
-  int tiles_m = 0, tiles_n = 0;
-};
-
-// Compute units of a gfx950 part (MI350X / MI355X); fixed so that workspace
-// queries and launches always plan identically.
-constexpr int kNumCU = 256;
-
-enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
-
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split,
-                   int n_seg = 1);
-
-hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
-                       int64_t seg, int64_t M, int64_t N, const void* w, void* out,
-                       OutKind out_kind, void* workspace, hipStream_t stream);
-
-// hyper-connection stream average of each tap: dst[t][r, h] = mean_s src[t][s*ss + r*rs + h]
-hipError_t launch_hc_average(const void* const* src, void* const* dst, int n_taps, int hc,
-                             int64_t rows, int64_t hidden, int64_t stream_stride,
-                             int64_t row_stride, bdr_dtype dt, hipStream_t stream);
-
-// fp8 (E4M3) weights [N, K] with one fp32 scale per row, bf16 A segments
-// (multiples of 64 elements); plan.stream == false means the shape is not
-// supported.
-GemmPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split, int n_seg = 1);
-hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, int64_t seg,
-                           int64_t M, int64_t N, const uint8_t* w_q, const float* w_scale,
-                           void* out, OutKind out_kind, void* workspace, hipStream_t stream);
 
 // ----------------------------------------------------------------------------
 // Markov bias + semi-autoregressive argmax over k positions.
@@ -72,7 +16,10 @@ hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, i
 size_t markov_workspace(int64_t B, int k);
 hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                          const void* w1, const void* w2, int rank, const int32_t* prev,
-                         int32_t* draft, void* workspace, int n_cu, hipStream_t stream);
+                         int32_t* draft, int32_t* status, void* workspace, int n_cu,
+                         hipStream_t stream);
+// process-wide limit of the chain's bounded waits (negative / non-finite: default)
+void set_poll_timeout_us(double us);
 
 // ----------------------------------------------------------------------------
 // Greedy verification.
@@ -95,7 +42,7 @@ size_t markov_sample_workspace(int64_t B, int k, int64_t V);
 hipError_t launch_markov_sample(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                                 const void* w1, const void* w2, int rank, const int32_t* prev,
                                 float inv_t, uint64_t seed, int32_t* draft, float* xout,
-                                void* workspace, int n_cu, hipStream_t stream);
+                                int32_t* status, void* workspace, int n_cu, hipStream_t stream);
 size_t sample_verify_workspace(int64_t B, int k, int64_t V);
 hipError_t launch_verify_sample(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
                                 const int32_t* draft, const float* X, const float* conf,

@@ -29,15 +29,19 @@
 //                       token, and every workgroup polls the B tokens.
 //             All workgroups must be resident at once: the grid is at most the
 //             number of compute units and each workgroup fits in one.  Polls
-//             are bounded; a time-out sets the error word of the workspace
-//             instead of hanging.  The last workgroup to finish (a completion
-//             counter) returns the slots to zero.
+//             are bounded in time (wall clock); a poll that gives up sets the
+//             error word of the workspace, and the token it was waiting for
+//             becomes -1 (no Markov bias as a later context) instead of the
+//             kernel hanging.  The last workgroup to finish (a completion
+//             counter) returns the slots to zero and moves the error word to
+//             the caller's status word when one is given.
 //   passes -- one launch per position (used when the markov_w2 slice does not
 //             fit in LDS); stream order provides the grid-wide dependency, and
 //             workgroup w folds its keys into group slot w % 16 (atomic max;
 //             readers take the max over the 16 group slots).
 //
-// Workspace (zero-filled before first use; every call leaves it zeroed):
+// Workspace (zero-filled before first use; every call leaves it zeroed, except
+// the error word when the caller passes no status word):
 //   keys[k][16][B] uint64 (passes) | slots[k][B][256] uint64 (chain, per
 //   workgroup, kSlotStride words apart) | tokens[k][B] uint64, each on its
 //   own 128-byte line (chain,
@@ -63,6 +67,8 @@ struct MarkovArgs {
   unsigned long long* tokens;    // chain: [k, B] tagged tokens (B > 2), kTokenStride apart
   unsigned* done;                // chain: completion counter
   unsigned* err;                 // error word
+  int32_t* status;               // optional: receives the error word at the end (then cleared)
+  unsigned long long poll_ticks; // wall-clock ticks a poll waits before giving up
   int32_t* draft;                // [B, k]
   int64_t vtiles;                // ceil(V / 16)
   // sampling (probabilistic drafting): the token of a position is the argmax
@@ -84,7 +90,6 @@ constexpr int kTokenStride = 16;      // uint64 words
 // four 26.8, sixteen 29.1; no change at B = 16 for two, worse for more).
 constexpr int kSlotStride = 2;        // uint64 words
 
-constexpr unsigned kSpinLimit = 1u << 22;   // ~0.2 s of polling before giving up
 
 // final key of row b at position pos: max over the 16 group slots
 __device__ __forceinline__ unsigned long long final_key(const MarkovArgs& g, int pos, int64_t b) {
@@ -109,6 +114,24 @@ __device__ __forceinline__ unsigned long long tag_key(unsigned long long key, un
 }
 __device__ __forceinline__ int32_t tagged_index(unsigned long long t) {
   return static_cast<int32_t>(0x1FFFFFu - static_cast<uint32_t>((t >> kTagBits) & 0x1FFFFFull));
+}
+// token of a reduced tagged key; a bare tag (no candidate: a poll that gave up)
+// is -1, outside every vocabulary (a finite maximum never has zero value bits)
+__device__ __forceinline__ int32_t tagged_token(unsigned long long t) {
+  return (t >> 32) == 0ull ? -1 : tagged_index(t);
+}
+
+// Bounded wait: false once a poll that started failing at *t0 has waited
+// longer than the workspace's limit (the first failed attempt starts the clock).
+__device__ __forceinline__ bool keep_polling(const MarkovArgs& g, unsigned long long& t0,
+                                             bool& started) {
+  const unsigned long long now = static_cast<unsigned long long>(wall_clock64());
+  if (!started) {
+    started = true;
+    t0 = now;
+    return true;
+  }
+  return now - t0 <= g.poll_ticks;
 }
 
 // E fragments: markov_w1 row of context token p (the lane's row; p < 0 or
@@ -175,7 +198,8 @@ __device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
                                                        int64_t stride, int n, unsigned tag,
                                                        int lane) {
   constexpr int PL = kChainSlots / 64;
-  unsigned it = 0;
+  unsigned long long t0 = 0;
+  bool started = false;
   for (;;) {
     unsigned long long t[PL];
 #pragma unroll
@@ -192,7 +216,7 @@ __device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
       m = umax64(m, t[j]);
     }
     if (__all(ok)) return wave_max64(m);
-    if (++it > kSpinLimit) {
+    if (!keep_polling(g, t0, started)) {
       if (lane == 0) atomicOr(g.err, 1u);
       return 0ull;
     }
@@ -475,7 +499,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
       if (single) {
         for (int64_t b = 0; b < g.B; ++b) {
           const int32_t tok =
-              tagged_index(poll_max(g, pos_slots + b * kChainSlots * kSlotStride, kSlotStride,
+              tagged_token(poll_max(g, pos_slots + b * kChainSlots * kSlotStride, kSlotStride,
                                     static_cast<int>(G), tag, lane));
           if (lane == 0) {
             ctx[b] = tok;
@@ -489,20 +513,24 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
               poll_max(g, pos_slots + b * kChainSlots * kSlotStride, kSlotStride,
                        static_cast<int>(G), tag, lane);
           if (lane == 0) {
-            g.draft[b * g.k + pos] = tagged_index(t);
+            g.draft[b * g.k + pos] = tagged_token(t);
             publish_u64(toks + b * kTokenStride, (t & ~kTagMask) | tag);
           }
         }
         for (int64_t b0 = 0; b0 < g.B; b0 += 64) {
           const int n = static_cast<int>(min<int64_t>(64, g.B - b0));
-          unsigned it = 0;
+          unsigned long long t0 = 0;
+          bool started = false;
           for (;;) {
             unsigned long long t = fetch_u64(toks + (b0 + (lane < n ? lane : n - 1)) * kTokenStride);
-            if (__all(lane >= n || (t & kTagMask) == tag)) {
-              if (lane < n) ctx[b0 + lane] = tagged_index(t);
+            const bool cur = (t & kTagMask) == tag;
+            if (__all(lane >= n || cur)) {
+              if (lane < n) ctx[b0 + lane] = tagged_token(t);
               break;
             }
-            if (++it > kSpinLimit) {
+            if (!keep_polling(g, t0, started)) {
+              // rows whose token never came get no Markov context
+              if (lane < n) ctx[b0 + lane] = cur ? tagged_token(t) : -1;
               if (lane == 0) atomicOr(g.err, 1u);
               break;
             }
@@ -527,7 +555,14 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
     if (!single)
       for (int64_t i = threadIdx.x; i < static_cast<int64_t>(g.k) * g.B; i += blockDim.x)
         g.tokens[i * kTokenStride] = 0ull;
-    if (threadIdx.x == 0) *g.done = 0u;
+    if (threadIdx.x == 0) {
+      *g.done = 0u;
+      // every workgroup's error report precedes its arrival on the counter
+      if (g.status) {
+        g.status[0] = static_cast<int32_t>(fetch_u32(g.err));
+        __hip_atomic_store(g.err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
@@ -624,8 +659,13 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
   publish_rows(g, b0, pos, wave, r16, grp, bv, bi, sk);
 }
 
-// last position's tokens; then the keys go back to zero
+// last position's tokens; then the keys go back to zero (the per-position
+// launches never wait on one another: the status is the error word as it stands)
 static __global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs g) {
+  if (g.status && threadIdx.x == 0) {
+    g.status[0] = static_cast<int32_t>(fetch_u32(g.err));
+    __hip_atomic_store(g.err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x)
     g.draft[b * g.k + (g.k - 1)] = key_index(final_key(g, g.k - 1, b));
   __syncthreads();
@@ -712,7 +752,7 @@ static hipError_t launch_typed(const MarkovArgs& g, int rks, int n_cu, hipStream
 // MarkovArgs over a workspace of markov_workspace(B, k) bytes (sampling fields unset).
 MarkovArgs markov_args(const float* logits, int64_t B, int k, int64_t V, const void* w1,
                        const void* w2, int rank, const int32_t* prev, int32_t* draft,
-                       void* workspace);
+                       int32_t* status, void* workspace);
 
 // Launch the schedule that fits (g.r already 0 when no Markov weights are given).
 template <bool SAMPLE>

@@ -14,12 +14,12 @@ size_t markov_sample_workspace(int64_t B, int k, int64_t V) {
 hipError_t launch_markov_sample(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                                 const void* w1, const void* w2, int rank, const int32_t* prev,
                                 float inv_t, uint64_t seed, int32_t* draft, float* xout,
-                                void* workspace, int n_cu, hipStream_t stream) {
+                                int32_t* status, void* workspace, int n_cu, hipStream_t stream) {
   float* noise = static_cast<float*>(workspace);
   void* mws = static_cast<char*>(workspace) + align256(static_cast<size_t>(B) * k * V * 4);
   hipError_t e = launch_gumbel_noise(noise, B, k, V, seed, kStreamDraft, stream);
   if (e != hipSuccess) return e;
-  MarkovArgs g = markov_args(logits, B, k, V, w1, w2, rank, prev, draft, mws);
+  MarkovArgs g = markov_args(logits, B, k, V, w1, w2, rank, prev, draft, status, mws);
   g.noise = noise;
   g.xout = xout;
   g.inv_t = inv_t;

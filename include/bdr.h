@@ -15,9 +15,12 @@
  *     library never allocates or frees device memory and never synchronises.
  *   - Workspaces hold cross-workgroup counters and argmax keys: a workspace
  *     must be zero-filled once before its first use, and every call that
- *     completes leaves it zero-filled again (except the Markov error word
- *     below), so it can be reused by later calls and by graph replays.  One
- *     workspace must not be used by two calls that can run concurrently.
+ *     completes leaves its counters and hand-off slots zero-filled again (the
+ *     Markov error word too when the call is given a status word), so it can
+ *     be reused by later calls and by graph replays.  Other workspace bytes
+ *     (argmax keys of verification, sampling noise) are scratch that every
+ *     call rewrites before reading.  One workspace must not be used by two
+ *     calls that can run concurrently.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream); all work is
  *     enqueued on it in order, so calls on one stream see each other's results.
  *   - A call with no work (rows == 0 or batch == 0) returns BDR_OK after
@@ -65,6 +68,13 @@ int bdr_abi_version(void);
 
 /* Text describing the last non-zero return on the calling thread. */
 const char* bdr_last_error(void);
+
+/* How long a bounded wait of the persistent Markov chain (below) polls before
+ * it gives up, for launches enqueued after this call, process-wide (default
+ * 50000 us; a negative or non-finite value restores the default).  0 makes a
+ * wait give up at its second unsuccessful attempt: tests use it to exercise
+ * the time-out path with every kernel still running to completion. */
+void bdr_set_markov_poll_timeout_us(double us);
 
 /* ---------------------------------------------------------------------------
  * S1  dflash_fuse_fc -- fuse the tapped target hidden states and apply the fc.
@@ -206,32 +216,51 @@ int dspark_lm_head_fp8(const void* hidden, int64_t rows, int64_t hidden_size,
  *               0 <= r <= BDR_MAX_RANK, r % 8 == 0 (bf16) or r % 4 == 0 (f32)
  *   prev_token  [B] int32, the accepted bonus token of the previous step
  *   draft_tokens[B, k] int32 out
+ *   status      optional device int32 out (NULL: not reported): 0 when every
+ *               wait of the call completed, non-zero when one gave up; written
+ *               by the call's last kernel, so it is valid once the stream has
+ *               reached the end of the call
  *   workspace   >= dspark_markov_workspace_bytes(B, k).  When markov_w2's
  *               per-compute-unit slice fits in LDS and B <= 256, all k
  *               positions run in one persistent launch whose workgroups hand
  *               each position's maxima to one another through the workspace;
- *               if the workgroups cannot all be resident the bounded waits give
- *               up and set the uint32 error word that starts the last 256
- *               bytes of dspark_markov_workspace_bytes(B, k) (the tokens are
- *               then invalid).
+ *               this needs every workgroup of the launch resident at once (one
+ *               per compute unit), so two such launches must not run at the
+ *               same time on one device.  Its waits are bounded in time
+ *               (bdr_set_markov_poll_timeout_us): a wait that gives up sets the
+ *               uint32 error word that starts the last 256 bytes of
+ *               dspark_markov_workspace_bytes(B, k), the token it waited for
+ *               becomes -1 and later positions of that row use no Markov bias
+ *               -- the draft is then invalid and `status` says so.  With a
+ *               status word the error word is moved into it and cleared; without
+ *               one it stays set until a call with a status word.
  * ------------------------------------------------------------------------- */
 size_t dspark_markov_workspace_bytes(int64_t batch, int k);
 int dspark_markov_argmax(const float* logits, int64_t batch, int k,
                          int64_t vocab, bdr_dtype wdt, const void* markov_w1,
                          const void* markov_w2, int rank,
                          const int32_t* prev_token, int32_t* draft_tokens,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int32_t* status, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * S2+S3  dspark_draft_block -- draft one block: LM head, then the Markov
  * semi-autoregressive argmax (exactly dspark_lm_head followed by
  * dspark_markov_argmax on the same stream).
  *
+ * The DSpark proposer turns the drafter's hidden states of the block into
+ * full-vocabulary logits with its LM head and then takes the greedy sample
+ * position by position, each biased by the Markov head on the previous
+ * position's prediction and position 0 on the accepted bonus token that
+ * propose() keeps ([recipe] DSpark port notes, dflash.py: propose() and
+ * _greedy_sample; qwen3_dflash.py: compute_markov_bias).
+ *
  *   draft_hidden [B, k, H] dtype -- the drafter's hidden states of the block
  *   lm_head_w    [V, H] dtype; markov_w1/markov_w2/rank as in S3 (dtype dt)
  *   prev_token   [B] int32; draft_tokens [B, k] int32 out
  *   logits_out   [B, k, V] fp32, optional: NULL keeps the logits in the
  *                workspace
+ *   status       optional device int32 out, as in S3
  *   workspace    >= dspark_draft_workspace_bytes(B, k, V, logits_out == NULL)
  * ------------------------------------------------------------------------- */
 size_t dspark_draft_workspace_bytes(int64_t batch, int k, int64_t vocab,
@@ -241,7 +270,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k,
                        const void* lm_head_w, const void* markov_w1,
                        const void* markov_w2, int rank,
                        const int32_t* prev_token, int32_t* draft_tokens,
-                       float* logits_out, void* workspace,
+                       float* logits_out, int32_t* status, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -318,6 +347,7 @@ int dspark_gumbel_noise(int64_t batch, int k, int64_t vocab, uint64_t seed,
  *   temperature T > 0; seed as above
  *   draft_tokens [B, k] int32 out
  *   draft_logits [B, k, V] fp32 out (x, before the division by T)
+ *   status       optional device int32 out, as in S3
  *   workspace    >= dspark_markov_sample_workspace_bytes(B, k, V): the draw
  *                noise, then a Markov workspace (same rules as S3; its error
  *                word is in the last 256 bytes of this size)
@@ -328,7 +358,7 @@ int dspark_markov_sample(const float* logits, int64_t batch, int k,
                          const void* markov_w2, int rank,
                          const int32_t* prev_token, float temperature,
                          uint64_t seed, int32_t* draft_tokens,
-                         float* draft_logits, void* workspace,
+                         float* draft_logits, int32_t* status, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* spec_verify_sample -- S4 by rejection sampling.

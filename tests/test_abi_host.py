@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 5
+    assert L.bdr_abi_version() == 6
 
 
 def test_workspace_sizes(L):
@@ -176,8 +176,8 @@ def test_markov_validation(L):
     from block_draft_readout_amd import _abi as A
     P = C.c_void_p(4096)
     ws = C.c_void_p(4096)
-    args = lambda B=16, k=8, V=1000, dt=A.BDR_BF16, w1=P, w2=P, r=64, prev=P, d=P, wp=ws, wn=4096: \
-        L.dspark_markov_argmax(P, B, k, V, dt, w1, w2, r, prev, d, wp, wn, None)
+    args = lambda B=16, k=8, V=1000, dt=A.BDR_BF16, w1=P, w2=P, r=64, prev=P, d=P, wp=ws, wn=4096, \
+        st=None: L.dspark_markov_argmax(P, B, k, V, dt, w1, w2, r, prev, d, st, wp, wn, None)
     assert args(k=0) == A.BDR_EINVAL
     assert args(k=17) == A.BDR_EUNSUPPORTED
     assert args(r=129) == A.BDR_EUNSUPPORTED
@@ -188,6 +188,7 @@ def test_markov_validation(L):
     assert args(B=-1) == A.BDR_EINVAL
     assert args(wp=None) == A.BDR_EWORKSPACE
     assert args(wn=8) == A.BDR_EWORKSPACE
+    assert args(st=C.c_void_p(4098)) == A.BDR_EINVAL  # misaligned status word
     assert args(B=0) == A.BDR_OK
 
 
@@ -196,8 +197,8 @@ def test_draft_block_validation(L):
     P = C.c_void_p(4096)
     f = lambda **kw: L.dspark_draft_block(kw.get("h", P), kw.get("B", 16), kw.get("k", 8), 5120,
                                           kw.get("V", 151936), A.BDR_BF16, kw.get("lm", P), P, P,
-                                          64, P, P, kw.get("lo", None), kw.get("ws", P),
-                                          kw.get("wn", 1024), None)
+                                          64, P, P, kw.get("lo", None), kw.get("st", None),
+                                          kw.get("ws", P), kw.get("wn", 1024), None)
     assert f(h=None) == A.BDR_EINVAL
     assert f(lm=None) == A.BDR_EINVAL
     assert f(k=20) == A.BDR_EUNSUPPORTED
@@ -242,7 +243,8 @@ def test_sampling_validation(L):
     P = C.c_void_p(4096)
     ws = C.c_void_p(4096)
     m = lambda T=1.0, B=4, k=8, V=1000, r=64, x=P, prev=P, wp=ws, wn=4096: \
-        L.dspark_markov_sample(P, B, k, V, A.BDR_BF16, P, P, r, prev, T, 7, P, x, wp, wn, None)
+        L.dspark_markov_sample(P, B, k, V, A.BDR_BF16, P, P, r, prev, T, 7, P, x, None, wp, wn,
+                               None)
     assert m(T=0.0) == A.BDR_EINVAL
     assert m(T=-1.0) == A.BDR_EINVAL
     assert m(T=float("nan")) == A.BDR_EINVAL
