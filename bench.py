@@ -5,9 +5,13 @@ dspark_lm_head + dspark_markov_argmax (S2 + S3; dspark_draft_block is exactly
 these two calls) -> spec_verify_greedy (S4).  Inputs cycle through a pool of
 pre-generated seeded steps that are resident in HBM before timing starts.
 
-Prints ONE JSON line: block-steps/s, the roofline of the dominant kernel (the
-LM-head GEMM, timed with HIP events on its launch stream), and the CPU oracle
-timed on a bounded sample of the same workload.
+Prints ONE JSON line: block-steps/s over K back-to-back steps (the headline),
+per-step medians and 10th/90th percentiles with the pool rotating, with the
+MALL flushed before each step and with one step repeated (warm), the roofline
+of the dominant kernel (the LM-head GEMM, timed with HIP events on its launch
+stream), each stage's time, algorithmic bytes, GB/s and fraction of the HBM
+peak, and the CPU oracle timed on a bounded sample of the same workload (plus
+one-thread figures of two small workloads).
 """
 from __future__ import annotations
 
@@ -36,9 +40,9 @@ def log(msg):
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "gemm_wg3.hip",
-                "gemm_ns.h", "gemm_ns_bf16.hip", "bdr_device.h", "bdr_internal.h")
+                "gemm_ns.h", "gemm_ns_bf16.hip", "bdr_device.h", "gemm_plan.h")
 GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_kernels.h",
-                    "bdr_device.h", "bdr_internal.h")
+                    "bdr_device.h", "gemm_plan.h")
 
 
 def kernel_source_hash(sources=GEMM_SOURCES) -> str:
@@ -81,6 +85,11 @@ class Step:
         self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
         self.prev = slot["prev0"].data_ptr()   # Markov context of position 0 (see --closed-loop)
+        # each slot may hold its own copy of the Markov weights (same values), so
+        # that consecutive steps find none of their inputs in the MALL
+        self.w1 = slot.get("w1", g["w1"]).data_ptr()
+        self.w2 = slot.get("w2", g["w2"]).data_ptr()
+        self.status = None        # device int32 for the Markov calls' status word
 
     def fc(self):
         w, b = self.w, self.b
@@ -109,13 +118,12 @@ class Step:
         if self.sample is not None:
             T, seed = self.sample
             return self.L.dspark_markov_sample(
-                b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt, self.g["w1"].data_ptr(),
-                self.g["w2"].data_ptr(), w.rank, self.prev, T, seed,
-                b["d"].data_ptr(), b["x"].data_ptr(), b["ws_ms"], b["ws_ms_n"], self.stream)
+                b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt, self.w1, self.w2,
+                w.rank, self.prev, T, seed, b["d"].data_ptr(), b["x"].data_ptr(), self.status,
+                b["ws_ms"], b["ws_ms_n"], self.stream)
         return self.L.dspark_markov_argmax(b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt,
-                                           self.g["w1"].data_ptr(), self.g["w2"].data_ptr(),
-                                           w.rank, self.prev, b["d"].data_ptr(),
-                                           b["ws_m"], b["ws_m_n"], self.stream)
+                                           self.w1, self.w2, w.rank, self.prev, b["d"].data_ptr(),
+                                           self.status, b["ws_m"], b["ws_m_n"], self.stream)
 
     def draft_block(self):
         w, b = self.w, self.b
@@ -124,10 +132,10 @@ class Step:
             return rc if rc != 0 else self.markov()
         return self.L.dspark_draft_block(self.s["draft_hidden"].data_ptr(), w.batch, w.k,
                                          w.hidden, w.vocab, self.dt, self.g["lm_w"].data_ptr(),
-                                         self.g["w1"].data_ptr(), self.g["w2"].data_ptr(), w.rank,
+                                         self.w1, self.w2, w.rank,
                                          self.s["prev0"].data_ptr(), b["d"].data_ptr(),
-                                         b["logits"].data_ptr(), b["ws_m"], b["ws_m_n"],
-                                         self.stream)
+                                         b["logits"].data_ptr(), self.status, b["ws_m"],
+                                         b["ws_m_n"], self.stream)
 
     def verify(self):
         w, b = self.w, self.b
@@ -227,19 +235,24 @@ def check(rc, what):
         raise RuntimeError(f"{what} failed ({rc}): {bdr.lib().bdr_last_error().decode()}")
 
 
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None, fp8=False):
     """The oracle, as it stands, on whole block-steps of the workload: repeats
     the step of pool slot 0 until about ``budget_s`` seconds of CPU work.
     ``sample`` = (temperature, seed) times the probabilistic path instead;
-    ``fp8`` times the fp8-weight fc and LM head."""
+    ``fp8`` times the fp8-weight fc and LM head.  ``cores`` is the number of
+    threads the oracle's BLAS calls use (its Python loops run on one)."""
     import oracle
     from oracle import fp8 as ofp8
     from oracle import sampling
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
+    blas = _blas_threads()
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -273,8 +286,44 @@ def cpu_baseline(w, W, slot_host, budget_s=10.0, max_steps=30, sample=None, fp8=
             "sample": f"{n} full {'probabilistic' if sample else 'greedy'} block-steps of "
                       f"{'(fp8 weights) ' if fp8 else ''}"
                       f"{w.name} (S1-S4, all {w.batch} rows) in "
-                      f"{dt:.1f} s on the host; numpy float64 with BLAS threads={blas}, "
-                      f"affinity cores={len(os.sched_getaffinity(0))}"}
+                      f"{dt:.1f} s on the host; numpy float64 BLAS on {blas} threads "
+                      f"(host affinity {len(os.sched_getaffinity(0))} cores)"}
+
+
+def cpu_one_thread(names=("tiny", "qwen27b_b1"), budget_s=4.0):
+    """The oracle on one thread (BLAS limited to 1) for small workloads: greedy
+    block-steps/s on a bounded sample of each (targets planted on the oracle's
+    own draft)."""
+    import oracle
+    import workloads
+    from workloads import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    out = {}
+    with threadpool_limits(limits=1):
+        for name in names:
+            w = workloads.get(name)
+            W = synth.make_weights(w)
+            s = synth.make_step(w, 0)
+            ref = oracle.block_step(w.dtype, s["taps"], W["fc_w"], s["draft_hidden"], W["lm_w"],
+                                    W["w1"], W["w2"], s["prev0"])
+            Y = synth.plant_targets(w, 0, s["noise"], ref["draft_tokens"])["target_logits"]
+            conf = synth.make_confidence(w, 0)
+            n, t0 = 0, time.perf_counter()
+            while True:
+                oracle.block_step(w.dtype, s["taps"], W["fc_w"], s["draft_hidden"], W["lm_w"],
+                                  W["w1"], W["w2"], s["prev0"], target_logits=Y, confidence=conf,
+                                  threshold=w.threshold)
+                n += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget_s or n >= 200:
+                    break
+            out[name] = {"value": n / dt, "unit": "block-steps/s", "cores": 1,
+                         "sample": f"{n} greedy block-steps in {dt:.1f} s"}
+            del W
+    return out
 
 
 def fc_only(args, w, L, bdr, synth, torch, dev):
@@ -374,12 +423,18 @@ def fc_only(args, w, L, bdr, synth, torch, dev):
         "cpu_baseline": None}), flush=True)
 
 
+def _pct(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen27b_b1")
+    ap.add_argument("--workload", default="adaptive_b16")
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--graph", action="store_true", help="replay HIP graphs of whole steps")
     ap.add_argument("--overlap", choices=("none", "lm", "chain"), default="chain",
@@ -403,6 +458,11 @@ def main():
     ap.add_argument("--hc", type=int, default=1,
                     help="with --fc-rows: average each tap over this many hyper-connection "
                          "streams (dflash_hc_average) before the fc; both are timed")
+    ap.add_argument("--shared-markov", action="store_true",
+                    help="one copy of the Markov weights for every pool slot (by default each "
+                         "slot has its own copy, so consecutive steps share no input)")
+    ap.add_argument("--dist-steps", type=int, default=50,
+                    help="steps of each per-step timing phase (rotated, cold, warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, copy a 1 GiB buffer 3 times (counter calibration)")
@@ -468,7 +528,8 @@ def main():
             "bonus": torch.empty(B, dtype=torch.int32, device=dev),
             "targ": torch.empty((B, k + 1), dtype=torch.int32, device=dev),
             "acc": torch.zeros(k, dtype=torch.int64, device=dev),
-            "prop": torch.zeros(k, dtype=torch.int64, device=dev)}
+            "prop": torch.zeros(k, dtype=torch.int64, device=dev),
+            "status": torch.full((1,), -1, dtype=torch.int32, device=dev)}
     sampling = args.draft == "sample"
     if sampling:
         bufs["x"] = torch.empty((B, k, V), dtype=torch.float32, device=dev)
@@ -493,10 +554,14 @@ def main():
     # pool of steps resident in HBM; targets planted on this path's own draft
     t0 = time.time()
     slots, host0 = [], None
+    verify_bytes = []
+    es = 2 if w.dtype == "bf16" else 4
     for p in range(args.pool):
         s = synth.make_step(w, p)
         slot = {"taps": [up(t) for t in s["taps"]], "draft_hidden": up(s["draft_hidden"]),
                 "prev0": up(s["prev0"])}
+        if not args.shared_markov:
+            slot["w1"], slot["w2"] = g["w1"].clone(), g["w2"].clone()
         conf = synth.make_confidence(w, p)
         slot["conf"] = None if conf is None else up(conf)
         st = Step(L, w, dt, g, slot, bufs, sptr,
@@ -508,10 +573,16 @@ def main():
         d_host = bufs["d"].cpu().numpy()
         Y = synth.plant_targets(w, p, s["noise"], d_host)["target_logits"]
         slot["Y"] = up(Y)
+        check(st.verify(), "verification")
+        torch.cuda.synchronize()
+        # verification reads the rows of the (confidence-truncated) blocks only
+        verify_bytes.append(int((bufs["bl"].cpu().numpy().astype(np.int64) + 1).sum()) * V * es)
         slots.append(st)
         if p == 0:
             host0 = {"taps": s["taps"], "draft_hidden": s["draft_hidden"], "prev0": s["prev0"],
                      "Y": Y, "conf": conf}
+    bufs["acc"].zero_()
+    bufs["prop"].zero_()
     log(f"pool of {args.pool} steps ready in {time.time() - t0:.1f}s")
 
     stream2 = torch.cuda.Stream(dev)          # default priority
@@ -596,7 +667,7 @@ def main():
         step_i(i)
     torch.cuda.synchronize()
 
-    # phase 1: whole steps
+    # phase 1 (the headline): K whole steps back to back, cycling the pool
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -607,8 +678,28 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # phase 2: the same steps eagerly, with HIP events around each LM-head launch
+    # phase 2: per-step distributions (HIP events around each step on the main
+    # stream; the fc joins it before the stop stamp)
     sptr_now = C.c_void_p(stream.cuda_stream)
+    nd = max(1, args.dist_steps)
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev)      # 1 GiB
+    dist = {}
+    for mode in ("rotated", "cold", "warm"):
+        tm = LaunchTimer(nd)
+        torch.cuda.synchronize()
+        for i in range(nd):
+            if mode == "cold":        # 1 GiB read between steps: the MALL holds none of the step
+                torch.amax(flush)
+            tm.start(i, sptr_now)
+            step_i(0 if mode == "warm" else i)
+            tm.stop(i, sptr_now)
+        torch.cuda.synchronize()
+        dist[mode] = _pct([tm.ms(i) * 1e3 for i in range(nd)])
+    del flush
+    log("per-step us (median/p10/p90): " + ", ".join(
+        f"{m} {d['median']:.1f}/{d['p10']:.1f}/{d['p90']:.1f}" for m, d in dist.items()))
+
+    # phase 3: the same steps in stream order, HIP events around each LM-head launch
     lm_t = LaunchTimer(args.steps)
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -622,7 +713,7 @@ def main():
     torch.cuda.synchronize()
     lm_ms = float(np.mean([lm_t.ms(i) for i in range(args.steps)]))
 
-    # phase 3: per-stage times (one stage at a time, events on the launch stream)
+    # phase 4: per-stage times (one stage at a time, events on the launch stream)
     stage_fns = (("fc", "fc"), ("lm_head", "lm_head"), ("markov", "markov"), ("verify", "verify"))
     st_t = LaunchTimer(args.steps * len(stage_fns))
     torch.cuda.synchronize()
@@ -633,19 +724,50 @@ def main():
             check(getattr(st, fn)(), fn)
             st_t.stop(i * len(stage_fns) + j, sptr_now)
     torch.cuda.synchronize()
-    stages_us = {name: round(float(np.mean([st_t.ms(i * len(stage_fns) + j)
-                                            for i in range(args.steps)])) * 1e3, 1)
-                 for j, (name, _) in enumerate(stage_fns)}
-    log(f"stages (us): {stages_us}")
+    stage_us = {name: float(np.mean([st_t.ms(i * len(stage_fns) + j)
+                                     for i in range(args.steps)])) * 1e3
+                for j, (name, _) in enumerate(stage_fns)}
 
-    es = 2 if w.dtype == "bf16" else 4
+    # every Markov wait of the timed steps completed: the workspace's error word
+    # is sticky until a call with a status word moves it out
+    st0 = slots[0]
+    st0.status = bufs["status"].data_ptr()
+    check(st0.markov(), "drafting (status)")
+    torch.cuda.synchronize()
+    st0.status = None
+    markov_status = int(bufs["status"].item())
+    if markov_status != 0:
+        raise RuntimeError(f"a bounded wait of the Markov chain gave up (status {markov_status})")
+
+    # algorithmic bytes of each stage (its own inputs and outputs, read or
+    # written once); the LM head is the dominant kernel
+    rk = w.rank
     if fp8:      # codes + row scales, bf16 hidden states, fp32 logits
         lm_bytes = V * H + V * 4 + B * k * H * es + B * k * V * 4
+        fc_bytes = H * w.n_taps * H + H * 4 + w.rows * w.n_taps * H * es + w.rows * H * es
     else:
         lm_bytes = V * H * es + B * k * H * es + B * k * V * 4
+        fc_bytes = (H * w.n_taps * H + w.rows * w.n_taps * H + w.rows * H) * es
+    markov_bytes = B * k * V * 4 + V * rk * es + B * k * rk * es + B * k * 4
+    if sampling:      # noise written and read, x written
+        markov_bytes += 3 * B * k * V * 4
+    conf_bytes = 0 if w.threshold is None else B * k * 4
+    verify_b = float(np.mean(verify_bytes)) + B * k * 4 + conf_bytes
+    stage_bytes = {"fc": fc_bytes, "lm_head": lm_bytes, "markov": markov_bytes,
+                   "verify": verify_b}
+    stages = {}
+    for name, us in stage_us.items():
+        gbs = stage_bytes[name] / (us * 1e-6) / 1e9
+        stages[name] = {"us": round(us, 2), "bytes": int(stage_bytes[name]),
+                        "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log("stages: " + ", ".join(f"{n} {v['us']:.1f} us {v['GBs']:.0f} GB/s ({v['frac']:.0%})"
+                               for n, v in stages.items()))
+    step_bytes = sum(stage_bytes.values())
     achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
     traffic = recorded_traffic(w.name, fp8)
-    log(f"step {ms_step * 1e3:.1f} us; LM head {lm_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
+    log(f"step {ms_step * 1e3:.1f} us ({step_bytes / 1e6:.1f} MB algorithmic = "
+        f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s); LM head {lm_ms * 1e3:.1f} us = "
+        f"{achieved:.0f} GB/s")
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -661,7 +783,12 @@ def main():
         log("timing the CPU oracle on one block-step ...")
         cpu = cpu_baseline(w, W, host0,
                            sample=(args.temperature, 0x5EED0000) if sampling else None, fp8=fp8)
-        log(f"cpu oracle: {1.0 / cpu['value']:.1f} s per block-step")
+        log(f"cpu oracle: {1.0 / cpu['value']:.1f} s per block-step on {cpu['cores']} threads")
+        one = cpu_one_thread()
+        if one:
+            cpu["one_thread"] = one
+            log("cpu oracle, one thread: " + ", ".join(
+                f"{n} {v['value']:.2f} block-steps/s" for n, v in one.items()))
 
     out = {
         "metric": "draft+verify block-steps/sec per GPU; HBM GB/s and % roofline",
@@ -677,7 +804,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.describe(), "batch": B, "k": k, "hidden": H, "vocab": V,
-                   "rank": w.rank, "n_taps": w.n_taps,
+                   "rank": w.rank, "n_taps": w.n_taps, "threshold": w.threshold,
                    "launch": "hip-graph" if graphs is not None else "eager",
                    "fc_overlap": "none (closed loop)" if args.closed_loop else args.overlap,
                    "loop": "closed" if args.closed_loop else "independent steps",
@@ -685,7 +812,8 @@ def main():
                    "weights": "fp8-e4m3 codes + fp32 row scales (fc, LM head)" if fp8
                    else w.dtype,
                    **({"temperature": args.temperature} if sampling else {}),
-                   "pool_steps": args.pool},
+                   "pool_steps": args.pool,
+                   "markov_weights": "one copy" if args.shared_markov else "one copy per slot"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
@@ -693,7 +821,13 @@ def main():
                      else "LM-head weight-streaming GEMM (dspark_lm_head)",
                      "avg_launch_us": lm_ms * 1e3,
                      "algorithmic_bytes_per_launch": lm_bytes},
-        "stages_us": stages_us,
+        "stages": stages,
+        "step_algorithmic_bytes": int(step_bytes),
+        "step_us": {"mean_back_to_back": ms_step * 1e3, **dist,
+                    "note": "rotated: pool slots in turn; cold: 1 GiB read before each step "
+                            "(outside its events); warm: slot 0 repeated; per-step events on "
+                            "the main stream"},
+        "markov_status": markov_status,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -117,25 +117,29 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   const int r16 = lane & 15;
   const int grp = lane >> 4;
 
-  // the workgroup's rows, then this wave's quarter
-  const int64_t g_lo = static_cast<int64_t>(blockIdx.x) * g.N / sa.n_waves;
-  const int64_t g_hi = static_cast<int64_t>(blockIdx.x + 1) * g.N / sa.n_waves;
+  // the workgroup's 16-row tiles, then this wave's quarter of them: ranges
+  // start on a tile boundary, so each 16-column piece of an output row is one
+  // aligned 64-byte store (a range starting mid-tile made every piece straddle
+  // two 64-byte blocks: 1.8x the logits' bytes written)
+  const int64_t n_t = (g.N + 15) / 16;
+  const int64_t t_lo = static_cast<int64_t>(blockIdx.x) * n_t / sa.n_waves;
+  const int64_t t_hi = static_cast<int64_t>(blockIdx.x + 1) * n_t / sa.n_waves;
   // (row indices fit 31 bits; readfirstlane keeps everything derived from the
   // wave index in scalar registers, so the load descriptors stay uniform)
   const int n_lo = __builtin_amdgcn_readfirstlane(
-      static_cast<int>(g_lo + (g_hi - g_lo) * wave / kNsWaves));
-  const int n_hi = __builtin_amdgcn_readfirstlane(
-      static_cast<int>(g_lo + (g_hi - g_lo) * (wave + 1) / kNsWaves));
-  const int ntiles = (n_hi - n_lo + 15) / 16;
+      static_cast<int>(16 * (t_lo + (t_hi - t_lo) * wave / kNsWaves)));
+  const int n_hi = __builtin_amdgcn_readfirstlane(static_cast<int>(
+      min<int64_t>(g.N, 16 * (t_lo + (t_hi - t_lo) * (wave + 1) / kNsWaves))));
+  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + 15) / 16 : 0;
   // passes: the same count on every wave (from the largest quarter); pass p
   // holds base (+1 for the first rem passes) of this wave's tiles
-  const int max_tiles = static_cast<int>(((g_hi - g_lo + kNsWaves - 1) / kNsWaves + 15) / 16);
+  const int max_tiles = static_cast<int>((t_hi - t_lo + kNsWaves - 1) / kNsWaves);
   const int npass = max(1, (max_tiles + NTW - 1) / NTW);
   const int pbase = ntiles / npass, prem = ntiles - pbase * npass;
   auto pass_lo = [&](int p) { return p * pbase + min(p, prem); };
   const uint32_t kb_lo = static_cast<uint32_t>(blockIdx.y * sa.kb_per_split);
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
-  if (g_hi <= g_lo || kb_lo >= kb_hi) return;   // whole workgroup
+  if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
   const int nkb = static_cast<int>(kb_hi - kb_lo);
   const OutRef out(g, blockIdx.y);
   const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));

@@ -18,3 +18,15 @@ def test_recorded_lm_head_traffic_matches_sources(fp8):
     t = bench.recorded_traffic("qwen27b_b1", fp8)
     assert t is not None, "LM-head counter summary missing or older than the GEMM sources"
     assert 0.98 * alg <= t <= 1.05 * alg, (t, alg)
+
+
+@pytest.mark.parametrize("name,M,H", [("adaptive_b16", 128, 5120), ("b16", 112, 5120),
+                                      ("flashnext_b4", 32, 2560)])
+def test_recorded_traffic_of_the_batched_workloads(name, M, H):
+    """The row-split LM head of the batched workloads: counter summary present
+    for the current sources, traffic within 5 % of the algorithmic bytes."""
+    V = 151936
+    alg = V * H * 2 + M * H * 2 + M * V * 4
+    t = bench.recorded_traffic(name, False)
+    assert t is not None, "LM-head counter summary missing or older than the GEMM sources"
+    assert 0.98 * alg <= t <= 1.05 * alg, (t, alg)
