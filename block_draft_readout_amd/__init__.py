@@ -20,6 +20,7 @@ from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
 
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
+    "dspark_draft_block_noalloc",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
     "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
@@ -343,6 +344,47 @@ def dspark_draft_block(draft_hidden: torch.Tensor, lm_head_w: torch.Tensor,
                                     _ptr(draft_tokens), _ptr(logits_out), _ptr(st), wp, wn,
                                     _stream(draft_hidden.device)))
     _status_out("dspark_draft_block", st, check and B > 0)
+    return draft_tokens
+
+
+def dspark_draft_block_noalloc(draft_hidden: torch.Tensor, lm_head_w: torch.Tensor,
+                               markov_w1: Optional[torch.Tensor], markov_w2: Optional[torch.Tensor],
+                               prev_token: torch.Tensor, draft_tokens: Optional[torch.Tensor] = None,
+                               logits_out: Optional[torch.Tensor] = None,
+                               status: Optional[torch.Tensor] = None,
+                               check: bool = True) -> torch.Tensor:
+    """dspark_draft_block with no workspace (the library's static per-device
+    scratch; batch * k <= 256): for callers that cannot allocate inside the
+    call.  Outputs not supplied are allocated here, before the call."""
+    L = lib()
+    _dev(draft_hidden, "draft_hidden")
+    _dev(lm_head_w, "lm_head_w")
+    B, k, H = draft_hidden.shape
+    V = lm_head_w.shape[0]
+    if lm_head_w.shape[1] != H or draft_hidden.dtype != lm_head_w.dtype:
+        raise ValueError("lm_head_w must be [V, H] with draft_hidden's dtype")
+    w1, w2, r = _markov_args(markov_w1, markov_w2, lm_head_w)
+    if w1 is not None and w1.dtype != lm_head_w.dtype:
+        raise ValueError("Markov weights must share the LM head's dtype")
+    _dev(prev_token, "prev_token")
+    if prev_token.dtype != torch.int32 or prev_token.numel() != B:
+        raise ValueError("prev_token must be int32 [B]")
+    dev = draft_hidden.device
+    if draft_tokens is None:
+        draft_tokens = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if logits_out is None:
+        logits_out = torch.empty((B, k, V), dtype=torch.float32, device=dev)
+    _dev(draft_tokens, "draft_tokens")
+    _dev(logits_out, "logits_out")
+    if logits_out.dtype != torch.float32 or tuple(logits_out.shape) != (B, k, V):
+        raise ValueError("logits_out must be fp32 [B, k, V]")
+    st = _status_in(status, check, dev)
+    _abi.check("dspark_draft_block_noalloc",
+               L.dspark_draft_block_noalloc(_ptr(draft_hidden), B, k, H, V, _dt(lm_head_w),
+                                            _ptr(lm_head_w), _ptr(w1), _ptr(w2), r,
+                                            _ptr(prev_token), _ptr(draft_tokens),
+                                            _ptr(logits_out), _ptr(st), _stream(dev)))
+    _status_out("dspark_draft_block_noalloc", st, check and B > 0)
     return draft_tokens
 
 

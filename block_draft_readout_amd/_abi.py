@@ -48,6 +48,8 @@ SIGNATURES = {
     "dspark_draft_workspace_bytes": (_sz, [_i64, _int, _i64, _int]),
     "dspark_draft_block": (_int, [_vp, _i64, _int, _i64, _i64, _int, _vp, _vp, _vp, _int, _vp,
                                   _vp, _vp, _vp, _vp, _sz, _vp]),
+    "dspark_draft_block_noalloc": (_int, [_vp, _i64, _int, _i64, _i64, _int, _vp, _vp, _vp, _int,
+                                          _vp, _vp, _vp, _vp, _vp]),
     "spec_verify_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "spec_verify_greedy": (_int, [_vp, _int, _i64, _int, _i64, _vp, _vp, C.c_float, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -150,6 +151,41 @@ int markov_shape(int dt, const void* w1, const void* w2, int rank, int64_t vocab
 }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------------------- no-allocation scratch
+// The Markov hand-off workspace of dspark_draft_block_noalloc.  Each device the
+// library runs on holds its own copy of this array until the process ends (zero
+// when the code object is loaded).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[BDR_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[256];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 256) return fail(BDR_EUNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(BDR_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BDR_OK;
+}
+
+// zero-fills n bytes (n % 16 == 0) with vector stores: the hand-off slots and
+// counters must start at zero, whatever an earlier call on this device left
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 
 }  // namespace
 
@@ -374,6 +410,50 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
   e = launch_markov(logits, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
                     draft_tokens, status, ws, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block Markov launch");
+  return BDR_OK;
+}
+
+// ---------------------------------------------------------------------------- S2+S3, no allocation
+int dspark_draft_block_noalloc(const void* draft_hidden, int64_t batch, int k, int64_t hidden,
+                               int64_t vocab, bdr_dtype dt, const void* lm_head_w,
+                               const void* markov_w1, const void* markov_w2, int rank,
+                               const int32_t* prev_token, int32_t* draft_tokens,
+                               float* logits_out, int32_t* status, void* stream) {
+  BDR_TRY(block_shape(batch, k, vocab));
+  BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
+  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank, vocab, k));
+  const size_t need = markov_workspace(batch, k);
+  if (need > BDR_NOALLOC_SCRATCH_BYTES)
+    return fail(BDR_EUNSUPPORTED,
+                "batch %lld x k %d needs %zu bytes of hand-off scratch; the static scratch "
+                "holds %d (batch * k <= 256)", static_cast<long long>(batch), k, need,
+                BDR_NOALLOC_SCRATCH_BYTES);
+  if (batch == 0) return BDR_OK;
+  BDR_TRY(need_ptr(draft_hidden, "draft_hidden"));
+  BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));
+  BDR_TRY(need_ptr(prev_token, "prev_token", 4));
+  BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
+  BDR_TRY(need_ptr(logits_out, "logits_out"));
+  if (status) BDR_TRY(need_ptr(status, "status", 4));
+  int cus = 0;
+  BDR_TRY(check_device(&cus));
+  void* ws = nullptr;
+  BDR_TRY(scratch_address(&ws));
+  const GemmPlan p = plan_gemm(batch * k, vocab, hidden, dt, false);
+  if (p.workspace != 0) return fail(BDR_EUNSUPPORTED, "LM-head plan needs a workspace");
+  const hipStream_t st = as_stream(stream);
+  const size_t n16 = need / 16;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n16 + 255) / 256, 1024))),
+                     dim3(256), 0, st, static_cast<uint4*>(ws), n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "dspark_draft_block_noalloc scratch clear");
+  const void* a[1] = {draft_hidden};
+  e = launch_gemm(p, dt, a, 1, hidden, batch * k, vocab, lm_head_w, logits_out, OUT_F32, nullptr,
+                  st);
+  if (e != hipSuccess) return hip_fail(e, "dspark_draft_block_noalloc LM-head launch");
+  e = launch_markov(logits_out, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
+                    draft_tokens, status, ws, cus, st);
+  if (e != hipSuccess) return hip_fail(e, "dspark_draft_block_noalloc Markov launch");
   return BDR_OK;
 }
 

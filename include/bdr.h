@@ -274,6 +274,27 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k,
                        size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dspark_draft_block_noalloc -- dspark_draft_block for callers that cannot
+ * allocate: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  Same arguments, results and status as
+ * dspark_draft_block with the logits in the caller's logits_out (required),
+ * and no workspace argument: the Markov chain's hand-off slots and counters
+ * live in a static scratch array of BDR_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  Enough for batch * k <= 256;
+ * larger blocks return BDR_EUNSUPPORTED.  The call clears the part of the
+ * scratch it uses (a fill kernel on `stream`, no memset node) and calls no
+ * allocator.  Every call on one GPU shares that GPU's scratch: calls that can
+ * run concurrently on one GPU race and must not be issued.
+ * ------------------------------------------------------------------------- */
+#define BDR_NOALLOC_SCRATCH_BYTES (1280 * 1024)
+int dspark_draft_block_noalloc(const void* draft_hidden, int64_t batch, int k,
+                               int64_t hidden, int64_t vocab, bdr_dtype dt,
+                               const void* lm_head_w, const void* markov_w1,
+                               const void* markov_w2, int rank,
+                               const int32_t* prev_token, int32_t* draft_tokens,
+                               float* logits_out, int32_t* status, void* stream);
+
+/* ---------------------------------------------------------------------------
  * S4  spec_verify_greedy -- greedy exact-match verification of a draft block.
  *
  *   L_b   = min{ i < k : confidence[b, i] < threshold }, else k
