@@ -58,10 +58,12 @@ def kernel_source_hash(sources=GEMM_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, fp8: bool = False):
-    """HBM bytes per LM-head launch from the committed rocprofv3 counter summary,
-    or None when the summary is missing or the kernel has changed since."""
-    name = f"lm_head_gemm_fp8_{workload}_pmc.md" if fp8 else f"lm_head_gemm_{workload}_pmc.md"
+def recorded_traffic(workload: str, fp8: bool = False, kernel: str = "lm_head_gemm"):
+    """HBM bytes per launch of the dominant kernel (the LM head, or the fc and
+    the LM head in one launch: kernel="fc_lm_head_gemm") from the committed
+    rocprofv3 counter summary, or None when the summary is missing or the
+    kernel has changed since."""
+    name = f"{kernel}_fp8_{workload}_pmc.md" if fp8 else f"{kernel}_{workload}_pmc.md"
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -101,6 +103,16 @@ class Step:
         return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
                                      self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
                                      b["ws_fc"], b["ws_fc_n"], self.fc_stream)
+
+    def fc_lm(self):
+        """S1 and S2 in one call (one launch on the batched workloads)."""
+        w, b = self.w, self.b
+        return self.L.dflash_fuse_fc_lm_head(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+                                             self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
+                                             self.s["draft_hidden"].data_ptr(), w.batch * w.k,
+                                             w.vocab, self.g["lm_w"].data_ptr(),
+                                             b["logits"].data_ptr(), b["ws_fcl"], b["ws_fcl_n"],
+                                             self.stream)
 
     def lm_head(self):
         w = self.w
@@ -437,10 +449,13 @@ def main():
     ap.add_argument("--workload", default="adaptive_b16")
     ap.add_argument("--pool", type=int, default=8)
     ap.add_argument("--graph", action="store_true", help="replay HIP graphs of whole steps")
-    ap.add_argument("--overlap", choices=("none", "lm", "chain"), default="chain",
-                    help="run the fc on a second stream, concurrently with the LM head "
-                         "(lm) or with the Markov chain and verification (chain); the fc "
-                         "output feeds the next step's drafter, not S2-S4 of this step")
+    ap.add_argument("--overlap", choices=("auto", "fused", "none", "lm", "chain"), default="auto",
+                    help="auto: whichever of fused and chain is faster over 20 warm steps; "
+                         "fused: the fc and the LM head in one call (dflash_fuse_fc_lm_head); "
+                         "otherwise the fc runs on its own: in order (none), or on a second "
+                         "stream concurrently with the LM head (lm) or with the Markov chain "
+                         "and verification (chain); the fc output feeds the next step's "
+                         "drafter, not S2-S4 of this step")
     ap.add_argument("--draft", choices=("greedy", "sample"), default="greedy",
                     help="greedy drafting + exact-match verification, or probabilistic "
                          "drafting + rejection-sampling verification")
@@ -503,6 +518,12 @@ def main():
     if fp8 and w.dtype != "bf16":
         print(json.dumps({"error": "--weights fp8 needs a bf16 workload"}))
         sys.exit(2)
+    if args.overlap == "auto" and (fp8 or args.closed_loop or args.graph):
+        # the fused call takes bf16 weights; a closed loop runs in order; graphs are
+        # captured before any timing
+        args.overlap = "chain"
+    if fp8 and args.overlap == "fused":
+        args.overlap = "chain"      # the fused call takes bf16 weights
     t0 = time.time()
     W = synth.make_weights_fp8(w) if fp8 else synth.make_weights(w)
     g = {k: up(v) for k, v in W.items()}
@@ -541,6 +562,8 @@ def main():
     for key, n in (("ws_fc", L.dflash_fuse_fc_fp8_workspace_bytes(w.rows, H, w.n_taps) if fp8
                      else L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
                    ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
+                   ("ws_fcl", 0 if fp8 else L.dflash_fuse_fc_lm_head_workspace_bytes(
+                       w.rows, H, w.n_taps, B * k, V, dt)),
                    ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
                    ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
                    ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0),
@@ -620,6 +643,11 @@ def main():
             st.prev = st.s["prev0"].data_ptr()
             loop_state["cur"] = nxt
             return
+        if args.overlap == "fused":
+            check(st.fc_lm(), "dflash_fuse_fc_lm_head")
+            check(st.markov(), "drafting")
+            check(st.verify(), "verification")
+            return
         if args.overlap == "none":
             check(st.fc(), "dflash_fuse_fc")
             check(st.lm_head(), "dspark_lm_head")
@@ -663,6 +691,29 @@ def main():
         else:
             run_step(slots[i % len(slots)])
 
+    # the schedule of the fc: one launch with the LM head, or beside the chain on a
+    # second stream -- whichever runs the whole step faster here (the two are
+    # timed in turn, four rounds of 10 steps each, after 10 warm steps of each)
+    overlap_choice = None
+    if args.overlap == "auto":
+        times = {"fused": 0.0, "chain": 0.0}
+        for rnd in range(5):
+            for cand in ("fused", "chain"):
+                args.overlap = cand
+                ea = torch.cuda.Event(enable_timing=True)
+                eb = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                ea.record(stream)
+                for i in range(10):
+                    step_i(i)
+                eb.record(stream)
+                torch.cuda.synchronize()
+                if rnd > 0:
+                    times[cand] += ea.elapsed_time(eb) / 40 * 1e3
+        args.overlap = min(times, key=times.get)
+        overlap_choice = {k: round(v, 1) for k, v in times.items()}
+        log(f"fc schedule: {args.overlap} (us per step over 40 warm steps: {overlap_choice})")
+
     for i in range(args.warmup):
         step_i(i)
     torch.cuda.synchronize()
@@ -699,15 +750,22 @@ def main():
     log("per-step us (median/p10/p90): " + ", ".join(
         f"{m} {d['median']:.1f}/{d['p10']:.1f}/{d['p90']:.1f}" for m, d in dist.items()))
 
-    # phase 3: the same steps in stream order, HIP events around each LM-head launch
+    # phase 3: the same steps in stream order, HIP events around each launch of the
+    # dominant kernel (the fc and the LM head in one launch when fused, else the LM head)
+    fused = args.overlap == "fused" and not args.closed_loop
     lm_t = LaunchTimer(args.steps)
     torch.cuda.synchronize()
     for i in range(args.steps):
         st = slots[i % len(slots)]
-        check(st.fc(), "dflash_fuse_fc")
-        lm_t.start(i, sptr_now)
-        check(st.lm_head(), "dspark_lm_head")
-        lm_t.stop(i, sptr_now)
+        if fused:
+            lm_t.start(i, sptr_now)
+            check(st.fc_lm(), "dflash_fuse_fc_lm_head")
+            lm_t.stop(i, sptr_now)
+        else:
+            check(st.fc(), "dflash_fuse_fc")
+            lm_t.start(i, sptr_now)
+            check(st.lm_head(), "dspark_lm_head")
+            lm_t.stop(i, sptr_now)
         check(st.markov(), "drafting")
         check(st.verify(), "verification")
     torch.cuda.synchronize()
@@ -715,6 +773,8 @@ def main():
 
     # phase 4: per-stage times (one stage at a time, events on the launch stream)
     stage_fns = (("fc", "fc"), ("lm_head", "lm_head"), ("markov", "markov"), ("verify", "verify"))
+    if not fp8:
+        stage_fns = stage_fns + (("fc_lm_head", "fc_lm"),)
     st_t = LaunchTimer(args.steps * len(stage_fns))
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -754,7 +814,7 @@ def main():
     conf_bytes = 0 if w.threshold is None else B * k * 4
     verify_b = float(np.mean(verify_bytes)) + B * k * 4 + conf_bytes
     stage_bytes = {"fc": fc_bytes, "lm_head": lm_bytes, "markov": markov_bytes,
-                   "verify": verify_b}
+                   "verify": verify_b, "fc_lm_head": fc_bytes + lm_bytes}
     stages = {}
     for name, us in stage_us.items():
         gbs = stage_bytes[name] / (us * 1e-6) / 1e9
@@ -762,12 +822,13 @@ def main():
                         "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
     log("stages: " + ", ".join(f"{n} {v['us']:.1f} us {v['GBs']:.0f} GB/s ({v['frac']:.0%})"
                                for n, v in stages.items()))
-    step_bytes = sum(stage_bytes.values())
-    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(w.name, fp8)
+    step_bytes = fc_bytes + lm_bytes + markov_bytes + verify_b
+    dom_bytes = fc_bytes + lm_bytes if fused else lm_bytes
+    achieved = dom_bytes / (lm_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(w.name, fp8, "fc_lm_head_gemm" if fused else "lm_head_gemm")
     log(f"step {ms_step * 1e3:.1f} us ({step_bytes / 1e6:.1f} MB algorithmic = "
-        f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s); LM head {lm_ms * 1e3:.1f} us = "
-        f"{achieved:.0f} GB/s")
+        f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s); "
+        f"{'fc + LM head' if fused else 'LM head'} {lm_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -807,6 +868,7 @@ def main():
                    "rank": w.rank, "n_taps": w.n_taps, "threshold": w.threshold,
                    "launch": "hip-graph" if graphs is not None else "eager",
                    "fc_overlap": "none (closed loop)" if args.closed_loop else args.overlap,
+                   **({"fc_overlap_auto_us": overlap_choice} if overlap_choice else {}),
                    "loop": "closed" if args.closed_loop else "independent steps",
                    "draft": args.draft,
                    "weights": "fp8-e4m3 codes + fp32 row scales (fc, LM head)" if fp8
@@ -818,9 +880,11 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
                      "kernel": "LM-head weight-streaming GEMM (dspark_lm_head_fp8)" if fp8
-                     else "LM-head weight-streaming GEMM (dspark_lm_head)",
+                     else ("fc + LM-head weight-streaming GEMMs in one launch "
+                           "(dflash_fuse_fc_lm_head)" if fused
+                           else "LM-head weight-streaming GEMM (dspark_lm_head)"),
                      "avg_launch_us": lm_ms * 1e3,
-                     "algorithmic_bytes_per_launch": lm_bytes},
+                     "algorithmic_bytes_per_launch": dom_bytes},
         "stages": stages,
         "step_algorithmic_bytes": int(step_bytes),
         "step_us": {"mean_back_to_back": ms_step * 1e3, **dist,

@@ -20,7 +20,7 @@ from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
 
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
-    "dspark_draft_block_noalloc",
+    "dspark_draft_block_noalloc", "dflash_fuse_fc_lm_head",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
     "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
@@ -230,6 +230,52 @@ def dspark_lm_head_fp8(hidden: torch.Tensor, lm_head_q: torch.Tensor, lm_head_sc
                                                           _ptr(lm_head_q), _ptr(lm_head_scale),
                                                           _ptr(logits), _stream(hidden.device)))
     return logits
+
+
+# ----------------------------------------------------------------------------- S1 + S2
+def dflash_fuse_fc_lm_head(taps: Sequence[torch.Tensor], fc_w: torch.Tensor,
+                           lm_hidden: torch.Tensor, lm_head_w: torch.Tensor,
+                           fc_out: Optional[torch.Tensor] = None,
+                           logits: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None):
+    """(fc_out [rows, H], logits [..., V] fp32): the drafter fc over the taps and the
+    LM head over lm_hidden [..., H] in one call (one launch when both take the
+    row-split kernel)."""
+    L = lib()
+    T = len(taps)
+    rows, H = taps[0].shape
+    for i, t in enumerate(taps):
+        _dev(t, f"taps[{i}]")
+        if t.shape != (rows, H) or t.dtype != fc_w.dtype:
+            raise ValueError("taps must all be [rows, H] with fc_w's dtype")
+    _dev(fc_w, "fc_w")
+    _dev(lm_hidden, "lm_hidden")
+    _dev(lm_head_w, "lm_head_w")
+    if tuple(fc_w.shape) != (H, T * H):
+        raise ValueError(f"fc_w must be [{H}, {T * H}]")
+    V = lm_head_w.shape[0]
+    if lm_head_w.shape[1] != H or lm_hidden.shape[-1] != H:
+        raise ValueError("lm_head_w must be [V, H] and lm_hidden [..., H]")
+    if lm_hidden.dtype != fc_w.dtype or lm_head_w.dtype != fc_w.dtype:
+        raise ValueError("all weights and activations must share one dtype")
+    dt = _dt(fc_w)
+    lm_rows = lm_hidden.numel() // H
+    dev = fc_w.device
+    if fc_out is None:
+        fc_out = torch.empty((rows, H), dtype=fc_w.dtype, device=dev)
+    if logits is None:
+        logits = torch.empty((*lm_hidden.shape[:-1], V), dtype=torch.float32, device=dev)
+    _dev(fc_out, "fc_out")
+    _dev(logits, "logits")
+    need = L.dflash_fuse_fc_lm_head_workspace_bytes(rows, H, T, lm_rows, V, dt)
+    ws = _workspace(need, dev, workspace)
+    wp, wn = _ws_ptr(ws)
+    arr = (C.c_void_p * T)(*[t.data_ptr() for t in taps])
+    _abi.check("dflash_fuse_fc_lm_head",
+               L.dflash_fuse_fc_lm_head(arr, T, rows, H, dt, _ptr(fc_w), _ptr(fc_out),
+                                        _ptr(lm_hidden), lm_rows, V, _ptr(lm_head_w),
+                                        _ptr(logits), wp, wn, _stream(dev)))
+    return fc_out, logits
 
 
 # ----------------------------------------------------------------------------- S3

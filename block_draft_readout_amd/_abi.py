@@ -34,6 +34,9 @@ SIGNATURES = {
     "dflash_fuse_fc_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
     "dflash_fuse_fc": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
     "dspark_lm_head": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
+    "dflash_fuse_fc_lm_head_workspace_bytes": (_sz, [_i64, _i64, _int, _i64, _i64, _int]),
+    "dflash_fuse_fc_lm_head": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp, _i64,
+                                      _i64, _vp, _vp, _vp, _sz, _vp]),
     "dflash_hc_average": (_int, [C.POINTER(_vp), _int, _int, _i64, _i64, _i64, _i64, _int,
                                  C.POINTER(_vp), _vp]),
     "dflash_fuse_fc_fp8_workspace_bytes": (_sz, [_i64, _i64, _int]),

@@ -224,6 +224,74 @@ int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows, int64_t hi
   return BDR_OK;
 }
 
+// ---------------------------------------------------------------------------- S1 + S2 in one launch
+namespace {
+// the pair plan when both GEMMs take it (bf16, row-split shapes), else !ok
+PairPlan fc_lm_pair(int64_t rows, int64_t hidden, int n_taps, int64_t lm_rows, int64_t vocab,
+                    bdr_dtype dt) {
+  if (dt != BDR_BF16 || rows == 0 || lm_rows == 0) return PairPlan{};
+  return plan_gemm_pair(lm_rows, vocab, hidden, rows, hidden, hidden * n_taps, n_taps);
+}
+}  // namespace
+
+size_t dflash_fuse_fc_lm_head_workspace_bytes(int64_t rows, int64_t hidden, int n_taps,
+                                              int64_t lm_rows, int64_t vocab, bdr_dtype dt) {
+  if (fc_shape(rows, hidden, n_taps, dt) != BDR_OK ||
+      lm_shape(lm_rows, hidden, vocab, dt) != BDR_OK)
+    return 0;
+  const PairPlan pp = fc_lm_pair(rows, hidden, n_taps, lm_rows, vocab, dt);
+  if (pp.ok) return pp.workspace;
+  return rows == 0 ? 0 : plan_gemm(rows, hidden, hidden * n_taps, dt, true, n_taps).workspace;
+}
+
+int dflash_fuse_fc_lm_head(const void* const* taps, int n_taps, int64_t rows, int64_t hidden,
+                           bdr_dtype dt, const void* fc_w, void* fc_out, const void* lm_hidden,
+                           int64_t lm_rows, int64_t vocab, const void* lm_head_w, float* logits,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  BDR_TRY(fc_shape(rows, hidden, n_taps, dt));
+  BDR_TRY(lm_shape(lm_rows, hidden, vocab, dt));
+  if (rows > 0) {
+    if (!taps) return fail(BDR_EINVAL, "taps must not be NULL");
+    for (int t = 0; t < n_taps; ++t) {
+      if (!taps[t]) return fail(BDR_EINVAL, "taps[%d] must not be NULL", t);
+      if (!aligned(taps[t], 16)) return fail(BDR_EINVAL, "taps[%d] must be 16-byte aligned", t);
+    }
+    BDR_TRY(need_ptr(fc_w, "fc_w"));
+    BDR_TRY(need_ptr(fc_out, "fc_out"));
+  }
+  if (lm_rows > 0) {
+    BDR_TRY(need_ptr(lm_hidden, "lm_hidden"));
+    BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));
+    BDR_TRY(need_ptr(logits, "logits"));
+  }
+  if (rows == 0 && lm_rows == 0) return BDR_OK;
+  const PairPlan pp = fc_lm_pair(rows, hidden, n_taps, lm_rows, vocab, dt);
+  const GemmPlan pf = rows > 0 && !pp.ok ? plan_gemm(rows, hidden, hidden * n_taps, dt, true, n_taps)
+                                         : GemmPlan{};
+  BDR_TRY(need_ws(workspace, workspace_bytes, pp.ok ? pp.workspace : pf.workspace));
+  BDR_TRY(check_device());
+  const hipStream_t st = as_stream(stream);
+  hipError_t e;
+  if (pp.ok) {
+    e = launch_gemm_pair(pp, lm_hidden, lm_head_w, logits, taps, n_taps, hidden, fc_w, fc_out,
+                         workspace, st);
+    if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_lm_head launch");
+    return BDR_OK;
+  }
+  if (rows > 0) {
+    e = launch_gemm(pf, dt, taps, n_taps, hidden, rows, hidden, fc_w, fc_out,
+                    dt == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace, st);
+    if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_lm_head fc launch");
+  }
+  if (lm_rows > 0) {
+    const GemmPlan pl = plan_gemm(lm_rows, vocab, hidden, dt, false);
+    const void* a[1] = {lm_hidden};
+    e = launch_gemm(pl, dt, a, 1, hidden, lm_rows, vocab, lm_head_w, logits, OUT_F32, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_lm_head LM-head launch");
+  }
+  return BDR_OK;
+}
+
 // ---------------------------------------------------------------------------- S2
 int dspark_lm_head(const void* hidden, int64_t rows, int64_t hidden_size, int64_t vocab,
                    bdr_dtype dt, const void* lm_head_w, float* logits, void* stream) {

@@ -447,6 +447,82 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   return true;
 }
 
+// Pair plan: the compute units are shared in proportion to each problem's
+// cost (weight bytes + a quarter of the A bytes staged per pass + split-K
+// partials), the split of problem 1 chosen so that its slowest workgroup and
+// problem 0's finish together.
+static double ns_wg_cost(int64_t M, int64_t rows, int64_t kbps, int ntw, int64_t ks, int64_t N) {
+  const int64_t tiles_w = ((rows + 3) / 4 + 15) / 16;
+  const int64_t npass = (tiles_w + ntw - 1) / ntw;
+  double c = static_cast<double>(kbps) * 128 * (2.0 * rows + 0.5 * M * npass);
+  if (ks > 1) c += static_cast<double>(ks) * M * N * 8 / kNumCU;
+  return c;
+}
+
+PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1,
+                        int n_seg1) {
+  PairPlan pp;
+  GemmPlan q0, q1;
+  if (!plan_ns(M0, N0, K0, 2, false, 1, &q0) || !plan_ns(M1, N1, K1, 2, true, n_seg1, &q1))
+    return pp;
+  if (q1.mt != q0.mt && q1.mt != q0.mt + 1) return pp;
+  const int ntw0 = ns_tiles(q0.mt), ntw1 = ns_tiles(q1.mt);
+  const int64_t kb0 = q0.kblocks, kb1 = q1.kblocks;
+  // passes of problem 0's waves on its own (one workgroup per compute unit):
+  // sharing the chip must not add a pass (each restages the whole A matrix)
+  auto passes0 = [&](int64_t nwg) {
+    const int64_t tiles_w = (((N0 + nwg - 1) / nwg + 3) / 4 + 15) / 16;
+    return (tiles_w + ntw0 - 1) / ntw0;
+  };
+  const int64_t alone = passes0(q0.n_waves);
+  double best = 1e300, best_c0 = 0, best_c1 = 0;
+  for (int64_t ks = 1; ks <= std::min<int64_t>(8, kb1); ++ks) {
+    const int64_t kbps = (kb1 + ks - 1) / ks;
+    const int64_t ks_eff = (kb1 + kbps - 1) / kbps;
+    for (int64_t nx = 1; nx * ks_eff <= kNumCU / 2 && nx <= (N1 + 63) / 64; ++nx) {
+      const int64_t n1 = nx * ks_eff, n0 = kNumCU - n1;
+      if (n0 > (N0 + 63) / 64 || passes0(n0) > alone) continue;
+      const double c0 = ns_wg_cost(M0, (N0 + n0 - 1) / n0, kb0, ntw0, 1, N0);
+      const double c1 = ns_wg_cost(M1, (N1 + nx - 1) / nx, kbps, ntw1, ks_eff, N1);
+      const double c = std::max(c0, c1);
+      if (c < best) {
+        best = c;
+        best_c0 = c0;
+        best_c1 = c1;
+        pp.n0 = static_cast<unsigned>(n0);
+        pp.n1 = static_cast<unsigned>(n1);
+        q1.n_waves = nx;
+        q1.ksplit = static_cast<int>(ks_eff);
+        q1.kb_per_split = kbps;
+      }
+    }
+  }
+  if (pp.n0 == 0) return pp;
+  // one launch only when problem 1's workgroups finish with problem 0's: when
+  // the pass rule leaves too few compute units for problem 1, two launches one
+  // after the other are faster
+  if (best_c1 > 1.15 * best_c0) {
+    pp.n0 = pp.n1 = 0;
+    return pp;
+  }
+  q0.n_waves = pp.n0;
+  q0.ksplit = 1;
+  q0.kb_per_split = kb0;
+  q0.workspace = 0;
+  q1.workspace = q1.ksplit > 1 ? align256(static_cast<size_t>(q1.ksplit) * M1 * N1 * 4) : 0;
+  // the row ranges must keep their 32-bit offsets with the fewer workgroups
+  const int64_t rows_w0 = ((N0 + pp.n0 - 1) / pp.n0 + 3) / 4;
+  const int64_t rows_w1 = ((N1 + q1.n_waves - 1) / q1.n_waves + 3) / 4;
+  if ((rows_w0 + 16) * K0 * 2 >= (int64_t(1) << 31) || (rows_w1 + 16) * K1 * 2 >= (int64_t(1) << 31))
+    return pp;
+  pp.p0 = q0;
+  pp.p1 = q1;
+  pp.workspace = q1.workspace;
+  pp.M0 = M0, pp.N0 = N0, pp.K0 = K0, pp.M1 = M1, pp.N1 = N1, pp.K1 = K1;
+  pp.ok = true;
+  return pp;
+}
+
 // bounds keeping the tiled variant's tile count and indices in 32 bits
 constexpr int64_t kMaxTileRows = int64_t(1) << 22;
 constexpr int64_t kMaxTileCols = int64_t(1) << 22;
@@ -648,6 +724,38 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(p, M, N, out, out_kind, workspace, stream);
+}
+
+hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, float* out0,
+                            const void* const* a1, int n_seg1, int64_t seg1, const void* w1,
+                            void* out1, void* workspace, hipStream_t stream) {
+  if (!pp.ok) return hipErrorInvalidValue;
+  GemmArgs g0{};
+  g0.a[0] = a0;
+  g0.seg = pp.K0;
+  g0.M = pp.M0;
+  g0.N = pp.N0;
+  g0.K = pp.K0;
+  g0.w = w0;
+  g0.out = out0;
+  g0.out_kind = OUT_F32;
+  g0.partial = 0;
+  GemmArgs g1{};
+  for (int t = 0; t < n_seg1; ++t) g1.a[t] = a1[t];
+  g1.seg = seg1;
+  g1.M = pp.M1;
+  g1.N = pp.N1;
+  g1.K = pp.K1;
+  g1.w = w1;
+  g1.out_kind = OUT_BF16;
+  const bool split = pp.p1.ksplit > 1;
+  g1.partial = split ? 1 : 0;
+  g1.out = split ? workspace : out1;
+  const StreamArgs s0{g0, pp.p0.n_waves, pp.p0.kblocks, pp.p0.kb_per_split};
+  const StreamArgs s1{g1, pp.p1.n_waves, pp.p1.kblocks, pp.p1.kb_per_split};
+  hipError_t e = launch_ns_pair_bf16(pp.p0.mt, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream);
+  if (e != hipSuccess || !split) return e;
+  return launch_splitk_reduce(pp.p1, pp.M1, pp.N1, out1, OUT_BF16, workspace, stream);
 }
 
 hipError_t launch_gemm_fp8(const GemmPlan& p, const void* const* a, int n_seg, int64_t seg,

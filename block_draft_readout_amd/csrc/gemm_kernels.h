@@ -460,5 +460,7 @@ hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t s
 // row-split workgroup kernel (gemm_ns.h): bf16 and fp8 weights, bf16 A
 hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_ns_pair_bf16(int mt0, int mt1, const StreamArgs& a0, const StreamArgs& a1,
+                               unsigned n0, unsigned n1, hipStream_t st);
 
 }  // namespace bdr

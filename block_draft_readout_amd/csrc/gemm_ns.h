@@ -97,8 +97,10 @@ __device__ __forceinline__ void ns_wait(int c) {
   BDR_WAIT_VM_LGKM(NI * C, 15);
 }
 
+// One workgroup's share of C: row range bx of sa.n_waves, K split by; lds is
+// the workgroup's dynamic LDS (ns_lds_bytes<S, MT>() bytes).
 template <typename S, int MT, int NTW>
-__global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
+__device__ __forceinline__ void ns_body(const StreamArgs& sa, unsigned bx, unsigned by, char* lds) {
   using SH = NsShape<S>;
   constexpr bool F8 = SH::F8;
   constexpr int VT = ns_vt<S, MT>();
@@ -111,7 +113,6 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   constexpr int NA = MT;                    // A loads per wave per block (4 * MT in all)
   static_assert(NI * kAhead + NA <= 63, "vmcnt range");
   const GemmArgs& g = sa.g;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int r16 = lane & 15;
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   // aligned 64-byte store (a range starting mid-tile made every piece straddle
   // two 64-byte blocks: 1.8x the logits' bytes written)
   const int64_t n_t = (g.N + 15) / 16;
-  const int64_t t_lo = static_cast<int64_t>(blockIdx.x) * n_t / sa.n_waves;
-  const int64_t t_hi = static_cast<int64_t>(blockIdx.x + 1) * n_t / sa.n_waves;
+  const int64_t t_lo = static_cast<int64_t>(bx) * n_t / sa.n_waves;
+  const int64_t t_hi = static_cast<int64_t>(bx + 1) * n_t / sa.n_waves;
   // (row indices fit 31 bits; readfirstlane keeps everything derived from the
   // wave index in scalar registers, so the load descriptors stay uniform)
   const int n_lo = __builtin_amdgcn_readfirstlane(
@@ -137,11 +138,11 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   const int npass = max(1, (max_tiles + NTW - 1) / NTW);
   const int pbase = ntiles / npass, prem = ntiles - pbase * npass;
   auto pass_lo = [&](int p) { return p * pbase + min(p, prem); };
-  const uint32_t kb_lo = static_cast<uint32_t>(blockIdx.y * sa.kb_per_split);
+  const uint32_t kb_lo = static_cast<uint32_t>(by * sa.kb_per_split);
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
   if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
   const int nkb = static_cast<int>(kb_hi - kb_lo);
-  const OutRef out(g, blockIdx.y);
+  const OutRef out(g, by);
   const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
   const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
@@ -343,6 +344,29 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   }
 }
 
+template <typename S, int MT, int NTW>
+__global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  ns_body<S, MT, NTW>(sa, blockIdx.x, blockIdx.y, lds);
+}
+
+// Two GEMMs in one launch (the drafter fc beside the LM head): the first n0
+// workgroups take problem 0 (row ranges of a0, no K split); the others take
+// problem 1, workgroup n0 + i being row range i % a1.n_waves of K split
+// i / a1.n_waves.  Problem 1 has MT or MT + 1 row tiles (MT1).
+template <typename S, int MT0, int MT1>
+__global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a0,
+                                                              const StreamArgs a1, unsigned n0) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if (blockIdx.x < n0) {
+    ns_body<S, MT0, NsTiles<MT0>::NTW>(a0, blockIdx.x, 0, lds);
+  } else {
+    const unsigned i = blockIdx.x - n0;
+    const unsigned nx = static_cast<unsigned>(a1.n_waves);
+    ns_body<S, MT1, NsTiles<MT1>::NTW>(a1, i % nx, i / nx, lds);
+  }
+}
+
 template <typename S, int MT>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
   constexpr int NTW = NsTiles<MT>::NTW;
@@ -357,6 +381,28 @@ hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
   const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
   hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, NTW>), grid, dim3(64 * kNsWaves),
                      (ns_lds_bytes<S, MT>()), st, sa);
+  return hipGetLastError();
+}
+
+}  // namespace bdr
+
+namespace bdr {
+
+template <typename S, int MT0, int MT1>
+hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
+                              unsigned n1, hipStream_t st) {
+  constexpr size_t lds = ns_lds_bytes<S, MT0>() > ns_lds_bytes<S, MT1>() ? ns_lds_bytes<S, MT0>()
+                                                                         : ns_lds_bytes<S, MT1>();
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ws_gemm_ns_pair_kernel<S, MT0, MT1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((ws_gemm_ns_pair_kernel<S, MT0, MT1>), dim3(n0 + n1), dim3(64 * kNsWaves),
+                     lds, st, a0, a1, n0);
   return hipGetLastError();
 }
 

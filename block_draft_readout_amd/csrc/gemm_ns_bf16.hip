@@ -18,4 +18,30 @@ hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t s
   }
 }
 
+// the fc (mt1 = mt0 or mt0 + 1 row tiles) beside the LM head (mt0 row tiles)
+hipError_t launch_ns_pair_bf16(int mt0, int mt1, const StreamArgs& a0, const StreamArgs& a1,
+                               unsigned n0, unsigned n1, hipStream_t st) {
+  const bool same = mt1 == mt0;
+  if (!same && mt1 != mt0 + 1) return hipErrorInvalidValue;
+#define BDR_PAIR(m)                                                                    \
+  case m:                                                                              \
+    return same ? launch_ns_pair_one<uint16_t, m, m>(a0, a1, n0, n1, st)               \
+                : launch_ns_pair_one<uint16_t, m, (m < 10 ? m + 1 : 10)>(a0, a1, n0, n1, st);
+  switch (mt0) {
+    BDR_PAIR(2)
+    BDR_PAIR(3)
+    BDR_PAIR(4)
+    BDR_PAIR(5)
+    BDR_PAIR(6)
+    BDR_PAIR(7)
+    BDR_PAIR(8)
+    BDR_PAIR(9)
+    case 10:
+      return same ? launch_ns_pair_one<uint16_t, 10, 10>(a0, a1, n0, n1, st)
+                  : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+#undef BDR_PAIR
+}
+
 }  // namespace bdr

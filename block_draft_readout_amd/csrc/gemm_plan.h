@@ -53,6 +53,24 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,
                        OutKind out_kind, void* workspace, hipStream_t stream);
 
+// Two bf16 GEMMs in one launch of the row-split kernel: problem 0 (the LM
+// head: no K split) and problem 1 (the drafter fc: n_seg1 segments, optional
+// K split) share the chip, each workgroup taking part of one of them.  ok is
+// false when either shape does not take the row-split kernel or their row tile
+// counts differ by more than one.
+struct PairPlan {
+  bool ok = false;
+  GemmPlan p0, p1;        // n_waves = workgroups along N; p1.ksplit along K
+  unsigned n0 = 0, n1 = 0;
+  size_t workspace = 0;   // problem 1's split-K partials
+  int64_t M0 = 0, N0 = 0, K0 = 0, M1 = 0, N1 = 0, K1 = 0;
+};
+PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1,
+                        int n_seg1);
+hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, float* out0,
+                            const void* const* a1, int n_seg1, int64_t seg1, const void* w1,
+                            void* out1, void* workspace, hipStream_t stream);
+
 // hyper-connection stream average of each tap: dst[t][r, h] = mean_s src[t][s*ss + r*rs + h]
 hipError_t launch_hc_average(const void* const* src, void* const* dst, int n_taps, int hc,
                              int64_t rows, int64_t hidden, int64_t stream_stride,

@@ -194,6 +194,37 @@ int dspark_lm_head_fp8(const void* hidden, int64_t rows, int64_t hidden_size,
                        const float* lm_head_scale, float* logits, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * S1 + S2  dflash_fuse_fc_lm_head -- the drafter fc (exactly dflash_fuse_fc)
+ * and the LM head (exactly dspark_lm_head) in one call.
+ *
+ * Both steps stream a weight matrix against a few hundred rows at most ([pr128]
+ * "What was missing" item 1: the concatenated tap features through fc.weight;
+ * [recipe] DSpark port notes: the proposer's full-vocabulary logits).  When
+ * both are bf16 with 16 < rows <= 160 they run as one launch in which every
+ * compute unit takes part of one of the two matrices, so neither runs on a
+ * partly idle chip; otherwise the two are launched in order.  The fc output
+ * is rounded to bf16 from a sum of fp32 partials over at most 8 ranges of the
+ * reduction (fixed order), so it can differ from dflash_fuse_fc's by the
+ * rounding of a different summation order; the logits equal dspark_lm_head's
+ * bit for bit.
+ *
+ *   taps, n_taps, rows, hidden, dt, fc_w, fc_out: as dflash_fuse_fc (out)
+ *   lm_hidden   [lm_rows, H] dtype; lm_head_w [V, H] dtype; logits [lm_rows, V]
+ *               fp32 out -- as dspark_lm_head
+ *   workspace   >= dflash_fuse_fc_lm_head_workspace_bytes(...) (may be NULL
+ *               when that returns 0)
+ * ------------------------------------------------------------------------- */
+size_t dflash_fuse_fc_lm_head_workspace_bytes(int64_t rows, int64_t hidden,
+                                              int n_taps, int64_t lm_rows,
+                                              int64_t vocab, bdr_dtype dt);
+int dflash_fuse_fc_lm_head(const void* const* taps, int n_taps, int64_t rows,
+                           int64_t hidden, bdr_dtype dt, const void* fc_w,
+                           void* fc_out, const void* lm_hidden, int64_t lm_rows,
+                           int64_t vocab, const void* lm_head_w, float* logits,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * S3  dspark_markov_argmax -- Markov bigram bias + semi-autoregressive argmax.
  *
  * For each row b: p = prev_token[b]; for i = 0..k-1:
