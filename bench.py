@@ -39,7 +39,7 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_wg1.hip", "gemm_wg2.hip", "gemm_wg3.hip",
+GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h",
                 "gemm_ns.h", "gemm_ns_bf16.hip", "bdr_device.h", "gemm_plan.h")
 GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_kernels.h",
                     "bdr_device.h", "gemm_plan.h")

@@ -11,11 +11,9 @@
 //   * ws_gemm_ns_kernel (16 < M <= 160, bf16 or fp8 weights): four-wave
 //     workgroups, each wave streaming its own W rows, the A slice staged once
 //     per workgroup and K block (gemm_ns.h, instantiated in gemm_ns_*.hip);
-//   * ws_gemm_stream_wg_kernel (16 < M <= 160, fp32): four-wave workgroups
-//     sharing each W visit (gemm_kernels.h, instantiated in gemm_wg1/2/3.hip);
 //   * gemm_tile_kernel (bf16, M > 160): LDS-tiled MFMA GEMM (gemm_tile.hip);
 //   * ws_gemm_kernel: a register-only fallback for the shapes the others do
-//     not take (tap segments not a multiple of 128 elements, fp32 M > 160);
+//     not take (fp32 with M > 16, tap segments not a multiple of 128 elements);
 //   * when N alone gives too few workgroups (the fc: N = H), K is split too;
 //     partials are summed in a fixed order by splitk_reduce_kernel, so the
 //     result is deterministic.
@@ -346,56 +344,6 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
   return true;
 }
 
-// Shared-visit workgroup plan (fp32, 16 < M <= 160): one workgroup per
-// compute unit and K split (a single round), each walking its row range in
-// passes of at most 8 tiles (accumulator budget).  The K split minimises the
-// per-compute-unit cost W bytes + a quarter of the A bytes re-read per pass
-// (+ the partial-sum round trip).
-static bool plan_stream_wg(int64_t M, int64_t N, int64_t K, int esize, bool allow_split,
-                           int n_seg, GemmPlan* p) {
-  const int64_t kbytes = K * esize;
-  const int64_t segbytes = kbytes / n_seg;
-  const int64_t mtiles = (M + 15) / 16;
-  if (esize != 4 || M <= 16 || mtiles > kWgMaxTiles || kbytes % 64 != 0) return false;
-  const int mtw = static_cast<int>((mtiles + kWgWaves - 1) / kWgWaves);
-  const int kbb = kWgKBB;
-  if (n_seg > 1 && segbytes % kbb != 0) return false;
-  const int ntmax = 8;
-  const int64_t kblocks = (kbytes + kbb - 1) / kbb;
-  double best = 1e300;
-  int64_t best_tiles = 0;
-  for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
-    const int64_t kbps = (kblocks + ks - 1) / ks;
-    const int64_t ks_eff = (kblocks + kbps - 1) / kbps;
-    if (ks_eff > kNumCU) continue;
-    int64_t nw = std::max<int64_t>(1, kNumCU / ks_eff);
-    nw = std::min<int64_t>(nw, (N + 15) / 16);
-    const int64_t rows = (N + nw - 1) / nw;
-    const int64_t tiles = (rows + 15) / 16;
-    const int64_t npass = (tiles + ntmax - 1) / ntmax;
-    double cost = static_cast<double>(kbps) * kbb * (rows + 0.25 * M * npass);
-    if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / kNumCU;
-    if (cost < best) {
-      best = cost;
-      best_tiles = (tiles + npass - 1) / npass;
-      p->n_waves = nw;
-      p->kb_per_split = kbps;
-      p->ksplit = static_cast<int>(ks_eff);
-    }
-  }
-  p->stream = true;
-  p->wg = true;
-  p->kbb = kbb;
-  p->mtw = mtw;
-  p->kblocks = kblocks;
-  p->nt = best_tiles <= 8 ? 8 : 0;
-  p->mt = static_cast<int>(mtiles);
-  p->m_groups = 1;
-  p->n_wg = p->n_waves;
-  p->workspace = p->ksplit > 1 ? align256(static_cast<size_t>(p->ksplit) * M * N * 4) : 0;
-  return p->nt > 0;
-}
-
 // Row-split workgroup plan (gemm_ns.h; bf16 or fp8 weights, bf16 A, 16 < M <=
 // 160): K blocks of 128 elements that never straddle a tap segment; one
 // workgroup per compute unit and K split, its rows split over four waves, each
@@ -584,8 +532,6 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
   {
     GemmPlan q;
     if (plan_ns(M, N, K, esize, allow_split, n_seg, &q)) return q;
-    q = GemmPlan{};
-    if (plan_stream_wg(M, N, K, esize, allow_split, n_seg, &q)) return q;
     if (plan_tile(M, N, K, esize, allow_split, n_seg, &q)) return q;
   }
   const int64_t mtiles = std::max<int64_t>(1, (M + 15) / 16);
@@ -704,12 +650,6 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   } else if (p.ns) {
     const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
     const hipError_t le = launch_ns_bf16(p, sa, stream);
-    if (le != hipSuccess) return le;
-  } else if (p.wg) {
-    const StreamArgs sa{g, p.n_waves, p.kblocks, p.kb_per_split};
-    const hipError_t le = p.mtw == 1   ? launch_wg_mtw1(p, sa, stream)
-                          : p.mtw == 2 ? launch_wg_mtw2(p, sa, stream)
-                                       : launch_wg_mtw3(p, sa, stream);
     if (le != hipSuccess) return le;
   } else if (p.stream) {
     if (dt == BDR_BF16)

@@ -23,13 +23,9 @@ struct GemmPlan {
   int64_t steps_per_split = 0;
   size_t workspace = 0;   // bytes of split-K partials
   // streaming variants: balanced row ranges x K-block ranges; one wave per
-  // range (M <= 16) or a four-wave workgroup per range (wg, 16 < M <= 192)
+  // range (M <= 16) or a four-wave workgroup per range (ns, 16 < M <= 160)
   bool stream = false;
-  bool wg = false;
   bool ns = false;        // row-split workgroup kernel (gemm_ns.h), mt = A row tiles
-  int kbb = 1024;         // W bytes per row per visit
-  int mtw = 1;            // A row tiles per wave (wg)
-  int nt = 1;             // 16-row W tiles per range (compile-time bound)
   int64_t n_waves = 0;    // row ranges (workgroups along N)
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;

@@ -1,8 +1,9 @@
 """GPU parity of the weight-streaming GEMM (drafter fc and LM head) across the
 shapes that select each kernel variant: the row-split workgroup kernel for
 bf16 with 2 to 10 A row tiles (tap segments, ranges walked in several passes,
-ragged M / N / K, split K), the shared-visit kernel for fp32, the tiled kernel
-above 160 rows, and the fallbacks just outside those shapes.  Compared with
+ragged M / N / K, split K), the register kernel that fp32 with more than 16
+rows takes, the tiled kernel above 160 rows, and the fallbacks just outside
+those shapes.  Compared with
 the oracle's float64 products."""
 import dataclasses
 
@@ -43,16 +44,16 @@ SHAPES = {
                     vocab=40000, rank=8),
     "m30_v60k": _w("m30_v60k", 48, "flashnext_b4", batch=6, k=5, hidden=512, n_taps=2,
                    vocab=60000, rank=8),
-    # ranges walked in two passes: LM M=112 over 100003 rows (25 tiles per range),
-    # and fp32 LM M=40 over 40000 rows (10 tiles per range, 8 per pass)
+    # ranges walked in two passes: LM M=112 over 100003 rows (25 tiles per range);
+    # fp32 LM M=40 over 40000 rows (the register kernel)
     "m112_v100k": _w("m112_v100k", 49, "b16", batch=16, k=7, hidden=256, n_taps=2,
                      vocab=100003, rank=8),
     "f32_m40_v40k": _w("f32_m40_v40k", 50, "tiny", batch=8, k=5, hidden=64, n_taps=2,
                        vocab=40000, rank=8),
-    # fp32: fc M=42, LM M=35 on 512-byte segments
+    # fp32: fc M=42, LM M=35 (the register kernel)
     "f32_m42": _w("f32_m42", 45, "tiny", batch=7, k=5, hidden=128, n_taps=2, vocab=2999,
                   rank=8),
-    # fp32: LM M=140 (3 tiles / wave) with a partial K block; fc falls back (256-byte segments)
+    # fp32: LM M=140 and fc M=160 (the register kernel)
     "f32_m140": _w("f32_m140", 46, "tiny", batch=20, k=7, hidden=64, n_taps=2, vocab=1500,
                    rank=8),
     # tiled kernel (M > 160): fc M=300 (ragged row tile, ragged 160-column tile, split K over
