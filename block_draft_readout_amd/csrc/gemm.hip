@@ -350,7 +350,9 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
 // walking its tiles in passes of ns_tiles(mt).  The K split minimises the
 // per-compute-unit cost W bytes + a quarter of the A bytes staged per pass (+
 // the partial-sum round trip).
-static int ns_tiles(int mt) {      // NsTiles<MT>::NTW
+static int ns_tiles(int mt, int esize) {   // NsLean<MT>::NTW (bf16), NsTiles<MT>::NTW (fp8)
+  if (esize == 2)
+    return mt <= 2 ? 16 : mt == 3 ? 14 : mt == 4 ? 12 : mt <= 6 ? 6 : mt <= 8 ? 5 : mt == 9 ? 4 : 3;
   return mt <= 3 ? 16 : mt == 4 ? 12 : mt == 5 ? 9 : mt == 6 ? 8 : mt == 7 ? 6 : mt == 8 ? 5
          : mt == 9 ? 4 : 3;
 }
@@ -361,7 +363,7 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   const int64_t mtiles = (M + 15) / 16;
   if (esize > 2 || M <= 16 || mtiles > 10 || K % (esize == 1 ? 16 : 8) != 0) return false;
   if (n_seg > 1 && (K / n_seg) % KE != 0) return false;
-  const int ntw = ns_tiles(static_cast<int>(mtiles));
+  const int ntw = ns_tiles(static_cast<int>(mtiles), esize);
   const int64_t kblocks = (K + KE - 1) / KE;
   double best = 1e300;
   for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
@@ -413,8 +415,8 @@ PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t 
   GemmPlan q0, q1;
   if (!plan_ns(M0, N0, K0, 2, false, 1, &q0) || !plan_ns(M1, N1, K1, 2, true, n_seg1, &q1))
     return pp;
-  if (q1.mt != q0.mt && q1.mt != q0.mt + 1) return pp;
-  const int ntw0 = ns_tiles(q0.mt), ntw1 = ns_tiles(q1.mt);
+  if ((q1.mt != q0.mt && q1.mt != q0.mt + 1) || q1.mt > 9) return pp;
+  const int ntw0 = ns_tiles(q0.mt, 2), ntw1 = ns_tiles(q1.mt, 2);
   const int64_t kb0 = q0.kblocks, kb1 = q1.kblocks;
   // passes of problem 0's waves on its own (one workgroup per compute unit):
   // sharing the chip must not add a pass (each restages the whole A matrix)

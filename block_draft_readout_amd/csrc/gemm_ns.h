@@ -344,10 +344,238 @@ __device__ __forceinline__ void ns_body(const StreamArgs& sa, unsigned bx, unsig
   }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 weights: the same organisation with a schedule fixed at compile time, so
+// the loop carries almost no bookkeeping (the generic loop above spent about
+// as many scalar instructions as MFMAs and kept the MFMA pipe ~28 % busy):
+//   * every pass has NTW tile slots; a wave's tiles past its range (at most a
+//     few in its last pass) read nothing (out-of-range loads) and are not
+//     stored;
+//   * the ring holds R visits with R dividing NTW, so the slot of tile t of
+//     every block is t % R and the visit loaded at step t -- R - 1 ahead, the
+//     slot consumed at step t - 1 -- is known at compile time, within this
+//     block or the next (or the next pass's first);
+//   * every block issues its MT A-staging loads (out of range past the last
+//     block or row), so each wait counts a compile-time number of loads:
+//     before the block's barrier NI * NTW (NI * (R - 1) for the first), before
+//     step t NI * (R - 1), + MT while the visit predates the block's A loads.
+// ----------------------------------------------------------------------------
+template <int MT> struct NsLean {   // tiles per pass, ring slots (as deep as LDS allows)
+  static constexpr int NTW = MT <= 2 ? 16 : MT == 3 ? 14 : MT == 4 ? 12 : MT <= 6 ? 6
+                           : MT <= 8 ? 5 : MT == 9 ? 4 : 3;
+  static constexpr int R = MT <= 2 ? 8 : MT == 3 ? 7 : MT <= 6 ? 6 : MT <= 8 ? 5 : MT == 9 ? 4 : 3;
+};
+
+template <int MT>
+constexpr size_t ns_lean_lds_bytes() {
+  using SH = NsShape<uint16_t>;
+  return static_cast<size_t>(kNsWaves * NsLean<MT>::R * SH::SLOT) +
+         static_cast<size_t>(2 * MT) * SH::ASLOT;
+}
+
+template <int N>
+__device__ __forceinline__ void ns_wait_vm() {
+  constexpr int n = N > 63 ? 63 : N;   // (a stricter wait is always safe)
+  BDR_WAIT_VM_LGKM(n, 15);
+}
+
+template <int MT>
+__device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, unsigned by,
+                                             char* lds) {
+  using S = uint16_t;
+  using SH = NsShape<S>;
+  constexpr int NTW = NsLean<MT>::NTW;
+  constexpr int R = NsLean<MT>::R;
+  static_assert(NTW % R == 0, "the ring divides the pass");
+  static_assert(ns_lean_lds_bytes<MT>() <= 160 * 1024, "LDS budget");
+  constexpr int NI = SH::NI;        // loads per visit
+  constexpr int NA = MT;            // A loads per wave per block
+  static_assert(NI * (R - 1) + NA <= 63, "vmcnt range");
+  const GemmArgs& g = sa.g;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  // tile-aligned ranges as in ns_body
+  const int64_t n_t = (g.N + 15) / 16;
+  const int64_t t_lo = static_cast<int64_t>(bx) * n_t / sa.n_waves;
+  const int64_t t_hi = static_cast<int64_t>(bx + 1) * n_t / sa.n_waves;
+  const int n_lo = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(16 * (t_lo + (t_hi - t_lo) * wave / kNsWaves)));
+  const int n_hi = __builtin_amdgcn_readfirstlane(static_cast<int>(
+      min<int64_t>(g.N, 16 * (t_lo + (t_hi - t_lo) * (wave + 1) / kNsWaves))));
+  const int max_tiles = static_cast<int>((t_hi - t_lo + kNsWaves - 1) / kNsWaves);
+  const int npass = max(1, (max_tiles + NTW - 1) / NTW);
+  const uint32_t kb_lo = static_cast<uint32_t>(by * sa.kb_per_split);
+  const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
+  if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
+  const OutRef out(g, by);
+  const uint32_t kbytes = static_cast<uint32_t>(g.K * 2);
+  const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
+  const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
+  const uint32_t wrows = static_cast<uint32_t>(n_hi > n_lo ? n_hi - n_lo : 0);
+  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
+                              wrows * kbytes);
+  char* const ring = lds + wave * (R * SH::SLOT);
+  char* const stage = lds + kNsWaves * R * SH::SLOT;             // [2][MT][ASLOT]
+  // lane mappings of ns_body (loads: consecutive lanes on one row, chunks
+  // XOR-permuted by the row in the load; operand reads undo the permutation)
+  constexpr int CPR = SH::WROW / 16;
+  const uint32_t w_chunk = static_cast<uint32_t>((lane % CPR) ^ (lane / CPR)) * 16;
+  uint32_t lane_off = static_cast<uint32_t>(lane / CPR) * kbytes + w_chunk;
+  asm volatile("" : "+v"(lane_off));
+  const uint32_t a_row = static_cast<uint32_t>(lane / 16);
+  const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ (lane / 16)) * 16;
+  const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
+  const int rs = r16 % SH::RPI;
+  const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
+  const int rs_a = r16 % 4;
+  const uint32_t tile_bytes = 16 * kbytes;
+  const uint32_t pass_bytes = static_cast<uint32_t>(NTW) * tile_bytes;
+  // the last K block may be partial: its row pieces end at tail_bytes
+  const uint32_t tail_bytes = kbytes - (static_cast<uint32_t>(sa.kblocks) - 1) * SH::WROW;
+  const uint32_t kb_last = static_cast<uint32_t>(sa.kblocks) - 1;
+
+  f32x4_t acc[NTW][MT];
+  auto zero_acc = [&]() {
+    static_for<NTW>([&](auto t) {
+      static_for<MT>([&](auto m) { acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; });
+    });
+  };
+  zero_acc();
+  u32x4_t a[MT][4];
+
+  // visit -> ring slot: sb = the visit's byte offset within this wave's rows
+  // (pass base + K block + tile), kOOB for a visit past the last pass
+  auto dma_w = [&](uint32_t sb, uint32_t kb, int slot) {
+    char* dst = ring + slot * SH::SLOT;
+    const bool cut = kb == kb_last && w_chunk >= tail_bytes;   // past a partial block's end
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t s_off = __builtin_amdgcn_readfirstlane(
+          sb == kOOB ? kOOB : sb + static_cast<uint32_t>(j * SH::RPI) * kbytes);
+      const uint32_t off = cut ? kOOB : lane_off + s_off;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16, off, 0, 0, 2);
+    }
+  };
+  // this wave's share of the A slice of block kb -> staging buffer b (all MT
+  // loads issued, out of range when !valid or past M)
+  auto dma_a = [&](uint32_t kb, int b, bool valid) {
+    const uint32_t k0 = kb * (kNsKE * 2);
+    const uint32_t ts = k0 / segbytes;
+    const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
+    const uint32_t lo = (valid && k0 + a_chunk < kbytes) ? (k0 - ts * segbytes) + a_chunk : kOOB;
+    char* dst = stage + b * (MT * SH::ASLOT);
+    static_for<MT>([&](auto i) {
+      const int j = wave + kNsWaves * i;
+      const int mt = j / 4;
+      const uint32_t row = static_cast<uint32_t>(16 * mt + 4 * (j % 4)) + a_row;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(dst + mt * SH::ASLOT + (j % 4) * (1024 + 64)),
+          16, lo == kOOB ? kOOB : lo + row * segbytes, 0, 0, 0);
+    });
+  };
+  auto stage_to_regs = [&](int b) {
+    const char* src = stage + b * (MT * SH::ASLOT) + rd_a;
+    static_for<MT>([&](auto m) {
+      static_for<4>([&](auto i) {
+        a[m][i] = *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + (((4 * i + grp) ^ rs_a) * 16));
+      });
+    });
+  };
+  auto compute = [&](auto t, int slot) {
+    const char* src = ring + slot * SH::SLOT + rd;
+    u32x4_t q[4];
+    static_for<4>([&](auto s) {
+      q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
+    });
+    static_for<4>([&](auto s) {
+      static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
+    });
+  };
+
+  // prologue: A of the first block, then the first R - 1 visits of pass 0
+  dma_a(kb_lo, 0, true);
+  static_for<R - 1>([&](auto t) { dma_w(kb_lo * SH::WROW + t * tile_bytes, kb_lo, t % R); });
+  int blk = 0;
+  const int nblk = npass * static_cast<int>(kb_hi - kb_lo);
+  uint32_t base = 0;
+  for (int p = 0; p < npass; ++p, base += pass_bytes) {
+    for (uint32_t kb = kb_lo; kb < kb_hi; ++kb, ++blk) {
+      if (blk == 0)
+        ns_wait_vm<NI * (R - 1)>();
+      else
+        ns_wait_vm<NI * NTW>();
+      BDR_WG_BARRIER();
+      stage_to_regs(blk & 1);
+      const bool last_blk = kb + 1 == kb_hi;
+      const uint32_t nkb = last_blk ? kb_lo : kb + 1;
+      const uint32_t nbase = last_blk ? (p + 1 < npass ? base + pass_bytes : kOOB) : base;
+      dma_a(nkb, (blk + 1) & 1, blk + 1 < nblk);
+      static_for<NTW>([&](auto t) {
+        constexpr int tn = decltype(t)::value + R - 1;   // the visit loaded at this step
+        // The refill below writes the slot the previous step read.  The
+        // compiler does not see the buffer-to-LDS write as touching those
+        // addresses and would hoist it among that step's LDS reads; an
+        // out-of-range load (a tile past the range) lands within a few cycles
+        // and would zero the slot under them.  Past this point the previous
+        // step's MFMAs, and so its LDS reads, have all been issued.
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (tn < NTW)
+          dma_w(base + kb * SH::WROW + tn * tile_bytes, kb, tn % R);
+        else
+          dma_w(nbase == kOOB ? kOOB : nbase + nkb * SH::WROW + (tn - NTW) * tile_bytes, nkb,
+                tn % R);
+        ns_wait_vm<NI * (R - 1) + (decltype(t)::value < R - 1 ? NA : 0)>();
+        compute(t, decltype(t)::value % R);
+        // the visit's LDS reads ahead of its MFMAs (one latency per visit)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+      });
+    }
+    // pass p complete: store the tiles in this wave's range, then clear
+    int64_t nb = static_cast<int64_t>(n_lo) + 16 * NTW * p + r16;
+    asm volatile("" : "+v"(nb));
+    static_for<NTW>([&](auto t) {
+      const int64_t n = nb + 16 * t;
+      if (n < n_hi) {
+        static_for<MT>([&](auto m) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t row = 16 * m + 4 * grp + i;
+            if (row < out.M) out.put(row, n, acc[t][m][i]);
+          }
+        });
+      }
+    });
+    zero_acc();
+  }
+  BDR_WAIT_VM_LGKM(0, 15);
+}
+
+// bf16 weights take the compile-time schedule, fp8 weights the generic loop
+template <typename S, int MT>
+__device__ __forceinline__ void ns_any_body(const StreamArgs& sa, unsigned bx, unsigned by,
+                                            char* lds) {
+  if constexpr (kIsFp8<S>)
+    ns_body<S, MT, NsTiles<MT>::NTW>(sa, bx, by, lds);
+  else
+    ns_lean_body<MT>(sa, bx, by, lds);
+}
+
+template <typename S, int MT>
+constexpr size_t ns_any_lds_bytes() {
+  if constexpr (kIsFp8<S>)
+    return ns_lds_bytes<S, MT>();
+  else
+    return ns_lean_lds_bytes<MT>();
+}
+
 template <typename S, int MT, int NTW>
 __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  ns_body<S, MT, NTW>(sa, blockIdx.x, blockIdx.y, lds);
+  ns_any_body<S, MT>(sa, blockIdx.x, blockIdx.y, lds);
 }
 
 // Two GEMMs in one launch (the drafter fc beside the LM head): the first n0
@@ -359,11 +587,11 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a
                                                               const StreamArgs a1, unsigned n0) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (blockIdx.x < n0) {
-    ns_body<S, MT0, NsTiles<MT0>::NTW>(a0, blockIdx.x, 0, lds);
+    ns_any_body<S, MT0>(a0, blockIdx.x, 0, lds);
   } else {
     const unsigned i = blockIdx.x - n0;
     const unsigned nx = static_cast<unsigned>(a1.n_waves);
-    ns_body<S, MT1, NsTiles<MT1>::NTW>(a1, i % nx, i / nx, lds);
+    ns_any_body<S, MT1>(a1, i % nx, i / nx, lds);
   }
 }
 
@@ -374,13 +602,13 @@ hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, NTW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ns_lds_bytes<S, MT>()));
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ns_any_lds_bytes<S, MT>()));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
   hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, NTW>), grid, dim3(64 * kNsWaves),
-                     (ns_lds_bytes<S, MT>()), st, sa);
+                     (ns_any_lds_bytes<S, MT>()), st, sa);
   return hipGetLastError();
 }
 
@@ -391,8 +619,9 @@ namespace bdr {
 template <typename S, int MT0, int MT1>
 hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
                               unsigned n1, hipStream_t st) {
-  constexpr size_t lds = ns_lds_bytes<S, MT0>() > ns_lds_bytes<S, MT1>() ? ns_lds_bytes<S, MT0>()
-                                                                         : ns_lds_bytes<S, MT1>();
+  constexpr size_t lds = ns_any_lds_bytes<S, MT0>() > ns_any_lds_bytes<S, MT1>()
+                             ? ns_any_lds_bytes<S, MT0>()
+                             : ns_any_lds_bytes<S, MT1>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
