@@ -307,6 +307,13 @@ def set_markov_poll_timeout_us(us: float) -> None:
     lib().bdr_set_markov_poll_timeout_us(float(us))
 
 
+def set_row_split_override(ring: int = 0, workgroups: int = 0, ksplit: int = 0) -> None:
+    """Process-wide plan override of the row-split GEMM (0 = the planner's
+    choice): the bf16 ring depth, the row ranges and the K splits."""
+    _abi.check("bdr_set_row_split_override",
+          lib().bdr_set_row_split_override(int(ring), int(workgroups), int(ksplit)))
+
+
 def _markov_args(w1, w2, dt_ref):
     if w1 is None and w2 is None:
         return None, None, 0

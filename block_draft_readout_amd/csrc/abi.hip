@@ -191,9 +191,17 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
 
 extern "C" {
 
-int bdr_abi_version(void) { return 6; }
+int bdr_abi_version(void) { return 7; }
 
 void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
+
+int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit) {
+  if (ring < 0 || workgroups < 0 || ksplit < 0 || workgroups > (int64_t(1) << 20) || ksplit > 256)
+    return fail(BDR_EINVAL, "row-split override: ring %d, workgroups %lld, ksplit %d out of range",
+                ring, static_cast<long long>(workgroups), ksplit);
+  bdr::set_row_split_override(ring, workgroups, ksplit);
+  return BDR_OK;
+}
 
 const char* bdr_last_error(void) { return g_err; }
 

@@ -22,6 +22,7 @@
 // no branches.  Inputs are bf16 (v_mfma_f32_16x16x32_bf16) or fp32
 // (v_mfma_f32_16x16x4_f32); accumulation is fp32.
 
+#include <atomic>
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -347,14 +348,74 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
 // Row-split workgroup plan (gemm_ns.h; bf16 or fp8 weights, bf16 A, 16 < M <=
 // 160): K blocks of 128 elements that never straddle a tap segment; one
 // workgroup per compute unit and K split, its rows split over four waves, each
-// walking its tiles in passes of ns_tiles(mt).  The K split minimises the
-// per-compute-unit cost W bytes + a quarter of the A bytes staged per pass (+
-// the partial-sum round trip).
-static int ns_tiles(int mt, int esize) {   // NsLean<MT>::NTW (bf16), NsTiles<MT>::NTW (fp8)
-  if (esize == 2)
-    return mt <= 2 ? 16 : mt == 3 ? 14 : mt == 4 ? 12 : mt <= 6 ? 6 : mt <= 8 ? 5 : mt == 9 ? 4 : 3;
-  return mt <= 3 ? 16 : mt == 4 ? 12 : mt == 5 ? 9 : mt == 6 ? 8 : mt == 7 ? 6 : mt == 8 ? 5
-         : mt == 9 ? 4 : 3;
+// walking its tiles in passes.  The K split minimises the per-compute-unit
+// cost W bytes + a quarter of the A bytes staged per pass (+ the partial-sum
+// round trip).
+//
+// bf16 passes are groups of `ring` slots (gemm_ns.h, ns_lean_body): with t
+// tiles a wave walks npass passes of ng groups; the ring depth is the one of
+// kNsLeanRings that leaves the fewest slots (empty ones still cost their
+// MFMAs and issue), the deepest among equals.
+static int64_t ns_lean_passes(int mt, int ring, int64_t tiles) {
+  const int64_t ntw = kNsLeanNtwMax[mt] / ring * ring;
+  return std::max<int64_t>(1, (tiles + ntw - 1) / ntw);
+}
+
+static int64_t ns_lean_slots(int mt, int ring, int64_t tiles) {
+  const int64_t npass = ns_lean_passes(mt, ring, tiles);
+  const int64_t ng = std::max<int64_t>(1, (tiles + npass * ring - 1) / (npass * ring));
+  return npass * ng * ring;
+}
+
+// pass `rings` to restrict the choice (the two-problem launch builds fewer)
+static int ns_pick_ring(int mt, int64_t tiles, const int* rings = nullptr) {
+  if (rings == nullptr) rings = kNsLeanRings[mt];
+  int best = 0;
+  int64_t best_slots = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int r = rings[i];
+    if (r == 0) continue;
+    const int64_t s = ns_lean_slots(mt, r, tiles);
+    if (best == 0 || s < best_slots) {
+      best = r;
+      best_slots = s;
+    }
+  }
+  return best;
+}
+
+// largest tile count of one wave when N rows are split over nwg workgroups
+static int64_t ns_wave_tiles(int64_t N, int64_t nwg) {
+  const int64_t n_t = (N + 15) / 16;
+  return ((n_t + nwg - 1) / nwg + 3) / 4;
+}
+
+// passes of a wave: bf16 with the ring it would take, fp8 in passes of
+// NsTiles<MT>::NTW
+static int64_t ns_passes(int mt, int esize, int64_t tiles, int* ring) {
+  if (esize == 2) {
+    const int r = ns_pick_ring(mt, tiles);
+    if (ring) *ring = r;
+    return ns_lean_passes(mt, r, tiles);
+  }
+  if (ring) *ring = 0;
+  const int ntw = mt <= 3 ? 16 : mt == 4 ? 12 : mt == 5 ? 9 : mt == 6 ? 8 : mt == 7 ? 6
+                  : mt == 8 ? 5 : mt == 9 ? 4 : 3;
+  return (tiles + ntw - 1) / ntw;
+}
+
+static std::atomic<int> g_ns_ring{0};
+static std::atomic<int64_t> g_ns_wg{0};
+static std::atomic<int> g_ns_ks{0};
+
+void set_row_split_override(int ring, int64_t workgroups, int ksplit) {
+  g_ns_ring.store(std::max(ring, 0));
+  g_ns_wg.store(std::max<int64_t>(workgroups, 0));
+  g_ns_ks.store(std::max(ksplit, 0));
+}
+
+static bool ns_overridden() {
+  return g_ns_ring.load() != 0 || g_ns_wg.load() != 0 || g_ns_ks.load() != 0;
 }
 
 static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
@@ -363,7 +424,6 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   const int64_t mtiles = (M + 15) / 16;
   if (esize > 2 || M <= 16 || mtiles > 10 || K % (esize == 1 ? 16 : 8) != 0) return false;
   if (n_seg > 1 && (K / n_seg) % KE != 0) return false;
-  const int ntw = ns_tiles(static_cast<int>(mtiles), esize);
   const int64_t kblocks = (K + KE - 1) / KE;
   double best = 1e300;
   for (int64_t ks = 1; ks <= (allow_split ? std::min<int64_t>(64, kblocks) : 1); ++ks) {
@@ -373,8 +433,7 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
     int64_t nwg = std::max<int64_t>(1, kNumCU / ks_eff);
     nwg = std::min<int64_t>(nwg, (N + 63) / 64);
     const int64_t rows = (N + nwg - 1) / nwg;
-    const int64_t tiles_w = ((rows + 3) / 4 + 15) / 16;
-    const int64_t npass = (tiles_w + ntw - 1) / ntw;
+    const int64_t npass = ns_passes(static_cast<int>(mtiles), esize, ns_wave_tiles(N, nwg), nullptr);
     double cost = static_cast<double>(kbps) * KE * (esize * rows + 0.5 * M * npass);
     if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / kNumCU;
     if (cost < best) {
@@ -384,12 +443,21 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
       p->ksplit = static_cast<int>(ks_eff);
     }
   }
-  // a wave's rows x row bytes are addressed with 32-bit offsets
+  if (const int64_t ks_o = std::min<int64_t>(g_ns_ks.load(), kblocks); ks_o > 0 && allow_split) {
+    p->kb_per_split = (kblocks + ks_o - 1) / ks_o;
+    p->ksplit = static_cast<int>((kblocks + p->kb_per_split - 1) / p->kb_per_split);
+  }
+  if (const int64_t wg_o = g_ns_wg.load(); wg_o > 0)
+    p->n_waves = std::min<int64_t>(wg_o, (N + 15) / 16);
+  // a wave's rows x row bytes are addressed with 32-bit offsets (with room for
+  // the empty slots of its last pass)
   const int64_t rows_w = ((N + p->n_waves - 1) / p->n_waves + 3) / 4;
-  if ((rows_w + 16) * K * esize >= (int64_t(1) << 31)) return false;
+  if ((rows_w + 256) * K * esize >= (int64_t(1) << 31)) return false;
   p->stream = true;
   p->ns = true;
   p->mt = static_cast<int>(mtiles);
+  ns_passes(p->mt, esize, ns_wave_tiles(N, p->n_waves), &p->ring);
+  if (esize == 2 && g_ns_ring.load() > 0) p->ring = g_ns_ring.load();   // (launch checks it is built)
   p->kblocks = kblocks;
   p->m_groups = 1;
   p->n_wg = p->n_waves;
@@ -400,30 +468,37 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
 // Pair plan: the compute units are shared in proportion to each problem's
 // cost (weight bytes + a quarter of the A bytes staged per pass + split-K
 // partials), the split of problem 1 chosen so that its slowest workgroup and
-// problem 0's finish together.
-static double ns_wg_cost(int64_t M, int64_t rows, int64_t kbps, int ntw, int64_t ks, int64_t N) {
-  const int64_t tiles_w = ((rows + 3) / 4 + 15) / 16;
-  const int64_t npass = (tiles_w + ntw - 1) / ntw;
+// problem 0's finish together.  Problem 1 (the fc: two or three tiles a wave)
+// takes ring 3.
+static double ns_wg_cost(int64_t M, int64_t rows, int64_t kbps, int64_t npass, int64_t ks,
+                         int64_t N) {
   double c = static_cast<double>(kbps) * 128 * (2.0 * rows + 0.5 * M * npass);
   if (ks > 1) c += static_cast<double>(ks) * M * N * 8 / kNumCU;
   return c;
 }
 
+// rings of problem 0 built for the two-problem launch (gemm_ns_pair_*.hip;
+// seven row tiles with ring 3 spills beside the fc and is left out)
+static constexpr int kPairRings[11][3] = {{0, 0, 0}, {0, 0, 0}, {8, 5, 3}, {7, 5, 3}, {6, 5, 3},
+                                          {6, 5, 3}, {6, 5, 3}, {5, 0, 0}, {5, 3, 0}, {4, 3, 0},
+                                          {0, 0, 0}};
+
 PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1,
                         int n_seg1) {
   PairPlan pp;
   GemmPlan q0, q1;
+  if (ns_overridden()) return pp;
   if (!plan_ns(M0, N0, K0, 2, false, 1, &q0) || !plan_ns(M1, N1, K1, 2, true, n_seg1, &q1))
     return pp;
   if ((q1.mt != q0.mt && q1.mt != q0.mt + 1) || q1.mt > 9) return pp;
-  const int ntw0 = ns_tiles(q0.mt, 2), ntw1 = ns_tiles(q1.mt, 2);
   const int64_t kb0 = q0.kblocks, kb1 = q1.kblocks;
   // passes of problem 0's waves on its own (one workgroup per compute unit):
   // sharing the chip must not add a pass (each restages the whole A matrix)
   auto passes0 = [&](int64_t nwg) {
-    const int64_t tiles_w = (((N0 + nwg - 1) / nwg + 3) / 4 + 15) / 16;
-    return (tiles_w + ntw0 - 1) / ntw0;
+    const int64_t t = ns_wave_tiles(N0, nwg);
+    return ns_lean_passes(q0.mt, ns_pick_ring(q0.mt, t, kPairRings[q0.mt]), t);
   };
+  auto passes1 = [&](int64_t nwg) { return ns_lean_passes(q1.mt, 3, ns_wave_tiles(N1, nwg)); };
   const int64_t alone = passes0(q0.n_waves);
   double best = 1e300, best_c0 = 0, best_c1 = 0;
   for (int64_t ks = 1; ks <= std::min<int64_t>(8, kb1); ++ks) {
@@ -432,8 +507,8 @@ PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t 
     for (int64_t nx = 1; nx * ks_eff <= kNumCU / 2 && nx <= (N1 + 63) / 64; ++nx) {
       const int64_t n1 = nx * ks_eff, n0 = kNumCU - n1;
       if (n0 > (N0 + 63) / 64 || passes0(n0) > alone) continue;
-      const double c0 = ns_wg_cost(M0, (N0 + n0 - 1) / n0, kb0, ntw0, 1, N0);
-      const double c1 = ns_wg_cost(M1, (N1 + nx - 1) / nx, kbps, ntw1, ks_eff, N1);
+      const double c0 = ns_wg_cost(M0, (N0 + n0 - 1) / n0, kb0, passes0(n0), 1, N0);
+      const double c1 = ns_wg_cost(M1, (N1 + nx - 1) / nx, kbps, passes1(nx), ks_eff, N1);
       const double c = std::max(c0, c1);
       if (c < best) {
         best = c;
@@ -459,11 +534,13 @@ PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t 
   q0.ksplit = 1;
   q0.kb_per_split = kb0;
   q0.workspace = 0;
+  q0.ring = ns_pick_ring(q0.mt, ns_wave_tiles(N0, pp.n0), kPairRings[q0.mt]);
+  q1.ring = 3;
   q1.workspace = q1.ksplit > 1 ? align256(static_cast<size_t>(q1.ksplit) * M1 * N1 * 4) : 0;
   // the row ranges must keep their 32-bit offsets with the fewer workgroups
   const int64_t rows_w0 = ((N0 + pp.n0 - 1) / pp.n0 + 3) / 4;
   const int64_t rows_w1 = ((N1 + q1.n_waves - 1) / q1.n_waves + 3) / 4;
-  if ((rows_w0 + 16) * K0 * 2 >= (int64_t(1) << 31) || (rows_w1 + 16) * K1 * 2 >= (int64_t(1) << 31))
+  if ((rows_w0 + 256) * K0 * 2 >= (int64_t(1) << 31) || (rows_w1 + 256) * K1 * 2 >= (int64_t(1) << 31))
     return pp;
   pp.p0 = q0;
   pp.p1 = q1;
@@ -695,7 +772,9 @@ hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, 
   g1.out = split ? workspace : out1;
   const StreamArgs s0{g0, pp.p0.n_waves, pp.p0.kblocks, pp.p0.kb_per_split};
   const StreamArgs s1{g1, pp.p1.n_waves, pp.p1.kblocks, pp.p1.kb_per_split};
-  hipError_t e = launch_ns_pair_bf16(pp.p0.mt, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream);
+  hipError_t e = pp.p0.mt <= 4
+                     ? launch_ns_pair_bf16_a(pp.p0.mt, pp.p0.ring, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream)
+                     : launch_ns_pair_bf16_b(pp.p0.mt, pp.p0.ring, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(pp.p1, pp.M1, pp.N1, out1, OUT_BF16, workspace, stream);
 }

@@ -19,7 +19,7 @@ struct GemmArgs {
   const void* w;                // [N, K]
   void* out;                    // final [M, N] or fp32 partials [ksplit, M, N]
   int out_kind;                 // OutKind of a final output
-  int partial;                  // 1: write fp32 partials indexed by blockIdx.y
+  int partial;                  // 1: write fp32 partials [split, M, N]
   int64_t steps_per_split;      // K steps handled by one workgroup along K
   const float* w_scale;         // fp8 weights: one scale per W row [N]; else unused
 };
@@ -119,7 +119,11 @@ hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t s
 // row-split workgroup kernel (gemm_ns.h): bf16 and fp8 weights, bf16 A
 hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
-hipError_t launch_ns_pair_bf16(int mt0, int mt1, const StreamArgs& a0, const StreamArgs& a1,
-                               unsigned n0, unsigned n1, hipStream_t st);
+// the LM head (mt0 row tiles, ring r0) beside the fc (mt1 = mt0 or mt0 + 1 row
+// tiles, ring 3) in one launch: mt0 2..4 (gemm_ns_pair_a.hip), 5..9 (_b)
+hipError_t launch_ns_pair_bf16_a(int mt0, int r0, int mt1, const StreamArgs& a0,
+                                 const StreamArgs& a1, unsigned n0, unsigned n1, hipStream_t st);
+hipError_t launch_ns_pair_bf16_b(int mt0, int r0, int mt1, const StreamArgs& a0,
+                                 const StreamArgs& a1, unsigned n0, unsigned n1, hipStream_t st);
 
 }  // namespace bdr

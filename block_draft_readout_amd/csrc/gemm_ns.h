@@ -348,29 +348,36 @@ __device__ __forceinline__ void ns_body(const StreamArgs& sa, unsigned bx, unsig
 // bf16 weights: the same organisation with a schedule fixed at compile time, so
 // the loop carries almost no bookkeeping (the generic loop above spent about
 // as many scalar instructions as MFMAs and kept the MFMA pipe ~28 % busy):
-//   * every pass has NTW tile slots; a wave's tiles past its range (at most a
-//     few in its last pass) read nothing (out-of-range loads) and are not
-//     stored;
-//   * the ring holds R visits with R dividing NTW, so the slot of tile t of
-//     every block is t % R and the visit loaded at step t -- R - 1 ahead, the
-//     slot consumed at step t - 1 -- is known at compile time, within this
-//     block or the next (or the next pass's first);
+//   * a pass holds ng groups of R tile slots (ng <= NG, chosen per workgroup
+//     from its range so that few slots stay empty); tile t of a pass lives in
+//     ring slot t % R in every K block;
+//   * the visit loaded at step t is the one R - 1 ahead, into the slot read at
+//     step t - 1: tile t + R - 1 of this block, or tile t + R - 1 - ng R of the
+//     next block (or of the next pass's first) -- the slot is known at compile
+//     time, only the tile's offset is selected at run time;
+//   * a slot past the wave's tiles (at most a few in its last pass) reads
+//     nothing (out-of-range loads) and is not stored;
 //   * every block issues its MT A-staging loads (out of range past the last
-//     block or row), so each wait counts a compile-time number of loads:
-//     before the block's barrier NI * NTW (NI * (R - 1) for the first), before
-//     step t NI * (R - 1), + MT while the visit predates the block's A loads.
+//     block or row), so each wait counts a compile-time number of loads: before
+//     step t NI * (R - 1), + MT while the visit predates the block's A loads;
+//     before a block's barrier NI * R (at least R visits followed its A loads),
+//     NI * (R - 1) for the first.
+// R is a template argument: deep rings for long ranges (the LM head), shallow
+// ones where a wave has two or three tiles (a K-split fc), so that the ring is
+// not filled with empty slots.
 // ----------------------------------------------------------------------------
-template <int MT> struct NsLean {   // tiles per pass, ring slots (as deep as LDS allows)
-  static constexpr int NTW = MT <= 2 ? 16 : MT == 3 ? 14 : MT == 4 ? 12 : MT <= 6 ? 6
-                           : MT <= 8 ? 5 : MT == 9 ? 4 : 3;
-  static constexpr int R = MT <= 2 ? 8 : MT == 3 ? 7 : MT <= 6 ? 6 : MT <= 8 ? 5 : MT == 9 ? 4 : 3;
+template <int MT> constexpr int ns_lean_ntw_max() { return kNsLeanNtwMax[MT]; }
+
+template <int MT, int R>
+struct NsLean {
+  static constexpr int NG = ns_lean_ntw_max<MT>() / R;   // groups of R slots per pass, at most
+  static constexpr int NTW = NG * R;
 };
 
-template <int MT>
+template <int MT, int R>
 constexpr size_t ns_lean_lds_bytes() {
   using SH = NsShape<uint16_t>;
-  return static_cast<size_t>(kNsWaves * NsLean<MT>::R * SH::SLOT) +
-         static_cast<size_t>(2 * MT) * SH::ASLOT;
+  return static_cast<size_t>(kNsWaves * R * SH::SLOT) + static_cast<size_t>(2 * MT) * SH::ASLOT;
 }
 
 template <int N>
@@ -379,15 +386,15 @@ __device__ __forceinline__ void ns_wait_vm() {
   BDR_WAIT_VM_LGKM(n, 15);
 }
 
-template <int MT>
+template <int MT, int R>
 __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, unsigned by,
                                              char* lds) {
   using S = uint16_t;
   using SH = NsShape<S>;
-  constexpr int NTW = NsLean<MT>::NTW;
-  constexpr int R = NsLean<MT>::R;
-  static_assert(NTW % R == 0, "the ring divides the pass");
-  static_assert(ns_lean_lds_bytes<MT>() <= 160 * 1024, "LDS budget");
+  constexpr int NG = NsLean<MT, R>::NG;
+  constexpr int NTW = NsLean<MT, R>::NTW;
+  static_assert(NG >= 1 && R >= 2, "ring shape");
+  static_assert(ns_lean_lds_bytes<MT, R>() <= 160 * 1024, "LDS budget");
   constexpr int NI = SH::NI;        // loads per visit
   constexpr int NA = MT;            // A loads per wave per block
   static_assert(NI * (R - 1) + NA <= 63, "vmcnt range");
@@ -404,8 +411,11 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
       static_cast<int>(16 * (t_lo + (t_hi - t_lo) * wave / kNsWaves)));
   const int n_hi = __builtin_amdgcn_readfirstlane(static_cast<int>(
       min<int64_t>(g.N, 16 * (t_lo + (t_hi - t_lo) * (wave + 1) / kNsWaves))));
+  // passes and groups: the same on every wave (from the largest quarter)
   const int max_tiles = static_cast<int>((t_hi - t_lo + kNsWaves - 1) / kNsWaves);
   const int npass = max(1, (max_tiles + NTW - 1) / NTW);
+  const int ng = __builtin_amdgcn_readfirstlane(
+      max(1, (max_tiles + npass * R - 1) / (npass * R)));
   const uint32_t kb_lo = static_cast<uint32_t>(by * sa.kb_per_split);
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
   if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
@@ -431,7 +441,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
   const int rs_a = r16 % 4;
   const uint32_t tile_bytes = 16 * kbytes;
-  const uint32_t pass_bytes = static_cast<uint32_t>(NTW) * tile_bytes;
+  const uint32_t pass_bytes = static_cast<uint32_t>(ng * R) * tile_bytes;
   // the last K block may be partial: its row pieces end at tail_bytes
   const uint32_t tail_bytes = kbytes - (static_cast<uint32_t>(sa.kblocks) - 1) * SH::WROW;
   const uint32_t kb_last = static_cast<uint32_t>(sa.kblocks) - 1;
@@ -495,9 +505,9 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
     });
   };
 
-  // prologue: A of the first block, then the first R - 1 visits of pass 0
+  // prologue: A of the first block, then tiles 0 .. R - 2 of pass 0 (ng >= 1)
   dma_a(kb_lo, 0, true);
-  static_for<R - 1>([&](auto t) { dma_w(kb_lo * SH::WROW + t * tile_bytes, kb_lo, t % R); });
+  static_for<R - 1>([&](auto t) { dma_w(kb_lo * SH::WROW + t * tile_bytes, kb_lo, t); });
   int blk = 0;
   const int nblk = npass * static_cast<int>(kb_hi - kb_lo);
   uint32_t base = 0;
@@ -506,40 +516,51 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
       if (blk == 0)
         ns_wait_vm<NI * (R - 1)>();
       else
-        ns_wait_vm<NI * NTW>();
+        ns_wait_vm<NI * R>();
       BDR_WG_BARRIER();
       stage_to_regs(blk & 1);
       const bool last_blk = kb + 1 == kb_hi;
       const uint32_t nkb = last_blk ? kb_lo : kb + 1;
       const uint32_t nbase = last_blk ? (p + 1 < npass ? base + pass_bytes : kOOB) : base;
       dma_a(nkb, (blk + 1) & 1, blk + 1 < nblk);
-      static_for<NTW>([&](auto t) {
-        constexpr int tn = decltype(t)::value + R - 1;   // the visit loaded at this step
-        // The refill below writes the slot the previous step read.  The
-        // compiler does not see the buffer-to-LDS write as touching those
-        // addresses and would hoist it among that step's LDS reads; an
-        // out-of-range load (a tile past the range) lands within a few cycles
-        // and would zero the slot under them.  Past this point the previous
-        // step's MFMAs, and so its LDS reads, have all been issued.
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (tn < NTW)
-          dma_w(base + kb * SH::WROW + tn * tile_bytes, kb, tn % R);
-        else
-          dma_w(nbase == kOOB ? kOOB : nbase + nkb * SH::WROW + (tn - NTW) * tile_bytes, nkb,
-                tn % R);
-        ns_wait_vm<NI * (R - 1) + (decltype(t)::value < R - 1 ? NA : 0)>();
-        compute(t, decltype(t)::value % R);
-        // the visit's LDS reads ahead of its MFMAs (one latency per visit)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+      const uint32_t here = base + kb * SH::WROW;
+      const uint32_t next = nbase == kOOB ? kOOB : nbase + nkb * SH::WROW;
+      static_for<NG>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        if (G < ng) {
+          const bool last_g = G + 1 >= ng;
+          static_for<R>([&](auto jc) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int T = G * R + J;
+            // The refill below writes the slot the previous step read.  The
+            // compiler does not see the buffer-to-LDS write as touching those
+            // addresses and would hoist it among that step's LDS reads; an
+            // out-of-range load (an empty slot) lands within a few cycles and
+            // would zero the slot under them.  Past this point the previous
+            // step's MFMAs, and so its LDS reads, have all been issued.
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (J == 0) {
+              dma_w(here + (T + R - 1) * tile_bytes, kb, R - 1);
+            } else {
+              const uint32_t in_blk = here + ((G + 1) * R + J - 1) * tile_bytes;
+              const uint32_t nx_blk = next == kOOB ? kOOB : next + (J - 1) * tile_bytes;
+              dma_w(last_g ? nx_blk : in_blk, last_g ? nkb : kb, J - 1);
+            }
+            ns_wait_vm<NI * (R - 1) + (T < R - 1 ? NA : 0)>();
+            compute(std::integral_constant<int, T>{}, J);
+            // the visit's LDS reads ahead of its MFMAs (one latency per visit)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+          });
+        }
       });
     }
     // pass p complete: store the tiles in this wave's range, then clear
-    int64_t nb = static_cast<int64_t>(n_lo) + 16 * NTW * p + r16;
+    int64_t nb = static_cast<int64_t>(n_lo) + 16 * static_cast<int64_t>(ng * R) * p + r16;
     asm volatile("" : "+v"(nb));
     static_for<NTW>([&](auto t) {
       const int64_t n = nb + 16 * t;
-      if (n < n_hi) {
+      if (t < ng * R && n < n_hi) {
         static_for<MT>([&](auto m) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -554,84 +575,90 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   BDR_WAIT_VM_LGKM(0, 15);
 }
 
-// bf16 weights take the compile-time schedule, fp8 weights the generic loop
-template <typename S, int MT>
+// bf16 weights take the compile-time schedule with ring depth R; fp8 weights,
+// and bf16 with R = 0, the generic loop
+template <typename S, int MT, int R>
 __device__ __forceinline__ void ns_any_body(const StreamArgs& sa, unsigned bx, unsigned by,
                                             char* lds) {
-  if constexpr (kIsFp8<S>)
+  if constexpr (kIsFp8<S> || R == 0)
     ns_body<S, MT, NsTiles<MT>::NTW>(sa, bx, by, lds);
   else
-    ns_lean_body<MT>(sa, bx, by, lds);
+    ns_lean_body<MT, R>(sa, bx, by, lds);
 }
 
-template <typename S, int MT>
+template <typename S, int MT, int R>
 constexpr size_t ns_any_lds_bytes() {
-  if constexpr (kIsFp8<S>)
+  if constexpr (kIsFp8<S> || R == 0)
     return ns_lds_bytes<S, MT>();
   else
-    return ns_lean_lds_bytes<MT>();
+    return ns_lean_lds_bytes<MT, R>();
 }
 
-template <typename S, int MT, int NTW>
+// K splits of one problem: ceil(kblocks / kb_per_split)
+__device__ __forceinline__ unsigned ns_splits(const StreamArgs& sa) {
+  return static_cast<unsigned>((sa.kblocks + sa.kb_per_split - 1) / sa.kb_per_split);
+}
+
+// One-dimensional grid of n_waves x splits workgroups.  Workgroup i takes K
+// split i % splits of row range i / splits: consecutive workgroups, which the
+// dispatcher spreads over the eight XCDs in turn, take different splits, so
+// with eight splits every XCD holds one split's workgroups and the A slice
+// they all read stays in that XCD's L2.
+template <typename S, int MT, int R>
 __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  ns_any_body<S, MT>(sa, blockIdx.x, blockIdx.y, lds);
+  const unsigned ks = ns_splits(sa);
+  ns_any_body<S, MT, R>(sa, blockIdx.x / ks, blockIdx.x % ks, lds);
 }
 
 // Two GEMMs in one launch (the drafter fc beside the LM head): the first n0
 // workgroups take problem 0 (row ranges of a0, no K split); the others take
-// problem 1, workgroup n0 + i being row range i % a1.n_waves of K split
-// i / a1.n_waves.  Problem 1 has MT or MT + 1 row tiles (MT1).
-template <typename S, int MT0, int MT1>
+// problem 1, workgroup n0 + i being K split i % splits of row range i / splits.
+template <typename S, int MT0, int R0, int MT1, int R1>
 __global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a0,
                                                               const StreamArgs a1, unsigned n0) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (blockIdx.x < n0) {
-    ns_any_body<S, MT0>(a0, blockIdx.x, 0, lds);
+    ns_any_body<S, MT0, R0>(a0, blockIdx.x, 0, lds);
   } else {
     const unsigned i = blockIdx.x - n0;
-    const unsigned nx = static_cast<unsigned>(a1.n_waves);
-    ns_any_body<S, MT1>(a1, i % nx, i / nx, lds);
+    const unsigned ks = ns_splits(a1);
+    ns_any_body<S, MT1, R1>(a1, i / ks, i % ks, lds);
   }
 }
 
-template <typename S, int MT>
+template <typename S, int MT, int R>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  constexpr int NTW = NsTiles<MT>::NTW;
+  constexpr size_t lds = ns_any_lds_bytes<S, MT, R>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, NTW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ns_any_lds_bytes<S, MT>()));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const dim3 grid(static_cast<unsigned>(p.n_waves), static_cast<unsigned>(p.ksplit));
-  hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, NTW>), grid, dim3(64 * kNsWaves),
-                     (ns_any_lds_bytes<S, MT>()), st, sa);
-  return hipGetLastError();
-}
-
-}  // namespace bdr
-
-namespace bdr {
-
-template <typename S, int MT0, int MT1>
-hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
-                              unsigned n1, hipStream_t st) {
-  constexpr size_t lds = ns_any_lds_bytes<S, MT0>() > ns_any_lds_bytes<S, MT1>()
-                             ? ns_any_lds_bytes<S, MT0>()
-                             : ns_any_lds_bytes<S, MT1>();
-  static bool attr_set = false;  // per instantiation
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ws_gemm_ns_pair_kernel<S, MT0, MT1>),
+        reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, R>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((ws_gemm_ns_pair_kernel<S, MT0, MT1>), dim3(n0 + n1), dim3(64 * kNsWaves),
-                     lds, st, a0, a1, n0);
+  const dim3 grid(static_cast<unsigned>(p.n_waves * p.ksplit));
+  hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, R>), grid, dim3(64 * kNsWaves), lds, st, sa);
+  return hipGetLastError();
+}
+
+template <typename S, int MT0, int R0, int MT1, int R1>
+hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
+                              unsigned n1, hipStream_t st) {
+  constexpr size_t lds = ns_any_lds_bytes<S, MT0, R0>() > ns_any_lds_bytes<S, MT1, R1>()
+                             ? ns_any_lds_bytes<S, MT0, R0>()
+                             : ns_any_lds_bytes<S, MT1, R1>();
+  static bool attr_set = false;  // per instantiation
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1>), dim3(n0 + n1),
+                     dim3(64 * kNsWaves), lds, st, a0, a1, n0);
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ struct GemmPlan {
   int64_t n_waves = 0;    // row ranges (workgroups along N)
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;
+  int ring = 0;           // ns with bf16 weights: LDS ring slots per wave (kNsLeanRings)
   // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
   // K steps of 64 (kblocks / kb_per_split count steps)
   bool tile = false;
@@ -40,10 +41,25 @@ struct GemmPlan {
 // queries and launches always plan identically.
 constexpr int kNumCU = 256;
 
+// Row-split kernel with bf16 weights (gemm_ns.h): per A row-tile count, the
+// accumulator tiles one pass can hold, and the ring depths built (deepest
+// first; 0 = none).  A deep ring keeps more loads in flight, a shallow one
+// wastes fewer slots on waves with few tiles.
+constexpr int kNsLeanNtwMax[11] = {0, 0, 16, 14, 12, 9, 8, 6, 5, 4, 3};
+constexpr int kNsLeanRings[11][3] = {{0, 0, 0}, {0, 0, 0}, {8, 5, 3}, {7, 5, 3}, {6, 5, 3},
+                                     {6, 5, 3}, {6, 5, 3}, {5, 3, 0},  {5, 3, 0}, {4, 3, 0},
+                                     {3, 0, 0}};
+
 enum OutKind { OUT_F32 = 0, OUT_BF16 = 1 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split,
                    int n_seg = 1);
+
+// Row-split plans (bf16 and fp8 weights, 16 < M <= 160) take these values in
+// place of their own where non-zero: the ring depth (bf16), the row ranges
+// and the K splits (bounded by the shape).  Process-wide; the two-problem
+// launch is not planned while any is set.
+void set_row_split_override(int ring, int64_t workgroups, int ksplit);
 
 hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, int n_seg,
                        int64_t seg, int64_t M, int64_t N, const void* w, void* out,

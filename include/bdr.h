@@ -77,6 +77,19 @@ const char* bdr_last_error(void);
  * the time-out path with every kernel still running to completion. */
 void bdr_set_markov_poll_timeout_us(double us);
 
+/* Plan override of the row-split GEMM (the fc and the LM head with 16 < rows
+ * <= 160), for calls planned after this one, process-wide; 0 leaves a value
+ * to the planner.  ring: LDS ring slots per wave of the bf16 kernel (built:
+ * 8, 5, 3 for 2 row tiles; 7, 5, 3 for 3; 6, 5, 3 for 4 to 6; 5, 3 for 7 and
+ * 8; 4, 3 for 9; 3 for 10 -- a call planned with any other fails with
+ * BDR_EHIP); workgroups: row ranges (at most one per 16 rows); ksplit: K
+ * splits of a call that may split K (at most one per 128-element K block).
+ * While any is set, dflash_fuse_fc_lm_head runs its two GEMMs one after the
+ * other.  Workspace sizes follow the override, so query them after setting
+ * it.  Tests and tuning use it to reach every kernel variant on small shapes.
+ * Returns BDR_EINVAL for a negative value, workgroups > 2^20 or ksplit > 256. */
+int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit);
+
 /* ---------------------------------------------------------------------------
  * S1  dflash_fuse_fc -- fuse the tapped target hidden states and apply the fc.
  *

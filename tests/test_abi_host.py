@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 6
+    assert L.bdr_abi_version() == 7
 
 
 def test_workspace_sizes(L):
@@ -308,3 +308,27 @@ def test_binding_fails_loudly_without_library(tmp_path):
             _abi.load(str(tmp_path / "missing.so"))
     finally:
         _abi._lib = saved
+
+
+def test_row_split_override_drives_the_plan(L):
+    """The plan override (host state only): invalid values are rejected, a
+    forced K split resizes the fc's partial-sum workspace, and clearing it
+    restores the planner's own plan."""
+    from block_draft_readout_amd import _abi as A
+    a256 = lambda x: (x + 255) // 256 * 256
+    rows, H, T = 144, 5120, 5
+    own = L.dflash_fuse_fc_workspace_bytes(rows, H, T, A.BDR_BF16)
+    assert own > 0 and own % (rows * H * 4) == 0
+    try:
+        for bad in [(-1, 0, 0), (0, -1, 0), (0, 0, -1), (0, 1 << 21, 0), (0, 0, 257)]:
+            assert L.bdr_set_row_split_override(*bad) == A.BDR_EINVAL, bad
+        for ks in (2, 3, 16):
+            assert L.bdr_set_row_split_override(0, 0, ks) == A.BDR_OK
+            assert L.dflash_fuse_fc_workspace_bytes(rows, H, T, A.BDR_BF16) == a256(ks * rows * H * 4)
+        # the fused fc + LM head is not planned as one launch meanwhile: its
+        # workspace is the fc's alone
+        fused = L.dflash_fuse_fc_lm_head_workspace_bytes(rows, H, T, 128, 151936, A.BDR_BF16)
+        assert fused == a256(16 * rows * H * 4)
+    finally:
+        assert L.bdr_set_row_split_override(0, 0, 0) == A.BDR_OK
+    assert L.dflash_fuse_fc_workspace_bytes(rows, H, T, A.BDR_BF16) == own

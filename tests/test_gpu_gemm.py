@@ -8,6 +8,7 @@ the oracle's float64 products."""
 import dataclasses
 
 import pytest
+import torch
 
 import oracle
 import workloads
@@ -135,6 +136,66 @@ def test_prefill_fc_parity_on_sampled_rows(hidden):
     ref = oracle.fuse_fc([t[sample] for t in taps], fc_w, "bf16")
     err = max_rel_err(oracle.widen(got[sample], "bf16"), ref)
     log(f"  {sample.size} rows, max rel err {err:.3e}")
+    assert err <= 4e-3
+
+
+# ring depths built for the bf16 row-split kernel by A row-tile count, and the
+# accumulator tiles a pass can hold
+RINGS = {2: (8, 5, 3), 3: (7, 5, 3), 4: (6, 5, 3), 5: (6, 5, 3), 6: (6, 5, 3), 7: (5, 3),
+         8: (5, 3), 9: (4, 3), 10: (3,)}
+NTW_MAX = {2: 16, 3: 14, 4: 12, 5: 9, 6: 8, 7: 6, 8: 5, 9: 4, 10: 3}
+RING_CASES = [(m, r) for m, rs in RINGS.items() for r in rs]
+
+
+def _ring_tiles(mt, ring):
+    """Tiles of the largest wave: more than a pass holds, so two passes, the
+    second with groups of slots left empty."""
+    return NTW_MAX[mt] // ring * ring + ring + 1
+
+
+@pytest.mark.parametrize("mt,ring", RING_CASES)
+def test_row_split_every_ring_lm_head(mt, ring):
+    """Every ring depth built for bf16 weights, forced through the plan
+    override on two row ranges: two passes per wave with empty slots in the
+    second, a ragged last tile, a partial last K block (H = 392)."""
+    import block_draft_readout_amd as bdr
+    import numpy as np
+    T = _ring_tiles(mt, ring)
+    M, N, H = 16 * mt - 3, 2 * 4 * T * 16 - 5, 392
+    rng = np.random.default_rng(mt * 100 + ring)
+    hid = synth.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    lm_w = synth.to_bf16_bits((rng.standard_normal((N, H)) / np.sqrt(H)).astype(np.float32))
+    bdr.set_row_split_override(ring, 2, 0)
+    try:
+        got = bdr.dspark_lm_head(dev(hid), dev(lm_w)).cpu().numpy()
+    finally:
+        bdr.set_row_split_override(0, 0, 0)
+    err = max_rel_err(got, oracle.lm_head(hid, lm_w, "bf16"))
+    log(f"ring {ring}, {mt} row tiles: LM head M={M} N={N} H={H} ({T} tiles a wave): "
+        f"max rel err {err:.3e}")
+    assert err <= 1e-3
+
+
+@pytest.mark.parametrize("mt,ring", RING_CASES)
+def test_row_split_every_ring_fc_split_k(mt, ring):
+    """The same on the fc: one row range of two passes per wave, two tap
+    segments, the K range split in two (fp32 partials, ordered reduction)."""
+    import block_draft_readout_amd as bdr
+    import numpy as np
+    T = _ring_tiles(mt, ring)
+    H = (64 * T + 127) // 128 * 128
+    rows = 16 * mt - 3
+    rng = np.random.default_rng(mt * 1000 + ring)
+    taps = [synth.to_bf16_bits(rng.standard_normal((rows, H)).astype(np.float32)) for _ in range(2)]
+    fc_w = synth.to_bf16_bits((rng.standard_normal((H, 2 * H)) / np.sqrt(2 * H)).astype(np.float32))
+    bdr.set_row_split_override(ring, 1, 2)
+    try:
+        out = bdr.dflash_fuse_fc([dev(t) for t in taps], dev(fc_w))
+        torch.cuda.synchronize()
+    finally:
+        bdr.set_row_split_override(0, 0, 0)
+    err = max_rel_err(oracle.widen(host_bits(out), "bf16"), oracle.fuse_fc(taps, fc_w, "bf16"))
+    log(f"ring {ring}, {mt} row tiles: fc rows={rows} H={H} split K: max rel err {err:.3e}")
     assert err <= 4e-3
 
 
