@@ -352,7 +352,7 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
 // cost W bytes + a quarter of the A bytes staged per pass (+ the partial-sum
 // round trip).
 //
-// bf16 passes are groups of `ring` slots (gemm_ns.h, ns_lean_body): with t
+// Passes are groups of `ring` slots (gemm_ns.h, ns_lean_body): with t
 // tiles a wave walks npass passes of ng groups; the ring depth is the one of
 // kNsLeanRings that leaves the fewest slots (empty ones still cost their
 // MFMAs and issue), the deepest among equals.
@@ -390,18 +390,11 @@ static int64_t ns_wave_tiles(int64_t N, int64_t nwg) {
   return ((n_t + nwg - 1) / nwg + 3) / 4;
 }
 
-// passes of a wave: bf16 with the ring it would take, fp8 in passes of
-// NsTiles<MT>::NTW
-static int64_t ns_passes(int mt, int esize, int64_t tiles, int* ring) {
-  if (esize == 2) {
-    const int r = ns_pick_ring(mt, tiles);
-    if (ring) *ring = r;
-    return ns_lean_passes(mt, r, tiles);
-  }
-  if (ring) *ring = 0;
-  const int ntw = mt <= 3 ? 16 : mt == 4 ? 12 : mt == 5 ? 9 : mt == 6 ? 8 : mt == 7 ? 6
-                  : mt == 8 ? 5 : mt == 9 ? 4 : 3;
-  return (tiles + ntw - 1) / ntw;
+// passes of a wave with the ring it would take (kNsLeanRings)
+static int64_t ns_passes(int mt, int64_t tiles, int* ring) {
+  const int r = ns_pick_ring(mt, tiles);
+  if (ring) *ring = r;
+  return ns_lean_passes(mt, r, tiles);
 }
 
 static std::atomic<int> g_ns_ring{0};
@@ -433,7 +426,7 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
     int64_t nwg = std::max<int64_t>(1, kNumCU / ks_eff);
     nwg = std::min<int64_t>(nwg, (N + 63) / 64);
     const int64_t rows = (N + nwg - 1) / nwg;
-    const int64_t npass = ns_passes(static_cast<int>(mtiles), esize, ns_wave_tiles(N, nwg), nullptr);
+    const int64_t npass = ns_passes(static_cast<int>(mtiles), ns_wave_tiles(N, nwg), nullptr);
     double cost = static_cast<double>(kbps) * KE * (esize * rows + 0.5 * M * npass);
     if (ks_eff > 1) cost += 34e3 + static_cast<double>(ks_eff) * M * N * 8 / kNumCU;
     if (cost < best) {
@@ -456,8 +449,8 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   p->stream = true;
   p->ns = true;
   p->mt = static_cast<int>(mtiles);
-  ns_passes(p->mt, esize, ns_wave_tiles(N, p->n_waves), &p->ring);
-  if (esize == 2 && g_ns_ring.load() > 0) p->ring = g_ns_ring.load();   // (launch checks it is built)
+  ns_passes(p->mt, ns_wave_tiles(N, p->n_waves), &p->ring);
+  if (g_ns_ring.load() > 0) p->ring = g_ns_ring.load();   // (the launch checks it is built)
   p->kblocks = kblocks;
   p->m_groups = 1;
   p->n_wg = p->n_waves;

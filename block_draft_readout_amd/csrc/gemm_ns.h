@@ -1,37 +1,51 @@
 // Row-split workgroup GEMM for 16 < M <= 160 (gfx950): C[M, N] = A[M, K] * W[N, K]^T,
 // W in bf16, or in fp8 (E4M3 codes, one fp32 scale per row) against bf16 A.
 //
-// Four waves per workgroup; the workgroup owns a balanced range of W rows and
-// each wave a quarter of it.  Every wave streams its own rows through a
-// private LDS ring with buffer-to-LDS loads (no workgroup barrier per visit,
-// and each fp8 code is widened once), while the A slice of the current K
-// block is shared: staged once per workgroup into LDS (double-buffered, one
-// barrier per K block) and held in every wave's registers for all the A row
-// tiles, so one W visit (16 rows x 128 reduction elements) feeds MT
-// independent accumulator chains.
+// Four waves per workgroup; the workgroup owns a balanced range of W rows (in
+// whole 16-row tiles) and each wave a quarter of it.  Every wave streams its
+// own rows through a private LDS ring with buffer-to-LDS loads (no workgroup
+// barrier per visit, and each fp8 code is widened once), while the A slice of
+// the current K block is shared: staged once per workgroup into LDS (double-
+// buffered, one barrier per K block) and held in every wave's registers for
+// all the A row tiles, so one W visit (16 rows x 128 reduction elements)
+// feeds MT independent accumulator chains.
 //
 //   K block   128 reduction elements: W visit rows of 256 bytes (bf16) or 128
 //             bytes (fp8), A slice rows of 256 bytes (never straddling a tap
 //             segment: segments are multiples of 128 elements);
-//   passes    a wave walks its tiles in passes of at most NTW (accumulator
-//             budget NTW * MT * 4 <= 256); every wave runs the same number of
+//   passes    a wave walks its tiles in passes (accumulator budget NTW * MT *
+//             4 registers); every wave of a workgroup runs the same number of
 //             passes and K blocks, so the barriers match;
 //   order     visits run pass by pass, K block by K block, tile by tile, and
 //             each wave's loads stream on across block and pass boundaries,
-//             kAhead = R - 1 visits ahead (a ring slot is refilled only after
-//             this wave multiplied the visit it held);
+//             R - 1 visits ahead (a ring slot is refilled only after this wave
+//             multiplied the visit it held);
 //   A stage   the slice of the next block is copied (each wave a quarter of
 //             the loads) right after the barrier of the current one; the
 //             buffer it overwrites was last read before that barrier.
 //
-// Loads to LDS are not tracked by the compiler, so the waits are explicit and
-// count what this wave issued afterwards (vmcnt retires in issue order):
-//   * before multiplying visit v: vmcnt <= kAhead * NI when the loads of v+1
-//     .. v+kAhead were issued (A loads issued after v only make this stricter),
-//     else vmcnt(0);
-//   * before the barrier of a block: this wave's share of its A slice is
-//     followed by the W loads of the visits it issued since, at least
-//     min(visits of the previous block, kAhead) of them: vmcnt <= NI times that.
+// The schedule is fixed at compile time, so the loop carries almost no
+// bookkeeping (a loop that tracked its visits at run time spent about as
+// many scalar instructions as MFMAs and kept the MFMA pipe ~28 % busy):
+//   * a pass holds ng groups of R tile slots (ng <= NG, chosen per workgroup
+//     from its range so that few slots stay empty); tile t of a pass lives in
+//     ring slot t % R in every K block;
+//   * the visit loaded at step t is the one R - 1 ahead, into the slot read at
+//     step t - 1: tile t + R - 1 of this block, or tile t + R - 1 - ng R of the
+//     next block (or of the next pass's first) -- the slot is known at compile
+//     time, only the tile's offset is selected at run time;
+//   * a slot past the wave's tiles (at most a few in its last pass) reads
+//     nothing (out-of-range loads) and is not stored;
+//   * loads to LDS are not tracked by the compiler, so the waits are explicit
+//     and count what this wave issued after the data it needs (vmcnt retires
+//     in issue order).  Every block issues its MT A-staging loads (out of
+//     range past the last block or row), so each wait counts a compile-time
+//     number of loads: before step t NI * (R - 1), + MT while the visit
+//     predates the block's A loads; before a block's barrier NI * R (at least
+//     R visits followed its A loads), NI * (R - 1) for the first.
+// R is a template argument: deep rings for long ranges (the LM head), shallow
+// ones where a wave has two or three tiles (a K-split fc), so that the ring is
+// not filled with empty slots.
 #pragma once
 
 #include "gemm_kernels.h"
@@ -53,319 +67,6 @@ struct NsShape {
   static constexpr int WSTEPS = F8 ? 2 : 4;         // 16-byte W reads per row per visit
 };
 
-// accumulator tiles per pass by A tiles: NTW * MT * 4 accumulators next to
-// MT * 16 operand registers (the largest counts that compile without spills)
-template <int MT> struct NsTiles {
-  static constexpr int NTW = MT <= 3 ? 16 : MT == 4 ? 12 : MT == 5 ? 9 : MT == 6 ? 8
-                           : MT == 7 ? 6 : MT == 8 ? 5 : MT == 9 ? 4 : 3;
-};
-
-// tiles per visit: one visit carries VT 16-row tiles (one load batch, one
-// wait).  Two fp8 tiles per visit measured ~7 % faster with 2..3 A tiles (the
-// codes of one tile are few bytes per visit); with more A tiles, and for
-// bf16, one tile per visit is faster.
-template <typename S, int MT>
-constexpr int ns_vt() { return kIsFp8<S> && MT <= 3 ? 2 : 1; }
-
-// ring slots per wave (of VT tiles each): as many as LDS holds beside two A
-// stagings of MT tiles, and as vmcnt can count (NI * VT * (R - 1) + MT <= 63)
-template <typename S, int MT>
-constexpr int ns_ring() {
-  constexpr int vt = ns_vt<S, MT>();
-  constexpr int fit = (160 * 1024 - 2 * MT * NsShape<S>::ASLOT) / (kNsWaves * vt * NsShape<S>::SLOT);
-  constexpr int cnt = (63 - MT) / (NsShape<S>::NI * vt) + 1;
-  constexpr int r = fit < cnt ? fit : cnt;
-  return r > 16 ? 16 : r;
-}
-
-// LDS bytes: four rings + two A stagings of MT tiles
-template <typename S, int MT>
-constexpr size_t ns_lds_bytes() {
-  return static_cast<size_t>(kNsWaves * ns_ring<S, MT>() * ns_vt<S, MT>() * NsShape<S>::SLOT) +
-         static_cast<size_t>(2 * MT) * NsShape<S>::ASLOT;
-}
-
-// wait until at most NI * c loads are outstanding, c in 0..C
-template <int NI, int C>
-__device__ __forceinline__ void ns_wait(int c) {
-  if constexpr (C > 0) {
-    if (c < C) {
-      ns_wait<NI, C - 1>(c);
-      return;
-    }
-  }
-  BDR_WAIT_VM_LGKM(NI * C, 15);
-}
-
-// One workgroup's share of C: row range bx of sa.n_waves, K split by; lds is
-// the workgroup's dynamic LDS (ns_lds_bytes<S, MT>() bytes).
-template <typename S, int MT, int NTW>
-__device__ __forceinline__ void ns_body(const StreamArgs& sa, unsigned bx, unsigned by, char* lds) {
-  using SH = NsShape<S>;
-  constexpr bool F8 = SH::F8;
-  constexpr int VT = ns_vt<S, MT>();
-  static_assert(NTW % VT == 0, "whole visits per pass");
-  constexpr int NI = SH::NI * VT;            // loads per visit
-  constexpr int SLOTV = VT * SH::SLOT;       // one visit in the ring
-  constexpr int R = ns_ring<S, MT>();
-  constexpr int kAhead = R - 1;
-  static_assert(ns_lds_bytes<S, MT>() <= 160 * 1024, "LDS budget");
-  constexpr int NA = MT;                    // A loads per wave per block (4 * MT in all)
-  static_assert(NI * kAhead + NA <= 63, "vmcnt range");
-  const GemmArgs& g = sa.g;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int lane = static_cast<int>(threadIdx.x) & 63;
-  const int r16 = lane & 15;
-  const int grp = lane >> 4;
-
-  // the workgroup's 16-row tiles, then this wave's quarter of them: ranges
-  // start on a tile boundary, so each 16-column piece of an output row is one
-  // aligned 64-byte store (a range starting mid-tile made every piece straddle
-  // two 64-byte blocks: 1.8x the logits' bytes written)
-  const int64_t n_t = (g.N + 15) / 16;
-  const int64_t t_lo = static_cast<int64_t>(bx) * n_t / sa.n_waves;
-  const int64_t t_hi = static_cast<int64_t>(bx + 1) * n_t / sa.n_waves;
-  // (row indices fit 31 bits; readfirstlane keeps everything derived from the
-  // wave index in scalar registers, so the load descriptors stay uniform)
-  const int n_lo = __builtin_amdgcn_readfirstlane(
-      static_cast<int>(16 * (t_lo + (t_hi - t_lo) * wave / kNsWaves)));
-  const int n_hi = __builtin_amdgcn_readfirstlane(static_cast<int>(
-      min<int64_t>(g.N, 16 * (t_lo + (t_hi - t_lo) * (wave + 1) / kNsWaves))));
-  const int ntiles = n_hi > n_lo ? (n_hi - n_lo + 15) / 16 : 0;
-  // passes: the same count on every wave (from the largest quarter); pass p
-  // holds base (+1 for the first rem passes) of this wave's tiles
-  const int max_tiles = static_cast<int>((t_hi - t_lo + kNsWaves - 1) / kNsWaves);
-  const int npass = max(1, (max_tiles + NTW - 1) / NTW);
-  const int pbase = ntiles / npass, prem = ntiles - pbase * npass;
-  auto pass_lo = [&](int p) { return p * pbase + min(p, prem); };
-  const uint32_t kb_lo = static_cast<uint32_t>(by * sa.kb_per_split);
-  const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
-  if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
-  const int nkb = static_cast<int>(kb_hi - kb_lo);
-  const OutRef out(g, by);
-  const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
-  const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
-  const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
-  const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
-  const int mtiles = static_cast<int>((g.M + 15) / 16);
-
-  // this wave's rows (a missing tile of a visit reads zeros)
-  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
-                              static_cast<uint32_t>(n_hi - n_lo) * kbytes);
-  char* const ring = lds + wave * (R * SLOTV);
-  char* const stage = lds + kNsWaves * R * SLOTV;             // [2][MT][ASLOT]
-  // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
-  // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
-  // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
-  // (chunk c at position c ^ row-in-load): with the padded groups, the 16
-  // rows a step reads then fall on 16 different bank groups.
-  constexpr int CPR = SH::WROW / 16;
-  const uint32_t w_row = static_cast<uint32_t>(lane / CPR);
-  const uint32_t w_chunk = static_cast<uint32_t>((lane % CPR) ^ (lane / CPR)) * 16;
-  const uint32_t a_row = static_cast<uint32_t>(lane / 16);
-  const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ (lane / 16)) * 16;
-  // operand reads: chunk c of row r16 at rd + ((c ^ rs) * 16) (W) / rd_a + ((c ^ rs_a) * 16) (A)
-  const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
-  const int rs = r16 % SH::RPI;
-  const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
-  const int rs_a = r16 % 4;
-
-  f32x4_t acc[NTW][MT];
-  auto zero_acc = [&]() {
-    static_for<NTW>([&](auto t) {
-      static_for<MT>([&](auto m) { acc[t][m] = f32x4_t{0.f, 0.f, 0.f, 0.f}; });
-    });
-  };
-  zero_acc();
-  u32x4_t a[MT][4];
-
-  // W visit (tiles t .. t+VT-1 of this wave, block kb) -> ring slot; a tile at
-  // or past `t_end` (the end of the pass) is not read (out-of-range loads,
-  // still counted by vmcnt)
-  auto dma_w = [&](uint32_t kb, int t, int t_end, int slot) {
-    const uint32_t k0 = kb * SH::WROW;
-    const uint32_t lo = k0 + w_chunk < kbytes ? w_chunk : kOOB;
-    char* dst = ring + slot * SLOTV;
-#pragma unroll
-    for (int u = 0; u < VT; ++u) {
-      const uint32_t lou = t + u < t_end ? lo : kOOB;
-#pragma unroll
-      for (int j = 0; j < SH::NI; ++j) {
-        const uint32_t row = static_cast<uint32_t>(16 * (t + u) + j * SH::RPI) + w_row;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (__attribute__((address_space(3))) void*)(dst + u * SH::SLOT + j * SH::GROUP), 16,
-            lou + row * kbytes + k0, 0, 0, 2);
-      }
-    }
-  };
-  // this wave's share of the A slice of block kb -> staging buffer b: loads
-  // j = wave, wave + 4, ... of the 4 * MT (tile j / 4, rows 4 * (j % 4) ..)
-  auto dma_a = [&](uint32_t kb, int b) {
-    const uint32_t k0 = kb * (kNsKE * 2);
-    const uint32_t ts = k0 / segbytes;
-    const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
-    const uint32_t lo = k0 + a_chunk < akbytes ? (k0 - ts * segbytes) + a_chunk : kOOB;
-    char* dst = stage + b * (MT * SH::ASLOT);
-    static_for<MT>([&](auto i) {
-      const int j = wave + kNsWaves * i;
-      const int mt = j / 4;
-      if (mt < mtiles) {
-        const uint32_t row = static_cast<uint32_t>(16 * mt + 4 * (j % 4)) + a_row;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(dst + mt * SH::ASLOT + (j % 4) * (1024 + 64)),
-            16, lo + row * segbytes, 0, 0, 0);
-      }
-    });
-  };
-  // A operands of every tile from staging buffer b: bf16 W -> chunk 4s + grp
-  // (elements 32s + 8grp ..); fp8 W -> chunk 8(i/2) + 2grp + i%2 (elements
-  // 64(i/2) + 16grp + 8(i%2) .., the order of the 16 codes a lane reads)
-  auto stage_to_regs = [&](int b) {
-    const char* src = stage + b * (MT * SH::ASLOT) + rd_a;
-    static_for<MT>([&](auto m) {
-      static_for<4>([&](auto i) {
-        const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
-        a[m][i] = (m < mtiles) ? *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + (c ^ rs_a) * 16)
-                               : u32x4_t{0u, 0u, 0u, 0u};
-      });
-    });
-  };
-  // one tile of a visit (ring slot `slot`, tile u) into the accumulators of tile t
-  auto compute = [&](auto t, int slot, int u) {
-    const char* src = ring + slot * SLOTV + u * SH::SLOT + rd;
-    u32x4_t q[SH::WSTEPS];
-    static_for<SH::WSTEPS>([&](auto s) {
-      q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
-    });
-    if constexpr (F8) {
-      static_for<SH::WSTEPS>([&](auto s) {
-        u32x4_t lo, hi;
-        e4m3x16_to_bf16(q[s], lo, hi);
-        static_for<MT>([&](auto m) {
-          acc[t][m] = mma16(a[m][2 * s], lo, acc[t][m], uint16_t());
-          acc[t][m] = mma16(a[m][2 * s + 1], hi, acc[t][m], uint16_t());
-        });
-      });
-    } else {
-      static_for<SH::WSTEPS>([&](auto s) {
-        static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
-      });
-    }
-  };
-
-  // visit cursor for the loads: pass ip, block ikb, tile it of the pass
-  int nvis = 0;
-  for (int p = 0; p < npass; ++p) nvis += (pass_lo(p + 1) - pass_lo(p) + VT - 1) / VT * nkb;
-  // (the pass bounds are recomputed only when the cursor changes pass)
-  int iv = 0, ip = 0, it = 0, slot = 0;
-  int ip_lo = 0, ip_n = pass_lo(1);
-  uint32_t ikb = kb_lo;
-  auto issue_next = [&]() {
-    while (ip_n == 0) {      // passes with no tiles on this wave
-      ++ip;
-      ip_lo = pass_lo(ip);
-      ip_n = pass_lo(ip + 1) - ip_lo;
-    }
-    dma_w(ikb, ip_lo + it, ip_lo + ip_n, slot);
-    ++iv;
-    slot = slot + 1 == R ? 0 : slot + 1;
-    it += VT;
-    if (it >= ip_n) {
-      it = 0;
-      if (++ikb == kb_hi) {
-        ikb = kb_lo;
-        ++ip;
-        ip_lo = pass_lo(ip);
-        ip_n = pass_lo(ip + 1) - ip_lo;
-      }
-    }
-  };
-
-  dma_a(kb_lo, 0);
-  for (int d = 0; d < kAhead && iv < nvis; ++d) issue_next();
-  int v = 0;                 // visit multiplied next
-  int vslot = 0;             // its ring slot (v % R)
-  int prev_vis = iv;         // visits whose loads followed the current A slice's
-  int blk = 0;
-  for (int p = 0; p < npass; ++p) {
-    const int tp = pass_lo(p);
-    const int ntp = pass_lo(p + 1) - tp;
-    for (uint32_t kb = kb_lo; kb < kb_hi; ++kb, ++blk) {
-      // this block's A slice: own share complete, then everyone's
-      ns_wait<NI, kAhead>(min(prev_vis, kAhead));
-      BDR_WG_BARRIER();
-      stage_to_regs(blk & 1);
-      const bool more = blk + 1 < npass * nkb;
-      if (more) dma_a(kb + 1 < kb_hi ? kb + 1 : kb_lo, (blk + 1) & 1);
-      int issued = 0;
-      static_for<NTW / VT>([&](auto vt) {
-        if (VT * vt < ntp) {
-          const bool full = v + kAhead < nvis;
-          if (full) {
-            issue_next();
-            ++issued;
-            BDR_WAIT_VM_LGKM(NI * kAhead, 15);
-          } else {
-            BDR_WAIT_VM_LGKM(0, 15);
-          }
-          static_for<VT>([&](auto u) {
-            compute(std::integral_constant<int, VT * decltype(vt)::value + decltype(u)::value>{},
-                    vslot, u);
-          });
-          // all of the visit's LDS reads ahead of its MFMAs (one latency per visit)
-          __builtin_amdgcn_sched_group_barrier(0x100, VT * SH::WSTEPS, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, VT * SH::WSTEPS * MT * (F8 ? 2 : 1), 0);
-          ++v;
-          vslot = vslot + 1 == R ? 0 : vslot + 1;
-        }
-      });
-      // loads issued after the next A slice: the W loads of this block's visits
-      prev_vis = issued;
-    }
-    // pass p complete: scale (fp8) and store, then clear.  The row base is
-    // opaque so that no part of the store addresses is kept live across the loop.
-    int64_t nbase = static_cast<int64_t>(n_lo) + 16 * tp + r16;
-    asm volatile("" : "+v"(nbase));
-    static_for<NTW>([&](auto t) {
-      const int64_t n = nbase + 16 * t;
-      if (t < ntp && n < n_hi) {
-        float s = 1.f;
-        if constexpr (F8) s = g.w_scale[n];
-        static_for<MT>([&](auto m) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t row = 16 * m + 4 * grp + i;
-            if (row < out.M) out.put(row, n, acc[t][m][i] * s);
-          }
-        });
-      }
-    });
-    zero_acc();
-  }
-}
-
-// ----------------------------------------------------------------------------
-// bf16 weights: the same organisation with a schedule fixed at compile time, so
-// the loop carries almost no bookkeeping (the generic loop above spent about
-// as many scalar instructions as MFMAs and kept the MFMA pipe ~28 % busy):
-//   * a pass holds ng groups of R tile slots (ng <= NG, chosen per workgroup
-//     from its range so that few slots stay empty); tile t of a pass lives in
-//     ring slot t % R in every K block;
-//   * the visit loaded at step t is the one R - 1 ahead, into the slot read at
-//     step t - 1: tile t + R - 1 of this block, or tile t + R - 1 - ng R of the
-//     next block (or of the next pass's first) -- the slot is known at compile
-//     time, only the tile's offset is selected at run time;
-//   * a slot past the wave's tiles (at most a few in its last pass) reads
-//     nothing (out-of-range loads) and is not stored;
-//   * every block issues its MT A-staging loads (out of range past the last
-//     block or row), so each wait counts a compile-time number of loads: before
-//     step t NI * (R - 1), + MT while the visit predates the block's A loads;
-//     before a block's barrier NI * R (at least R visits followed its A loads),
-//     NI * (R - 1) for the first.
-// R is a template argument: deep rings for long ranges (the LM head), shallow
-// ones where a wave has two or three tiles (a K-split fc), so that the ring is
-// not filled with empty slots.
-// ----------------------------------------------------------------------------
 template <int MT> constexpr int ns_lean_ntw_max() { return kNsLeanNtwMax[MT]; }
 
 template <int MT, int R>
@@ -374,9 +75,9 @@ struct NsLean {
   static constexpr int NTW = NG * R;
 };
 
-template <int MT, int R>
+template <typename S, int MT, int R>
 constexpr size_t ns_lean_lds_bytes() {
-  using SH = NsShape<uint16_t>;
+  using SH = NsShape<S>;
   return static_cast<size_t>(kNsWaves * R * SH::SLOT) + static_cast<size_t>(2 * MT) * SH::ASLOT;
 }
 
@@ -386,15 +87,15 @@ __device__ __forceinline__ void ns_wait_vm() {
   BDR_WAIT_VM_LGKM(n, 15);
 }
 
-template <int MT, int R>
+template <typename S, int MT, int R>
 __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, unsigned by,
                                              char* lds) {
-  using S = uint16_t;
   using SH = NsShape<S>;
+  constexpr bool F8 = SH::F8;
   constexpr int NG = NsLean<MT, R>::NG;
   constexpr int NTW = NsLean<MT, R>::NTW;
   static_assert(NG >= 1 && R >= 2, "ring shape");
-  static_assert(ns_lean_lds_bytes<MT, R>() <= 160 * 1024, "LDS budget");
+  static_assert(ns_lean_lds_bytes<S, MT, R>() <= 160 * 1024, "LDS budget");
   constexpr int NI = SH::NI;        // loads per visit
   constexpr int NA = MT;            // A loads per wave per block
   static_assert(NI * (R - 1) + NA <= 63, "vmcnt range");
@@ -403,7 +104,12 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  // tile-aligned ranges as in ns_body
+  // the workgroup's 16-row tiles, then this wave's quarter of them: ranges
+  // start on a tile boundary, so each 16-column piece of an output row is one
+  // aligned 64-byte store (a range starting mid-tile made every piece straddle
+  // two 64-byte blocks: 1.8x the logits' bytes written).  Row indices fit 31
+  // bits; readfirstlane keeps everything derived from the wave index in
+  // scalar registers, so the load descriptors stay uniform.
   const int64_t n_t = (g.N + 15) / 16;
   const int64_t t_lo = static_cast<int64_t>(bx) * n_t / sa.n_waves;
   const int64_t t_hi = static_cast<int64_t>(bx + 1) * n_t / sa.n_waves;
@@ -420,7 +126,8 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
   if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
   const OutRef out(g, by);
-  const uint32_t kbytes = static_cast<uint32_t>(g.K * 2);
+  const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
+  const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
   const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
   const uint32_t wrows = static_cast<uint32_t>(n_hi > n_lo ? n_hi - n_lo : 0);
@@ -428,8 +135,11 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
                               wrows * kbytes);
   char* const ring = lds + wave * (R * SH::SLOT);
   char* const stage = lds + kNsWaves * R * SH::SLOT;             // [2][MT][ASLOT]
-  // lane mappings of ns_body (loads: consecutive lanes on one row, chunks
-  // XOR-permuted by the row in the load; operand reads undo the permutation)
+  // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
+  // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
+  // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
+  // (chunk c at position c ^ row-in-load): with the padded groups, the 16
+  // rows an operand read touches fall on 16 different bank groups.
   constexpr int CPR = SH::WROW / 16;
   const uint32_t w_chunk = static_cast<uint32_t>((lane % CPR) ^ (lane / CPR)) * 16;
   uint32_t lane_off = static_cast<uint32_t>(lane / CPR) * kbytes + w_chunk;
@@ -475,7 +185,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
     const uint32_t k0 = kb * (kNsKE * 2);
     const uint32_t ts = k0 / segbytes;
     const rsrc_t ra = make_rsrc(seg_base(g, static_cast<int>(ts)), abytes);
-    const uint32_t lo = (valid && k0 + a_chunk < kbytes) ? (k0 - ts * segbytes) + a_chunk : kOOB;
+    const uint32_t lo = (valid && k0 + a_chunk < akbytes) ? (k0 - ts * segbytes) + a_chunk : kOOB;
     char* dst = stage + b * (MT * SH::ASLOT);
     static_for<MT>([&](auto i) {
       const int j = wave + kNsWaves * i;
@@ -486,23 +196,38 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
           16, lo == kOOB ? kOOB : lo + row * segbytes, 0, 0, 0);
     });
   };
+  // A operands of every tile: bf16 W -> chunk 4i + grp (elements 32i + 8grp ..);
+  // fp8 W -> chunk 8(i/2) + 2grp + i%2 (elements 64(i/2) + 16grp + 8(i%2) ..,
+  // the order of the 16 codes a lane reads)
   auto stage_to_regs = [&](int b) {
     const char* src = stage + b * (MT * SH::ASLOT) + rd_a;
     static_for<MT>([&](auto m) {
       static_for<4>([&](auto i) {
-        a[m][i] = *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + (((4 * i + grp) ^ rs_a) * 16));
+        const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
+        a[m][i] = *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + ((c ^ rs_a) * 16));
       });
     });
   };
   auto compute = [&](auto t, int slot) {
     const char* src = ring + slot * SH::SLOT + rd;
-    u32x4_t q[4];
-    static_for<4>([&](auto s) {
+    u32x4_t q[SH::WSTEPS];
+    static_for<SH::WSTEPS>([&](auto s) {
       q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
     });
-    static_for<4>([&](auto s) {
-      static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
-    });
+    if constexpr (F8) {
+      static_for<SH::WSTEPS>([&](auto s) {
+        u32x4_t lo, hi;
+        e4m3x16_to_bf16(q[s], lo, hi);
+        static_for<MT>([&](auto m) {
+          acc[t][m] = mma16(a[m][2 * s], lo, acc[t][m], uint16_t());
+          acc[t][m] = mma16(a[m][2 * s + 1], hi, acc[t][m], uint16_t());
+        });
+      });
+    } else {
+      static_for<4>([&](auto s) {
+        static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
+      });
+    }
   };
 
   // prologue: A of the first block, then tiles 0 .. R - 2 of pass 0 (ng >= 1)
@@ -549,7 +274,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
             ns_wait_vm<NI * (R - 1) + (T < R - 1 ? NA : 0)>();
             compute(std::integral_constant<int, T>{}, J);
             // the visit's LDS reads ahead of its MFMAs (one latency per visit)
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
           });
         }
@@ -561,11 +286,13 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
     static_for<NTW>([&](auto t) {
       const int64_t n = nb + 16 * t;
       if (t < ng * R && n < n_hi) {
+        float sc = 1.f;
+        if constexpr (F8) sc = g.w_scale[n];
         static_for<MT>([&](auto m) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int64_t row = 16 * m + 4 * grp + i;
-            if (row < out.M) out.put(row, n, acc[t][m][i]);
+            if (row < out.M) out.put(row, n, F8 ? acc[t][m][i] * sc : acc[t][m][i]);
           }
         });
       }
@@ -575,24 +302,6 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   BDR_WAIT_VM_LGKM(0, 15);
 }
 
-// bf16 weights take the compile-time schedule with ring depth R; fp8 weights,
-// and bf16 with R = 0, the generic loop
-template <typename S, int MT, int R>
-__device__ __forceinline__ void ns_any_body(const StreamArgs& sa, unsigned bx, unsigned by,
-                                            char* lds) {
-  if constexpr (kIsFp8<S> || R == 0)
-    ns_body<S, MT, NsTiles<MT>::NTW>(sa, bx, by, lds);
-  else
-    ns_lean_body<MT, R>(sa, bx, by, lds);
-}
-
-template <typename S, int MT, int R>
-constexpr size_t ns_any_lds_bytes() {
-  if constexpr (kIsFp8<S> || R == 0)
-    return ns_lds_bytes<S, MT>();
-  else
-    return ns_lean_lds_bytes<MT, R>();
-}
 
 // K splits of one problem: ceil(kblocks / kb_per_split)
 __device__ __forceinline__ unsigned ns_splits(const StreamArgs& sa) {
@@ -608,7 +317,7 @@ template <typename S, int MT, int R>
 __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const unsigned ks = ns_splits(sa);
-  ns_any_body<S, MT, R>(sa, blockIdx.x / ks, blockIdx.x % ks, lds);
+  ns_lean_body<S, MT, R>(sa, blockIdx.x / ks, blockIdx.x % ks, lds);
 }
 
 // Two GEMMs in one launch (the drafter fc beside the LM head): the first n0
@@ -619,17 +328,17 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a
                                                               const StreamArgs a1, unsigned n0) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (blockIdx.x < n0) {
-    ns_any_body<S, MT0, R0>(a0, blockIdx.x, 0, lds);
+    ns_lean_body<S, MT0, R0>(a0, blockIdx.x, 0, lds);
   } else {
     const unsigned i = blockIdx.x - n0;
     const unsigned ks = ns_splits(a1);
-    ns_any_body<S, MT1, R1>(a1, i / ks, i % ks, lds);
+    ns_lean_body<S, MT1, R1>(a1, i / ks, i % ks, lds);
   }
 }
 
 template <typename S, int MT, int R>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  constexpr size_t lds = ns_any_lds_bytes<S, MT, R>();
+  constexpr size_t lds = ns_lean_lds_bytes<S, MT, R>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
@@ -646,9 +355,9 @@ hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
 template <typename S, int MT0, int R0, int MT1, int R1>
 hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
                               unsigned n1, hipStream_t st) {
-  constexpr size_t lds = ns_any_lds_bytes<S, MT0, R0>() > ns_any_lds_bytes<S, MT1, R1>()
-                             ? ns_any_lds_bytes<S, MT0, R0>()
-                             : ns_any_lds_bytes<S, MT1, R1>();
+  constexpr size_t lds = ns_lean_lds_bytes<S, MT0, R0>() > ns_lean_lds_bytes<S, MT1, R1>()
+                             ? ns_lean_lds_bytes<S, MT0, R0>()
+                             : ns_lean_lds_bytes<S, MT1, R1>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(

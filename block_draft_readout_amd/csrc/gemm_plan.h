@@ -29,7 +29,7 @@ struct GemmPlan {
   int64_t n_waves = 0;    // row ranges (workgroups along N)
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;
-  int ring = 0;           // ns with bf16 weights: LDS ring slots per wave (kNsLeanRings)
+  int ring = 0;           // ns: LDS ring slots per wave (kNsLeanRings)
   // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
   // K steps of 64 (kblocks / kb_per_split count steps)
   bool tile = false;
@@ -41,7 +41,7 @@ struct GemmPlan {
 // queries and launches always plan identically.
 constexpr int kNumCU = 256;
 
-// Row-split kernel with bf16 weights (gemm_ns.h): per A row-tile count, the
+// Row-split kernel (gemm_ns.h, bf16 and fp8 weights): per A row-tile count, the
 // accumulator tiles one pass can hold, and the ring depths built (deepest
 // first; 0 = none).  A deep ring keeps more loads in flight, a shallow one
 // wastes fewer slots on waves with few tiles.
@@ -56,7 +56,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_spl
                    int n_seg = 1);
 
 // Row-split plans (bf16 and fp8 weights, 16 < M <= 160) take these values in
-// place of their own where non-zero: the ring depth (bf16), the row ranges
+// place of their own where non-zero: the ring depth, the row ranges
 // and the K splits (bounded by the shape).  Process-wide; the two-problem
 // launch is not planned while any is set.
 void set_row_split_override(int ring, int64_t workgroups, int ksplit);

@@ -20,6 +20,20 @@ REL_TOL = {"bf16": 2e-2, "f32": 1e-4}
 NEAR_TIE = 1e-2
 
 
+# Row-split GEMM: ring depths built by A row-tile count (bf16 and fp8 weights)
+# and the accumulator tiles one pass holds
+RINGS = {2: (8, 5, 3), 3: (7, 5, 3), 4: (6, 5, 3), 5: (6, 5, 3), 6: (6, 5, 3), 7: (5, 3),
+         8: (5, 3), 9: (4, 3), 10: (3,)}
+NTW_MAX = {2: 16, 3: 14, 4: 12, 5: 9, 6: 8, 7: 6, 8: 5, 9: 4, 10: 3}
+RING_CASES = [(m, r) for m, rs in RINGS.items() for r in rs]
+
+
+def ring_tiles(mt: int, ring: int) -> int:
+    """Tiles of the largest wave for a ring test: more than a pass holds, so
+    two passes, the second with groups of slots left empty."""
+    return NTW_MAX[mt] // ring * ring + ring + 1
+
+
 def log(msg: str) -> None:
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 

@@ -22,7 +22,7 @@ import oracle
 import workloads
 from oracle import fp8
 from workloads import synth
-from gpu_util import check_draft, dev, host_bits, log, max_rel_err
+from gpu_util import RING_CASES, check_draft, dev, host_bits, log, max_rel_err, ring_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -102,6 +102,47 @@ def test_lm_head_fp8_random_codes_wide_range():
     err = max_rel_err(got, fp8.lm_head_fp8(hid, q, s, "bf16"))
     log(f"lm head fp8, random codes: max rel err {err:.3e}")
     assert err <= LM_TOL
+
+
+@pytest.mark.parametrize("mt,ring", RING_CASES)
+def test_lm_head_fp8_every_ring(mt, ring):
+    """Every ring depth of the row-split kernel with fp8 weights, forced
+    through the plan override on two row ranges: two passes per wave with empty
+    slots in the second, a ragged last tile, a partial last K block (H = 448)."""
+    T = ring_tiles(mt, ring)
+    M, V, H = 16 * mt - 3, 2 * 4 * T * 16 - 5, 448
+    rng = np.random.default_rng(mt * 100 + ring + 7)
+    hid = _bf16(rng, (M, H))
+    q, s = synth.quantize_e4m3_rows(rng.standard_normal((V, H)).astype(np.float32) / np.sqrt(H))
+    bdr().set_row_split_override(ring, 2, 0)
+    try:
+        got = bdr().dspark_lm_head_fp8(dev(hid), dev(q), dev(s)).cpu().numpy()
+    finally:
+        bdr().set_row_split_override(0, 0, 0)
+    err = max_rel_err(got, fp8.lm_head_fp8(hid, q, s, "bf16"))
+    log(f"ring {ring}, {mt} row tiles: fp8 LM head M={M} V={V} H={H}: max rel err {err:.3e}")
+    assert err <= LM_TOL
+
+
+@pytest.mark.parametrize("mt,ring", RING_CASES)
+def test_fc_fp8_every_ring_split_k(mt, ring):
+    """The same on the fp8 fc: one row range, two tap segments, K split in two."""
+    T = ring_tiles(mt, ring)
+    H = (64 * T + 127) // 128 * 128
+    rows = 16 * mt - 3
+    rng = np.random.default_rng(mt * 1000 + ring + 7)
+    taps = [_bf16(rng, (rows, H)) for _ in range(2)]
+    q, s = synth.quantize_e4m3_rows(rng.standard_normal((H, 2 * H)).astype(np.float32)
+                                    / np.sqrt(2 * H))
+    bdr().set_row_split_override(ring, 1, 2)
+    try:
+        out = bdr().dflash_fuse_fc_fp8([dev(t) for t in taps], dev(q), dev(s))
+        torch.cuda.synchronize()
+    finally:
+        bdr().set_row_split_override(0, 0, 0)
+    err = max_rel_err(oracle.widen(host_bits(out), "bf16"), fp8.fuse_fc_fp8(taps, q, s, "bf16"))
+    log(f"ring {ring}, {mt} row tiles: fp8 fc rows={rows} H={H} split K: max rel err {err:.3e}")
+    assert err <= FC_TOL
 
 
 FC_CASES = [(5, 64, 5), (9, 192, 3), (8, 2560, 5), (36, 2560, 5), (8, 5120, 5), (20, 1024, 2),

@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads
 from workloads import synth
-from gpu_util import REL_TOL, dev, host_bits, log, max_rel_err
+from gpu_util import RING_CASES, REL_TOL, dev, host_bits, log, max_rel_err, ring_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -139,28 +139,14 @@ def test_prefill_fc_parity_on_sampled_rows(hidden):
     assert err <= 4e-3
 
 
-# ring depths built for the bf16 row-split kernel by A row-tile count, and the
-# accumulator tiles a pass can hold
-RINGS = {2: (8, 5, 3), 3: (7, 5, 3), 4: (6, 5, 3), 5: (6, 5, 3), 6: (6, 5, 3), 7: (5, 3),
-         8: (5, 3), 9: (4, 3), 10: (3,)}
-NTW_MAX = {2: 16, 3: 14, 4: 12, 5: 9, 6: 8, 7: 6, 8: 5, 9: 4, 10: 3}
-RING_CASES = [(m, r) for m, rs in RINGS.items() for r in rs]
-
-
-def _ring_tiles(mt, ring):
-    """Tiles of the largest wave: more than a pass holds, so two passes, the
-    second with groups of slots left empty."""
-    return NTW_MAX[mt] // ring * ring + ring + 1
-
-
 @pytest.mark.parametrize("mt,ring", RING_CASES)
 def test_row_split_every_ring_lm_head(mt, ring):
-    """Every ring depth built for bf16 weights, forced through the plan
+    """Every ring depth built, forced through the plan
     override on two row ranges: two passes per wave with empty slots in the
     second, a ragged last tile, a partial last K block (H = 392)."""
     import block_draft_readout_amd as bdr
     import numpy as np
-    T = _ring_tiles(mt, ring)
+    T = ring_tiles(mt, ring)
     M, N, H = 16 * mt - 3, 2 * 4 * T * 16 - 5, 392
     rng = np.random.default_rng(mt * 100 + ring)
     hid = synth.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
@@ -182,7 +168,7 @@ def test_row_split_every_ring_fc_split_k(mt, ring):
     segments, the K range split in two (fp32 partials, ordered reduction)."""
     import block_draft_readout_amd as bdr
     import numpy as np
-    T = _ring_tiles(mt, ring)
+    T = ring_tiles(mt, ring)
     H = (64 * T + 127) // 128 * 128
     rows = 16 * mt - 3
     rng = np.random.default_rng(mt * 1000 + ring)
