@@ -442,6 +442,8 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   }
   if (const int64_t wg_o = g_ns_wg.load(); wg_o > 0)
     p->n_waves = std::min<int64_t>(wg_o, (N + 15) / 16);
+  // the output (or one K split's partials) is addressed with 32-bit offsets
+  if (M * N * 4 >= (int64_t(1) << 32)) return false;
   // a wave's rows x row bytes are addressed with 32-bit offsets (with room for
   // the empty slots of its last pass)
   const int64_t rows_w = ((N + p->n_waves - 1) / p->n_waves + 3) / 4;

@@ -125,7 +125,15 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const uint32_t kb_lo = static_cast<uint32_t>(by * sa.kb_per_split);
   const uint32_t kb_hi = static_cast<uint32_t>(min<int64_t>(sa.kblocks, kb_lo + sa.kb_per_split));
   if (t_hi <= t_lo || kb_lo >= kb_hi) return;   // whole workgroup
-  const OutRef out(g, by);
+  // output: fp32 partials of K split `by`, or the final fp32 / bf16 C (the
+  // plan keeps M * N * 4 below 2^32)
+  const bool o_bf16 = !g.partial && g.out_kind == OUT_BF16;
+  const uint32_t o_es = o_bf16 ? 2 : 4;
+  const uint32_t o_row = static_cast<uint32_t>(g.N) * o_es;      // bytes per output row
+  const rsrc_t ro = make_rsrc(
+      static_cast<char*>(g.out) + (g.partial ? static_cast<int64_t>(by) * g.M * g.N * 4 : 0),
+      static_cast<uint32_t>(g.M) * o_row);
+  const uint32_t o_lane = static_cast<uint32_t>(4 * grp) * o_row;  // this lane's first row
   const uint32_t kbytes = static_cast<uint32_t>(g.K * static_cast<int64_t>(sizeof(S)));
   const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
@@ -196,38 +204,57 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
           16, lo == kOOB ? kOOB : lo + row * segbytes, 0, 0, 0);
     });
   };
-  // A operands of every tile: bf16 W -> chunk 4i + grp (elements 32i + 8grp ..);
-  // fp8 W -> chunk 8(i/2) + 2grp + i%2 (elements 64(i/2) + 16grp + 8(i%2) ..,
-  // the order of the 16 codes a lane reads)
-  auto stage_to_regs = [&](int b) {
+  // Operands of one visit.  A: bf16 W -> chunk 4i + grp of each A row
+  // (elements 32i + 8grp ..); fp8 W -> chunk 8(i/2) + 2grp + i%2 (elements
+  // 64(i/2) + 16grp + 8(i%2) .., the order of the 16 codes a lane reads).  W
+  // part i (i = 0..3) of the visit: bf16 its read q[i]; fp8 the low (i even)
+  // or high (i odd) eight codes of read q[i/2], widened.  Each accumulator
+  // takes parts 0, 1, 2, 3 in that order.
+  auto read_a = [&](int b, auto i) {
     const char* src = stage + b * (MT * SH::ASLOT) + rd_a;
+    const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
     static_for<MT>([&](auto m) {
-      static_for<4>([&](auto i) {
-        const int c = F8 ? 8 * (i / 2) + 2 * grp + i % 2 : 4 * i + grp;
-        a[m][i] = *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + ((c ^ rs_a) * 16));
-      });
+      a[m][i] = *reinterpret_cast<const u32x4_t*>(src + m * SH::ASLOT + ((c ^ rs_a) * 16));
     });
   };
-  auto compute = [&](auto t, int slot) {
+  auto read_w = [&](int slot, u32x4_t (&q)[SH::WSTEPS]) {
     const char* src = ring + slot * SH::SLOT + rd;
-    u32x4_t q[SH::WSTEPS];
     static_for<SH::WSTEPS>([&](auto s) {
       q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
     });
+  };
+  auto mma_part = [&](auto t, auto i, const u32x4_t (&q)[SH::WSTEPS], u32x4_t& lo, u32x4_t& hi) {
     if constexpr (F8) {
-      static_for<SH::WSTEPS>([&](auto s) {
-        u32x4_t lo, hi;
-        e4m3x16_to_bf16(q[s], lo, hi);
-        static_for<MT>([&](auto m) {
-          acc[t][m] = mma16(a[m][2 * s], lo, acc[t][m], uint16_t());
-          acc[t][m] = mma16(a[m][2 * s + 1], hi, acc[t][m], uint16_t());
-        });
+      if constexpr (i % 2 == 0) e4m3x16_to_bf16(q[i / 2], lo, hi);
+      static_for<MT>([&](auto m) {
+        acc[t][m] = mma16(a[m][i], i % 2 == 0 ? lo : hi, acc[t][m], uint16_t());
       });
     } else {
-      static_for<4>([&](auto s) {
-        static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][s], q[s], acc[t][m], uint16_t()); });
-      });
+      static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][i], q[i], acc[t][m], uint16_t()); });
     }
+  };
+  // a visit with the A operands in registers: its LDS reads, then its MFMAs
+  // (one latency per visit)
+  auto compute = [&](auto t, int slot) {
+    u32x4_t q[SH::WSTEPS], lo, hi;
+    read_w(slot, q);
+    static_for<4>([&](auto i) { mma_part(t, i, q, lo, hi); });
+    __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+  };
+  // the first visit of a block, which also brings the block's A slice (staging
+  // buffer b) into registers: part i's A reads, then its MFMAs, so the MFMAs of
+  // one part run while the next part's reads are in flight (at most 15 LDS
+  // reads can be outstanding)
+  auto compute_first = [&](auto t, int slot, int b) {
+    u32x4_t q[SH::WSTEPS], lo, hi;
+    read_w(slot, q);
+    static_for<4>([&](auto i) {
+      read_a(b, i);
+      mma_part(t, i, q, lo, hi);
+      __builtin_amdgcn_sched_group_barrier(0x100, i == 0 ? SH::WSTEPS + MT : MT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+    });
   };
 
   // prologue: A of the first block, then tiles 0 .. R - 2 of pass 0 (ng >= 1)
@@ -243,7 +270,9 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
       else
         ns_wait_vm<NI * R>();
       BDR_WG_BARRIER();
-      stage_to_regs(blk & 1);
+      // the next block's A slice first: its segment pointer may come from a
+      // scalar load, whose wait would otherwise also wait for this block's A
+      // reads
       const bool last_blk = kb + 1 == kb_hi;
       const uint32_t nkb = last_blk ? kb_lo : kb + 1;
       const uint32_t nbase = last_blk ? (p + 1 < npass ? base + pass_bytes : kOOB) : base;
@@ -272,28 +301,35 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
               dma_w(last_g ? nx_blk : in_blk, last_g ? nkb : kb, J - 1);
             }
             ns_wait_vm<NI * (R - 1) + (T < R - 1 ? NA : 0)>();
-            compute(std::integral_constant<int, T>{}, J);
-            // the visit's LDS reads ahead of its MFMAs (one latency per visit)
-            __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+            if constexpr (T == 0)
+              compute_first(std::integral_constant<int, T>{}, J, blk & 1);
+            else
+              compute(std::integral_constant<int, T>{}, J);
           });
         }
       });
     }
-    // pass p complete: store the tiles in this wave's range, then clear
-    int64_t nb = static_cast<int64_t>(n_lo) + 16 * static_cast<int64_t>(ng * R) * p + r16;
-    asm volatile("" : "+v"(nb));
+    // pass p complete: store the tiles in this wave's range, then clear.  The
+    // stores go through a descriptor over this output (or K split), one 32-bit
+    // byte offset per store: rows past M fall beyond its size and are dropped.
+    const int nb = n_lo + 16 * ng * R * p + r16;
     static_for<NTW>([&](auto t) {
-      const int64_t n = nb + 16 * t;
+      const int n = nb + 16 * t;
       if (t < ng * R && n < n_hi) {
         float sc = 1.f;
         if constexpr (F8) sc = g.w_scale[n];
+        uint32_t off = o_lane + static_cast<uint32_t>(n) * o_es;
+        asm volatile("" : "+v"(off));
         static_for<MT>([&](auto m) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t row = 16 * m + 4 * grp + i;
-            if (row < out.M) out.put(row, n, F8 ? acc[t][m][i] * sc : acc[t][m][i]);
-          }
+          static_for<4>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const float v = F8 ? acc[t][m][i] * sc : acc[t][m][i];
+            const uint32_t o = off + static_cast<uint32_t>(16 * m + i) * o_row;
+            if (o_bf16)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), ro, o, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ro, o, 0, 0);
+          });
         });
       }
     });
