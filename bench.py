@@ -809,8 +809,8 @@ def main():
         lm_bytes = V * H * es + B * k * H * es + B * k * V * 4
         fc_bytes = (H * w.n_taps * H + w.rows * w.n_taps * H + w.rows * H) * es
     markov_bytes = B * k * V * 4 + V * rk * es + B * k * rk * es + B * k * 4
-    if sampling:      # noise written and read, x written
-        markov_bytes += 3 * B * k * V * 4
+    if sampling:      # x written (the chain generates the draws' noise itself)
+        markov_bytes += B * k * V * 4
     conf_bytes = 0 if w.threshold is None else B * k * 4
     verify_b = float(np.mean(verify_bytes)) + B * k * 4 + conf_bytes
     stage_bytes = {"fc": fc_bytes, "lm_head": lm_bytes, "markov": markov_bytes,

@@ -72,8 +72,11 @@ struct MarkovArgs {
   int32_t* draft;                // [B, k]
   int64_t vtiles;                // ceil(V / 16)
   // sampling (probabilistic drafting): the token of a position is the argmax
-  // of x * inv_t + noise, x = logits + bias, and x is stored
-  const float* noise;            // [B, k, V] Gumbel noise of the draws
+  // of x * inv_t + G, x = logits + bias, and x is stored; G is the standard
+  // Gumbel variate of entry v of (row b, position i) from Philox4x32-10 keyed
+  // by the seed, counter (v / 4, b, i, kStreamDraft), word v % 4 -- generated here, where
+  // it is used, rather than read from memory
+  uint32_t seed_lo, seed_hi;     // Philox key
   float* xout;                   // [B, k, V] biased logits x (the draft distribution)
   float inv_t;                   // 1 / temperature
 };
@@ -293,8 +296,6 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
     const int nb = static_cast<int>(min<int64_t>(16, g.B - b0));
     const int64_t first = (b0 * g.k + pos) * g.V;
     const rsrc_t rz = make_rsrc(g.logits + first, block_bytes(b0));
-    rsrc_t rg;
-    if constexpr (SAMPLE) rg = make_rsrc(g.noise + first, block_bytes(b0));
     const uint32_t lane_off = static_cast<uint32_t>(r16) * zrow;
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
@@ -304,7 +305,26 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
                                ? lane_off + static_cast<uint32_t>(v0) * 4u
                                : kOOB;
       zv[u] = bload16(rz, off);
-      if constexpr (SAMPLE) gv[u] = bload16(rg, off);
+    }
+  };
+  // sampling: the Gumbel variates of the lane's quads (entries v0 .. v0 + 3 of
+  // row b0 + r16 are words 0..3 of one Philox call); ALU work, done while the
+  // hand-off waits
+  auto gen_noise = [&](int pos, int64_t b0, int cwo, int ntlo, int vbo) {
+    if constexpr (SAMPLE) {
+      const uint32_t row = static_cast<uint32_t>(b0 + r16);
+#pragma unroll
+      for (int u = 0; u < MAXT; ++u) {
+        const int tile = cwo + 4 * u;
+        const int v0 = vbo + 16 * tile;
+        if (tile < ntlo && v0 < V32 && row < g.B) {
+          const u32x4_t x = philox4x32_10(
+              u32x4_t{static_cast<uint32_t>(v0) >> 2, row, static_cast<uint32_t>(pos), kStreamDraft},
+              g.seed_lo, g.seed_hi);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) gv[u][w] = __float_as_uint(gumbel_of(bits_to_uniform(x[w])));
+        }
+      }
     }
   };
   // One row (B == 1): the product is taken the other way round, D[row][entry]
@@ -320,25 +340,42 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
     const int64_t first = static_cast<int64_t>(pos) * g.V;
     const uint32_t bytes = static_cast<uint32_t>(V32) * 4u;
     const rsrc_t rz = make_rsrc(g.logits + first, bytes);
-    rsrc_t rg;
-    if constexpr (SAMPLE) rg = make_rsrc(g.noise + first, bytes);
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
       const int tile = cwo + 4 * u;
       const int v = vbo + 16 * tile;
       const uint32_t off = (grp == 0 && tile < ntlo && v < V32) ? static_cast<uint32_t>(v) * 4u : kOOB;
       z1[u] = bload_f32(rz, off);
-      if constexpr (SAMPLE) {
-        n1[u] = bload_f32(rg, off);
-        x1[u] = off;
+      if constexpr (SAMPLE) x1[u] = off;
+    }
+  };
+  // sampling, one row: the lane's entry v is word v % 4 (= r16 % 4) of the
+  // Philox call of its quad
+  auto gen_noise1 = [&](int pos, int cwo, int ntlo, int vbo) {
+    if constexpr (ONE && SAMPLE) {
+      const int w = r16 & 3;
+#pragma unroll
+      for (int u = 0; u < MAXT; ++u) {
+        const int tile = cwo + 4 * u;
+        const int v = vbo + 16 * tile;
+        if (grp == 0 && tile < ntlo && v < V32) {
+          const u32x4_t x = philox4x32_10(
+              u32x4_t{static_cast<uint32_t>(v) >> 2, 0u, static_cast<uint32_t>(pos), kStreamDraft},
+              g.seed_lo, g.seed_hi);
+          const uint32_t bits = w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3];
+          n1[u] = gumbel_of(bits_to_uniform(bits));
+        }
       }
     }
   };
   if (cw >= 0) {
-    if constexpr (ONE)
+    if constexpr (ONE) {
       load_z1(0, cw, ntl, vbase1);
-    else
+      gen_noise1(0, cw, ntl, vbase1);
+    } else {
       load_z(0, 0, cw, ntl, vbase);
+      gen_noise(0, 0, cw, ntl, vbase);
+    }
   }
   BDR_WAIT_VM(0);
   __syncthreads();
@@ -398,7 +435,10 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           key = rowgroup_max16(key);
           if (lane == 0) sk[cw][0][0] = key;
         } else {
-          if (b0 > 0) load_z(pos, b0, cwo, ntlo, vbo);   // the first row group's logits were prefetched
+          if (b0 > 0) {   // the first row group's logits (and noise) were prefetched
+            load_z(pos, b0, cwo, ntlo, vbo);
+            gen_noise(pos, b0, cwo, ntlo, vbo);
+          }
           u32x4_t ef[NC];
           context_frags<S, RKS>(g, b0 + r16 < g.B ? ctx[b0 + r16] : -1, grp, ef);
           // entries past the workgroup's range or the vocabulary get logit
@@ -490,6 +530,17 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
                     tag_key(key, tag));
       }
       if (!last_group) BDR_LDS_BARRIER();   // sk is rewritten by the next row group
+    }
+    // sampling: the next position's noise, while wave 0 waits for the hand-off
+    if constexpr (SAMPLE) {
+      if (cw >= 0 && pos + 1 < g.k) {
+        int cwo = cw, ntlo = ntl, vbo = ONE ? vbase1 : vbase;
+        asm volatile("" : "+s"(cwo), "+s"(ntlo), "+v"(vbo));
+        if constexpr (ONE)
+          gen_noise1(pos + 1, cwo, ntlo, vbo);
+        else
+          gen_noise(pos + 1, 0, cwo, ntlo, vbo);
+      }
     }
     // contexts of the next position (and this position's tokens)
     if (wave == 0) {
@@ -591,11 +642,8 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
   const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
   const uint32_t blk = static_cast<uint32_t>(((nb - 1) * g.k * g.V + g.V) * 4);
   const rsrc_t rz = make_rsrc(g.logits + (b0 * g.k + pos) * g.V, blk);
-  rsrc_t rn, rx;
-  if constexpr (SAMPLE) {
-    rn = make_rsrc(g.noise + (b0 * g.k + pos) * g.V, blk);
-    rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, blk);
-  }
+  rsrc_t rx;
+  if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, blk);
   uint32_t zrow[4];
   bool bok[4];
   float bv[4];
@@ -630,7 +678,18 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
       for (int i = 0; i < 4; ++i) {
         const uint32_t off = (vok && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB;
         zv[u][i] = bload_f32(rz, off);
-        if constexpr (SAMPLE) gn[u][i] = bload_f32(rn, off);
+        if constexpr (SAMPLE) {
+          // entry v of row b0 + 4 grp + i: word v % 4 of its quad's Philox call
+          gn[u][i] = 0.f;
+          if (vok && bok[i]) {
+            const u32x4_t x = philox4x32_10(
+                u32x4_t{static_cast<uint32_t>(v) >> 2, static_cast<uint32_t>(b0 + 4 * grp + i),
+                        static_cast<uint32_t>(pos), kStreamDraft},
+                g.seed_lo, g.seed_hi);
+            const int w = static_cast<int>(v & 3);
+            gn[u][i] = gumbel_of(bits_to_uniform(w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3]));
+          }
+        }
       }
     }
 #pragma unroll

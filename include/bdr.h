@@ -19,7 +19,7 @@
  *     completes leaves its counters and hand-off slots zero-filled again (the
  *     Markov error word too when the call is given a status word), so it can
  *     be reused by later calls and by graph replays.  Other workspace bytes
- *     (argmax keys of verification, sampling noise) are scratch that every
+ *     (argmax keys and log-sum-exp partials of verification) are scratch that every
  *     call rewrites before reading.  One workspace must not be used by two
  *     calls that can run concurrently.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream); all work is
@@ -414,9 +414,11 @@ int dspark_gumbel_noise(int64_t batch, int k, int64_t vocab, uint64_t seed,
  *   draft_tokens [B, k] int32 out
  *   draft_logits [B, k, V] fp32 out (x, before the division by T)
  *   status       optional device int32 out, as in S3
- *   workspace    >= dspark_markov_sample_workspace_bytes(B, k, V): the draw
- *                noise, then a Markov workspace (same rules as S3; its error
- *                word is in the last 256 bytes of this size)
+ *   workspace    >= dspark_markov_sample_workspace_bytes(B, k, V): a Markov
+ *                workspace (same rules as S3; its error word is in the last
+ *                256 bytes of this size).  The draws' noise is generated by
+ *                the chain itself, entry by entry, from the same Philox
+ *                words dspark_gumbel_noise writes for stream 0.
  * ------------------------------------------------------------------------- */
 size_t dspark_markov_sample_workspace_bytes(int64_t batch, int k, int64_t vocab);
 int dspark_markov_sample(const float* logits, int64_t batch, int k,
