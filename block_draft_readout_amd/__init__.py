@@ -311,7 +311,7 @@ def set_row_split_override(ring: int = 0, workgroups: int = 0, ksplit: int = 0) 
     """Process-wide plan override of the row-split GEMM (0 = the planner's
     choice): the bf16 ring depth, the row ranges and the K splits."""
     _abi.check("bdr_set_row_split_override",
-          lib().bdr_set_row_split_override(int(ring), int(workgroups), int(ksplit)))
+               lib().bdr_set_row_split_override(int(ring), int(workgroups), int(ksplit)))
 
 
 def _markov_args(w1, w2, dt_ref):
