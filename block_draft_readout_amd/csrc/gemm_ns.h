@@ -65,6 +65,13 @@ struct NsShape {
   static constexpr int SLOT = NI * GROUP;           // one visit
   static constexpr int ASLOT = 4 * (1024 + 64);     // one A tile: 16 rows x 256 B, 4 rows per load
   static constexpr int WSTEPS = F8 ? 2 : 4;         // 16-byte W reads per row per visit
+  // LDS position of 16-byte chunk c of a row = c ^ wx(row in load, load of the
+  // visit) for W, c ^ ax(row in load) for A.  Chosen so that the 16 rows one
+  // operand read touches spread over the banks with no conflict, with 128
+  // banks served 32 lanes at a time (the fp8 reads of the bf16 permutation
+  // measured about one conflict cycle per LDS instruction).
+  static constexpr int wx(int ril, int load) { return F8 ? (ril >> 1) ^ (load ? 4 : 0) : ril; }
+  static constexpr int ax(int ril) { return F8 ? ril ^ (ril >> 1) : ril; }
 };
 
 template <int MT> constexpr int ns_lean_ntw_max() { return kNsLeanNtwMax[MT]; }
@@ -146,18 +153,23 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
   // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
   // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
-  // (chunk c at position c ^ row-in-load): with the padded groups, the 16
-  // rows an operand read touches fall on 16 different bank groups.
+  // (NsShape::wx / ax): lane l of load j fetches the chunk that belongs at
+  // position l % CPR, and operand reads undo the permutation.
   constexpr int CPR = SH::WROW / 16;
-  const uint32_t w_chunk = static_cast<uint32_t>((lane % CPR) ^ (lane / CPR)) * 16;
-  uint32_t lane_off = static_cast<uint32_t>(lane / CPR) * kbytes + w_chunk;
-  asm volatile("" : "+v"(lane_off));
+  constexpr int NPERM = F8 ? NI : 1;   // distinct permutations among a visit's loads
+  uint32_t w_chunk[NPERM], lane_off[NPERM];
+#pragma unroll
+  for (int j = 0; j < NPERM; ++j) {
+    w_chunk[j] = static_cast<uint32_t>((lane % CPR) ^ SH::wx(lane / CPR, j)) * 16;
+    lane_off[j] = static_cast<uint32_t>(lane / CPR) * kbytes + w_chunk[j];
+    asm volatile("" : "+v"(lane_off[j]));
+  }
   const uint32_t a_row = static_cast<uint32_t>(lane / 16);
-  const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ (lane / 16)) * 16;
+  const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ SH::ax(lane / 16)) * 16;
   const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
-  const int rs = r16 % SH::RPI;
+  const int rs = SH::wx(r16 % SH::RPI, r16 / SH::RPI);
   const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
-  const int rs_a = r16 % 4;
+  const int rs_a = SH::ax(r16 % 4);
   const uint32_t tile_bytes = 16 * kbytes;
   const uint32_t pass_bytes = static_cast<uint32_t>(ng * R) * tile_bytes;
   // the last K block may be partial: its row pieces end at tail_bytes
@@ -177,12 +189,13 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   // (pass base + K block + tile), kOOB for a visit past the last pass
   auto dma_w = [&](uint32_t sb, uint32_t kb, int slot) {
     char* dst = ring + slot * SH::SLOT;
-    const bool cut = kb == kb_last && w_chunk >= tail_bytes;   // past a partial block's end
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
+      const int jp = NPERM > 1 ? j : 0;
+      const bool cut = kb == kb_last && w_chunk[jp] >= tail_bytes;   // past a partial block's end
       const uint32_t s_off = __builtin_amdgcn_readfirstlane(
           sb == kOOB ? kOOB : sb + static_cast<uint32_t>(j * SH::RPI) * kbytes);
-      const uint32_t off = cut ? kOOB : lane_off + s_off;
+      const uint32_t off = cut ? kOOB : lane_off[jp] + s_off;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16, off, 0, 0, 2);
     }
