@@ -33,7 +33,7 @@
 namespace bdr {
 
 constexpr int kF8KB = 1024;             // codes (= bytes) of each W row per visit
-constexpr int kF8PadRow = kF8KB + 16;   // LDS row stride
+constexpr int kF8PadRow = kF8KB + 32;   // LDS row stride (bank-conflict-free reads, as kPadRow)
 constexpr int kF8Steps = kF8KB / 64;    // 64-element steps per visit
 
 // NT: 16-row tiles per workgroup (compile time; the last ones may be empty)
