@@ -24,7 +24,7 @@ __all__ = [
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
     "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
-    "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us", "MARKOV_TIMED_OUT",
+    "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us", "set_markov_forced_time_out", "MARKOV_TIMED_OUT",
 ]
 
 
@@ -305,6 +305,12 @@ def set_markov_poll_timeout_us(us: float) -> None:
     """Process-wide limit of the Markov chain's bounded waits for later launches
     (negative: the default)."""
     lib().bdr_set_markov_poll_timeout_us(float(us))
+
+
+def set_markov_forced_time_out(on: bool) -> None:
+    """Process-wide error-path hook for later launches: every bounded wait of
+    the chain disregards what it reads and gives up once its limit passes."""
+    lib().bdr_set_markov_forced_time_out(1 if on else 0)
 
 
 def set_row_split_override(ring: int = 0, workgroups: int = 0, ksplit: int = 0) -> None:

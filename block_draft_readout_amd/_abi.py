@@ -31,6 +31,7 @@ SIGNATURES = {
     "bdr_abi_version": (_int, []),
     "bdr_last_error": (C.c_char_p, []),
     "bdr_set_markov_poll_timeout_us": (None, [C.c_double]),
+    "bdr_set_markov_forced_time_out": (None, [C.c_int]),
     "bdr_set_row_split_override": (_int, [_int, _i64, _int]),
     "dflash_fuse_fc_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
     "dflash_fuse_fc": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),

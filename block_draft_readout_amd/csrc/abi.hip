@@ -191,9 +191,11 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
 
 extern "C" {
 
-int bdr_abi_version(void) { return 7; }
+int bdr_abi_version(void) { return 8; }
 
 void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
+
+void bdr_set_markov_forced_time_out(int on) { bdr::set_forced_time_out(on != 0); }
 
 int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit) {
   if (ring < 0 || workgroups < 0 || ksplit < 0 || workgroups > (int64_t(1) << 20) || ksplit > 256)

@@ -20,6 +20,7 @@ hipError_t launch_markov(const float* logits, int64_t B, int k, int64_t V, bdr_d
                          hipStream_t stream);
 // process-wide limit of the chain's bounded waits (negative / non-finite: default)
 void set_poll_timeout_us(double us);
+void set_forced_time_out(bool on);
 
 // ----------------------------------------------------------------------------
 // Greedy verification.

@@ -17,6 +17,12 @@ void set_poll_timeout_us(double us) {
   g_poll_timeout_us.store(std::isfinite(us) && us >= 0.0 ? us : kDefaultPollTimeoutUs);
 }
 
+// While set, every bounded wait disregards what it reads and gives up when its
+// limit passes, so the time-out path runs whatever the workgroups' timing.
+static std::atomic<unsigned> g_forced_time_out{0u};
+
+void set_forced_time_out(bool on) { g_forced_time_out.store(on ? 1u : 0u); }
+
 // wall-clock ticks of the current device for the poll limit (the device's
 // constant-rate counter; its rate in kHz is a device attribute)
 static unsigned long long poll_ticks() {
@@ -71,6 +77,7 @@ MarkovArgs markov_args(const float* logits, int64_t B, int k, int64_t V, const v
   g.err = reinterpret_cast<unsigned*>(ws + off);   // the last 256 bytes
   g.status = status;
   g.poll_ticks = poll_ticks();
+  g.forced_time_out = g_forced_time_out.load();
   g.draft = draft;
   g.vtiles = (V + 15) / 16;
   return g;

@@ -69,6 +69,7 @@ struct MarkovArgs {
   unsigned* err;                 // error word
   int32_t* status;               // optional: receives the error word at the end (then cleared)
   unsigned long long poll_ticks; // wall-clock ticks a poll waits before giving up
+  uint32_t forced_time_out;      // nonzero: every wait disregards what it reads (error-path tests)
   int32_t* draft;                // [B, k]
   int64_t vtiles;                // ceil(V / 16)
   // sampling (probabilistic drafting): the token of a position is the argmax
@@ -218,7 +219,7 @@ __device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
       ok = ok & cur;
       m = umax64(m, t[j]);
     }
-    if (__all(ok)) return wave_max64(m);
+    if (__all(ok) && !g.forced_time_out) return wave_max64(m);
     if (!keep_polling(g, t0, started)) {
       if (lane == 0) atomicOr(g.err, 1u);
       return 0ull;
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
           for (;;) {
             unsigned long long t = fetch_u64(toks + (b0 + (lane < n ? lane : n - 1)) * kTokenStride);
             const bool cur = (t & kTagMask) == tag;
-            if (__all(lane >= n || cur)) {
+            if (__all(lane >= n || cur) && !g.forced_time_out) {
               if (lane < n) ctx[b0 + lane] = tagged_token(t);
               break;
             }

@@ -77,6 +77,16 @@ const char* bdr_last_error(void);
  * the time-out path with every kernel still running to completion. */
 void bdr_set_markov_poll_timeout_us(double us);
 
+/* Error-path hook of the same waits, for launches enqueued after this call,
+ * process-wide: while on (nonzero) every bounded wait disregards what it reads
+ * and gives up once its limit passes, so the chain runs to completion with
+ * every draft token -1 and reports the time-out in its status word, however
+ * the workgroups' arrivals fall (with the 0 limit above a wait gives up at its
+ * second attempt; with the default one each wait takes the full limit).  A
+ * zero limit alone makes a wait give up only when its first look finds the
+ * hand-off incomplete, which workgroups running in step may never do. */
+void bdr_set_markov_forced_time_out(int on);
+
 /* Plan override of the row-split GEMM (the fc and the LM head with 16 < rows
  * <= 160), for calls planned after this one, process-wide; 0 leaves a value
  * to the planner.  ring: LDS ring slots per wave of the bf16 kernel (built:

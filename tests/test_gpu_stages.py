@@ -460,11 +460,12 @@ def test_graph_replay_matches_eager():
 
 @pytest.mark.parametrize("B", [1, 16])
 def test_chain_time_out_is_reported(B):
-    """The chain's bounded waits made to give up at once (a limit of 0 set from
-    the host): every kernel still runs to completion, the status word reports
-    the time-out and the binding raises; the error word does not outlive the
-    call that reported it, and with the default limit the same call reports 0
-    and drafts the oracle's tokens."""
+    """The chain's bounded waits made to give up (the host's error-path hook,
+    which has every wait disregard what it reads, with a limit of 0): every
+    kernel still runs to completion, every draft token is -1, the status word
+    reports the time-out and the binding raises; the error word does not
+    outlive the call that reported it, and with the hook off and the default
+    limit the same call reports 0 and drafts the oracle's tokens."""
     g = np.random.default_rng(700 + B)
     k, V, r = 8, 151936, 64
     Z = (g.standard_normal((B, k, V)) * 3).astype(np.float32)
@@ -477,15 +478,18 @@ def test_chain_time_out_is_reported(B):
                      device="cuda")
     status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     m.set_markov_poll_timeout_us(0.0)
+    m.set_markov_forced_time_out(True)
     try:
-        log(f"chain time-out B={B}: waits limited to 0 us")
-        m.dspark_markov_argmax(Zd, w1d, w2d, pd, workspace=ws, status=status, check=False)
+        log(f"chain time-out B={B}: waits forced to give up, limit 0 us")
+        d = m.dspark_markov_argmax(Zd, w1d, w2d, pd, workspace=ws, status=status, check=False)
         torch.cuda.synchronize()
         assert int(status.item()) != 0
+        assert bool((d == -1).all())
         with pytest.raises(m.BdrError) as e:
             m.dspark_markov_argmax(Zd, w1d, w2d, pd, workspace=ws)
         assert e.value.code == m.MARKOV_TIMED_OUT
     finally:
+        m.set_markov_forced_time_out(False)
         m.set_markov_poll_timeout_us(-1.0)
     torch.cuda.synchronize()
     d = m.dspark_markov_argmax(Zd, w1d, w2d, pd, workspace=ws, status=status, check=False)
