@@ -58,12 +58,14 @@ def kernel_source_hash(sources=GEMM_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str, fp8: bool = False, kernel: str = "lm_head_gemm"):
+def recorded_traffic(workload: str, weights: str = "native", kernel: str = "lm_head_gemm"):
     """HBM bytes per launch of the dominant kernel (the LM head, or the fc and
     the LM head in one launch: kernel="fc_lm_head_gemm") from the committed
-    rocprofv3 counter summary, or None when the summary is missing or the
-    kernel has changed since."""
-    name = f"{kernel}_fp8_{workload}_pmc.md" if fp8 else f"{kernel}_{workload}_pmc.md"
+    rocprofv3 counter summary of that weight format (native, packed, fp8), or
+    None when the summary is missing or the kernel has changed since."""
+    fp8 = weights == "fp8"
+    name = (f"{kernel}_{weights}_{workload}_pmc.md" if weights != "native"
+            else f"{kernel}_{workload}_pmc.md")
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -79,10 +81,11 @@ def recorded_traffic(workload: str, fp8: bool = False, kernel: str = "lm_head_ge
 class Step:
     """Pre-bound C-ABI calls of one pool slot (pointers resolved once)."""
 
-    def __init__(self, L, w, dt, g, slot, bufs, stream, sample=None, fp8=False):
+    def __init__(self, L, w, dt, g, slot, bufs, stream, sample=None, fp8=False, wdt=None):
         self.L, self.w, self.dt, self.g, self.s, self.b = L, w, dt, g, slot, bufs
         self.sample = sample      # None: greedy; else (temperature, seed)
         self.fp8 = fp8            # fc and LM head weights as E4M3 codes + row scales
+        self.wdt = dt if wdt is None else wdt   # dtype of the calls with fc / LM-head weights
         self.stream = stream
         self.fc_stream = stream   # the fc may run on a second stream (see --overlap)
         self.taps = (C.c_void_p * w.n_taps)(*[t.data_ptr() for t in slot["taps"]])
@@ -100,14 +103,14 @@ class Step:
                                              self.g["fc_q"].data_ptr(), self.g["fc_scale"].data_ptr(),
                                              b["F"].data_ptr(), b["ws_fc"], b["ws_fc_n"],
                                              self.fc_stream)
-        return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+        return self.L.dflash_fuse_fc(self.taps, w.n_taps, w.rows, w.hidden, self.wdt,
                                      self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
                                      b["ws_fc"], b["ws_fc_n"], self.fc_stream)
 
     def fc_lm(self):
         """S1 and S2 in one call (one launch on the batched workloads)."""
         w, b = self.w, self.b
-        return self.L.dflash_fuse_fc_lm_head(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+        return self.L.dflash_fuse_fc_lm_head(self.taps, w.n_taps, w.rows, w.hidden, self.wdt,
                                              self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
                                              self.s["draft_hidden"].data_ptr(), w.batch * w.k,
                                              w.vocab, self.g["lm_w"].data_ptr(),
@@ -122,7 +125,7 @@ class Step:
                                              self.g["lm_scale"].data_ptr(),
                                              self.b["logits"].data_ptr(), self.stream)
         return self.L.dspark_lm_head(self.s["draft_hidden"].data_ptr(), w.batch * w.k, w.hidden,
-                                     w.vocab, self.dt, self.g["lm_w"].data_ptr(),
+                                     w.vocab, self.wdt, self.g["lm_w"].data_ptr(),
                                      self.b["logits"].data_ptr(), self.stream)
 
     def markov(self):
@@ -143,7 +146,7 @@ class Step:
             rc = self.lm_head()
             return rc if rc != 0 else self.markov()
         return self.L.dspark_draft_block(self.s["draft_hidden"].data_ptr(), w.batch, w.k,
-                                         w.hidden, w.vocab, self.dt, self.g["lm_w"].data_ptr(),
+                                         w.hidden, w.vocab, self.wdt, self.g["lm_w"].data_ptr(),
                                          self.w1, self.w2, w.rank,
                                          self.s["prev0"].data_ptr(), b["d"].data_ptr(),
                                          b["logits"].data_ptr(), self.status, b["ws_m"],
@@ -183,7 +186,7 @@ class Step:
                 b["row_count"].data_ptr(), w.rows, self.g["fc_q"].data_ptr(),
                 self.g["fc_scale"].data_ptr(), b["F"].data_ptr(), b["ws_fcr"], b["ws_fcr_n"],
                 self.stream)
-        return self.L.dflash_fuse_fc_rows(self.taps, w.n_taps, w.rows, w.hidden, self.dt,
+        return self.L.dflash_fuse_fc_rows(self.taps, w.n_taps, w.rows, w.hidden, self.wdt,
                                           b["row_index"].data_ptr(), b["row_count"].data_ptr(),
                                           w.rows, self.g["fc_w"].data_ptr(), b["F"].data_ptr(),
                                           b["ws_fcr"], b["ws_fcr_n"], self.stream)
@@ -467,9 +470,12 @@ def main():
     ap.add_argument("--fc-rows", type=int, default=0,
                     help="time the drafter fc alone on this many rows (the prefill-shaped, "
                          "MFMA-bound fc) with the workload's H and taps, instead of block-steps")
-    ap.add_argument("--weights", choices=("native", "fp8"), default="native",
-                    help="native: fc and LM head weights in the workload's dtype; fp8: E4M3 "
-                         "codes with one fp32 scale per row (bf16 workloads)")
+    ap.add_argument("--weights", choices=("auto", "native", "packed", "fp8"), default="auto",
+                    help="native: fc and LM head weights in the workload's dtype, row-major; "
+                         "packed: bf16 fc and LM head weights in the packed layout "
+                         "(bdr_pack_weight, done once before timing); fp8: E4M3 codes with "
+                         "one fp32 scale per row (bf16 workloads); auto: packed for bf16 "
+                         "workloads whose LM head has more than 16 rows, else native")
     ap.add_argument("--hc", type=int, default=1,
                     help="with --fc-rows: average each tap over this many hyper-connection "
                          "streams (dflash_hc_average) before the fc; both are timed")
@@ -487,8 +493,9 @@ def main():
         print(json.dumps({"error": "--closed-loop runs eagerly (no --graph)"}))
         sys.exit(2)
     fp8 = args.weights == "fp8"
-    if fp8 and args.fc_rows > 0:
-        print(json.dumps({"error": "--weights fp8 times block-steps (not --fc-rows)"}))
+    packed = args.weights == "packed"
+    if (fp8 or packed) and args.fc_rows > 0:
+        print(json.dumps({"error": f"--weights {args.weights} times block-steps (not --fc-rows)"}))
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -500,6 +507,12 @@ def main():
     from workloads import synth
 
     w = workloads.get(args.workload)
+    if args.weights == "auto":
+        # the packed layout serves the batched (row-split) GEMMs; up to 16 rows the
+        # row-major layout's one-sequence kernel is the faster one
+        args.weights = ("packed" if w.dtype == "bf16" and w.batch * w.k > 16 and args.fc_rows == 0
+                        else "native")
+        packed = args.weights == "packed"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = bdr.lib()
@@ -515,9 +528,10 @@ def main():
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
-    if fp8 and w.dtype != "bf16":
-        print(json.dumps({"error": "--weights fp8 needs a bf16 workload"}))
+    if (fp8 or packed) and w.dtype != "bf16":
+        print(json.dumps({"error": f"--weights {args.weights} needs a bf16 workload"}))
         sys.exit(2)
+    wdt = bdr.BDR_BF16_PACKED if packed else dt
     if args.overlap == "auto" and (fp8 or args.closed_loop or args.graph):
         # the fused call takes bf16 weights; a closed loop runs in order; graphs are
         # captured before any timing
@@ -527,6 +541,9 @@ def main():
     t0 = time.time()
     W = synth.make_weights_fp8(w) if fp8 else synth.make_weights(w)
     g = {k: up(v) for k, v in W.items()}
+    if packed:      # the load-time copy; the row-major weights are not kept
+        g["fc_w"], g["lm_w"] = bdr.pack_weight(g["fc_w"]), bdr.pack_weight(g["lm_w"])
+        torch.cuda.synchronize()
     log(f"{w.describe()}: weights ready in {time.time() - t0:.1f}s")
 
     stream = torch.cuda.current_stream(dev)
@@ -560,15 +577,15 @@ def main():
                           ("row_offsets", (B + 1,))):
             bufs[name] = torch.zeros(shp, dtype=torch.int32, device=dev)
     for key, n in (("ws_fc", L.dflash_fuse_fc_fp8_workspace_bytes(w.rows, H, w.n_taps) if fp8
-                     else L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, dt)),
+                     else L.dflash_fuse_fc_workspace_bytes(w.rows, H, w.n_taps, wdt)),
                    ("ws_m", L.dspark_markov_workspace_bytes(B, k)),
                    ("ws_fcl", 0 if fp8 else L.dflash_fuse_fc_lm_head_workspace_bytes(
-                       w.rows, H, w.n_taps, B * k, V, dt)),
+                       w.rows, H, w.n_taps, B * k, V, wdt)),
                    ("ws_v", L.spec_verify_workspace_bytes(B, k, V)),
                    ("ws_ms", L.dspark_markov_sample_workspace_bytes(B, k, V) if sampling else 0),
                    ("ws_vs", L.spec_verify_sample_workspace_bytes(B, k, V) if sampling else 0),
                    ("ws_fcr", (L.dflash_fuse_fc_rows_fp8_workspace_bytes(w.rows, H, w.n_taps) if fp8
-                               else L.dflash_fuse_fc_rows_workspace_bytes(w.rows, H, w.n_taps, dt))
+                               else L.dflash_fuse_fc_rows_workspace_bytes(w.rows, H, w.n_taps, wdt))
                     if args.closed_loop else 0)):
         p, n2, t = ws(n)
         bufs[key], bufs[key + "_n"] = p, n2
@@ -588,7 +605,8 @@ def main():
         conf = synth.make_confidence(w, p)
         slot["conf"] = None if conf is None else up(conf)
         st = Step(L, w, dt, g, slot, bufs, sptr,
-                  sample=(args.temperature, 0x5EED0000 + p) if sampling else None, fp8=fp8)
+                  sample=(args.temperature, 0x5EED0000 + p) if sampling else None, fp8=fp8,
+                  wdt=wdt)
         check(st.draft_block(), "dspark_draft_block")
         if sampling:   # plant the targets on this step's sampled draft
             check(st.markov(), "dspark_markov_sample")
@@ -825,7 +843,7 @@ def main():
     step_bytes = fc_bytes + lm_bytes + markov_bytes + verify_b
     dom_bytes = fc_bytes + lm_bytes if fused else lm_bytes
     achieved = dom_bytes / (lm_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(w.name, fp8, "fc_lm_head_gemm" if fused else "lm_head_gemm")
+    traffic = recorded_traffic(w.name, args.weights, "fc_lm_head_gemm" if fused else "lm_head_gemm")
     log(f"step {ms_step * 1e3:.1f} us ({step_bytes / 1e6:.1f} MB algorithmic = "
         f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s); "
         f"{'fc + LM head' if fused else 'LM head'} {lm_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
@@ -872,7 +890,8 @@ def main():
                    "loop": "closed" if args.closed_loop else "independent steps",
                    "draft": args.draft,
                    "weights": "fp8-e4m3 codes + fp32 row scales (fc, LM head)" if fp8
-                   else w.dtype,
+                   else ("bf16, fc and LM head in the packed layout (bdr_pack_weight)" if packed
+                         else w.dtype),
                    **({"temperature": args.temperature} if sampling else {}),
                    "pool_steps": args.pool,
                    "markov_weights": "one copy" if args.shared_markov else "one copy per slot"},
@@ -882,7 +901,8 @@ def main():
                      "kernel": "LM-head weight-streaming GEMM (dspark_lm_head_fp8)" if fp8
                      else ("fc + LM-head weight-streaming GEMMs in one launch "
                            "(dflash_fuse_fc_lm_head)" if fused
-                           else "LM-head weight-streaming GEMM (dspark_lm_head)"),
+                           else "LM-head weight-streaming GEMM (dspark_lm_head)")
+                     + (", packed weights" if packed else ""),
                      "avg_launch_us": lm_ms * 1e3,
                      "algorithmic_bytes_per_launch": dom_bytes},
         "stages": stages,

@@ -16,14 +16,14 @@ from typing import Dict, Optional, Sequence
 import torch
 
 from . import _abi
-from ._abi import BdrError, BDR_BF16, BDR_F32  # noqa: F401
+from ._abi import BdrError, BDR_BF16, BDR_BF16_PACKED, BDR_F32  # noqa: F401
 
 __all__ = [
     "dflash_fuse_fc", "dspark_lm_head", "dspark_markov_argmax", "dspark_draft_block",
     "dspark_draft_block_noalloc", "dflash_fuse_fc_lm_head",
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
-    "dflash_hc_average", "dflash_fuse_fc_rows_fp8",
+    "dflash_hc_average", "dflash_fuse_fc_rows_fp8", "PackedWeight", "pack_weight",
     "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us", "set_markov_forced_time_out", "MARKOV_TIMED_OUT",
 ]
 
@@ -33,7 +33,50 @@ def lib():
     return _abi.load()
 
 
-def _dt(t: torch.Tensor) -> int:
+class PackedWeight:
+    """A bf16 weight [rows, cols] in the packed layout of bdr_pack_weight (the
+    bytes in ``data``).  dflash_fuse_fc, dflash_fuse_fc_rows, dspark_lm_head,
+    dflash_fuse_fc_lm_head, dspark_draft_block and dspark_draft_block_noalloc
+    take it in place of the bf16 tensor; their results are those of the
+    row-major weight."""
+
+    dtype = torch.bfloat16
+    is_cuda = True
+
+    def __init__(self, data: torch.Tensor, rows: int, cols: int):
+        self.data = data
+        self.shape = torch.Size((rows, cols))
+        self.device = data.device
+
+    def is_contiguous(self) -> bool:
+        return True
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def pack_weight(w: torch.Tensor) -> PackedWeight:
+    """The packed copy of a bf16 weight [rows, cols] (cols % 8 == 0), written on
+    w's device and current stream."""
+    L = lib()
+    _dev(w, "w")
+    if w.dtype != torch.bfloat16 or w.dim() != 2:
+        raise ValueError("pack_weight takes a bf16 [rows, cols] tensor")
+    rows, cols = w.shape
+    n = L.bdr_packed_weight_bytes(rows, cols)
+    if n == 0:
+        raise BdrError("bdr_pack_weight", _abi.BDR_EUNSUPPORTED,
+                       f"weight [{rows}, {cols}] cannot be packed (cols % 8 == 0 and a packed "
+                       "copy under 2^31 bytes are required)")
+    data = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _abi.check("bdr_pack_weight", L.bdr_pack_weight(_ptr(w), rows, cols, _ptr(data),
+                                                    _stream(w.device)))
+    return PackedWeight(data, rows, cols)
+
+
+def _dt(t) -> int:
+    if isinstance(t, PackedWeight):
+        return BDR_BF16_PACKED
     if t.dtype == torch.bfloat16:
         return BDR_BF16
     if t.dtype == torch.float32:
@@ -258,6 +301,8 @@ def dflash_fuse_fc_lm_head(taps: Sequence[torch.Tensor], fc_w: torch.Tensor,
         raise ValueError("lm_head_w must be [V, H] and lm_hidden [..., H]")
     if lm_hidden.dtype != fc_w.dtype or lm_head_w.dtype != fc_w.dtype:
         raise ValueError("all weights and activations must share one dtype")
+    if isinstance(fc_w, PackedWeight) != isinstance(lm_head_w, PackedWeight):
+        raise ValueError("fc_w and lm_head_w must both be packed or both be tensors")
     dt = _dt(fc_w)
     lm_rows = lm_hidden.numel() // H
     dev = fc_w.device

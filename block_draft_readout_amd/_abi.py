@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(PKG, "libbdr.so")
 
 BDR_F32 = 0
 BDR_BF16 = 1
+BDR_BF16_PACKED = 2
 
 BDR_OK = 0
 BDR_EINVAL = -1
@@ -33,6 +34,8 @@ SIGNATURES = {
     "bdr_set_markov_poll_timeout_us": (None, [C.c_double]),
     "bdr_set_markov_forced_time_out": (None, [C.c_int]),
     "bdr_set_row_split_override": (_int, [_int, _i64, _int]),
+    "bdr_packed_weight_bytes": (_sz, [_i64, _i64]),
+    "bdr_pack_weight": (_int, [_vp, _i64, _i64, _vp, _vp]),
     "dflash_fuse_fc_workspace_bytes": (_sz, [_i64, _i64, _int, _int]),
     "dflash_fuse_fc": (_int, [C.POINTER(_vp), _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
     "dspark_lm_head": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),

@@ -34,6 +34,8 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 bool valid_dtype(int dt) { return dt == BDR_F32 || dt == BDR_BF16; }
+// calls with a GEMM weight also take the packed bf16 layout
+bool valid_gemm_dtype(int dt) { return valid_dtype(dt) || dt == BDR_BF16_PACKED; }
 
 constexpr int64_t kMaxVocab = 0x7FFFFFFELL;
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor; keeps index math in range
@@ -88,8 +90,9 @@ int need_ws(const void* ws, size_t have, size_t need) {
     if (rc_ != BDR_OK) return rc_; \
   } while (0)
 
-int fc_shape(int64_t rows, int64_t hidden, int n_taps, int dt) {
-  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+int fc_shape(int64_t rows, int64_t hidden, int n_taps, int wdt) {
+  if (!valid_gemm_dtype(wdt)) return fail(BDR_EINVAL, "unknown dtype %d", wdt);
+  const int dt = act_dtype(static_cast<bdr_dtype>(wdt));
   if (n_taps < 1) return fail(BDR_EINVAL, "n_taps must be >= 1, got %d", n_taps);
   if (n_taps > BDR_MAX_TAPS) return fail(BDR_EUNSUPPORTED, "n_taps %d > %d", n_taps, BDR_MAX_TAPS);
   if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
@@ -102,11 +105,18 @@ int fc_shape(int64_t rows, int64_t hidden, int n_taps, int dt) {
   const int64_t es = dt == BDR_BF16 ? 2 : 4;
   if (rows > kMaxBytes / (hidden * es) || hidden * n_taps > kMaxBytes / (64 * es))
     return fail(BDR_EUNSUPPORTED, "fc problem too large (per-operand byte limit 2^31)");
+  if (wdt == BDR_BF16_PACKED) {
+    if (n_taps > 1 && hidden % 128)
+      return fail(BDR_EUNSUPPORTED, "a multi-tap fc with packed weights needs hidden %% 128 == 0");
+    if (packed_weight_bytes(hidden, hidden * n_taps) == 0)
+      return fail(BDR_EUNSUPPORTED, "packed fc_w would reach 2^31 bytes");
+  }
   return BDR_OK;
 }
 
-int lm_shape(int64_t rows, int64_t hidden, int64_t vocab, int dt) {
-  if (!valid_dtype(dt)) return fail(BDR_EINVAL, "unknown dtype %d", dt);
+int lm_shape(int64_t rows, int64_t hidden, int64_t vocab, int wdt) {
+  if (!valid_gemm_dtype(wdt)) return fail(BDR_EINVAL, "unknown dtype %d", wdt);
+  const int dt = act_dtype(static_cast<bdr_dtype>(wdt));
   if (rows < 0) return fail(BDR_EINVAL, "rows must be >= 0");
   if (hidden <= 0) return fail(BDR_EINVAL, "hidden must be > 0");
   if (vocab <= 0) return fail(BDR_EINVAL, "vocab must be > 0");
@@ -119,6 +129,13 @@ int lm_shape(int64_t rows, int64_t hidden, int64_t vocab, int dt) {
   if (rows > kMaxBytes / (hidden * es) || hidden > kMaxBytes / (64 * es) ||
       vocab > kMaxElems / hidden || rows > kMaxElems / vocab)
     return fail(BDR_EUNSUPPORTED, "LM-head problem too large (per-operand byte limit 2^31)");
+  if (wdt == BDR_BF16_PACKED) {
+    if (packed_weight_bytes(vocab, hidden) == 0)
+      return fail(BDR_EUNSUPPORTED, "packed lm_head_w would reach 2^31 bytes");
+    // a slab's logits are addressed with 32-bit offsets
+    if (std::min<int64_t>(rows, kPackedSlabRows) * vocab * 4 >= (int64_t(1) << 32))
+      return fail(BDR_EUNSUPPORTED, "LM head with packed weights: vocab too large");
+  }
   return BDR_OK;
 }
 
@@ -191,7 +208,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
 
 extern "C" {
 
-int bdr_abi_version(void) { return 8; }
+int bdr_abi_version(void) { return 9; }
 
 void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
 
@@ -206,6 +223,28 @@ int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit) {
 }
 
 const char* bdr_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------- packed weights
+size_t bdr_packed_weight_bytes(int64_t rows, int64_t cols) {
+  return packed_weight_bytes(rows, cols);
+}
+
+int bdr_pack_weight(const void* w, int64_t rows, int64_t cols, void* packed, void* stream) {
+  const size_t bytes = packed_weight_bytes(rows, cols);
+  if (bytes == 0)
+    return fail(BDR_EUNSUPPORTED, "weight [%lld, %lld] cannot be packed (cols %% 8 == 0 and a "
+                "packed copy under 2^31 bytes are required)", static_cast<long long>(rows),
+                static_cast<long long>(cols));
+  BDR_TRY(need_ptr(w, "w"));
+  BDR_TRY(need_ptr(packed, "packed"));
+  const uintptr_t w0 = reinterpret_cast<uintptr_t>(w), p0 = reinterpret_cast<uintptr_t>(packed);
+  const uintptr_t wbytes = static_cast<uintptr_t>(rows) * static_cast<uintptr_t>(cols) * 2;
+  if (w0 < p0 + bytes && p0 < w0 + wbytes) return fail(BDR_EINVAL, "packed overlaps w");
+  BDR_TRY(check_device());
+  const hipError_t e = launch_pack_weight(w, rows, cols, packed, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "bdr_pack_weight launch");
+  return BDR_OK;
+}
 
 // ---------------------------------------------------------------------------- S1
 size_t dflash_fuse_fc_workspace_bytes(int64_t rows, int64_t hidden, int n_taps, bdr_dtype dt) {
@@ -229,7 +268,8 @@ int dflash_fuse_fc(const void* const* taps, int n_taps, int64_t rows, int64_t hi
   BDR_TRY(need_ws(workspace, workspace_bytes, p.workspace));
   BDR_TRY(check_device());
   hipError_t e = launch_gemm(p, dt, taps, n_taps, hidden, rows, hidden, fc_w, out,
-                             dt == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace, as_stream(stream));
+                             act_dtype(dt) == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace,
+                             as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc launch");
   return BDR_OK;
 }
@@ -239,7 +279,7 @@ namespace {
 // the pair plan when both GEMMs take it (bf16, row-split shapes), else !ok
 PairPlan fc_lm_pair(int64_t rows, int64_t hidden, int n_taps, int64_t lm_rows, int64_t vocab,
                     bdr_dtype dt) {
-  if (dt != BDR_BF16 || rows == 0 || lm_rows == 0) return PairPlan{};
+  if (act_dtype(dt) != BDR_BF16 || rows == 0 || lm_rows == 0) return PairPlan{};
   return plan_gemm_pair(lm_rows, vocab, hidden, rows, hidden, hidden * n_taps, n_taps);
 }
 }  // namespace
@@ -284,13 +324,13 @@ int dflash_fuse_fc_lm_head(const void* const* taps, int n_taps, int64_t rows, in
   hipError_t e;
   if (pp.ok) {
     e = launch_gemm_pair(pp, lm_hidden, lm_head_w, logits, taps, n_taps, hidden, fc_w, fc_out,
-                         workspace, st);
+                         workspace, dt == BDR_BF16_PACKED, st);
     if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_lm_head launch");
     return BDR_OK;
   }
   if (rows > 0) {
     e = launch_gemm(pf, dt, taps, n_taps, hidden, rows, hidden, fc_w, fc_out,
-                    dt == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace, st);
+                    act_dtype(dt) == BDR_BF16 ? OUT_BF16 : OUT_F32, workspace, st);
     if (e != hipSuccess) return hip_fail(e, "dflash_fuse_fc_lm_head fc launch");
   }
   if (lm_rows > 0) {
@@ -462,7 +502,7 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
                        void* workspace, size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
-  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank, vocab, k));
+  BDR_TRY(markov_shape(act_dtype(dt), markov_w1, markov_w2, rank, vocab, k));
   if (batch == 0) return BDR_OK;
   BDR_TRY(need_ptr(draft_hidden, "draft_hidden"));
   BDR_TRY(need_ptr(lm_head_w, "lm_head_w"));
@@ -485,8 +525,8 @@ int dspark_draft_block(const void* draft_hidden, int64_t batch, int k, int64_t h
   hipError_t e = launch_gemm(p, dt, a, 1, hidden, batch * k, vocab, lm_head_w, logits, OUT_F32,
                              nullptr, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block LM-head launch");
-  e = launch_markov(logits, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
-                    draft_tokens, status, ws, cus, as_stream(stream));
+  e = launch_markov(logits, batch, k, vocab, act_dtype(dt), markov_w1, markov_w2, rank,
+                    prev_token, draft_tokens, status, ws, cus, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block Markov launch");
   return BDR_OK;
 }
@@ -499,7 +539,7 @@ int dspark_draft_block_noalloc(const void* draft_hidden, int64_t batch, int k, i
                                float* logits_out, int32_t* status, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(lm_shape(batch * k, hidden, vocab, dt));
-  BDR_TRY(markov_shape(dt, markov_w1, markov_w2, rank, vocab, k));
+  BDR_TRY(markov_shape(act_dtype(dt), markov_w1, markov_w2, rank, vocab, k));
   const size_t need = markov_workspace(batch, k);
   if (need > BDR_NOALLOC_SCRATCH_BYTES)
     return fail(BDR_EUNSUPPORTED,
@@ -529,8 +569,8 @@ int dspark_draft_block_noalloc(const void* draft_hidden, int64_t batch, int k, i
   e = launch_gemm(p, dt, a, 1, hidden, batch * k, vocab, lm_head_w, logits_out, OUT_F32, nullptr,
                   st);
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block_noalloc LM-head launch");
-  e = launch_markov(logits_out, batch, k, vocab, dt, markov_w1, markov_w2, rank, prev_token,
-                    draft_tokens, status, ws, cus, st);
+  e = launch_markov(logits_out, batch, k, vocab, act_dtype(dt), markov_w1, markov_w2, rank,
+                    prev_token, draft_tokens, status, ws, cus, st);
   if (e != hipSuccess) return hip_fail(e, "dspark_draft_block_noalloc Markov launch");
   return BDR_OK;
 }

@@ -414,11 +414,16 @@ static bool ns_overridden() {
   return g_ns_ring.load() != 0 || g_ns_wg.load() != 0 || g_ns_ks.load() != 0;
 }
 
+// packed: bf16 weights in the packed layout, any M in 1..160 (at least two A
+// row tiles; rows past M read as zero)
 static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
-                    GemmPlan* p) {
+                    GemmPlan* p, bool packed = false) {
   constexpr int KE = 128;
-  const int64_t mtiles = (M + 15) / 16;
-  if (esize > 2 || M <= 16 || mtiles > 10 || K % (esize == 1 ? 16 : 8) != 0) return false;
+  const int64_t mtiles = packed ? std::max<int64_t>(2, (M + 15) / 16) : (M + 15) / 16;
+  if (esize > 2 || (M <= 16 && !packed) || M < 1 || mtiles > 10 ||
+      K % (esize == 1 ? 16 : 8) != 0)
+    return false;
+  if (packed && (esize != 2 || packed_weight_bytes(N, K) == 0)) return false;
   if (n_seg > 1 && (K / n_seg) % KE != 0) return false;
   const int64_t kblocks = (K + KE - 1) / KE;
   double best = 1e300;
@@ -448,9 +453,10 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   // the output (or one K split's partials) is addressed with 32-bit offsets
   if (M * N * 4 >= (int64_t(1) << 32)) return false;
   // a wave's rows x row bytes are addressed with 32-bit offsets (with room for
-  // the empty slots of its last pass)
+  // the empty slots of its last pass); packed weights: the whole copy is under
+  // 2^31 bytes
   const int64_t rows_w = ((N + p->n_waves - 1) / p->n_waves + 3) / 4;
-  if ((rows_w + 256) * K * esize >= (int64_t(1) << 31)) return false;
+  if (!packed && (rows_w + 256) * K * esize >= (int64_t(1) << 31)) return false;
   p->stream = true;
   p->ns = true;
   p->mt = static_cast<int>(mtiles);
@@ -603,6 +609,16 @@ static bool plan_tile(int64_t M, int64_t N, int64_t K, int esize, bool allow_spl
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bdr_dtype dt, bool allow_split, int n_seg) {
   GemmPlan p;
+  if (dt == BDR_BF16_PACKED) {
+    // the row-split kernel over slabs of at most kPackedSlabRows rows, each
+    // planned as the largest (the last may be shorter); p.ns stays false when
+    // the shape does not fit it
+    const int64_t slab = std::min<int64_t>(M, kPackedSlabRows);
+    plan_ns(slab, N, K, 2, allow_split, n_seg, &p, true);
+    p.packed = true;
+    p.slab = M > slab ? slab : 0;
+    return p;
+  }
   const int ks = dt == BDR_BF16 ? Elem<uint16_t>::KSTEP : Elem<float>::KSTEP;
   const int esize = dt == BDR_BF16 ? 2 : 4;
   if (plan_stream(M, N, K, esize, allow_split, n_seg, &p)) return p;
@@ -721,6 +737,26 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
   const bool split = p.ksplit > 1;
   g.partial = split ? 1 : 0;
   g.out = split ? workspace : out;
+  if (p.packed) {
+    // slab by slab (sharing the workspace, in stream order)
+    if (!p.ns) return hipErrorInvalidValue;
+    g.w_packed = 1;
+    const int64_t slab = p.slab > 0 ? p.slab : M;
+    const int64_t out_es = out_kind == OUT_BF16 ? 2 : 4;
+    for (int64_t m0 = 0; m0 < M; m0 += slab) {
+      GemmArgs gs = g;
+      gs.M = std::min<int64_t>(slab, M - m0);
+      for (int t = 0; t < n_seg; ++t) gs.a[t] = static_cast<const char*>(a[t]) + m0 * seg * 2;
+      void* o = static_cast<char*>(out) + m0 * N * out_es;
+      gs.out = split ? workspace : o;
+      const StreamArgs sa{gs, p.n_waves, p.kblocks, p.kb_per_split};
+      hipError_t e = launch_ns_bf16(p, sa, stream);
+      if (e == hipSuccess) e = hipGetLastError();
+      if (e == hipSuccess && split) e = launch_splitk_reduce(p, gs.M, N, o, out_kind, workspace, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (p.tile) {
     const hipError_t le = launch_gemm_tile(p, g, stream);
     if (le != hipSuccess) return le;
@@ -745,7 +781,7 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
 
 hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, float* out0,
                             const void* const* a1, int n_seg1, int64_t seg1, const void* w1,
-                            void* out1, void* workspace, hipStream_t stream) {
+                            void* out1, void* workspace, bool packed, hipStream_t stream) {
   if (!pp.ok) return hipErrorInvalidValue;
   GemmArgs g0{};
   g0.a[0] = a0;
@@ -757,6 +793,7 @@ hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, 
   g0.out = out0;
   g0.out_kind = OUT_F32;
   g0.partial = 0;
+  g0.w_packed = packed ? 1 : 0;
   GemmArgs g1{};
   for (int t = 0; t < n_seg1; ++t) g1.a[t] = a1[t];
   g1.seg = seg1;
@@ -764,6 +801,7 @@ hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, 
   g1.N = pp.N1;
   g1.K = pp.K1;
   g1.w = w1;
+  g1.w_packed = packed ? 1 : 0;
   g1.out_kind = OUT_BF16;
   const bool split = pp.p1.ksplit > 1;
   g1.partial = split ? 1 : 0;

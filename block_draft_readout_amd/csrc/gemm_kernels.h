@@ -22,6 +22,7 @@ struct GemmArgs {
   int partial;                  // 1: write fp32 partials [split, M, N]
   int64_t steps_per_split;      // K steps handled by one workgroup along K
   const float* w_scale;         // fp8 weights: one scale per W row [N]; else unused
+  int w_packed;                 // 1: W in the packed layout (row-split kernel only)
 };
 
 // Segment base pointer chosen with scalar selects (t is uniform), so the

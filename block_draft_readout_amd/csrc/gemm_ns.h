@@ -145,9 +145,21 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
   const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
+  // W layout.  Rows: [N, K].  Packed: the visits themselves, K block by K block
+  // and tile by tile ([kblocks][ceil(N / 16)][16][WROW], zero-padded), so a
+  // visit is one contiguous 16 * WROW bytes and the visits of one K block are
+  // adjacent.  A visit's bytes sit at block * kb_str + tile * tile_bytes, its
+  // rows row_str apart.
+  const bool packed = g.w_packed != 0;
+  const uint32_t row_str = packed ? static_cast<uint32_t>(SH::WROW) : kbytes;
+  const uint32_t kb_str = packed ? static_cast<uint32_t>(n_t * 16 * SH::WROW)
+                                 : static_cast<uint32_t>(SH::WROW);
   const uint32_t wrows = static_cast<uint32_t>(n_hi > n_lo ? n_hi - n_lo : 0);
-  const rsrc_t rw = make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
-                              wrows * kbytes);
+  const rsrc_t rw =
+      packed ? make_rsrc(static_cast<const char*>(g.w) + static_cast<int64_t>(n_lo) * SH::WROW,
+                         static_cast<uint32_t>((sa.kblocks * n_t * 16 - n_lo) * SH::WROW))
+             : make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
+                         wrows * kbytes);
   char* const ring = lds + wave * (R * SH::SLOT);
   char* const stage = lds + kNsWaves * R * SH::SLOT;             // [2][MT][ASLOT]
   // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
@@ -161,7 +173,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
 #pragma unroll
   for (int j = 0; j < NPERM; ++j) {
     w_chunk[j] = static_cast<uint32_t>((lane % CPR) ^ SH::wx(lane / CPR, j)) * 16;
-    lane_off[j] = static_cast<uint32_t>(lane / CPR) * kbytes + w_chunk[j];
+    lane_off[j] = static_cast<uint32_t>(lane / CPR) * row_str + w_chunk[j];
     asm volatile("" : "+v"(lane_off[j]));
   }
   const uint32_t a_row = static_cast<uint32_t>(lane / 16);
@@ -170,7 +182,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const int rs = SH::wx(r16 % SH::RPI, r16 / SH::RPI);
   const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
   const int rs_a = SH::ax(r16 % 4);
-  const uint32_t tile_bytes = 16 * kbytes;
+  const uint32_t tile_bytes = 16 * row_str;
   const uint32_t pass_bytes = static_cast<uint32_t>(ng * R) * tile_bytes;
   // the last K block may be partial: its row pieces end at tail_bytes
   const uint32_t tail_bytes = kbytes - (static_cast<uint32_t>(sa.kblocks) - 1) * SH::WROW;
@@ -186,15 +198,19 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   u32x4_t a[MT][4];
 
   // visit -> ring slot: sb = the visit's byte offset within this wave's rows
-  // (pass base + K block + tile), kOOB for a visit past the last pass
-  auto dma_w = [&](uint32_t sb, uint32_t kb, int slot) {
+  // (pass base + K block + tile), kOOB for a visit past the last pass; ti = its
+  // tile within the wave's range, a tile past the range (an empty slot) reads
+  // nothing (in the packed layout the descriptor reaches past the range)
+  const int wtiles = __builtin_amdgcn_readfirstlane((n_hi - n_lo + 15) / 16);
+  auto dma_w = [&](uint32_t sb, int ti, uint32_t kb, int slot) {
     char* dst = ring + slot * SH::SLOT;
+    const bool none = sb == kOOB || ti >= wtiles;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int jp = NPERM > 1 ? j : 0;
       const bool cut = kb == kb_last && w_chunk[jp] >= tail_bytes;   // past a partial block's end
       const uint32_t s_off = __builtin_amdgcn_readfirstlane(
-          sb == kOOB ? kOOB : sb + static_cast<uint32_t>(j * SH::RPI) * kbytes);
+          none ? kOOB : sb + static_cast<uint32_t>(j * SH::RPI) * row_str);
       const uint32_t off = cut ? kOOB : lane_off[jp] + s_off;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16, off, 0, 0, 2);
@@ -272,11 +288,13 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
 
   // prologue: A of the first block, then tiles 0 .. R - 2 of pass 0 (ng >= 1)
   dma_a(kb_lo, 0, true);
-  static_for<R - 1>([&](auto t) { dma_w(kb_lo * SH::WROW + t * tile_bytes, kb_lo, t); });
+  static_for<R - 1>([&](auto t) { dma_w(kb_lo * kb_str + t * tile_bytes, t, kb_lo, t); });
   int blk = 0;
   const int nblk = npass * static_cast<int>(kb_hi - kb_lo);
+  const int pass_tiles = ng * R;
   uint32_t base = 0;
-  for (int p = 0; p < npass; ++p, base += pass_bytes) {
+  int pt = 0;   // first tile of the pass
+  for (int p = 0; p < npass; ++p, base += pass_bytes, pt += pass_tiles) {
     for (uint32_t kb = kb_lo; kb < kb_hi; ++kb, ++blk) {
       if (blk == 0)
         ns_wait_vm<NI * (R - 1)>();
@@ -289,9 +307,10 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
       const bool last_blk = kb + 1 == kb_hi;
       const uint32_t nkb = last_blk ? kb_lo : kb + 1;
       const uint32_t nbase = last_blk ? (p + 1 < npass ? base + pass_bytes : kOOB) : base;
+      const int npt = last_blk ? pt + pass_tiles : pt;
       dma_a(nkb, (blk + 1) & 1, blk + 1 < nblk);
-      const uint32_t here = base + kb * SH::WROW;
-      const uint32_t next = nbase == kOOB ? kOOB : nbase + nkb * SH::WROW;
+      const uint32_t here = base + kb * kb_str;
+      const uint32_t next = nbase == kOOB ? kOOB : nbase + nkb * kb_str;
       static_for<NG>([&](auto gc) {
         constexpr int G = decltype(gc)::value;
         if (G < ng) {
@@ -307,11 +326,12 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
             // step's MFMAs, and so its LDS reads, have all been issued.
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (J == 0) {
-              dma_w(here + (T + R - 1) * tile_bytes, kb, R - 1);
+              dma_w(here + (T + R - 1) * tile_bytes, pt + T + R - 1, kb, R - 1);
             } else {
               const uint32_t in_blk = here + ((G + 1) * R + J - 1) * tile_bytes;
               const uint32_t nx_blk = next == kOOB ? kOOB : next + (J - 1) * tile_bytes;
-              dma_w(last_g ? nx_blk : in_blk, last_g ? nkb : kb, J - 1);
+              dma_w(last_g ? nx_blk : in_blk, last_g ? npt + J - 1 : pt + (G + 1) * R + J - 1,
+                    last_g ? nkb : kb, J - 1);
             }
             ns_wait_vm<NI * (R - 1) + (T < R - 1 ? NA : 0)>();
             if constexpr (T == 0)

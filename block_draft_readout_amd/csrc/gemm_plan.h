@@ -35,7 +35,23 @@ struct GemmPlan {
   bool tile = false;
   int tile_shape = 0;     // 0: 256 x 160 tiles, 3 LDS stages; 1: 256 x 320, 2 stages
   int tiles_m = 0, tiles_n = 0;
+  // packed bf16 weights: always the row-split kernel (mt >= 2), over slabs of
+  // `slab` rows when M is larger (0: one slab)
+  bool packed = false;
+  int64_t slab = 0;
 };
+
+// Storage of activations and outputs under a weight dtype: the packed layout
+// holds bf16 weights and takes bf16 activations.
+inline bdr_dtype act_dtype(bdr_dtype dt) { return dt == BDR_BF16_PACKED ? BDR_BF16 : dt; }
+
+// Rows per slab of a GEMM with packed weights (the row-split kernel's maximum).
+constexpr int64_t kPackedSlabRows = 160;
+
+// Bytes of the packed copy of a bf16 [rows, cols] weight (0: not packable).
+size_t packed_weight_bytes(int64_t rows, int64_t cols);
+hipError_t launch_pack_weight(const void* w, int64_t rows, int64_t cols, void* packed,
+                              hipStream_t stream);
 
 // Compute units of a gfx950 part (MI350X / MI355X); fixed so that workspace
 // queries and launches always plan identically.
@@ -81,7 +97,7 @@ PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t 
                         int n_seg1);
 hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, float* out0,
                             const void* const* a1, int n_seg1, int64_t seg1, const void* w1,
-                            void* out1, void* workspace, hipStream_t stream);
+                            void* out1, void* workspace, bool packed, hipStream_t stream);
 
 // hyper-connection stream average of each tap: dst[t][r, h] = mean_s src[t][s*ss + r*rs + h]
 hipError_t launch_hc_average(const void* const* src, void* const* dst, int n_taps, int hc,

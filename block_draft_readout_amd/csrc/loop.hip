@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs g) {
 
 // gathered taps (n_taps x [max_rows, H]) | fc workspace
 static size_t gathered_bytes(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {
-  return align256(static_cast<size_t>(max_rows) * hidden * (dt == BDR_BF16 ? 2 : 4)) * n_taps;
+  return align256(static_cast<size_t>(max_rows) * hidden * (act_dtype(dt) == BDR_BF16 ? 2 : 4)) * n_taps;
 }
 
 size_t fc_rows_workspace(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {
@@ -182,7 +182,7 @@ hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int
                           bdr_dtype dt, const int32_t* row_index, const int32_t* row_count,
                           int64_t max_rows, const void* fc_w, void* out, void* workspace,
                           hipStream_t stream) {
-  const int64_t es = dt == BDR_BF16 ? 2 : 4;
+  const int64_t es = act_dtype(dt) == BDR_BF16 ? 2 : 4;
   char* ws = static_cast<char*>(workspace);
   const void* gathered[BDR_MAX_TAPS] = {};
   hipError_t e = launch_gather(taps, n_taps, rows, hidden, es, row_index, row_count, max_rows, ws,
@@ -190,7 +190,7 @@ hipError_t launch_fc_rows(const void* const* taps, int n_taps, int64_t rows, int
   if (e != hipSuccess) return e;
   const GemmPlan p = plan_gemm(max_rows, hidden, hidden * n_taps, dt, true, n_taps);
   return launch_gemm(p, dt, gathered, n_taps, hidden, max_rows, hidden, fc_w, out,
-                     dt == BDR_BF16 ? OUT_BF16 : OUT_F32,
+                     act_dtype(dt) == BDR_BF16 ? OUT_BF16 : OUT_F32,
                      ws + gathered_bytes(max_rows, hidden, n_taps, dt), stream);
 }
 

@@ -38,6 +38,9 @@
  *     under 2^31 bytes (BDR_EUNSUPPORTED otherwise).
  *   - Token ids are int32, counters int64.  dtype selects the storage of
  *     weights and activations (BDR_BF16 or BDR_F32); accumulation is fp32.
+ *     BDR_BF16_PACKED is bf16 storage with the GEMM weight (fc_w, lm_head_w)
+ *     in the packed layout of bdr_pack_weight; only the calls that document
+ *     it accept it.
  *   - Entry points are reentrant; calls that share a workspace must be ordered
  *     on one stream.
  */
@@ -51,7 +54,7 @@
 extern "C" {
 #endif
 
-typedef enum bdr_dtype { BDR_F32 = 0, BDR_BF16 = 1 } bdr_dtype;
+typedef enum bdr_dtype { BDR_F32 = 0, BDR_BF16 = 1, BDR_BF16_PACKED = 2 } bdr_dtype;
 
 #define BDR_OK            0
 #define BDR_EINVAL       -1  /* null required pointer, bad size, misalignment     */
@@ -99,6 +102,44 @@ void bdr_set_markov_forced_time_out(int on);
  * it.  Tests and tuning use it to reach every kernel variant on small shapes.
  * Returns BDR_EINVAL for a negative value, workgroups > 2^20 or ksplit > 256. */
 int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit);
+
+/* ---------------------------------------------------------------------------
+ * Packed weights -- a bf16 weight matrix [rows, cols] (fc_w: rows = H, cols =
+ * n_taps*H; lm_head_w: rows = V, cols = H) rearranged once, at load time, so
+ * that the decode GEMMs read it as contiguous blocks.
+ *
+ * The fc and the LM head stream their weight once per call against a few
+ * hundred activation rows at most ([pr128] "What was missing" item 1: the
+ * concatenated tap features through fc.weight; [recipe] DSpark port notes:
+ * the proposer's full-vocabulary logits), so HBM bandwidth bounds them.  Their
+ * kernel reads 16 weight rows x 128 columns at a time; in the row-major
+ * layout those are 16 pieces of 256 bytes, one row-length apart.  The packed
+ * layout stores each such block as 4096 contiguous bytes, the blocks of one
+ * 128-column range side by side:
+ *
+ *   packed[c][t][r][j] = w[16 t + r][128 c + j]   (0 where outside w)
+ *   c < ceil(cols / 128), t < ceil(rows / 16), r < 16, j < 128
+ *
+ * The results are those of the row-major layout (bit for bit where both take
+ * the same plan: 17 to 160 activation rows).  Calls that accept
+ * BDR_BF16_PACKED (dflash_fuse_fc, dflash_fuse_fc_rows, dspark_lm_head,
+ * dflash_fuse_fc_lm_head, dspark_draft_block, dspark_draft_block_noalloc and
+ * their workspace queries) read fc_w / lm_head_w packed and everything else
+ * as BDR_BF16; they serve every row count, up to 16 rows with the batched
+ * kernel (the row-major layout's one-sequence kernel is faster there) and
+ * above 160 rows in slabs of 160 rows, each streaming the weight again.  A
+ * multi-tap fc with packed weights needs H % 128 == 0.
+ *
+ * bdr_packed_weight_bytes: bytes of the packed copy; 0 when cols % 8 != 0,
+ *   rows or cols <= 0, or the packed copy would reach 2^31 bytes.
+ * bdr_pack_weight: writes the packed copy of w.
+ *   w       [rows, cols] bf16, device, 16-byte aligned
+ *   packed  device buffer of bdr_packed_weight_bytes(rows, cols), 16-byte
+ *           aligned, not overlapping w; the caller owns both
+ *   Returns BDR_EUNSUPPORTED where bdr_packed_weight_bytes returns 0.
+ * ------------------------------------------------------------------------- */
+size_t bdr_packed_weight_bytes(int64_t rows, int64_t cols);
+int bdr_pack_weight(const void* w, int64_t rows, int64_t cols, void* packed, void* stream);
 
 /* ---------------------------------------------------------------------------
  * S1  dflash_fuse_fc -- fuse the tapped target hidden states and apply the fc.

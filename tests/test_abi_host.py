@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 8
+    assert L.bdr_abi_version() == 9
 
 
 def test_workspace_sizes(L):
@@ -332,3 +332,60 @@ def test_row_split_override_drives_the_plan(L):
     finally:
         assert L.bdr_set_row_split_override(0, 0, 0) == A.BDR_OK
     assert L.dflash_fuse_fc_workspace_bytes(rows, H, T, A.BDR_BF16) == own
+
+
+def test_packed_weight_bytes(L):
+    """Bytes of the packed copy: ceil(rows / 16) tiles x ceil(cols / 128)
+    blocks x 4096; 0 where the layout cannot hold the matrix."""
+    assert L.bdr_packed_weight_bytes(151936, 5120) == 9496 * 40 * 4096
+    assert L.bdr_packed_weight_bytes(5120, 25600) == 320 * 200 * 4096
+    assert L.bdr_packed_weight_bytes(17, 136) == 2 * 2 * 4096
+    assert L.bdr_packed_weight_bytes(1, 8) == 4096
+    assert L.bdr_packed_weight_bytes(16, 12) == 0           # cols % 8
+    assert L.bdr_packed_weight_bytes(0, 128) == 0
+    assert L.bdr_packed_weight_bytes(16, -8) == 0
+    assert L.bdr_packed_weight_bytes(1 << 20, 1 << 10) == 0  # 2^31 bytes
+    assert L.bdr_packed_weight_bytes((1 << 20) - 16, 1 << 10) == (1 << 31) - 16 * 2048
+    assert L.bdr_packed_weight_bytes(1 << 62, 1 << 40) == 0
+
+
+def test_packed_weight_validation(L):
+    from block_draft_readout_amd import _abi as A
+    P = C.c_void_p(4096)
+    Q = C.c_void_p(1 << 40)
+    assert L.bdr_pack_weight(P, 16, 12, Q, None) == A.BDR_EUNSUPPORTED
+    assert L.bdr_pack_weight(None, 16, 128, Q, None) == A.BDR_EINVAL
+    assert L.bdr_pack_weight(P, 16, 128, None, None) == A.BDR_EINVAL
+    assert L.bdr_pack_weight(P, 16, 128, C.c_void_p(4104), None) == A.BDR_EINVAL   # alignment
+    assert L.bdr_pack_weight(P, 16, 128, C.c_void_p(4096 + 2048), None) == A.BDR_EINVAL
+    assert b"overlaps" in L.bdr_last_error()
+
+
+def test_packed_dtype_acceptance(L):
+    """BDR_BF16_PACKED is taken by the GEMM calls (same workspace as bf16 where
+    the plans agree, the 160-row slab's above) and refused, before the device,
+    by the calls whose dtype describes something else."""
+    from block_draft_readout_amd import _abi as A
+    PK = A.BDR_BF16_PACKED
+    assert L.dflash_fuse_fc_workspace_bytes(144, 5120, 5, PK) == \
+        L.dflash_fuse_fc_workspace_bytes(144, 5120, 5, A.BDR_BF16)
+    assert L.dflash_fuse_fc_workspace_bytes(400, 5120, 5, PK) == \
+        L.dflash_fuse_fc_workspace_bytes(160, 5120, 5, A.BDR_BF16)
+    assert L.dflash_fuse_fc_workspace_bytes(8, 5120, 5, PK) > 0
+    assert L.dflash_fuse_fc_workspace_bytes(20, 160, 2, PK) == 0       # multi-tap H % 128
+    assert L.dflash_fuse_fc_rows_workspace_bytes(144, 5120, 5, PK) == \
+        L.dflash_fuse_fc_rows_workspace_bytes(144, 5120, 5, A.BDR_BF16)
+    assert L.dflash_fuse_fc_lm_head_workspace_bytes(144, 5120, 5, 128, 151936, PK) == \
+        L.dflash_fuse_fc_lm_head_workspace_bytes(144, 5120, 5, 128, 151936, A.BDR_BF16)
+    P = C.c_void_p(4096)
+    taps = (C.c_void_p * 2)(*([4096] * 2))
+    assert L.dflash_fuse_fc(taps, 2, 20, 160, PK, P, P, None, 0, None) == A.BDR_EUNSUPPORTED
+    assert b"128" in L.bdr_last_error()
+    assert L.dspark_lm_head(P, 7, 5120, 1 << 20, PK, P, P, None) == A.BDR_EUNSUPPORTED  # 2^31 bytes
+    assert L.dspark_lm_head(P, 0, 5120, 151936, PK, P, P, None) == A.BDR_OK
+    # the Markov and verification dtypes describe their own operands
+    assert L.dspark_markov_argmax(P, 1, 8, 1000, PK, P, P, 8, P, P, None, P, 1 << 20, None) == A.BDR_EINVAL
+    assert L.spec_verify_greedy(P, PK, 16, 8, 151936, P, None, 0.3, P, P, P, None, None, None,
+                                None, 0, None) == A.BDR_EINVAL
+    hc = (C.c_void_p * 1)(4096)
+    assert L.dflash_hc_average(hc, 1, 2, 8, 128, 1024, 128, PK, hc, None) == A.BDR_EINVAL
