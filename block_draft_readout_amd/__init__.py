@@ -24,7 +24,8 @@ __all__ = [
     "spec_verify_greedy", "dspark_gumbel_noise", "dspark_markov_sample", "spec_verify_sample",
     "spec_commit", "dflash_fuse_fc_rows", "dflash_fuse_fc_fp8", "dspark_lm_head_fp8",
     "dflash_hc_average", "dflash_fuse_fc_rows_fp8", "PackedWeight", "pack_weight",
-    "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us", "set_markov_forced_time_out", "MARKOV_TIMED_OUT",
+    "workspace_bytes", "lib", "BdrError", "set_markov_poll_timeout_us",
+    "set_markov_forced_time_out", "MARKOV_TIMED_OUT",
 ]
 
 

@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs g) {
 
 // gathered taps (n_taps x [max_rows, H]) | fc workspace
 static size_t gathered_bytes(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {
-  return align256(static_cast<size_t>(max_rows) * hidden * (act_dtype(dt) == BDR_BF16 ? 2 : 4)) * n_taps;
+  const size_t es = act_dtype(dt) == BDR_BF16 ? 2 : 4;
+  return align256(static_cast<size_t>(max_rows) * hidden * es) * n_taps;
 }
 
 size_t fc_rows_workspace(int64_t max_rows, int64_t hidden, int n_taps, bdr_dtype dt) {

@@ -35,8 +35,10 @@ def _reference_packing(w: torch.Tensor) -> torch.Tensor:
 
 
 def _bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
-    return a.shape == b.shape and bool((a.view(torch.int32 if a.dtype == torch.float32 else torch.int16)
-                                        == b.view(torch.int32 if b.dtype == torch.float32 else torch.int16)).all())
+    if a.shape != b.shape or a.dtype != b.dtype:
+        return False
+    iv = torch.int32 if a.dtype == torch.float32 else torch.int16
+    return bool((a.view(iv) == b.view(iv)).all())
 
 
 def _randn_bf16(shape, seed, scale=1.0):
