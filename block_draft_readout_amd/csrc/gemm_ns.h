@@ -18,8 +18,9 @@
 //             passes and K blocks, so the barriers match;
 //   order     visits run pass by pass, K block by K block, tile by tile, and
 //             each wave's loads stream on across block and pass boundaries,
-//             R - 1 visits ahead (a ring slot is refilled only after this wave
-//             multiplied the visit it held);
+//             R visits ahead (a ring slot is refilled as soon as this wave's
+//             LDS reads of the visit it held are done, before that visit's
+//             MFMAs, so R visits are in flight while they run);
 //   A stage   the slice of the next block is copied (each wave a quarter of
 //             the loads) right after the barrier of the current one; the
 //             buffer it overwrites was last read before that barrier.
@@ -30,9 +31,9 @@
 //   * a pass holds ng groups of R tile slots (ng <= NG, chosen per workgroup
 //     from its range so that few slots stay empty); tile t of a pass lives in
 //     ring slot t % R in every K block;
-//   * the visit loaded at step t is the one R - 1 ahead, into the slot read at
-//     step t - 1: tile t + R - 1 of this block, or tile t + R - 1 - ng R of the
-//     next block (or of the next pass's first) -- the slot is known at compile
+//   * the visit loaded at step t is the one R ahead, into the slot step t has
+//     just read: tile t + R of this block, or tile t + R - ng R of the next
+//     block (or of the next pass's first) -- the slot is known at compile
 //     time, only the tile's offset is selected at run time;
 //   * a slot past the wave's tiles (at most a few in its last pass) reads
 //     nothing (out-of-range loads) and is not stored;
@@ -41,8 +42,8 @@
 //     in issue order).  Every block issues its MT A-staging loads (out of
 //     range past the last block or row), so each wait counts a compile-time
 //     number of loads: before step t NI * (R - 1), + MT while the visit
-//     predates the block's A loads; before a block's barrier NI * R (at least
-//     R visits followed its A loads), NI * (R - 1) for the first.
+//     predates the block's A loads (t < R); before a block's barrier NI * R
+//     (at least R visits followed its A loads).
 // R is a template argument: deep rings for long ranges (the LM head), shallow
 // ones where a wave has two or three tiles (a K-split fc), so that the ring is
 // not filled with empty slots.
@@ -262,33 +263,39 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
       static_for<MT>([&](auto m) { acc[t][m] = mma16(a[m][i], q[i], acc[t][m], uint16_t()); });
     }
   };
-  // a visit with the A operands in registers: its LDS reads, then its MFMAs
-  // (one latency per visit)
-  auto compute = [&](auto t, int slot) {
+  // a visit with the A operands in registers: its LDS reads; once they are
+  // done the slot is refilled (`refill`: the visit R ahead), so those loads are
+  // in flight during this visit's MFMAs
+  auto compute = [&](auto t, int slot, auto&& refill) {
     u32x4_t q[SH::WSTEPS], lo, hi;
     read_w(slot, q);
+    BDR_WAIT_VM_LGKM(63, 0);
+    refill();
+    __builtin_amdgcn_sched_barrier(0);
     static_for<4>([&](auto i) { mma_part(t, i, q, lo, hi); });
-    __builtin_amdgcn_sched_group_barrier(0x100, SH::WSTEPS, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
   };
   // the first visit of a block, which also brings the block's A slice (staging
-  // buffer b) into registers: part i's A reads, then its MFMAs, so the MFMAs of
-  // one part run while the next part's reads are in flight (at most 15 LDS
-  // reads can be outstanding)
-  auto compute_first = [&](auto t, int slot, int b) {
+  // buffer b) into registers: the weight reads and part 0's A reads, the
+  // refill, then part i's MFMAs with part i + 1's A reads in flight (at most 15
+  // LDS reads can be outstanding)
+  auto compute_first = [&](auto t, int slot, int b, auto&& refill) {
     u32x4_t q[SH::WSTEPS], lo, hi;
     read_w(slot, q);
+    read_a(b, std::integral_constant<int, 0>{});
+    BDR_WAIT_VM_LGKM(63, 0);
+    refill();
     static_for<4>([&](auto i) {
-      read_a(b, i);
+      if constexpr (i > 0) read_a(b, i);
       mma_part(t, i, q, lo, hi);
-      __builtin_amdgcn_sched_group_barrier(0x100, i == 0 ? SH::WSTEPS + MT : MT, 0);
+      if constexpr (i > 0) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
     });
   };
 
-  // prologue: A of the first block, then tiles 0 .. R - 2 of pass 0 (ng >= 1)
+  // prologue: A of the first block, then tiles 0 .. R - 1 of pass 0 (ng >= 1)
   dma_a(kb_lo, 0, true);
-  static_for<R - 1>([&](auto t) { dma_w(kb_lo * kb_str + t * tile_bytes, t, kb_lo, t); });
+  static_for<R>([&](auto t) { dma_w(kb_lo * kb_str + t * tile_bytes, t, kb_lo, t); });
   int blk = 0;
   const int nblk = npass * static_cast<int>(kb_hi - kb_lo);
   const int pass_tiles = ng * R;
@@ -296,10 +303,9 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   int pt = 0;   // first tile of the pass
   for (int p = 0; p < npass; ++p, base += pass_bytes, pt += pass_tiles) {
     for (uint32_t kb = kb_lo; kb < kb_hi; ++kb, ++blk) {
-      if (blk == 0)
-        ns_wait_vm<NI * (R - 1)>();
-      else
-        ns_wait_vm<NI * R>();
+      // this block's A slice has landed once at most R visits are outstanding
+      // (R or more followed its loads)
+      ns_wait_vm<NI * R>();
       BDR_WG_BARRIER();
       // the next block's A slice first: its segment pointer may come from a
       // scalar load, whose wait would otherwise also wait for this block's A
@@ -318,26 +324,26 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
           static_for<R>([&](auto jc) {
             constexpr int J = decltype(jc)::value;
             constexpr int T = G * R + J;
-            // The refill below writes the slot the previous step read.  The
-            // compiler does not see the buffer-to-LDS write as touching those
-            // addresses and would hoist it among that step's LDS reads; an
-            // out-of-range load (an empty slot) lands within a few cycles and
-            // would zero the slot under them.  Past this point the previous
-            // step's MFMAs, and so its LDS reads, have all been issued.
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (J == 0) {
-              dma_w(here + (T + R - 1) * tile_bytes, pt + T + R - 1, kb, R - 1);
-            } else {
-              const uint32_t in_blk = here + ((G + 1) * R + J - 1) * tile_bytes;
-              const uint32_t nx_blk = next == kOOB ? kOOB : next + (J - 1) * tile_bytes;
-              dma_w(last_g ? nx_blk : in_blk, last_g ? npt + J - 1 : pt + (G + 1) * R + J - 1,
-                    last_g ? nkb : kb, J - 1);
-            }
-            ns_wait_vm<NI * (R - 1) + (T < R - 1 ? NA : 0)>();
+            // visit T (slot J) has landed: issued R steps back, R - 1 visits
+            // followed it, and this block's A loads too while T < R
+            ns_wait_vm<NI * (R - 1) + (T < R ? NA : 0)>();
+            // The refill writes the slot this step reads: visit T + R, tile
+            // (G + 1) R + J of this block or tile J of the next block.  The
+            // compiler does not see the buffer-to-LDS write as touching those
+            // addresses; it is issued after a wait for this step's LDS reads
+            // (an out-of-range load, for an empty slot, lands within a few
+            // cycles and would zero the slot under reads still in flight).
+            const uint32_t in_blk = here + ((G + 1) * R + J) * tile_bytes;
+            const uint32_t nx_blk = next == kOOB ? kOOB : next + J * tile_bytes;
+            auto refill = [&]() {
+              dma_w(last_g ? nx_blk : in_blk, last_g ? npt + J : pt + (G + 1) * R + J,
+                    last_g ? nkb : kb, J);
+            };
             if constexpr (T == 0)
-              compute_first(std::integral_constant<int, T>{}, J, blk & 1);
+              compute_first(std::integral_constant<int, T>{}, J, blk & 1, refill);
             else
-              compute(std::integral_constant<int, T>{}, J);
+              compute(std::integral_constant<int, T>{}, J, refill);
           });
         }
       });
