@@ -39,8 +39,9 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h",
-                "gemm_ns.h", "gemm_ns_bf16.hip", "bdr_device.h", "gemm_plan.h")
+GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_ns.h", "gemm_ns_bf16.hip",
+                "gemm_ns_packed.hip", "gemm_ns_pair_a.hip", "gemm_ns_pair_b.hip",
+                "gemm_ns_pair_packed.hip", "pack.hip", "bdr_device.h", "gemm_plan.h")
 GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_kernels.h",
                     "bdr_device.h", "gemm_plan.h")
 

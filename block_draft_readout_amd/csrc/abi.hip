@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
 
 extern "C" {
 
-int bdr_abi_version(void) { return 9; }
+int bdr_abi_version(void) { return 10; }
 
 void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
 
@@ -280,7 +280,8 @@ namespace {
 PairPlan fc_lm_pair(int64_t rows, int64_t hidden, int n_taps, int64_t lm_rows, int64_t vocab,
                     bdr_dtype dt) {
   if (act_dtype(dt) != BDR_BF16 || rows == 0 || lm_rows == 0) return PairPlan{};
-  return plan_gemm_pair(lm_rows, vocab, hidden, rows, hidden, hidden * n_taps, n_taps);
+  return plan_gemm_pair(lm_rows, vocab, hidden, rows, hidden, hidden * n_taps, n_taps,
+                        dt == BDR_BF16_PACKED);
 }
 }  // namespace
 

@@ -43,6 +43,11 @@ __device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// the same with the non-temporal hint (data streamed once)
+__device__ __forceinline__ u32x4_t bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+
 __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

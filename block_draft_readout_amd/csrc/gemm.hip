@@ -359,26 +359,28 @@ static bool plan_stream(int64_t M, int64_t N, int64_t K, int esize, bool allow_s
 // tiles a wave walks npass passes of ng groups; the ring depth is the one of
 // kNsLeanRings that leaves the fewest slots (empty ones still cost their
 // MFMAs and issue), the deepest among equals.
-static int64_t ns_lean_passes(int mt, int ring, int64_t tiles) {
-  const int64_t ntw = kNsLeanNtwMax[mt] / ring * ring;
+// reg: the register ring (packed weights), whose passes hold one group of
+// `ring` tiles
+static int64_t ns_lean_passes(int mt, int ring, int64_t tiles, bool reg = false) {
+  const int64_t ntw = reg ? ring : kNsLeanNtwMax[mt] / ring * ring;
   return std::max<int64_t>(1, (tiles + ntw - 1) / ntw);
 }
 
-static int64_t ns_lean_slots(int mt, int ring, int64_t tiles) {
-  const int64_t npass = ns_lean_passes(mt, ring, tiles);
-  const int64_t ng = std::max<int64_t>(1, (tiles + npass * ring - 1) / (npass * ring));
+static int64_t ns_lean_slots(int mt, int ring, int64_t tiles, bool reg = false) {
+  const int64_t npass = ns_lean_passes(mt, ring, tiles, reg);
+  const int64_t ng = reg ? 1 : std::max<int64_t>(1, (tiles + npass * ring - 1) / (npass * ring));
   return npass * ng * ring;
 }
 
 // pass `rings` to restrict the choice (the two-problem launch builds fewer)
-static int ns_pick_ring(int mt, int64_t tiles, const int* rings = nullptr) {
+static int ns_pick_ring(int mt, int64_t tiles, const int* rings = nullptr, bool reg = false) {
   if (rings == nullptr) rings = kNsLeanRings[mt];
   int best = 0;
   int64_t best_slots = 0;
   for (int i = 0; i < 3; ++i) {
     const int r = rings[i];
     if (r == 0) continue;
-    const int64_t s = ns_lean_slots(mt, r, tiles);
+    const int64_t s = ns_lean_slots(mt, r, tiles, reg);
     if (best == 0 || s < best_slots) {
       best = r;
       best_slots = s;
@@ -394,10 +396,10 @@ static int64_t ns_wave_tiles(int64_t N, int64_t nwg) {
 }
 
 // passes of a wave with the ring it would take (kNsLeanRings)
-static int64_t ns_passes(int mt, int64_t tiles, int* ring) {
-  const int r = ns_pick_ring(mt, tiles);
+static int64_t ns_passes(int mt, int64_t tiles, int* ring, bool reg = false) {
+  const int r = ns_pick_ring(mt, tiles, nullptr, reg);
   if (ring) *ring = r;
-  return ns_lean_passes(mt, r, tiles);
+  return ns_lean_passes(mt, r, tiles, reg);
 }
 
 static std::atomic<int> g_ns_ring{0};
@@ -415,7 +417,10 @@ static bool ns_overridden() {
 }
 
 // packed: bf16 weights in the packed layout, any M in 1..160 (at least two A
-// row tiles; rows past M read as zero)
+// row tiles; rows past M read as zero), by the register ring from
+// kNsRegMinMt row tiles on.  The row ranges and K splits are chosen as for the
+// row-major layout (so the two give the same sums bit for bit); only the ring
+// depth follows the register ring.
 static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split, int n_seg,
                     GemmPlan* p, bool packed = false) {
   constexpr int KE = 128;
@@ -460,7 +465,8 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   p->stream = true;
   p->ns = true;
   p->mt = static_cast<int>(mtiles);
-  ns_passes(p->mt, ns_wave_tiles(N, p->n_waves), &p->ring);
+  p->reg = packed && p->mt >= kNsRegMinMt;
+  ns_passes(p->mt, ns_wave_tiles(N, p->n_waves), &p->ring, p->reg);
   if (g_ns_ring.load() > 0) p->ring = g_ns_ring.load();   // (the launch checks it is built)
   p->kblocks = kblocks;
   p->m_groups = 1;
@@ -488,7 +494,7 @@ static constexpr int kPairRings[11][3] = {{0, 0, 0}, {0, 0, 0}, {8, 5, 3}, {7, 5
                                           {0, 0, 0}};
 
 PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1,
-                        int n_seg1) {
+                        int n_seg1, bool packed) {
   PairPlan pp;
   GemmPlan q0, q1;
   if (ns_overridden()) return pp;
@@ -538,8 +544,13 @@ PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t 
   q0.ksplit = 1;
   q0.kb_per_split = kb0;
   q0.workspace = 0;
-  q0.ring = ns_pick_ring(q0.mt, ns_wave_tiles(N0, pp.n0), kPairRings[q0.mt]);
+  // (the register ring, packed weights from kNsRegMinMt row tiles on, is
+  // built for every ring of kNsLeanRings; the fc beside it takes it too)
+  const bool reg = packed && q0.mt >= kNsRegMinMt;
+  q0.ring = ns_pick_ring(q0.mt, ns_wave_tiles(N0, pp.n0),
+                         reg ? kNsLeanRings[q0.mt] : kPairRings[q0.mt], reg);
   q1.ring = 3;
+  q0.reg = q1.reg = reg;
   q1.workspace = q1.ksplit > 1 ? align256(static_cast<size_t>(q1.ksplit) * M1 * N1 * 4) : 0;
   // the row ranges must keep their 32-bit offsets with the fewer workgroups
   const int64_t rows_w0 = ((N0 + pp.n0 - 1) / pp.n0 + 3) / 4;
@@ -750,7 +761,7 @@ hipError_t launch_gemm(const GemmPlan& p, bdr_dtype dt, const void* const* a, in
       void* o = static_cast<char*>(out) + m0 * N * out_es;
       gs.out = split ? workspace : o;
       const StreamArgs sa{gs, p.n_waves, p.kblocks, p.kb_per_split};
-      hipError_t e = launch_ns_bf16(p, sa, stream);
+      hipError_t e = p.reg ? launch_ns_bf16_packed(p, sa, stream) : launch_ns_bf16(p, sa, stream);
       if (e == hipSuccess) e = hipGetLastError();
       if (e == hipSuccess && split) e = launch_splitk_reduce(p, gs.M, N, o, out_kind, workspace, stream);
       if (e != hipSuccess) return e;
@@ -808,9 +819,11 @@ hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, 
   g1.out = split ? workspace : out1;
   const StreamArgs s0{g0, pp.p0.n_waves, pp.p0.kblocks, pp.p0.kb_per_split};
   const StreamArgs s1{g1, pp.p1.n_waves, pp.p1.kblocks, pp.p1.kb_per_split};
-  hipError_t e = pp.p0.mt <= 4
-                     ? launch_ns_pair_bf16_a(pp.p0.mt, pp.p0.ring, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream)
-                     : launch_ns_pair_bf16_b(pp.p0.mt, pp.p0.ring, pp.p1.mt, s0, s1, pp.n0, pp.n1, stream);
+  const int m0 = pp.p0.mt, r0 = pp.p0.ring, m1 = pp.p1.mt;
+  const unsigned n0 = pp.n0, n1 = pp.n1;
+  hipError_t e = pp.p0.reg ? launch_ns_pair_bf16_packed(m0, r0, m1, s0, s1, n0, n1, stream)
+                 : m0 <= 4 ? launch_ns_pair_bf16_a(m0, r0, m1, s0, s1, n0, n1, stream)
+                           : launch_ns_pair_bf16_b(m0, r0, m1, s0, s1, n0, n1, stream);
   if (e != hipSuccess || !split) return e;
   return launch_splitk_reduce(pp.p1, pp.M1, pp.N1, out1, OUT_BF16, workspace, stream);
 }

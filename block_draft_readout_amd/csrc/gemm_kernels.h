@@ -126,5 +126,11 @@ hipError_t launch_ns_pair_bf16_a(int mt0, int r0, int mt1, const StreamArgs& a0,
                                  const StreamArgs& a1, unsigned n0, unsigned n1, hipStream_t st);
 hipError_t launch_ns_pair_bf16_b(int mt0, int r0, int mt1, const StreamArgs& a0,
                                  const StreamArgs& a1, unsigned n0, unsigned n1, hipStream_t st);
+// the same with the register ring, for bf16 weights in the packed layout with
+// at least kNsRegMinMt A row tiles (gemm_ns_packed.hip, gemm_ns_pair_packed.hip)
+hipError_t launch_ns_bf16_packed(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_ns_pair_bf16_packed(int mt0, int r0, int mt1, const StreamArgs& a0,
+                                      const StreamArgs& a1, unsigned n0, unsigned n1,
+                                      hipStream_t st);
 
 }  // namespace bdr

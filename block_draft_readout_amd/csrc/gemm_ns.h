@@ -47,6 +47,15 @@
 // R is a template argument: deep rings for long ranges (the LM head), shallow
 // ones where a wave has two or three tiles (a K-split fc), so that the ring is
 // not filled with empty slots.
+//
+// Weights in the packed layout (bf16) come in visits stored in MFMA operand
+// order (1 KB part i holds, for lane l = 16 g + r, elements 32 i + 8 g .. + 7
+// of the visit's row r).  The LDS ring copies each part to one load group and
+// reads it back linearly; with REG = true (five or more A row tiles) they skip
+// LDS: four contiguous 1 KB loads put a visit straight into the registers the
+// MFMAs read, and the ring is R visits of registers (a pass is one group of R
+// tiles, the register budget).  Its slot is refilled once the visit's MFMAs
+// are issued; the waits count the same loads as above.
 #pragma once
 
 #include "gemm_kernels.h"
@@ -77,16 +86,18 @@ struct NsShape {
 
 template <int MT> constexpr int ns_lean_ntw_max() { return kNsLeanNtwMax[MT]; }
 
-template <int MT, int R>
+template <int MT, int R, bool REG = false>
 struct NsLean {
-  static constexpr int NG = ns_lean_ntw_max<MT>() / R;   // groups of R slots per pass, at most
+  // groups of R slots per pass, at most (the register ring: one)
+  static constexpr int NG = REG ? 1 : ns_lean_ntw_max<MT>() / R;
   static constexpr int NTW = NG * R;
 };
 
-template <typename S, int MT, int R>
+template <typename S, int MT, int R, bool REG = false>
 constexpr size_t ns_lean_lds_bytes() {
   using SH = NsShape<S>;
-  return static_cast<size_t>(kNsWaves * R * SH::SLOT) + static_cast<size_t>(2 * MT) * SH::ASLOT;
+  return (REG ? size_t(0) : static_cast<size_t>(kNsWaves * R * SH::SLOT)) +
+         static_cast<size_t>(2 * MT) * SH::ASLOT;
 }
 
 template <int N>
@@ -95,15 +106,16 @@ __device__ __forceinline__ void ns_wait_vm() {
   BDR_WAIT_VM_LGKM(n, 15);
 }
 
-template <typename S, int MT, int R>
+template <typename S, int MT, int R, bool REG = false>
 __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, unsigned by,
                                              char* lds) {
   using SH = NsShape<S>;
   constexpr bool F8 = SH::F8;
-  constexpr int NG = NsLean<MT, R>::NG;
-  constexpr int NTW = NsLean<MT, R>::NTW;
+  static_assert(!(REG && F8), "the register ring takes bf16 weights");
+  constexpr int NG = NsLean<MT, R, REG>::NG;
+  constexpr int NTW = NsLean<MT, R, REG>::NTW;
   static_assert(NG >= 1 && R >= 2, "ring shape");
-  static_assert(ns_lean_lds_bytes<S, MT, R>() <= 160 * 1024, "LDS budget");
+  static_assert(ns_lean_lds_bytes<S, MT, R, REG>() <= 160 * 1024, "LDS budget");
   constexpr int NI = SH::NI;        // loads per visit
   constexpr int NA = MT;            // A loads per wave per block
   static_assert(NI * (R - 1) + NA <= 63, "vmcnt range");
@@ -146,12 +158,13 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const uint32_t akbytes = static_cast<uint32_t>(g.K * 2);
   const uint32_t segbytes = static_cast<uint32_t>(g.seg * 2);
   const uint32_t abytes = static_cast<uint32_t>(g.M) * segbytes;
-  // W layout.  Rows: [N, K].  Packed: the visits themselves, K block by K block
-  // and tile by tile ([kblocks][ceil(N / 16)][16][WROW], zero-padded), so a
-  // visit is one contiguous 16 * WROW bytes and the visits of one K block are
-  // adjacent.  A visit's bytes sit at block * kb_str + tile * tile_bytes, its
-  // rows row_str apart.
-  const bool packed = g.w_packed != 0;
+  // W layout.  Rows: [N, K].  Packed (bf16 only; always with the register
+  // ring): the visits themselves, K block by K block and tile by tile
+  // ([kblocks][ceil(N / 16)][4096 bytes], zero-padded, each in operand order),
+  // so a visit is one contiguous 4 KB and the visits of one K block are
+  // adjacent.  A visit's bytes sit at block * kb_str + tile * tile_bytes (rows
+  // row_str apart in the row-major layout).
+  const bool packed = REG || (!F8 && g.w_packed != 0);
   const uint32_t row_str = packed ? static_cast<uint32_t>(SH::WROW) : kbytes;
   const uint32_t kb_str = packed ? static_cast<uint32_t>(n_t * 16 * SH::WROW)
                                  : static_cast<uint32_t>(SH::WROW);
@@ -161,8 +174,8 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
                          static_cast<uint32_t>((sa.kblocks * n_t * 16 - n_lo) * SH::WROW))
              : make_rsrc(static_cast<const S*>(g.w) + static_cast<int64_t>(n_lo) * g.K,
                          wrows * kbytes);
-  char* const ring = lds + wave * (R * SH::SLOT);
-  char* const stage = lds + kNsWaves * R * SH::SLOT;             // [2][MT][ASLOT]
+  char* const ring = lds + wave * (R * SH::SLOT);                // (LDS ring)
+  char* const stage = lds + (REG ? 0 : kNsWaves * R * SH::SLOT);  // [2][MT][ASLOT]
   // Load lane mapping: consecutive lanes read one row's bytes (row lane / CPR
   // of the load, CPR = 16-byte chunks per row), so every quad of lanes reads
   // 64 contiguous bytes.  Each row is stored in LDS with its chunks permuted
@@ -170,17 +183,26 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   // position l % CPR, and operand reads undo the permutation.
   constexpr int CPR = SH::WROW / 16;
   constexpr int NPERM = F8 ? NI : 1;   // distinct permutations among a visit's loads
+  // (packed: load j of a visit is its part j, lane l's 16 bytes at 16 l,
+  // stored as they come and read back linearly)
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16;
   uint32_t w_chunk[NPERM], lane_off[NPERM];
 #pragma unroll
   for (int j = 0; j < NPERM; ++j) {
     w_chunk[j] = static_cast<uint32_t>((lane % CPR) ^ SH::wx(lane / CPR, j)) * 16;
-    lane_off[j] = static_cast<uint32_t>(lane / CPR) * row_str + w_chunk[j];
-    asm volatile("" : "+v"(lane_off[j]));
+    lane_off[j] = packed ? lane16 : static_cast<uint32_t>(lane / CPR) * row_str + w_chunk[j];
+    if constexpr (!REG) asm volatile("" : "+v"(lane_off[j]));
   }
+  const uint32_t jstride = packed ? 1024u : static_cast<uint32_t>(SH::RPI) * row_str;
   const uint32_t a_row = static_cast<uint32_t>(lane / 16);
   const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ SH::ax(lane / 16)) * 16;
   const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
   const int rs = SH::wx(r16 % SH::RPI, r16 / SH::RPI);
+  uint32_t w_rd[SH::WSTEPS];   // LDS offset of each 16-byte W operand read within a slot
+  static_for<SH::WSTEPS>([&](auto q) {
+    w_rd[q] = packed ? static_cast<uint32_t>(q * SH::GROUP) + lane16
+                     : rd + static_cast<uint32_t>(((4 * q + grp) ^ rs) * 16);
+  });
   const uint32_t rd_a = static_cast<uint32_t>((r16 / 4) * (1024 + 64) + (r16 % 4) * 256);
   const int rs_a = SH::ax(r16 % 4);
   const uint32_t tile_bytes = 16 * row_str;
@@ -197,24 +219,35 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   };
   zero_acc();
   u32x4_t a[MT][4];
+  u32x4_t wr[REG ? R : 1][4];   // the register ring
 
   // visit -> ring slot: sb = the visit's byte offset within this wave's rows
   // (pass base + K block + tile), kOOB for a visit past the last pass; ti = its
   // tile within the wave's range, a tile past the range (an empty slot) reads
-  // nothing (in the packed layout the descriptor reaches past the range)
+  // nothing (in the packed layout the descriptor reaches past the range).  The
+  // slot is a compile-time constant.
   const int wtiles = __builtin_amdgcn_readfirstlane((n_hi - n_lo + 15) / 16);
-  auto dma_w = [&](uint32_t sb, int ti, uint32_t kb, int slot) {
-    char* dst = ring + slot * SH::SLOT;
+  auto dma_w = [&](uint32_t sb, int ti, uint32_t kb, auto slot) {
     const bool none = sb == kOOB || ti >= wtiles;
+    if constexpr (REG) {
+      // part i (1 KB) -> wr[slot][i]; a partial last block reads the copy's zeros
+      const uint32_t s_off = __builtin_amdgcn_readfirstlane(none ? kOOB : sb);
+      static_for<4>([&](auto i) {
+        wr[slot][i] = bload16_nt(rw, s_off + static_cast<uint32_t>(i * 1024) + lane16);
+      });
+    } else {
+      char* dst = ring + slot * SH::SLOT;
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int jp = NPERM > 1 ? j : 0;
-      const bool cut = kb == kb_last && w_chunk[jp] >= tail_bytes;   // past a partial block's end
-      const uint32_t s_off = __builtin_amdgcn_readfirstlane(
-          none ? kOOB : sb + static_cast<uint32_t>(j * SH::RPI) * row_str);
-      const uint32_t off = cut ? kOOB : lane_off[jp] + s_off;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16, off, 0, 0, 2);
+      for (int j = 0; j < NI; ++j) {
+        const int jp = NPERM > 1 ? j : 0;
+        // past a partial block's end (the packed copy holds zeros there)
+        const bool cut = !packed && kb == kb_last && w_chunk[jp] >= tail_bytes;
+        const uint32_t s_off = __builtin_amdgcn_readfirstlane(
+            none ? kOOB : sb + static_cast<uint32_t>(j) * jstride);
+        const uint32_t off = cut ? kOOB : lane_off[jp] + s_off;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void*)(dst + j * SH::GROUP), 16, off, 0, 0, 2);
+      }
     }
   };
   // this wave's share of the A slice of block kb -> staging buffer b (all MT
@@ -248,10 +281,8 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
     });
   };
   auto read_w = [&](int slot, u32x4_t (&q)[SH::WSTEPS]) {
-    const char* src = ring + slot * SH::SLOT + rd;
-    static_for<SH::WSTEPS>([&](auto s) {
-      q[s] = *reinterpret_cast<const u32x4_t*>(src + (((4 * s + grp) ^ rs) * 16));
-    });
+    const char* src = ring + slot * SH::SLOT;
+    static_for<SH::WSTEPS>([&](auto s) { q[s] = *reinterpret_cast<const u32x4_t*>(src + w_rd[s]); });
   };
   auto mma_part = [&](auto t, auto i, const u32x4_t (&q)[SH::WSTEPS], u32x4_t& lo, u32x4_t& hi) {
     if constexpr (F8) {
@@ -265,32 +296,50 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   };
   // a visit with the A operands in registers: its LDS reads; once they are
   // done the slot is refilled (`refill`: the visit R ahead), so those loads are
-  // in flight during this visit's MFMAs
-  auto compute = [&](auto t, int slot, auto&& refill) {
-    u32x4_t q[SH::WSTEPS], lo, hi;
-    read_w(slot, q);
-    BDR_WAIT_VM_LGKM(63, 0);
-    refill();
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<4>([&](auto i) { mma_part(t, i, q, lo, hi); });
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+  // in flight during this visit's MFMAs.  The register ring refills the slot
+  // after its MFMAs are issued (their order left to the compiler: scheduling
+  // groups as below made it wait for every A read before each MFMA of a
+  // block's first visit).
+  auto compute = [&](auto t, auto slot, auto&& refill) {
+    u32x4_t lo, hi;
+    if constexpr (REG) {
+      static_for<4>([&](auto i) { mma_part(t, i, wr[slot], lo, hi); });
+      refill();
+    } else {
+      u32x4_t q[SH::WSTEPS];
+      read_w(slot, q);
+      BDR_WAIT_VM_LGKM(63, 0);
+      refill();
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<4>([&](auto i) { mma_part(t, i, q, lo, hi); });
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * MT, 0);
+    }
   };
   // the first visit of a block, which also brings the block's A slice (staging
   // buffer b) into registers: the weight reads and part 0's A reads, the
   // refill, then part i's MFMAs with part i + 1's A reads in flight (at most 15
   // LDS reads can be outstanding)
-  auto compute_first = [&](auto t, int slot, int b, auto&& refill) {
-    u32x4_t q[SH::WSTEPS], lo, hi;
-    read_w(slot, q);
-    read_a(b, std::integral_constant<int, 0>{});
-    BDR_WAIT_VM_LGKM(63, 0);
-    refill();
-    static_for<4>([&](auto i) {
-      if constexpr (i > 0) read_a(b, i);
-      mma_part(t, i, q, lo, hi);
-      if constexpr (i > 0) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
-    });
+  auto compute_first = [&](auto t, auto slot, int b, auto&& refill) {
+    u32x4_t lo, hi;
+    if constexpr (REG) {
+      static_for<4>([&](auto i) {
+        read_a(b, i);
+        mma_part(t, i, wr[slot], lo, hi);
+      });
+      refill();
+    } else {
+      u32x4_t q[SH::WSTEPS];
+      read_w(slot, q);
+      read_a(b, std::integral_constant<int, 0>{});
+      BDR_WAIT_VM_LGKM(63, 0);
+      refill();
+      static_for<4>([&](auto i) {
+        if constexpr (i > 0) read_a(b, i);
+        mma_part(t, i, q, lo, hi);
+        if constexpr (i > 0) __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+      });
+    }
   };
 
   // prologue: A of the first block, then tiles 0 .. R - 1 of pass 0 (ng >= 1)
@@ -338,12 +387,12 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
             const uint32_t nx_blk = next == kOOB ? kOOB : next + J * tile_bytes;
             auto refill = [&]() {
               dma_w(last_g ? nx_blk : in_blk, last_g ? npt + J : pt + (G + 1) * R + J,
-                    last_g ? nkb : kb, J);
+                    last_g ? nkb : kb, jc);
             };
             if constexpr (T == 0)
-              compute_first(std::integral_constant<int, T>{}, J, blk & 1, refill);
+              compute_first(std::integral_constant<int, T>{}, jc, blk & 1, refill);
             else
-              compute(std::integral_constant<int, T>{}, J, refill);
+              compute(std::integral_constant<int, T>{}, jc, refill);
           });
         }
       });
@@ -388,60 +437,63 @@ __device__ __forceinline__ unsigned ns_splits(const StreamArgs& sa) {
 // dispatcher spreads over the eight XCDs in turn, take different splits, so
 // with eight splits every XCD holds one split's workgroups and the A slice
 // they all read stays in that XCD's L2.
-template <typename S, int MT, int R>
+template <typename S, int MT, int R, bool REG = false>
 __global__ __launch_bounds__(256) void ws_gemm_ns_kernel(const StreamArgs sa) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const unsigned ks = ns_splits(sa);
-  ns_lean_body<S, MT, R>(sa, blockIdx.x / ks, blockIdx.x % ks, lds);
+  ns_lean_body<S, MT, R, REG>(sa, blockIdx.x / ks, blockIdx.x % ks, lds);
 }
 
 // Two GEMMs in one launch (the drafter fc beside the LM head): the first n0
 // workgroups take problem 0 (row ranges of a0, no K split); the others take
 // problem 1, workgroup n0 + i being K split i % splits of row range i / splits.
-template <typename S, int MT0, int R0, int MT1, int R1>
+template <typename S, int MT0, int R0, int MT1, int R1, bool REG = false>
 __global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a0,
                                                               const StreamArgs a1, unsigned n0) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   if (blockIdx.x < n0) {
-    ns_lean_body<S, MT0, R0>(a0, blockIdx.x, 0, lds);
+    ns_lean_body<S, MT0, R0, REG>(a0, blockIdx.x, 0, lds);
   } else {
     const unsigned i = blockIdx.x - n0;
     const unsigned ks = ns_splits(a1);
-    ns_lean_body<S, MT1, R1>(a1, i / ks, i % ks, lds);
+    ns_lean_body<S, MT1, R1, REG>(a1, i / ks, i % ks, lds);
   }
 }
 
-template <typename S, int MT, int R>
+// REG: the register ring, which reads the packed layout only
+template <typename S, int MT, int R, bool REG = false>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  constexpr size_t lds = ns_lean_lds_bytes<S, MT, R>();
+  if (REG && sa.g.w_packed == 0) return hipErrorInvalidValue;
+  constexpr size_t lds = ns_lean_lds_bytes<S, MT, R, REG>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, R>),
+        reinterpret_cast<const void*>(&ws_gemm_ns_kernel<S, MT, R, REG>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(static_cast<unsigned>(p.n_waves * p.ksplit));
-  hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, R>), grid, dim3(64 * kNsWaves), lds, st, sa);
+  hipLaunchKernelGGL((ws_gemm_ns_kernel<S, MT, R, REG>), grid, dim3(64 * kNsWaves), lds, st, sa);
   return hipGetLastError();
 }
 
-template <typename S, int MT0, int R0, int MT1, int R1>
+template <typename S, int MT0, int R0, int MT1, int R1, bool REG = false>
 hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
                               unsigned n1, hipStream_t st) {
-  constexpr size_t lds = ns_lean_lds_bytes<S, MT0, R0>() > ns_lean_lds_bytes<S, MT1, R1>()
-                             ? ns_lean_lds_bytes<S, MT0, R0>()
-                             : ns_lean_lds_bytes<S, MT1, R1>();
+  if (REG && (a0.g.w_packed == 0 || a1.g.w_packed == 0)) return hipErrorInvalidValue;
+  constexpr size_t l0 = ns_lean_lds_bytes<S, MT0, R0, REG>();
+  constexpr size_t l1 = ns_lean_lds_bytes<S, MT1, R1, REG>();
+  constexpr size_t lds = l0 > l1 ? l0 : l1;
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1>),
+        reinterpret_cast<const void*>(&ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1, REG>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1>), dim3(n0 + n1),
+  hipLaunchKernelGGL((ws_gemm_ns_pair_kernel<S, MT0, R0, MT1, R1, REG>), dim3(n0 + n1),
                      dim3(64 * kNsWaves), lds, st, a0, a1, n0);
   return hipGetLastError();
 }

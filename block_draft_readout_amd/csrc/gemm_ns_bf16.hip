@@ -1,4 +1,5 @@
-// Instantiations of the row-split workgroup GEMM (gemm_ns.h) for bf16 weights:
+// Instantiations of the row-split workgroup GEMM (gemm_ns.h) with the LDS ring
+// for bf16 weights, row-major or (fewer than kNsRegMinMt A row tiles) packed:
 // every A row-tile count with each ring depth of kNsLeanRings.
 #include "gemm_ns.h"
 

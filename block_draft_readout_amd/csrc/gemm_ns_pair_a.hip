@@ -1,6 +1,7 @@
-// Instantiations of the two-problem row-split launch (gemm_ns.h), bf16
-// weights, LM head with 2 to 4 A row tiles: the LM head (mt0 tiles, ring r0 of
-// kNsLeanRings) beside the fc (mt0 or mt0 + 1 tiles, ring 3).
+// Instantiations of the two-problem row-split launch (gemm_ns.h) with the LDS
+// ring, bf16 weights (row-major or packed), LM head with 2 to 4 A row tiles:
+// the LM head (mt0 tiles, ring r0 of kNsLeanRings) beside the fc (mt0 or
+// mt0 + 1 tiles, ring 3).
 #include "gemm_ns.h"
 
 namespace bdr {

@@ -1,7 +1,7 @@
-// Instantiations of the two-problem row-split launch (gemm_ns.h), bf16
-// weights, LM head with 5 to 9 A row tiles (ring r0 of kNsLeanRings; seven
-// tiles with ring 3 spills and is left out) beside the fc (mt0 or mt0 + 1
-// tiles, at most 9, ring 3).
+// Instantiations of the two-problem row-split launch (gemm_ns.h) with the LDS
+// ring, row-major bf16 weights, LM head with 5 to 9 A row tiles (ring r0 of
+// kNsLeanRings; seven tiles with ring 3 spills and is left out) beside the fc
+// (mt0 or mt0 + 1 tiles, at most 9, ring 3).
 #include "gemm_ns.h"
 
 namespace bdr {

@@ -30,6 +30,7 @@ struct GemmPlan {
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;
   int ring = 0;           // ns: LDS ring slots per wave (kNsLeanRings)
+  bool reg = false;       // ns: the register ring (packed bf16, mt >= kNsRegMinMt)
   // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
   // K steps of 64 (kblocks / kb_per_split count steps)
   bool tile = false;
@@ -62,6 +63,10 @@ constexpr int kNumCU = 256;
 // first; 0 = none).  A deep ring keeps more loads in flight, a shallow one
 // wastes fewer slots on waves with few tiles.
 constexpr int kNsLeanNtwMax[11] = {0, 0, 16, 14, 12, 9, 8, 6, 5, 4, 3};
+// bf16 weights in the packed layout take the register ring from this many A
+// row tiles on (the same ring depths; one group of R tiles per pass); fewer
+// row tiles stream faster through the LDS ring
+constexpr int kNsRegMinMt = 5;
 constexpr int kNsLeanRings[11][3] = {{0, 0, 0}, {0, 0, 0}, {8, 5, 3}, {7, 5, 3}, {6, 5, 3},
                                      {6, 5, 3}, {6, 5, 3}, {5, 3, 0},  {5, 3, 0}, {4, 3, 0},
                                      {3, 0, 0}};
@@ -94,7 +99,7 @@ struct PairPlan {
   int64_t M0 = 0, N0 = 0, K0 = 0, M1 = 0, N1 = 0, K1 = 0;
 };
 PairPlan plan_gemm_pair(int64_t M0, int64_t N0, int64_t K0, int64_t M1, int64_t N1, int64_t K1,
-                        int n_seg1);
+                        int n_seg1, bool packed = false);
 hipError_t launch_gemm_pair(const PairPlan& pp, const void* a0, const void* w0, float* out0,
                             const void* const* a1, int n_seg1, int64_t seg1, const void* w1,
                             void* out1, void* workspace, bool packed, hipStream_t stream);

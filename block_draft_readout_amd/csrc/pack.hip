@@ -5,16 +5,20 @@
 // "What was missing" item 1; the DSpark port notes of the Qwen3.8-27B DFlash
 // drafter recipe), so they are bound by how fast HBM delivers the weight.  The
 // row-split kernel reads it in visits of 16 rows x 128 columns; the packed
-// layout stores each visit as 4096 contiguous bytes and the visits of one
-// 128-column range side by side:
+// layout stores each visit as 4096 contiguous bytes, the visits of one
+// 128-column range side by side, and within a visit the elements in the order
+// the MFMA operands take them:
 //
-//   packed[c][t][r][j] = w[16 t + r][128 c + j]   (zero outside w)
+//   packed[c][t][i][g][r][e] = w[16 t + r][128 c + 32 i + 8 g + e]   (zero outside w)
 //
-// so the chip's concurrent visits sweep one contiguous range of HBM instead of
-// 16 row pieces of 256 bytes each (a read-only probe streamed 6.65 TB/s from
-// the packed order against 5.94 from the row pieces).  A one-time copy at load
-// time: each thread moves 16-byte chunks, reads and writes coalesced in the
-// packed order.
+// (i, g < 4, r < 16, e < 8), so the chip's concurrent visits sweep one
+// contiguous range of HBM instead of 16 row pieces of 256 bytes each (a
+// read-only probe streamed 6.65 TB/s from the packed order against 5.94 from
+// the row pieces), and each 1 KB quarter i of a visit is, lane l = 16 g + r
+// taking 16 bytes, the operand of 64 lanes for elements 32 i .. 32 i + 31: a
+// visit goes from HBM into registers with four contiguous 1 KB loads.  A
+// one-time copy at load time: each thread moves one 16-byte chunk, the writes
+// coalesced in the packed order.
 
 #include <hip/hip_runtime.h>
 
@@ -27,7 +31,7 @@ namespace {
 
 constexpr int64_t kPackCols = 128;   // columns per visit
 constexpr int64_t kPackRows = 16;    // rows per visit
-constexpr int64_t kChunks = kPackCols * 2 / 16;   // 16-byte chunks per visit row
+constexpr int64_t kVisitChunks = kPackRows * kPackCols * 2 / 16;   // 16-byte chunks per visit
 
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __restrict__ w,
                                                           uint4* __restrict__ packed,
@@ -35,10 +39,11 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const uint16_t* __rest
                                                           int64_t tiles, int64_t total) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t j = (i % kChunks) * 8;                  // column within the visit
-    const int64_t r = (i / kChunks) % kPackRows;
-    const int64_t t = (i / (kChunks * kPackRows)) % tiles;
-    const int64_t c = i / (kChunks * kPackRows * tiles);
+    const int64_t q = i % kVisitChunks;                   // chunk within the visit: [i][g][r]
+    const int64_t r = q % kPackRows;
+    const int64_t j = 32 * (q / 64) + 8 * ((q / kPackRows) % 4);   // column within the visit
+    const int64_t t = (i / kVisitChunks) % tiles;
+    const int64_t c = i / (kVisitChunks * tiles);
     const int64_t n = kPackRows * t + r;
     const int64_t k = kPackCols * c + j;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);

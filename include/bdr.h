@@ -67,7 +67,8 @@ typedef enum bdr_dtype { BDR_F32 = 0, BDR_BF16 = 1, BDR_BF16_PACKED = 2 } bdr_dt
 #define BDR_MAX_RANK   128
 #define BDR_MAX_HC     16
 
-/* Version of this interface (incremented on any signature change). */
+/* Version of this interface (incremented on any signature change or change
+ * of a documented data layout). */
 int bdr_abi_version(void);
 
 /* Text describing the last non-zero return on the calling thread. */
@@ -115,10 +116,13 @@ int bdr_set_row_split_override(int ring, int64_t workgroups, int ksplit);
  * kernel reads 16 weight rows x 128 columns at a time; in the row-major
  * layout those are 16 pieces of 256 bytes, one row-length apart.  The packed
  * layout stores each such block as 4096 contiguous bytes, the blocks of one
- * 128-column range side by side:
+ * 128-column range side by side, and within a block the elements in the order
+ * the matrix-core operands take them (each 1 KB quarter is what 64 lanes load
+ * for 32 columns, straight into registers):
  *
- *   packed[c][t][r][j] = w[16 t + r][128 c + j]   (0 where outside w)
- *   c < ceil(cols / 128), t < ceil(rows / 16), r < 16, j < 128
+ *   packed[c][t][i][g][r][e] = w[16 t + r][128 c + 32 i + 8 g + e]
+ *                              (0 where outside w)
+ *   c < ceil(cols / 128), t < ceil(rows / 16), i < 4, g < 4, r < 16, e < 8
  *
  * The results are those of the row-major layout (bit for bit where both take
  * the same plan: 17 to 160 activation rows).  Calls that accept

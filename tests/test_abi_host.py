@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 9
+    assert L.bdr_abi_version() == 10
 
 
 def test_workspace_sizes(L):

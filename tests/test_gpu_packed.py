@@ -26,12 +26,15 @@ def _bdr():
 
 
 def _reference_packing(w: torch.Tensor) -> torch.Tensor:
-    """packed[c][t][r][j] = w[16 t + r][128 c + j], zero outside w, as uint8 bytes."""
+    """packed[c][t][i][g][r][e] = w[16 t + r][128 c + 32 i + 8 g + e], zero
+    outside w, as uint8 bytes."""
     rows, cols = w.shape
     T, C = (rows + 15) // 16, (cols + 127) // 128
     p = torch.zeros((T * 16, C * 128), dtype=w.dtype, device=w.device)
     p[:rows, :cols] = w
-    return p.view(T, 16, C, 128).permute(2, 0, 1, 3).contiguous().view(-1).view(torch.uint8)
+    # [t][r][c][i][g][e] -> [c][t][i][g][r][e]
+    return (p.view(T, 16, C, 4, 4, 8).permute(2, 0, 3, 4, 1, 5).contiguous().view(-1)
+            .view(torch.uint8))
 
 
 def _bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
