@@ -237,10 +237,27 @@ __device__ __forceinline__ unsigned long long poll_max(const MarkovArgs& g,
     __builtin_amdgcn_sched_barrier(0);                 \
   } while (0)
 
-constexpr int kChainWaves = 5;   // wave 0: hand-off; waves 1..4: vocabulary tiles
+// Waves of a chain workgroup: wave 0 for the hand-off and four compute waves,
+// each with a quarter of the workgroup's vocabulary tiles (sampling: the
+// compute waves generate the next position's noise while wave 0 waits).  W4:
+// four waves, wave 0 also taking the hand-off once its tiles are compared,
+// each within 168 registers (three waves' worth), so that a batched fc wave
+// of up to 344 registers fits beside the chain on every SIMD and that GEMM
+// runs beside it (with five waves one SIMD holds two chain waves).  Built
+// for greedy drafting with ranks up to 64 and at most ten tiles a wave (more
+// would spill), and launched from kChainW4MinB rows on (for fewer rows the fc
+// runs in one launch with the LM head, and wave 0's own logits prefetch,
+// which its polls retire behind, made the chain slower).
+constexpr int kChainW4MinB = 8;
+template <bool W4>
+constexpr int chain_waves() {
+  return W4 ? 4 : 5;
+}
 
-template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE>
-__global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const MarkovArgs g) {
+template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE, bool W4 = false>
+__global__ __launch_bounds__(64 * chain_waves<W4>(), W4 ? 3 : 2)
+void markov_chain_kernel(const MarkovArgs g) {
+  static_assert(!W4 || (!SAMPLE && RKS <= 2 && MAXT <= 10), "four-wave chain: greedy, small");
   extern __shared__ u32x4_t w2s[];   // [tile][chunk][lane] operand chunks of markov_w2
   constexpr int E = Elem<S>::PER16;
   constexpr int KS = Elem<S>::KSTEP;
@@ -248,7 +265,8 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
   constexpr int NC = RKS > 0 ? RKS : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int cw = wave - 1;           // compute wave index, -1 for the hand-off wave
+  constexpr int NW = chain_waves<W4>();
+  const int cw = W4 ? wave : wave - 1;   // compute wave index, -1 for a hand-off-only wave 0
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   const unsigned G = gridDim.x;
@@ -265,7 +283,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void markov_chain_kernel(const Ma
   // of chunk q land at w2s[q*64 + l])
   if constexpr (RKS > 0) {
     const rsrc_t r2 = make_rsrc(g.w2, static_cast<uint32_t>(g.V * g.r * ES));
-    for (int q = wave; q < ntl * RKS; q += kChainWaves) {
+    for (int q = wave; q < ntl * RKS; q += NW) {
       const int tile = q / RKS;
       const int c = q - tile * RKS;
       const int64_t v = (t_lo + tile) * 16 + r16;
@@ -735,25 +753,28 @@ static __global__ __launch_bounds__(256) void markov_finalize_kernel(MarkovArgs 
 
 constexpr size_t kChainLdsMax = 150 * 1024;
 
-template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE>
+template <typename S, int RKS, int MAXT, bool SAMPLE, bool ONE, bool W4 = false>
 static hipError_t launch_chain_r(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE>),
+        reinterpret_cast<const void*>(&markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE, W4>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kChainLdsMax));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE>), dim3(G),
-                     dim3(64 * kChainWaves), lds, st, g);
+  hipLaunchKernelGGL((markov_chain_kernel<S, RKS, MAXT, SAMPLE, ONE, W4>), dim3(G),
+                     dim3(64 * chain_waves<W4>()), lds, st, g);
   return hipSuccess;
 }
 
 template <typename S, int RKS, int MAXT, bool SAMPLE>
 static hipError_t launch_chain_t(const MarkovArgs& g, unsigned G, size_t lds, hipStream_t st) {
-  return g.B == 1 ? launch_chain_r<S, RKS, MAXT, SAMPLE, true>(g, G, lds, st)
-                  : launch_chain_r<S, RKS, MAXT, SAMPLE, false>(g, G, lds, st);
+  if (g.B == 1) return launch_chain_r<S, RKS, MAXT, SAMPLE, true>(g, G, lds, st);
+  if constexpr (!SAMPLE && RKS <= 2 && MAXT <= 10) {
+    if (g.B >= kChainW4MinB) return launch_chain_r<S, RKS, MAXT, false, false, true>(g, G, lds, st);
+  }
+  return launch_chain_r<S, RKS, MAXT, SAMPLE, false>(g, G, lds, st);
 }
 
 // MAXT: 16-entry vocabulary tiles per wave (the workgroup's tiles / 4, rounded up)

@@ -339,6 +339,24 @@ def test_markov_row_count_limits(B):
     log(f"markov B={B}: {c}")
 
 
+@pytest.mark.parametrize("B", [7, 8, 16, 33])
+def test_chain_wave_layouts(B):
+    """Both chain layouts against the oracle at the full vocabulary and rank
+    64: five waves (a hand-off wave beside four compute waves) below eight
+    rows, four waves (wave 0 compares its tiles, then takes the hand-off) from
+    eight on; 7 and 8 sit on either side of the switch, 33 takes three row
+    groups, the last holding one row."""
+    g = np.random.default_rng(900 + B)
+    k, V, r = 8, 151936, 64
+    Z = (g.standard_normal((B, k, V)) * 3).astype(np.float32)
+    w1 = synth.to_bf16_bits(g.standard_normal((V, r)).astype(np.float32))
+    w2 = synth.to_bf16_bits((g.standard_normal((V, r)) * 0.3).astype(np.float32))
+    prev = g.integers(0, V, B).astype(np.int32)
+    d = bdr().dspark_markov_argmax(dev(Z), dev(w1), dev(w2), dev(prev)).cpu().numpy()
+    c = check_draft(d, Z, w1, w2, prev, "bf16")
+    log(f"chain B={B}: {c}")
+
+
 def test_sentinel_outputs_all_written_and_deterministic():
     w = MID["mid_bf16"]
     W, s = _data(w)
@@ -458,7 +476,7 @@ def test_graph_replay_matches_eager():
     assert torch.equal(acc, acc_eager * 10)
 
 
-@pytest.mark.parametrize("B", [1, 16])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_chain_time_out_is_reported(B):
     """The chain's bounded waits made to give up (the host's error-path hook,
     which has every wait disregard what it reads, with a limit of 0): every
