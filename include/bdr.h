@@ -93,10 +93,11 @@ void bdr_set_markov_forced_time_out(int on);
 
 /* Plan override of the row-split GEMM (the fc and the LM head with 16 < rows
  * <= 160), for calls planned after this one, process-wide; 0 leaves a value
- * to the planner.  ring: LDS ring slots per wave of the bf16 kernel (built:
- * 8, 5, 3 for 2 row tiles; 7, 5, 3 for 3; 6, 5, 3 for 4 to 6; 5, 3 for 7 and
- * 8; 4, 3 for 9; 3 for 10 -- a call planned with any other fails with
- * BDR_EHIP); workgroups: row ranges (at most one per 16 rows); ksplit: K
+ * to the planner.  ring: weight ring slots per wave of the bf16 kernel (in
+ * LDS, or in registers for packed weights with five or more row tiles;
+ * built: 8, 5, 3 for 2 row tiles; 7, 5, 3 for 3; 6, 5, 3 for 4 to 6; 5, 3
+ * for 7 and 8; 4, 3 for 9; 3 for 10 -- a call planned with any other fails
+ * with BDR_EHIP); workgroups: row ranges (at most one per 16 rows); ksplit: K
  * splits of a call that may split K (at most one per 128-element K block).
  * While any is set, dflash_fuse_fc_lm_head runs its two GEMMs one after the
  * other.  Workspace sizes follow the override, so query them after setting
