@@ -42,8 +42,8 @@ def log(msg):
 GEMM_SOURCES = ("gemm.hip", "gemm_kernels.h", "gemm_ns.h", "gemm_ns_bf16.hip",
                 "gemm_ns_packed.hip", "gemm_ns_pair_a.hip", "gemm_ns_pair_b.hip",
                 "gemm_ns_pair_packed.hip", "pack.hip", "bdr_device.h", "gemm_plan.h")
-GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_kernels.h",
-                    "bdr_device.h", "gemm_plan.h")
+GEMM_FP8_SOURCES = ("gemm_fp8.hip", "gemm_ns.h", "gemm_ns_fp8.hip", "gemm_ns_fp8_reg.hip",
+                    "gemm_kernels.h", "bdr_device.h", "gemm_plan.h")
 
 
 def kernel_source_hash(sources=GEMM_SOURCES) -> str:

@@ -465,7 +465,10 @@ static bool plan_ns(int64_t M, int64_t N, int64_t K, int esize, bool allow_split
   p->stream = true;
   p->ns = true;
   p->mt = static_cast<int>(mtiles);
-  p->reg = packed && p->mt >= kNsRegMinMt;
+  // (fp8 codes: only K-split plans, the fc: straight operand loads of row-major
+  // codes slowed the fp8 LM head 205 -> 237 us, while the fc, bound by its
+  // widening and MFMAs rather than its stream, fits beside the chain with them)
+  p->reg = p->mt >= kNsRegMinMt && (packed || (esize == 1 && p->ksplit > 1));
   ns_passes(p->mt, ns_wave_tiles(N, p->n_waves), &p->ring, p->reg);
   if (g_ns_ring.load() > 0) p->ring = g_ns_ring.load();   // (the launch checks it is built)
   p->kblocks = kblocks;

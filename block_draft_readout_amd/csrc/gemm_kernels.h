@@ -120,6 +120,7 @@ hipError_t launch_stream_fp8(const GemmPlan& p, const GemmArgs& g, hipStream_t s
 // row-split workgroup kernel (gemm_ns.h): bf16 and fp8 weights, bf16 A
 hipError_t launch_ns_bf16(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
+hipError_t launch_ns_fp8_reg(const GemmPlan& p, const StreamArgs& sa, hipStream_t st);
 // the LM head (mt0 row tiles, ring r0) beside the fc (mt1 = mt0 or mt0 + 1 row
 // tiles, ring 3) in one launch: mt0 2..4 (gemm_ns_pair_a.hip), 5..9 (_b)
 hipError_t launch_ns_pair_bf16_a(int mt0, int r0, int mt1, const StreamArgs& a0,

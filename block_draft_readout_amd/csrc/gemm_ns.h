@@ -55,7 +55,10 @@
 // LDS: four contiguous 1 KB loads put a visit straight into the registers the
 // MFMAs read, and the ring is R visits of registers (a pass is one group of R
 // tiles, the register budget).  Its slot is refilled once the visit's MFMAs
-// are issued; the waits count the same loads as above.
+// are issued; the waits count the same loads as above.  fp8 codes (the fc's
+// K-split plans) take the register ring from the row-major matrix: load p of
+// a visit gives lane l = 16 g + r the 16 codes of row r at 64 p + 16 g, the
+// operand order of the LDS path's reads, with no LDS ring beside the chain.
 #pragma once
 
 #include "gemm_kernels.h"
@@ -111,7 +114,6 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
                                              char* lds) {
   using SH = NsShape<S>;
   constexpr bool F8 = SH::F8;
-  static_assert(!(REG && F8), "the register ring takes bf16 weights");
   constexpr int NG = NsLean<MT, R, REG>::NG;
   constexpr int NTW = NsLean<MT, R, REG>::NTW;
   static_assert(NG >= 1 && R >= 2, "ring shape");
@@ -164,7 +166,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   // so a visit is one contiguous 4 KB and the visits of one K block are
   // adjacent.  A visit's bytes sit at block * kb_str + tile * tile_bytes (rows
   // row_str apart in the row-major layout).
-  const bool packed = REG || (!F8 && g.w_packed != 0);
+  const bool packed = !F8 && (REG || g.w_packed != 0);
   const uint32_t row_str = packed ? static_cast<uint32_t>(SH::WROW) : kbytes;
   const uint32_t kb_str = packed ? static_cast<uint32_t>(n_t * 16 * SH::WROW)
                                  : static_cast<uint32_t>(SH::WROW);
@@ -194,6 +196,13 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
     if constexpr (!REG) asm volatile("" : "+v"(lane_off[j]));
   }
   const uint32_t jstride = packed ? 1024u : static_cast<uint32_t>(SH::RPI) * row_str;
+  // (fp8, register ring) the column of load q of a visit's row and the lane's
+  // offset within the visit
+  uint32_t f8_col[2], f8_lane[2];
+  static_for<2>([&](auto q) {
+    f8_col[q] = static_cast<uint32_t>(64 * q + 16 * grp);
+    f8_lane[q] = static_cast<uint32_t>(r16) * row_str + f8_col[q];
+  });
   const uint32_t a_row = static_cast<uint32_t>(lane / 16);
   const uint32_t a_chunk = static_cast<uint32_t>((lane % 16) ^ SH::ax(lane / 16)) * 16;
   const uint32_t rd = static_cast<uint32_t>((r16 / SH::RPI) * SH::GROUP + (r16 % SH::RPI) * SH::WROW);
@@ -219,7 +228,7 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   };
   zero_acc();
   u32x4_t a[MT][4];
-  u32x4_t wr[REG ? R : 1][4];   // the register ring
+  u32x4_t wr[REG ? R : 1][SH::WSTEPS];   // the register ring
 
   // visit -> ring slot: sb = the visit's byte offset within this wave's rows
   // (pass base + K block + tile), kOOB for a visit past the last pass; ti = its
@@ -229,7 +238,17 @@ __device__ __forceinline__ void ns_lean_body(const StreamArgs& sa, unsigned bx, 
   const int wtiles = __builtin_amdgcn_readfirstlane((n_hi - n_lo + 15) / 16);
   auto dma_w = [&](uint32_t sb, int ti, uint32_t kb, auto slot) {
     const bool none = sb == kOOB || ti >= wtiles;
-    if constexpr (REG) {
+    if constexpr (REG && F8) {
+      // row-major codes straight into operand layout: load p gives lane
+      // (grp, r16) the 16 codes of the visit's row r16 at 64 p + 16 grp (rows
+      // past the wave's range lie beyond the descriptor; codes past a partial
+      // last block are cut)
+      const uint32_t s_off = __builtin_amdgcn_readfirstlane(none ? kOOB : sb);
+      static_for<2>([&](auto q) {
+        const bool cut = kb == kb_last && f8_col[q] >= tail_bytes;
+        wr[slot][q] = bload16_nt(rw, cut ? kOOB : s_off + f8_lane[q]);
+      });
+    } else if constexpr (REG) {
       // part i (1 KB) -> wr[slot][i]; a partial last block reads the copy's zeros
       const uint32_t s_off = __builtin_amdgcn_readfirstlane(none ? kOOB : sb);
       static_for<4>([&](auto i) {
@@ -460,10 +479,11 @@ __global__ __launch_bounds__(256) void ws_gemm_ns_pair_kernel(const StreamArgs a
   }
 }
 
-// REG: the register ring, which reads the packed layout only
+// REG: the register ring (bf16 weights: the packed layout only; fp8 codes:
+// row-major)
 template <typename S, int MT, int R, bool REG = false>
 hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
-  if (REG && sa.g.w_packed == 0) return hipErrorInvalidValue;
+  if (REG && !kIsFp8<S> && sa.g.w_packed == 0) return hipErrorInvalidValue;
   constexpr size_t lds = ns_lean_lds_bytes<S, MT, R, REG>();
   static bool attr_set = false;  // per instantiation
   if (!attr_set) {
@@ -481,7 +501,7 @@ hipError_t launch_ns_one(const GemmPlan& p, const StreamArgs& sa, hipStream_t st
 template <typename S, int MT0, int R0, int MT1, int R1, bool REG = false>
 hipError_t launch_ns_pair_one(const StreamArgs& a0, const StreamArgs& a1, unsigned n0,
                               unsigned n1, hipStream_t st) {
-  if (REG && (a0.g.w_packed == 0 || a1.g.w_packed == 0)) return hipErrorInvalidValue;
+  if (REG && !kIsFp8<S> && (a0.g.w_packed == 0 || a1.g.w_packed == 0)) return hipErrorInvalidValue;
   constexpr size_t l0 = ns_lean_lds_bytes<S, MT0, R0, REG>();
   constexpr size_t l1 = ns_lean_lds_bytes<S, MT1, R1, REG>();
   constexpr size_t lds = l0 > l1 ? l0 : l1;

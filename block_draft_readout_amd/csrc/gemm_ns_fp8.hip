@@ -1,11 +1,12 @@
-// Instantiations of the row-split workgroup GEMM (gemm_ns.h) for fp8 (E4M3)
-// weights with per-row scales: every A row-tile count with each ring depth of
-// kNsLeanRings.
+// Instantiations of the row-split workgroup GEMM (gemm_ns.h) with the LDS ring
+// for fp8 (E4M3) weights with per-row scales: every A row-tile count with each
+// ring depth of kNsLeanRings.
 #include "gemm_ns.h"
 
 namespace bdr {
 
 hipError_t launch_ns_fp8(const GemmPlan& p, const StreamArgs& sa, hipStream_t st) {
+  if (p.reg) return launch_ns_fp8_reg(p, sa, st);   // the register ring (gemm_ns_fp8_reg.hip)
 #define BDR_NS(MT, R) \
   if (p.mt == MT && p.ring == R) return launch_ns_one<uint8_t, MT, R>(p, sa, st);
   BDR_NS(2, 8) BDR_NS(2, 5) BDR_NS(2, 3)

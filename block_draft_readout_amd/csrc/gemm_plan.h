@@ -30,7 +30,7 @@ struct GemmPlan {
   int64_t kblocks = 0;
   int64_t kb_per_split = 0;
   int ring = 0;           // ns: LDS ring slots per wave (kNsLeanRings)
-  bool reg = false;       // ns: the register ring (packed bf16, mt >= kNsRegMinMt)
+  bool reg = false;       // ns: the register ring (kNsRegMinMt)
   // tiled variant for many rows (bf16, M > 160): 256 x 160 output tiles,
   // K steps of 64 (kblocks / kb_per_split count steps)
   bool tile = false;
@@ -63,9 +63,10 @@ constexpr int kNumCU = 256;
 // first; 0 = none).  A deep ring keeps more loads in flight, a shallow one
 // wastes fewer slots on waves with few tiles.
 constexpr int kNsLeanNtwMax[11] = {0, 0, 16, 14, 12, 9, 8, 6, 5, 4, 3};
-// bf16 weights in the packed layout take the register ring from this many A
-// row tiles on (the same ring depths; one group of R tiles per pass); fewer
-// row tiles stream faster through the LDS ring
+// bf16 weights in the packed layout, and fp8 codes in K-split plans (the fc),
+// take the register ring from this many A row tiles on (the same ring depths;
+// one group of R tiles per pass); fewer row tiles stream faster through the
+// LDS ring
 constexpr int kNsRegMinMt = 5;
 constexpr int kNsLeanRings[11][3] = {{0, 0, 0}, {0, 0, 0}, {8, 5, 3}, {7, 5, 3}, {6, 5, 3},
                                      {6, 5, 3}, {6, 5, 3}, {5, 3, 0},  {5, 3, 0}, {4, 3, 0},
