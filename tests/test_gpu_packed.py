@@ -160,11 +160,13 @@ def test_packed_every_ring_fc_split_k(mt, ring):
 
 
 @pytest.mark.parametrize("lm_rows,fc_rows,H,T,V", [(32, 40, 512, 5, 30011), (128, 144, 5120, 5, 151936),
-                                                   (32, 40, 2560, 5, 151936)])
+                                                   (32, 40, 2560, 5, 151936), (80, 96, 1024, 5, 60011),
+                                                   (112, 128, 2048, 3, 90011)])
 def test_fused_fc_lm_head_packed(lm_rows, fc_rows, H, T, V):
     """dflash_fuse_fc_lm_head with both weights packed gives the bits of the
-    row-major call (one launch or two, as the plan decides), at a small shape and
-    at the 16- and 4-sequence sizes."""
+    row-major call (one launch or two, as the plan decides), at small and mid
+    shapes (five and seven LM row tiles: the register ring beside the fc) and at
+    the 16- and 4-sequence sizes."""
     bdr = _bdr()
     taps = [_randn_bf16((fc_rows, H), 30 + t) for t in range(T)]
     fc_w = _randn_bf16((H, T * H), 40, (T * H) ** -0.5)
