@@ -145,6 +145,26 @@ def test_fc_fp8_every_ring_split_k(mt, ring):
     assert err <= FC_TOL
 
 
+@pytest.mark.parametrize("rows,ring", [(80, 5), (144, 3)])
+def test_fc_fp8_register_ring_partial_block(rows, ring):
+    """The fp8 fc's register ring (K-split plans with five or more row tiles)
+    on one tap with H = 192: the second 128-code block is partial, so its codes
+    past K are cut from the operand loads; K forced into two splits."""
+    H = 192
+    rng = np.random.default_rng(rows * 10 + ring)
+    taps = [_bf16(rng, (rows, H))]
+    q, s = synth.quantize_e4m3_rows(rng.standard_normal((H, H)).astype(np.float32) / np.sqrt(H))
+    bdr().set_row_split_override(ring, 1, 2)
+    try:
+        out = bdr().dflash_fuse_fc_fp8([dev(t) for t in taps], dev(q), dev(s))
+        torch.cuda.synchronize()
+    finally:
+        bdr().set_row_split_override(0, 0, 0)
+    err = max_rel_err(oracle.widen(host_bits(out), "bf16"), fp8.fuse_fc_fp8(taps, q, s, "bf16"))
+    log(f"fp8 fc register ring, partial block: rows={rows} H={H} ring {ring}: max rel err {err:.3e}")
+    assert err <= FC_TOL
+
+
 FC_CASES = [(5, 64, 5), (9, 192, 3), (8, 2560, 5), (36, 2560, 5), (8, 5120, 5), (20, 1024, 2),
             (128, 5120, 5), (144, 256, 3), (20, 192, 3), (40, 64, 5), (176, 512, 2)]
 
