@@ -153,6 +153,21 @@ __device__ __forceinline__ void lse_add(Lse& a, float f) {
   }
 }
 
+// eight entries at once: one rescale of the running sum to the new maximum,
+// then eight independent exponentials (a third of the per-entry ALU work of
+// lse_add, and no dependent chain between entries)
+__device__ __forceinline__ void lse_add8(Lse& a, const float (&f)[8]) {
+  const float mx = fmaxf(fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])),
+                         fmaxf(fmaxf(f[4], f[5]), fmaxf(f[6], f[7])));
+  const float m = fmaxf(a.m, mx);
+  float e[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) e[t] = exp2_hw(f[t] - m);
+  const float s8 = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  a.s = a.s * exp2_hw(a.m - m) + s8;   // a.m = -inf, a.s = 0 at the start: 0
+  a.m = m;
+}
+
 __device__ __forceinline__ Lse lse_merge(Lse a, Lse b) {
   if (b.s == 0.f) return a;
   if (a.s == 0.f) return b;
@@ -298,10 +313,14 @@ __global__ __launch_bounds__(256) void sample_lse_kernel(const SampleArgs g) {
         for (int u = 0; u < U; ++u) {
           if (v0 + u * 2048 < c1) {
             const S* ye = reinterpret_cast<const S*>(yq[u]);
+            float fy[8], fx[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) lse_add(lp, to_f32<S>(ye[t]) * c2);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) lse_add(lq, __uint_as_float(xq[u][t >> 2][t & 3]) * c2);
+            for (int t = 0; t < 8; ++t) {
+              fy[t] = to_f32<S>(ye[t]) * c2;
+              fx[t] = __uint_as_float(xq[u][t >> 2][t & 3]) * c2;
+            }
+            lse_add8(lp, fy);
+            lse_add8(lq, fx);
           }
         }
       }
@@ -360,24 +379,52 @@ __global__ __launch_bounds__(256) void sample_draw_kernel(const SampleArgs g) {
   __shared__ int last;
   float bp = -INFINITY, br = -INFINITY;
   uint32_t ip = 0xFFFFFFFFu, ir = 0xFFFFFFFFu;
+  const bool vec4 = (g.V & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & (4 * sizeof(S) - 1)) == 0 &&
+                    (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   for (int64_t v0 = c0 + static_cast<int64_t>(threadIdx.x) * 4; v0 < c1; v0 += 256 * 4) {
     const u32x4_t u = philox4x32_10(
         u32x4_t{static_cast<uint32_t>(v0 >> 2), static_cast<uint32_t>(b), static_cast<uint32_t>(s),
                 kStreamResample},
         g.k0, g.k1);
+    // the quad's logits in one load each where the whole quad is in range and
+    // the rows are 16-byte aligned (V a multiple of 4), else entry by entry
+    float yq[4], xq[4];
+    if (vec4 && v0 + 3 < c1) {
+      if constexpr (sizeof(S) == 2) {
+        const uint2 t = *reinterpret_cast<const uint2*>(y + v0);
+        yq[0] = __uint_as_float(t.x << 16);
+        yq[1] = __uint_as_float(t.x & 0xFFFF0000u);
+        yq[2] = __uint_as_float(t.y << 16);
+        yq[3] = __uint_as_float(t.y & 0xFFFF0000u);
+      } else {
+        const float4 t = *reinterpret_cast<const float4*>(y + v0);
+        yq[0] = t.x; yq[1] = t.y; yq[2] = t.z; yq[3] = t.w;
+      }
+      if (resid) {
+        const float4 t = *reinterpret_cast<const float4*>(x + v0);
+        xq[0] = t.x; xq[1] = t.y; xq[2] = t.z; xq[3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int64_t v = v0 + w < c1 ? v0 + w : c0;   // clamped: always readable
+        yq[w] = to_f32<S>(y[v]);
+        xq[w] = resid ? x[v] : 0.f;
+      }
+    }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int64_t v = v0 + w;
       if (v < c1) {
         const float G = gumbel_of(bits_to_uniform(u[w]));
-        const float yv = to_f32<S>(y[v]);
+        const float yv = yq[w];
         const float kp = yv * g.inv_t + G;
         if (kp > bp) {
           bp = kp;
           ip = static_cast<uint32_t>(v);
         }
         if (resid) {
-          const float wv = exp2_hw(yv * c2 - lse_p) - exp2_hw(x[v] * c2 - lse_q);
+          const float wv = exp2_hw(yv * c2 - lse_p) - exp2_hw(xq[w] * c2 - lse_q);
           if (wv > 0.f) {
             const float kr = log2_hw(wv) * kLn2 + G;
             if (kr > br) {
