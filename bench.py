@@ -133,9 +133,12 @@ class Step:
         w, b = self.w, self.b
         if self.sample is not None:
             T, seed = self.sample
+            conf = self.s.get("conf")
+            th = float("nan") if w.threshold is None else w.threshold
             return self.L.dspark_markov_sample(
                 b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt, self.w1, self.w2,
-                w.rank, self.prev, T, seed, b["d"].data_ptr(), b["x"].data_ptr(), self.status,
+                w.rank, self.prev, T, seed, b["d"].data_ptr(), b["x"].data_ptr(),
+                None if conf is None else conf.data_ptr(), th, self.status,
                 b["ws_ms"], b["ws_ms_n"], self.stream)
         return self.L.dspark_markov_argmax(b["logits"].data_ptr(), w.batch, w.k, w.vocab, self.dt,
                                            self.w1, self.w2, w.rank, self.prev, b["d"].data_ptr(),
@@ -596,6 +599,7 @@ def main():
     t0 = time.time()
     slots, host0 = [], None
     verify_bytes = []
+    x_positions = []     # sampling: (row, position) pairs whose x is written (j < L_b)
     es = 2 if w.dtype == "bf16" else 4
     for p in range(args.pool):
         s = synth.make_step(w, p)
@@ -619,6 +623,7 @@ def main():
         torch.cuda.synchronize()
         # verification reads the rows of the (confidence-truncated) blocks only
         verify_bytes.append(int((bufs["bl"].cpu().numpy().astype(np.int64) + 1).sum()) * V * es)
+        x_positions.append(int(bufs["bl"].cpu().numpy().astype(np.int64).sum()))
         slots.append(st)
         if p == 0:
             host0 = {"taps": s["taps"], "draft_hidden": s["draft_hidden"], "prev0": s["prev0"],
@@ -828,8 +833,8 @@ def main():
         lm_bytes = V * H * es + B * k * H * es + B * k * V * 4
         fc_bytes = (H * w.n_taps * H + w.rows * w.n_taps * H + w.rows * H) * es
     markov_bytes = B * k * V * 4 + V * rk * es + B * k * rk * es + B * k * 4
-    if sampling:      # x written (the chain generates the draws' noise itself)
-        markov_bytes += B * k * V * 4
+    if sampling:      # x written at j < L_b (the chain generates the draws' noise itself)
+        markov_bytes += int(round(float(np.mean(x_positions)) * V * 4))
     conf_bytes = 0 if w.threshold is None else B * k * 4
     verify_b = float(np.mean(verify_bytes)) + B * k * 4 + conf_bytes
     stage_bytes = {"fc": fc_bytes, "lm_head": lm_bytes, "markov": markov_bytes,

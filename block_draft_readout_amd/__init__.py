@@ -566,13 +566,17 @@ def dspark_markov_sample(logits: torch.Tensor, markov_w1: Optional[torch.Tensor]
                          draft_logits: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None,
                          status: Optional[torch.Tensor] = None,
-                         check: bool = True):
+                         check: bool = True,
+                         confidence: Optional[torch.Tensor] = None,
+                         threshold: Optional[float] = None):
     """Probabilistic drafting: (draft_tokens [B, k] int32, draft_logits [B, k, V] fp32)
     (``status`` / ``check`` as in dspark_markov_argmax).
 
     Each position's token is drawn from softmax((logits + Markov bias) / T) and
     becomes the next position's Markov context; draft_logits holds the biased
-    logits the tokens were drawn from (the q of rejection sampling).
+    logits the tokens were drawn from (the q of rejection sampling).  With
+    ``confidence`` [B, k] and ``threshold``, draft_logits is written only at the
+    positions j < L_b that spec_verify_sample reads (the rest keep their values).
     """
     L = lib()
     _dev(logits, "logits")
@@ -590,14 +594,19 @@ def dspark_markov_sample(logits: torch.Tensor, markov_w1: Optional[torch.Tensor]
         draft_logits = torch.empty((B, k, V), dtype=torch.float32, device=logits.device)
     _dev(draft_tokens, "draft_tokens")
     _dev(draft_logits, "draft_logits")
+    if confidence is not None:
+        _dev(confidence, "confidence")
+        if confidence.dtype != torch.float32 or confidence.numel() != B * k:
+            raise ValueError("confidence must be fp32 [B, k]")
+    th = float("nan") if threshold is None else float(threshold)
     ws = _workspace(L.dspark_markov_sample_workspace_bytes(B, k, V), logits.device, workspace)
     wp, wn = _ws_ptr(ws)
     st = _status_in(status, check, logits.device)
     _abi.check("dspark_markov_sample",
                L.dspark_markov_sample(_ptr(logits), B, k, V, wdt, _ptr(w1), _ptr(w2), r,
                                       _ptr(prev_token), float(temperature), int(seed),
-                                      _ptr(draft_tokens), _ptr(draft_logits), _ptr(st), wp, wn,
-                                      _stream(logits.device)))
+                                      _ptr(draft_tokens), _ptr(draft_logits), _ptr(confidence),
+                                      th, _ptr(st), wp, wn, _stream(logits.device)))
     _status_out("dspark_markov_sample", st, check and B > 0)
     return draft_tokens, draft_logits
 

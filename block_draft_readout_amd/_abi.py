@@ -64,7 +64,7 @@ SIGNATURES = {
     "dspark_gumbel_noise": (_int, [_i64, _int, _i64, _u64, _int, _vp, _vp]),
     "dspark_markov_sample_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "dspark_markov_sample": (_int, [_vp, _i64, _int, _i64, _int, _vp, _vp, _int, _vp, C.c_float,
-                                    _u64, _vp, _vp, _vp, _vp, _sz, _vp]),
+                                    _u64, _vp, _vp, _vp, C.c_float, _vp, _vp, _sz, _vp]),
     "spec_verify_sample_workspace_bytes": (_sz, [_i64, _int, _i64]),
     "spec_verify_sample": (_int, [_vp, _int, _i64, _int, _i64, _vp, _vp, _vp, C.c_float,
                                   C.c_float, _u64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

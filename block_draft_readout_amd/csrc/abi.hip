@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
 
 extern "C" {
 
-int bdr_abi_version(void) { return 10; }
+int bdr_abi_version(void) { return 11; }
 
 void bdr_set_markov_poll_timeout_us(double us) { bdr::set_poll_timeout_us(us); }
 
@@ -637,8 +637,9 @@ size_t dspark_markov_sample_workspace_bytes(int64_t batch, int k, int64_t vocab)
 int dspark_markov_sample(const float* logits, int64_t batch, int k, int64_t vocab,
                          bdr_dtype wdt, const void* markov_w1, const void* markov_w2, int rank,
                          const int32_t* prev_token, float temperature, uint64_t seed,
-                         int32_t* draft_tokens, float* draft_logits, int32_t* status,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         int32_t* draft_tokens, float* draft_logits, const float* confidence,
+                         float threshold, int32_t* status, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   BDR_TRY(block_shape(batch, k, vocab));
   BDR_TRY(markov_shape(wdt, markov_w1, markov_w2, rank, vocab, k));
   BDR_TRY(need_temperature(temperature));
@@ -647,13 +648,15 @@ int dspark_markov_sample(const float* logits, int64_t batch, int k, int64_t voca
   BDR_TRY(need_ptr(prev_token, "prev_token", 4));
   BDR_TRY(need_ptr(draft_tokens, "draft_tokens", 4));
   BDR_TRY(need_ptr(draft_logits, "draft_logits"));
+  if (confidence) BDR_TRY(need_ptr(confidence, "confidence", 4));
   if (status) BDR_TRY(need_ptr(status, "status", 4));
   BDR_TRY(need_ws(workspace, workspace_bytes, markov_sample_workspace(batch, k, vocab)));
   int cus = 0;
   BDR_TRY(check_device(&cus));
   hipError_t e = launch_markov_sample(logits, batch, k, vocab, wdt, markov_w1, markov_w2, rank,
                                       prev_token, 1.0f / temperature, seed, draft_tokens,
-                                      draft_logits, status, workspace, cus, as_stream(stream));
+                                      draft_logits, confidence, threshold, status, workspace, cus,
+                                      as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "dspark_markov_sample launch");
   return BDR_OK;
 }

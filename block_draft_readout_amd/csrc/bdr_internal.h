@@ -43,7 +43,8 @@ size_t markov_sample_workspace(int64_t B, int k, int64_t V);
 hipError_t launch_markov_sample(const float* logits, int64_t B, int k, int64_t V, bdr_dtype wdt,
                                 const void* w1, const void* w2, int rank, const int32_t* prev,
                                 float inv_t, uint64_t seed, int32_t* draft, float* xout,
-                                int32_t* status, void* workspace, int n_cu, hipStream_t stream);
+                                const float* conf, float threshold, int32_t* status,
+                                void* workspace, int n_cu, hipStream_t stream);
 size_t sample_verify_workspace(int64_t B, int k, int64_t V);
 hipError_t launch_verify_sample(const void* Y, bdr_dtype dt, int64_t B, int k, int64_t V,
                                 const int32_t* draft, const float* X, const float* conf,

@@ -55,6 +55,15 @@
 
 namespace bdr {
 
+// x of the sampling chain is written once and read once by verification:
+// streaming (non-temporal) stores keep it from displacing the hand-off lines
+__device__ __forceinline__ void xstore16(f32x4_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 2);
+}
+__device__ __forceinline__ void xstore_f32(float v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 2);
+}
+
 struct MarkovArgs {
   const float* logits;           // [B, k, V]
   int64_t B, V;
@@ -80,7 +89,17 @@ struct MarkovArgs {
   uint32_t seed_lo, seed_hi;     // Philox key
   float* xout;                   // [B, k, V] biased logits x (the draft distribution)
   float inv_t;                   // 1 / temperature
+  // x only for the positions verification reads: j < L_b, L_b the block length
+  // by confidence (conf [B, k] and threshold th, when use_conf)
+  const float* conf;
+  float th;
+  int use_conf;
 };
+
+// positions of row b whose x is stored
+__device__ __forceinline__ int markov_x_len(const MarkovArgs& g, int64_t b) {
+  return g.use_conf ? truncated_length<BDR_MAX_K>(g.conf + b * g.k, g.th, g.k) : g.k;
+}
 
 constexpr int kChainSlots = kNumCU;   // workgroups of the chain (at most)
 constexpr int kChainMaxB = 256;       // rows the chain keeps contexts of in LDS
@@ -277,6 +296,7 @@ void markov_chain_kernel(const MarkovArgs g) {
 
   __shared__ unsigned long long sk[4][4][16];      // [compute wave][lane group][row]
   __shared__ int32_t ctx[kChainMaxB];              // context token of every row
+  __shared__ int xlen[SAMPLE ? kChainMaxB : 1];    // sampling: positions of x stored per row
   __shared__ int last_flag;
 
   // stage this workgroup's markov_w2 rows in operand layout (lane l's 16 bytes
@@ -293,7 +313,10 @@ void markov_chain_kernel(const MarkovArgs g) {
           r2, (__attribute__((address_space(3))) void*)(&w2s[q * 64]), 16, off, 0, 0, 0);
     }
   }
-  for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x) ctx[b] = g.prev[b];
+  for (int64_t b = threadIdx.x; b < g.B; b += blockDim.x) {
+    ctx[b] = g.prev[b];
+    if constexpr (SAMPLE) xlen[b] = markov_x_len(g, b);
+  }
 
   // logits of position pos, row b0 + r16, vocabulary entries 16 * tile + 4 * grp
   // .. + 3 of this compute wave's tiles: one 16-byte load per tile (entries
@@ -423,8 +446,11 @@ void markov_chain_kernel(const MarkovArgs g) {
           float bv = -INFINITY;
           int bu = -1;   // tile slot u of the lane's maximum
           rsrc_t rx;
-          if constexpr (SAMPLE)
+          bool xl = false;   // x of this position is stored
+          if constexpr (SAMPLE) {
             rx = make_rsrc(g.xout + static_cast<int64_t>(pos) * g.V, static_cast<uint32_t>(V32) * 4u);
+            xl = pos < xlen[0];
+          }
 #pragma unroll
           for (int u = 0; u < MAXT; ++u) {
             const int tile = cwo + 4 * u;
@@ -439,7 +465,7 @@ void markov_chain_kernel(const MarkovArgs g) {
             float key = sv;
             if constexpr (SAMPLE) {
               key = sv * g.inv_t + n1[u];
-              bstore_f32(sv, rx, x1[u]);
+              xstore_f32(sv, rx, xl ? x1[u] : kOOB);
             }
             if (key > bv) {
               bv = key;
@@ -478,6 +504,8 @@ void markov_chain_kernel(const MarkovArgs g) {
           float bv = -INFINITY;
           int bs = -1;
           const bool row_ok = r16 < nb;
+          bool x_ok = false;   // x of row r16 at this position is stored
+          if constexpr (SAMPLE) x_ok = row_ok && pos < xlen[row_ok ? b0 + r16 : 0];
           rsrc_t rx;
           f32x4_t xt = {0.f, 0.f, 0.f, 0.f};
           uint32_t toff = kOOB;
@@ -509,12 +537,12 @@ void markov_chain_kernel(const MarkovArgs g) {
             if constexpr (SAMPLE) {
               // entries of the lane's quad that exist (<= 0: none)
               const int v0 = vbo + 16 * tile;
-              const int lim = (row_ok && tile < ntlo) ? V32 - v0 : 0;
+              const int lim = (x_ok && tile < ntlo) ? V32 - v0 : 0;
               // x of the lane's four entries in one 16-byte store; the quad that
               // straddles the end of the row (at most one per lane) is kept for
               // element stores after the loop
               const uint32_t off = static_cast<uint32_t>(r16) * zrow + static_cast<uint32_t>(v0) * 4u;
-              bstore16(xs, rx, lim >= 4 ? off : kOOB);
+              xstore16(xs, rx, lim >= 4 ? off : kOOB);
               const bool part = lim > 0 && lim < 4;
               xt = part ? xs : xt;
               toff = part ? off : toff;
@@ -524,7 +552,7 @@ void markov_chain_kernel(const MarkovArgs g) {
             const int tn = V32 & 3;   // entries of a straddling quad
             if (toff != kOOB) {
 #pragma unroll
-              for (int i = 0; i < 3; ++i) bstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
+              for (int i = 0; i < 3; ++i) xstore_f32(xt[i], rx, i < tn ? toff + 4u * i : kOOB);
             }
           }
           // the next position's first logits: independent of the hand-off below
@@ -665,12 +693,14 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
   if constexpr (SAMPLE) rx = make_rsrc(g.xout + (b0 * g.k + pos) * g.V, blk);
   uint32_t zrow[4];
   bool bok[4];
+  bool xok[4];   // sampling: x of the row at this position is stored
   float bv[4];
   uint32_t bi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rb = 4 * grp + i;
     bok[i] = rb < nb;
+    xok[i] = SAMPLE && bok[i] && pos < markov_x_len(g, b0 + rb);
     zrow[i] = static_cast<uint32_t>(rb * g.k * g.V * 4);
     bv[i] = -INFINITY;
     bi[i] = 0xFFFFFFFFu;
@@ -725,7 +755,7 @@ __global__ __launch_bounds__(256) void markov_pass_kernel(const MarkovArgs g, in
         float key = s;
         if constexpr (SAMPLE) {
           key = s * g.inv_t + gn[u][i];
-          bstore_f32(s, rx, (v < g.V && bok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
+          xstore_f32(s, rx, (v < g.V && xok[i]) ? zrow[i] + static_cast<uint32_t>(v * 4) : kOOB);
         }
         if (v < g.V && bok[i] && key > bv[i]) {
           bv[i] = key;

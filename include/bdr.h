@@ -469,6 +469,12 @@ int dspark_gumbel_noise(int64_t batch, int k, int64_t vocab, uint64_t seed,
  *   temperature T > 0; seed as above
  *   draft_tokens [B, k] int32 out
  *   draft_logits [B, k, V] fp32 out (x, before the division by T)
+ *   confidence   [B, k] fp32 or NULL, threshold: as in spec_verify_greedy.
+ *                Given (and threshold not NaN), x is written only at the
+ *                positions j < L_b, the ones spec_verify_sample reads with
+ *                the same confidence and threshold; the other positions of
+ *                draft_logits keep what they held.  The tokens are drawn at
+ *                every position either way.
  *   status       optional device int32 out, as in S3
  *   workspace    >= dspark_markov_sample_workspace_bytes(B, k, V): a Markov
  *                workspace (same rules as S3; its error word is in the last
@@ -482,7 +488,8 @@ int dspark_markov_sample(const float* logits, int64_t batch, int k,
                          const void* markov_w2, int rank,
                          const int32_t* prev_token, float temperature,
                          uint64_t seed, int32_t* draft_tokens,
-                         float* draft_logits, int32_t* status, void* workspace,
+                         float* draft_logits, const float* confidence,
+                         float threshold, int32_t* status, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* spec_verify_sample -- S4 by rejection sampling.

@@ -45,7 +45,7 @@ def test_binding_declares_every_header_symbol():
 
 
 def test_version(L):
-    assert L.bdr_abi_version() == 10
+    assert L.bdr_abi_version() == 11
 
 
 def test_workspace_sizes(L):
@@ -243,8 +243,8 @@ def test_sampling_validation(L):
     P = C.c_void_p(4096)
     ws = C.c_void_p(4096)
     m = lambda T=1.0, B=4, k=8, V=1000, r=64, x=P, prev=P, wp=ws, wn=4096: \
-        L.dspark_markov_sample(P, B, k, V, A.BDR_BF16, P, P, r, prev, T, 7, P, x, None, wp, wn,
-                               None)
+        L.dspark_markov_sample(P, B, k, V, A.BDR_BF16, P, P, r, prev, T, 7, P, x, None,
+                               float("nan"), None, wp, wn, None)
     assert m(T=0.0) == A.BDR_EINVAL
     assert m(T=-1.0) == A.BDR_EINVAL
     assert m(T=float("nan")) == A.BDR_EINVAL

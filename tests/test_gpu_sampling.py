@@ -119,6 +119,40 @@ def test_markov_sample_parity(name):
     log(f"  {c}")
 
 
+@pytest.mark.parametrize("name", ["bf16_b5", "bf16_b20", "f32_r128_passes", "b1_bf16_r64",
+                                  "b16_vocab"])
+def test_markov_sample_x_only_where_verified(name):
+    """With the block's confidences and threshold, draft_logits is written only
+    at the positions j < L_b (the first confidence below the threshold ends the
+    block) and elsewhere keeps what it held; the tokens are those of the call
+    without them, and x where written is the same, bit for bit."""
+    B, k, V, r, dtype, std, T = DRAFT_CASES[name]
+    cid = 70 + list(DRAFT_CASES).index(name)
+    seed = 1000 + cid
+    Z = _logits(cid, B, k, V, std)
+    w1, w2 = _markov(cid, V, r, dtype) if r else (None, None)
+    prev = np.random.default_rng(cid).integers(0, V, B).astype(np.int32)
+    rng = np.random.default_rng(cid + 5)
+    conf = rng.random((B, k)).astype(np.float32)
+    conf[0] = 1.0                       # one row never truncated
+    if B > 1:
+        conf[1, 0] = 0.0                # one row truncated at position 0 (no x at all)
+    th = 0.3
+    L = np.array([next((j for j in range(k) if conf[b, j] < th), k) for b in range(B)])
+    args = (dev(Z), dev(w1) if r else None, dev(w2) if r else None, dev(prev), T, seed)
+    d_all, x_all = bdr().dspark_markov_sample(*args)
+    x_gated = torch.full((B, k, V), float("nan"), dtype=torch.float32, device="cuda")
+    d, _ = bdr().dspark_markov_sample(*args, draft_logits=x_gated, confidence=dev(conf),
+                                      threshold=th)
+    assert np.array_equal(d.cpu().numpy(), d_all.cpu().numpy())
+    xa, xg = x_all.cpu().numpy(), x_gated.cpu().numpy()
+    live = np.arange(k)[None, :] < L[:, None]
+    assert np.array_equal(xg[live].view(np.uint32), xa[live].view(np.uint32))
+    assert np.isnan(xg[~live]).all()
+    log(f"markov sample {name}, x gated by confidence: {int(live.sum())} of {B * k} positions "
+        f"written")
+
+
 def test_small_temperature_is_the_greedy_chain():
     B, k, V, r = 4, 6, 5003, 64
     Z = _logits(90, B, k, V, 3.0)
